@@ -1,0 +1,76 @@
+"""Byte and FLOP accounting for the CSA step (algorithmic, not measured).
+
+These are the quantities a roofline compares against: bytes the method must
+move from HBM, FLOPs it must perform. Written per unit so the totals can be
+re-derived by hand.
+"""
+from __future__ import annotations
+
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def kv_cache_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, elem_bytes: int) -> int:
+    """Uncompressed K+V cache per token: 2 x layers x KV heads x head dim x bytes.
+
+    The formula the Model-architectures atlas gives in its MQA/GQA entry.
+    """
+    return 2 * n_layers * n_kv_heads * d_head * elem_bytes
+
+
+def index_scan_bytes(n_entries: int, d_i: int, kv_dtype: str, page_entries: int = 64) -> int:
+    """Bytes one query's indexer scan reads: its visible indexer keys (+ page scales)."""
+    b = n_entries * d_i * DTYPE_BYTES[kv_dtype]
+    if kv_dtype == "fp8":
+        b += -(-n_entries // page_entries) * 4
+    return b
+
+
+def attend_bytes(k_sel: int, window: int, d: int, h_q: int, kv_dtype: str, act_dtype: str) -> int:
+    """Bytes one query's attention reads and writes for one layer.
+
+    Gathered compressed K and V rows (plus one K and one V page scale per
+    gathered entry for fp8), the window's raw K and V rows, the query, the
+    output, and the Top-K row it reads.
+    """
+    kvb = DTYPE_BYTES[kv_dtype]
+    ab = DTYPE_BYTES[act_dtype]
+    b = k_sel * 2 * d * kvb
+    if kv_dtype == "fp8":
+        b += k_sel * 2 * 4
+    b += window * 2 * d * ab
+    b += 2 * h_q * d * ab
+    b += k_sel * 4
+    return b
+
+
+def decode_step_bytes(n_seq: int, entries: list[int] | int, d: int, d_i: int, h_q: int, h_i: int,
+                      k: int, window: int, group: int, kv_dtype: str, act_dtype: str) -> int:
+    """Algorithmic HBM bytes of one decode step: one index pass + `group` attends.
+
+    entries: visible compressed entries per sequence (one int for all, or a list).
+    """
+    if isinstance(entries, int):
+        entries = [entries] * n_seq
+    ab = DTYPE_BYTES[act_dtype]
+    total = 0
+    for n in entries:
+        total += index_scan_bytes(n, d_i, kv_dtype)
+        total += h_i * d_i * ab + h_i * 4 + k * 4          # q_idx, w, Top-K row written
+        k_sel = min(k, n)
+        total += group * attend_bytes(k_sel, window, d, h_q, kv_dtype, act_dtype)
+    return total
+
+
+def index_flops(n_scores: int, h_i: int, d_i: int) -> int:
+    """Multiply-adds of the indexer, counted as 2 FLOP each, per visible score."""
+    return n_scores * h_i * d_i * 2
+
+
+def attend_flops(n_queries: int, h_q: int, n_keys: int, d: int) -> int:
+    """QK^T and PV: 2 x 2 x heads x keys x dim per query."""
+    return n_queries * h_q * n_keys * d * 4
+
+
+def prefill_visible_scores(prior_tokens: int, chunk: int, r: int) -> int:
+    """Visible (query, entry) pairs of a prefill chunk: query t sees (t+1)//r entries."""
+    return sum((prior_tokens + tau + 1) // r for tau in range(chunk))

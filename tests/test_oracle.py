@@ -1,0 +1,397 @@
+"""The oracle pinned to things other than itself (CPU only).
+
+Every pin is a closed form, a library routine the method reduces to in a
+special case, a brute-force computation written differently, or a value a
+page prints. A plausible slip in the oracle (a dropped term, a wrong sign or
+index, a transposed operand, a wrong rounding) fails at least one of these.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+
+RNG = np.random.default_rng(1234)
+
+
+# --------------------------------------------------------------------------- bf16
+
+def test_bf16_round_matches_torch():
+    x = RNG.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    # exact bf16 midpoints (the 16 dropped bits are 0x8000) exercise ties-to-even
+    base = (RNG.standard_normal(2000) * 100).astype(np.float32).view(np.uint32)
+    mids = ((base & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, mids, np.float32([0.0, -0.0, 1e-40, -3e-39, 65504.0])])
+    ours = O.round_bf16(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_round_is_direct_from_float64():
+    # 1 + 2^-8 is an exact tie -> even (1.0); 1 + 2^-8 + 2^-40 is just above
+    # the tie -> rounds up to 1 + 2^-7. A double rounding through float32
+    # would collapse the second case onto the tie and give 1.0.
+    v = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -40, -(1 + 2 ** -8 + 2 ** -40)])
+    assert list(O.round_bf16(v)) == [0x3F80, 0x3F82, 0x3F81, 0xBF81]
+    assert np.array_equal(O.decode_bf16(O.round_bf16(v)), [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -(1 + 2 ** -7)])
+
+
+# --------------------------------------------------------------------------- e4m3
+
+def _load_e4m3(golden_dir):
+    vals, codes = [], []
+    with open(os.path.join(golden_dir, "e4m3_codes.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split()
+            vals.append(float(a))
+            codes.append(int(b, 16))
+    return np.array(vals), np.array(codes, dtype=np.uint8)
+
+
+def test_e4m3_golden_codes(golden_dir):
+    vals, codes = _load_e4m3(golden_dir)
+    got = O.e4m3_encode(vals.astype(np.float32))
+    bad = [(v, hex(c), hex(g)) for v, c, g in zip(vals, codes, got) if c != g]
+    assert not bad, bad
+
+
+def test_e4m3_max_is_448_and_fp4_range():
+    assert O.e4m3_decode(np.uint8([0x7E]))[0] == 448.0
+    assert O.e4m3_decode(np.uint8([0xFE]))[0] == -448.0
+    assert np.isnan(O.e4m3_decode(np.uint8([0x7F]))[0])
+    # the FP4 section's range figure: E4M3 scale max times E2M1 element max
+    assert O.E4M3_MAX * 6 == 2688
+
+
+def test_e4m3_roundtrip_all_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = O.e4m3_decode(codes)
+    back = O.e4m3_encode(vals.astype(np.float32))
+    # +0 and -0 keep their sign bits
+    assert np.array_equal(back, codes)
+
+
+def test_e4m3_nearest_and_monotone():
+    finite = np.array([c for c in range(128) if c != 0x7F], dtype=np.uint8)
+    grid = np.sort(O.e4m3_decode(finite))           # 0 .. 448, all non-negative codes
+    x = np.sort(RNG.uniform(0, 500, 5000)).astype(np.float32)
+    got = O.e4m3_decode(O.e4m3_encode(x))
+    assert np.all(np.diff(got) >= 0)
+    # brute force: the decoded value is a nearest grid point (ties aside)
+    for xi, gi in zip(x[::25], got[::25]):
+        d = np.abs(grid - min(float(xi), 448.0))
+        assert abs(gi - min(float(xi), 448.0)) <= d.min() + 1e-12
+
+
+def test_fp8_page_amax_hits_448_and_exact_values_roundtrip():
+    x = (RNG.standard_normal((40, 16)) * 5).astype(np.float32)
+    codes, s = O.fp8_quantize_page(x)
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert codes[i] in (0x7E, 0xFE)
+    assert s == np.float32(np.max(np.abs(x)) / np.float32(448.0))
+    # values that are E4M3 grid points times a power-of-two scale come back exactly
+    grid = O.e4m3_decode(RNG.integers(0, 0x7E, (8, 8)).astype(np.uint8))
+    grid[0, 0] = 448.0
+    y = (grid * 0.125).astype(np.float32)
+    c2, s2 = O.fp8_quantize_page(y)
+    assert s2 == np.float32(0.125)
+    assert np.array_equal(O.e4m3_decode(c2) * s2, grid * 0.125)
+    # all-zero page keeps scale 1
+    c3, s3 = O.fp8_quantize_page(np.zeros((3, 4), np.float32))
+    assert s3 == 1.0 and not c3.any()
+
+
+def test_store_fp8_pages_are_independent():
+    x = RNG.standard_normal((150, 8))
+    x[70, :] = 400.0                     # a large entry in page 1 only
+    vals, (codes, scales) = O.store(x, "fp8")
+    assert scales.shape == (3,)
+    assert scales[1] > 50 * scales[0]
+    # the partly filled last page (entries 128..149) is scaled by its own amax
+    assert scales[2] == np.float32(np.float32(np.max(np.abs(x[128:].astype(np.float32)))) / np.float32(448))
+    assert np.allclose(vals, x, rtol=0.07, atol=scales.max() * 2 ** -9)
+
+
+# --------------------------------------------------------------------------- compress
+
+def _rand_rows(n, d):
+    return RNG.standard_normal((n, d))
+
+
+def test_compress_ratio1_is_identity():
+    K, V, Z = _rand_rows(37, 8), _rand_rows(37, 8), _rand_rows(37, 8)
+    kb, vb, ki = O.compress(K, V, Z, 1, P=np.eye(8)[:, :4])
+    assert np.array_equal(kb, K) and np.array_equal(vb, V)
+    assert np.array_equal(ki, K[:, :4])
+
+
+def test_compress_equal_gates_is_mean():
+    K, V = _rand_rows(40, 6), _rand_rows(40, 6)
+    Z = np.full((40, 6), 0.3)
+    kb, vb, _ = O.compress(K, V, Z, 4)
+    np.testing.assert_allclose(kb, K.reshape(10, 4, 6).mean(axis=1), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(vb, V.reshape(10, 4, 6).mean(axis=1), rtol=0, atol=1e-15)
+
+
+def test_compress_dominant_gate_picks_row():
+    K, V = _rand_rows(8, 5), _rand_rows(8, 5)
+    Z = np.zeros((8, 5))
+    Z[2, :] = 800.0      # row 2 of block 0
+    Z[5, 1] = 800.0      # row 1 of block 1, channel 1 only
+    kb, vb, _ = O.compress(K, V, Z, 4)
+    assert np.array_equal(kb[0], K[2]) and np.array_equal(vb[0], V[2])
+    assert kb[1, 1] == K[5, 1]
+    np.testing.assert_allclose(kb[1, [0, 2, 3, 4]], K[4:8][:, [0, 2, 3, 4]].mean(axis=0), atol=1e-15)
+
+
+def test_compress_r2_closed_form():
+    # gate logits (0, ln 3) give weights (1/4, 3/4) on every channel
+    K = np.array([[4.0, -8.0], [8.0, 4.0]])
+    V = np.array([[1.0, 2.0], [3.0, 6.0]])
+    Z = np.array([[0.0, 0.0], [math.log(3.0), math.log(3.0)]])
+    kb, vb, _ = O.compress(K, V, Z, 2)
+    np.testing.assert_allclose(kb, [[7.0, 1.0]], atol=1e-14)
+    np.testing.assert_allclose(vb, [[2.5, 5.0]], atol=1e-14)
+
+
+def test_compress_gate_is_per_channel_and_shared_by_k_and_v():
+    K = np.array([[1.0, 0.0], [0.0, 1.0]])
+    Z = np.array([[0.0, math.log(3.0)], [math.log(3.0), 0.0]])
+    kb, vb, _ = O.compress(K, K * 2.0, Z, 2)
+    np.testing.assert_allclose(kb, [[0.25, 0.25]], atol=1e-15)
+    np.testing.assert_allclose(vb, [[0.5, 0.5]], atol=1e-15)
+
+
+def test_compress_bounds_permutation_linearity_and_tail():
+    K, V, Z = _rand_rows(4 * 9 + 3, 7), _rand_rows(4 * 9 + 3, 7), _rand_rows(4 * 9 + 3, 7) * 2
+    kb, vb, _ = O.compress(K, V, Z, 4)
+    assert kb.shape == (9, 7)                       # trailing 3 rows: no entry
+    blocks = K[:36].reshape(9, 4, 7)
+    assert np.all(kb <= blocks.max(axis=1) + 1e-12) and np.all(kb >= blocks.min(axis=1) - 1e-12)
+    perm = np.concatenate([np.array([2, 0, 3, 1]) + 4 * b for b in range(9)])
+    kb2, vb2, _ = O.compress(K[perm], V[perm], Z[perm], 4)
+    np.testing.assert_allclose(kb2, kb, atol=1e-14)
+    kb3, _, _ = O.compress(3.0 * K - 1.0, V, Z, 4)
+    np.testing.assert_allclose(kb3, 3.0 * kb - 1.0, atol=1e-13)
+
+
+def test_compress_indexer_key_is_right_projection():
+    K, V, Z = _rand_rows(16, 6), _rand_rows(16, 6), _rand_rows(16, 6)
+    P = np.zeros((6, 3))
+    P[4, 0] = 1.0       # output 0 <- channel 4
+    P[1, 2] = -2.0      # output 2 <- -2 * channel 1
+    kb, _, ki = O.compress(K, V, Z, 4, P)
+    np.testing.assert_allclose(ki[:, 0], kb[:, 4], atol=1e-15)
+    np.testing.assert_allclose(ki[:, 1], 0.0)
+    np.testing.assert_allclose(ki[:, 2], -2.0 * kb[:, 1], atol=1e-15)
+
+
+# --------------------------------------------------------------------------- index
+
+def test_index_scores_brute_force():
+    H, DI, N = 3, 5, 17
+    q = RNG.standard_normal((H, DI))
+    w = RNG.uniform(0, 1, H)
+    k = RNG.standard_normal((N, DI))
+    got = O.index_scores(q, w, k)
+    for j in range(N):
+        s = 0.0
+        for h in range(H):
+            dot = 0.0
+            for d in range(DI):
+                dot += q[h][d] * k[j][d]
+            s += w[h] * (dot if dot > 0 else 0.0)
+        assert abs(float(got[j]) - s) <= 1e-6 * max(1.0, abs(s))
+    assert np.all(got >= 0)
+
+
+def test_index_single_head_is_relu_dot_and_homogeneous():
+    q = RNG.standard_normal((1, 8))
+    k = RNG.standard_normal((30, 8))
+    got = O.index_scores(q, np.ones(1), k)
+    np.testing.assert_allclose(got, np.maximum(k @ q[0], 0), rtol=1e-6, atol=1e-7)
+    q4 = RNG.standard_normal((4, 8))
+    w4 = RNG.uniform(0, 1, 4)
+    np.testing.assert_allclose(O.index_scores(q4, 2.5 * w4, k), 2.5 * O.index_scores(q4, w4, k), rtol=1e-6)
+    # a head whose query opposes every key contributes nothing
+    qn = np.vstack([q4[:1], -np.abs(k).sum(axis=0, keepdims=True) * 0 - 1e3 * np.sign(k.mean(axis=0))])
+    k_pos = np.abs(k) * np.sign(k.mean(axis=0))
+    s_two = O.index_scores(qn, np.array([1.0, 7.0]), k_pos)
+    s_one = O.index_scores(qn[:1], np.array([1.0]), k_pos)
+    np.testing.assert_allclose(s_two, s_one, rtol=1e-6)
+
+
+def test_visible_entries():
+    assert [O.visible_entries(t, 4) for t in range(10)] == [0, 0, 0, 1, 1, 1, 1, 2, 2, 2]
+    assert O.visible_entries(4095, 4) == 1024
+    assert O.visible_entries(131072 + 2047, 4) == 32768 + 512
+
+
+# --------------------------------------------------------------------------- top-k
+
+def test_topk_golden(golden_dir):
+    with open(os.path.join(golden_dir, "topk_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = O.topk(np.array(c["scores"], dtype=np.float32), c["k"])
+        assert got.tolist() == c["expect"], c
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (10, 3), (64, 64), (100, 7), (256, 64), (200, 300)])
+def test_topk_brute_force(n, k):
+    for trial in range(5):
+        s = RNG.standard_normal(n).astype(np.float32)
+        s = np.maximum(s, 0)                                  # exact zeros, like ReLU sums
+        s[RNG.integers(0, n, n // 4)] = np.float32(0.5)        # exact ties
+        got = O.topk(s, k)
+        ranked = sorted(range(n), key=lambda j: (-float(s[j]), j))[:k]
+        want = sorted(ranked) + [-1] * max(0, k - n)
+        assert got.tolist() == want
+
+
+# --------------------------------------------------------------------------- attend
+
+def _sdpa(q, k, v, mask=None, causal=False, scale=None):
+    """torch scaled_dot_product_attention in float64 on the CPU, MQA expanded."""
+    H = q.shape[1]
+    Q = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)                 # [1,H,L,D]
+    Kt = torch.from_numpy(k).unsqueeze(0).unsqueeze(0).expand(1, H, -1, -1)
+    Vt = torch.from_numpy(v).unsqueeze(0).unsqueeze(0).expand(1, H, -1, -1)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, attn_mask=m, is_causal=causal, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_ratio1_all_selected_no_window_is_dense_causal_attention():
+    """r = 1 keeps main KV uncompressed (CSA2 'The indexer selects, SWA covers
+    the rest'); selecting every visible entry with no window must then be plain
+    causal attention."""
+    L, H, D, DI = 48, 4, 16, 8
+    K, V, Z = _rand_rows(L, D), _rand_rows(L, D), _rand_rows(L, D)
+    P = RNG.standard_normal((D, DI)) / 4
+    kbar, vbar, kidx = O.compress(K, V, Z, 1, P)
+    Q = RNG.standard_normal((L, H, D))
+    qi = RNG.standard_normal((L, 2, DI))
+    w = RNG.uniform(0, 1, (L, 2))
+    scale = 1 / math.sqrt(D)
+    out = np.zeros((L, H, D))
+    for t in range(L):
+        T, (o,) = O.decode_step(qi[t], w[t], kidx, 1, L, t,
+                                [dict(q=Q[t], W=0, scale=scale, kbar=kbar, vbar=vbar, rawk=K, rawv=V)])
+        assert sorted(T[T >= 0].tolist()) == list(range(t + 1))
+        out[t] = o
+    ref = _sdpa(Q, K, V, causal=True, scale=scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("W,s", [(1, 0), (5, 0), (12, 0), (5, 9)])
+def test_no_selection_is_banded_window_attention(W, s):
+    """k = 0 leaves only the window; 'SWA Bounded Replay' > 'Replay only the
+    window': keys [max(s, i-W+1), i]."""
+    L, H, D = 30, 3, 8
+    K, V = _rand_rows(L, D), _rand_rows(L, D)
+    Q = RNG.standard_normal((L, H, D))
+    scale = 0.7
+    out = np.zeros((L, H, D))
+    for t in range(s, L):
+        out[t] = O.attend_step(Q[t], np.zeros(0, np.int32), t, W, scale, np.zeros((0, D)), np.zeros((0, D)), K, V,
+                               swa_start=s)
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    band = (j <= i) & (j >= np.maximum(s, i - W + 1))
+    band[:s] = np.eye(L, dtype=bool)[:s]          # rows before s are not compared
+    ref = _sdpa(Q, K, V, mask=band, scale=scale)
+    np.testing.assert_allclose(out[s:], ref[s:], rtol=0, atol=1e-12)
+
+
+def test_attend_degenerate_cases():
+    H, D = 4, 8
+    q = RNG.standard_normal((H, D))
+    k1, v1 = RNG.standard_normal((1, D)), RNG.standard_normal((1, D))
+    np.testing.assert_allclose(O.attend(q, k1, v1, 0.3), np.repeat(v1, H, axis=0), atol=1e-15)
+    keys, vals = RNG.standard_normal((9, D)), RNG.standard_normal((9, D))
+    np.testing.assert_allclose(O.attend(np.zeros((H, D)), keys, vals, 0.3),
+                               np.repeat(vals.mean(axis=0, keepdims=True), H, axis=0), atol=1e-14)
+    vals1 = vals.copy()
+    vals1[:, 3] = 1.0
+    np.testing.assert_allclose(O.attend(q, keys, vals1, 0.3)[:, 3], 1.0, atol=1e-14)
+    p = O.softmax_weights(q, keys, 0.3)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert O.attend(q, np.zeros((0, D)), np.zeros((0, D)), 1.0).shape == (H, D)
+
+
+def test_attend_union_keeps_duplicates_and_is_order_free():
+    D, H = 6, 2
+    kbar, vbar = RNG.standard_normal((10, D)), RNG.standard_normal((10, D))
+    K, V = RNG.standard_normal((40, D)), RNG.standard_normal((40, D))
+    q = RNG.standard_normal((H, D))
+    T = np.array([7, 2, 5, -1], dtype=np.int32)
+    got = O.attend_step(q, T, 33, 3, 0.5, kbar, vbar, K, V)
+    keys = np.vstack([kbar[[7, 2, 5]], K[31:34]])
+    vals = np.vstack([vbar[[7, 2, 5]], V[31:34]])
+    np.testing.assert_allclose(got, _sdpa(q[None], keys, vals, scale=0.5)[0], atol=1e-12)
+    got2 = O.attend_step(q, T[[2, 0, 3, 1]], 33, 3, 0.5, kbar, vbar, K, V)
+    np.testing.assert_allclose(got2, got, atol=1e-14)
+    # an entry whose rows also sit in the window is kept in both branches
+    kbar2 = kbar.copy()
+    kbar2[5] = K[32]
+    vbar2 = vbar.copy()
+    vbar2[5] = V[32]
+    got3 = O.attend_step(q, np.array([5], np.int32), 33, 3, 0.5, kbar2, vbar2, K, V)
+    keys3 = np.vstack([K[32:33], K[31:34]])
+    vals3 = np.vstack([V[32:33], V[31:34]])
+    np.testing.assert_allclose(got3, _sdpa(q[None], keys3, vals3, scale=0.5)[0], atol=1e-12)
+
+
+def test_reuse_group_equals_independent_attends():
+    """'Full, Reindex, and Reuse': Reuse layers follow the latest selection."""
+    D, DI, H, E = 8, 4, 2, 40
+    kidx = RNG.standard_normal((E, DI))
+    layers = []
+    for _ in range(3):
+        layers.append(dict(q=RNG.standard_normal((H, D)), W=4, scale=0.4,
+                           kbar=RNG.standard_normal((E, D)), vbar=RNG.standard_normal((E, D)),
+                           rawk=RNG.standard_normal((4 * E, D)), rawv=RNG.standard_normal((4 * E, D))))
+    qi, w = RNG.standard_normal((2, DI)), RNG.uniform(0, 1, 2)
+    T, outs = O.decode_step(qi, w, kidx, 4, 8, 4 * E - 1, layers)
+    for L, o in zip(layers, outs):
+        np.testing.assert_allclose(o, O.attend_step(L["q"], T, 4 * E - 1, 4, 0.4, L["kbar"], L["vbar"],
+                                                    L["rawk"], L["rawv"]), atol=0)
+
+
+# --------------------------------------------------------------------------- accounting
+
+def test_worked_sizes(golden_dir):
+    from compressed_sparse_attention_csa_amd import accounting as A
+    with open(os.path.join(golden_dir, "worked_sizes.json")) as f:
+        g = json.load(f)
+    kv = g["kv_bytes_per_token"]
+    mha = A.kv_cache_bytes_per_token(kv["layers"], kv["heads"], kv["d_head"], kv["bytes"])
+    mqa = A.kv_cache_bytes_per_token(kv["layers"], 1, kv["d_head"], kv["bytes"])
+    gqa = A.kv_cache_bytes_per_token(kv["layers"], kv["gqa_groups"], kv["d_head"], kv["bytes"])
+    # the atlas quotes decimal units
+    assert round(mha / 1e6, 1) == kv["mha_mb"]
+    assert round(mqa / 1e3) == kv["mqa_kb"]
+    assert round(gqa / 1e6, 2) == kv["gqa_mb"]
+    pool = g["candidate_pool"]
+    assert pool["blocks"] * pool["block_positions"] == pool["pool"]
+    assert round(100 * pool["pool"] / pool["context"], 1) == pool["fraction_percent"]
+    assert g["fp4_range"]["e4m3_max"] * g["fp4_range"]["e2m1_max"] == g["fp4_range"]["range"]
+    rp = g["bounded_replay"]
+    assert rp["layers"] * rp["n_win"] == rp["exact_tokens"]
+    gk = g["global_kv_bytes_per_token"]
+    assert gk["value"] * 1e6 / 1e9 == gk["per_1m_tokens_gb"]
+    mla = g["mla_floats"]
+    assert mla["latent"] + mla["rope"] == mla["total"]
+    assert 2 * 128 * 128 == mla["mha_equiv"]
+    # the prefill chunk's visible score count: 2,048 queries over 131,072 prior tokens, r = 4
+    assert A.prefill_visible_scores(131072, 2048, 4) == 67_632_640
+    assert A.index_flops(67_632_640, 4, 64) == 34_627_911_680
+    assert A.attend_flops(2048, 64, 1152, 128) == 77_309_411_328
