@@ -1,0 +1,277 @@
+// csa_compress kernels: gated pooling of r raw rows into one compressed entry,
+// indexer-key projection, and the page write (with per-page FP8 scaling).
+//
+// Method: Model-architectures atlas, compressed-KV entry (every r KV rows
+// folded into one entry with learned compression weights); DeepSeek-V4.1-Flash
+// technical-report walkthrough, "Compressed Sparse Attention 2" > "A simpler
+// compressor" (non-overlapping groups, no absolute positional embedding,
+// indexer K projected from the main-KV entry) and "Causal Encoder-Decoder" >
+// "One hidden state feeds the decoder" (entries C and compression weights Z).
+//
+// One workgroup owns one (sequence, page): it computes the page's new entries
+// in fp32, then writes them. For FP8 pages it also re-quantises the page's
+// earlier entries (kept in fp32 staging) under the page's new amax, so the
+// bytes of a page never depend on how its entries were appended.
+#include "csa_device.h"
+#include "csa_internal.h"
+
+namespace csa {
+
+namespace {
+
+template <int ACT>
+__device__ __forceinline__ float2 load2(const void *base, int64_t elem) {
+  if constexpr (ACT == DT_F32) {
+    return *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + elem);
+  } else {
+    uint32_t w = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(base) + elem);
+    return make_float2(bf16_to_f32(static_cast<uint16_t>(w & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(w >> 16)));
+  }
+}
+
+template <int KV>
+__device__ __forceinline__ void store2(void *base, int64_t elem, float a, float b) {
+  if constexpr (KV == DT_F32) {
+    *reinterpret_cast<float2 *>(reinterpret_cast<float *>(base) + elem) = make_float2(a, b);
+  } else if constexpr (KV == DT_BF16) {
+    uint32_t w = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(base) + elem) = w;
+  }
+}
+
+template <int KV>
+__device__ __forceinline__ void store1(void *base, int64_t elem, float a) {
+  if constexpr (KV == DT_F32) {
+    reinterpret_cast<float *>(base)[elem] = a;
+  } else if constexpr (KV == DT_BF16) {
+    reinterpret_cast<uint16_t *>(base)[elem] = f32_to_bf16(a);
+  }
+}
+
+constexpr int kThreads = 256;
+constexpr int kSlotsPerThread = kPage / (kThreads / 64);   // 16
+
+template <int ACT, int KV>
+__global__ __launch_bounds__(kThreads) void compress_pages_kernel(const CompressArgs a) {
+  __shared__ float kb_s[kPage][kD];
+  __shared__ float red[16];
+
+  // ---- which (sequence, page) this workgroup owns
+  int wg = blockIdx.x, item = 0, acc = 0;
+  for (; item < a.n_items - 1; ++item) {
+    if (wg < acc + a.it[item].n_pages) break;
+    acc += a.it[item].n_pages;
+  }
+  const CompressItem it = a.it[item];
+  const int page = it.page0 + (wg - acc);
+  const int seq = it.seq;
+  const int r = a.r;
+  const int new_len = it.old_len + it.n_new;
+  const int nb_old = it.old_len / r, nb_new = new_len / r;
+  const int pstart = page * kPage;
+  const int e0 = max(pstart, nb_old), e1 = min(pstart + kPage, nb_new);
+  const int filled = e1 - pstart;                     // slots [0, filled) hold entries after this call
+  const int pp = a.block_table[static_cast<int64_t>(seq) * a.bt_stride + page];
+  const bool page_ok = pp >= 0 && pp < a.pool_pages;
+  if (!page_ok && threadIdx.x == 0) flag_error(a.err, ERR_PAGE);
+
+  const int t = threadIdx.x, dp = t & 63, eb = t >> 6;
+  const int d0 = 2 * dp;
+
+  float kk[kSlotsPerThread][2], vv[kSlotsPerThread][2];
+#pragma unroll
+  for (int m = 0; m < kSlotsPerThread; ++m) {
+    const int slot = eb + 4 * m, e = pstart + slot;
+    float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+    if (e >= e0 && e < e1) {
+      // gated pooling over rows [e*r, e*r + r): softmax of the gate per channel
+      float zm0 = -INFINITY, zm1 = -INFINITY;
+      for (int u = 0; u < r; ++u) {
+        const int row = e * r + u;
+        float2 z = row >= it.old_len
+                       ? load2<ACT>(a.gate, static_cast<int64_t>(it.row_off + row - it.old_len) * kD + d0)
+                       : load2<ACT>(a.gate_stage, (static_cast<int64_t>(seq) * r + row % r) * kD + d0);
+        zm0 = fmaxf(zm0, z.x);
+        zm1 = fmaxf(zm1, z.y);
+      }
+      float ws0 = 0.f, ws1 = 0.f;
+      for (int u = 0; u < r; ++u) {
+        const int row = e * r + u;
+        float2 z, kx, vx;
+        if (row >= it.old_len) {
+          const int64_t off = static_cast<int64_t>(it.row_off + row - it.old_len) * kD + d0;
+          z = load2<ACT>(a.gate, off);
+          kx = load2<ACT>(a.raw_k, off);
+          vx = load2<ACT>(a.raw_v, off);
+        } else {
+          z = load2<ACT>(a.gate_stage, (static_cast<int64_t>(seq) * r + row % r) * kD + d0);
+          const int64_t ro = (static_cast<int64_t>(seq) * a.R + row % a.R) * kD + d0;
+          kx = load2<ACT>(a.ring_k, ro);
+          vx = load2<ACT>(a.ring_v, ro);
+        }
+        const float w0 = expf(z.x - zm0), w1 = expf(z.y - zm1);
+        ws0 += w0; ws1 += w1;
+        k0 += w0 * kx.x; k1 += w1 * kx.y;
+        v0 += w0 * vx.x; v1 += w1 * vx.y;
+      }
+      k0 /= ws0; k1 /= ws1; v0 /= ws0; v1 /= ws1;
+    } else if (KV == DT_FP8 && slot < filled && e < e0) {
+      // an entry appended by an earlier call: its fp32 value from staging
+      const int64_t so = (static_cast<int64_t>(seq) * kPage + slot) * kD + d0;
+      const float2 kx = *reinterpret_cast<const float2 *>(a.kbar_stage + so);
+      const float2 vx = *reinterpret_cast<const float2 *>(a.vbar_stage + so);
+      k0 = kx.x; k1 = kx.y; v0 = vx.x; v1 = vx.y;
+    }
+    kk[m][0] = k0; kk[m][1] = k1;
+    vv[m][0] = v0; vv[m][1] = v1;
+    if (a.write_idx) {
+      kb_s[slot][d0] = k0;
+      kb_s[slot][d0 + 1] = k1;
+    }
+  }
+
+  // ---- indexer key: KI = Kbar @ P (fp32, before any rounding); thread owns column c
+  const int c = dp;
+  float ki[kSlotsPerThread];
+#pragma unroll
+  for (int m = 0; m < kSlotsPerThread; ++m) ki[m] = 0.f;
+  if (a.write_idx) {
+    __syncthreads();
+    for (int d = 0; d < kD; ++d) {
+      const float p = a.proj[d * kDI + c];
+#pragma unroll
+      for (int m = 0; m < kSlotsPerThread; ++m) ki[m] += kb_s[eb + 4 * m][d] * p;
+    }
+    if constexpr (KV == DT_FP8) {
+#pragma unroll
+      for (int m = 0; m < kSlotsPerThread; ++m) {
+        const int slot = eb + 4 * m, e = pstart + slot;
+        if (slot < filled && e < e0) ki[m] = a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot) * kDI + c];
+      }
+    }
+  }
+
+  const int64_t kv_page = static_cast<int64_t>(pp) * kPage * kD;
+  const int64_t ki_page = static_cast<int64_t>(pp) * kPage * kDI;
+
+  if constexpr (KV != DT_FP8) {
+    if (!page_ok) return;
+#pragma unroll
+    for (int m = 0; m < kSlotsPerThread; ++m) {
+      const int slot = eb + 4 * m, e = pstart + slot;
+      if (e >= e0 && e < e1) {
+        store2<KV>(a.kbar, kv_page + slot * kD + d0, kk[m][0], kk[m][1]);
+        store2<KV>(a.vbar, kv_page + slot * kD + d0, vv[m][0], vv[m][1]);
+        if (a.write_idx) store1<KV>(a.kidx, ki_page + slot * kDI + c, ki[m]);
+      }
+    }
+  } else {
+    // ---- FP8: one scale per page and stream, amax over the filled slots
+    float ak = 0.f, av = 0.f, ai = 0.f;
+#pragma unroll
+    for (int m = 0; m < kSlotsPerThread; ++m) {
+      if (eb + 4 * m < filled) {
+        ak = fmaxf(ak, fmaxf(fabsf(kk[m][0]), fabsf(kk[m][1])));
+        av = fmaxf(av, fmaxf(fabsf(vv[m][0]), fabsf(vv[m][1])));
+        ai = fmaxf(ai, fabsf(ki[m]));
+      }
+    }
+    ak = block_max(ak, red);
+    av = block_max(av, red + 4);
+    ai = block_max(ai, red + 8);
+    const float sk = ak > 0.f ? ak / 448.0f : 1.0f;
+    const float sv = av > 0.f ? av / 448.0f : 1.0f;
+    const float si = ai > 0.f ? ai / 448.0f : 1.0f;
+    const bool open_after = filled < kPage;
+    if (page_ok) {
+      uint8_t *kp = reinterpret_cast<uint8_t *>(a.kbar) + kv_page;
+      uint8_t *vp = reinterpret_cast<uint8_t *>(a.vbar) + kv_page;
+      uint8_t *ip = reinterpret_cast<uint8_t *>(a.kidx) + ki_page;
+#pragma unroll
+      for (int m = 0; m < kSlotsPerThread; ++m) {
+        const int slot = eb + 4 * m;
+        if (slot < filled) {
+          const uint32_t ck = f32_to_e4m3(kk[m][0] / sk) | (f32_to_e4m3(kk[m][1] / sk) << 8);
+          const uint32_t cv = f32_to_e4m3(vv[m][0] / sv) | (f32_to_e4m3(vv[m][1] / sv) << 8);
+          *reinterpret_cast<uint16_t *>(kp + slot * kD + d0) = static_cast<uint16_t>(ck);
+          *reinterpret_cast<uint16_t *>(vp + slot * kD + d0) = static_cast<uint16_t>(cv);
+          if (a.write_idx) ip[slot * kDI + c] = static_cast<uint8_t>(f32_to_e4m3(ki[m] / si));
+        }
+      }
+      if (threadIdx.x == 0) {
+        a.kbar_scale[pp] = sk;
+        a.vbar_scale[pp] = sv;
+        if (a.write_idx) a.kidx_scale[pp] = si;
+      }
+    }
+    if (open_after) {
+#pragma unroll
+      for (int m = 0; m < kSlotsPerThread; ++m) {
+        const int slot = eb + 4 * m, e = pstart + slot;
+        if (e >= e0 && e < e1) {
+          const int64_t so = (static_cast<int64_t>(seq) * kPage + slot) * kD + d0;
+          *reinterpret_cast<float2 *>(a.kbar_stage + so) = make_float2(kk[m][0], kk[m][1]);
+          *reinterpret_cast<float2 *>(a.vbar_stage + so) = make_float2(vv[m][0], vv[m][1]);
+          if (a.write_idx) a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot) * kDI + c] = ki[m];
+        }
+      }
+    }
+  }
+}
+
+// Copies the newest raw rows into the window ring and the open block's gate
+// logits into gate staging. Runs after the page kernel, which still reads the
+// previous ring/staging contents for a block straddling two calls.
+template <int ACT>
+__global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
+  int wg = blockIdx.x, item = 0, acc = 0;
+  for (; item < a.n_items - 1; ++item) {
+    if (wg < acc + a.chunks[item]) break;
+    acc += a.chunks[item];
+  }
+  const CompressItem it = a.it[item];
+  const int chunk = wg - acc;
+  const int new_len = it.old_len + it.n_new;
+  const int lo = max(it.old_len, new_len - a.R);
+  const int glo = max(it.old_len, (new_len / a.r) * a.r);
+  constexpr int kEsz = ACT == DT_F32 ? 4 : 2;
+  constexpr int kVec = kD * kEsz / 16;                 // 16-byte vectors per row
+  const int row_begin = min(lo, glo) + chunk * a.rows_per_wg;
+  const int row_end = min(new_len, row_begin + a.rows_per_wg);
+  const int n_vec = (row_end - row_begin) * kVec;
+  for (int v = threadIdx.x; v < n_vec; v += blockDim.x) {
+    const int row = row_begin + v / kVec, col = v % kVec;
+    const int64_t src = static_cast<int64_t>(it.row_off + row - it.old_len) * kVec + col;
+    if (row >= lo) {
+      const int64_t dst = (static_cast<int64_t>(it.seq) * a.R + row % a.R) * kVec + col;
+      reinterpret_cast<uint4 *>(a.ring_k)[dst] = reinterpret_cast<const uint4 *>(a.raw_k)[src];
+      reinterpret_cast<uint4 *>(a.ring_v)[dst] = reinterpret_cast<const uint4 *>(a.raw_v)[src];
+    }
+    if (row >= glo) {
+      const int64_t dst = (static_cast<int64_t>(it.seq) * a.r + row % a.r) * kVec + col;
+      reinterpret_cast<uint4 *>(a.gate_stage)[dst] = reinterpret_cast<const uint4 *>(a.gate)[src];
+    }
+  }
+}
+
+}  // namespace
+
+void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s) {
+  if (n_wg <= 0) return;
+  if (kv == DT_F32 && act == DT_F32)
+    hipLaunchKernelGGL((compress_pages_kernel<DT_F32, DT_F32>), dim3(n_wg), dim3(kThreads), 0, s, a);
+  else if (kv == DT_BF16 && act == DT_BF16)
+    hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_BF16>), dim3(n_wg), dim3(kThreads), 0, s, a);
+  else if (kv == DT_FP8 && act == DT_BF16)
+    hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(kThreads), 0, s, a);
+}
+
+void launch_compress_ring(const RingArgs &a, int n_wg, int act, hipStream_t s) {
+  if (n_wg <= 0) return;
+  if (act == DT_F32)
+    hipLaunchKernelGGL((compress_ring_kernel<DT_F32>), dim3(n_wg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((compress_ring_kernel<DT_BF16>), dim3(n_wg), dim3(256), 0, s, a);
+}
+
+}  // namespace csa

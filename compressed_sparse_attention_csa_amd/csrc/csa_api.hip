@@ -1,0 +1,567 @@
+// C ABI of the CSA hot path: handle, host-side validation and launch planning.
+// The kernels live in compress.hip, index.hip and attend.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "csa_device.h"
+#include "csa_internal.h"
+
+using namespace csa;
+
+struct csa_cache {
+  uint64_t magic;
+  csa_config cfg;
+  csa_buffers buf;
+  std::vector<int64_t> len;  // [n_layers][max_seqs] raw rows appended
+  uint32_t *err;             // device error word (workspace head)
+  char *scratch;             // workspace after the head
+  size_t scratch_bytes;
+  bool profiling;
+  std::vector<hipEvent_t> events;  // start/stop pairs
+  size_t events_used;
+};
+
+namespace {
+
+constexpr uint64_t kMagic = 0x4353414d49333535ull;  // "CSAMI355"
+constexpr size_t kHead = 256;
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status s, const char *fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof(msg), fmt, ap);
+  va_end(ap);
+  g_last_error = msg;
+  return s;
+}
+
+bool handle_ok(csa_cache_t h) { return h != nullptr && h->magic == kMagic; }
+
+int dt_bytes(int dt) { return dt == CSA_F32 ? 4 : (dt == CSA_BF16 ? 2 : 1); }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+csa_status check_config(const csa_config *c) {
+  if (!c) return fail(CSA_ERR_INVALID_ARG, "config is NULL");
+  if (c->ratio < 1 || c->ratio > 64) return fail(CSA_ERR_UNSUPPORTED, "ratio %d outside [1, 64]", c->ratio);
+  if (c->head_dim != CSA_HEAD_DIM) return fail(CSA_ERR_UNSUPPORTED, "head_dim %d != %d", c->head_dim, CSA_HEAD_DIM);
+  if (c->idx_dim != CSA_IDX_DIM) return fail(CSA_ERR_UNSUPPORTED, "idx_dim %d != %d", c->idx_dim, CSA_IDX_DIM);
+  if (!(c->q_heads == 16 || c->q_heads == 32 || c->q_heads == 64 || c->q_heads == 128))
+    return fail(CSA_ERR_UNSUPPORTED, "q_heads %d not in {16, 32, 64, 128}", c->q_heads);
+  if (c->idx_heads < 1 || c->idx_heads > CSA_MAX_IDX_HEADS)
+    return fail(CSA_ERR_UNSUPPORTED, "idx_heads %d outside [1, %d]", c->idx_heads, CSA_MAX_IDX_HEADS);
+  if (c->window < 0) return fail(CSA_ERR_SHAPE, "window %d < 0", c->window);
+  if (c->ring_rows < std::max(std::max(c->window, c->ratio), 1))
+    return fail(CSA_ERR_SHAPE, "ring_rows %d < max(window, ratio, 1)", c->ring_rows);
+  if (c->n_layers < 1 || c->n_layers > CSA_MAX_LAYERS)
+    return fail(CSA_ERR_SHAPE, "n_layers %d outside [1, %d]", c->n_layers, CSA_MAX_LAYERS);
+  if (c->max_seqs < 1 || c->max_pages_per_seq < 1 || c->pool_pages < 1)
+    return fail(CSA_ERR_SHAPE, "max_seqs, max_pages_per_seq and pool_pages must be >= 1");
+  if (static_cast<int64_t>(c->max_pages_per_seq) * CSA_PAGE_ENTRIES * c->ratio > (1ll << 30))
+    return fail(CSA_ERR_UNSUPPORTED, "max_pages_per_seq * 64 * ratio exceeds 2^30 raw rows");
+  const bool ok = (c->kv_dtype == CSA_F32 && c->act_dtype == CSA_F32) ||
+                  (c->kv_dtype == CSA_BF16 && c->act_dtype == CSA_BF16) ||
+                  (c->kv_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16);
+  if (!ok) return fail(CSA_ERR_DTYPE, "unsupported (kv_dtype, act_dtype) = (%d, %d)", c->kv_dtype, c->act_dtype);
+  return CSA_OK;
+}
+
+struct Plan {  // workspace needs
+  size_t idx_decode, idx_chunk, attend;
+};
+
+int64_t ecap(const csa_config &c) { return static_cast<int64_t>(c.max_pages_per_seq) * CSA_PAGE_ENTRIES; }
+
+size_t idx_decode_bytes(int nq, int64_t s_stride) {
+  return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) * 2 + align_up(static_cast<size_t>(nq) * kCandCap * 4, 256) * 2 +
+         align_up(static_cast<size_t>(nq) * 4, 256);
+}
+size_t idx_chunk_bytes(int nq, int64_t s_stride, int64_t m_stride) {
+  return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) + align_up(static_cast<size_t>(nq) * m_stride * 4, 256);
+}
+size_t attend_bytes(int nq, int n_splits, int H) {
+  return static_cast<size_t>(nq) * n_splits * H * (kD + 2) * 4;
+}
+
+int n_blocks_for(int k, int W) { return (k + kKeyBlock - 1) / kKeyBlock + (W > 0 ? (W + kKeyBlock - 1) / kKeyBlock : 0); }
+
+bool is_chunk(int n, const int32_t *seq, const int32_t *pos) {
+  if (n < 2) return false;
+  for (int i = 1; i < n; ++i)
+    if (seq[i] != seq[0] || pos[i] != pos[0] + i) return false;
+  return true;
+}
+
+void record(csa_cache_t h, hipStream_t s, bool start) {
+  if (!h->profiling) return;
+  if (start) {
+    if (h->events_used + 2 > h->events.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+      h->events.push_back(a);
+      h->events.push_back(b);
+    }
+    (void)hipEventRecord(h->events[h->events_used], s);
+  } else {
+    (void)hipEventRecord(h->events[h->events_used + 1], s);
+    h->events_used += 2;
+  }
+}
+
+// ------------------------------------------------------------------ debug conversions
+__global__ void debug_convert_kernel(int kind, const void *in, void *out, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (kind == 0) {
+    const uint32_t c = reinterpret_cast<const uint8_t *>(in)[i];
+    reinterpret_cast<float *>(out)[i] = fp8x2_to_f32<false>(c)[0];
+  } else if (kind == 1) {
+    const uint32_t c = reinterpret_cast<const uint8_t *>(in)[i];
+    reinterpret_cast<uint16_t *>(out)[i] = __builtin_bit_cast(uint16_t, fp8x2_to_bf16<false>(c)[0]);
+  } else if (kind == 2) {
+    reinterpret_cast<uint8_t *>(out)[i] = static_cast<uint8_t>(f32_to_e4m3(reinterpret_cast<const float *>(in)[i]));
+  } else {
+    reinterpret_cast<uint16_t *>(out)[i] = f32_to_bf16(reinterpret_cast<const float *>(in)[i]);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *csa_status_string(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID_ARG: return "CSA_ERR_INVALID_ARG";
+    case CSA_ERR_SHAPE: return "CSA_ERR_SHAPE";
+    case CSA_ERR_DTYPE: return "CSA_ERR_DTYPE";
+    case CSA_ERR_CAPACITY: return "CSA_ERR_CAPACITY";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP";
+  }
+  return "CSA_ERR_UNKNOWN";
+}
+
+const char *csa_last_error(void) { return g_last_error.c_str(); }
+
+csa_status csa_buffer_sizes_for(const csa_config *cfg, csa_buffer_sizes *out) {
+  csa_status st = check_config(cfg);
+  if (st != CSA_OK) return st;
+  if (!out) return fail(CSA_ERR_INVALID_ARG, "out is NULL");
+  const size_t P = cfg->pool_pages, S = cfg->max_seqs;
+  const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3;
+  const int kb = dt_bytes(cfg->kv_dtype), ab = dt_bytes(cfg->act_dtype);
+  out->kv_pool = P * kPage * kD * kb;
+  out->idx_pool = P * kPage * kDI * kb;
+  out->page_scale = fp8 ? P * 4 : 0;
+  out->kv_stage = fp8 ? S * kPage * kD * 4 : 0;
+  out->idx_stage = fp8 ? S * kPage * kDI * 4 : 0;
+  out->ring = S * static_cast<size_t>(cfg->ring_rows) * kD * ab;
+  out->gate_stage = S * static_cast<size_t>(cfg->ratio) * kD * ab;
+  out->block_table = S * static_cast<size_t>(cfg->max_pages_per_seq) * 4;
+  return CSA_OK;
+}
+
+size_t csa_workspace_size(const csa_config *cfg, int32_t max_queries, int32_t max_k) {
+  if (check_config(cfg) != CSA_OK || max_queries < 1 || max_k < 0 || max_k > CSA_MAX_TOPK) return 0;
+  const int64_t E = ecap(*cfg);
+  const int64_t s_dec = (E + kIdxChunk - 1) / kIdxChunk * kIdxChunk;
+  const int nq_dec = std::min<int>(max_queries, kIdxMaxQ);
+  const size_t a = idx_decode_bytes(nq_dec, s_dec);
+  const int64_t s_chunk = (E + 63) / 64 * 64;
+  const size_t b = max_queries > 1 ? idx_chunk_bytes(max_queries, s_chunk, s_chunk) : 0;
+  const size_t c = attend_bytes(std::min<int>(max_queries, kAttMaxQ), std::max(1, n_blocks_for(max_k, cfg->window)), cfg->q_heads);
+  return kHead + std::max(a, std::max(b, c)) + 1024;
+}
+
+csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_cache_t *out) {
+  csa_status st = check_config(cfg);
+  if (st != CSA_OK) return st;
+  if (!bufs || !out) return fail(CSA_ERR_INVALID_ARG, "buffers or out is NULL");
+  const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (!bufs->kbar[l] || !bufs->vbar[l] || !bufs->ring_k[l] || !bufs->ring_v[l] || !bufs->gate_stage[l])
+      return fail(CSA_ERR_INVALID_ARG, "layer %d: kbar, vbar, ring_k, ring_v and gate_stage are required", l);
+    if (fp8 && (!bufs->kbar_scale[l] || !bufs->vbar_scale[l] || !bufs->kbar_stage[l] || !bufs->vbar_stage[l]))
+      return fail(CSA_ERR_INVALID_ARG, "layer %d: fp8 caches need scale and staging buffers", l);
+  }
+  if (!bufs->kidx || !bufs->block_table || !bufs->workspace)
+    return fail(CSA_ERR_INVALID_ARG, "kidx, block_table and workspace are required");
+  if (fp8 && (!bufs->kidx_scale || !bufs->kidx_stage))
+    return fail(CSA_ERR_INVALID_ARG, "fp8 caches need kidx_scale and kidx_stage");
+  if (reinterpret_cast<uintptr_t>(bufs->workspace) % 256 != 0) return fail(CSA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (bufs->workspace_bytes < kHead + 1024) return fail(CSA_ERR_CAPACITY, "workspace too small");
+  csa_cache *h = new (std::nothrow) csa_cache();
+  if (!h) return fail(CSA_ERR_INVALID_ARG, "out of host memory");
+  h->magic = kMagic;
+  h->cfg = *cfg;
+  h->buf = *bufs;
+  h->len.assign(static_cast<size_t>(cfg->n_layers) * cfg->max_seqs, 0);
+  h->err = reinterpret_cast<uint32_t *>(bufs->workspace);
+  h->scratch = reinterpret_cast<char *>(bufs->workspace) + kHead;
+  h->scratch_bytes = bufs->workspace_bytes - kHead;
+  h->profiling = false;
+  h->events_used = 0;
+  *out = h;
+  return CSA_OK;
+}
+
+csa_status csa_cache_destroy(csa_cache_t h) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  h->magic = 0;
+  delete h;
+  return CSA_OK;
+}
+
+csa_status csa_seq_reset(csa_cache_t h, int32_t seq) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  if (seq < 0 || seq >= h->cfg.max_seqs) return fail(CSA_ERR_INVALID_ARG, "seq %d out of range", seq);
+  for (int l = 0; l < h->cfg.n_layers; ++l) h->len[static_cast<size_t>(l) * h->cfg.max_seqs + seq] = 0;
+  return CSA_OK;
+}
+
+int64_t csa_seq_len(csa_cache_t h, int32_t layer, int32_t seq) {
+  if (!handle_ok(h) || layer < 0 || layer >= h->cfg.n_layers || seq < 0 || seq >= h->cfg.max_seqs) return -1;
+  return h->len[static_cast<size_t>(layer) * h->cfg.max_seqs + seq];
+}
+
+csa_status csa_seq_set_len(csa_cache_t h, int32_t layer, int32_t seq, int64_t len) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  if (layer < 0 || layer >= h->cfg.n_layers || seq < 0 || seq >= h->cfg.max_seqs)
+    return fail(CSA_ERR_INVALID_ARG, "layer/seq out of range");
+  if (len < 0 || len / h->cfg.ratio > ecap(h->cfg) || len > (1ll << 30))
+    return fail(CSA_ERR_CAPACITY, "length %lld exceeds the block-table row", static_cast<long long>(len));
+  h->len[static_cast<size_t>(layer) * h->cfg.max_seqs + seq] = len;
+  return CSA_OK;
+}
+
+csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *n_new,
+                        const void *raw_k, const void *raw_v, const void *gate, const float *proj_idx,
+                        hipStream_t stream) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  const csa_config &c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(CSA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (n_seqs < 1 || !seq_ids || !n_new) return fail(CSA_ERR_INVALID_ARG, "n_seqs >= 1 with seq_ids and n_new required");
+  if ((layer == 0) != (proj_idx != nullptr))
+    return fail(CSA_ERR_INVALID_ARG, "layer 0 (and only layer 0) must pass proj_idx");
+  int64_t total = 0;
+  std::vector<char> seen(c.max_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (s < 0 || s >= c.max_seqs) return fail(CSA_ERR_INVALID_ARG, "seq_ids[%d] = %d out of range", i, s);
+    if (seen[s]) return fail(CSA_ERR_INVALID_ARG, "seq %d listed twice", s);
+    seen[s] = 1;
+    if (n_new[i] < 0) return fail(CSA_ERR_SHAPE, "n_new[%d] < 0", i);
+    const int64_t nl = h->len[static_cast<size_t>(layer) * c.max_seqs + s] + n_new[i];
+    if (nl > (1ll << 30) || nl / c.ratio > ecap(c))
+      return fail(CSA_ERR_CAPACITY, "seq %d would hold %lld rows, more than its block-table row maps", s, static_cast<long long>(nl));
+    total += n_new[i];
+  }
+  if (total > 0 && (!raw_k || !raw_v || !gate)) return fail(CSA_ERR_INVALID_ARG, "raw_k, raw_v and gate are required");
+  if (total == 0) return CSA_OK;
+  if (total > (1ll << 31) / kD) return fail(CSA_ERR_UNSUPPORTED, "too many rows in one call");
+
+  const bool fp8 = c.kv_dtype == CSA_FP8_E4M3;
+  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
+  CompressArgs base{};
+  base.raw_k = raw_k; base.raw_v = raw_v; base.gate = gate;
+  base.ring_k = h->buf.ring_k[layer]; base.ring_v = h->buf.ring_v[layer]; base.gate_stage = h->buf.gate_stage[layer];
+  base.proj = proj_idx;
+  base.kbar = h->buf.kbar[layer]; base.vbar = h->buf.vbar[layer]; base.kidx = h->buf.kidx;
+  base.kbar_scale = h->buf.kbar_scale[layer]; base.vbar_scale = h->buf.vbar_scale[layer]; base.kidx_scale = h->buf.kidx_scale;
+  base.kbar_stage = h->buf.kbar_stage[layer]; base.vbar_stage = h->buf.vbar_stage[layer]; base.kidx_stage = h->buf.kidx_stage;
+  base.block_table = h->buf.block_table;
+  base.err = h->err;
+  base.r = c.ratio; base.R = c.ring_rows; base.bt_stride = c.max_pages_per_seq; base.pool_pages = c.pool_pages;
+  base.write_idx = proj_idx != nullptr;
+
+  // items in call order; row offsets into the packed input
+  std::vector<CompressItem> items;
+  int64_t off = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    CompressItem it{};
+    it.seq = seq_ids[i];
+    it.old_len = static_cast<int32_t>(h->len[static_cast<size_t>(layer) * c.max_seqs + it.seq]);
+    it.n_new = n_new[i];
+    it.row_off = static_cast<int32_t>(off);
+    off += n_new[i];
+    if (it.n_new > 0) items.push_back(it);
+  }
+
+  RingArgs ring{};
+  ring.raw_k = raw_k; ring.raw_v = raw_v; ring.gate = gate;
+  ring.ring_k = h->buf.ring_k[layer]; ring.ring_v = h->buf.ring_v[layer]; ring.gate_stage = h->buf.gate_stage[layer];
+  ring.r = c.ratio; ring.R = c.ring_rows; ring.rows_per_wg = 64;
+
+  for (size_t g0 = 0; g0 < items.size(); g0 += kCompressMaxItems) {
+    const size_t g1 = std::min(items.size(), g0 + kCompressMaxItems);
+    // page launches: A = first pages holding earlier entries (fp8 only), B = the rest
+    CompressArgs A = base, B = base;
+    A.n_items = B.n_items = 0;
+    int wgA = 0, wgB = 0;
+    for (size_t i = g0; i < g1; ++i) {
+      CompressItem it = items[i];
+      const int nb_old = it.old_len / c.ratio, nb_new = (it.old_len + it.n_new) / c.ratio;
+      if (nb_new <= nb_old) continue;
+      const int p0 = nb_old / kPage, p1 = (nb_new - 1) / kPage;
+      int first = p0;
+      if (fp8 && nb_old % kPage != 0) {
+        CompressItem a = it;
+        a.page0 = p0; a.n_pages = 1;
+        A.it[A.n_items++] = a;
+        wgA += 1;
+        first = p0 + 1;
+      }
+      if (first <= p1) {
+        CompressItem b = it;
+        b.page0 = first; b.n_pages = p1 - first + 1;
+        B.it[B.n_items++] = b;
+        wgB += b.n_pages;
+      }
+    }
+    launch_compress_pages(A, wgA, kv, act, stream);
+    launch_compress_pages(B, wgB, kv, act, stream);
+    // ring / gate staging
+    RingArgs R = ring;
+    R.n_items = 0;
+    int wgR = 0;
+    for (size_t i = g0; i < g1; ++i) {
+      const CompressItem &it = items[i];
+      const int new_len = it.old_len + it.n_new;
+      const int lo = std::max(it.old_len, new_len - c.ring_rows);
+      const int glo = std::max(it.old_len, (new_len / c.ratio) * c.ratio);
+      const int first = std::min(lo, glo);
+      const int rows = new_len - first;
+      if (rows <= 0) continue;
+      R.it[R.n_items] = it;
+      R.chunks[R.n_items] = (rows + R.rows_per_wg - 1) / R.rows_per_wg;
+      wgR += R.chunks[R.n_items];
+      R.n_items++;
+    }
+    launch_compress_ring(R, wgR, act, stream);
+  }
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_compress");
+  for (int i = 0; i < n_seqs; ++i) h->len[static_cast<size_t>(layer) * c.max_seqs + seq_ids[i]] += n_new[i];
+  return CSA_OK;
+}
+
+csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
+                          const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  const csa_config &c = h->cfg;
+  if (n_q < 1 || !q_seq || !q_pos || !q_idx || !w_idx || !topk)
+    return fail(CSA_ERR_INVALID_ARG, "n_q >= 1 and all pointers are required");
+  if (k < 1 || k > CSA_MAX_TOPK) return fail(CSA_ERR_UNSUPPORTED, "k = %d outside [1, %d]", k, CSA_MAX_TOPK);
+  for (int i = 0; i < n_q; ++i) {
+    if (q_seq[i] < 0 || q_seq[i] >= c.max_seqs) return fail(CSA_ERR_INVALID_ARG, "q_seq[%d] out of range", i);
+    const int64_t L = h->len[q_seq[i]];
+    if (q_pos[i] < 0 || q_pos[i] >= L)
+      return fail(CSA_ERR_INVALID_ARG, "q_pos[%d] = %d not below the sequence length %lld", i, q_pos[i], static_cast<long long>(L));
+  }
+  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
+  const int ab = dt_bytes(c.act_dtype);
+
+  if (is_chunk(n_q, q_seq, q_pos)) {
+    const int pos0 = q_pos[0];
+    const int n_min = (pos0 + 1) / c.ratio, n_max = (pos0 + n_q) / c.ratio;
+    int glog2 = 0;
+    while (glog2 < 4 && (n_min >> (glog2 + 1)) >= 2 * k) ++glog2;
+    const int64_t s_stride = (static_cast<int64_t>(n_max) + 63) / 64 * 64;
+    const int64_t m_stride = (s_stride + (1 << glog2) - 1) >> glog2;
+    const size_t need = idx_chunk_bytes(n_q, s_stride, m_stride);
+    if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for a %d-token chunk (%zu > %zu bytes)", n_q, need, h->scratch_bytes);
+    IdxChunkScanArgs s{};
+    s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale;
+    s.bt_row = h->buf.block_table + static_cast<int64_t>(q_seq[0]) * c.max_pages_per_seq;
+    s.q_idx = q_idx; s.w_idx = w_idx;
+    s.S = reinterpret_cast<float *>(h->scratch);
+    s.M = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(n_q) * s_stride * 4, 256));
+    s.err = h->err;
+    s.pool_pages = c.pool_pages; s.h_i = c.idx_heads; s.s_stride = static_cast<int32_t>(s_stride);
+    s.m_stride = static_cast<int32_t>(m_stride); s.n_tok = n_q; s.pos0 = pos0; s.r = c.ratio; s.glog2 = glog2;
+    s.n_etiles = (n_max + 255) / 256;
+    record(h, stream, true);
+    if (n_max > 0) launch_idx_chunk_scan(s, kv, act, stream);
+    record(h, stream, false);
+    IdxChunkSelectArgs sel{};
+    sel.S = s.S; sel.M = s.M; sel.topk = topk; sel.err = h->err;
+    sel.s_stride = s.s_stride; sel.m_stride = s.m_stride; sel.n_tok = n_q; sel.pos0 = pos0; sel.r = c.ratio;
+    sel.glog2 = glog2; sel.k = k;
+    launch_idx_chunk_select(sel, stream);
+  } else {
+    for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
+      const int nq = std::min(kIdxMaxQ, n_q - g0);
+      int nmax = 0;
+      for (int i = 0; i < nq; ++i) nmax = std::max(nmax, (q_pos[g0 + i] + 1) / c.ratio);
+      const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(nmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
+      const size_t need = idx_decode_bytes(nq, s_stride);
+      if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small (%zu > %zu bytes)", need, h->scratch_bytes);
+      char *p = h->scratch;
+      float *S = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
+      float *M = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
+      float *cs = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * kCandCap * 4, 256);
+      int32_t *cj = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(nq) * kCandCap * 4, 256);
+      int32_t *cnt = reinterpret_cast<int32_t *>(p);
+
+      IdxScanArgs s{};
+      s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;
+      s.q_idx = reinterpret_cast<const char *>(q_idx) + static_cast<int64_t>(g0) * c.idx_heads * kDI * ab;
+      s.w_idx = w_idx + static_cast<int64_t>(g0) * c.idx_heads;
+      s.S = S; s.M = M; s.cnt = cnt; s.err = h->err;
+      s.bt_stride = c.max_pages_per_seq; s.pool_pages = c.pool_pages; s.h_i = c.idx_heads;
+      s.s_stride = static_cast<int32_t>(s_stride); s.n_q = nq;
+      IdxFilterArgs f{};
+      f.S = S; f.M = M; f.cand_s = cs; f.cand_j = cj; f.cnt = cnt; f.s_stride = s.s_stride; f.k = k; f.n_q = nq;
+      IdxFinalArgs fin{};
+      fin.S = S; fin.cand_s = cs; fin.cand_j = cj; fin.cnt = cnt; fin.err = h->err;
+      fin.topk = topk + static_cast<int64_t>(g0) * k; fin.s_stride = s.s_stride; fin.k = k; fin.n_q = nq;
+      int wg = 0, slices = 0;
+      for (int i = 0; i < nq; ++i) {
+        const int N = (q_pos[g0 + i] + 1) / c.ratio;
+        int glog2 = 0;
+        while (glog2 < 8 && (((N + (2 << glog2) - 1) >> (glog2 + 1)) >= 4 * k)) ++glog2;
+        if (((N + (1 << glog2) - 1) >> glog2) > kMaxGroups)
+          return fail(CSA_ERR_UNSUPPORTED, "query %d sees %d entries; at most %d are supported for k = %d", g0 + i, N, kMaxGroups << 8, k);
+        s.q[i].seq = q_seq[g0 + i];
+        s.q[i].n_vis = N;
+        s.q[i].chunk0 = wg;
+        s.q[i].glog2 = glog2;
+        wg += (N + kIdxChunk - 1) / kIdxChunk;
+        f.slice0[i] = slices;
+        f.n_vis[i] = N;
+        f.glog2[i] = glog2;
+        slices += N > k ? (N + kFilterSlice - 1) / kFilterSlice : 0;
+        fin.n_vis[i] = N;
+      }
+      f.slice0[nq] = slices;
+      s.total_wg = wg;
+      record(h, stream, true);
+      launch_idx_scan(s, kv, act, stream);
+      record(h, stream, false);
+      launch_idx_filter(f, slices, stream);
+      launch_idx_final(fin, stream);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_topk");
+  return CSA_OK;
+}
+
+csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q,
+                      const int32_t *topk, int32_t k, float scale, void *out, hipStream_t stream) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  const csa_config &c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(CSA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (n_q < 1 || !q_seq || !q_pos || !q || !out) return fail(CSA_ERR_INVALID_ARG, "n_q >= 1 and q_seq, q_pos, q, out required");
+  if (k < 0 || k > CSA_MAX_TOPK) return fail(CSA_ERR_UNSUPPORTED, "k = %d outside [0, %d]", k, CSA_MAX_TOPK);
+  if (k > 0 && !topk) return fail(CSA_ERR_INVALID_ARG, "topk required when k > 0");
+  for (int i = 0; i < n_q; ++i) {
+    if (q_seq[i] < 0 || q_seq[i] >= c.max_seqs) return fail(CSA_ERR_INVALID_ARG, "q_seq[%d] out of range", i);
+    const int64_t L = h->len[static_cast<size_t>(layer) * c.max_seqs + q_seq[i]];
+    if (q_pos[i] < 0 || q_pos[i] >= L)
+      return fail(CSA_ERR_INVALID_ARG, "q_pos[%d] = %d not below the layer's sequence length %lld", i, q_pos[i], static_cast<long long>(L));
+    if (c.window > 0 && (L - 1 - q_pos[i]) > c.ring_rows - c.window)
+      return fail(CSA_ERR_CAPACITY, "query %d: window rows already left the %d-row ring", i, c.ring_rows);
+  }
+  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
+  const int ab = dt_bytes(c.act_dtype);
+  AttendArgs a{};
+  a.kbar = h->buf.kbar[layer]; a.vbar = h->buf.vbar[layer];
+  a.kbar_scale = h->buf.kbar_scale[layer]; a.vbar_scale = h->buf.vbar_scale[layer];
+  a.ring_k = h->buf.ring_k[layer]; a.ring_v = h->buf.ring_v[layer];
+  a.block_table = h->buf.block_table;
+  a.err = h->err;
+  a.scale = scale; a.k = k; a.W = c.window; a.R = c.ring_rows; a.r = c.ratio;
+  a.bt_stride = c.max_pages_per_seq; a.pool_pages = c.pool_pages; a.H = c.q_heads;
+  a.n_sparse_blocks = (k + kKeyBlock - 1) / kKeyBlock;
+  a.n_blocks = n_blocks_for(k, c.window);
+  const size_t qrow = static_cast<size_t>(c.q_heads) * kD * ab;
+
+  if (is_chunk(n_q, q_seq, q_pos)) {
+    a.q = q; a.out = out; a.topk = topk;
+    a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0];
+    a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
+    launch_attend(a, n_q, kv, act, stream);
+  } else {
+    for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {
+      const int nq = std::min(kAttMaxQ, n_q - g0);
+      AttendArgs b = a;
+      b.q = reinterpret_cast<const char *>(q) + g0 * qrow;
+      b.out = reinterpret_cast<char *>(out) + g0 * qrow;
+      b.topk = topk ? topk + static_cast<int64_t>(g0) * k : nullptr;
+      b.chunk = 0; b.n_q = nq;
+      for (int i = 0; i < nq; ++i) { b.qd[i].seq = q_seq[g0 + i]; b.qd[i].pos = q_pos[g0 + i]; }
+      const int want = std::max(1, std::min(b.n_blocks, (1024 + nq - 1) / nq));
+      b.blocks_per_split = std::max(1, (b.n_blocks + want - 1) / want);
+      b.n_splits = std::max(1, (b.n_blocks + b.blocks_per_split - 1) / b.blocks_per_split);
+      if (b.n_splits > 1) {
+        const size_t need = attend_bytes(nq, b.n_splits, c.q_heads);
+        if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for attention partials");
+        b.part = reinterpret_cast<float *>(h->scratch);
+      }
+      launch_attend(b, nq * b.n_splits, kv, act, stream);
+      if (b.n_splits > 1) {
+        MergeArgs m{};
+        m.part = b.part; m.out = b.out; m.n_splits = b.n_splits; m.H = c.q_heads; m.n_q = nq;
+        launch_attend_merge(m, act, stream);
+      }
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_attend");
+  return CSA_OK;
+}
+
+csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags) {
+  if (!handle_ok(h) || !flags) return fail(CSA_ERR_INVALID_ARG, "invalid handle or flags");
+  if (hipStreamSynchronize(stream) != hipSuccess) return fail(CSA_ERR_HIP, "stream synchronize failed");
+  uint32_t v = 0;
+  if (hipMemcpy(&v, h->err, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(CSA_ERR_HIP, "error-word read failed");
+  if (hipMemset(h->err, 0, 4) != hipSuccess) return fail(CSA_ERR_HIP, "error-word clear failed");
+  *flags = v;
+  return CSA_OK;
+}
+
+csa_status csa_profile_begin(csa_cache_t h) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  h->profiling = true;
+  h->events_used = 0;
+  return CSA_OK;
+}
+
+csa_status csa_profile_end(csa_cache_t h, double *total_ms, int32_t *launches) {
+  if (!handle_ok(h) || !total_ms || !launches) return fail(CSA_ERR_INVALID_ARG, "invalid arguments");
+  double tot = 0.0;
+  for (size_t i = 0; i + 1 < h->events_used; i += 2) {
+    if (hipEventSynchronize(h->events[i + 1]) != hipSuccess) return fail(CSA_ERR_HIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, h->events[i], h->events[i + 1]) != hipSuccess) return fail(CSA_ERR_HIP, "elapsed time failed");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = static_cast<int32_t>(h->events_used / 2);
+  h->profiling = false;
+  h->events_used = 0;
+  return CSA_OK;
+}
+
+csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream) {
+  if (kind < 0 || kind > 3 || !in || !out || n < 0) return fail(CSA_ERR_INVALID_ARG, "bad debug conversion arguments");
+  if (n == 0) return CSA_OK;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(debug_convert_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, kind, in, out, n);
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed");
+  return CSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Device-side building blocks shared by the CSA kernels (gfx950, wave64).
+//
+// Number formats: bf16 is stored as uint16 bits; fp8 is OCP E4M3 (e4m3fn:
+// bias 7, no infinities, max 448) stored as uint8 codes with one fp32 scale
+// per 64-entry page.
+//
+// MFMA fragments: every dot-product tile here uses the 16x16 MFMA shapes
+// (bf16 16x16x32, fp32 16x16x4). In both, lane l supplies operand row/column
+// l % 16 and the lanes of quarter g = l / 16 supply one quarter of the
+// contraction slice; the output element (row 4*g + v, column l % 16) lands in
+// accumulator register v of lane l. A contraction is split into "chunks" of 32
+// elements and quarter g of chunk c takes 8 contiguous elements starting at
+// g * (len / 4) + 8 * c of the full vector; since the A and B operands use the
+// same rule, which hardware k-slot a pair lands in does not matter.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// error-word bits (see csa_read_errors)
+enum : uint32_t { ERR_PAGE = 1u, ERR_TOPK = 2u, ERR_FALLBACK = 4u };
+
+__device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------------ fp8 e4m3
+
+// Two fp8 codes (byte pair `hi` of a 32-bit word) -> two fp32 values.
+template <bool HI>
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+}
+
+// Two fp8 codes -> two bf16 values (exact: every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ bf16x2_t fp8x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI);
+}
+
+// fp32 -> E4M3 code, round-to-nearest-even, saturating to +-448. The sign bit
+// is the sign of the input (a negative value that rounds to zero gives 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a < 448.0f)) return sign | 0x7eu;            // also catches NaN / inf
+  if (a < 0.015625f) {                                 // below 2^-6: spacing 2^-9
+    const uint32_t m = static_cast<uint32_t>(rintf(a * 512.0f));  // 0..8 (8 == 2^-6 == code 0x08)
+    return sign | m;
+  }
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;   // -6..8
+  uint32_t mant = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));     // 8..16
+  if (mant == 16u) { mant = 8u; ++e; }
+  return sign | (static_cast<uint32_t>(e + 7) << 3) | (mant - 8u);
+}
+
+// ------------------------------------------------------------------ fragments
+
+// 8 contiguous operand elements of one lane, in the compute type.
+template <typename CT> struct Frag;
+template <> struct Frag<float> { float v[8]; };
+template <> struct Frag<__bf16> { bf16x8_t v; };
+
+__device__ __forceinline__ f32x4_t mma(const Frag<__bf16> &a, const Frag<__bf16> &b, f32x4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma(const Frag<float> &a, const Frag<float> &b, f32x4_t acc) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[u], b.v[u], acc, 0, 0, 0);
+  return acc;
+}
+
+// Load 8 contiguous elements of storage dtype SD from p (element pointer) as compute type CT.
+template <int SD, typename CT> struct LoadFrag;
+
+template <> struct LoadFrag<DT_F32, float> {
+  static __device__ __forceinline__ Frag<float> load(const void *p) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+    float4 a = q[0], b = q[1];
+    Frag<float> f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+};
+template <> struct LoadFrag<DT_BF16, __bf16> {
+  static __device__ __forceinline__ Frag<__bf16> load(const void *p) {
+    Frag<__bf16> f;
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+    return f;
+  }
+};
+template <> struct LoadFrag<DT_FP8, __bf16> {
+  static __device__ __forceinline__ Frag<__bf16> load(const void *p) {
+    uint2 u = *reinterpret_cast<const uint2 *>(p);
+    bf16x2_t a = fp8x2_to_bf16<false>(u.x), b = fp8x2_to_bf16<true>(u.x);
+    bf16x2_t c = fp8x2_to_bf16<false>(u.y), d = fp8x2_to_bf16<true>(u.y);
+    Frag<__bf16> f;
+    f.v = bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return f;
+  }
+};
+
+// Frag from 8 fp32 values (rounded to the compute type).
+__device__ __forceinline__ Frag<float> frag_from_f32(const float *x, Frag<float> *) {
+  Frag<float> f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) f.v[u] = x[u];
+  return f;
+}
+__device__ __forceinline__ Frag<__bf16> frag_from_f32(const float *x, Frag<__bf16> *) {
+  uint32_t w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    w[u] = static_cast<uint32_t>(f32_to_bf16(x[2 * u])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * u + 1])) << 16);
+  Frag<__bf16> f;
+  f.v = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+  return f;
+}
+
+template <typename CT>
+__device__ __forceinline__ Frag<CT> zero_frag() {
+  const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  return frag_from_f32(z, static_cast<Frag<CT> *>(nullptr));
+}
+
+// ------------------------------------------------------------------ element access
+
+template <int SD> struct Elem;
+template <> struct Elem<DT_F32> {
+  static constexpr int bytes = 4;
+  static __device__ __forceinline__ float get(const void *p, int64_t i) { return reinterpret_cast<const float *>(p)[i]; }
+};
+template <> struct Elem<DT_BF16> {
+  static constexpr int bytes = 2;
+  static __device__ __forceinline__ float get(const void *p, int64_t i) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
+  }
+};
+
+// ------------------------------------------------------------------ reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Block-wide max of non-negative values over blockDim.x threads (multiple of 64).
+__device__ __forceinline__ float block_max(float v, float *scratch /* >= 16 floats of LDS */) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+
+}  // namespace csa

@@ -1,0 +1,156 @@
+// Host-side internals shared by the C-ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+constexpr int kPage = CSA_PAGE_ENTRIES;
+constexpr int kD = CSA_HEAD_DIM;
+constexpr int kDI = CSA_IDX_DIM;
+
+// ------------------------------------------------------------------ compress
+
+constexpr int kCompressMaxItems = 64;
+
+struct CompressItem {
+  int32_t seq, old_len, n_new, row_off, page0, n_pages;
+};
+
+struct CompressArgs {
+  const void *raw_k, *raw_v, *gate;               // packed new rows [sum n_new][D]
+  const void *ring_k, *ring_v, *gate_stage;       // this layer's ring [max_seqs][R][D], gate stage [max_seqs][r][D]
+  const float *proj;                              // [D][D_I] or null
+  void *kbar, *vbar, *kidx;                       // pools
+  float *kbar_scale, *vbar_scale, *kidx_scale;    // fp8 page scales
+  float *kbar_stage, *vbar_stage, *kidx_stage;    // fp8 open-page staging
+  const int32_t *block_table;
+  uint32_t *err;
+  int32_t r, R, bt_stride, pool_pages, write_idx, n_items;
+  CompressItem it[kCompressMaxItems];
+};
+
+struct RingArgs {
+  const void *raw_k, *raw_v, *gate;
+  void *ring_k, *ring_v, *gate_stage;
+  int32_t r, R, n_items, rows_per_wg;
+  int32_t chunks[kCompressMaxItems];              // WGs per item
+  CompressItem it[kCompressMaxItems];
+};
+
+void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s);
+void launch_compress_ring(const RingArgs &a, int n_wg, int act, hipStream_t s);
+
+// ------------------------------------------------------------------ index (decode)
+
+constexpr int kIdxMaxQ = 128;        // queries per decode launch group
+constexpr int kIdxChunk = 1024;      // entries per scan workgroup
+constexpr int kFilterSlice = 4096;   // scores per filter workgroup
+constexpr int kCandCap = 8192;       // candidates kept per query
+constexpr int kMaxGroups = 8192;     // group maxima per query (threshold select in LDS)
+
+struct IdxQuery {
+  int32_t seq, n_vis, chunk0, glog2;  // visible entries, first scan-WG index, log2 group size
+};
+
+struct IdxScanArgs {
+  const void *kidx;
+  const float *kidx_scale;
+  const int32_t *block_table;
+  const void *q_idx;   // [n_q][H_I][D_I] (this group's rows)
+  const float *w_idx;  // [n_q][H_I]
+  float *S;            // [n_q][s_stride]
+  float *M;            // [n_q][s_stride]
+  int32_t *cnt;        // [n_q]
+  uint32_t *err;
+  int32_t bt_stride, pool_pages, h_i, s_stride, n_q, total_wg;
+  IdxQuery q[kIdxMaxQ];
+};
+
+struct IdxFilterArgs {
+  const float *S, *M;
+  float *cand_s;       // [n_q][kCandCap]
+  int32_t *cand_j;     // [n_q][kCandCap]
+  int32_t *cnt;
+  int32_t s_stride, k, n_q;
+  int32_t slice0[kIdxMaxQ + 1];   // prefix of filter WGs
+  int32_t n_vis[kIdxMaxQ];
+  int32_t glog2[kIdxMaxQ];
+};
+
+struct IdxFinalArgs {
+  const float *S;
+  const float *cand_s;
+  const int32_t *cand_j;
+  const int32_t *cnt;
+  int32_t *topk;       // [n_q][k]
+  uint32_t *err;
+  int32_t s_stride, k, n_q;
+  int32_t n_vis[kIdxMaxQ];
+};
+
+// chunk (prefill) index: all queries of one sequence at consecutive positions
+struct IdxChunkScanArgs {
+  const void *kidx;
+  const float *kidx_scale;
+  const int32_t *bt_row;   // block-table row of the sequence
+  const void *q_idx;
+  const float *w_idx;
+  float *S, *M;
+  uint32_t *err;
+  int32_t pool_pages, h_i, s_stride, m_stride, n_tok, pos0, r, glog2, n_etiles;
+};
+
+struct IdxChunkSelectArgs {
+  const float *S, *M;
+  int32_t *topk;
+  uint32_t *err;
+  int32_t s_stride, m_stride, n_tok, pos0, r, glog2, k;
+};
+
+void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s);
+void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s);
+void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
+void launch_idx_chunk_scan(const IdxChunkScanArgs &a, int kv, int act, hipStream_t s);
+void launch_idx_chunk_select(const IdxChunkSelectArgs &a, hipStream_t s);
+
+// ------------------------------------------------------------------ attend
+
+constexpr int kAttMaxQ = 128;
+constexpr int kKeyBlock = 64;        // keys per attention block
+
+struct AttQuery {
+  int32_t seq, pos;
+};
+
+struct AttendArgs {
+  const void *q;            // [n_q][H][D]
+  void *out;                // [n_q][H][D]
+  const int32_t *topk;      // [n_q][k]
+  const void *kbar, *vbar;
+  const float *kbar_scale, *vbar_scale;
+  const void *ring_k, *ring_v;
+  const int32_t *block_table;
+  float *part;              // [n_q][n_splits][H][D + 2]
+  uint32_t *err;
+  float scale;
+  int32_t k, W, R, r, bt_stride, pool_pages, H;
+  int32_t n_sparse_blocks, n_blocks, blocks_per_split, n_splits, n_q;
+  int32_t chunk;            // 1: queries are a chunk (seq0, pos0 + i)
+  int32_t seq0, pos0;
+  AttQuery qd[kAttMaxQ];
+};
+
+struct MergeArgs {
+  const float *part;
+  void *out;
+  int32_t n_splits, H, n_q;
+};
+
+void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s);
+void launch_attend_merge(const MergeArgs &a, int act, hipStream_t s);
+
+
+}  // namespace csa

@@ -1,0 +1,549 @@
+// csa_index_topk kernels: lightning-indexer scores over the paged indexer-key
+// cache and an exact per-query Top-K.
+//
+// Method: DeepSeek-V4.1-Flash technical-report walkthrough, "Compressed Sparse
+// Attention 2" > "The indexer selects, SWA covers the rest" (indexer query
+// scores the main-KV entries through their indexer keys; the top entries per
+// query are kept); Model-architectures atlas, trained-sparse-attention entry
+// (a lightning indexer run as MQA, several query heads over one key).
+// Score: s[t][j] = sum_h w[t][h] * max(0, q[t][h] . KI[j]).
+//
+// Decode (one query per sequence):
+//   scan   - one workgroup per 1,024 visible entries of a query. MFMA with the
+//            indexer heads as rows (16x16 tiles, rows >= H_I zero) and 16
+//            entries as columns; writes fp32 scores and the max of every group
+//            of G consecutive scores.
+//   filter - tau = the k-th largest group maximum is a lower bound of the
+//            k-th largest score (the maxima are k distinct scores). Each
+//            workgroup re-derives tau by an LDS radix select and appends the
+//            scores >= tau of its slice to a candidate list.
+//   final  - exact selection among the candidates on 64-bit keys
+//            (score bits, ~index), so ties go to the lower index; bitonic sort
+//            of the chosen indices; -1 padding.
+// Prefill chunk (queries of one sequence at consecutive positions):
+//   chunk scan   - MFMA GEMM tile of 64 queries x 256 entries, with (query,
+//                  head) pairs as the 16 rows of each tile, so every lane's 4
+//                  accumulators are the 4 heads of one (query, entry) score.
+//   chunk select - per query: tau from its group maxima, filter, exact select.
+#include "csa_device.h"
+#include "csa_internal.h"
+
+namespace csa {
+
+namespace {
+
+template <int KV> struct ComputeT { using type = __bf16; };
+template <> struct ComputeT<DT_F32> { using type = float; };
+
+template <int SD> constexpr int elem_bytes() { return SD == DT_F32 ? 4 : (SD == DT_BF16 ? 2 : 1); }
+
+// ------------------------------------------------------------------ block radix select
+
+// Value of the k-th largest (1 <= k <= n) of n uint32 keys produced by get(i).
+template <typename Get>
+__device__ uint32_t kth_largest_u32(Get get, int n, int k, int *hist, int *sh) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63;
+  uint32_t prefix = 0;
+  int rem = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+    for (int i = t; i < 256; i += bd) hist[i] = 0;
+    __syncthreads();
+    for (int i = t; i < n; i += bd) {
+      const uint32_t v = get(i);
+      if ((v & hmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (t < 64) {
+      int c[4], s = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; s += c[j]; }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - s;
+      if (excl < rem && rem <= incl) {
+        int cum = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= rem) { sh[0] = 255 - 4 * lane - j; sh[1] = rem - cum; break; }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(sh[0]) << shift;
+    rem = sh[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Same for 64-bit keys (8 passes).
+template <typename Get>
+__device__ uint64_t kth_largest_u64(Get get, int n, int k, int *hist, int *sh) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63;
+  uint64_t prefix = 0;
+  int rem = k;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+    for (int i = t; i < 256; i += bd) hist[i] = 0;
+    __syncthreads();
+    for (int i = t; i < n; i += bd) {
+      const uint64_t v = get(i);
+      if ((v & hmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (t < 64) {
+      int c[4], s = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; s += c[j]; }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - s;
+      if (excl < rem && rem <= incl) {
+        int cum = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= rem) { sh[0] = 255 - 4 * lane - j; sh[1] = rem - cum; break; }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint64_t>(sh[0]) << shift;
+    rem = sh[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__device__ __forceinline__ uint64_t score_key(float s, int j) {
+  return (static_cast<uint64_t>(__float_as_uint(s)) << 32) | static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(j));
+}
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key & 0xffffffffull));
+}
+
+// Ascending bitonic sort of n (power of two) ints in LDS.
+__device__ void bitonic_sort(int *arr, int n) {
+  const int t = threadIdx.x, bd = blockDim.x;
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < (n >> 1); i += bd) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const int x = arr[lo], y = arr[hi];
+        if ((x > y) == asc) { arr[lo] = y; arr[hi] = x; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+constexpr int kSelCap = 6144;   // candidates held in LDS by the select kernels
+
+// Exact Top-K of one query from `n` candidates given by getters, written
+// ascending into out[0..k) (n >= k). sel is LDS of >= next_pow2(k) ints.
+template <typename GetKey>
+__device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *hist, int *sh, int32_t *out) {
+  const uint64_t kth = kth_largest_u64(key_of, n, k, hist, sh);
+  if (threadIdx.x == 0) sh[2] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint64_t key = key_of(i);
+    if (key >= kth) {
+      const int p = atomicAdd(&sh[2], 1);
+      sel[p] = key_index(key);
+    }
+  }
+  __syncthreads();
+  int np2 = 1;
+  while (np2 < k) np2 <<= 1;
+  for (int i = k + threadIdx.x; i < np2; i += blockDim.x) sel[i] = 0x7fffffff;
+  __syncthreads();
+  bitonic_sort(sel, np2);
+  for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = sel[i];
+}
+
+// ------------------------------------------------------------------ decode scan
+
+template <int ACT, int KV>
+__global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
+  using CT = typename ComputeT<KV>::type;
+  const int wg = blockIdx.x;
+  int qi = 0;
+  for (; qi < a.n_q - 1; ++qi)
+    if (wg < a.q[qi + 1].chunk0) break;
+  const IdxQuery Q = a.q[qi];
+  const int chunk = wg - Q.chunk0;
+  const int N = Q.n_vis;
+  if (chunk == 0 && threadIdx.x == 0) a.cnt[qi] = 0;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
+
+  // A operand: indexer query heads as rows (rows >= H_I are zero)
+  Frag<CT> qa[2];
+  {
+    qa[0] = qa[1] = zero_frag<CT>();
+    if (col < a.h_i) {
+      const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + col) * kDI * AE;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qa[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+    }
+  }
+  float wv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
+
+  const int glog2 = Q.glog2, G = 1 << glog2;
+  float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
+  float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
+  const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
+  const char *kbase = reinterpret_cast<const char *>(a.kidx);
+
+  const int wave_e0 = chunk * kIdxChunk + w * 256;
+  float run = -1.f;
+  for (int pg = 0; pg < 4; ++pg) {
+    const int e_page = wave_e0 + pg * kPage;
+    if (e_page >= N) break;
+    const int pp = bt[e_page >> 6];
+    const bool ok = pp >= 0 && pp < a.pool_pages;
+    if (!ok && lane == 0) flag_error(a.err, ERR_PAGE);
+    const float sc = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
+    Frag<CT> kb[4][2];
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) {
+      const int e = e_page + tl * 16 + col;
+      if (ok && e < N) {
+        const char *row = kbase + (static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI * KE;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) kb[tl][c] = LoadFrag<KV, CT>::load(row + (16 * g + 8 * c) * KE);
+      } else {
+        kb[tl][0] = kb[tl][1] = zero_frag<CT>();
+      }
+    }
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mma(qa[0], kb[tl][0], acc);
+      acc = mma(qa[1], kb[tl][1], acc);
+      const int e_tile = e_page + tl * 16;
+      const int e = e_tile + col;
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
+      s = (e < N && ok) ? s * sc : -1.f;
+      if (g == 0 && e < N) Srow[e] = s;
+      float m = s;
+      if (G <= 16) {
+        for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (g == 0 && (col & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
+      } else {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        run = fmaxf(run, m);
+        const bool last = (((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N);
+        if (last) {
+          if (lane == 0 && e_tile < N) Mrow[e_tile >> glog2] = run;
+          run = -1.f;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode filter
+
+__global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) {
+  __shared__ uint32_t vals[kMaxGroups];
+  __shared__ int hist[256];
+  __shared__ int sh[4];
+  const int wg = blockIdx.x;
+  int qi = 0;
+  for (; qi < a.n_q - 1; ++qi)
+    if (wg < a.slice0[qi + 1]) break;
+  const int slice = wg - a.slice0[qi];
+  const int N = a.n_vis[qi];
+  const int glog2 = a.glog2[qi];
+  const int nG = (N + (1 << glog2) - 1) >> glog2;
+  const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
+  const float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
+
+  float tau = 0.f;
+  if (nG > a.k) {
+    for (int i = threadIdx.x; i < nG; i += blockDim.x) vals[i] = __float_as_uint(Mrow[i]);
+    __syncthreads();
+    const uint32_t b = kth_largest_u32([&](int i) { return vals[i]; }, nG, a.k, hist, sh);
+    tau = __uint_as_float(b);
+  }
+  const int e_begin = slice * kFilterSlice, e_end = min(N, e_begin + kFilterSlice);
+  const int lane = threadIdx.x & 63;
+  int32_t *cnt = a.cnt + qi;
+  for (int e0 = e_begin; e0 < e_end; e0 += blockDim.x) {
+    const int e = e0 + threadIdx.x;
+    const float s = e < e_end ? Srow[e] : -1.f;
+    const bool pass = e < e_end && s >= tau;
+    const uint64_t mask = __ballot(pass);
+    const int n = __popcll(mask);
+    if (n == 0) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(cnt, n);
+    base = __shfl(base, 0, 64);
+    if (pass) {
+      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+      if (pos < kCandCap) {
+        a.cand_s[static_cast<int64_t>(qi) * kCandCap + pos] = s;
+        a.cand_j[static_cast<int64_t>(qi) * kCandCap + pos] = e;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode final
+
+__global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
+  __shared__ uint64_t keys[kSelCap];
+  __shared__ int sel[CSA_MAX_TOPK];
+  __shared__ int hist[256];
+  __shared__ int sh[4];
+  const int qi = blockIdx.x;
+  const int N = a.n_vis[qi], k = a.k;
+  int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
+  if (N <= k) {
+    for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < N ? i : -1;
+    return;
+  }
+  const int c = a.cnt[qi];
+  if (c >= k && c <= kSelCap) {
+    for (int i = threadIdx.x; i < c; i += blockDim.x)
+      keys[i] = score_key(a.cand_s[static_cast<int64_t>(qi) * kCandCap + i], a.cand_j[static_cast<int64_t>(qi) * kCandCap + i]);
+    __syncthreads();
+    select_and_write([&](int i) { return keys[i]; }, c, k, sel, hist, sh, out);
+  } else {
+    // more candidates than LDS holds (heavy ties): exact select straight from the scores
+    if (threadIdx.x == 0) flag_error(a.err, ERR_FALLBACK);
+    const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
+    select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out);
+  }
+}
+
+// ------------------------------------------------------------------ chunk scan (prefill GEMM)
+
+constexpr int kCQ = 64;     // queries per tile
+constexpr int kCE = 256;    // entries per tile
+constexpr int kLdsRow = kDI + 8;
+
+template <int ACT, int KV>
+__global__ __launch_bounds__(256) void idx_chunk_scan_kernel(const IdxChunkScanArgs a) {
+  using CT = typename ComputeT<KV>::type;
+  constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
+  __shared__ CT kt[kCE][kLdsRow];
+  __shared__ float psc[kCE / kPage];
+
+  const int qt = blockIdx.x / a.n_etiles, et = blockIdx.x % a.n_etiles;
+  const int q0 = qt * kCQ, e0 = et * kCE;
+  const int qlast = min(a.n_tok, q0 + kCQ) - 1;
+  const int nvis_max = (a.pos0 + qlast + 1) / a.r;
+  if (e0 >= nvis_max) return;
+
+  // ---- stage the entry tile (4 pages) into LDS in the compute type
+  {
+    constexpr int kChunkElems = 16 / KE;   // elements per 16-byte load
+    constexpr int kChunksPerRow = kDI / kChunkElems;
+    const char *kbase = reinterpret_cast<const char *>(a.kidx);
+    for (int i = threadIdx.x; i < kCE * kChunksPerRow; i += blockDim.x) {
+      const int le = i / kChunksPerRow, ch = i % kChunksPerRow;
+      const int e = e0 + le;
+      const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
+      const bool ok = pp >= 0 && pp < a.pool_pages;
+      CT *dst = &kt[le][ch * kChunkElems];
+      if (ok) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(kbase + ((static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI + ch * kChunkElems) * KE);
+        if constexpr (KV == DT_FP8) {
+          const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x2_t lo = fp8x2_to_bf16<false>(wds[q]), hi = fp8x2_to_bf16<true>(wds[q]);
+            dst[4 * q + 0] = lo[0]; dst[4 * q + 1] = lo[1]; dst[4 * q + 2] = hi[0]; dst[4 * q + 3] = hi[1];
+          }
+        } else {
+          *reinterpret_cast<uint4 *>(dst) = u;
+        }
+      } else {
+        for (int q = 0; q < kChunkElems; ++q) dst[q] = CT(0.f);
+      }
+    }
+    if (threadIdx.x < kCE / kPage) {
+      const int e = e0 + threadIdx.x * kPage;
+      const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
+      const bool ok = pp >= 0 && pp < a.pool_pages;
+      if (e < nvis_max && !ok) flag_error(a.err, ERR_PAGE);
+      psc[threadIdx.x] = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  const int qw = q0 + 16 * w;   // the wave's first query
+
+  // A operands: (query, head) pairs as rows: row = 4*q + h
+  Frag<CT> qa[4][2];
+  float wq[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int qq = qw + 4 * mt + (col >> 2), hh = col & 3;
+    qa[mt][0] = qa[mt][1] = zero_frag<CT>();
+    if (qq < a.n_tok && hh < a.h_i) {
+      const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qq) * a.h_i + hh) * kDI * AE;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qa[mt][c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+    }
+    const int qo = qw + 4 * mt + g;   // the query this lane scores
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wq[mt][v] = (qo < a.n_tok && v < a.h_i) ? a.w_idx[qo * a.h_i + v] : 0.f;
+  }
+
+  const int glog2 = a.glog2, G = 1 << glog2;
+#pragma unroll 1
+  for (int pg = 0; pg < kCE / kPage; ++pg) {
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int le = pg * kPage + nt * 16 + col;
+      Frag<CT> kb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const CT *src = &kt[le][16 * g + 8 * c];
+        if constexpr (KV == DT_F32) {
+          kb[c] = LoadFrag<DT_F32, float>::load(src);
+        } else {
+          kb[c] = LoadFrag<DT_BF16, __bf16>::load(src);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        acc[mt][nt] = mma(qa[mt][0], kb[0], acc[mt][nt]);
+        acc[mt][nt] = mma(qa[mt][1], kb[1], acc[mt][nt]);
+      }
+    }
+    const float sc = psc[pg];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int qo = qw + 4 * mt + g;
+      const int nvis = (a.pos0 + qo + 1) / a.r;
+      float *Srow = a.S + static_cast<int64_t>(qo) * a.s_stride;
+      float *Mrow = a.M + static_cast<int64_t>(qo) * a.m_stride;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int e = e0 + pg * kPage + nt * 16 + col;
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s += wq[mt][v] * fmaxf(acc[mt][nt][v], 0.f);
+        const bool vis = qo < a.n_tok && e < nvis;
+        s = vis ? s * sc : -1.f;
+        if (vis) Srow[e] = s;
+        float m = s;
+        for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (vis && (col & (G - 1)) == 0) Mrow[e >> glog2] = m;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ chunk select
+
+__global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkSelectArgs a) {
+  __shared__ uint64_t keys[kSelCap];
+  __shared__ int sel[CSA_MAX_TOPK];
+  __shared__ int hist[256];
+  __shared__ int sh[4];
+  const int qi = blockIdx.x;
+  const int N = (a.pos0 + qi + 1) / a.r, k = a.k;
+  int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
+  if (N <= k) {
+    for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < N ? i : -1;
+    return;
+  }
+  const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
+  const float *Mrow = a.M + static_cast<int64_t>(qi) * a.m_stride;
+  const int glog2 = a.glog2;
+  const int nG = (N + (1 << glog2) - 1) >> glog2;
+  float tau = 0.f;
+  if (nG > k) {
+    const uint32_t b = kth_largest_u32([&](int i) { return __float_as_uint(Mrow[i]); }, nG, k, hist, sh);
+    tau = __uint_as_float(b);
+  }
+  if (threadIdx.x == 0) sh[3] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    const float s = Srow[e];
+    if (s >= tau) {
+      const int p = atomicAdd(&sh[3], 1);
+      if (p < kSelCap) keys[p] = score_key(s, e);
+    }
+  }
+  __syncthreads();
+  const int c = sh[3];
+  if (c <= kSelCap) {
+    select_and_write([&](int i) { return keys[i]; }, c, k, sel, hist, sh, out);
+  } else {
+    if (threadIdx.x == 0) flag_error(a.err, ERR_FALLBACK);
+    select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out);
+  }
+}
+
+}  // namespace
+
+void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s) {
+  if (a.total_wg <= 0) return;
+  if (kv == DT_F32 && act == DT_F32)
+    hipLaunchKernelGGL((idx_scan_kernel<DT_F32, DT_F32>), dim3(a.total_wg), dim3(256), 0, s, a);
+  else if (kv == DT_BF16 && act == DT_BF16)
+    hipLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(256), 0, s, a);
+  else if (kv == DT_FP8 && act == DT_BF16)
+    hipLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(256), 0, s, a);
+}
+
+void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s) {
+  if (n_wg <= 0) return;
+  hipLaunchKernelGGL(idx_filter_kernel, dim3(n_wg), dim3(256), 0, s, a);
+}
+
+void launch_idx_final(const IdxFinalArgs &a, hipStream_t s) {
+  if (a.n_q <= 0) return;
+  hipLaunchKernelGGL(idx_final_kernel, dim3(a.n_q), dim3(512), 0, s, a);
+}
+
+void launch_idx_chunk_scan(const IdxChunkScanArgs &a, int kv, int act, hipStream_t s) {
+  const int n_qt = (a.n_tok + kCQ - 1) / kCQ;
+  const int n_wg = n_qt * a.n_etiles;
+  if (n_wg <= 0) return;
+  if (kv == DT_F32 && act == DT_F32)
+    hipLaunchKernelGGL((idx_chunk_scan_kernel<DT_F32, DT_F32>), dim3(n_wg), dim3(256), 0, s, a);
+  else if (kv == DT_BF16 && act == DT_BF16)
+    hipLaunchKernelGGL((idx_chunk_scan_kernel<DT_BF16, DT_BF16>), dim3(n_wg), dim3(256), 0, s, a);
+  else if (kv == DT_FP8 && act == DT_BF16)
+    hipLaunchKernelGGL((idx_chunk_scan_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(256), 0, s, a);
+}
+
+void launch_idx_chunk_select(const IdxChunkSelectArgs &a, hipStream_t s) {
+  if (a.n_tok <= 0) return;
+  hipLaunchKernelGGL(idx_chunk_select_kernel, dim3(a.n_tok), dim3(512), 0, s, a);
+}
+
+}  // namespace csa

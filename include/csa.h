@@ -1,0 +1,253 @@
+/*
+ * csa.h - C ABI of the MI355X (gfx950) Compressed Sparse Attention hot path.
+ *
+ * One CSA layer group over one shared, paged, compressed global KV cache:
+ *   csa_compress    gated pooling of every r raw KV rows into one entry,
+ *                   indexer-key projection, quantisation into cache pages;
+ *   csa_index_topk  lightning-indexer scores and the per-query Top-K;
+ *   csa_attend      one softmax over the gathered Top-K entries plus the
+ *                   last W raw rows (sliding window).
+ *
+ * Sources (cited by page title and section):
+ *   [Walkthrough] "DeepSeek-V4.1-Flash technical report" chaptered walkthrough:
+ *       "Compressed Sparse Attention 2" (modes table; "The indexer selects, SWA
+ *       covers the rest"; "A simpler compressor"), "Causal Encoder-Decoder"
+ *       ("One hidden state feeds the decoder"), "SWA Bounded Replay"
+ *       ("Replay only the window").
+ *   [Atlas] "Model architectures" atlas: compressed-KV (CSA/HCA) entry,
+ *       sliding-window entry, MQA/GQA entry, IndexCache entry.
+ *
+ * Conventions
+ * -----------
+ * - Every pointer named "dev" is device memory; every other pointer is host
+ *   memory. The library never allocates device memory: the caller allocates
+ *   every buffer (e.g. torch tensors) and keeps it alive while the handle
+ *   lives. Nothing here synchronises a stream except csa_read_errors().
+ * - All work is enqueued on the caller's stream, in call order. A handle is
+ *   not thread-safe and must be used from one stream at a time.
+ * - Every entry point validates its arguments on the host before enqueuing
+ *   anything. On error it enqueues nothing, leaves the handle unchanged and
+ *   returns a status; csa_last_error() then holds a message. No C++
+ *   exception crosses this boundary.
+ * - Device-side bounds checks (page ids outside the pool, a Top-K index past
+ *   the visible entries) never fault: the offending read or write is skipped
+ *   and a bit is set in the device error word (csa_read_errors).
+ * - Element layouts are row-major and dense unless stated.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_MAX_LAYERS 8      /* layers sharing one handle (one Top-K selection) */
+#define CSA_PAGE_ENTRIES 64   /* compressed entries per cache page */
+#define CSA_HEAD_DIM 128      /* D: the one supported KV head dimension */
+#define CSA_IDX_DIM 64        /* D_I: the one supported indexer key dimension */
+#define CSA_MAX_IDX_HEADS 4   /* H_I <= 4 */
+#define CSA_MAX_TOPK 2048     /* k <= 2048 */
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* null/destroyed handle, bad pointer, bad index */
+  CSA_ERR_SHAPE = 2,       /* sizes inconsistent with the config */
+  CSA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
+  CSA_ERR_CAPACITY = 4,    /* sequence, page, ring or workspace capacity exceeded */
+  CSA_ERR_UNSUPPORTED = 5, /* valid request outside this build's limits */
+  CSA_ERR_HIP = 6          /* a HIP runtime call failed */
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+
+/* Static shape of a layer group's cache.
+ * Supported (kv_dtype, act_dtype): (F32, F32), (BF16, BF16), (FP8_E4M3, BF16). */
+typedef struct csa_config {
+  int32_t ratio;             /* r >= 1: raw rows per compressed entry (1 keeps main KV uncompressed) */
+  int32_t head_dim;          /* D, must be CSA_HEAD_DIM */
+  int32_t q_heads;           /* H_q: query heads sharing the single KV head, multiple of 16, <= 128 */
+  int32_t idx_heads;         /* H_I: indexer query heads, 1..CSA_MAX_IDX_HEADS */
+  int32_t idx_dim;           /* D_I, must be CSA_IDX_DIM */
+  int32_t window;            /* W >= 0: sliding-window length in raw rows (0 disables the branch) */
+  int32_t ring_rows;         /* R: raw rows kept per sequence and layer; >= max(W, r, 1).
+                                A prefill chunk of n tokens needs R >= n + W - 1. */
+  int32_t n_layers;          /* 1..CSA_MAX_LAYERS; layer 0 is the indexing (Full) layer */
+  int32_t max_seqs;          /* sequences addressable through the block table */
+  int32_t max_pages_per_seq; /* block-table row length */
+  int32_t pool_pages;        /* physical pages in every pool */
+  int32_t kv_dtype;          /* csa_dtype of compressed entries and indexer keys */
+  int32_t act_dtype;         /* csa_dtype of raw rows, queries and outputs (F32 or BF16) */
+} csa_config;
+
+/* Device buffers of one handle (all caller-allocated, all "dev").
+ * Pools are indexed by physical page: entry j of sequence b lives at slot
+ * j % 64 of physical page block_table[b * max_pages_per_seq + j / 64].
+ * Per-layer arrays use entries [0, n_layers); unused entries may be NULL.
+ * Scale and staging arrays are used only when kv_dtype == CSA_FP8_E4M3 (else NULL). */
+typedef struct csa_buffers {
+  void *kbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed keys */
+  void *vbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed values */
+  float *kbar_scale[CSA_MAX_LAYERS]; /* [pool_pages] fp32 page scale (fp8) */
+  float *vbar_scale[CSA_MAX_LAYERS];
+  float *kbar_stage[CSA_MAX_LAYERS]; /* [max_seqs][64][D] fp32 values of each sequence's open page (fp8) */
+  float *vbar_stage[CSA_MAX_LAYERS];
+  void *ring_k[CSA_MAX_LAYERS];      /* [max_seqs][R][D] act_dtype: last R raw keys (row i at slot i % R) */
+  void *ring_v[CSA_MAX_LAYERS];      /* [max_seqs][R][D] act_dtype: last R raw values */
+  void *gate_stage[CSA_MAX_LAYERS];  /* [max_seqs][r][D] act_dtype: gate logits of the open r-block */
+  void *kidx;                        /* [pool_pages][64][D_I] kv_dtype: indexer keys (layer 0) */
+  float *kidx_scale;                 /* [pool_pages] fp32 (fp8) */
+  float *kidx_stage;                 /* [max_seqs][64][D_I] fp32 (fp8) */
+  const int32_t *block_table;        /* [max_seqs][max_pages_per_seq] physical page ids */
+  void *workspace;                   /* scratch, >= csa_workspace_size() bytes, 256-byte aligned,
+                                        zero-filled before csa_cache_create */
+  size_t workspace_bytes;
+} csa_buffers;
+
+/* Byte sizes of the buffers above for a config (for the caller's allocator). */
+typedef struct csa_buffer_sizes {
+  size_t kv_pool;      /* each kbar[l] / vbar[l] */
+  size_t idx_pool;     /* kidx */
+  size_t page_scale;   /* each *_scale (0 unless fp8) */
+  size_t kv_stage;     /* each kbar_stage[l] / vbar_stage[l] (0 unless fp8) */
+  size_t idx_stage;    /* kidx_stage (0 unless fp8) */
+  size_t ring;         /* each ring_k[l] / ring_v[l] */
+  size_t gate_stage;   /* each gate_stage[l] */
+  size_t block_table;  /* block_table */
+} csa_buffer_sizes;
+
+typedef struct csa_cache *csa_cache_t;
+
+/* Human-readable name of a status. Never NULL. */
+const char *csa_status_string(csa_status s);
+
+/* Message describing the last failed call on this host thread ("" if none). */
+const char *csa_last_error(void);
+
+/* Fills *out for cfg. Returns CSA_ERR_* if cfg is invalid. */
+csa_status csa_buffer_sizes_for(const csa_config *cfg, csa_buffer_sizes *out);
+
+/* Workspace bytes needed for calls with up to max_queries queries per call
+ * (a prefill chunk counts its tokens) and k <= max_k. 0 if cfg is invalid. */
+size_t csa_workspace_size(const csa_config *cfg, int32_t max_queries, int32_t max_k);
+
+/* Creates a handle over caller-owned buffers. Every sequence starts empty. */
+csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_cache_t *out);
+
+/* Destroys a handle (host memory only; the caller's buffers are untouched). */
+csa_status csa_cache_destroy(csa_cache_t h);
+
+/* Marks sequence `seq` empty in every layer (host bookkeeping only). */
+csa_status csa_seq_reset(csa_cache_t h, int32_t seq);
+
+/* Raw rows appended so far to (layer, seq); -1 on bad arguments. */
+int64_t csa_seq_len(csa_cache_t h, int32_t layer, int32_t seq);
+
+/* Restores the length of (layer, seq) after the caller restored its buffer
+ * contents (checkpoint / resume). len must fit the sequence's block table. */
+csa_status csa_seq_set_len(csa_cache_t h, int32_t layer, int32_t seq, int64_t len);
+
+/*
+ * csa_compress - append raw rows to sequences of one layer and build the
+ * compressed entries of every r-block they complete.
+ * [Atlas] compressed-KV entry (every r KV rows squeezed into one entry with
+ * learned compression weights); [Walkthrough] "A simpler compressor" (no
+ * overlap between groups, no positional embedding, indexer K projected from
+ * the main-KV entry) and "One hidden state feeds the decoder" (entries and
+ * compression weights are projections of one hidden state).
+ *
+ * For block j (rows [j*r, (j+1)*r)) and channel d: w_i = softmax_i(Z[i][d]),
+ * Kbar[j][d] = sum_i w_i K[i][d], Vbar likewise with the same w,
+ * KI[j] = Kbar[j] @ proj_idx (before rounding). Entries are rounded to
+ * kv_dtype; with FP8 each page of each stream carries one fp32 scale
+ * amax/448 over its filled entries, and a page that gains entries is
+ * re-quantised whole from fp32 staging, so incremental appends produce the
+ * same bytes as one bulk call.
+ *
+ *   layer       0..n_layers-1. Layer 0 must pass proj_idx (it writes the
+ *               indexer keys); other layers must pass NULL.
+ *   n_seqs      number of sequences appended to (>= 1); seq_ids (host) are distinct.
+ *   n_new       (host) rows appended per sequence, >= 0.
+ *   raw_k, raw_v, gate (dev) [sum(n_new)][D] act_dtype, sequences packed in
+ *               seq_ids order.
+ *   proj_idx    (dev) [D][D_I] fp32, or NULL.
+ * The block table must map every page the new entries land on.
+ * Errors: CSA_ERR_CAPACITY if a sequence would outgrow its block-table row.
+ */
+csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                        const int32_t *n_new, const void *raw_k, const void *raw_v, const void *gate,
+                        const float *proj_idx, hipStream_t stream);
+
+/*
+ * csa_index_topk - lightning-indexer scores and per-query Top-K over the
+ * entries each query may see. [Walkthrough] CSA2 "The indexer selects, SWA
+ * covers the rest" (indexer query against indexer key, top entries per
+ * query); [Atlas] trained-sparse-attention entry (lightning indexer run as
+ * MQA, several indexer heads over one shared key).
+ *
+ *   s[t][j] = sum_h w[t][h] * max(0, q_idx[t][h] . KI[j]), for the entries
+ *   visible to a query at raw position t: (j+1)*r <= t+1.
+ *   topk[t] = the k visible j with the largest s (ties -> lower j), ascending;
+ *   -1 pads the row when fewer than k entries are visible.
+ *
+ *   n_q         queries (>= 1). q_seq, q_pos (host) [n_q]: sequence and raw
+ *               position of each query; q_pos < csa_seq_len(h, 0, q_seq).
+ *               When all queries share one sequence at consecutive positions
+ *               (a prefill chunk), the chunk kernels run.
+ *   q_idx       (dev) [n_q][H_I][D_I] act_dtype.   w_idx (dev) [n_q][H_I] fp32, >= 0.
+ *   k           1..CSA_MAX_TOPK.   topk (dev) [n_q][k] int32 output.
+ */
+csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                          const void *q_idx, const float *w_idx, int32_t k, int32_t *topk,
+                          hipStream_t stream);
+
+/*
+ * csa_attend - one layer's attention for n_q queries: one softmax over the
+ * gathered Top-K entries of that layer's compressed cache plus the raw rows
+ * [max(0, t-W+1), t] of its window ring. [Walkthrough] CSA2 "The indexer
+ * selects, SWA covers the rest"; "SWA Bounded Replay" > "Replay only the
+ * window" (window rule); [Atlas] MQA/GQA entry (all query heads share the one
+ * KV head). Reuse-mode layers call this with the Top-K rows produced for the
+ * indexing layer ([Walkthrough] CSA2 "Full, Reindex, and Reuse").
+ *
+ *   out[t][h] = sum_key p * v,  p = softmax over keys of scale * q[t][h] . key
+ *   keys = {Kbar[j] : j in topk[t], j >= 0} u {K[i] : max(0,t-W+1) <= i <= t}
+ *   (no de-duplication between the two branches; entries with fp8 storage
+ *   are dequantised with their page scales).
+ *
+ *   layer       0..n_layers-1.  q_seq, q_pos (host) [n_q] as for csa_index_topk,
+ *               q_pos < csa_seq_len(h, layer, q_seq).
+ *   q           (dev) [n_q][H_q][D] act_dtype.   topk (dev) [n_q][k] int32, k >= 0.
+ *   scale       logit scale (1/sqrt(D) in the method).
+ *   out         (dev) [n_q][H_q][D] act_dtype.
+ */
+csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
+                      const int32_t *q_pos, const void *q, const int32_t *topk, int32_t k, float scale,
+                      void *out, hipStream_t stream);
+
+/* Synchronises `stream`, returns the device error word in *flags (bit 0: a
+ * page id outside the pool was met; bit 1: a Top-K index outside the visible
+ * range was met; bit 2: an internal capacity fallback ran) and clears it. */
+csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags);
+
+/* Timing of the indexer scan kernel (the dominant kernel of a decode step):
+ * after csa_profile_begin, every csa_index_topk call records a HIP event pair
+ * around its scan launch on the call's stream; csa_profile_end synchronises
+ * and returns the summed elapsed milliseconds and the number of launches. */
+csa_status csa_profile_begin(csa_cache_t h);
+csa_status csa_profile_end(csa_cache_t h, double *total_ms, int32_t *launches);
+
+/* Runs the device number-format routines on n values (tests of the codecs):
+ * kind 0: fp8 e4m3 codes (uint8) -> fp32 as the attention/indexer kernels decode them;
+ * kind 1: fp8 e4m3 codes (uint8) -> bf16 bits (uint16) as the MFMA operands are built;
+ * kind 2: fp32 -> fp8 e4m3 codes (uint8) as the compressor encodes (RNE, saturating);
+ * kind 3: fp32 -> bf16 bits (RNE). in/out are device pointers. */
+csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

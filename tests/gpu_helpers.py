@@ -1,0 +1,150 @@
+"""Shared helpers for the GPU parity tests: build caches from seeded inputs,
+write oracle-made cache contents into device pools, and compare results.
+
+The oracle side only ever sees values generated here or computed by the
+oracle itself; nothing read back from the GPU is fed to it.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from compressed_sparse_attention_csa_amd import binding as B
+from compressed_sparse_attention_csa_amd import synth as Sy
+from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+from oracle import csa_oracle as O
+
+TORCH_ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 2e-3, "bf16": 2e-2}
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a CPU/GPU tensor's values."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def shuffled_block_table(seed: int, max_seqs: int, max_pages: int, pool_pages: int, device="cuda") -> torch.Tensor:
+    perm = Sy.permutation(seed, pool_pages, salt=7)
+    assert pool_pages >= max_seqs * max_pages
+    bt = torch.tensor(perm[: max_seqs * max_pages], dtype=torch.int32).view(max_seqs, max_pages)
+    return bt.to(device)
+
+
+def make_cache(seed=0, **kw) -> CsaCache:
+    spec = CacheSpec(**kw)
+    bt = shuffled_block_table(seed, spec.max_seqs, spec.max_pages_per_seq, spec.pool_pages)
+    return CsaCache(spec, "cuda", block_table=bt)
+
+
+def raw_rows(seed, kind, layer, seq, row0, n, act, device="cpu"):
+    return Sy.normal_rows(seed, Sy.stream_id(kind, layer, seq), row0, n, 128, device=device, dtype=TORCH_ACT[act])
+
+
+# --------------------------------------------------------------------------- writing oracle contents
+
+def store_raw_to_torch(raw, dtype: str):
+    """Oracle cache payload -> torch tensor of the pool's element type (CPU)."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(raw))
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16)
+    codes, _ = raw
+    return torch.from_numpy(np.ascontiguousarray(codes))
+
+
+def write_logical(cache: CsaCache, pool: torch.Tensor, seq: int, values: torch.Tensor):
+    """Write logical entries [0, E) of `seq` into their physical pages."""
+    E = values.shape[0]
+    if E == 0:
+        return
+    n_pages = (E + 63) // 64
+    padded = torch.zeros((n_pages * 64, *values.shape[1:]), dtype=values.dtype)
+    padded[:E] = values
+    pages = cache.block_table[seq, :n_pages].long()
+    pool[pages] = padded.view(n_pages, 64, *values.shape[1:]).to(pool.device)
+
+
+def write_scales(cache: CsaCache, scales_t: torch.Tensor, seq: int, scales: np.ndarray):
+    n = scales.shape[0]
+    if n == 0:
+        return
+    pages = cache.block_table[seq, :n].long()
+    scales_t[pages] = torch.from_numpy(scales.astype(np.float32)).to(scales_t.device)
+
+
+def fill_index_keys(cache: CsaCache, seed: int, seq: int, n_entries: int):
+    """Seeded indexer keys for `seq`, stored through the oracle's codec. Returns decoded float64 values."""
+    x = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_KI, 0, seq), 0, n_entries, 64).double().numpy()
+    dt = cache.spec.kv_dtype
+    vals, raw = O.store(x, dt)
+    write_logical(cache, cache.kidx, seq, store_raw_to_torch(raw, dt))
+    if dt == "fp8":
+        write_scales(cache, cache.kidx_scale, seq, raw[1])
+    return vals
+
+
+def fill_main_kv(cache: CsaCache, seed: int, layer: int, seq: int, n_entries: int):
+    """Seeded compressed K/V for (layer, seq) stored through the oracle's codec."""
+    dt = cache.spec.kv_dtype
+    out = []
+    for kind, pool, scales in ((Sy.KIND_KBAR, cache.kbar[layer], cache.kbar_scale), (Sy.KIND_VBAR, cache.vbar[layer], cache.vbar_scale)):
+        x = Sy.normal_rows(seed, Sy.stream_id(kind, layer, seq), 0, n_entries, 128).double().numpy()
+        vals, raw = O.store(x, dt)
+        write_logical(cache, pool, seq, store_raw_to_torch(raw, dt))
+        if dt == "fp8":
+            write_scales(cache, scales[layer], seq, raw[1])
+        out.append(vals)
+    return out
+
+
+def fill_ring(cache: CsaCache, seed: int, layer: int, seq: int, length: int):
+    """Raw K/V rows of (layer, seq) for positions [length - R, length) into the ring.
+    Returns float64 (K, V) for rows [0, length) — rows older than the ring are
+    returned too (the oracle may index them; the GPU must not need them)."""
+    act = cache.spec.act_dtype
+    R = cache.cfg.ring_rows
+    K = raw_rows(seed, Sy.KIND_K, layer, seq, 0, length, act)
+    V = raw_rows(seed, Sy.KIND_V, layer, seq, 0, length, act)
+    lo = max(0, length - R)
+    rows = torch.arange(lo, length)
+    cache.ring_k[layer][seq, rows % R] = K[lo:].to(cache.device)
+    cache.ring_v[layer][seq, rows % R] = V[lo:].to(cache.device)
+    return to64(K), to64(V)
+
+
+# --------------------------------------------------------------------------- comparisons
+
+def topk_matches(gpu_T: np.ndarray, oracle_T: np.ndarray, oracle_scores: np.ndarray, rel=1e-6):
+    """Index sets equal, except entries whose oracle score is within `rel` of the
+    oracle's k-th score (near-ties that fp32 accumulation order may swap).
+    Returns (ok, message)."""
+    g = [int(x) for x in gpu_T if x >= 0]
+    o = [int(x) for x in oracle_T if x >= 0]
+    if len(g) != len(o):
+        return False, f"count {len(g)} != {len(o)}"
+    if list(gpu_T) != sorted(g) + [-1] * (len(gpu_T) - len(g)):
+        return False, "gpu row not ascending / badly padded"
+    diff = set(g) ^ set(o)
+    if not diff:
+        return True, ""
+    kth = min(float(oracle_scores[j]) for j in o)
+    bad = [j for j in diff if abs(float(oracle_scores[j]) - kth) > rel * max(abs(kth), 1e-30)]
+    if bad:
+        return False, f"{len(diff)} differing, {len(bad)} outside the tie band, e.g. {bad[:5]} (kth={kth})"
+    return True, f"{len(diff)} near-tie swaps"
+
+
+def max_abs(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def e4m3_ulp(x: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(e, -5) - 4)

