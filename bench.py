@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA decode step on one MI355X.
+
+Workload (batch-4 long-context decode): 4 sequences of 1,048,576 raw tokens,
+r = 4 gated pooling -> 262,144 compressed entries per sequence, fp8 (E4M3)
+compressed cache with one fp32 scale per 64-entry page, 64 query heads of dim
+128 over one KV head, 4 indexer heads of dim 64, Top-1024, a 128-token
+window, and one indexer pass whose Top-K is reused by a group of 4 layers that
+each keep their own compressed K/V. A step is one csa_index_topk over the 4
+queries plus 4 csa_attend calls (one per layer). Inputs are seeded synthetic
+data resident in HBM before timing; steps rotate over 8 identical cache
+replicas so the 256 MB last-level cache cannot hold a step's working set.
+
+The timed steps are replays of one HIP graph per replica (the step's kernels
+captured once). Prints one JSON line: decode tokens/s, the indexer scan
+kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events around
+every scan launch of an eager pass over the same steps), and the CPU
+oracle's throughput on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA decode tokens/s/GPU at 1M ctx + achieved HBM GB/s vs peak; prefill MFMA util"
+HBM_PEAK_GBPS = 8000.0
+
+# the workload
+BATCH, CONTEXT, RATIO, TOPK, WINDOW, HEADS, IDX_HEADS, LAYERS = 4, 1 << 20, 4, 1024, 128, 64, 4, 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample budget")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 512 MiB device copy after timing (reference kernel for HBM counters)")
+    return ap.parse_args()
+
+
+def build_cache(seed, replicas, dev):
+    import torch
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+
+    entries = CONTEXT // RATIO
+    pages = entries // 64
+    spec = CacheSpec(ratio=RATIO, q_heads=HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW,
+                     n_layers=LAYERS, max_seqs=BATCH, max_pages_per_seq=pages, pool_pages=BATCH * pages,
+                     kv_dtype="fp8", act_dtype="bf16", max_queries=BATCH, max_k=TOPK)
+    perm = torch.tensor(Sy.permutation(seed, BATCH * pages, salt=3), dtype=torch.int32)
+    bt = perm.view(BATCH, pages).to(dev)
+    base = CsaCache(spec, dev, block_table=bt)
+    P = Sy.proj_matrix(seed, 128, 64, device=dev)
+    chunk = 1 << 18
+    for layer in range(LAYERS):
+        for b in range(BATCH):
+            for r0 in range(0, CONTEXT, chunk):
+                K = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_K, layer, b), r0, chunk, 128, dev, torch.bfloat16)
+                V = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_V, layer, b), r0, chunk, 128, dev, torch.bfloat16)
+                Z = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Z, layer, b), r0, chunk, 128, dev, torch.bfloat16)
+                base.compress(layer, [b], [chunk], K, V, Z, P if layer == 0 else None)
+    torch.cuda.synchronize()
+    flags = base.read_errors()
+    if flags:
+        raise RuntimeError(f"cache build raised device error flags {flags}")
+    caches = [base]
+    for _ in range(1, replicas):
+        c = CsaCache(spec, dev, block_table=bt)
+        for src, dst in ((base.kbar, c.kbar), (base.vbar, c.vbar), (base.kbar_scale, c.kbar_scale),
+                         (base.vbar_scale, c.vbar_scale), (base.ring_k, c.ring_k), (base.ring_v, c.ring_v),
+                         (base.kbar_stage, c.kbar_stage), (base.vbar_stage, c.vbar_stage),
+                         (base.gate_stage, c.gate_stage)):
+            for s_, d_ in zip(src, dst):
+                d_.copy_(s_)
+        c.kidx.copy_(base.kidx)
+        c.kidx_scale.copy_(base.kidx_scale)
+        c.kidx_stage.copy_(base.kidx_stage)
+        for layer in range(LAYERS):
+            for b in range(BATCH):
+                B.csa_seq_set_len(c.handle, layer, b, CONTEXT)
+        caches.append(c)
+    torch.cuda.synchronize()
+    return caches
+
+
+def scan_bytes_per_launch():
+    from compressed_sparse_attention_csa_amd import accounting as A
+    per_q = A.index_scan_bytes(CONTEXT // RATIO, 64, "fp8") + IDX_HEADS * 64 * 2 + IDX_HEADS * 4
+    return BATCH * per_q
+
+
+def step_bytes():
+    from compressed_sparse_attention_csa_amd import accounting as A
+    return A.decode_step_bytes(BATCH, CONTEXT // RATIO, 128, 64, HEADS, IDX_HEADS, TOPK, WINDOW, LAYERS, "fp8", "bf16")
+
+
+def traffic_from_profiles():
+    """HBM bytes per scan launch from the committed counter summary, if it was
+    taken on the current scan kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "index_scan_1m_decode_traffic.json")
+    src = os.path.join(ROOT, "compressed_sparse_attention_csa_amd", "csrc", "index.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("source_sha256") != h:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(seed, budget_s):
+    """The oracle, as it stands, on one query of the step at a time: indexer
+    scores over 262,144 fp8-decoded indexer keys, Top-1024, and 4 layer attends
+    (64 heads over 1,024 gathered entries + 128 window rows)."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import csa_oracle as O
+
+    rng = np.random.default_rng(seed)
+    E = CONTEXT // RATIO
+    kidx, _ = O.store(rng.standard_normal((E, 64)) * 0.5, "fp8")
+    layers = []
+    for _ in range(LAYERS):
+        # compressed K/V rows: only gathered rows are touched, a 65,536-entry pool indexed modulo stands in
+        pool_k, _ = O.store(rng.standard_normal((65536, 128)) * 0.5, "fp8")
+        pool_v, _ = O.store(rng.standard_normal((65536, 128)) * 0.5, "fp8")
+        layers.append((pool_k, pool_v, rng.standard_normal((WINDOW, 128)), rng.standard_normal((WINDOW, 128))))
+    scale = 1 / math.sqrt(128)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        qi = rng.standard_normal((IDX_HEADS, 64))
+        w = rng.uniform(0, 1, IDX_HEADS)
+        s = O.index_scores(qi, w, kidx)
+        T = O.topk(s, TOPK)
+        for pk, pv, rk, rv in layers:
+            q = rng.standard_normal((HEADS, 128))
+            ent = T[T >= 0] % pk.shape[0]
+            keys = np.concatenate([pk[ent], rk], axis=0)
+            vals = np.concatenate([pv[ent], rv], axis=0)
+            O.attend(q, keys, vals, scale)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and n >= 3:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} single-query steps of the workload (index over {E:,} fp8 indexer keys, Top-{TOPK}, "
+                      f"{LAYERS} attends of {HEADS} heads over {TOPK}+{WINDOW} keys) in {el:.1f} s, float64 NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd import synth as Sy
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+    t_build = time.time()
+    caches = build_cache(args.seed, args.replicas, dev)
+    print(f"[bench] cache built: {len(caches)} replicas in {time.time() - t_build:.1f} s", file=sys.stderr, flush=True)
+
+    # per-step inputs, resident in HBM
+    q_seq = list(range(BATCH))
+    q_pos = [CONTEXT - 1] * BATCH
+    qi = Sy.normal_rows(args.seed, Sy.stream_id(Sy.KIND_QI), 0, BATCH * IDX_HEADS, 64, dev, torch.bfloat16).view(BATCH, IDX_HEADS, 64)
+    w = Sy.uniform_rows(args.seed, Sy.stream_id(Sy.KIND_W), 0, BATCH, IDX_HEADS, dev)
+    qs = [Sy.normal_rows(args.seed, Sy.stream_id(Sy.KIND_Q, l), 0, BATCH * HEADS, 128, dev, torch.bfloat16).view(BATCH, HEADS, 128)
+          for l in range(LAYERS)]
+    topk = [torch.empty((BATCH, TOPK), dtype=torch.int32, device=dev) for _ in caches]
+    outs = [torch.empty((BATCH, HEADS, 128), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
+    scale = 1.0 / math.sqrt(128)
+    def step(i):
+        c = caches[i % len(caches)]
+        T = topk[i % len(caches)]
+        stream = torch.cuda.current_stream()
+        B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, TOPK, T, stream)
+        for l in range(LAYERS):
+            B.csa_attend(c.handle, l, q_seq, q_pos, qs[l], T, TOPK, scale, outs[l], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # one HIP graph per replica: the step's kernels are launched by replay, so
+    # host-side launch cost does not enter the timed region
+    graphs = []
+    cap = torch.cuda.Stream()
+    for r in range(len(caches)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            c = caches[r]
+            s_ = torch.cuda.current_stream()
+            B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, TOPK, topk[r], s_)
+            for l in range(LAYERS):
+                B.csa_attend(c.handle, l, q_seq, q_pos, qs[l], topk[r], TOPK, scale, outs[l], s_)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # kernel timing: eager steps with a HIP event pair around every scan launch
+    for c in caches:
+        B.csa_profile_begin(c.handle)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    scan_ms, launches = 0.0, 0
+    for c in caches:
+        ms, n = B.csa_profile_end(c.handle)
+        scan_ms += ms
+        launches += n
+    flags = max(c.read_errors() for c in caches)
+    if flags:
+        raise RuntimeError(f"device error flags {flags}")
+
+    if args.calib_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = BATCH * args.steps / elapsed
+    scan_avg_ms = scan_ms / max(1, launches)
+    sb = scan_bytes_per_launch()
+    achieved = sb / (scan_avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode, batch 4, 1,048,576-token context, fp8 cache (fp32 scale per 64-entry page), "
+                               "r=4, Top-1024, W=128, 64 query heads, 4-layer index reuse",
+                   "batch": BATCH, "context": CONTEXT, "ratio": RATIO, "k": TOPK, "window": WINDOW,
+                   "q_heads": HEADS, "idx_heads": IDX_HEADS, "group_layers": LAYERS, "kv_dtype": "fp8_e4m3",
+                   "replicas": len(caches), "parallelism": "none (1 GPU)"},
+        "step_hbm_gbps": round(step_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_bytes": step_bytes(),
+        "roofline": {"bound": "hbm", "kernel": "idx_scan (indexer scores over the fp8 indexer-key pages)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(),
+                     "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

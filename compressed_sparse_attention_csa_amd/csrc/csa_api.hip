@@ -30,7 +30,7 @@ struct csa_cache {
 namespace {
 
 constexpr uint64_t kMagic = 0x4353414d49333535ull;  // "CSAMI355"
-constexpr size_t kHead = 256;
+constexpr size_t kHead = 256;       // device error word
 thread_local std::string g_last_error;
 
 csa_status fail(csa_status s, const char *fmt, ...) {
@@ -65,6 +65,9 @@ csa_status check_config(const csa_config *c) {
     return fail(CSA_ERR_SHAPE, "n_layers %d outside [1, %d]", c->n_layers, CSA_MAX_LAYERS);
   if (c->max_seqs < 1 || c->max_pages_per_seq < 1 || c->pool_pages < 1)
     return fail(CSA_ERR_SHAPE, "max_seqs, max_pages_per_seq and pool_pages must be >= 1");
+  if (static_cast<int64_t>(c->pool_pages) * CSA_PAGE_ENTRIES >= (1ll << 31) ||
+      static_cast<int64_t>(c->max_seqs) * c->ring_rows >= (1ll << 31))
+    return fail(CSA_ERR_UNSUPPORTED, "pool_pages * 64 and max_seqs * ring_rows must stay below 2^31 rows");
   if (static_cast<int64_t>(c->max_pages_per_seq) * CSA_PAGE_ENTRIES * c->ratio > (1ll << 30))
     return fail(CSA_ERR_UNSUPPORTED, "max_pages_per_seq * 64 * ratio exceeds 2^30 raw rows");
   const bool ok = (c->kv_dtype == CSA_F32 && c->act_dtype == CSA_F32) ||
@@ -80,18 +83,38 @@ struct Plan {  // workspace needs
 
 int64_t ecap(const csa_config &c) { return static_cast<int64_t>(c.max_pages_per_seq) * CSA_PAGE_ENTRIES; }
 
+int64_t max_slices_for(int64_t s_stride) { return (s_stride + kFilterSlice - 1) / kFilterSlice; }
+
+// S, M, candidate scores, candidate indices (each [nq][s_stride]) and per-slice counts
 size_t idx_decode_bytes(int nq, int64_t s_stride) {
-  return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) * 2 + align_up(static_cast<size_t>(nq) * kCandCap * 4, 256) * 2 +
-         align_up(static_cast<size_t>(nq) * 4, 256);
+  return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) * 4 +
+         align_up(static_cast<size_t>(nq) * max_slices_for(s_stride) * 4, 256);
 }
 size_t idx_chunk_bytes(int nq, int64_t s_stride, int64_t m_stride) {
   return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) + align_up(static_cast<size_t>(nq) * m_stride * 4, 256);
 }
 size_t attend_bytes(int nq, int n_splits, int H) {
-  return static_cast<size_t>(nq) * n_splits * H * (kD + 2) * 4;
+  return align_up(static_cast<size_t>(nq) * n_splits * H * kD * 4, 256) + align_up(static_cast<size_t>(nq) * n_splits * H * 2 * 4, 256);
 }
 
 int n_blocks_for(int k, int W) { return (k + kKeyBlock - 1) / kKeyBlock + (W > 0 ? (W + kKeyBlock - 1) / kKeyBlock : 0); }
+
+constexpr int kMaxSplits = kAttMaxSplits;
+
+// Blocks of 64 keys per attention workgroup for a decode batch of nq queries
+// with nb blocks each: enough workgroups to spread the gathers over the chip,
+// few enough splits that the fused merge stays cheap.
+int attend_blocks_per_split(int nq, int nb) {
+#ifdef CSA_ATTEND_BPS
+  int bps = CSA_ATTEND_BPS;
+#else
+  const int want_splits = std::max(1, std::min(nb, (256 + nq - 1) / nq));
+  int bps = (nb + want_splits - 1) / want_splits;
+#endif
+  bps = std::max(bps, (nb + kMaxSplits - 1) / kMaxSplits);
+  bps = std::min(bps, kAttMaxSplitKeys / kKeyBlock);
+  return std::max(1, bps);
+}
 
 bool is_chunk(int n, const int32_t *seq, const int32_t *pos) {
   if (n < 2) return false;
@@ -178,7 +201,7 @@ size_t csa_workspace_size(const csa_config *cfg, int32_t max_queries, int32_t ma
   const size_t a = idx_decode_bytes(nq_dec, s_dec);
   const int64_t s_chunk = (E + 63) / 64 * 64;
   const size_t b = max_queries > 1 ? idx_chunk_bytes(max_queries, s_chunk, s_chunk) : 0;
-  const size_t c = attend_bytes(std::min<int>(max_queries, kAttMaxQ), std::max(1, n_blocks_for(max_k, cfg->window)), cfg->q_heads);
+  const size_t c = attend_bytes(std::min<int>(max_queries, kAttMaxQ), kMaxSplits, cfg->q_heads);
   return kHead + std::max(a, std::max(b, c)) + 1024;
 }
 
@@ -410,27 +433,31 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
       char *p = h->scratch;
       float *S = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
       float *M = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
-      float *cs = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * kCandCap * 4, 256);
-      int32_t *cj = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(nq) * kCandCap * 4, 256);
+      float *cs = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
+      int32_t *cj = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
       int32_t *cnt = reinterpret_cast<int32_t *>(p);
+      const int32_t max_slices = static_cast<int32_t>(max_slices_for(s_stride));
 
       IdxScanArgs s{};
       s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;
       s.q_idx = reinterpret_cast<const char *>(q_idx) + static_cast<int64_t>(g0) * c.idx_heads * kDI * ab;
       s.w_idx = w_idx + static_cast<int64_t>(g0) * c.idx_heads;
-      s.S = S; s.M = M; s.cnt = cnt; s.err = h->err;
+      s.S = S; s.M = M; s.err = h->err;
       s.bt_stride = c.max_pages_per_seq; s.pool_pages = c.pool_pages; s.h_i = c.idx_heads;
       s.s_stride = static_cast<int32_t>(s_stride); s.n_q = nq;
       IdxFilterArgs f{};
       f.S = S; f.M = M; f.cand_s = cs; f.cand_j = cj; f.cnt = cnt; f.s_stride = s.s_stride; f.k = k; f.n_q = nq;
+      f.max_slices = max_slices;
       IdxFinalArgs fin{};
       fin.S = S; fin.cand_s = cs; fin.cand_j = cj; fin.cnt = cnt; fin.err = h->err;
       fin.topk = topk + static_cast<int64_t>(g0) * k; fin.s_stride = s.s_stride; fin.k = k; fin.n_q = nq;
+      fin.max_slices = max_slices;
       int wg = 0, slices = 0;
       for (int i = 0; i < nq; ++i) {
         const int N = (q_pos[g0 + i] + 1) / c.ratio;
         int glog2 = 0;
         while (glog2 < 8 && (((N + (2 << glog2) - 1) >> (glog2 + 1)) >= 4 * k)) ++glog2;
+        while (glog2 < 8 && ((N + (1 << glog2) - 1) >> glog2) > kMaxGroups) ++glog2;
         if (((N + (1 << glog2) - 1) >> glog2) > kMaxGroups)
           return fail(CSA_ERR_UNSUPPORTED, "query %d sees %d entries; at most %d are supported for k = %d", g0 + i, N, kMaxGroups << 8, k);
         s.q[i].seq = q_seq[g0 + i];
@@ -489,6 +516,8 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
   const size_t qrow = static_cast<size_t>(c.q_heads) * kD * ab;
 
   if (is_chunk(n_q, q_seq, q_pos)) {
+    if (a.n_blocks * kKeyBlock > kAttMaxSplitKeys)
+      return fail(CSA_ERR_UNSUPPORTED, "a prefill chunk supports at most %d keys per query", kAttMaxSplitKeys);
     a.q = q; a.out = out; a.topk = topk;
     a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0];
     a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
@@ -502,20 +531,16 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
       b.topk = topk ? topk + static_cast<int64_t>(g0) * k : nullptr;
       b.chunk = 0; b.n_q = nq;
       for (int i = 0; i < nq; ++i) { b.qd[i].seq = q_seq[g0 + i]; b.qd[i].pos = q_pos[g0 + i]; }
-      const int want = std::max(1, std::min(b.n_blocks, (1024 + nq - 1) / nq));
-      b.blocks_per_split = std::max(1, (b.n_blocks + want - 1) / want);
-      b.n_splits = std::max(1, (b.n_blocks + b.blocks_per_split - 1) / b.blocks_per_split);
+      const int nb = std::max(1, b.n_blocks);
+      b.blocks_per_split = attend_blocks_per_split(nq, nb);
+      b.n_splits = (nb + b.blocks_per_split - 1) / b.blocks_per_split;
       if (b.n_splits > 1) {
         const size_t need = attend_bytes(nq, b.n_splits, c.q_heads);
         if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for attention partials");
-        b.part = reinterpret_cast<float *>(h->scratch);
+        b.part_o = reinterpret_cast<float *>(h->scratch);
+        b.part_ml = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(nq) * b.n_splits * c.q_heads * kD * 4, 256));
       }
       launch_attend(b, nq * b.n_splits, kv, act, stream);
-      if (b.n_splits > 1) {
-        MergeArgs m{};
-        m.part = b.part; m.out = b.out; m.n_splits = b.n_splits; m.H = c.q_heads; m.n_q = nq;
-        launch_attend_merge(m, act, stream);
-      }
     }
   }
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_attend");

@@ -48,8 +48,8 @@ void launch_compress_ring(const RingArgs &a, int n_wg, int act, hipStream_t s);
 constexpr int kIdxMaxQ = 128;        // queries per decode launch group
 constexpr int kIdxChunk = 1024;      // entries per scan workgroup
 constexpr int kFilterSlice = 4096;   // scores per filter workgroup
-constexpr int kCandCap = 8192;       // candidates kept per query
 constexpr int kMaxGroups = 8192;     // group maxima per query (threshold select in LDS)
+constexpr int kMaxSlices = 512;      // filter slices per query (<= 2M visible entries)
 
 struct IdxQuery {
   int32_t seq, n_vis, chunk0, glog2;  // visible entries, first scan-WG index, log2 group size
@@ -63,7 +63,6 @@ struct IdxScanArgs {
   const float *w_idx;  // [n_q][H_I]
   float *S;            // [n_q][s_stride]
   float *M;            // [n_q][s_stride]
-  int32_t *cnt;        // [n_q]
   uint32_t *err;
   int32_t bt_stride, pool_pages, h_i, s_stride, n_q, total_wg;
   IdxQuery q[kIdxMaxQ];
@@ -71,10 +70,10 @@ struct IdxScanArgs {
 
 struct IdxFilterArgs {
   const float *S, *M;
-  float *cand_s;       // [n_q][kCandCap]
-  int32_t *cand_j;     // [n_q][kCandCap]
-  int32_t *cnt;
-  int32_t s_stride, k, n_q;
+  float *cand_s;       // [n_q][s_stride]: slice i's candidates at [i * kFilterSlice, ...), index order
+  int32_t *cand_j;     // [n_q][s_stride]
+  int32_t *cnt;        // [n_q][max_slices] candidates per slice
+  int32_t s_stride, k, n_q, max_slices;
   int32_t slice0[kIdxMaxQ + 1];   // prefix of filter WGs
   int32_t n_vis[kIdxMaxQ];
   int32_t glog2[kIdxMaxQ];
@@ -87,7 +86,7 @@ struct IdxFinalArgs {
   const int32_t *cnt;
   int32_t *topk;       // [n_q][k]
   uint32_t *err;
-  int32_t s_stride, k, n_q;
+  int32_t s_stride, k, n_q, max_slices;
   int32_t n_vis[kIdxMaxQ];
 };
 
@@ -125,6 +124,9 @@ struct AttQuery {
   int32_t seq, pos;
 };
 
+constexpr int kAttMaxSplitKeys = 2304;   // keys one workgroup resolves up front (36 blocks)
+constexpr int kAttMaxSplits = 32;        // splits per query merged by the merge kernel
+
 struct AttendArgs {
   const void *q;            // [n_q][H][D]
   void *out;                // [n_q][H][D]
@@ -133,7 +135,8 @@ struct AttendArgs {
   const float *kbar_scale, *vbar_scale;
   const void *ring_k, *ring_v;
   const int32_t *block_table;
-  float *part;              // [n_q][n_splits][H][D + 2]
+  float *part_o;            // [n_q][n_splits][H][D] unnormalised partial outputs
+  float *part_ml;           // [n_q][n_splits][2][H] running max and sum
   uint32_t *err;
   float scale;
   int32_t k, W, R, r, bt_stride, pool_pages, H;
@@ -143,14 +146,7 @@ struct AttendArgs {
   AttQuery qd[kAttMaxQ];
 };
 
-struct MergeArgs {
-  const float *part;
-  void *out;
-  int32_t n_splits, H, n_q;
-};
-
 void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s);
-void launch_attend_merge(const MergeArgs &a, int act, hipStream_t s);
 
 
 }  // namespace csa

@@ -39,51 +39,8 @@ template <int SD> constexpr int elem_bytes() { return SD == DT_F32 ? 4 : (SD == 
 
 // ------------------------------------------------------------------ block radix select
 
-// Value of the k-th largest (1 <= k <= n) of n uint32 keys produced by get(i).
-template <typename Get>
-__device__ uint32_t kth_largest_u32(Get get, int n, int k, int *hist, int *sh) {
-  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63;
-  uint32_t prefix = 0;
-  int rem = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-    for (int i = t; i < 256; i += bd) hist[i] = 0;
-    __syncthreads();
-    for (int i = t; i < n; i += bd) {
-      const uint32_t v = get(i);
-      if ((v & hmask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (t < 64) {
-      int c[4], s = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; s += c[j]; }
-      int incl = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      const int excl = incl - s;
-      if (excl < rem && rem <= incl) {
-        int cum = excl;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (cum + c[j] >= rem) { sh[0] = 255 - 4 * lane - j; sh[1] = rem - cum; break; }
-          cum += c[j];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(sh[0]) << shift;
-    rem = sh[1];
-    __syncthreads();
-  }
-  return prefix;
-}
-
-// Same for 64-bit keys (8 passes).
+// Value of the k-th largest (1 <= k <= n) of n 64-bit keys produced by get(i),
+// by MSB-first radix passes over 8-bit digits with an LDS histogram.
 template <typename Get>
 __device__ uint64_t kth_largest_u64(Get get, int n, int k, int *hist, int *sh) {
   const int t = threadIdx.x, bd = blockDim.x, lane = t & 63;
@@ -151,9 +108,131 @@ __device__ void bitonic_sort(int *arr, int n) {
 }
 
 constexpr int kSelCap = 6144;   // candidates held in LDS by the select kernels
+constexpr int kTauBins = 1024;
 
-// Exact Top-K of one query from `n` candidates given by getters, written
-// ascending into out[0..k) (n >= k). sel is LDS of >= next_pow2(k) ints.
+__device__ __forceinline__ float block_reduce_max(float v, float *red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+__device__ __forceinline__ float block_reduce_min(float v, float *red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fminf(r, red[i]);
+  return r;
+}
+
+// A threshold tau <= the k-th largest of n (> k) non-negative values given by
+// get(i): values are binned linearly between their min and max, the highest
+// bins holding at least k values are kept, and tau is the smallest value in
+// them (an actual element, so at least k elements are >= tau). Any tau below
+// the k-th largest keeps the filter exact; binning only decides how tight it is.
+template <typename Get>
+__device__ float tau_lower_bound(Get get, int n, int k, int *hist, float *red, int *sh) {
+  const int t = threadIdx.x, bd = blockDim.x;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = t; i < n; i += bd) {
+    const float v = get(i);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  lo = block_reduce_min(lo, red);
+  hi = block_reduce_max(hi, red);
+  if (!(hi > lo)) return lo;
+  const float sc = static_cast<float>(kTauBins - 1) / (hi - lo);
+  for (int i = t; i < kTauBins; i += bd) hist[i] = 0;
+  __syncthreads();
+  for (int i = t; i < n; i += bd) {
+    const int b = min(kTauBins - 1, static_cast<int>((get(i) - lo) * sc));
+    atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  // suffix counts from the top bin down: thread t owns bins [kTauBins-1-4t-3, kTauBins-1-4t]
+  if (t == 0) sh[0] = 0;
+  __syncthreads();
+  int c4[4], tot = 0;
+  const bool owner = t < kTauBins / 4;
+  if (owner) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { c4[j] = hist[kTauBins - 1 - 4 * t - j]; tot += c4[j]; }
+  }
+  // block-wide inclusive scan of tot in thread order
+  int incl = owner ? tot : 0;
+  const int lane = t & 63, w = t >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __shared__ int wsum[16];
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+  incl += base;
+  const int excl = incl - (owner ? tot : 0);
+  if (owner && excl < k && incl >= k) {
+    int cum = excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cum += c4[j];
+      if (cum >= k) { sh[0] = kTauBins - 1 - 4 * t - j; break; }
+    }
+  }
+  __syncthreads();
+  const int bstar = sh[0];
+  float m = INFINITY;
+  for (int i = t; i < n; i += bd) {
+    const float v = get(i);
+    if (min(kTauBins - 1, static_cast<int>((v - lo) * sc)) >= bstar) m = fminf(m, v);
+  }
+  return block_reduce_min(m, red);
+}
+
+// Ascending bitonic sort of n (power of two) 64-bit keys in LDS.
+__device__ void bitonic_sort_u64(uint64_t *arr, int n) {
+  const int t = threadIdx.x, bd = blockDim.x;
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < (n >> 1); i += bd) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const uint64_t x = arr[lo], y = arr[hi];
+        if ((x > y) == asc) { arr[lo] = y; arr[hi] = x; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Exact Top-K from c candidate keys already in LDS (k <= c <= kSelCap): sort
+// the keys, keep the k largest (keys are unique: score bits, then ~index, so
+// ties go to the lower index), sort their indices ascending, write out[0..k).
+__device__ void select_sorted_and_write(uint64_t *keys, int c, int k, int *sel, int32_t *out) {
+  int np = 1;
+  while (np < c) np <<= 1;
+  for (int i = c + threadIdx.x; i < np; i += blockDim.x) keys[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_u64(keys, np);
+  int np2 = 1;
+  while (np2 < k) np2 <<= 1;
+  for (int i = threadIdx.x; i < np2; i += blockDim.x) sel[i] = i < k ? key_index(keys[np - 1 - i]) : 0x7fffffff;
+  __syncthreads();
+  bitonic_sort(sel, np2);
+  for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = sel[i];
+}
+
+// Exact Top-K of one query from `n` candidates given by a getter (any n >= k;
+// slow multi-pass radix path, used only when candidates overflow LDS),
+// written ascending into out[0..k). sel is LDS of >= next_pow2(k) ints.
 template <typename GetKey>
 __device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *hist, int *sh, int32_t *out) {
   const uint64_t kth = kth_largest_u64(key_of, n, k, hist, sh);
@@ -175,6 +254,106 @@ __device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *his
   for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = sel[i];
 }
 
+
+// Exact Top-K of c candidates held in LDS in ascending index order (keys
+// cand_key[i] = score bits << 32 | ~index, scores >= 0), written ascending
+// into out[0..k), c >= k. The k-th largest key is found without sorting:
+// a linear histogram of the scores locates the bin b* holding it; every
+// candidate in a higher bin is selected; inside b* the (k - above) largest
+// keys are found by exact ranking. The selected candidates are then compacted
+// in their (index) order. Returns false (and writes nothing) when bin b*
+// holds more than kRankCap candidates; the caller then takes a slower path.
+constexpr int kRankCap = 1024;
+constexpr int kSelBins = 2048;
+
+__device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist, float *red, int *sh,
+                               uint64_t *bin_keys, int32_t *out) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6, nw = bd >> 6;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = t; i < c; i += bd) {
+    const float v = __uint_as_float(static_cast<uint32_t>(cand_key[i] >> 32));
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  lo = block_reduce_min(lo, red);
+  hi = block_reduce_max(hi, red);
+  const float sc = hi > lo ? static_cast<float>(kSelBins - 1) / (hi - lo) : 0.f;
+  auto bin_of = [&](uint64_t key) {
+    return min(kSelBins - 1, static_cast<int>((__uint_as_float(static_cast<uint32_t>(key >> 32)) - lo) * sc));
+  };
+  for (int i = t; i < kSelBins; i += bd) hist[i] = 0;
+  __syncthreads();
+  for (int i = t; i < c; i += bd) atomicAdd(&hist[bin_of(cand_key[i])], 1);
+  __syncthreads();
+  // bin b* holding the k-th largest: suffix counts, kSelBins / bd bins per thread (descending)
+  constexpr int kMaxPer = kSelBins / 256;
+  const int per = kSelBins / bd;
+  int cnt[kMaxPer], tot = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    cnt[j] = j < per ? hist[kSelBins - 1 - per * t - j] : 0;
+    tot += cnt[j];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __shared__ int wsum2[16];
+  if (lane == 63) wsum2[w] = incl;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum2[i];
+  const int excl = incl - tot;
+  if (excl < k && incl >= k) {
+    int cum = excl;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      if (j < per && cum + cnt[j] >= k) { sh[0] = kSelBins - 1 - per * t - j; sh[1] = cum; break; }
+      cum += cnt[j];
+    }
+  }
+  __syncthreads();
+  const int bstar = sh[0], above = sh[1];
+  const int need = k - above;            // keys to take from bin b*
+  const int m = hist[bstar];
+  if (m > kRankCap) return false;
+  if (t == 0) sh[2] = 0;
+  __syncthreads();
+  for (int i = t; i < c; i += bd)
+    if (bin_of(cand_key[i]) == bstar) bin_keys[atomicAdd(&sh[2], 1)] = cand_key[i];
+  __syncthreads();
+  // threshold key: the need-th largest key of the bin, by exact rank
+  for (int i = t; i < m; i += bd) {
+    const uint64_t x = bin_keys[i];
+    int r = 0;
+    for (int j = 0; j < m; ++j) r += bin_keys[j] > x;
+    if (r == need - 1) sh[3] = static_cast<int>(i);
+  }
+  __syncthreads();
+  const uint64_t kth = bin_keys[sh[3]];
+  // ordered compaction of the selected candidates (keys >= kth): thread-contiguous ranges
+  const int span = (c + bd - 1) / bd;
+  const int i0 = min(c, t * span), i1 = min(c, i0 + span);
+  int mine = 0;
+  for (int i = i0; i < i1; ++i) mine += cand_key[i] >= kth;
+  int inc2 = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc2, o, 64);
+    if (lane >= o) inc2 += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum2[w] = inc2;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) inc2 += wsum2[i];
+  int pos = inc2 - mine;
+  for (int i = i0; i < i1; ++i)
+    if (cand_key[i] >= kth) out[pos++] = key_index(cand_key[i]);
+  (void)nw;
+  return true;
+}
+
 // ------------------------------------------------------------------ decode scan
 
 template <int ACT, int KV>
@@ -187,7 +366,6 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
   const IdxQuery Q = a.q[qi];
   const int chunk = wg - Q.chunk0;
   const int N = Q.n_vis;
-  if (chunk == 0 && threadIdx.x == 0) a.cnt[qi] = 0;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
   constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
@@ -212,51 +390,83 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
   const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
   const char *kbase = reinterpret_cast<const char *>(a.kidx);
 
+  // the wave's 4 pages (256 entries): page ids once, then every load in flight
   const int wave_e0 = chunk * kIdxChunk + w * 256;
+  int my_pp = -1;
+  if (lane < 4 && wave_e0 + lane * kPage < N) my_pp = bt[(wave_e0 >> 6) + lane];
+  int pps[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pps[p] = __shfl(my_pp, p, 64);
+
+  constexpr int PB = KV == DT_FP8 ? 4 : (KV == DT_BF16 ? 2 : 1);   // pages per load batch
+  constexpr int RW = 32 * KE / 16;                                   // uint4 per lane per tile (2 chunks)
   float run = -1.f;
-  for (int pg = 0; pg < 4; ++pg) {
-    const int e_page = wave_e0 + pg * kPage;
-    if (e_page >= N) break;
-    const int pp = bt[e_page >> 6];
-    const bool ok = pp >= 0 && pp < a.pool_pages;
-    if (!ok && lane == 0) flag_error(a.err, ERR_PAGE);
-    const float sc = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
-    Frag<CT> kb[4][2];
+#pragma unroll 1
+  for (int pb = 0; pb < 4; pb += PB) {
+    if (wave_e0 + pb * kPage >= N) break;
+    uint4 raw[PB][4][RW];
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      const int e = e_page + tl * 16 + col;
-      if (ok && e < N) {
-        const char *row = kbase + (static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI * KE;
+    for (int p = 0; p < PB; ++p) {
+      const int pp = pps[pb + p];
+      const bool ok = pp >= 0 && pp < a.pool_pages;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) kb[tl][c] = LoadFrag<KV, CT>::load(row + (16 * g + 8 * c) * KE);
-      } else {
-        kb[tl][0] = kb[tl][1] = zero_frag<CT>();
+      for (int tl = 0; tl < 4; ++tl) {
+        const int e = wave_e0 + (pb + p) * kPage + tl * 16 + col;
+        if (ok && e < N) {
+          const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI * KE + 16 * g * KE);
+#pragma unroll
+          for (int u = 0; u < RW; ++u) raw[p][tl][u] = src[u];
+        } else {
+#pragma unroll
+          for (int u = 0; u < RW; ++u) raw[p][tl][u] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
+    float scs[PB];
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma(qa[0], kb[tl][0], acc);
-      acc = mma(qa[1], kb[tl][1], acc);
-      const int e_tile = e_page + tl * 16;
-      const int e = e_tile + col;
-      float s = 0.f;
+    for (int p = 0; p < PB; ++p) {
+      const int pp = pps[pb + p];
+      const bool ok = pp >= 0 && pp < a.pool_pages;
+      if (!ok && lane == 0 && wave_e0 + (pb + p) * kPage < N) flag_error(a.err, ERR_PAGE);
+      scs[p] = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
+    }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
-      s = (e < N && ok) ? s * sc : -1.f;
-      if (g == 0 && e < N) Srow[e] = s;
-      float m = s;
-      if (G <= 16) {
-        for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (g == 0 && (col & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
-      } else {
+    for (int p = 0; p < PB; ++p) {
+      const int e_page = wave_e0 + (pb + p) * kPage;
+      const bool ok = pps[pb + p] >= 0 && pps[pb + p] < a.pool_pages;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        run = fmaxf(run, m);
-        const bool last = (((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N);
-        if (last) {
-          if (lane == 0 && e_tile < N) Mrow[e_tile >> glog2] = run;
-          run = -1.f;
+      for (int tl = 0; tl < 4; ++tl) {
+        Frag<CT> kb[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const char *rp = reinterpret_cast<const char *>(&raw[p][tl][0]) + 8 * c * KE;
+          if constexpr (KV == DT_FP8) kb[c] = LoadFrag<DT_FP8, __bf16>::load(rp);
+          else if constexpr (KV == DT_BF16) kb[c] = LoadFrag<DT_BF16, __bf16>::load(rp);
+          else kb[c] = LoadFrag<DT_F32, float>::load(rp);
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma(qa[0], kb[0], acc);
+        acc = mma(qa[1], kb[1], acc);
+        const int e_tile = e_page + tl * 16;
+        const int e = e_tile + col;
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
+        s = (e < N && ok) ? s * scs[p] : -1.f;
+        if (g == 0 && e < N) Srow[e] = s;
+        float m = s;
+        if (G <= 16) {
+          for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          if (g == 0 && (col & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
+        } else {
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          run = fmaxf(run, m);
+          const bool last = (((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N);
+          if (last) {
+            if (lane == 0 && e_tile < N) Mrow[e_tile >> glog2] = run;
+            run = -1.f;
+          }
         }
       }
     }
@@ -266,10 +476,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
 // ------------------------------------------------------------------ decode filter
 
 __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) {
-  __shared__ uint32_t vals[kMaxGroups];
-  __shared__ int hist[256];
+  __shared__ float vals[kMaxGroups];
+  __shared__ int hist[kTauBins];
+  __shared__ float red[16];
   __shared__ int sh[4];
-  const int wg = blockIdx.x;
+  __shared__ int wcnt[4];
+  const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int qi = 0;
   for (; qi < a.n_q - 1; ++qi)
     if (wg < a.slice0[qi + 1]) break;
@@ -279,60 +491,127 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
   const int nG = (N + (1 << glog2) - 1) >> glog2;
   const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
   const float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
-
-  float tau = 0.f;
-  if (nG > a.k) {
-    for (int i = threadIdx.x; i < nG; i += blockDim.x) vals[i] = __float_as_uint(Mrow[i]);
-    __syncthreads();
-    const uint32_t b = kth_largest_u32([&](int i) { return vals[i]; }, nG, a.k, hist, sh);
-    tau = __uint_as_float(b);
-  }
   const int e_begin = slice * kFilterSlice, e_end = min(N, e_begin + kFilterSlice);
-  const int lane = threadIdx.x & 63;
-  int32_t *cnt = a.cnt + qi;
-  for (int e0 = e_begin; e0 < e_end; e0 += blockDim.x) {
-    const int e = e0 + threadIdx.x;
-    const float s = e < e_end ? Srow[e] : -1.f;
-    const bool pass = e < e_end && s >= tau;
-    const uint64_t mask = __ballot(pass);
-    const int n = __popcll(mask);
-    if (n == 0) continue;
-    int base = 0;
-    if (lane == 0) base = atomicAdd(cnt, n);
-    base = __shfl(base, 0, 64);
-    if (pass) {
-      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-      if (pos < kCandCap) {
-        a.cand_s[static_cast<int64_t>(qi) * kCandCap + pos] = s;
-        a.cand_j[static_cast<int64_t>(qi) * kCandCap + pos] = e;
-      }
+
+  // this slice's scores, 16 consecutive per thread (so a thread-order prefix
+  // keeps ascending index order); every load issued before any is used
+  constexpr int kPer = kFilterSlice / 256;
+  const int t0 = e_begin + tid * kPer;
+  float sv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; u += 4) {
+    if (t0 + u + 3 < e_end) {
+      const float4 v = *reinterpret_cast<const float4 *>(Srow + t0 + u);
+      sv[u] = v.x; sv[u + 1] = v.y; sv[u + 2] = v.z; sv[u + 3] = v.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sv[u + q] = t0 + u + q < e_end ? Srow[t0 + u + q] : -1.f;
     }
   }
+  // group maxima -> LDS (8 independent loads per round)
+  for (int base = 0; base < nG; base += 256 * 8) {
+    float tmp[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 256 + tid;
+      tmp[u] = i < nG ? Mrow[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 256 + tid;
+      if (i < nG) vals[i] = tmp[u];
+    }
+  }
+  __syncthreads();
+  float tau = 0.f;
+  if (nG > a.k) tau = tau_lower_bound([&](int i) { return vals[i]; }, nG, a.k, hist, red, sh);
+
+  // ordered compaction into this slice's own region
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) mine += (t0 + u < e_end && sv[u] >= tau) ? 1 : 0;
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wcnt[w] = incl;
+  __syncthreads();
+  int pos = incl - mine;
+  for (int i = 0; i < w; ++i) pos += wcnt[i];
+  const int64_t region = static_cast<int64_t>(qi) * a.s_stride + static_cast<int64_t>(slice) * kFilterSlice;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (t0 + u < e_end && sv[u] >= tau) {
+      a.cand_s[region + pos] = sv[u];
+      a.cand_j[region + pos] = t0 + u;
+      ++pos;
+    }
+  }
+  if (tid == 0) a.cnt[static_cast<int64_t>(qi) * a.max_slices + slice] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
 }
 
 // ------------------------------------------------------------------ decode final
 
 __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
   __shared__ uint64_t keys[kSelCap];
+  __shared__ uint64_t bin_keys[kRankCap];
   __shared__ int sel[CSA_MAX_TOPK];
-  __shared__ int hist[256];
+  __shared__ int hist[kSelBins];
+  __shared__ int soff[kMaxSlices + 1];
+  __shared__ float red[16];
   __shared__ int sh[4];
-  const int qi = blockIdx.x;
+  const int qi = blockIdx.x, tid = threadIdx.x;
   const int N = a.n_vis[qi], k = a.k;
   int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
   if (N <= k) {
-    for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < N ? i : -1;
+    for (int i = tid; i < k; i += blockDim.x) out[i] = i < N ? i : -1;
     return;
   }
-  const int c = a.cnt[qi];
+  // slice counts -> offsets (slices in index order, each region already ordered)
+  const int ns = (N + kFilterSlice - 1) / kFilterSlice;
+  const int32_t *cnts = a.cnt + static_cast<int64_t>(qi) * a.max_slices;
+  for (int i = tid; i < ns; i += blockDim.x) soff[i + 1] = cnts[i];
+  if (tid == 0) soff[0] = 0;
+  __syncthreads();
+  if (tid == 0)
+    for (int i = 0; i < ns; ++i) soff[i + 1] += soff[i];
+  __syncthreads();
+  const int c = soff[ns];
+  bool done = false;
   if (c >= k && c <= kSelCap) {
-    for (int i = threadIdx.x; i < c; i += blockDim.x)
-      keys[i] = score_key(a.cand_s[static_cast<int64_t>(qi) * kCandCap + i], a.cand_j[static_cast<int64_t>(qi) * kCandCap + i]);
+    const int64_t qbase = static_cast<int64_t>(qi) * a.s_stride;
+    constexpr int kPer = (kSelCap + 511) / 512;
+    float ts[kPer];
+    int tj[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * 512 + tid;
+      ts[u] = 0.f;
+      tj[u] = 0;
+      if (i < c) {
+        int lo = 0, hi = ns;            // slice s with soff[s] <= i < soff[s+1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (soff[mid] <= i) lo = mid; else hi = mid;
+        }
+        const int64_t o = qbase + static_cast<int64_t>(lo) * kFilterSlice + (i - soff[lo]);
+        ts[u] = a.cand_s[o];
+        tj[u] = a.cand_j[o];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * 512 + tid;
+      if (i < c) keys[i] = score_key(ts[u], tj[u]);
+    }
     __syncthreads();
-    select_and_write([&](int i) { return keys[i]; }, c, k, sel, hist, sh, out);
-  } else {
-    // more candidates than LDS holds (heavy ties): exact select straight from the scores
-    if (threadIdx.x == 0) flag_error(a.err, ERR_FALLBACK);
+    done = select_ordered(keys, c, k, hist, red, sh, bin_keys, out);
+  }
+  if (!done) {
+    // heavy ties or too many candidates: exact select straight from the scores
+    if (tid == 0) flag_error(a.err, ERR_FALLBACK);
     const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
     select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out);
   }
@@ -468,9 +747,10 @@ __global__ __launch_bounds__(256) void idx_chunk_scan_kernel(const IdxChunkScanA
 // ------------------------------------------------------------------ chunk select
 
 __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkSelectArgs a) {
-  __shared__ uint64_t keys[kSelCap];
+  __shared__ uint64_t keys[8192];
   __shared__ int sel[CSA_MAX_TOPK];
-  __shared__ int hist[256];
+  __shared__ int hist[kTauBins];
+  __shared__ float red[16];
   __shared__ int sh[4];
   const int qi = blockIdx.x;
   const int N = (a.pos0 + qi + 1) / a.r, k = a.k;
@@ -484,10 +764,7 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkSel
   const int glog2 = a.glog2;
   const int nG = (N + (1 << glog2) - 1) >> glog2;
   float tau = 0.f;
-  if (nG > k) {
-    const uint32_t b = kth_largest_u32([&](int i) { return __float_as_uint(Mrow[i]); }, nG, k, hist, sh);
-    tau = __uint_as_float(b);
-  }
+  if (nG > k) tau = tau_lower_bound([&](int i) { return Mrow[i]; }, nG, k, hist, red, sh);
   if (threadIdx.x == 0) sh[3] = 0;
   __syncthreads();
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
@@ -500,7 +777,7 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkSel
   __syncthreads();
   const int c = sh[3];
   if (c <= kSelCap) {
-    select_and_write([&](int i) { return keys[i]; }, c, k, sel, hist, sh, out);
+    select_sorted_and_write(keys, c, k, sel, out);
   } else {
     if (threadIdx.x == 0) flag_error(a.err, ERR_FALLBACK);
     select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out);

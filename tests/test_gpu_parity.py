@@ -475,3 +475,42 @@ def test_bad_page_ids_are_flagged_not_faulting():
     cache.block_table[0, 5] = 5
     cache.attend(0, [0], [1599], q, Tvis, 64, 0.1)
     assert cache.read_errors() & B.ERR_TOPK
+
+
+def test_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph: every replay, with eager work in
+    between, reproduces the eager outputs bit for bit."""
+    cache = make_cache(71, ratio=4, q_heads=64, window=128, ring_rows=128, max_seqs=3, max_pages_per_seq=40,
+                       pool_pages=121, kv_dtype="fp8", act_dtype="bf16", max_queries=3, max_k=512)
+    lens = [4 * 2500, 4 * 1000 + 3, 4 * 300]
+    for b, L in enumerate(lens):
+        fill_main_kv(cache, 71, 0, b, L // 4)
+        fill_index_keys(cache, 71, b, L // 4)
+        fill_ring(cache, 71, 0, b, L)
+        B.csa_seq_set_len(cache.handle, 0, b, L)
+    q_seq, q_pos = [0, 1, 2], [L - 1 for L in lens]
+    qi = Sy.normal_rows(71, Sy.stream_id(Sy.KIND_QI), 0, 12, 64, dtype=torch.bfloat16).view(3, 4, 64).cuda()
+    w = Sy.uniform_rows(71, Sy.stream_id(Sy.KIND_W), 0, 3, 4).cuda()
+    q = Sy.normal_rows(71, Sy.stream_id(Sy.KIND_Q), 0, 192, 128, dtype=torch.bfloat16).view(3, 64, 128).cuda()
+    T = torch.empty((3, 512), dtype=torch.int32, device="cuda")
+    out = torch.empty((3, 64, 128), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream()
+    B.csa_index_topk(cache.handle, q_seq, q_pos, qi, w, 512, T, s)
+    B.csa_attend(cache.handle, 0, q_seq, q_pos, q, T, 512, 0.088, out, s)
+    torch.cuda.synchronize()
+    T_ref, out_ref = T.clone(), out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream()
+        B.csa_index_topk(cache.handle, q_seq, q_pos, qi, w, 512, T, cs)
+        B.csa_attend(cache.handle, 0, q_seq, q_pos, q, T, 512, 0.088, out, cs)
+    for rep in range(4):
+        T.zero_()
+        out.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()       # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(T, T_ref), f"replay {rep}: Top-K differs"
+        assert torch.equal(out, out_ref), f"replay {rep}: output differs"
+        del junk
+    assert cache.read_errors() == 0
