@@ -7,23 +7,24 @@
 // Bounded Replay" > "Replay only the window" (window keys [max(s, i-W+1), i]);
 // Model-architectures atlas, MQA/GQA entry (many query heads, one KV head).
 //
-// Work decomposition: the keys of a query are cut into blocks of 64 (Top-K
-// blocks first, then window blocks). A 256-thread workgroup owns (query,
-// split), a split being a run of blocks:
-//   1. it resolves the source of every key of the split once (Top-K index ->
-//      page -> pool row and page scales, or window row -> ring row) into LDS;
-//   2. per block, the 64 K and V rows (fp8 codes converted exactly to bf16)
-//      go to LDS, K row-major and V transposed, while the next block's rows
-//      are already being loaded into registers;
-//   3. each active wave takes 16 heads: S^T[key][head] = K . Q^T with keys as
-//      MFMA rows and heads as columns, so a lane holds one head and 4 keys per
-//      16-key tile; after the online-softmax update those probabilities are
-//      already the A operand of O = P . V (heads as rows, keys contracted),
-//      paired with V^T from LDS.
-// With one split per query the workgroup writes the normalised output. With
-// several, each writes (m, l, O) partials; the last split of a query to finish
-// (release fence + arrival counter) merges them with the log-sum-exp
-// rescaling, which equals one softmax over the union of keys.
+// Work decomposition. The keys of a query are cut into blocks of 64 (Top-K
+// blocks first, then window blocks). A workgroup owns (query, split), a split
+// being a run of blocks, and has HG x KSTR waves: HG head groups times KSTR
+// key streams. Each round it gathers KSTR blocks (one per stream) into LDS, K
+// row-major and V transposed in the MFMA compute type (fp8 codes convert
+// exactly to bf16; page scales are applied to the logits and probabilities),
+// while the next round's rows are already being loaded into registers. Wave
+// (head group, stream) then runs, for its 16-head tiles and its stream's block:
+//   S^T[key][head] = K . Q^T  (keys as MFMA rows, heads as columns), so a lane
+//   holds one head and 4 keys per 16-key tile; after the online-softmax update
+//   those probabilities are already the A operand of O = P . V (heads as rows,
+//   keys contracted) against V^T from LDS.
+// The streams' (m, l, O) are merged in LDS at the end. With one split per
+// query the workgroup writes the output; with several, each writes its (m, l,
+// O) partial and a merge kernel combines them with the log-sum-exp rescaling,
+// which equals one softmax over the union of all keys. (A merge by the last
+// split to finish would need a device-scope release fence per workgroup, which
+// on this multi-XCD part writes back the L2 and costs more than the launch.)
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -44,9 +45,6 @@ __device__ __forceinline__ CT to_ct(float x) {
     return __builtin_bit_cast(__bf16, f32_to_bf16(x));
   }
 }
-
-constexpr int kThreads = 256;
-constexpr int kMaxSplits = kAttMaxSplits;
 
 // Raw bytes of one 32-element segment of a row, by storage dtype.
 template <int SD> struct Seg { uint4 u[SD == DT_F32 ? 8 : (SD == DT_BF16 ? 4 : 2)]; };
@@ -96,20 +94,45 @@ __device__ __forceinline__ void seg_values(const Seg<SD> &s, CT *dst) {
   }
 }
 
-// AW: waves that compute (min(4, H/16)); NHT: 16-head tiles per computing wave.
-template <int ACT, int KV, int AW, int NHT>
-__global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
+constexpr int KSTR = kAttKeyStreams;   // key streams per workgroup
+
+// One gather item: 32 dims of one key's K and V row, as raw bytes of either
+// the pool format (KV) or the window-ring format (ACT); kind says which.
+template <int ACT, int KV>
+struct Item {
+  static constexpr int RW = (sizeof(Seg<KV>) > sizeof(Seg<ACT>) ? sizeof(Seg<KV>) : sizeof(Seg<ACT>)) / 16;
+  uint4 k[RW], v[RW];
+  float ks, vs;
+  int kind;   // 0 masked, 1 pool row, 2 ring row
+};
+
+template <int SD, int RW>
+__device__ __forceinline__ const Seg<SD> &as_seg(const uint4 (&u)[RW]) {
+  return *reinterpret_cast<const Seg<SD> *>(&u[0]);
+}
+
+// HG: head groups (waves per stream); NTW: 16-head tiles per wave.
+template <int ACT, int KV, int HG, int NTW>
+__global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs a) {
   using CT = typename ComputeT<KV>::type;
+  constexpr int NT = HG * KSTR * 64;
+  constexpr int H = HG * NTW * 16;
   constexpr int KE = KV == DT_F32 ? 4 : (KV == DT_BF16 ? 2 : 1);
   constexpr int AE = ACT == DT_F32 ? 4 : 2;
   constexpr int KS = kD + kpad<CT>();          // K row stride (elements)
   constexpr int VS = kKeyBlock + kpad<CT>();   // V^T row stride (elements)
-  constexpr int H = AW * NHT * 16;
-  __shared__ CT Ks[kKeyBlock * KS];
-  __shared__ CT Vt[kD * VS];
+  constexpr int ITEMS = KSTR * 256 / NT;       // gather items per thread per round
+  constexpr bool PREFETCH = KV != DT_F32;      // fp32 rows are too large to hold a round in registers
+  constexpr int KV_LDS = KSTR * (kKeyBlock * KS + kD * VS) * static_cast<int>(sizeof(CT));
+  static_assert((KSTR - 1) * H * kD * 4 <= KV_LDS, "stream partials must fit in the K/V buffers");
+
+  __shared__ __align__(16) char kv_lds[KV_LDS];
   __shared__ int32_t src_row[kAttMaxSplitKeys];   // >= 0 pool row; < 0: -(ring row) - 1
   __shared__ uint8_t kvalid[kAttMaxSplitKeys];
-  __shared__ float ksc[kKeyBlock], vsc[kKeyBlock];  // page scales of the block in LDS
+  __shared__ float ksc[KSTR][kKeyBlock], vsc[KSTR][kKeyBlock];
+  __shared__ float sm_m[KSTR][H], sm_l[KSTR][H];
+  CT *Ks = reinterpret_cast<CT *>(kv_lds);                       // [KSTR][64][KS]
+  CT *Vt = Ks + KSTR * kKeyBlock * KS;                           // [KSTR][D][VS]
 
   const int qi = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
   const int seq = a.chunk ? a.seq0 : a.qd[qi].seq;
@@ -123,8 +146,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
   const int32_t *trow = a.topk + static_cast<int64_t>(qi) * a.k;
   const int tid = threadIdx.x;
 
-  // ---------------- 1. resolve every key of the split
-  for (int i = tid; i < n_keys; i += kThreads) {
+  // ---------------- 1. resolve every key of the split once
+  for (int i = tid; i < n_keys; i += NT) {
     const int b = b_begin + i / kKeyBlock, kk = i % kKeyBlock;
     int valid = 0;
     int32_t row = 0;
@@ -156,91 +179,117 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
   }
   __syncthreads();
 
-  // ---------------- register prefetch of one block: thread owns (key, 32-dim segment)
-  const int pk = tid & 63, psg = tid >> 6;
-  Seg<KV> kseg, vseg;
-  Seg<ACT> kraw, vraw;
-  float pks = 1.f, pvs = 1.f;
-  auto prefetch = [&](int b) {
+  // ---------------- gather: item = (stream, key, 32-dim segment)
+  using It = Item<ACT, KV>;
+  auto load_item = [&](It &x, int gi, int r) {
+    const int st = gi >> 8, pk = gi & 63, psg = (gi >> 6) & 3;
+    const int b = b_begin + r * KSTR + st;
     const int i = (b - b_begin) * kKeyBlock + pk;
+    x.ks = 1.f;
+    x.vs = 1.f;
+    x.kind = 0;
+    if (b >= b_end || kvalid[i] == 0) return;
     const int64_t row = src_row[i];
-    pks = 1.f;
-    pvs = 1.f;
-    if (kvalid[i] == 0) {
-      zero_seg(kseg); zero_seg(vseg); zero_seg(kraw); zero_seg(vraw);
-    } else if (row >= 0) {
+    if (row >= 0) {
+      x.kind = 1;
       const int64_t off = (row * kD + 32 * psg) * KE;
-      load_seg(kseg, reinterpret_cast<const char *>(a.kbar) + off);
-      load_seg(vseg, reinterpret_cast<const char *>(a.vbar) + off);
+      load_seg(*reinterpret_cast<Seg<KV> *>(&x.k[0]), reinterpret_cast<const char *>(a.kbar) + off);
+      load_seg(*reinterpret_cast<Seg<KV> *>(&x.v[0]), reinterpret_cast<const char *>(a.vbar) + off);
       if constexpr (KV == DT_FP8) {
-        if (psg == 0) { pks = a.kbar_scale[row >> 6]; pvs = a.vbar_scale[row >> 6]; }
+        if (psg == 0) { x.ks = a.kbar_scale[row >> 6]; x.vs = a.vbar_scale[row >> 6]; }
       }
     } else {
+      x.kind = 2;
       const int64_t off = ((-row - 1) * kD + 32 * psg) * AE;
-      load_seg(kraw, reinterpret_cast<const char *>(a.ring_k) + off);
-      load_seg(vraw, reinterpret_cast<const char *>(a.ring_v) + off);
+      load_seg(*reinterpret_cast<Seg<ACT> *>(&x.k[0]), reinterpret_cast<const char *>(a.ring_k) + off);
+      load_seg(*reinterpret_cast<Seg<ACT> *>(&x.v[0]), reinterpret_cast<const char *>(a.ring_v) + off);
     }
   };
-  auto commit = [&](int b) {
-    const int i = (b - b_begin) * kKeyBlock + pk;
+  auto commit_item = [&](const It &x, int gi) {
+    const int st = gi >> 8, pk = gi & 63, psg = (gi >> 6) & 3;
     CT kv[32], vv[32];
-    if (src_row[i] >= 0 || !kvalid[i]) {
-      seg_values<KV, CT>(kseg, kv);
-      seg_values<KV, CT>(vseg, vv);
+    if (x.kind == 1) {
+      seg_values<KV, CT>(as_seg<KV>(x.k), kv);
+      seg_values<KV, CT>(as_seg<KV>(x.v), vv);
+    } else if (x.kind == 2) {
+      seg_values<ACT, CT>(as_seg<ACT>(x.k), kv);
+      seg_values<ACT, CT>(as_seg<ACT>(x.v), vv);
     } else {
-      seg_values<ACT, CT>(kraw, kv);
-      seg_values<ACT, CT>(vraw, vv);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) { kv[u] = to_ct<CT>(0.f); vv[u] = to_ct<CT>(0.f); }
     }
+    CT *kd = Ks + (st * kKeyBlock + pk) * KS + 32 * psg;
+    CT *vd = Vt + st * kD * VS + (32 * psg) * VS + pk;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) Ks[pk * KS + 32 * psg + u] = kv[u];
+    for (int u = 0; u < 32; ++u) kd[u] = kv[u];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) Vt[(32 * psg + u) * VS + pk] = vv[u];
-    if (psg == 0) { ksc[pk] = pks; vsc[pk] = pvs; }
+    for (int u = 0; u < 32; ++u) vd[u * VS] = vv[u];
+    if (psg == 0) { ksc[st][pk] = x.ks; vsc[st][pk] = x.vs; }
+  };
+  It items[PREFETCH ? ITEMS : 1];
+  auto load_round = [&](int r) {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) load_item(items[it], tid + it * NT, r);
+  };
+  auto commit_round = [&](int r) {
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) commit_item(items[it], tid + it * NT);
+    } else {
+      for (int it = 0; it < ITEMS; ++it) {
+        load_item(items[0], tid + it * NT, r);
+        commit_item(items[0], tid + it * NT);
+      }
+    }
   };
 
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
-  const bool computes = w < AW;
+  const int lane = tid & 63, w = tid >> 6, hg = w % HG, ks = w / HG, g = lane >> 4, col = lane & 15;
 
   // Q fragments (B operand of S^T) for this wave's head tiles
-  Frag<CT> qf[NHT][4];
-  f32x4_t O[NHT][8];
-  float m_run[NHT], l_run[NHT];
+  Frag<CT> qf[NTW][4];
+  f32x4_t O[NTW][8];
+  float m_run[NTW], l_run[NTW];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const int head = 16 * (w + AW * ht) + col;
-    if (computes) {
-      const char *qrow = reinterpret_cast<const char *>(a.q) + (static_cast<int64_t>(qi) * H + head) * kD * AE;
+  for (int j = 0; j < NTW; ++j) {
+    const int head = 16 * (hg + HG * j) + col;
+    const char *qrow = reinterpret_cast<const char *>(a.q) + (static_cast<int64_t>(qi) * H + head) * kD * AE;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[ht][c] = LoadFrag<ACT, CT>::load(qrow + (32 * g + 8 * c) * AE);
-    }
+    for (int c = 0; c < 4; ++c) qf[j][c] = LoadFrag<ACT, CT>::load(qrow + (32 * g + 8 * c) * AE);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) O[ht][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_run[ht] = -INFINITY;
-    l_run[ht] = 0.f;
+    for (int n = 0; n < 8; ++n) O[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
   }
 
-  if (b_begin < b_end) prefetch(b_begin);
-  for (int b = b_begin; b < b_end; ++b) {
-    __syncthreads();                 // previous block's LDS reads are done
-    commit(b);
+  const int n_rounds = (b_end - b_begin + KSTR - 1) / KSTR;
+  if constexpr (PREFETCH) {
+    if (n_rounds > 0) load_round(0);
+  }
+  for (int r = 0; r < n_rounds; ++r) {
+    __syncthreads();                   // previous round's LDS reads are done
+    commit_round(r);
     __syncthreads();
-    if (b + 1 < b_end) prefetch(b + 1);   // in flight during this block's math
-    if (!computes) continue;
+    if constexpr (PREFETCH) {
+      if (r + 1 < n_rounds) load_round(r + 1);   // in flight during this round's math
+    }
+    const int b = b_begin + r * KSTR + ks;
+    if (b >= b_end) continue;
     const int kb0 = (b - b_begin) * kKeyBlock;
+    const CT *Kb = Ks + ks * kKeyBlock * KS;
+    const CT *Vb = Vt + ks * kD * VS;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      // S^T = K . Q^T
+    for (int j = 0; j < NTW; ++j) {
       f32x4_t S[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const CT *src = &Ks[(16 * kt + col) * KS + 32 * g + 8 * c];
+          const CT *src = Kb + (16 * kt + col) * KS + 32 * g + 8 * c;
           Frag<CT> kf;
           if constexpr (sizeof(CT) == 4) kf = LoadFrag<DT_F32, float>::load(src);
           else kf = LoadFrag<DT_BF16, __bf16>::load(src);
-          S[kt] = mma(kf, qf[ht][c], S[kt]);
+          S[kt] = mma(kf, qf[j][c], S[kt]);
         }
       }
       // logits and online softmax (lane's head = col; keys 16*kt + 4*g + v)
@@ -250,14 +299,14 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int key = kb0 + 16 * kt + 4 * g + v;
-          x[kt][v] = kvalid[key] ? S[kt][v] * (a.scale * ksc[key - kb0]) : -INFINITY;
+          const int key = 16 * kt + 4 * g + v;
+          x[kt][v] = kvalid[kb0 + key] ? S[kt][v] * (a.scale * ksc[ks][key]) : -INFINITY;
           bm = fmaxf(bm, x[kt][v]);
         }
       bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
       bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      const float m_new = fmaxf(m_run[ht], bm);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run[ht] - m_new);
+      const float m_new = fmaxf(m_run[j], bm);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run[j] - m_new);
       float psum = 0.f;
       float p[4][4];
 #pragma unroll
@@ -267,27 +316,26 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
           p[kt][v] = (x[kt][v] == -INFINITY) ? 0.f : __expf(x[kt][v] - m_new);
           psum += p[kt][v];
         }
-      l_run[ht] = l_run[ht] * alpha + psum;
-      m_run[ht] = m_new;
+      l_run[j] = l_run[j] * alpha + psum;
+      m_run[j] = m_new;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float av = __shfl(alpha, 4 * g + v, 64);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) O[ht][n][v] *= av;
+        for (int n = 0; n < 8; ++n) O[j][n][v] *= av;
       }
-      // O += P . V
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         float pv[8];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          pv[v] = p[2 * kc][v] * vsc[32 * kc + 4 * g + v];
-          pv[4 + v] = p[2 * kc + 1][v] * vsc[32 * kc + 16 + 4 * g + v];
+          pv[v] = p[2 * kc][v] * vsc[ks][32 * kc + 4 * g + v];
+          pv[4 + v] = p[2 * kc + 1][v] * vsc[ks][32 * kc + 16 + 4 * g + v];
         }
         const Frag<CT> pf = frag_from_f32(pv, static_cast<Frag<CT> *>(nullptr));
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const CT *vr = &Vt[(16 * n + col) * VS + 32 * kc + 4 * g];
+          const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
           Frag<CT> vf;
           if constexpr (sizeof(CT) == 4) {
 #pragma unroll
@@ -297,67 +345,112 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(const AttendArgs a) {
             const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
             vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
           }
-          O[ht][n] = mma(pf, vf, O[ht][n]);
+          O[j][n] = mma(pf, vf, O[j][n]);
         }
       }
     }
   }
 
-  // ---------------- finish
-  if (a.n_splits == 1) {
-    if (!computes) return;
+  // ---------------- 2. merge the key streams in LDS (stream 0 keeps the result)
+  float *po = reinterpret_cast<float *>(kv_lds);   // [KSTR-1][H][D] partial outputs of streams >= 1
+  __syncthreads();                                 // all rounds done: K/V buffers are free
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      float l_tot = l_run[ht] + __shfl_xor(l_run[ht], 16, 64);
-      l_tot += __shfl_xor(l_tot, 32, 64);
+  for (int j = 0; j < NTW; ++j) {
+    const int h0 = 16 * (hg + HG * j);
+    float l_tot = l_run[j] + __shfl_xor(l_run[j], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (g == 0) {
+      sm_m[ks][h0 + col] = m_run[j];
+      sm_l[ks][h0 + col] = l_tot;
+    }
+    if (ks > 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) po[((ks - 1) * H + h0 + 4 * g + v) * kD + 16 * n + col] = O[j][n][v];
+    }
+  }
+  __syncthreads();
+  float Lh[NTW][4];   // per O row (head 4g + v of each tile): merged denominator and max
+  float Mh[NTW][4];
+  if (ks == 0) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int h0 = 16 * (hg + HG * j);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int h = 16 * (w + AW * ht) + 4 * g + v;
-        const float lh = __shfl(l_tot, 4 * g + v, 64);
-        const float inv = lh > 0.f ? 1.f / lh : 0.f;
+        const int h = h0 + 4 * g + v;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < KSTR; ++s) mx = fmaxf(mx, sm_m[s][h]);
+        float L = 0.f;
+        float al[KSTR];
+#pragma unroll
+        for (int s = 0; s < KSTR; ++s) {
+          al[s] = (sm_m[s][h] == -INFINITY) ? 0.f : __expf(sm_m[s][h] - mx);
+          L += al[s] * sm_l[s][h];
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          float o = al[0] * O[j][n][v];
+#pragma unroll
+          for (int s = 1; s < KSTR; ++s) o += al[s] * po[((s - 1) * H + h) * kD + 16 * n + col];
+          O[j][n][v] = o;
+        }
+        Lh[j][v] = L;
+        Mh[j][v] = mx;
+      }
+    }
+  }
+
+  if (a.n_splits == 1) {
+    if (ks != 0) return;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int h = 16 * (hg + HG * j) + 4 * g + v;
+        const float inv = Lh[j][v] > 0.f ? 1.f / Lh[j][v] : 0.f;
         const int64_t ob = (static_cast<int64_t>(qi) * H + h) * kD;
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const float o = O[ht][n][v] * inv;
+          const float o = O[j][n][v] * inv;
           if constexpr (ACT == DT_F32) reinterpret_cast<float *>(a.out)[ob + 16 * n + col] = o;
           else reinterpret_cast<uint16_t *>(a.out)[ob + 16 * n + col] = f32_to_bf16(o);
         }
       }
-    }
     return;
   }
 
+  // ---------------- 3. several splits: write this split's partial; the merge kernel combines them
   const int64_t pbase = static_cast<int64_t>(qi) * a.n_splits + split;
-  if (computes) {
+  if (ks == 0) {
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      float l_tot = l_run[ht] + __shfl_xor(l_run[ht], 16, 64);
-      l_tot += __shfl_xor(l_tot, 32, 64);
-      const int h0 = 16 * (w + AW * ht);
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float *po = a.part_o + (pbase * H + h0 + 4 * g + v) * kD;
+        const int h = 16 * (hg + HG * j) + 4 * g + v;
+        float *pr = a.part_o + (pbase * H + h) * kD;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) po[16 * n + col] = O[ht][n][v];
+        for (int n = 0; n < 8; ++n) pr[16 * n + col] = O[j][n][v];
+        if (col == 0) {
+          a.part_ml[(pbase * 2 + 0) * H + h] = Mh[j][v];
+          a.part_ml[(pbase * 2 + 1) * H + h] = Lh[j][v];
+        }
       }
-      if (g == 0) {
-        a.part_ml[(pbase * 2 + 0) * H + h0 + col] = m_run[ht];
-        a.part_ml[(pbase * 2 + 1) * H + h0 + col] = l_tot;
-      }
-    }
   }
 }
 
 // Combines the split partials of (query, head): one softmax over the union of
 // every split's keys. Thread d owns output dimension d; all of its loads are
-// independent, so the whole merge is about one memory round trip.
+// independent, so the merge costs about one memory round trip.
 template <int ACT>
 __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   const int qi = blockIdx.x / a.H, h = blockIdx.x % a.H, d = threadIdx.x;
   const int64_t q0 = static_cast<int64_t>(qi) * a.n_splits;
-  float m[kMaxSplits], l[kMaxSplits], o[kMaxSplits];
+  float m[kAttMaxSplits], l[kAttMaxSplits], o[kAttMaxSplits];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < kAttMaxSplits; ++s) {
     const bool ok = s < a.n_splits;
     m[s] = ok ? a.part_ml[((q0 + s) * 2 + 0) * a.H + h] : -INFINITY;
     l[s] = ok ? a.part_ml[((q0 + s) * 2 + 1) * a.H + h] : 0.f;
@@ -365,10 +458,10 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) mx = fmaxf(mx, m[s]);
+  for (int s = 0; s < kAttMaxSplits; ++s) mx = fmaxf(mx, m[s]);
   float L = 0.f, acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < kAttMaxSplits; ++s) {
     const float e = (m[s] == -INFINITY) ? 0.f : __expf(m[s] - mx);
     L += e * l[s];
     acc += e * o[s];
@@ -382,10 +475,10 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
 template <int ACT, int KV>
 void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s) {
   switch (a.H) {
-    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(kThreads), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(1 * KSTR * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(2 * KSTR * 64), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
     default: break;
   }
 }

@@ -108,8 +108,10 @@ int attend_blocks_per_split(int nq, int nb) {
 #ifdef CSA_ATTEND_BPS
   int bps = CSA_ATTEND_BPS;
 #else
-  const int want_splits = std::max(1, std::min(nb, (256 + nq - 1) / nq));
-  int bps = (nb + want_splits - 1) / want_splits;
+  // Latency-bound: a workgroup that walks several blocks in sequence waits a
+  // memory round trip per block, so decode batches take one round per split.
+  int bps = kAttKeyStreams;
+  (void)nq;
 #endif
   bps = std::max(bps, (nb + kMaxSplits - 1) / kMaxSplits);
   bps = std::min(bps, kAttMaxSplitKeys / kKeyBlock);

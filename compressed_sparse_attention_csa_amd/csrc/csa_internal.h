@@ -125,7 +125,8 @@ struct AttQuery {
 };
 
 constexpr int kAttMaxSplitKeys = 2304;   // keys one workgroup resolves up front (36 blocks)
-constexpr int kAttMaxSplits = 32;        // splits per query merged by the merge kernel
+constexpr int kAttKeyStreams = 1;        // 64-key blocks a workgroup processes per round
+constexpr int kAttMaxSplits = 40;        // splits per query combined by the merge kernel
 
 struct AttendArgs {
   const void *q;            // [n_q][H][D]
