@@ -48,7 +48,80 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device copy after timing (reference kernel for HBM counters)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk MFMA-utilisation leg")
+    ap.add_argument("--prefill-only", action="store_true", help="only run the prefill-chunk leg (development)")
     return ap.parse_args()
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PF_PRIOR, PF_CHUNK, PF_K = 131072, 2048, 1024
+
+
+def prefill_leg(seed, dev, steps=5):
+    """Prefill chunk: 2,048 new tokens appended to a 131,072-token context (bf16,
+    r = 4, Top-1024 per query token, W = 128, 64 heads). One step = compress the
+    chunk, index (MFMA score GEMM + exact select) and attend all 2,048 tokens.
+    Reports MFMA utilisation of the index GEMM and of the attention kernel from
+    HIP events around their launches."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+
+    total = PF_PRIOR + PF_CHUNK
+    pages = (total // RATIO + 63) // 64
+    spec = CacheSpec(ratio=RATIO, q_heads=HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW + PF_CHUNK,
+                     n_layers=1, max_seqs=1, max_pages_per_seq=pages, pool_pages=pages, kv_dtype="bf16",
+                     act_dtype="bf16", max_queries=PF_CHUNK, max_k=PF_K)
+    bt = torch.tensor(Sy.permutation(seed, pages, salt=5), dtype=torch.int32).view(1, pages).to(dev)
+    c = CsaCache(spec, dev, block_table=bt)
+    P = Sy.proj_matrix(seed, 128, 64, device=dev)
+    rows = lambda kind, r0, n: Sy.normal_rows(seed, Sy.stream_id(kind, 0, 0), r0, n, 128, dev, torch.bfloat16)
+    c.compress(0, [0], [PF_PRIOR], rows(Sy.KIND_K, 0, PF_PRIOR), rows(Sy.KIND_V, 0, PF_PRIOR), rows(Sy.KIND_Z, 0, PF_PRIOR), P)
+    ck, cv, cz = rows(Sy.KIND_K, PF_PRIOR, PF_CHUNK), rows(Sy.KIND_V, PF_PRIOR, PF_CHUNK), rows(Sy.KIND_Z, PF_PRIOR, PF_CHUNK)
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI, 0, 1), 0, PF_CHUNK * IDX_HEADS, 64, dev, torch.bfloat16).view(PF_CHUNK, IDX_HEADS, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W, 0, 1), 0, PF_CHUNK, IDX_HEADS, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, 0, 1), 0, PF_CHUNK * HEADS, 128, dev, torch.bfloat16).view(PF_CHUNK, HEADS, 128)
+    T = torch.empty((PF_CHUNK, PF_K), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    q_seq, q_pos = [0] * PF_CHUNK, list(range(PF_PRIOR, total))
+    scale = 1.0 / math.sqrt(128)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_step, t_att = [], []
+    for i in range(steps + 1):
+        B.csa_seq_set_len(c.handle, 0, 0, PF_PRIOR)
+        torch.cuda.synchronize()
+        ev[0].record()
+        c.compress(0, [0], [PF_CHUNK], ck, cv, cz, P)
+        if i == steps:
+            B.csa_profile_begin(c.handle)
+        c.index_topk(q_seq, q_pos, qi, w, PF_K, T)
+        ev[1].record()
+        c.attend(0, q_seq, q_pos, q, T, PF_K, scale, out)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if i > 0:
+            t_step.append(ev[0].elapsed_time(ev[2]))
+            t_att.append(ev[1].elapsed_time(ev[2]))
+    scan_ms, n = B.csa_profile_end(c.handle)
+    flags = c.read_errors()
+    if flags:
+        raise RuntimeError(f"prefill leg raised device error flags {flags}")
+    idx_flops = A.index_flops(A.prefill_visible_scores(PF_PRIOR, PF_CHUNK, RATIO), IDX_HEADS, 64)
+    att_flops = A.attend_flops(PF_CHUNK, HEADS, PF_K + WINDOW, 128)
+    att_ms = min(t_att)
+    res = {"workload": "prefill chunk: 2,048 tokens on a 131,072-token context, bf16, r=4, Top-1024, W=128, 64 heads",
+           "ms_per_chunk": round(min(t_step), 4), "tokens_per_s": round(PF_CHUNK / (min(t_step) * 1e-3), 1),
+           "index_gemm": {"tflops": round(idx_flops / (scan_ms / max(n, 1) * 1e-3) / 1e12, 1),
+                          "util": round(idx_flops / (scan_ms / max(n, 1) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "us": round(scan_ms / max(n, 1) * 1e3, 2), "gflop": round(idx_flops / 1e9, 2)},
+           "attend": {"tflops": round(att_flops / (att_ms * 1e-3) / 1e12, 1),
+                      "util": round(att_flops / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "us": round(att_ms * 1e3, 2), "gflop": round(att_flops / 1e9, 2)},
+           "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+    c.close()
+    return res
 
 
 def build_cache(seed, replicas, dev):
@@ -179,6 +252,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()
+    if args.prefill_only:
+        print(json.dumps(prefill_leg(args.seed, dev)), flush=True)
+        return
     t_build = time.time()
     caches = build_cache(args.seed, args.replicas, dev)
     print(f"[bench] cache built: {len(caches)} replicas in {time.time() - t_build:.1f} s", file=sys.stderr, flush=True)
@@ -278,6 +354,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(),
                      "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
     }
+    if not args.no_prefill:
+        del caches, graphs
+        torch.cuda.empty_cache()
+        line["prefill"] = prefill_leg(args.seed, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -94,7 +94,6 @@ __device__ __forceinline__ void seg_values(const Seg<SD> &s, CT *dst) {
   }
 }
 
-constexpr int KSTR = kAttKeyStreams;   // key streams per workgroup
 
 // One gather item: 32 dims of one key's K and V row, as raw bytes of either
 // the pool format (KV) or the window-ring format (ACT); kind says which.
@@ -111,8 +110,8 @@ __device__ __forceinline__ const Seg<SD> &as_seg(const uint4 (&u)[RW]) {
   return *reinterpret_cast<const Seg<SD> *>(&u[0]);
 }
 
-// HG: head groups (waves per stream); NTW: 16-head tiles per wave.
-template <int ACT, int KV, int HG, int NTW>
+// HG: head groups (waves per stream); NTW: 16-head tiles per wave; KSTR: key streams.
+template <int ACT, int KV, int HG, int NTW, int KSTR>
 __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs a) {
   using CT = typename ComputeT<KV>::type;
   constexpr int NT = HG * KSTR * 64;
@@ -146,25 +145,45 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
   const int32_t *trow = a.topk + static_cast<int64_t>(qi) * a.k;
   const int tid = threadIdx.x;
 
-  // ---------------- 1. resolve every key of the split once
-  for (int i = tid; i < n_keys; i += NT) {
+  // ---------------- 1. resolve every key of the split once: all Top-K reads
+  // of a thread first, then all of its block-table reads (two round trips)
+  constexpr int kMaxPer = (kAttMaxSplitKeys + NT - 1) / NT;
+  int jv[kMaxPer];
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = tid + u * NT;
+    jv[u] = -1;
+    if (i < n_keys) {
+      const int b = b_begin + i / kKeyBlock, kk = i % kKeyBlock;
+      if (b < a.n_sparse_blocks) {
+        const int slot = b * kKeyBlock + kk;
+        jv[u] = slot < a.k ? trow[slot] : -1;
+      }
+    }
+  }
+  int pv[kMaxPer];
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int j = jv[u];
+    pv[u] = (j >= 0 && j < n_vis) ? bt[j >> 6] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = tid + u * NT;
+    if (i >= n_keys) continue;
     const int b = b_begin + i / kKeyBlock, kk = i % kKeyBlock;
     int valid = 0;
     int32_t row = 0;
     if (b < a.n_sparse_blocks) {
-      const int slot = b * kKeyBlock + kk;
-      const int j = slot < a.k ? trow[slot] : -1;
+      const int j = jv[u], pp = pv[u];
       if (j >= 0) {
         if (j >= n_vis) {
           flag_error(a.err, ERR_TOPK);
+        } else if (pp >= 0 && pp < a.pool_pages) {
+          valid = 1;
+          row = pp * kPage + (j & 63);
         } else {
-          const int pp = bt[j >> 6];
-          if (pp >= 0 && pp < a.pool_pages) {
-            valid = 1;
-            row = pp * kPage + (j & 63);
-          } else {
-            flag_error(a.err, ERR_PAGE);
-          }
+          flag_error(a.err, ERR_PAGE);
         }
       }
     } else {
@@ -472,15 +491,23 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   else reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(out);
 }
 
-template <int ACT, int KV>
-void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s) {
+template <int ACT, int KV, int KSTR>
+void launch_attend_k(const AttendArgs &a, int n_wg, hipStream_t s) {
   switch (a.H) {
-    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(1 * KSTR * 64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(2 * KSTR * 64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1, KSTR>), dim3(n_wg), dim3(1 * KSTR * 64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1, KSTR>), dim3(n_wg), dim3(2 * KSTR * 64), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1, KSTR>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2, KSTR>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
     default: break;
   }
+}
+
+template <int ACT, int KV>
+void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s) {
+  // decode: one block per split (latency-bound); a prefill chunk walks all of a
+  // query's blocks in one workgroup, two blocks per round
+  if (a.chunk && KV != DT_F32) launch_attend_k<ACT, KV, kAttChunkKeyStreams>(a, n_wg, s);
+  else launch_attend_k<ACT, KV, kAttKeyStreams>(a, n_wg, s);
 }
 
 }  // namespace

@@ -54,6 +54,7 @@ constexpr int kSlotsPerThread = kPage / (kThreads / 64);   // 16
 template <int ACT, int KV>
 __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const CompressArgs a) {
   __shared__ float kb_s[kPage][kD];
+  __shared__ float p_s[kD][kDI];   // indexer projection, staged once
   __shared__ float red[16];
 
   // ---- which (sequence, page) this workgroup owns
@@ -77,6 +78,15 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
 
   const int t = threadIdx.x, dp = t & 63, eb = t >> 6;
   const int d0 = 2 * dp;
+  if (a.write_idx) {
+    // 8 independent 16-byte loads per thread
+    const float4 *src = reinterpret_cast<const float4 *>(a.proj);
+    float4 tmp[kD * kDI / 4 / kThreads];
+#pragma unroll
+    for (int u = 0; u < kD * kDI / 4 / kThreads; ++u) tmp[u] = src[u * kThreads + t];
+#pragma unroll
+    for (int u = 0; u < kD * kDI / 4 / kThreads; ++u) reinterpret_cast<float4 *>(&p_s[0][0])[u * kThreads + t] = tmp[u];
+  }
 
   float kk[kSlotsPerThread][2], vv[kSlotsPerThread][2];
 #pragma unroll
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   if (a.write_idx) {
     __syncthreads();
     for (int d = 0; d < kD; ++d) {
-      const float p = a.proj[d * kDI + c];
+      const float p = p_s[d][c];
 #pragma unroll
       for (int m = 0; m < kSlotsPerThread; ++m) ki[m] += kb_s[eb + 4 * m][d] * p;
     }

@@ -90,9 +90,15 @@ size_t idx_decode_bytes(int nq, int64_t s_stride) {
   return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) * 4 +
          align_up(static_cast<size_t>(nq) * max_slices_for(s_stride) * 4, 256);
 }
-size_t idx_chunk_bytes(int nq, int64_t s_stride, int64_t m_stride) {
-  return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) + align_up(static_cast<size_t>(nq) * m_stride * 4, 256);
+// sampled scores, tau, per-tile counts, per-tile candidate regions, fallback rows
+size_t idx_chunk_bytes(int nq, int64_t ss_stride, int64_t fb_stride) {
+  const int64_t tiles = (fb_stride + 255) / 256;
+  return align_up(static_cast<size_t>(nq) * ss_stride * 4, 256) + align_up(static_cast<size_t>(nq) * 4, 256) +
+         align_up(static_cast<size_t>(nq) * tiles * 4, 256) +
+         2 * align_up(static_cast<size_t>(nq) * tiles * kChunkTileCand * 4, 256) +
+         align_up(static_cast<size_t>(nq) * fb_stride * 4, 256);
 }
+
 size_t attend_bytes(int nq, int n_splits, int H) {
   return align_up(static_cast<size_t>(nq) * n_splits * H * kD * 4, 256) + align_up(static_cast<size_t>(nq) * n_splits * H * 2 * 4, 256);
 }
@@ -202,7 +208,8 @@ size_t csa_workspace_size(const csa_config *cfg, int32_t max_queries, int32_t ma
   const int nq_dec = std::min<int>(max_queries, kIdxMaxQ);
   const size_t a = idx_decode_bytes(nq_dec, s_dec);
   const int64_t s_chunk = (E + 63) / 64 * 64;
-  const size_t b = max_queries > 1 ? idx_chunk_bytes(max_queries, s_chunk, s_chunk) : 0;
+  const int64_t ss_chunk = (E / kChunkSample + 255) / 256 * 256 + 256;
+  const size_t b = max_queries > 1 ? idx_chunk_bytes(max_queries, ss_chunk, s_chunk) : 0;
   const size_t c = attend_bytes(std::min<int>(max_queries, kAttMaxQ), kMaxSplits, cfg->q_heads);
   return kHead + std::max(a, std::max(b, c)) + 1024;
 }
@@ -399,31 +406,33 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
 
   if (is_chunk(n_q, q_seq, q_pos)) {
     const int pos0 = q_pos[0];
-    const int n_min = (pos0 + 1) / c.ratio, n_max = (pos0 + n_q) / c.ratio;
-    int glog2 = 0;
-    while (glog2 < 4 && (n_min >> (glog2 + 1)) >= 2 * k) ++glog2;
-    const int64_t s_stride = (static_cast<int64_t>(n_max) + 63) / 64 * 64;
-    const int64_t m_stride = (s_stride + (1 << glog2) - 1) >> glog2;
-    const size_t need = idx_chunk_bytes(n_q, s_stride, m_stride);
+    const int n_max = (pos0 + n_q) / c.ratio;
+    const int64_t ss_stride = (static_cast<int64_t>(n_max) / kChunkSample + 255) / 256 * 256 + 256;
+    const int64_t fb_stride = (static_cast<int64_t>(n_max) + 63) / 64 * 64;
+    const size_t need = idx_chunk_bytes(n_q, ss_stride, fb_stride);
     if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for a %d-token chunk (%zu > %zu bytes)", n_q, need, h->scratch_bytes);
-    IdxChunkScanArgs s{};
+    char *p = h->scratch;
+    IdxChunkArgs s{};
+    s.ss = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * ss_stride * 4, 256);
+    const int64_t tiles = (fb_stride + 255) / 256;
+    s.tau = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * 4, 256);
+    s.cnt = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * 4, 256);
+    s.cand_s = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 4, 256);
+    s.cand_j = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 4, 256);
+    s.fb_rows = reinterpret_cast<float *>(p);
     s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale;
     s.bt_row = h->buf.block_table + static_cast<int64_t>(q_seq[0]) * c.max_pages_per_seq;
-    s.q_idx = q_idx; s.w_idx = w_idx;
-    s.S = reinterpret_cast<float *>(h->scratch);
-    s.M = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(n_q) * s_stride * 4, 256));
-    s.err = h->err;
-    s.pool_pages = c.pool_pages; s.h_i = c.idx_heads; s.s_stride = static_cast<int32_t>(s_stride);
-    s.m_stride = static_cast<int32_t>(m_stride); s.n_tok = n_q; s.pos0 = pos0; s.r = c.ratio; s.glog2 = glog2;
+    s.q_idx = q_idx; s.w_idx = w_idx; s.topk = topk; s.err = h->err;
+    s.pool_pages = c.pool_pages; s.h_i = c.idx_heads; s.ss_stride = static_cast<int32_t>(ss_stride);
+    s.fb_stride = static_cast<int32_t>(fb_stride); s.n_tok = n_q; s.pos0 = pos0; s.r = c.ratio; s.k = k;
+    s.m_s = std::max(1, (2 * k + kChunkSample - 1) / kChunkSample);
     s.n_etiles = (n_max + 255) / 256;
+    s.n_stiles = (n_max / kChunkSample + 255) / 256;
+    s.kv_dtype = kv; s.act_dtype = act;
     record(h, stream, true);
-    if (n_max > 0) launch_idx_chunk_scan(s, kv, act, stream);
+    launch_idx_chunk(s, kv, act, stream);
     record(h, stream, false);
-    IdxChunkSelectArgs sel{};
-    sel.S = s.S; sel.M = s.M; sel.topk = topk; sel.err = h->err;
-    sel.s_stride = s.s_stride; sel.m_stride = s.m_stride; sel.n_tok = n_q; sel.pos0 = pos0; sel.r = c.ratio;
-    sel.glog2 = glog2; sel.k = k;
-    launch_idx_chunk_select(sel, stream);
+    launch_idx_chunk_select(s, stream);
   } else {
     for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
       const int nq = std::min(kIdxMaxQ, n_q - g0);

@@ -91,29 +91,32 @@ struct IdxFinalArgs {
 };
 
 // chunk (prefill) index: all queries of one sequence at consecutive positions
-struct IdxChunkScanArgs {
+constexpr int kChunkSample = 16;     // the sample GEMM scores entries 16m + 15
+constexpr int kChunkCandCap = 4096;  // candidates one select keeps in LDS
+constexpr int kChunkTileCand = 64;   // candidate slots per (query, 256-entry tile)
+
+struct IdxChunkArgs {
   const void *kidx;
   const float *kidx_scale;
   const int32_t *bt_row;   // block-table row of the sequence
-  const void *q_idx;
-  const float *w_idx;
-  float *S, *M;
+  const void *q_idx;       // [n_tok][H_I][D_I]
+  const float *w_idx;      // [n_tok][H_I]
+  float *ss;               // [n_tok][ss_stride] sampled scores
+  float *tau;              // [n_tok] thresholds
+  int32_t *cnt;            // [n_tok][n_etiles] candidates per (query, entry tile)
+  float *cand_s;           // [n_tok][n_etiles][kChunkTileCand]
+  int32_t *cand_j;         // [n_tok][n_etiles][kChunkTileCand]
+  float *fb_rows;          // [n_tok][fb_stride] full rows for the exact fallback
+  int32_t *topk;           // [n_tok][k]
   uint32_t *err;
-  int32_t pool_pages, h_i, s_stride, m_stride, n_tok, pos0, r, glog2, n_etiles;
-};
-
-struct IdxChunkSelectArgs {
-  const float *S, *M;
-  int32_t *topk;
-  uint32_t *err;
-  int32_t s_stride, m_stride, n_tok, pos0, r, glog2, k;
+  int32_t pool_pages, h_i, ss_stride, fb_stride, n_tok, pos0, r, k, m_s, n_etiles, n_stiles, kv_dtype, act_dtype;
 };
 
 void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s);
 void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s);
 void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
-void launch_idx_chunk_scan(const IdxChunkScanArgs &a, int kv, int act, hipStream_t s);
-void launch_idx_chunk_select(const IdxChunkSelectArgs &a, hipStream_t s);
+void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s);
+void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s);
 
 // ------------------------------------------------------------------ attend
 
@@ -125,7 +128,8 @@ struct AttQuery {
 };
 
 constexpr int kAttMaxSplitKeys = 2304;   // keys one workgroup resolves up front (36 blocks)
-constexpr int kAttKeyStreams = 1;        // 64-key blocks a workgroup processes per round
+constexpr int kAttKeyStreams = 1;        // 64-key blocks a decode workgroup processes per round
+constexpr int kAttChunkKeyStreams = 1;   // the same for a prefill chunk (one workgroup per query)
 constexpr int kAttMaxSplits = 40;        // splits per query combined by the merge kernel
 
 struct AttendArgs {

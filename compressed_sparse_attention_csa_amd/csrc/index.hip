@@ -25,6 +25,8 @@
 //                  head) pairs as the 16 rows of each tile, so every lane's 4
 //                  accumulators are the 4 heads of one (query, entry) score.
 //   chunk select - per query: tau from its group maxima, filter, exact select.
+#include <type_traits>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -354,6 +356,33 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   return true;
 }
 
+
+// In-place inclusive prefix sum of arr[1..n] in LDS (arr[0] = 0 is left as is):
+// thread-contiguous chunks, wave scan of chunk totals, block combine.
+__device__ void block_prefix_sum(int *arr, int n, int *wsum) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
+  const int span = (n + bd - 1) / bd;
+  const int i0 = 1 + min(n, t * span), i1 = 1 + min(n, t * span + span);
+  int mine = 0;
+  for (int i = i0; i < i1; ++i) mine += arr[i];
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum[i];
+  int run = incl - mine;
+  for (int i = i0; i < i1; ++i) {
+    run += arr[i];
+    arr[i] = run;
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------ decode scan
 
 template <int ACT, int KV>
@@ -562,6 +591,7 @@ __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
   __shared__ int soff[kMaxSlices + 1];
   __shared__ float red[16];
   __shared__ int sh[4];
+  __shared__ int wsum_f[16];
   const int qi = blockIdx.x, tid = threadIdx.x;
   const int N = a.n_vis[qi], k = a.k;
   int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
@@ -575,9 +605,7 @@ __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
   for (int i = tid; i < ns; i += blockDim.x) soff[i + 1] = cnts[i];
   if (tid == 0) soff[0] = 0;
   __syncthreads();
-  if (tid == 0)
-    for (int i = 0; i < ns; ++i) soff[i + 1] += soff[i];
-  __syncthreads();
+  block_prefix_sum(soff, ns, wsum_f);
   const int c = soff[ns];
   bool done = false;
   if (c >= k && c <= kSelCap) {
@@ -617,68 +645,58 @@ __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ chunk scan (prefill GEMM)
+// ------------------------------------------------------------------ chunk (prefill) index
+//
+// Queries of one sequence at consecutive positions share the indexer keys, so
+// scores are an MFMA GEMM: tiles of 64 queries x 256 entries, the 16 rows of
+// each MFMA tile being 4 queries x 4 indexer heads, so each lane's 4
+// accumulators are the 4 heads of one (query, entry) pair.
+// The full score matrix is never written. A sample GEMM over every 16th entry
+// gives each query a threshold tau (about its (2k/16)-th best sample, so about
+// 2k entries of the row score >= tau); the main GEMM keeps only scores >= tau.
+// The select kernel checks it got at least k of them (otherwise it recomputes
+// the row and selects exactly), finds the exact k-th key by binning plus an
+// exact rank inside one bin, and orders the output with an LDS bitmap.
 
 constexpr int kCQ = 64;     // queries per tile
 constexpr int kCE = 256;    // entries per tile
 constexpr int kLdsRow = kDI + 8;
+constexpr int kWgCand = kChunkTileCand;
+constexpr int kChunkTilesPerWg = 1;   // entry tiles one workgroup walks (next tile prefetched)
+constexpr int kBitmapWords = 8192;
+constexpr int kMaxChunkTiles = kBitmapWords * 32 / kCE;   // 1024 entry tiles (262,144 entries)
 
-template <int ACT, int KV>
-__global__ __launch_bounds__(256) void idx_chunk_scan_kernel(const IdxChunkScanArgs a) {
+template <int ACT, int KV, int MODE>
+__global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs a) {
   using CT = typename ComputeT<KV>::type;
   constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
+  constexpr bool SAMPLE = MODE == 0;
+  constexpr int kChunkElems = 16 / KE;                 // elements per 16-byte load
+  constexpr int kChunksPerRow = kDI / kChunkElems;
+  constexpr int kLoads = kCE * kChunksPerRow / 256;    // 16-byte loads per thread per tile
   __shared__ CT kt[kCE][kLdsRow];
-  __shared__ float psc[kCE / kPage];
+  __shared__ float rsc[kCE];
+  __shared__ int lcnt[SAMPLE ? 1 : kCQ];
 
-  const int qt = blockIdx.x / a.n_etiles, et = blockIdx.x % a.n_etiles;
-  const int q0 = qt * kCQ, e0 = et * kCE;
+  const int n_et = SAMPLE ? a.n_stiles : a.n_etiles;
+  const int n_eg = (n_et + kChunkTilesPerWg - 1) / kChunkTilesPerWg;   // entry-tile groups
+  const int qt = blockIdx.x / n_eg, eg = blockIdx.x % n_eg;
+  const int q0 = qt * kCQ;
   const int qlast = min(a.n_tok, q0 + kCQ) - 1;
   const int nvis_max = (a.pos0 + qlast + 1) / a.r;
-  if (e0 >= nvis_max) return;
-
-  // ---- stage the entry tile (4 pages) into LDS in the compute type
-  {
-    constexpr int kChunkElems = 16 / KE;   // elements per 16-byte load
-    constexpr int kChunksPerRow = kDI / kChunkElems;
-    const char *kbase = reinterpret_cast<const char *>(a.kidx);
-    for (int i = threadIdx.x; i < kCE * kChunksPerRow; i += blockDim.x) {
-      const int le = i / kChunksPerRow, ch = i % kChunksPerRow;
-      const int e = e0 + le;
-      const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
-      const bool ok = pp >= 0 && pp < a.pool_pages;
-      CT *dst = &kt[le][ch * kChunkElems];
-      if (ok) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(kbase + ((static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI + ch * kChunkElems) * KE);
-        if constexpr (KV == DT_FP8) {
-          const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bf16x2_t lo = fp8x2_to_bf16<false>(wds[q]), hi = fp8x2_to_bf16<true>(wds[q]);
-            dst[4 * q + 0] = lo[0]; dst[4 * q + 1] = lo[1]; dst[4 * q + 2] = hi[0]; dst[4 * q + 3] = hi[1];
-          }
-        } else {
-          *reinterpret_cast<uint4 *>(dst) = u;
-        }
-      } else {
-        for (int q = 0; q < kChunkElems; ++q) dst[q] = CT(0.f);
-      }
-    }
-    if (threadIdx.x < kCE / kPage) {
-      const int e = e0 + threadIdx.x * kPage;
-      const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
-      const bool ok = pp >= 0 && pp < a.pool_pages;
-      if (e < nvis_max && !ok) flag_error(a.err, ERR_PAGE);
-      psc[threadIdx.x] = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
-    }
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  auto entry_of = [&](int m) { return SAMPLE ? m * kChunkSample + (kChunkSample - 1) : m; };
+  const int et_begin = eg * kChunkTilesPerWg;
+  int et_end = min(n_et, et_begin + kChunkTilesPerWg);
+  while (et_end > et_begin && entry_of((et_end - 1) * kCE) >= nvis_max) --et_end;
+  if (et_end <= et_begin) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
   const int qw = q0 + 16 * w;   // the wave's first query
+  const char *kbase = reinterpret_cast<const char *>(a.kidx);
 
   // A operands: (query, head) pairs as rows: row = 4*q + h
   Frag<CT> qa[4][2];
-  float wq[4][4];
+  float wq[4][4], tq[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int qq = qw + 4 * mt + (col >> 2), hh = col & 3;
@@ -691,96 +709,343 @@ __global__ __launch_bounds__(256) void idx_chunk_scan_kernel(const IdxChunkScanA
     const int qo = qw + 4 * mt + g;   // the query this lane scores
 #pragma unroll
     for (int v = 0; v < 4; ++v) wq[mt][v] = (qo < a.n_tok && v < a.h_i) ? a.w_idx[qo * a.h_i + v] : 0.f;
+    tq[mt] = INFINITY;
+    if constexpr (!SAMPLE) tq[mt] = qo < a.n_tok ? a.tau[qo] : INFINITY;
   }
 
-  const int glog2 = a.glog2, G = 1 << glog2;
+  // register prefetch of one tile's indexer keys: all loads of a thread in flight together
+  uint4 raw[kLoads];
+  float rscale = 1.f;
+  auto load_tile = [&](int et) {
+    const int m0 = et * kCE;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int i = u * 256 + tid;
+      const int le = i / kChunksPerRow, ch = i % kChunksPerRow;
+      const int e = entry_of(m0 + le);
+      const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
+      raw[u] = (pp >= 0 && pp < a.pool_pages)
+                   ? *reinterpret_cast<const uint4 *>(kbase + ((static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI + ch * kChunkElems) * KE)
+                   : make_uint4(0, 0, 0, 0);
+    }
+    const int e = entry_of(m0 + tid);
+    const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
+    const bool ok = pp >= 0 && pp < a.pool_pages;
+    if (e < nvis_max && !ok) flag_error(a.err, ERR_PAGE);
+    rscale = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
+  };
+  auto commit_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int i = u * 256 + tid;
+      const int le = i / kChunksPerRow, ch = i % kChunksPerRow;
+      CT *dst = &kt[le][ch * kChunkElems];
+      if constexpr (KV == DT_FP8) {
+        const uint32_t wds[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x2_t lo = fp8x2_to_bf16<false>(wds[q]), hi = fp8x2_to_bf16<true>(wds[q]);
+          dst[4 * q + 0] = lo[0]; dst[4 * q + 1] = lo[1]; dst[4 * q + 2] = hi[0]; dst[4 * q + 3] = hi[1];
+        }
+      } else {
+        *reinterpret_cast<uint4 *>(dst) = raw[u];
+      }
+    }
+    rsc[tid] = rscale;
+  };
+
+  load_tile(et_begin);
+  for (int et = et_begin; et < et_end; ++et) {
+    const int m0 = et * kCE;
+    __syncthreads();                 // previous tile's LDS reads (and flush) are done
+    commit_tile();
+    if constexpr (!SAMPLE) {
+      if (tid < kCQ) lcnt[tid] = 0;
+    }
+    __syncthreads();
+    if (et + 1 < et_end) load_tile(et + 1);   // in flight during this tile's MFMAs
+
 #pragma unroll 1
-  for (int pg = 0; pg < kCE / kPage; ++pg) {
-    f32x4_t acc[4][4];
+    for (int pg = 0; pg < kCE / 64; ++pg) {
+      f32x4_t acc[4][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int le = pg * kPage + nt * 16 + col;
-      Frag<CT> kb[2];
+      for (int nt = 0; nt < 4; ++nt) {
+        const int le = pg * 64 + nt * 16 + col;
+        Frag<CT> kb[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const CT *src = &kt[le][16 * g + 8 * c];
-        if constexpr (KV == DT_F32) {
-          kb[c] = LoadFrag<DT_F32, float>::load(src);
-        } else {
-          kb[c] = LoadFrag<DT_BF16, __bf16>::load(src);
+        for (int c = 0; c < 2; ++c) {
+          const CT *src = &kt[le][16 * g + 8 * c];
+          if constexpr (KV == DT_F32) kb[c] = LoadFrag<DT_F32, float>::load(src);
+          else kb[c] = LoadFrag<DT_BF16, __bf16>::load(src);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc[mt][nt] = mma(qa[mt][0], kb[0], acc[mt][nt]);
+          acc[mt][nt] = mma(qa[mt][1], kb[1], acc[mt][nt]);
         }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        acc[mt][nt] = mma(qa[mt][0], kb[0], acc[mt][nt]);
-        acc[mt][nt] = mma(qa[mt][1], kb[1], acc[mt][nt]);
+        const int qo = qw + 4 * mt + g;
+        const int nvis = (a.pos0 + qo + 1) / a.r;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int le = pg * 64 + nt * 16 + col;
+          const int e = entry_of(m0 + le);
+          float s = 0.f;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s += wq[mt][v] * fmaxf(acc[mt][nt][v], 0.f);
+          s *= rsc[le];
+          const bool vis = qo < a.n_tok && e < nvis;
+          if constexpr (SAMPLE) {
+            if (vis) a.ss[static_cast<int64_t>(qo) * a.ss_stride + m0 + le] = s;
+          } else {
+            if (vis && s >= tq[mt]) {
+              // this (query, entry tile) owns candidate slots [0, kWgCand) of its region
+              const int ql = 16 * w + 4 * mt + g;
+              const int slot = atomicAdd(&lcnt[ql], 1);
+              if (slot < kWgCand) {
+                const int64_t o = (static_cast<int64_t>(qo) * a.n_etiles + et) * kWgCand + slot;
+                a.cand_s[o] = s;
+                a.cand_j[o] = e;
+              }
+            }
+          }
+        }
       }
     }
-    const float sc = psc[pg];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int qo = qw + 4 * mt + g;
-      const int nvis = (a.pos0 + qo + 1) / a.r;
-      float *Srow = a.S + static_cast<int64_t>(qo) * a.s_stride;
-      float *Mrow = a.M + static_cast<int64_t>(qo) * a.m_stride;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int e = e0 + pg * kPage + nt * 16 + col;
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s += wq[mt][v] * fmaxf(acc[mt][nt][v], 0.f);
-        const bool vis = qo < a.n_tok && e < nvis;
-        s = vis ? s * sc : -1.f;
-        if (vis) Srow[e] = s;
-        float m = s;
-        for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (vis && (col & (G - 1)) == 0) Mrow[e >> glog2] = m;
-      }
+    if constexpr (!SAMPLE) {
+      __syncthreads();
+      if (tid < kCQ && q0 + tid < a.n_tok) a.cnt[static_cast<int64_t>(q0 + tid) * a.n_etiles + et] = lcnt[tid];
     }
   }
 }
 
-// ------------------------------------------------------------------ chunk select
-
-__global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkSelectArgs a) {
-  __shared__ uint64_t keys[8192];
-  __shared__ int sel[CSA_MAX_TOPK];
+// Per query: tau from its sampled scores.
+__global__ __launch_bounds__(256) void idx_chunk_tau_kernel(const IdxChunkArgs a) {
   __shared__ int hist[kTauBins];
   __shared__ float red[16];
   __shared__ int sh[4];
   const int qi = blockIdx.x;
-  const int N = (a.pos0 + qi + 1) / a.r, k = a.k;
-  int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
-  if (N <= k) {
-    for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < N ? i : -1;
-    return;
-  }
-  const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
-  const float *Mrow = a.M + static_cast<int64_t>(qi) * a.m_stride;
-  const int glog2 = a.glog2;
-  const int nG = (N + (1 << glog2) - 1) >> glog2;
+  const int N = (a.pos0 + qi + 1) / a.r;
+  const int ns = N / kChunkSample;          // visible samples: entries 16m + 15 < N
   float tau = 0.f;
-  if (nG > k) tau = tau_lower_bound([&](int i) { return Mrow[i]; }, nG, k, hist, red, sh);
-  if (threadIdx.x == 0) sh[3] = 0;
+  if (ns > a.m_s) {
+    const float *row = a.ss + static_cast<int64_t>(qi) * a.ss_stride;
+    tau = tau_lower_bound([&](int i) { return row[i]; }, ns, a.m_s, hist, red, sh);
+  }
+  if (threadIdx.x == 0) a.tau[qi] = tau;
+}
+
+// Exact k-th largest key of c keys in LDS (c >= k): linear score bins, then an
+// exact rank inside the bin holding it. Returns false if that bin is too full.
+__device__ bool kth_key_binned(const uint64_t *keys, int c, int k, int *hist, float *red, int *sh, uint64_t *bin_keys,
+                               uint64_t *kth_out) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = t; i < c; i += bd) {
+    const float v = __uint_as_float(static_cast<uint32_t>(keys[i] >> 32));
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  lo = block_reduce_min(lo, red);
+  hi = block_reduce_max(hi, red);
+  const float sc = hi > lo ? static_cast<float>(kSelBins - 1) / (hi - lo) : 0.f;
+  auto bin_of = [&](uint64_t key) {
+    return min(kSelBins - 1, static_cast<int>((__uint_as_float(static_cast<uint32_t>(key >> 32)) - lo) * sc));
+  };
+  for (int i = t; i < kSelBins; i += bd) hist[i] = 0;
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    const float s = Srow[e];
-    if (s >= tau) {
-      const int p = atomicAdd(&sh[3], 1);
-      if (p < kSelCap) keys[p] = score_key(s, e);
+  for (int i = t; i < c; i += bd) atomicAdd(&hist[bin_of(keys[i])], 1);
+  __syncthreads();
+  constexpr int kMaxPer = kSelBins / 256;
+  const int per = kSelBins / bd;
+  int cnt[kMaxPer], tot = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    cnt[j] = j < per ? hist[kSelBins - 1 - per * t - j] : 0;
+    tot += cnt[j];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __shared__ int wsum3[16];
+  if (lane == 63) wsum3[w] = incl;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum3[i];
+  const int excl = incl - tot;
+  if (excl < k && incl >= k) {
+    int cum = excl;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      if (j < per && cum + cnt[j] >= k) { sh[0] = kSelBins - 1 - per * t - j; sh[1] = cum; break; }
+      cum += cnt[j];
     }
   }
   __syncthreads();
-  const int c = sh[3];
-  if (c <= kSelCap) {
-    select_sorted_and_write(keys, c, k, sel, out);
-  } else {
-    if (threadIdx.x == 0) flag_error(a.err, ERR_FALLBACK);
-    select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out);
+  const int bstar = sh[0], need = k - sh[1];
+  const int m = hist[bstar];
+  if (m > kRankCap) return false;
+  if (t == 0) sh[2] = 0;
+  __syncthreads();
+  for (int i = t; i < c; i += bd)
+    if (bin_of(keys[i]) == bstar) bin_keys[atomicAdd(&sh[2], 1)] = keys[i];
+  __syncthreads();
+  for (int i = t; i < m; i += bd) {
+    const uint64_t x = bin_keys[i];
+    int r = 0;
+    for (int j = 0; j < m; ++j) r += bin_keys[j] > x;
+    if (r == need - 1) sh[3] = i;
+  }
+  __syncthreads();
+  *kth_out = bin_keys[sh[3]];
+  return true;
+}
+
+__device__ __forceinline__ float chunk_q(const IdxChunkArgs &a, int q, int h, int d) {
+  const int64_t i = (static_cast<int64_t>(q) * a.h_i + h) * kDI + d;
+  return a.act_dtype == DT_F32 ? reinterpret_cast<const float *>(a.q_idx)[i]
+                               : bf16_to_f32(reinterpret_cast<const uint16_t *>(a.q_idx)[i]);
+}
+__device__ __forceinline__ float chunk_k(const IdxChunkArgs &a, int pp, int slot, int d) {
+  const int64_t i = (static_cast<int64_t>(pp) * kPage + slot) * kDI + d;
+  if (a.kv_dtype == DT_F32) return reinterpret_cast<const float *>(a.kidx)[i];
+  if (a.kv_dtype == DT_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t *>(a.kidx)[i]);
+  return fp8x2_to_f32<false>(reinterpret_cast<const uint8_t *>(a.kidx)[i])[0];
+}
+
+__global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArgs a) {
+  __shared__ uint64_t keys[kChunkCandCap];
+  __shared__ uint64_t bin_keys[kRankCap];
+  __shared__ uint32_t bitmap[kBitmapWords];
+  __shared__ int hist[kSelBins];
+  __shared__ int sel[CSA_MAX_TOPK];
+  __shared__ float red[16];
+  __shared__ int sh[4];
+  __shared__ int wsum[16];
+  __shared__ int toff[kMaxChunkTiles + 1];
+  const int qi = blockIdx.x, tid = threadIdx.x, bd = blockDim.x, lane = tid & 63, w = tid >> 6;
+  const int N = (a.pos0 + qi + 1) / a.r, k = a.k;
+  int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
+  if (N <= k) {
+    for (int i = tid; i < k; i += bd) out[i] = i < N ? i : -1;
+    return;
+  }
+  // per-tile candidate counts of this query -> offsets (tiles past its visible range hold none)
+  const int n_tiles = (N + kCE - 1) / kCE;
+  const int32_t *tc = a.cnt + static_cast<int64_t>(qi) * a.n_etiles;
+  if (tid == 0) { toff[0] = 0; sh[3] = 0; }
+  __syncthreads();
+  for (int i = tid; i < n_tiles; i += bd) {
+    const int v = tc[i];
+    if (v > kWgCand) sh[3] = 1;          // a tile overflowed its slots
+    toff[i + 1] = min(v, kWgCand);
+  }
+  __syncthreads();
+  block_prefix_sum(toff, n_tiles, wsum);
+  const int c = toff[n_tiles];
+  bool done = false;
+  if (sh[3] == 0 && c >= k && c <= kChunkCandCap && N <= kBitmapWords * 32) {
+    const float *cs = a.cand_s + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
+    const int32_t *cj = a.cand_j + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
+    constexpr int kPer = kChunkCandCap / 512;
+    float ts[kPer];
+    int tj[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * 512 + tid;
+      ts[u] = 0.f;
+      tj[u] = 0;
+      if (i < c) {
+        int lo = 0, hi = n_tiles;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (toff[mid] <= i) lo = mid; else hi = mid;
+        }
+        const int64_t o = static_cast<int64_t>(lo) * kWgCand + (i - toff[lo]);
+        ts[u] = cs[o];
+        tj[u] = cj[o];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = u * 512 + tid;
+      if (i < c) keys[i] = score_key(ts[u], tj[u]);
+    }
+    const int nwords = (N + 31) >> 5;
+    for (int i = tid; i < nwords; i += bd) bitmap[i] = 0u;
+    __syncthreads();
+    uint64_t kth = 0;
+    if (kth_key_binned(keys, c, k, hist, red, sh, bin_keys, &kth)) {
+      for (int i = tid; i < c; i += bd)
+        if (keys[i] >= kth) {
+          const int j = key_index(keys[i]);
+          atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        }
+      __syncthreads();
+      // ascending output: thread-contiguous word ranges, popcount prefix
+      const int span = (nwords + bd - 1) / bd;
+      const int w0 = min(nwords, tid * span), w1 = min(nwords, w0 + span);
+      int mine = 0;
+      for (int i = w0; i < w1; ++i) mine += __popc(bitmap[i]);
+      int incl = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      for (int i = 0; i < w; ++i) incl += wsum[i];
+      int pos = incl - mine;
+      for (int i = w0; i < w1; ++i) {
+        uint32_t bits = bitmap[i];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          out[pos++] = i * 32 + b;
+        }
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    // too few or too many candidates, or heavy ties: score the whole row and select exactly
+    if (tid == 0) flag_error(a.err, ERR_FALLBACK);
+    __syncthreads();
+    float *row = a.fb_rows + static_cast<int64_t>(qi) * a.fb_stride;
+    const int t = a.pos0 + qi;
+    (void)t;
+    float qv[CSA_MAX_IDX_HEADS][kDI];
+    float wv[CSA_MAX_IDX_HEADS];
+    for (int h = 0; h < a.h_i; ++h) {
+      wv[h] = a.w_idx[qi * a.h_i + h];
+      for (int d = 0; d < kDI; ++d) qv[h][d] = chunk_q(a, qi, h, d);
+    }
+    for (int e = tid; e < N; e += bd) {
+      const int pp = a.bt_row[e >> 6];
+      float sres = -1.f;
+      if (pp >= 0 && pp < a.pool_pages) {
+        const float sc = a.kv_dtype == DT_FP8 ? a.kidx_scale[pp] : 1.f;
+        float acc = 0.f;
+        for (int h = 0; h < a.h_i; ++h) {
+          float dot = 0.f;
+          for (int d = 0; d < kDI; ++d) dot += qv[h][d] * chunk_k(a, pp, e & 63, d);
+          acc += wv[h] * fmaxf(dot, 0.f);
+        }
+        sres = acc * sc;
+      }
+      row[e] = sres;
+    }
+    __syncthreads();
+    select_and_write([&](int i) { return score_key(row[i], i); }, N, k, sel, hist, sh, out);
   }
 }
 
@@ -806,19 +1071,25 @@ void launch_idx_final(const IdxFinalArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(idx_final_kernel, dim3(a.n_q), dim3(512), 0, s, a);
 }
 
-void launch_idx_chunk_scan(const IdxChunkScanArgs &a, int kv, int act, hipStream_t s) {
+void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s) {
   const int n_qt = (a.n_tok + kCQ - 1) / kCQ;
-  const int n_wg = n_qt * a.n_etiles;
-  if (n_wg <= 0) return;
-  if (kv == DT_F32 && act == DT_F32)
-    hipLaunchKernelGGL((idx_chunk_scan_kernel<DT_F32, DT_F32>), dim3(n_wg), dim3(256), 0, s, a);
-  else if (kv == DT_BF16 && act == DT_BF16)
-    hipLaunchKernelGGL((idx_chunk_scan_kernel<DT_BF16, DT_BF16>), dim3(n_wg), dim3(256), 0, s, a);
-  else if (kv == DT_FP8 && act == DT_BF16)
-    hipLaunchKernelGGL((idx_chunk_scan_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(256), 0, s, a);
+  auto gemm = [&](auto mode_tag, int n_et) {
+    constexpr int M = decltype(mode_tag)::value;
+    const int n_wg = n_qt * ((n_et + kChunkTilesPerWg - 1) / kChunkTilesPerWg);
+    if (n_wg <= 0) return;
+    if (kv == DT_F32 && act == DT_F32)
+      hipLaunchKernelGGL((idx_chunk_gemm_kernel<DT_F32, DT_F32, M>), dim3(n_wg), dim3(256), 0, s, a);
+    else if (kv == DT_BF16 && act == DT_BF16)
+      hipLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_BF16, M>), dim3(n_wg), dim3(256), 0, s, a);
+    else if (kv == DT_FP8 && act == DT_BF16)
+      hipLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_FP8, M>), dim3(n_wg), dim3(256), 0, s, a);
+  };
+  gemm(std::integral_constant<int, 0>{}, a.n_stiles);
+  hipLaunchKernelGGL(idx_chunk_tau_kernel, dim3(a.n_tok), dim3(256), 0, s, a);
+  gemm(std::integral_constant<int, 1>{}, a.n_etiles);
 }
 
-void launch_idx_chunk_select(const IdxChunkSelectArgs &a, hipStream_t s) {
+void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s) {
   if (a.n_tok <= 0) return;
   hipLaunchKernelGGL(idx_chunk_select_kernel, dim3(a.n_tok), dim3(512), 0, s, a);
 }

@@ -251,6 +251,7 @@ def test_index_chunk_matches_oracle(kv, act):
 def test_index_chunk_short_context():
     # early chunk queries see fewer than k entries
     _index_case("bf16", "bf16", lens=[1000], k=200, chunk=(0, 600))
+    _index_case("fp8", "bf16", lens=[4 * 5000 + 2], k=1024, chunk=(0, 257))
 
 
 # --------------------------------------------------------------------------- attend (isolated)
@@ -514,3 +515,41 @@ def test_graph_replay_matches_eager():
         assert torch.equal(out, out_ref), f"replay {rep}: output differs"
         del junk
     assert cache.read_errors() == 0
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_index_chunk_threshold_fallback_is_exact(kv, act):
+    """Adversarial prefill chunk: only the entries the threshold pass samples
+    (every 16th) carry signal, so the sampled threshold admits fewer than k
+    candidates; the exact full-row fallback must still return the oracle's Top-K."""
+    from gpu_helpers import store_raw_to_torch, write_logical, write_scales
+    r, L, k, n_tok, seed = 4, 4 * 6000, 512, 96, 13
+    cache = make_cache(seed, ratio=r, q_heads=16, window=0, ring_rows=8, max_seqs=1,
+                       max_pages_per_seq=L // r // 64 + 2, pool_pages=L // r // 64 + 3, kv_dtype=kv,
+                       act_dtype=act, max_queries=n_tok, max_k=k)
+    n = L // r
+    x = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_KI, 0, 0), 0, n, 64).double().numpy()
+    mask = (np.arange(n) % 16) == 15
+    x[~mask] *= 1e-3
+    vals, raw = O.store(x, kv)
+    write_logical(cache, cache.kidx, 0, store_raw_to_torch(raw, kv))
+    if kv == "fp8":
+        write_scales(cache, cache.kidx_scale, 0, raw[1])
+    B.csa_seq_set_len(cache.handle, 0, 0, L)
+    q_pos = list(range(L - n_tok, L))
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, n_tok * 4, 64, dtype=TORCH_ACT[act]).view(n_tok, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, n_tok, 4)
+    T = cache.index_topk([0] * n_tok, q_pos, qi.cuda(), w.cuda(), k).cpu().numpy()
+    flags = cache.read_errors()
+    assert flags & B.ERR_FALLBACK, "the adversarial case should take the exact fallback"
+    assert flags & ~B.ERR_FALLBACK == 0
+    q64, w64 = to64(qi), to64(w)
+    for i in range(0, n_tok, 7):
+        N = O.visible_entries(q_pos[i], r)
+        s = O.index_scores(q64[i], w64[i], vals[:N])
+        ok, msg = topk_matches(T[i], O.topk(s, k), s)
+        assert ok, f"token {i}: {msg}"
+
+
+def test_index_chunk_exact_ties():
+    _index_case("bf16", "bf16", lens=[4 * 3000], k=96, dup_keys=True, exact=True, chunk=(0, 130))
