@@ -553,3 +553,65 @@ def test_index_chunk_threshold_fallback_is_exact(kv, act):
 
 def test_index_chunk_exact_ties():
     _index_case("bf16", "bf16", lens=[4 * 3000], k=96, dup_keys=True, exact=True, chunk=(0, 130))
+
+
+# --------------------------------------------------------------------------- ragged serving step
+
+def test_serving_steps_ragged_paged_fp8():
+    """Ragged requests (log-uniform lengths) on a shared paged fp8 pool with a
+    shuffled free list: bulk build, then steps that append one token to every
+    request (compress re-quantises open pages), index and attend; the final step
+    is compared with the oracle run on each request's full raw rows."""
+    seed, r, k, W, H = 17, 4, 128, 32, 16
+    lens = Sy.log_uniform_lengths(seed, 8, 1024, 16384)
+    steps = 3
+    final = [L + steps for L in lens]
+    pages = [(L // r + 63) // 64 + 1 for L in final]
+    max_pages = max(pages)
+    pool = sum(pages) + 3
+    perm = Sy.permutation(seed, pool, salt=11)
+    bt = torch.full((len(lens), max_pages), -1, dtype=torch.int32)
+    off = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = torch.tensor(perm[off:off + p], dtype=torch.int32)
+        off += p
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+    spec = CacheSpec(ratio=r, q_heads=H, idx_heads=4, window=W, ring_rows=W, n_layers=1, max_seqs=len(lens),
+                     max_pages_per_seq=max_pages, pool_pages=pool, kv_dtype="fp8", act_dtype="bf16",
+                     max_queries=len(lens), max_k=k)
+    cache = CsaCache(spec, "cuda", block_table=bt.cuda())
+    P = Sy.proj_matrix(seed, 128, 64)
+    raw = [[raw_rows(seed, kind, 0, b, 0, final[b], "bf16") for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+           for b in range(len(lens))]
+    ids = list(range(len(lens)))
+    cache.compress(0, ids, lens, *(torch.cat([raw[b][a][:lens[b]] for b in ids]).cuda() for a in range(3)), P.cuda())
+    scale = 1 / math.sqrt(128)
+    for st in range(steps):
+        cur = [L + st for L in lens]
+        cache.compress(0, ids, [1] * len(ids), *(torch.cat([raw[b][a][cur[b]:cur[b] + 1] for b in ids]).cuda()
+                                                  for a in range(3)), P.cuda())
+        qpos = [c for c in cur]
+        qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI, 0, st), 0, len(ids) * 4, 64, dtype=torch.bfloat16).view(-1, 4, 64)
+        w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W, 0, st), 0, len(ids), 4)
+        q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, 0, st), 0, len(ids) * H, 128, dtype=torch.bfloat16).view(-1, H, 128)
+        T = cache.index_topk(ids, qpos, qi.cuda(), w.cuda(), k)
+        out = to64(cache.attend(0, ids, qpos, q.cuda(), T, k, scale))
+    assert cache.read_errors() == 0
+    Tg = T.cpu().numpy()
+    for b in ids:
+        K, V, Z = (to64(t) for t in raw[b])
+        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        kis, kbs, vbs = O.store(ki, "fp8")[0], O.store(kb, "fp8")[0], O.store(vb, "fp8")[0]
+        t = final[b] - 1
+        N = O.visible_entries(t, r)
+        s = O.index_scores(to64(qi[b]), to64(w[b]), kis[:N])
+        To = O.topk(s, k)
+        ok, msg = topk_matches(Tg[b], To, s, rel=2e-2)
+        assert ok, f"request {b}: {msg}"
+        ref = O.attend_step(to64(q[b]), To, t, W, scale, kbs, vbs, K, V)
+        assert max_abs(out[b], ref) <= 2e-2, f"request {b}: max-abs {max_abs(out[b], ref)}"
+        # the device pages equal a one-shot quantisation of the same entries
+        n = final[b] // r
+        got = cache.logical(cache.kidx, b, n).cpu().numpy()
+        _, (codes, _) = O.store(ki[:n], "fp8")
+        assert np.mean(got == codes) > 0.99
