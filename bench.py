@@ -61,8 +61,9 @@ def prefill_leg(seed, dev, steps=5):
     """Prefill chunk: 2,048 new tokens appended to a 131,072-token context (bf16,
     r = 4, Top-1024 per query token, W = 128, 64 heads). One step = compress the
     chunk, index (MFMA score GEMM + exact select) and attend all 2,048 tokens.
-    Reports MFMA utilisation of the index GEMM and of the attention kernel from
-    HIP events around their launches."""
+    Reports MFMA utilisation of the index score GEMM (the pass that scores every
+    visible entry; events stamped by the kernel launch itself) and of the
+    attention kernel (events around its launch)."""
     import torch
     from compressed_sparse_attention_csa_amd import accounting as A
     from compressed_sparse_attention_csa_amd import binding as B

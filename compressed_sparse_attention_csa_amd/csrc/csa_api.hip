@@ -131,20 +131,25 @@ bool is_chunk(int n, const int32_t *seq, const int32_t *pos) {
   return true;
 }
 
-void record(csa_cache_t h, hipStream_t s, bool start) {
-  if (!h->profiling) return;
-  if (start) {
-    if (h->events_used + 2 > h->events.size()) {
-      hipEvent_t a, b;
-      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
-      h->events.push_back(a);
-      h->events.push_back(b);
-    }
-    (void)hipEventRecord(h->events[h->events_used], s);
-  } else {
-    (void)hipEventRecord(h->events[h->events_used + 1], s);
-    h->events_used += 2;
+// Event pair for the next profiled launch, or {nullptr, nullptr} when profiling
+// is off or the stream is being captured. The launcher hands the pair to
+// hipExtLaunchKernelGGL, which stamps them with the kernel's own start and end.
+struct ProfPair { hipEvent_t start = nullptr, stop = nullptr; };
+
+ProfPair prof_events(csa_cache_t h, hipStream_t s) {
+  if (!h->profiling) return {};
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return {};
+  if (h->events_used + 2 > h->events.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return {};
+    if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return {}; }
+    h->events.push_back(a);
+    h->events.push_back(b);
   }
+  ProfPair p{h->events[h->events_used], h->events[h->events_used + 1]};
+  h->events_used += 2;
+  return p;
 }
 
 // ------------------------------------------------------------------ debug conversions
@@ -429,9 +434,8 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
     s.n_etiles = (n_max + 255) / 256;
     s.n_stiles = (n_max / kChunkSample + 255) / 256;
     s.kv_dtype = kv; s.act_dtype = act;
-    record(h, stream, true);
-    launch_idx_chunk(s, kv, act, stream);
-    record(h, stream, false);
+    const ProfPair ev = prof_events(h, stream);
+    launch_idx_chunk(s, kv, act, stream, ev.start, ev.stop);
     launch_idx_chunk_select(s, stream);
   } else {
     for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
@@ -484,9 +488,8 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
       }
       f.slice0[nq] = slices;
       s.total_wg = wg;
-      record(h, stream, true);
-      launch_idx_scan(s, kv, act, stream);
-      record(h, stream, false);
+      const ProfPair ev = prof_events(h, stream);
+      launch_idx_scan(s, kv, act, stream, ev.start, ev.stop);
       launch_idx_filter(f, slices, stream);
       launch_idx_final(fin, stream);
     }

@@ -112,10 +112,14 @@ struct IdxChunkArgs {
   int32_t pool_pages, h_i, ss_stride, fb_stride, n_tok, pos0, r, k, m_s, n_etiles, n_stiles, kv_dtype, act_dtype;
 };
 
-void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s);
+// ev0/ev1 (may be null): events stamped with the start and end of the launch
+// that does the score work (the scan; in chunk mode the full-score GEMM pass).
+void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
+                     hipEvent_t ev1 = nullptr);
 void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s);
 void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
-void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s);
+void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
+                      hipEvent_t ev1 = nullptr);
 void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s);
 
 // ------------------------------------------------------------------ attend

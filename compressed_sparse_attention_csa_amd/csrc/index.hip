@@ -28,6 +28,8 @@
 #include <type_traits>
 
 #include "csa_device.h"
+#include <hip/hip_ext.h>
+
 #include "csa_internal.h"
 
 namespace csa {
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
   for (int p = 0; p < 4; ++p) pps[p] = __shfl(my_pp, p, 64);
 
   constexpr int PB = KV == DT_FP8 ? 4 : (KV == DT_BF16 ? 2 : 1);   // pages per load batch
-  constexpr int RW = 32 * KE / 16;                                   // uint4 per lane per tile (2 chunks)
+  constexpr int RW = 16 * KE / 16;                                   // uint4 per lane per tile: its 16 dims
   float run = -1.f;
 #pragma unroll 1
   for (int pb = 0; pb < 4; pb += PB) {
@@ -1051,14 +1053,14 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
 
 }  // namespace
 
-void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s) {
+void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.total_wg <= 0) return;
   if (kv == DT_F32 && act == DT_F32)
-    hipLaunchKernelGGL((idx_scan_kernel<DT_F32, DT_F32>), dim3(a.total_wg), dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((idx_scan_kernel<DT_F32, DT_F32>), dim3(a.total_wg), dim3(256), 0, s, ev0, ev1, 0, a);
   else if (kv == DT_BF16 && act == DT_BF16)
-    hipLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(256), 0, s, ev0, ev1, 0, a);
   else if (kv == DT_FP8 && act == DT_BF16)
-    hipLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(256), 0, s, ev0, ev1, 0, a);
 }
 
 void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s) {
@@ -1071,22 +1073,22 @@ void launch_idx_final(const IdxFinalArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(idx_final_kernel, dim3(a.n_q), dim3(512), 0, s, a);
 }
 
-void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s) {
+void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int n_qt = (a.n_tok + kCQ - 1) / kCQ;
-  auto gemm = [&](auto mode_tag, int n_et) {
+  auto gemm = [&](auto mode_tag, int n_et, hipEvent_t e0, hipEvent_t e1) {
     constexpr int M = decltype(mode_tag)::value;
     const int n_wg = n_qt * ((n_et + kChunkTilesPerWg - 1) / kChunkTilesPerWg);
     if (n_wg <= 0) return;
     if (kv == DT_F32 && act == DT_F32)
-      hipLaunchKernelGGL((idx_chunk_gemm_kernel<DT_F32, DT_F32, M>), dim3(n_wg), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((idx_chunk_gemm_kernel<DT_F32, DT_F32, M>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a);
     else if (kv == DT_BF16 && act == DT_BF16)
-      hipLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_BF16, M>), dim3(n_wg), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_BF16, M>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a);
     else if (kv == DT_FP8 && act == DT_BF16)
-      hipLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_FP8, M>), dim3(n_wg), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_FP8, M>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a);
   };
-  gemm(std::integral_constant<int, 0>{}, a.n_stiles);
+  gemm(std::integral_constant<int, 0>{}, a.n_stiles, nullptr, nullptr);
   hipLaunchKernelGGL(idx_chunk_tau_kernel, dim3(a.n_tok), dim3(256), 0, s, a);
-  gemm(std::integral_constant<int, 1>{}, a.n_etiles);
+  gemm(std::integral_constant<int, 1>{}, a.n_etiles, ev0, ev1);
 }
 
 void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s) {

@@ -233,10 +233,12 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
  * range was met; bit 2: an internal capacity fallback ran) and clears it. */
 csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags);
 
-/* Timing of the indexer scan kernel (the dominant kernel of a decode step):
- * after csa_profile_begin, every csa_index_topk call records a HIP event pair
- * around its scan launch on the call's stream; csa_profile_end synchronises
- * and returns the summed elapsed milliseconds and the number of launches. */
+/* Timing of the indexer score kernel (the dominant kernel of a decode step;
+ * in chunk mode the GEMM pass that scores every visible entry): after
+ * csa_profile_begin, every csa_index_topk call issued outside stream capture
+ * launches that kernel with a HIP event pair stamped with the kernel's own
+ * start and end (hipExtLaunchKernelGGL); csa_profile_end synchronises and
+ * returns the summed elapsed milliseconds and the number of timed launches. */
 csa_status csa_profile_begin(csa_cache_t h);
 csa_status csa_profile_end(csa_cache_t h, double *total_ms, int32_t *launches);
 
