@@ -470,11 +470,15 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
       int wg = 0, slices = 0;
       for (int i = 0; i < nq; ++i) {
         const int N = (q_pos[g0 + i] + 1) / c.ratio;
+        // group size G = 2^glog2: at least 4k groups where possible, at most
+        // kMaxGroups, and G <= 256 entries and within one scan workgroup
+        constexpr int kGMax = kIdxChunk < 256 ? (kIdxChunk < 128 ? 6 : 7) : 8;
+        static_assert(kIdxChunk >= 64, "a scan workgroup covers whole pages");
         int glog2 = 0;
-        while (glog2 < 8 && (((N + (2 << glog2) - 1) >> (glog2 + 1)) >= 4 * k)) ++glog2;
-        while (glog2 < 8 && ((N + (1 << glog2) - 1) >> glog2) > kMaxGroups) ++glog2;
+        while (glog2 < kGMax && (((N + (2 << glog2) - 1) >> (glog2 + 1)) >= 4 * k)) ++glog2;
+        while (glog2 < kGMax && ((N + (1 << glog2) - 1) >> glog2) > kMaxGroups) ++glog2;
         if (((N + (1 << glog2) - 1) >> glog2) > kMaxGroups)
-          return fail(CSA_ERR_UNSUPPORTED, "query %d sees %d entries; at most %d are supported for k = %d", g0 + i, N, kMaxGroups << 8, k);
+          return fail(CSA_ERR_UNSUPPORTED, "query %d sees %d entries; at most %d are supported for k = %d", g0 + i, N, kMaxGroups << kGMax, k);
         s.q[i].seq = q_seq[g0 + i];
         s.q[i].n_vis = N;
         s.q[i].chunk0 = wg;

@@ -46,7 +46,9 @@ void launch_compress_ring(const RingArgs &a, int n_wg, int act, hipStream_t s);
 // ------------------------------------------------------------------ index (decode)
 
 constexpr int kIdxMaxQ = 128;        // queries per decode launch group
-constexpr int kIdxChunk = 1024;      // entries per scan workgroup
+constexpr int kScanPagesPerWave = 1;                     // indexer-key pages per scan wave
+constexpr int kScanWaves = 4;                            // waves per scan workgroup
+constexpr int kIdxChunk = kScanWaves * kScanPagesPerWave * 64;   // entries per scan workgroup
 constexpr int kFilterSlice = 4096;   // scores per filter workgroup
 constexpr int kMaxGroups = 8192;     // group maxima per query (threshold select in LDS)
 constexpr int kMaxSlices = 512;      // filter slices per query (<= 2M visible entries)

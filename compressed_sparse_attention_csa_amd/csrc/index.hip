@@ -387,86 +387,98 @@ __device__ void block_prefix_sum(int *arr, int n, int *wsum) {
 
 // ------------------------------------------------------------------ decode scan
 
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+
+// One workgroup = kScanWaves waves, each owning kScanPagesPerWave consecutive pages of
+// one query's visible entries. A wave reads its page ids, issues every key
+// load of its pages at once, and scores 16 entries per MFMA (indexer heads as
+// rows, entries as columns). Small workgroups keep many of them resident per
+// CU, so one workgroup's block-table round trip overlaps others' key streams.
 template <int ACT, int KV>
-__global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
+__global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScanArgs a) {
   using CT = typename ComputeT<KV>::type;
+  constexpr int PPW = kScanPagesPerWave;
   const int wg = blockIdx.x;
-  int qi = 0;
-  for (; qi < a.n_q - 1; ++qi)
-    if (wg < a.q[qi + 1].chunk0) break;
+  // owning query: the last one whose first workgroup is <= wg
+  int qlo = 0, qhi = a.n_q;
+  while (qhi - qlo > 1) {
+    const int mid = (qlo + qhi) >> 1;
+    if (a.q[mid].chunk0 <= wg) qlo = mid; else qhi = mid;
+  }
+  const int qi = qlo;
   const IdxQuery Q = a.q[qi];
   const int chunk = wg - Q.chunk0;
   const int N = Q.n_vis;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, col = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
 
-  // A operand: indexer query heads as rows (rows >= H_I are zero)
-  Frag<CT> qa[2];
-  {
+  const int glog2 = Q.glog2, G = 1 << glog2;
+  const bool cross = G > PPW * kPage;   // a group spans several waves of the workgroup
+  float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
+  float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
+  const int wave_e0 = chunk * kIdxChunk + w * (PPW * kPage);
+  float run = -INFINITY;
+
+  if (wave_e0 < N) {
+    const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
+    const char *kbase = reinterpret_cast<const char *>(a.kidx);
+    int pps[PPW];
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) pps[p] = wave_e0 + p * kPage < N ? bt[(wave_e0 >> 6) + p] : -1;
+
+    // A operand: indexer query heads as rows (rows >= H_I are zero)
+    Frag<CT> qa[2];
     qa[0] = qa[1] = zero_frag<CT>();
     if (col < a.h_i) {
       const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + col) * kDI * AE;
 #pragma unroll
       for (int c = 0; c < 2; ++c) qa[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
     }
-  }
-  float wv[4];
+    float wv[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
+    for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
 
-  const int glog2 = Q.glog2, G = 1 << glog2;
-  float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
-  float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
-  const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
-  const char *kbase = reinterpret_cast<const char *>(a.kidx);
-
-  // the wave's 4 pages (256 entries): page ids once, then every load in flight
-  const int wave_e0 = chunk * kIdxChunk + w * 256;
-  int my_pp = -1;
-  if (lane < 4 && wave_e0 + lane * kPage < N) my_pp = bt[(wave_e0 >> 6) + lane];
-  int pps[4];
+    // every key load of the wave in flight together: lane (g, col) reads dims
+    // [16g, 16g + 16) of entry col of each 16-entry tile; the key stream is
+    // read once, so the loads are non-temporal
+    constexpr int RW = KE;   // uint4 per lane per tile
+    uint4 raw[PPW][4][RW];
+    bool okp[PPW];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) pps[p] = __shfl(my_pp, p, 64);
-
-  constexpr int PB = KV == DT_FP8 ? 4 : (KV == DT_BF16 ? 2 : 1);   // pages per load batch
-  constexpr int RW = 16 * KE / 16;                                   // uint4 per lane per tile: its 16 dims
-  float run = -1.f;
-#pragma unroll 1
-  for (int pb = 0; pb < 4; pb += PB) {
-    if (wave_e0 + pb * kPage >= N) break;
-    uint4 raw[PB][4][RW];
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int pp = pps[pb + p];
-      const bool ok = pp >= 0 && pp < a.pool_pages;
+    for (int p = 0; p < PPW; ++p) {
+      const int pp = pps[p];
+      okp[p] = pp >= 0 && pp < a.pool_pages;
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl) {
-        const int e = wave_e0 + (pb + p) * kPage + tl * 16 + col;
-        if (ok && e < N) {
-          const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI * KE + 16 * g * KE);
+        const int e = wave_e0 + p * kPage + tl * 16 + col;
+        if (okp[p] && e < N) {
+          const uint4 *src = reinterpret_cast<const uint4 *>(kbase + ((static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI + 16 * g) * KE);
 #pragma unroll
-          for (int u = 0; u < RW; ++u) raw[p][tl][u] = src[u];
+          for (int u = 0; u < RW; ++u) {
+            const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(src + u));
+            raw[p][tl][u] = make_uint4(t.x, t.y, t.z, t.w);
+          }
         } else {
 #pragma unroll
           for (int u = 0; u < RW; ++u) raw[p][tl][u] = make_uint4(0, 0, 0, 0);
         }
       }
     }
-    float scs[PB];
+    float scs[PPW];
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int pp = pps[pb + p];
-      const bool ok = pp >= 0 && pp < a.pool_pages;
-      if (!ok && lane == 0 && wave_e0 + (pb + p) * kPage < N) flag_error(a.err, ERR_PAGE);
-      scs[p] = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
+    for (int p = 0; p < PPW; ++p) {
+      if (!okp[p] && lane == 0 && wave_e0 + p * kPage < N) flag_error(a.err, ERR_PAGE);
+      scs[p] = (KV == DT_FP8 && okp[p]) ? a.kidx_scale[pps[p]] : 1.f;
     }
+
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int e_page = wave_e0 + (pb + p) * kPage;
-      const bool ok = pps[pb + p] >= 0 && pps[pb + p] < a.pool_pages;
+    for (int p = 0; p < PPW; ++p) {
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl) {
+        const int e_tile = wave_e0 + p * kPage + tl * 16;
+        if (e_tile >= N) break;
         Frag<CT> kb[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -478,14 +490,14 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma(qa[0], kb[0], acc);
         acc = mma(qa[1], kb[1], acc);
-        const int e_tile = e_page + tl * 16;
         const int e = e_tile + col;
         float s = 0.f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
-        s = (e < N && ok) ? s * scs[p] : -1.f;
+        s = okp[p] ? s * scs[p] : -1.f;   // a missing page scores -1 (and is flagged)
         if (g == 0 && e < N) Srow[e] = s;
-        float m = s;
+        // group maxima: entries past N do not take part
+        float m = e < N ? s : -INFINITY;
         if (G <= 16) {
           for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
           if (g == 0 && (col & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
@@ -493,12 +505,27 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(const IdxScanArgs a) {
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
           run = fmaxf(run, m);
-          const bool last = (((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N);
-          if (last) {
-            if (lane == 0 && e_tile < N) Mrow[e_tile >> glog2] = run;
-            run = -1.f;
+          if (!cross && ((((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N))) {
+            if (lane == 0) Mrow[e_tile >> glog2] = run;
+            run = -INFINITY;
           }
         }
+      }
+    }
+  }
+  if (cross) {
+    // groups of G entries = G / (PPW * 64) consecutive waves, all inside this workgroup
+    __shared__ float wmax[kScanWaves];
+    if (lane == 0) wmax[w] = run;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int wpg = G / (PPW * kPage);
+      for (int w0 = 0; w0 < kScanWaves; w0 += wpg) {
+        const int e0 = chunk * kIdxChunk + w0 * (PPW * kPage);
+        if (e0 >= N) break;
+        float m = -INFINITY;
+        for (int u = 0; u < wpg; ++u) m = fmaxf(m, wmax[w0 + u]);
+        Mrow[e0 >> glog2] = m;
       }
     }
   }
@@ -1056,11 +1083,11 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
 void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.total_wg <= 0) return;
   if (kv == DT_F32 && act == DT_F32)
-    hipExtLaunchKernelGGL((idx_scan_kernel<DT_F32, DT_F32>), dim3(a.total_wg), dim3(256), 0, s, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((idx_scan_kernel<DT_F32, DT_F32>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
   else if (kv == DT_BF16 && act == DT_BF16)
-    hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(256), 0, s, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
   else if (kv == DT_FP8 && act == DT_BF16)
-    hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(256), 0, s, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
 }
 
 void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s) {
