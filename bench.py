@@ -184,8 +184,8 @@ def step_bytes():
 
 
 def traffic_from_profiles():
-    """HBM bytes per scan launch from the committed counter summary, if it was
-    taken on the current scan kernel source; else None."""
+    """(HBM bytes per scan launch, scope) from the committed counter record, if
+    it was taken on the current scan kernel source; else (None, None)."""
     path = os.path.join(ROOT, "profiles", "index_scan_1m_decode_traffic.json")
     src = os.path.join(ROOT, "compressed_sparse_attention_csa_amd", "csrc", "index.hip")
     try:
@@ -194,10 +194,10 @@ def traffic_from_profiles():
         with open(src, "rb") as f:
             h = hashlib.sha256(f.read()).hexdigest()
         if rec.get("source_sha256") != h:
-            return None
-        return rec.get("bytes_per_launch")
+            return None, None
+        return rec.get("bytes_per_launch"), rec.get("scope")
     except (OSError, ValueError):
-        return None
+        return None, None
 
 
 def cpu_baseline(seed, budget_s):
@@ -330,6 +330,7 @@ def main():
     scan_avg_ms = scan_ms / max(1, launches)
     sb = scan_bytes_per_launch()
     achieved = sb / (scan_avg_ms * 1e-3) / 1e9
+    traffic, traffic_scope = traffic_from_profiles()
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -352,7 +353,8 @@ def main():
         "step_bytes": step_bytes(),
         "roofline": {"bound": "hbm", "kernel": "idx_scan (indexer scores over the fp8 indexer-key pages)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_scope": traffic_scope,
                      "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
     }
     if not args.no_prefill:
