@@ -95,3 +95,119 @@ def test_decode_1m_context_sampled(bench_mod):
         assert err <= 2e-2, f"layer {layer}: max-abs {err}"
     for cc in caches:
         cc.close()
+
+
+def _oracle_entries(seed, layer, seq, n_rows, dev, with_proj, kv, r=4, step=1 << 16):
+    """Oracle compressed entries of (layer, seq) from the seeded raw rows, stored in `kv`."""
+    P = to64(Sy.proj_matrix(seed, 128, 64)) if with_proj else None
+    E = n_rows // r
+    kb, vb = np.empty((E, 128)), np.empty((E, 128))
+    ki = np.empty((E, 64)) if with_proj else None
+    for r0 in range(0, E * r, step):
+        n = min(step, E * r - r0)
+        K, V, Z = (to64(_rows(seed, kind, layer, seq, r0, n, dev)) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+        a, b_, c_ = O.compress(K, V, Z, r, P)
+        sl = slice(r0 // r, (r0 + n) // r)
+        kb[sl], vb[sl] = a, b_
+        if with_proj:
+            ki[sl] = c_
+    return (O.store(kb, kv)[0], O.store(vb, kv)[0], O.store(ki, kv)[0] if with_proj else None)
+
+
+def _check_query(seed, dev, seq, t, qi_row, w_row, q_row, T_row, out_row, k, W, kv, tol, n_rows):
+    kbs, vbs, kis = _oracle_entries(seed, 0, seq, n_rows, dev, True, kv)
+    N = O.visible_entries(t, 4)
+    s = O.index_scores(to64(qi_row), to64(w_row), kis[:N])
+    To = O.topk(s, k)
+    ok, msg = topk_matches(T_row, To, s, rel=2e-2)
+    assert ok, f"sequence {seq}: {msg}"
+    lo = max(0, t - W + 1)
+    Kw = np.zeros((t + 1, 128))
+    Vw = np.zeros((t + 1, 128))
+    Kw[lo:] = to64(_rows(seed, Sy.KIND_K, 0, seq, lo, t + 1 - lo, dev))
+    Vw[lo:] = to64(_rows(seed, Sy.KIND_V, 0, seq, lo, t + 1 - lo, dev))
+    ref = O.attend_step(to64(q_row), To, t, W, 1.0 / math.sqrt(128), kbs, vbs, Kw, Vw)
+    err = max_abs(out_row, ref)
+    assert err <= tol, f"sequence {seq}: max-abs {err}"
+
+
+def test_decode_batch32_64k_bf16_sampled():
+    """32 sequences of 65,536 bf16 tokens (16,384 entries each), 64 heads,
+    Top-512, W = 128: one decode step for all 32; sequences 0 and 31 checked
+    against the oracle, every row checked for validity."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+    seed, dev, B_, L, k, W, H = 1, torch.device("cuda:0"), 32, 1 << 16, 512, 128, 64
+    pages = L // 4 // 64
+    spec = CacheSpec(ratio=4, q_heads=H, idx_heads=4, window=W, ring_rows=W, n_layers=1, max_seqs=B_,
+                     max_pages_per_seq=pages, pool_pages=B_ * pages, kv_dtype="bf16", act_dtype="bf16",
+                     max_queries=B_, max_k=k)
+    bt = torch.tensor(Sy.permutation(seed, B_ * pages, salt=9), dtype=torch.int32).view(B_, pages).to(dev)
+    c = CsaCache(spec, dev, block_table=bt)
+    P = Sy.proj_matrix(seed, 128, 64, device=dev)
+    for b in range(B_):
+        K, V, Z = (_rows(seed, kind, 0, b, 0, L, dev) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+        c.compress(0, [b], [L], K, V, Z, P)
+    ids, pos = list(range(B_)), [L - 1] * B_
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, B_ * 4, 64, dev, torch.bfloat16).view(B_, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, B_, 4, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, B_ * H, 128, dev, torch.bfloat16).view(B_, H, 128)
+    T = c.index_topk(ids, pos, qi, w, k)
+    out = to64(c.attend(0, ids, pos, q, T, k, 1.0 / math.sqrt(128)))
+    assert c.read_errors() == 0
+    Tg = T.cpu().numpy()
+    for b in range(B_):
+        assert np.all(np.diff(Tg[b]) > 0) and Tg[b][0] >= 0 and Tg[b][-1] < L // 4
+    for b in (0, B_ - 1):
+        _check_query(seed, dev, b, L - 1, qi[b], w[b], q[b], Tg[b], out[b], k, W, "bf16", 2e-2, L)
+    c.close()
+
+
+def test_serving_64_requests_4k_to_256k_sampled():
+    """64 requests with log-uniform contexts from 4K to 256K tokens on one
+    shared paged fp8 pool (shuffled free list): bulk build, then one serving
+    step that appends one token per request (compress), indexes (Top-512) and
+    attends (W = 128, 64 heads). The longest and the shortest request are
+    checked against the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+    seed, dev, nreq, k, W, H = 2, torch.device("cuda:0"), 64, 512, 128, 64
+    lens = Sy.log_uniform_lengths(seed, nreq, 4096, 262144)
+    final = [L + 1 for L in lens]
+    pages = [(L // 4 + 63) // 64 for L in final]
+    pool = sum(pages) + 16
+    perm = Sy.permutation(seed, pool, salt=13)
+    max_pages = max(pages)
+    bt = torch.full((nreq, max_pages), -1, dtype=torch.int32)
+    off = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = torch.tensor(perm[off:off + p], dtype=torch.int32)
+        off += p
+    spec = CacheSpec(ratio=4, q_heads=H, idx_heads=4, window=W, ring_rows=W, n_layers=1, max_seqs=nreq,
+                     max_pages_per_seq=max_pages, pool_pages=pool, kv_dtype="fp8", act_dtype="bf16",
+                     max_queries=nreq, max_k=k)
+    c = CsaCache(spec, dev, block_table=bt.to(dev))
+    P = Sy.proj_matrix(seed, 128, 64, device=dev)
+    for b in range(nreq):
+        K, V, Z = (_rows(seed, kind, 0, b, 0, lens[b], dev) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+        c.compress(0, [b], [lens[b]], K, V, Z, P)
+    ids = list(range(nreq))
+    new = [torch.cat([_rows(seed, kind, 0, b, lens[b], 1, dev) for b in ids]) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+    c.compress(0, ids, [1] * nreq, *new, P)
+    pos = lens[:]          # the appended token's position
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, nreq * 4, 64, dev, torch.bfloat16).view(nreq, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, nreq, 4, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, nreq * H, 128, dev, torch.bfloat16).view(nreq, H, 128)
+    T = c.index_topk(ids, pos, qi, w, k)
+    out = to64(c.attend(0, ids, pos, q, T, k, 1.0 / math.sqrt(128)))
+    assert c.read_errors() == 0
+    Tg = T.cpu().numpy()
+    for b in ids:
+        N = final[b] // 4
+        row = Tg[b][Tg[b] >= 0]
+        assert len(row) == min(k, N) and np.all(np.diff(row) > 0) and row[-1] < N
+    for b in (int(np.argmax(lens)), int(np.argmin(lens))):
+        _check_query(seed, dev, b, pos[b], qi[b], w[b], q[b], Tg[b], out[b], k, W, "fp8", 2e-2, final[b])
+    c.close()
