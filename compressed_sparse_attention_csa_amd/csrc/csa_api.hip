@@ -95,7 +95,7 @@ size_t idx_chunk_bytes(int nq, int64_t ss_stride, int64_t fb_stride) {
   const int64_t tiles = (fb_stride + 255) / 256;
   return align_up(static_cast<size_t>(nq) * ss_stride * 4, 256) + align_up(static_cast<size_t>(nq) * 4, 256) +
          align_up(static_cast<size_t>(nq) * tiles * 4, 256) +
-         2 * align_up(static_cast<size_t>(nq) * tiles * kChunkTileCand * 4, 256) +
+         align_up(static_cast<size_t>(nq) * tiles * kChunkTileCand * 8, 256) +
          align_up(static_cast<size_t>(nq) * fb_stride * 4, 256);
 }
 
@@ -422,8 +422,7 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
     const int64_t tiles = (fb_stride + 255) / 256;
     s.tau = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * 4, 256);
     s.cnt = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * 4, 256);
-    s.cand_s = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 4, 256);
-    s.cand_j = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 4, 256);
+    s.cand = reinterpret_cast<uint64_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 8, 256);
     s.fb_rows = reinterpret_cast<float *>(p);
     s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale;
     s.bt_row = h->buf.block_table + static_cast<int64_t>(q_seq[0]) * c.max_pages_per_seq;

@@ -106,8 +106,7 @@ struct IdxChunkArgs {
   float *ss;               // [n_tok][ss_stride] sampled scores
   float *tau;              // [n_tok] thresholds
   int32_t *cnt;            // [n_tok][n_etiles] candidates per (query, entry tile)
-  float *cand_s;           // [n_tok][n_etiles][kChunkTileCand]
-  int32_t *cand_j;         // [n_tok][n_etiles][kChunkTileCand]
+  uint64_t *cand;          // [n_tok][n_etiles][kChunkTileCand] keys (score bits << 32 | ~entry), entry order
   float *fb_rows;          // [n_tok][fb_stride] full rows for the exact fallback
   int32_t *topk;           // [n_tok][k]
   uint32_t *err;

@@ -88,6 +88,10 @@ __device__ uint64_t kth_largest_u64(Get get, int n, int k, int *hist, int *sh) {
   return prefix;
 }
 
+// max(x, 0) as one integer max on the bit pattern (negative floats, -0.0
+// included, are negative integers); no NaN quieting step.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ uint64_t score_key(float s, int j) {
   return (static_cast<uint64_t>(__float_as_uint(s)) << 32) | static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(j));
 }
@@ -134,6 +138,22 @@ __device__ __forceinline__ float block_reduce_min(float v, float *red) {
   return r;
 }
 
+// Block-wide min and max in one exchange (red holds >= 2 x waves floats).
+__device__ __forceinline__ void block_reduce_minmax(float &lo, float &hi, float *red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+  }
+  const int nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = lo; red[nw + (threadIdx.x >> 6)] = hi; }
+  __syncthreads();
+  lo = red[0];
+  hi = red[nw];
+  for (int i = 1; i < nw; ++i) { lo = fminf(lo, red[i]); hi = fmaxf(hi, red[nw + i]); }
+}
+
 // A threshold tau <= the k-th largest of n (> k) non-negative values given by
 // get(i): values are binned linearly between their min and max, the highest
 // bins holding at least k values are kept, and tau is the smallest value in
@@ -148,8 +168,7 @@ __device__ float tau_lower_bound(Get get, int n, int k, int *hist, float *red, i
     lo = fminf(lo, v);
     hi = fmaxf(hi, v);
   }
-  lo = block_reduce_min(lo, red);
-  hi = block_reduce_max(hi, red);
+  block_reduce_minmax(lo, hi, red);
   if (!(hi > lo)) return lo;
   const float sc = static_cast<float>(kTauBins - 1) / (hi - lo);
   for (int i = t; i < kTauBins; i += bd) hist[i] = 0;
@@ -279,8 +298,7 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
     lo = fminf(lo, v);
     hi = fmaxf(hi, v);
   }
-  lo = block_reduce_min(lo, red);
-  hi = block_reduce_max(hi, red);
+  block_reduce_minmax(lo, hi, red);
   const float sc = hi > lo ? static_cast<float>(kSelBins - 1) / (hi - lo) : 0.f;
   auto bin_of = [&](uint64_t key) {
     return min(kSelBins - 1, static_cast<int>((__uint_as_float(static_cast<uint32_t>(key >> 32)) - lo) * sc));
@@ -536,7 +554,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
 __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) {
   __shared__ float vals[kMaxGroups];
   __shared__ int hist[kTauBins];
-  __shared__ float red[16];
+  __shared__ float red[32];
   __shared__ int sh[4];
   __shared__ int wcnt[4];
   const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -618,7 +636,7 @@ __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
   __shared__ int sel[CSA_MAX_TOPK];
   __shared__ int hist[kSelBins];
   __shared__ int soff[kMaxSlices + 1];
-  __shared__ float red[16];
+  __shared__ float red[32];
   __shared__ int sh[4];
   __shared__ int wsum_f[16];
   const int qi = blockIdx.x, tid = threadIdx.x;
@@ -691,9 +709,10 @@ constexpr int kCQ = 64;     // queries per tile
 constexpr int kCE = 256;    // entries per tile
 constexpr int kLdsRow = kDI + 8;
 constexpr int kWgCand = kChunkTileCand;
-constexpr int kChunkTilesPerWg = 1;   // entry tiles one workgroup walks (next tile prefetched)
-constexpr int kBitmapWords = 8192;
-constexpr int kMaxChunkTiles = kBitmapWords * 32 / kCE;   // 1024 entry tiles (262,144 entries)
+constexpr int kChunkTilesPerWg = 4;   // entry tiles a full-score workgroup walks (next tile prefetched)
+// the sample pass touches 64 pages per tile and has few tiles: one tile per workgroup
+template <int MODE> constexpr int chunk_tiles_per_wg() { return MODE == 0 ? 1 : kChunkTilesPerWg; }
+constexpr int kMaxChunkTiles = 1024;  // entry tiles per query the select accepts (262,144 entries)
 
 template <int ACT, int KV, int MODE>
 __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs a) {
@@ -703,25 +722,35 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
   constexpr int kChunkElems = 16 / KE;                 // elements per 16-byte load
   constexpr int kChunksPerRow = kDI / kChunkElems;
   constexpr int kLoads = kCE * kChunksPerRow / 256;    // 16-byte loads per thread per tile
+  constexpr int kPagesPerTile = SAMPLE ? kCE * kChunkSample / kPage : kCE / kPage;
+  constexpr int TPW = chunk_tiles_per_wg<MODE>();
   __shared__ CT kt[kCE][kLdsRow];
   __shared__ float rsc[kCE];
-  __shared__ int lcnt[SAMPLE ? 1 : kCQ];
+  __shared__ int32_t pid[TPW * kPagesPerTile];
 
   const int n_et = SAMPLE ? a.n_stiles : a.n_etiles;
-  const int n_eg = (n_et + kChunkTilesPerWg - 1) / kChunkTilesPerWg;   // entry-tile groups
+  const int n_eg = (n_et + TPW - 1) / TPW;   // entry-tile groups
   const int qt = blockIdx.x / n_eg, eg = blockIdx.x % n_eg;
   const int q0 = qt * kCQ;
   const int qlast = min(a.n_tok, q0 + kCQ) - 1;
   const int nvis_max = (a.pos0 + qlast + 1) / a.r;
   auto entry_of = [&](int m) { return SAMPLE ? m * kChunkSample + (kChunkSample - 1) : m; };
-  const int et_begin = eg * kChunkTilesPerWg;
-  int et_end = min(n_et, et_begin + kChunkTilesPerWg);
+  const int et_begin = eg * TPW;
+  int et_end = min(n_et, et_begin + TPW);
   while (et_end > et_begin && entry_of((et_end - 1) * kCE) >= nvis_max) --et_end;
   if (et_end <= et_begin) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
   const int qw = q0 + 16 * w;   // the wave's first query
   const char *kbase = reinterpret_cast<const char *>(a.kidx);
+
+  // physical page of every page the walked tiles touch (pages are contiguous
+  // per tile in both modes), read once, in the same round trip as the queries
+  const int page0 = et_begin * kPagesPerTile;
+  for (int i = tid; i < (et_end - et_begin) * kPagesPerTile; i += 256) {
+    const int lp = page0 + i;
+    pid[i] = lp * kPage < nvis_max ? a.bt_row[lp] : -1;
+  }
 
   // A operands: (query, head) pairs as rows: row = 4*q + h
   Frag<CT> qa[4][2];
@@ -741,10 +770,22 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
     tq[mt] = INFINITY;
     if constexpr (!SAMPLE) tq[mt] = qo < a.n_tok ? a.tau[qo] : INFINITY;
   }
+  // visibility of each of the lane's queries, and of the wave's first (smallest) one
+  int nvis[4];
+  bool qok[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int qo = qw + 4 * mt + g;
+    qok[mt] = qo < a.n_tok;
+    nvis[mt] = (a.pos0 + qo + 1) / a.r;
+  }
+  const int nvis_lo = (a.pos0 + qw + 1) / a.r;
+  __syncthreads();   // pid ready
 
   // register prefetch of one tile's indexer keys: all loads of a thread in flight together
   uint4 raw[kLoads];
   float rscale = 1.f;
+  auto page_of = [&](int et, int e) { return pid[(et - et_begin) * kPagesPerTile + ((e >> 6) - et * kPagesPerTile)]; };
   auto load_tile = [&](int et) {
     const int m0 = et * kCE;
 #pragma unroll
@@ -752,13 +793,13 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
       const int i = u * 256 + tid;
       const int le = i / kChunksPerRow, ch = i % kChunksPerRow;
       const int e = entry_of(m0 + le);
-      const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
+      const int pp = e < nvis_max ? page_of(et, e) : -1;
       raw[u] = (pp >= 0 && pp < a.pool_pages)
                    ? *reinterpret_cast<const uint4 *>(kbase + ((static_cast<int64_t>(pp) * kPage + (e & 63)) * kDI + ch * kChunkElems) * KE)
                    : make_uint4(0, 0, 0, 0);
     }
     const int e = entry_of(m0 + tid);
-    const int pp = e < nvis_max ? a.bt_row[e >> 6] : -1;
+    const int pp = e < nvis_max ? page_of(et, e) : -1;
     const bool ok = pp >= 0 && pp < a.pool_pages;
     if (e < nvis_max && !ok) flag_error(a.err, ERR_PAGE);
     rscale = (KV == DT_FP8 && ok) ? a.kidx_scale[pp] : 1.f;
@@ -786,16 +827,21 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
   load_tile(et_begin);
   for (int et = et_begin; et < et_end; ++et) {
     const int m0 = et * kCE;
-    __syncthreads();                 // previous tile's LDS reads (and flush) are done
+    __syncthreads();                 // previous tile's LDS reads are done
     commit_tile();
-    if constexpr (!SAMPLE) {
-      if (tid < kCQ) lcnt[tid] = 0;
-    }
     __syncthreads();
     if (et + 1 < et_end) load_tile(et + 1);   // in flight during this tile's MFMAs
 
+    // candidates of (query, this tile) so far; every lane of a 16-lane group
+    // scores the same query, so the group's ballot orders its slots by entry
+    int run[4] = {0, 0, 0, 0};
+    // every (query, entry) pair of the wave visible in this tile: skip the per-score test
+    const bool full = qw + 15 < a.n_tok && entry_of(m0 + kCE - 1) < nvis_lo;
 #pragma unroll 1
     for (int pg = 0; pg < kCE / 64; ++pg) {
+      float psc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) psc[nt] = KV == DT_FP8 ? rsc[pg * 64 + nt * 16 + col] : 1.f;
       f32x4_t acc[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -820,36 +866,36 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int qo = qw + 4 * mt + g;
-        const int nvis = (a.pos0 + qo + 1) / a.r;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const int le = pg * 64 + nt * 16 + col;
           const int e = entry_of(m0 + le);
           float s = 0.f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) s += wq[mt][v] * fmaxf(acc[mt][nt][v], 0.f);
-          s *= rsc[le];
-          const bool vis = qo < a.n_tok && e < nvis;
+          for (int v = 0; v < 4; ++v) s += wq[mt][v] * relu_bits(acc[mt][nt][v]);
+          if constexpr (KV == DT_FP8) s *= psc[nt];
+          const bool vis = full || (qok[mt] && e < nvis[mt]);
           if constexpr (SAMPLE) {
             if (vis) a.ss[static_cast<int64_t>(qo) * a.ss_stride + m0 + le] = s;
           } else {
-            if (vis && s >= tq[mt]) {
-              // this (query, entry tile) owns candidate slots [0, kWgCand) of its region
-              const int ql = 16 * w + 4 * mt + g;
-              const int slot = atomicAdd(&lcnt[ql], 1);
-              if (slot < kWgCand) {
-                const int64_t o = (static_cast<int64_t>(qo) * a.n_etiles + et) * kWgCand + slot;
-                a.cand_s[o] = s;
-                a.cand_j[o] = e;
-              }
+            const bool take = vis && s >= tq[mt];
+            const uint32_t seg = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(take) >> (16 * g)) & 0xffffu;
+            if (take) {
+              const int slot = run[mt] + __popc(seg & ((1u << col) - 1u));
+              if (slot < kWgCand)
+                a.cand[(static_cast<int64_t>(qo) * a.n_etiles + et) * kWgCand + slot] = score_key(s, e);
             }
+            run[mt] += __popc(seg);
           }
         }
       }
     }
     if constexpr (!SAMPLE) {
-      __syncthreads();
-      if (tid < kCQ && q0 + tid < a.n_tok) a.cnt[static_cast<int64_t>(q0 + tid) * a.n_etiles + et] = lcnt[tid];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int qo = qw + 4 * mt + g;
+        if (col == 0 && qo < a.n_tok) a.cnt[static_cast<int64_t>(qo) * a.n_etiles + et] = run[mt];
+      }
     }
   }
 }
@@ -857,7 +903,7 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
 // Per query: tau from its sampled scores.
 __global__ __launch_bounds__(256) void idx_chunk_tau_kernel(const IdxChunkArgs a) {
   __shared__ int hist[kTauBins];
-  __shared__ float red[16];
+  __shared__ float red[32];
   __shared__ int sh[4];
   const int qi = blockIdx.x;
   const int N = (a.pos0 + qi + 1) / a.r;
@@ -870,74 +916,7 @@ __global__ __launch_bounds__(256) void idx_chunk_tau_kernel(const IdxChunkArgs a
   if (threadIdx.x == 0) a.tau[qi] = tau;
 }
 
-// Exact k-th largest key of c keys in LDS (c >= k): linear score bins, then an
-// exact rank inside the bin holding it. Returns false if that bin is too full.
-__device__ bool kth_key_binned(const uint64_t *keys, int c, int k, int *hist, float *red, int *sh, uint64_t *bin_keys,
-                               uint64_t *kth_out) {
-  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int i = t; i < c; i += bd) {
-    const float v = __uint_as_float(static_cast<uint32_t>(keys[i] >> 32));
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-  }
-  lo = block_reduce_min(lo, red);
-  hi = block_reduce_max(hi, red);
-  const float sc = hi > lo ? static_cast<float>(kSelBins - 1) / (hi - lo) : 0.f;
-  auto bin_of = [&](uint64_t key) {
-    return min(kSelBins - 1, static_cast<int>((__uint_as_float(static_cast<uint32_t>(key >> 32)) - lo) * sc));
-  };
-  for (int i = t; i < kSelBins; i += bd) hist[i] = 0;
-  __syncthreads();
-  for (int i = t; i < c; i += bd) atomicAdd(&hist[bin_of(keys[i])], 1);
-  __syncthreads();
-  constexpr int kMaxPer = kSelBins / 256;
-  const int per = kSelBins / bd;
-  int cnt[kMaxPer], tot = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    cnt[j] = j < per ? hist[kSelBins - 1 - per * t - j] : 0;
-    tot += cnt[j];
-  }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  __shared__ int wsum3[16];
-  if (lane == 63) wsum3[w] = incl;
-  __syncthreads();
-  for (int i = 0; i < w; ++i) incl += wsum3[i];
-  const int excl = incl - tot;
-  if (excl < k && incl >= k) {
-    int cum = excl;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      if (j < per && cum + cnt[j] >= k) { sh[0] = kSelBins - 1 - per * t - j; sh[1] = cum; break; }
-      cum += cnt[j];
-    }
-  }
-  __syncthreads();
-  const int bstar = sh[0], need = k - sh[1];
-  const int m = hist[bstar];
-  if (m > kRankCap) return false;
-  if (t == 0) sh[2] = 0;
-  __syncthreads();
-  for (int i = t; i < c; i += bd)
-    if (bin_of(keys[i]) == bstar) bin_keys[atomicAdd(&sh[2], 1)] = keys[i];
-  __syncthreads();
-  for (int i = t; i < m; i += bd) {
-    const uint64_t x = bin_keys[i];
-    int r = 0;
-    for (int j = 0; j < m; ++j) r += bin_keys[j] > x;
-    if (r == need - 1) sh[3] = i;
-  }
-  __syncthreads();
-  *kth_out = bin_keys[sh[3]];
-  return true;
-}
-
+// Element loads for the fallback's plain re-scoring of one row.
 __device__ __forceinline__ float chunk_q(const IdxChunkArgs &a, int q, int h, int d) {
   const int64_t i = (static_cast<int64_t>(q) * a.h_i + h) * kDI + d;
   return a.act_dtype == DT_F32 ? reinterpret_cast<const float *>(a.q_idx)[i]
@@ -950,17 +929,19 @@ __device__ __forceinline__ float chunk_k(const IdxChunkArgs &a, int pp, int slot
   return fp8x2_to_f32<false>(reinterpret_cast<const uint8_t *>(a.kidx)[i])[0];
 }
 
+// Per query: its candidates (per-tile slot runs, already in entry order) are
+// gathered into LDS and the exact Top-K is selected and written ascending.
 __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArgs a) {
-  __shared__ uint64_t keys[kChunkCandCap];
+  __shared__ uint64_t keys[kChunkCandCap];   // the fallback reuses it as its index list
   __shared__ uint64_t bin_keys[kRankCap];
-  __shared__ uint32_t bitmap[kBitmapWords];
   __shared__ int hist[kSelBins];
-  __shared__ int sel[CSA_MAX_TOPK];
-  __shared__ float red[16];
+  __shared__ float red[32];
   __shared__ int sh[4];
   __shared__ int wsum[16];
   __shared__ int toff[kMaxChunkTiles + 1];
-  const int qi = blockIdx.x, tid = threadIdx.x, bd = blockDim.x, lane = tid & 63, w = tid >> 6;
+  int *sel = reinterpret_cast<int *>(keys);
+  static_assert(kChunkCandCap * 2 >= CSA_MAX_TOPK, "fallback index list fits the key buffer");
+  const int qi = blockIdx.x, tid = threadIdx.x, bd = blockDim.x;
   const int N = (a.pos0 + qi + 1) / a.r, k = a.k;
   int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
   if (N <= k) {
@@ -981,69 +962,31 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
   block_prefix_sum(toff, n_tiles, wsum);
   const int c = toff[n_tiles];
   bool done = false;
-  if (sh[3] == 0 && c >= k && c <= kChunkCandCap && N <= kBitmapWords * 32) {
-    const float *cs = a.cand_s + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
-    const int32_t *cj = a.cand_j + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
+  if (sh[3] == 0 && c >= k && c <= kChunkCandCap && n_tiles <= kMaxChunkTiles) {
+    const uint64_t *cq = a.cand + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
     constexpr int kPer = kChunkCandCap / 512;
-    float ts[kPer];
-    int tj[kPer];
+    uint64_t tk[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = u * 512 + tid;
-      ts[u] = 0.f;
-      tj[u] = 0;
+      tk[u] = 0;
       if (i < c) {
-        int lo = 0, hi = n_tiles;
+        int lo = 0, hi = n_tiles;       // tile with toff[lo] <= i < toff[lo + 1]
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
           if (toff[mid] <= i) lo = mid; else hi = mid;
         }
-        const int64_t o = static_cast<int64_t>(lo) * kWgCand + (i - toff[lo]);
-        ts[u] = cs[o];
-        tj[u] = cj[o];
+        tk[u] = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];
       }
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = u * 512 + tid;
-      if (i < c) keys[i] = score_key(ts[u], tj[u]);
+      if (i < c) keys[i] = tk[u];
     }
-    const int nwords = (N + 31) >> 5;
-    for (int i = tid; i < nwords; i += bd) bitmap[i] = 0u;
     __syncthreads();
-    uint64_t kth = 0;
-    if (kth_key_binned(keys, c, k, hist, red, sh, bin_keys, &kth)) {
-      for (int i = tid; i < c; i += bd)
-        if (keys[i] >= kth) {
-          const int j = key_index(keys[i]);
-          atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-        }
-      __syncthreads();
-      // ascending output: thread-contiguous word ranges, popcount prefix
-      const int span = (nwords + bd - 1) / bd;
-      const int w0 = min(nwords, tid * span), w1 = min(nwords, w0 + span);
-      int mine = 0;
-      for (int i = w0; i < w1; ++i) mine += __popc(bitmap[i]);
-      int incl = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      if (lane == 63) wsum[w] = incl;
-      __syncthreads();
-      for (int i = 0; i < w; ++i) incl += wsum[i];
-      int pos = incl - mine;
-      for (int i = w0; i < w1; ++i) {
-        uint32_t bits = bitmap[i];
-        while (bits) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          out[pos++] = i * 32 + b;
-        }
-      }
-      done = true;
-    }
+    done = select_ordered(keys, c, k, hist, red, sh, bin_keys, out);
+    __syncthreads();
   }
   if (!done) {
     // too few or too many candidates, or heavy ties: score the whole row and select exactly
@@ -1052,12 +995,6 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
     float *row = a.fb_rows + static_cast<int64_t>(qi) * a.fb_stride;
     const int t = a.pos0 + qi;
     (void)t;
-    float qv[CSA_MAX_IDX_HEADS][kDI];
-    float wv[CSA_MAX_IDX_HEADS];
-    for (int h = 0; h < a.h_i; ++h) {
-      wv[h] = a.w_idx[qi * a.h_i + h];
-      for (int d = 0; d < kDI; ++d) qv[h][d] = chunk_q(a, qi, h, d);
-    }
     for (int e = tid; e < N; e += bd) {
       const int pp = a.bt_row[e >> 6];
       float sres = -1.f;
@@ -1066,8 +1003,8 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
         float acc = 0.f;
         for (int h = 0; h < a.h_i; ++h) {
           float dot = 0.f;
-          for (int d = 0; d < kDI; ++d) dot += qv[h][d] * chunk_k(a, pp, e & 63, d);
-          acc += wv[h] * fmaxf(dot, 0.f);
+          for (int d = 0; d < kDI; ++d) dot += chunk_q(a, qi, h, d) * chunk_k(a, pp, e & 63, d);
+          acc += a.w_idx[qi * a.h_i + h] * fmaxf(dot, 0.f);
         }
         sres = acc * sc;
       }
@@ -1104,7 +1041,7 @@ void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hip
   const int n_qt = (a.n_tok + kCQ - 1) / kCQ;
   auto gemm = [&](auto mode_tag, int n_et, hipEvent_t e0, hipEvent_t e1) {
     constexpr int M = decltype(mode_tag)::value;
-    const int n_wg = n_qt * ((n_et + kChunkTilesPerWg - 1) / kChunkTilesPerWg);
+    const int n_wg = n_qt * ((n_et + chunk_tiles_per_wg<M>() - 1) / chunk_tiles_per_wg<M>());
     if (n_wg <= 0) return;
     if (kv == DT_F32 && act == DT_F32)
       hipExtLaunchKernelGGL((idx_chunk_gemm_kernel<DT_F32, DT_F32, M>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a);
