@@ -46,6 +46,10 @@ __device__ __forceinline__ CT to_ct(float x) {
   }
 }
 
+__device__ __forceinline__ float f4_at(const float4 &f, int i) {
+  return i == 0 ? f.x : (i == 1 ? f.y : (i == 2 ? f.z : f.w));
+}
+
 // Raw bytes of one 32-element segment of a row, by storage dtype.
 template <int SD> struct Seg { uint4 u[SD == DT_F32 ? 8 : (SD == DT_BF16 ? 4 : 2)]; };
 
@@ -128,7 +132,11 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
   __shared__ __align__(16) char kv_lds[KV_LDS];
   __shared__ int32_t src_row[kAttMaxSplitKeys];   // >= 0 pool row; < 0: -(ring row) - 1
   __shared__ uint8_t kvalid[kAttMaxSplitKeys];
-  __shared__ float ksc[KSTR][kKeyBlock], vsc[KSTR][kKeyBlock];
+  // per key of the block: logit = S * kmul + kbias (kmul = scale x page scale,
+  // kbias = -inf for a masked key), probability weight vsc = value page scale
+  __shared__ __align__(16) float kmul[KSTR][kKeyBlock];
+  __shared__ __align__(16) float kbias[KSTR][kKeyBlock];
+  __shared__ __align__(16) float vsc[KSTR][kKeyBlock];
   __shared__ float sm_m[KSTR][H], sm_l[KSTR][H];
   CT *Ks = reinterpret_cast<CT *>(kv_lds);                       // [KSTR][64][KS]
   CT *Vt = Ks + KSTR * kKeyBlock * KS;                           // [KSTR][D][VS]
@@ -243,7 +251,11 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
     for (int u = 0; u < 32; ++u) kd[u] = kv[u];
 #pragma unroll
     for (int u = 0; u < 32; ++u) vd[u * VS] = vv[u];
-    if (psg == 0) { ksc[st][pk] = x.ks; vsc[st][pk] = x.vs; }
+    if (psg == 0) {
+      kmul[st][pk] = x.kind != 0 ? a.scale * x.ks : 0.f;
+      kbias[st][pk] = x.kind != 0 ? 0.f : -INFINITY;
+      vsc[st][pk] = x.vs;
+    }
   };
   It items[PREFETCH ? ITEMS : 1];
   auto load_round = [&](int r) {
@@ -298,18 +310,32 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
     const CT *Vb = Vt + ks * kD * VS;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
+      // S^T tiles; the next tile's K fragments are read while this one multiplies
       f32x4_t S[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      Frag<CT> kf[2][4];
+      auto load_kf = [&](Frag<CT> (&dst)[4], int kt) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const CT *src = Kb + (16 * kt + col) * KS + 32 * g + 8 * c;
-          Frag<CT> kf;
-          if constexpr (sizeof(CT) == 4) kf = LoadFrag<DT_F32, float>::load(src);
-          else kf = LoadFrag<DT_BF16, __bf16>::load(src);
-          S[kt] = mma(kf, qf[j][c], S[kt]);
+          if constexpr (sizeof(CT) == 4) dst[c] = LoadFrag<DT_F32, float>::load(src);
+          else dst[c] = LoadFrag<DT_BF16, __bf16>::load(src);
         }
+      };
+      load_kf(kf[0], 0);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        if (kt + 1 < 4) load_kf(kf[(kt + 1) & 1], kt + 1);
+        S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) S[kt] = mma(kf[kt & 1][c], qf[j][c], S[kt]);
+      }
+      // per-key factors of the lane's keys 16*kt + 4*g + v, four at a time
+      float4 km[4], kbi[4], vs4[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        km[kt] = *reinterpret_cast<const float4 *>(&kmul[ks][16 * kt + 4 * g]);
+        kbi[kt] = *reinterpret_cast<const float4 *>(&kbias[ks][16 * kt + 4 * g]);
+        vs4[kt] = *reinterpret_cast<const float4 *>(&vsc[ks][16 * kt + 4 * g]);
       }
       // logits and online softmax (lane's head = col; keys 16*kt + 4*g + v)
       float x[4][4];
@@ -318,8 +344,7 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int key = 16 * kt + 4 * g + v;
-          x[kt][v] = kvalid[kb0 + key] ? S[kt][v] * (a.scale * ksc[ks][key]) : -INFINITY;
+          x[kt][v] = fmaf(S[kt][v], f4_at(km[kt], v), f4_at(kbi[kt], v));
           bm = fmaxf(bm, x[kt][v]);
         }
       bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
@@ -343,28 +368,36 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
 #pragma unroll
         for (int n = 0; n < 8; ++n) O[j][n][v] *= av;
       }
+      // O += P . V over the two 32-key halves; V^T fragments read one step ahead
+      auto load_vf = [&](int kc, int n) {
+        const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
+        Frag<CT> vf;
+        if constexpr (sizeof(CT) == 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) { vf.v[u] = vr[u]; vf.v[4 + u] = vr[16 + u]; }
+        } else {
+          const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+          const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
+          vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
+        return vf;
+      };
+      Frag<CT> vfb[2];
+      vfb[0] = load_vf(0, 0);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         float pv[8];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          pv[v] = p[2 * kc][v] * vsc[ks][32 * kc + 4 * g + v];
-          pv[4 + v] = p[2 * kc + 1][v] * vsc[ks][32 * kc + 16 + 4 * g + v];
+          pv[v] = p[2 * kc][v] * f4_at(vs4[2 * kc], v);
+          pv[4 + v] = p[2 * kc + 1][v] * f4_at(vs4[2 * kc + 1], v);
         }
         const Frag<CT> pf = frag_from_f32(pv, static_cast<Frag<CT> *>(nullptr));
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
-          Frag<CT> vf;
-          if constexpr (sizeof(CT) == 4) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) { vf.v[u] = vr[u]; vf.v[4 + u] = vr[16 + u]; }
-          } else {
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
-            vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          }
-          O[j][n] = mma(pf, vf, O[j][n]);
+          const int step = kc * 8 + n;
+          if (step + 1 < 16) vfb[(step + 1) & 1] = load_vf((step + 1) >> 3, (step + 1) & 7);
+          O[j][n] = mma(pf, vfb[step & 1], O[j][n]);
         }
       }
     }
