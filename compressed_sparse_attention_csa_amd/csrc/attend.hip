@@ -9,22 +9,25 @@
 //
 // Work decomposition. The keys of a query are cut into blocks of 64 (Top-K
 // blocks first, then window blocks). A workgroup owns (query, split), a split
-// being a run of blocks, and has HG x KSTR waves: HG head groups times KSTR
-// key streams. Each round it gathers KSTR blocks (one per stream) into LDS, K
-// row-major and V transposed in the MFMA compute type (fp8 codes convert
-// exactly to bf16; page scales are applied to the logits and probabilities),
-// while the next round's rows are already being loaded into registers. Wave
-// (head group, stream) then runs, for its 16-head tiles and its stream's block:
+// being a run of blocks, and has HG waves (head groups). Each round it gathers
+// one block into LDS, K row-major and V transposed in the MFMA compute type
+// (fp8 codes convert exactly to bf16; page scales are applied to the logits
+// and probabilities): a block's rows move as 16-byte chunks, 16 consecutive
+// lanes per 256-byte row, and the next block is already in flight in
+// registers during this block's math. Each wave then runs, for its 16-head
+// tiles:
 //   S^T[key][head] = K . Q^T  (keys as MFMA rows, heads as columns), so a lane
 //   holds one head and 4 keys per 16-key tile; after the online-softmax update
 //   those probabilities are already the A operand of O = P . V (heads as rows,
 //   keys contracted) against V^T from LDS.
-// The streams' (m, l, O) are merged in LDS at the end. With one split per
-// query the workgroup writes the output; with several, each writes its (m, l,
-// O) partial and a merge kernel combines them with the log-sum-exp rescaling,
-// which equals one softmax over the union of all keys. (A merge by the last
-// split to finish would need a device-scope release fence per workgroup, which
-// on this multi-XCD part writes back the L2 and costs more than the launch.)
+// With one split per query the workgroup writes the output; with several,
+// each writes its (m, l, O) partial and a merge kernel combines them with the
+// log-sum-exp rescaling, which equals one softmax over the union of all keys.
+// (A merge by the last split to finish would need a device-scope release
+// fence per workgroup, which on this multi-XCD part writes back the L2 and
+// costs more than the launch.)
+#include <type_traits>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -46,100 +49,78 @@ __device__ __forceinline__ CT to_ct(float x) {
   }
 }
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i supplies the address of
+// 4 consecutive 16-bit values D[i][0..3]; lane j receives D[4q + j/4][j%4],
+// q = 0..3 (a transposed 16 x 4 tile).
+__device__ __forceinline__ uint2 lds_read_tr16(const void *p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t *)(const_cast<void *>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
 __device__ __forceinline__ float f4_at(const float4 &f, int i) {
   return i == 0 ? f.x : (i == 1 ? f.y : (i == 2 ? f.z : f.w));
 }
 
-// Raw bytes of one 32-element segment of a row, by storage dtype.
-template <int SD> struct Seg { uint4 u[SD == DT_F32 ? 8 : (SD == DT_BF16 ? 4 : 2)]; };
-
-template <int SD>
-__device__ __forceinline__ void load_seg(Seg<SD> &s, const char *src) {
-  const uint4 *p = reinterpret_cast<const uint4 *>(src);
-#pragma unroll
-  for (int q = 0; q < static_cast<int>(sizeof(s.u) / 16); ++q) s.u[q] = p[q];
-}
-template <int SD>
-__device__ __forceinline__ void zero_seg(Seg<SD> &s) {
-#pragma unroll
-  for (int q = 0; q < static_cast<int>(sizeof(s.u) / 16); ++q) s.u[q] = make_uint4(0, 0, 0, 0);
-}
-
-// Segment -> 32 compute-type values.
+// 16 bytes of a row (E = 16 / element size elements) -> compute type.
 template <int SD, typename CT>
-__device__ __forceinline__ void seg_values(const Seg<SD> &s, CT *dst) {
+__device__ __forceinline__ void chunk_values(const uint4 &u, CT *dst) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   if constexpr (SD == DT_F32) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      dst[4 * q + 0] = to_ct<CT>(__uint_as_float(s.u[q].x)); dst[4 * q + 1] = to_ct<CT>(__uint_as_float(s.u[q].y));
-      dst[4 * q + 2] = to_ct<CT>(__uint_as_float(s.u[q].z)); dst[4 * q + 3] = to_ct<CT>(__uint_as_float(s.u[q].w));
-    }
+    for (int q = 0; q < 4; ++q) dst[q] = to_ct<CT>(__uint_as_float(w[q]));
   } else if constexpr (SD == DT_BF16) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t w[4] = {s.u[q].x, s.u[q].y, s.u[q].z, s.u[q].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dst[8 * q + 2 * u + 0] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[u] & 0xffffu));
-        dst[8 * q + 2 * u + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[u] >> 16));
-      }
+      dst[2 * q + 0] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[q] & 0xffffu));
+      dst[2 * q + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w[q] >> 16));
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t w[4] = {s.u[q].x, s.u[q].y, s.u[q].z, s.u[q].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x2_t lo = fp8x2_to_bf16<false>(w[u]), hi = fp8x2_to_bf16<true>(w[u]);
-        dst[16 * q + 4 * u + 0] = lo[0]; dst[16 * q + 4 * u + 1] = lo[1];
-        dst[16 * q + 4 * u + 2] = hi[0]; dst[16 * q + 4 * u + 3] = hi[1];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2_t lo = fp8x2_to_bf16<false>(w[q]), hi = fp8x2_to_bf16<true>(w[q]);
+      dst[4 * q + 0] = lo[0]; dst[4 * q + 1] = lo[1];
+      dst[4 * q + 2] = hi[0]; dst[4 * q + 3] = hi[1];
     }
   }
 }
 
+constexpr int32_t kMaskedRow = INT32_MIN;   // src_row of a key that takes no part
 
-// One gather item: 32 dims of one key's K and V row, as raw bytes of either
-// the pool format (KV) or the window-ring format (ACT); kind says which.
-template <int ACT, int KV>
-struct Item {
-  static constexpr int RW = (sizeof(Seg<KV>) > sizeof(Seg<ACT>) ? sizeof(Seg<KV>) : sizeof(Seg<ACT>)) / 16;
-  uint4 k[RW], v[RW];
-  float ks, vs;
-  int kind;   // 0 masked, 1 pool row, 2 ring row
-};
+template <int SD> constexpr int elem_bytes_of() { return SD == DT_F32 ? 4 : (SD == DT_BF16 ? 2 : 1); }
 
-template <int SD, int RW>
-__device__ __forceinline__ const Seg<SD> &as_seg(const uint4 (&u)[RW]) {
-  return *reinterpret_cast<const Seg<SD> *>(&u[0]);
-}
-
-// HG: head groups (waves per stream); NTW: 16-head tiles per wave; KSTR: key streams.
-template <int ACT, int KV, int HG, int NTW, int KSTR>
-__global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs a) {
+// HG: head groups (waves); NTW: 16-head tiles per wave.
+template <int ACT, int KV, int HG, int NTW>
+__global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   using CT = typename ComputeT<KV>::type;
-  constexpr int NT = HG * KSTR * 64;
+  constexpr int NT = HG * 64;
   constexpr int H = HG * NTW * 16;
-  constexpr int KE = KV == DT_F32 ? 4 : (KV == DT_BF16 ? 2 : 1);
-  constexpr int AE = ACT == DT_F32 ? 4 : 2;
+  constexpr int KE = elem_bytes_of<KV>(), AE = elem_bytes_of<ACT>();
   constexpr int KS = kD + kpad<CT>();          // K row stride (elements)
-  constexpr int VS = kKeyBlock + kpad<CT>();   // V^T row stride (elements)
-  constexpr int ITEMS = KSTR * 256 / NT;       // gather items per thread per round
-  constexpr bool PREFETCH = KV != DT_F32;      // fp32 rows are too large to hold a round in registers
-  constexpr int KV_LDS = KSTR * (kKeyBlock * KS + kD * VS) * static_cast<int>(sizeof(CT));
-  static_assert((KSTR - 1) * H * kD * 4 <= KV_LDS, "stream partials must fit in the K/V buffers");
+  // bf16: V row-major like K, read as transposed MFMA fragments; fp32: V^T
+  constexpr bool VROW = sizeof(CT) == 2;
+  constexpr int VS = VROW ? KS : kKeyBlock + kpad<CT>();   // V (or V^T) row stride (elements)
+  // a block's K and V rows move as 16-byte chunks, 16 consecutive lanes per
+  // 256-byte row, so every wave load covers whole rows
+  constexpr int CPR_P = kD * KE / 16, CPR_R = kD * AE / 16;   // chunks per pool / ring row
+  constexpr int CPR_MAX = CPR_P > CPR_R ? CPR_P : CPR_R;
+  static_assert((CPR_P & (CPR_P - 1)) == 0 && (CPR_R & (CPR_R - 1)) == 0, "chunks per row are powers of two");
+  constexpr int U = 2 * kKeyBlock * CPR_MAX / NT;              // chunk slots per thread per block
+  constexpr bool PREFETCH = U <= 8;                            // whole block held in registers
+  constexpr int KV_LDS = (kKeyBlock * KS + (VROW ? kKeyBlock : kD) * VS) * static_cast<int>(sizeof(CT));
 
   __shared__ __align__(16) char kv_lds[KV_LDS];
-  __shared__ int32_t src_row[kAttMaxSplitKeys];   // >= 0 pool row; < 0: -(ring row) - 1
+  __shared__ int32_t src_row[kAttMaxSplitKeys];   // >= 0 pool row; < 0: -(ring row) - 1; kMaskedRow
   __shared__ uint8_t kvalid[kAttMaxSplitKeys];
   // per key of the block: logit = S * kmul + kbias (kmul = scale x page scale,
   // kbias = -inf for a masked key), probability weight vsc = value page scale
-  __shared__ __align__(16) float kmul[KSTR][kKeyBlock];
-  __shared__ __align__(16) float kbias[KSTR][kKeyBlock];
-  __shared__ __align__(16) float vsc[KSTR][kKeyBlock];
-  __shared__ float sm_m[KSTR][H], sm_l[KSTR][H];
-  CT *Ks = reinterpret_cast<CT *>(kv_lds);                       // [KSTR][64][KS]
-  CT *Vt = Ks + KSTR * kKeyBlock * KS;                           // [KSTR][D][VS]
+  __shared__ __align__(16) float kmul[kKeyBlock];
+  __shared__ __align__(16) float kbias[kKeyBlock];
+  __shared__ __align__(16) float vsc[kKeyBlock];
+  CT *Ks = reinterpret_cast<CT *>(kv_lds);                       // [64][KS]
+  CT *Vt = Ks + kKeyBlock * KS;                                  // [64][VS] (bf16) or [D][VS]
 
   const int qi = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
   const int seq = a.chunk ? a.seq0 : a.qd[qi].seq;
@@ -201,80 +182,129 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
         row = -(seq * a.R + r % a.R) - 1;
       }
     }
-    src_row[i] = row;
+    src_row[i] = valid ? row : kMaskedRow;
     kvalid[i] = valid;
   }
   __syncthreads();
 
-  // ---------------- gather: item = (stream, key, 32-dim segment)
-  using It = Item<ACT, KV>;
-  auto load_item = [&](It &x, int gi, int r) {
-    const int st = gi >> 8, pk = gi & 63, psg = (gi >> 6) & 3;
-    const int b = b_begin + r * KSTR + st;
-    const int i = (b - b_begin) * kKeyBlock + pk;
-    x.ks = 1.f;
-    x.vs = 1.f;
-    x.kind = 0;
-    if (b >= b_end || kvalid[i] == 0) return;
-    const int64_t row = src_row[i];
-    if (row >= 0) {
-      x.kind = 1;
-      const int64_t off = (row * kD + 32 * psg) * KE;
-      load_seg(*reinterpret_cast<Seg<KV> *>(&x.k[0]), reinterpret_cast<const char *>(a.kbar) + off);
-      load_seg(*reinterpret_cast<Seg<KV> *>(&x.v[0]), reinterpret_cast<const char *>(a.vbar) + off);
-      if constexpr (KV == DT_FP8) {
-        if (psg == 0) { x.ks = a.kbar_scale[row >> 6]; x.vs = a.vbar_scale[row >> 6]; }
+  // ---------------- gather: slot s of block b = (K or V, key, 16-byte chunk)
+  // A masked slot's register is never written (a zero written beside an
+  // in-flight load would have to wait for it); vmask says which slots hold data.
+  uint4 raw[PREFETCH ? U : 1];
+  uint32_t vmask = 0;
+  float ks_pref = 1.f, vs_pref = 1.f;   // page scales of key tid (tid < 64)
+  // slot s of a block with cpr (a power of two) chunks per row: (K or V, key, chunk)
+  auto slot_key = [](int s, int cpr) { return (s & (kKeyBlock * cpr - 1)) >> (31 - __builtin_clz(cpr)); };
+  // 16-byte chunk of slot s, for a block whose rows live at kbase / vbase with
+  // row_bytes per row (ring rows are stored as -(row) - 1)
+  auto slot_ptr = [](const char *kbase, const char *vbase, int64_t row_bytes, int s, int cpr, int32_t row) {
+    const int kv = s >= kKeyBlock * cpr;
+    const int64_t r = row >= 0 ? row : -static_cast<int64_t>(row) - 1;
+    return reinterpret_cast<const uint4 *>((kv ? vbase : kbase) + r * row_bytes) + (s & (cpr - 1));
+  };
+  auto load_scales = [&](int b) {
+    ks_pref = vs_pref = 1.f;
+    if constexpr (KV == DT_FP8) {
+      if (tid < kKeyBlock && b < a.n_sparse_blocks) {
+        const int i = (b - b_begin) * kKeyBlock + tid;
+        const int32_t row = src_row[i];
+        if (row != kMaskedRow) {
+          ks_pref = a.kbar_scale[row >> 6];
+          vs_pref = a.vbar_scale[row >> 6];
+        }
       }
-    } else {
-      x.kind = 2;
-      const int64_t off = ((-row - 1) * kD + 32 * psg) * AE;
-      load_seg(*reinterpret_cast<Seg<ACT> *>(&x.k[0]), reinterpret_cast<const char *>(a.ring_k) + off);
-      load_seg(*reinterpret_cast<Seg<ACT> *>(&x.v[0]), reinterpret_cast<const char *>(a.ring_v) + off);
     }
   };
-  auto commit_item = [&](const It &x, int gi) {
-    const int st = gi >> 8, pk = gi & 63, psg = (gi >> 6) & 3;
-    CT kv[32], vv[32];
-    if (x.kind == 1) {
-      seg_values<KV, CT>(as_seg<KV>(x.k), kv);
-      seg_values<KV, CT>(as_seg<KV>(x.v), vv);
-    } else if (x.kind == 2) {
-      seg_values<ACT, CT>(as_seg<ACT>(x.k), kv);
-      seg_values<ACT, CT>(as_seg<ACT>(x.v), vv);
+  // chunk -> compute type -> K row-major or V^T in LDS; SD is the storage type
+  // of the block's rows (pool or ring), so the element count is a constant
+  auto commit_chunk = [&](auto sd_tag, int s, const uint4 &u) {
+    constexpr int SD = decltype(sd_tag)::value;
+    constexpr int E = 16 / elem_bytes_of<SD>();
+    constexpr int CPR = kD / E;
+    if (s >= 2 * kKeyBlock * CPR) return;
+    const int kv = s >= kKeyBlock * CPR;
+    const int L = s - kv * kKeyBlock * CPR;
+    const int key = L / CPR, d0 = (L % CPR) * E;
+    CT vals[E];
+    chunk_values<SD, CT>(u, vals);
+    if (kv == 0) {
+      CT *kd = Ks + key * KS + d0;
+#pragma unroll
+      for (int q = 0; q < E; ++q) kd[q] = vals[q];
+    } else if constexpr (VROW) {
+      CT *vd = Vt + key * VS + d0;
+#pragma unroll
+      for (int q = 0; q < E; ++q) vd[q] = vals[q];
     } else {
+      CT *vd = Vt + d0 * VS + key;
 #pragma unroll
-      for (int u = 0; u < 32; ++u) { kv[u] = to_ct<CT>(0.f); vv[u] = to_ct<CT>(0.f); }
-    }
-    CT *kd = Ks + (st * kKeyBlock + pk) * KS + 32 * psg;
-    CT *vd = Vt + st * kD * VS + (32 * psg) * VS + pk;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) kd[u] = kv[u];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) vd[u * VS] = vv[u];
-    if (psg == 0) {
-      kmul[st][pk] = x.kind != 0 ? a.scale * x.ks : 0.f;
-      kbias[st][pk] = x.kind != 0 ? 0.f : -INFINITY;
-      vsc[st][pk] = x.vs;
+      for (int q = 0; q < E; ++q) vd[q * VS] = vals[q];
     }
   };
-  It items[PREFETCH ? ITEMS : 1];
+  auto commit_slot = [&](int b, int s, const uint4 &u) {
+    if constexpr (KV == ACT) {
+      commit_chunk(std::integral_constant<int, KV>{}, s, u);
+    } else {
+      if (b < a.n_sparse_blocks) commit_chunk(std::integral_constant<int, KV>{}, s, u);
+      else commit_chunk(std::integral_constant<int, ACT>{}, s, u);
+    }
+  };
   auto load_round = [&](int r) {
+    const int b = b_begin + r;
+    if constexpr (PREFETCH) {
+      vmask = 0;
+      if (b < b_end) {
+        const bool pool = b < a.n_sparse_blocks;
+        const int cpr = pool ? CPR_P : CPR_R;
+        const int nslot = 2 * kKeyBlock * cpr;
+        const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
+        const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
+        const int64_t row_bytes = pool ? kD * KE : kD * AE;
+        // every slot's row first (one LDS round trip), then every load
+        int32_t rows[U];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) load_item(items[it], tid + it * NT, r);
+        for (int u = 0; u < U; ++u) {
+          const int s = tid + u * NT;
+          rows[u] = s < nslot ? src_row[(b - b_begin) * kKeyBlock + slot_key(s, cpr)] : kMaskedRow;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (rows[u] != kMaskedRow) {
+            raw[u] = *slot_ptr(kbase, vbase, row_bytes, tid + u * NT, cpr, rows[u]);
+            vmask |= 1u << u;
+          }
+        }
+      }
+    }
+    if (b < b_end) load_scales(b);
   };
   auto commit_round = [&](int r) {
+    const int b = b_begin + r;
     if constexpr (PREFETCH) {
 #pragma unroll
-      for (int it = 0; it < ITEMS; ++it) commit_item(items[it], tid + it * NT);
+      for (int u = 0; u < U; ++u) commit_slot(b, tid + u * NT, ((vmask >> u) & 1u) ? raw[u] : make_uint4(0, 0, 0, 0));
     } else {
-      for (int it = 0; it < ITEMS; ++it) {
-        load_item(items[0], tid + it * NT, r);
-        commit_item(items[0], tid + it * NT);
+      const bool pool = b < a.n_sparse_blocks;
+      const int cpr = pool ? CPR_P : CPR_R;
+      const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
+      const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
+      const int64_t row_bytes = pool ? kD * KE : kD * AE;
+      for (int u = 0; u < U; ++u) {
+        const int s = tid + u * NT;
+        if (s >= 2 * kKeyBlock * cpr) break;
+        const int32_t row = src_row[(b - b_begin) * kKeyBlock + slot_key(s, cpr)];
+        commit_slot(b, s, row != kMaskedRow ? *slot_ptr(kbase, vbase, row_bytes, s, cpr, row) : make_uint4(0, 0, 0, 0));
       }
+    }
+    if (tid < kKeyBlock) {
+      const bool valid = kvalid[(b - b_begin) * kKeyBlock + tid] != 0;
+      kmul[tid] = valid ? a.scale * ks_pref : 0.f;
+      kbias[tid] = valid ? 0.f : -INFINITY;
+      vsc[tid] = vs_pref;
     }
   };
 
-  const int lane = tid & 63, w = tid >> 6, hg = w % HG, ks = w / HG, g = lane >> 4, col = lane & 15;
+  const int lane = tid & 63, hg = tid >> 6, g = lane >> 4, col = lane & 15;
 
   // Q fragments (B operand of S^T) for this wave's head tiles
   Frag<CT> qf[NTW][4];
@@ -292,22 +322,15 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
     l_run[j] = 0.f;
   }
 
-  const int n_rounds = (b_end - b_begin + KSTR - 1) / KSTR;
-  if constexpr (PREFETCH) {
-    if (n_rounds > 0) load_round(0);
-  }
+  const int n_rounds = b_end - b_begin;
+  if (n_rounds > 0) load_round(0);
   for (int r = 0; r < n_rounds; ++r) {
     __syncthreads();                   // previous round's LDS reads are done
     commit_round(r);
     __syncthreads();
-    if constexpr (PREFETCH) {
-      if (r + 1 < n_rounds) load_round(r + 1);   // in flight during this round's math
-    }
-    const int b = b_begin + r * KSTR + ks;
-    if (b >= b_end) continue;
-    const int kb0 = (b - b_begin) * kKeyBlock;
-    const CT *Kb = Ks + ks * kKeyBlock * KS;
-    const CT *Vb = Vt + ks * kD * VS;
+    if (r + 1 < n_rounds) load_round(r + 1);   // in flight during this round's math
+    const CT *Kb = Ks;
+    const CT *Vb = Vt;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       // S^T tiles; the next tile's K fragments are read while this one multiplies
@@ -330,12 +353,11 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
         for (int c = 0; c < 4; ++c) S[kt] = mma(kf[kt & 1][c], qf[j][c], S[kt]);
       }
       // per-key factors of the lane's keys 16*kt + 4*g + v, four at a time
-      float4 km[4], kbi[4], vs4[4];
+      float4 km[4], kbi[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        km[kt] = *reinterpret_cast<const float4 *>(&kmul[ks][16 * kt + 4 * g]);
-        kbi[kt] = *reinterpret_cast<const float4 *>(&kbias[ks][16 * kt + 4 * g]);
-        vs4[kt] = *reinterpret_cast<const float4 *>(&vsc[ks][16 * kt + 4 * g]);
+        km[kt] = *reinterpret_cast<const float4 *>(&kmul[16 * kt + 4 * g]);
+        kbi[kt] = *reinterpret_cast<const float4 *>(&kbias[16 * kt + 4 * g]);
       }
       // logits and online softmax (lane's head = col; keys 16*kt + 4*g + v)
       float x[4][4];
@@ -370,18 +392,25 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
       }
       // O += P . V over the two 32-key halves; V^T fragments read one step ahead
       auto load_vf = [&](int kc, int n) {
-        const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
         Frag<CT> vf;
-        if constexpr (sizeof(CT) == 4) {
+        if constexpr (VROW) {
+          // keys 32kc + 4g + (0..3) and + 16 for dim 16n + col: in each 16-lane
+          // group lane i reads 4 dims of key 4g + i/4, and the transposing read
+          // hands lane col those 4 keys at its dim
+          const CT *vr = Vb + (32 * kc + 4 * g + (col >> 2)) * VS + 16 * n + 4 * (col & 3);
+          const uint2 lo = lds_read_tr16(vr);
+          const uint2 hi = lds_read_tr16(vr + 16 * VS);
+          vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
 #pragma unroll
           for (int u = 0; u < 4; ++u) { vf.v[u] = vr[u]; vf.v[4 + u] = vr[16 + u]; }
-        } else {
-          const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
-          vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
         return vf;
       };
+      float4 vs4[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) vs4[kt] = *reinterpret_cast<const float4 *>(&vsc[16 * kt + 4 * g]);
       Frag<CT> vfb[2];
       vfb[0] = load_vf(0, 0);
 #pragma unroll
@@ -403,60 +432,20 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
     }
   }
 
-  // ---------------- 2. merge the key streams in LDS (stream 0 keeps the result)
-  float *po = reinterpret_cast<float *>(kv_lds);   // [KSTR-1][H][D] partial outputs of streams >= 1
-  __syncthreads();                                 // all rounds done: K/V buffers are free
+  // ---------------- 2. per O row (head 16*tile + 4g + v): its running max and sum
+  float Lh[NTW][4], Mh[NTW][4];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    const int h0 = 16 * (hg + HG * j);
     float l_tot = l_run[j] + __shfl_xor(l_run[j], 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    if (g == 0) {
-      sm_m[ks][h0 + col] = m_run[j];
-      sm_l[ks][h0 + col] = l_tot;
-    }
-    if (ks > 0) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int n = 0; n < 8; ++n) po[((ks - 1) * H + h0 + 4 * g + v) * kD + 16 * n + col] = O[j][n][v];
-    }
-  }
-  __syncthreads();
-  float Lh[NTW][4];   // per O row (head 4g + v of each tile): merged denominator and max
-  float Mh[NTW][4];
-  if (ks == 0) {
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int h0 = 16 * (hg + HG * j);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int h = h0 + 4 * g + v;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < KSTR; ++s) mx = fmaxf(mx, sm_m[s][h]);
-        float L = 0.f;
-        float al[KSTR];
-#pragma unroll
-        for (int s = 0; s < KSTR; ++s) {
-          al[s] = (sm_m[s][h] == -INFINITY) ? 0.f : __expf(sm_m[s][h] - mx);
-          L += al[s] * sm_l[s][h];
-        }
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          float o = al[0] * O[j][n][v];
-#pragma unroll
-          for (int s = 1; s < KSTR; ++s) o += al[s] * po[((s - 1) * H + h) * kD + 16 * n + col];
-          O[j][n][v] = o;
-        }
-        Lh[j][v] = L;
-        Mh[j][v] = mx;
-      }
+    for (int v = 0; v < 4; ++v) {
+      Mh[j][v] = __shfl(m_run[j], 4 * g + v, 64);
+      Lh[j][v] = __shfl(l_tot, 4 * g + v, 64);
     }
   }
 
   if (a.n_splits == 1) {
-    if (ks != 0) return;
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -476,21 +465,19 @@ __global__ __launch_bounds__(HG * KSTR * 64) void attend_kernel(const AttendArgs
 
   // ---------------- 3. several splits: write this split's partial; the merge kernel combines them
   const int64_t pbase = static_cast<int64_t>(qi) * a.n_splits + split;
-  if (ks == 0) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+  for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int h = 16 * (hg + HG * j) + 4 * g + v;
-        float *pr = a.part_o + (pbase * H + h) * kD;
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * (hg + HG * j) + 4 * g + v;
+      float *pr = a.part_o + (pbase * H + h) * kD;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) pr[16 * n + col] = O[j][n][v];
-        if (col == 0) {
-          a.part_ml[(pbase * 2 + 0) * H + h] = Mh[j][v];
-          a.part_ml[(pbase * 2 + 1) * H + h] = Lh[j][v];
-        }
+      for (int n = 0; n < 8; ++n) pr[16 * n + col] = O[j][n][v];
+      if (col == 0) {
+        a.part_ml[(pbase * 2 + 0) * H + h] = Mh[j][v];
+        a.part_ml[(pbase * 2 + 1) * H + h] = Lh[j][v];
       }
-  }
+    }
 }
 
 // Combines the split partials of (query, head): one softmax over the union of
@@ -524,23 +511,15 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   else reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(out);
 }
 
-template <int ACT, int KV, int KSTR>
-void launch_attend_k(const AttendArgs &a, int n_wg, hipStream_t s) {
-  switch (a.H) {
-    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1, KSTR>), dim3(n_wg), dim3(1 * KSTR * 64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1, KSTR>), dim3(n_wg), dim3(2 * KSTR * 64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1, KSTR>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2, KSTR>), dim3(n_wg), dim3(4 * KSTR * 64), 0, s, a); break;
-    default: break;
-  }
-}
-
 template <int ACT, int KV>
 void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s) {
-  // decode: one block per split (latency-bound); a prefill chunk walks all of a
-  // query's blocks in one workgroup, two blocks per round
-  if (a.chunk && KV != DT_F32) launch_attend_k<ACT, KV, kAttChunkKeyStreams>(a, n_wg, s);
-  else launch_attend_k<ACT, KV, kAttKeyStreams>(a, n_wg, s);
+  switch (a.H) {
+    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(128), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(256), 0, s, a); break;
+    default: break;
+  }
 }
 
 }  // namespace
