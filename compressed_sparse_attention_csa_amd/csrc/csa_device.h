@@ -38,12 +38,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN kept quiet).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16: the compiler emits gfx950's
+// v_cvt_pk_bf16_f32 (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two at once (one v_cvt_pk_bf16_f32): lo in bits 0-15, hi in bits 16-31.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ------------------------------------------------------------------ fp8 e4m3
@@ -134,8 +139,7 @@ __device__ __forceinline__ Frag<float> frag_from_f32(const float *x, Frag<float>
 __device__ __forceinline__ Frag<__bf16> frag_from_f32(const float *x, Frag<__bf16> *) {
   uint32_t w[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    w[u] = static_cast<uint32_t>(f32_to_bf16(x[2 * u])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * u + 1])) << 16);
+  for (int u = 0; u < 4; ++u) w[u] = f32x2_to_bf16x2(x[2 * u], x[2 * u + 1]);
   Frag<__bf16> f;
   f.v = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
   return f;
