@@ -115,9 +115,9 @@ def lib() -> C.CDLL:
     L.csa_read_errors.restype = C.c_int
     L.csa_read_errors.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
     L.csa_profile_begin.restype = C.c_int
-    L.csa_profile_begin.argtypes = [vp]
+    L.csa_profile_begin.argtypes = [vp, C.c_int32]
     L.csa_profile_end.restype = C.c_int
-    L.csa_profile_end.argtypes = [vp, C.POINTER(C.c_double), pi32]
+    L.csa_profile_end.argtypes = [vp, C.c_int32, C.POINTER(C.c_double), pi32]
     L.csa_debug_convert.restype = C.c_int
     L.csa_debug_convert.argtypes = [i32, vp, vp, i64, vp]
     _LIB = L
@@ -201,14 +201,18 @@ def csa_read_errors(h: int, stream=None) -> int:
     return int(v.value)
 
 
-def csa_profile_begin(h: int) -> None:
-    check(lib().csa_profile_begin(C.c_void_p(h)))
+PROFILE_INDEX = 1    # CSA_PROFILE_INDEX
+PROFILE_ATTEND = 2   # CSA_PROFILE_ATTEND
 
 
-def csa_profile_end(h: int) -> tuple[float, int]:
+def csa_profile_begin(h: int, kernels: int = PROFILE_INDEX) -> None:
+    check(lib().csa_profile_begin(C.c_void_p(h), int(kernels)))
+
+
+def csa_profile_end(h: int, kernel: int = PROFILE_INDEX) -> tuple[float, int]:
     ms = C.c_double(0.0)
     n = C.c_int32(0)
-    check(lib().csa_profile_end(C.c_void_p(h), C.byref(ms), C.byref(n)))
+    check(lib().csa_profile_end(C.c_void_p(h), int(kernel), C.byref(ms), C.byref(n)))
     return float(ms.value), int(n.value)
 
 

@@ -28,6 +28,8 @@
 // costs more than the launch.)
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -512,23 +514,23 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
 }
 
 template <int ACT, int KV>
-void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s) {
+void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.H) {
-    case 16: hipLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(128), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(256), 0, s, a); break;
+    case 16: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(64), 0, s, e0, e1, 0, a); break;
+    case 32: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
+    case 64: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
+    case 128: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
     default: break;
   }
 }
 
 }  // namespace
 
-void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s) {
+void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (n_wg <= 0) return;
-  if (kv == DT_F32 && act == DT_F32) launch_attend_t<DT_F32, DT_F32>(a, n_wg, s);
-  else if (kv == DT_BF16 && act == DT_BF16) launch_attend_t<DT_BF16, DT_BF16>(a, n_wg, s);
-  else if (kv == DT_FP8 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP8>(a, n_wg, s);
+  if (kv == DT_F32 && act == DT_F32) launch_attend_t<DT_F32, DT_F32>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_BF16 && act == DT_BF16) launch_attend_t<DT_BF16, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP8 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP8>(a, n_wg, s, ev0, ev1);
   if (a.n_splits > 1) {
     if (act == DT_F32) hipLaunchKernelGGL(attend_merge_kernel<DT_F32>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);
     else hipLaunchKernelGGL(attend_merge_kernel<DT_BF16>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);

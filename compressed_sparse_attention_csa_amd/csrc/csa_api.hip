@@ -22,9 +22,10 @@ struct csa_cache {
   uint32_t *err;             // device error word (workspace head)
   char *scratch;             // workspace after the head
   size_t scratch_bytes;
-  bool profiling;
-  std::vector<hipEvent_t> events;  // start/stop pairs
-  size_t events_used;
+  int32_t profiling;                 // CSA_PROFILE_* bits being recorded
+  std::vector<hipEvent_t> events;    // start/stop pairs
+  std::vector<int32_t> event_kind;   // CSA_PROFILE_* bit of each pair
+  size_t events_used;                // pairs in use
 };
 
 namespace {
@@ -136,19 +137,21 @@ bool is_chunk(int n, const int32_t *seq, const int32_t *pos) {
 // hipExtLaunchKernelGGL, which stamps them with the kernel's own start and end.
 struct ProfPair { hipEvent_t start = nullptr, stop = nullptr; };
 
-ProfPair prof_events(csa_cache_t h, hipStream_t s) {
-  if (!h->profiling) return {};
+ProfPair prof_events(csa_cache_t h, hipStream_t s, int32_t kind) {
+  if (!(h->profiling & kind)) return {};
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return {};
-  if (h->events_used + 2 > h->events.size()) {
+  if (2 * (h->events_used + 1) > h->events.size()) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return {};
     if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return {}; }
     h->events.push_back(a);
     h->events.push_back(b);
+    h->event_kind.push_back(0);
   }
-  ProfPair p{h->events[h->events_used], h->events[h->events_used + 1]};
-  h->events_used += 2;
+  ProfPair p{h->events[2 * h->events_used], h->events[2 * h->events_used + 1]};
+  h->event_kind[h->events_used] = kind;
+  ++h->events_used;
   return p;
 }
 
@@ -245,7 +248,7 @@ csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_
   h->err = reinterpret_cast<uint32_t *>(bufs->workspace);
   h->scratch = reinterpret_cast<char *>(bufs->workspace) + kHead;
   h->scratch_bytes = bufs->workspace_bytes - kHead;
-  h->profiling = false;
+  h->profiling = 0;
   h->events_used = 0;
   *out = h;
   return CSA_OK;
@@ -433,7 +436,7 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
     s.n_etiles = (n_max + 255) / 256;
     s.n_stiles = (n_max / kChunkSample + 255) / 256;
     s.kv_dtype = kv; s.act_dtype = act;
-    const ProfPair ev = prof_events(h, stream);
+    const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
     launch_idx_chunk(s, kv, act, stream, ev.start, ev.stop);
     launch_idx_chunk_select(s, stream);
   } else {
@@ -491,7 +494,7 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
       }
       f.slice0[nq] = slices;
       s.total_wg = wg;
-      const ProfPair ev = prof_events(h, stream);
+      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
       launch_idx_scan(s, kv, act, stream, ev.start, ev.stop);
       launch_idx_filter(f, slices, stream);
       launch_idx_final(fin, stream);
@@ -538,7 +541,8 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
     a.q = q; a.out = out; a.topk = topk;
     a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0];
     a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
-    launch_attend(a, n_q, kv, act, stream);
+    const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
+    launch_attend(a, n_q, kv, act, stream, ev.start, ev.stop);
   } else {
     for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {
       const int nq = std::min(kAttMaxQ, n_q - g0);
@@ -557,7 +561,8 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
         b.part_o = reinterpret_cast<float *>(h->scratch);
         b.part_ml = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(nq) * b.n_splits * c.q_heads * kD * 4, 256));
       }
-      launch_attend(b, nq * b.n_splits, kv, act, stream);
+      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
+      launch_attend(b, nq * b.n_splits, kv, act, stream, ev.start, ev.stop);
     }
   }
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_attend");
@@ -574,26 +579,34 @@ csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags) {
   return CSA_OK;
 }
 
-csa_status csa_profile_begin(csa_cache_t h) {
+csa_status csa_profile_begin(csa_cache_t h, int32_t kernels) {
   if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
-  h->profiling = true;
+  if (kernels <= 0 || (kernels & ~(CSA_PROFILE_INDEX | CSA_PROFILE_ATTEND)))
+    return fail(CSA_ERR_INVALID_ARG, "kernels must be a nonzero mask of CSA_PROFILE_INDEX / CSA_PROFILE_ATTEND");
+  h->profiling = kernels;
   h->events_used = 0;
   return CSA_OK;
 }
 
-csa_status csa_profile_end(csa_cache_t h, double *total_ms, int32_t *launches) {
+csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int32_t *launches) {
   if (!handle_ok(h) || !total_ms || !launches) return fail(CSA_ERR_INVALID_ARG, "invalid arguments");
+  if (kernel != CSA_PROFILE_INDEX && kernel != CSA_PROFILE_ATTEND)
+    return fail(CSA_ERR_INVALID_ARG, "kernel must be CSA_PROFILE_INDEX or CSA_PROFILE_ATTEND");
   double tot = 0.0;
-  for (size_t i = 0; i + 1 < h->events_used; i += 2) {
-    if (hipEventSynchronize(h->events[i + 1]) != hipSuccess) return fail(CSA_ERR_HIP, "event synchronize failed");
+  int32_t n = 0;
+  for (size_t i = 0; i < h->events_used; ++i) {
+    if (h->event_kind[i] != kernel) continue;
+    if (hipEventSynchronize(h->events[2 * i + 1]) != hipSuccess) return fail(CSA_ERR_HIP, "event synchronize failed");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, h->events[i], h->events[i + 1]) != hipSuccess) return fail(CSA_ERR_HIP, "elapsed time failed");
+    if (hipEventElapsedTime(&ms, h->events[2 * i], h->events[2 * i + 1]) != hipSuccess)
+      return fail(CSA_ERR_HIP, "elapsed time failed");
     tot += ms;
+    ++n;
   }
   *total_ms = tot;
-  *launches = static_cast<int32_t>(h->events_used / 2);
-  h->profiling = false;
-  h->events_used = 0;
+  *launches = n;
+  h->profiling &= ~kernel;
+  if (h->profiling == 0) h->events_used = 0;
   return CSA_OK;
 }
 

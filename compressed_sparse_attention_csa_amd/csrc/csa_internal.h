@@ -156,7 +156,9 @@ struct AttendArgs {
   AttQuery qd[kAttMaxQ];
 };
 
-void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s);
+// ev0/ev1 (may be null): events stamped with the start and end of the attention kernel launch.
+void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
+                   hipEvent_t ev1 = nullptr);
 
 
 }  // namespace csa

@@ -233,14 +233,20 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
  * range was met; bit 2: an internal capacity fallback ran) and clears it. */
 csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags);
 
-/* Timing of the indexer score kernel (the dominant kernel of a decode step;
- * in chunk mode the GEMM pass that scores every visible entry): after
- * csa_profile_begin, every csa_index_topk call issued outside stream capture
- * launches that kernel with a HIP event pair stamped with the kernel's own
- * start and end (hipExtLaunchKernelGGL); csa_profile_end synchronises and
- * returns the summed elapsed milliseconds and the number of timed launches. */
-csa_status csa_profile_begin(csa_cache_t h);
-csa_status csa_profile_end(csa_cache_t h, double *total_ms, int32_t *launches);
+/* Kernel timing. csa_profile_begin(h, kernels) starts recording, for every
+ * later call on h issued outside stream capture, a HIP event pair stamped by
+ * the kernel launch itself (hipExtLaunchKernelGGL) around:
+ *   CSA_PROFILE_INDEX   the indexer score kernel of csa_index_topk (the decode
+ *                       scan; in chunk mode the GEMM pass that scores every
+ *                       visible entry);
+ *   CSA_PROFILE_ATTEND  the attention kernel of csa_attend (not its split merge).
+ * csa_profile_end(h, kernel, ...) synchronises and returns the summed elapsed
+ * milliseconds and the number of timed launches of one kind (one bit), and
+ * stops recording that kind. Errors: CSA_ERR_INVALID_ARG for a bad mask. */
+#define CSA_PROFILE_INDEX 1
+#define CSA_PROFILE_ATTEND 2
+csa_status csa_profile_begin(csa_cache_t h, int32_t kernels);
+csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int32_t *launches);
 
 /* Runs the device number-format routines on n values (tests of the codecs):
  * kind 0: fp8 e4m3 codes (uint8) -> fp32 as the attention/indexer kernels decode them;

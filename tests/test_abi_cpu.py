@@ -183,3 +183,22 @@ def test_destroyed_handle_rejected():
     assert L.csa_seq_reset(C.c_void_p(0), 0) == 1
     assert L.csa_cache_destroy(C.c_void_p(0)) == 1
     assert L.csa_debug_convert(7, C.c_void_p(0x10), C.c_void_p(0x10), 4, C.c_void_p(0)) == 1
+
+
+def test_profile_masks_validated():
+    """Kernel-timing calls take a mask of CSA_PROFILE_INDEX (1) / CSA_PROFILE_ATTEND (2);
+    with nothing launched, ending a kind returns zero launches."""
+    cfg = _spec()
+    h = _fake_handle(cfg)
+    L = B.lib()
+    try:
+        assert L.csa_profile_begin(C.c_void_p(h), 0) == 1
+        assert L.csa_profile_begin(C.c_void_p(h), 4) == 1
+        assert L.csa_profile_begin(C.c_void_p(h), 3) == 0
+        ms, n = C.c_double(-1.0), C.c_int32(-1)
+        assert L.csa_profile_end(C.c_void_p(h), 3, C.byref(ms), C.byref(n)) == 1
+        assert L.csa_profile_end(C.c_void_p(h), 2, C.byref(ms), C.byref(n)) == 0
+        assert n.value == 0 and ms.value == 0.0
+        assert B.csa_profile_end(h, B.PROFILE_INDEX) == (0.0, 0)
+    finally:
+        B.csa_cache_destroy(h)
