@@ -31,6 +31,8 @@ Parity status per function (what pins it in ``tests/test_oracle.py``):
   topk .................. brute-force full sort with hand-made tie fixtures
   attend / attend_step .. r = 1, k = all, W = 0 -> torch SDPA causal; k = 0 ->
                           banded SDPA; single key; equal logits -> mean
+  hca_attend_step ....... r = 1, W = 0 -> torch SDPA causal; a pure-Python
+                          loop softmax over the explicit key list
 None is "parity unpinned".
 """
 from __future__ import annotations
@@ -300,6 +302,22 @@ def attend_step(q: np.ndarray, T: np.ndarray, t: int, W: int, scale: float,
     keys = np.concatenate([np.asarray(kbar, np.float64)[ent], np.asarray(rawk, np.float64)[rows]], axis=0)
     vals = np.concatenate([np.asarray(vbar, np.float64)[ent], np.asarray(rawv, np.float64)[rows]], axis=0)
     return attend(q, keys, vals, scale)
+
+
+def hca_attend_step(q: np.ndarray, t: int, r: int, W: int, scale: float,
+                    kbar: np.ndarray, vbar: np.ndarray, rawk: np.ndarray, rawv: np.ndarray,
+                    swa_start: int = 0) -> np.ndarray:
+    """Heavily compressed attention for one query: no indexer, every visible
+    compressed entry takes part.
+
+    [Atlas] compressed-KV entry: HCA uses the same compression primitive far
+    more aggressively (large r) and then runs ordinary dense attention over
+    the resulting short stream. Reading: the layer keeps the sliding-window
+    branch of the CSA layers (W = 0 drops it), and the softmax runs over the
+    union exactly as in attend_step.
+    """
+    T = np.arange(visible_entries(t, r), dtype=np.int64)
+    return attend_step(q, T, t, W, scale, kbar, vbar, rawk, rawv, swa_start)
 
 
 def softmax_weights(q: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:

@@ -395,3 +395,40 @@ def test_worked_sizes(golden_dir):
     assert A.prefill_visible_scores(131072, 2048, 4) == 67_632_640
     assert A.index_flops(67_632_640, 4, 64) == 34_627_911_680
     assert A.attend_flops(2048, 64, 1152, 128) == 77_309_411_328
+
+
+# --------------------------------------------------------------------------- heavily compressed attention
+
+def test_hca_ratio1_no_window_is_dense_causal_attention():
+    """HCA runs dense attention over the compressed stream ([Atlas] compressed
+    KV); with r = 1 and no window that is plain causal attention."""
+    L, H, D = 40, 3, 16
+    K, V, Z = _rand_rows(L, D), _rand_rows(L, D), _rand_rows(L, D)
+    kbar, vbar, _ = O.compress(K, V, Z, 1)
+    Q = RNG.standard_normal((L, H, D))
+    scale = 1 / math.sqrt(D)
+    out = np.stack([O.hca_attend_step(Q[t], t, 1, 0, scale, kbar, vbar, K, V) for t in range(L)])
+    ref = _sdpa(Q, K, V, causal=True, scale=scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("r,W,t,s", [(4, 0, 37, 0), (4, 6, 37, 0), (8, 3, 50, 0), (8, 10, 63, 58), (16, 5, 14, 0)])
+def test_hca_matches_loop_softmax_over_explicit_keys(r, W, t, s):
+    """Brute force: every entry j with (j+1)*r <= t+1 plus rows
+    [max(s, t-W+1), t], one softmax per head written as plain Python loops."""
+    L, H, D = 64, 2, 6
+    K, V, Z = _rand_rows(L, D), _rand_rows(L, D), _rand_rows(L, D)
+    kbar, vbar, _ = O.compress(K, V, Z, r)
+    q = RNG.standard_normal((H, D))
+    scale = 0.4
+    got = O.hca_attend_step(q, t, r, W, scale, kbar, vbar, K, V, swa_start=s)
+    keys = [(kbar[j], vbar[j]) for j in range(L // r) if (j + 1) * r <= t + 1]
+    if W > 0:
+        keys += [(K[i], V[i]) for i in range(max(s, t - W + 1), t + 1)]
+    for h in range(H):
+        logits = [scale * sum(q[h][d] * kv[0][d] for d in range(D)) for kv in keys]
+        m = max(logits)
+        e = [math.exp(x - m) for x in logits]
+        tot = sum(e)
+        want = [sum(e[i] * keys[i][1][d] for i in range(len(keys))) / tot for d in range(D)]
+        np.testing.assert_allclose(got[h], want, rtol=0, atol=1e-12)
