@@ -71,7 +71,7 @@ EXPORTS = [
     "csa_status_string", "csa_last_error", "csa_buffer_sizes_for", "csa_workspace_size",
     "csa_cache_create", "csa_cache_destroy", "csa_seq_reset", "csa_seq_len", "csa_seq_set_len",
     "csa_compress", "csa_index_topk", "csa_attend", "csa_read_errors",
-    "csa_profile_begin", "csa_profile_end", "csa_debug_convert",
+    "csa_profile_begin", "csa_profile_end", "csa_debug_convert", "csa_attend_dense",
 ]
 
 _LIB = None
@@ -112,6 +112,8 @@ def lib() -> C.CDLL:
     L.csa_index_topk.argtypes = [vp, i32, pi32, pi32, vp, vp, i32, vp, vp]
     L.csa_attend.restype = C.c_int
     L.csa_attend.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, i32, C.c_float, vp, vp]
+    L.csa_attend_dense.restype = C.c_int
+    L.csa_attend_dense.argtypes = [vp, i32, i32, pi32, pi32, vp, C.c_float, vp, vp]
     L.csa_read_errors.restype = C.c_int
     L.csa_read_errors.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
     L.csa_profile_begin.restype = C.c_int
@@ -193,6 +195,11 @@ def csa_index_topk(h: int, q_seq, q_pos, q_idx, w_idx, k: int, topk, stream=None
 def csa_attend(h: int, layer: int, q_seq, q_pos, q, topk, k: int, scale: float, out, stream=None) -> None:
     check(lib().csa_attend(C.c_void_p(h), layer, len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q), _ptr(topk),
                            k, float(scale), _ptr(out), _stream(stream)))
+
+
+def csa_attend_dense(h: int, layer: int, q_seq, q_pos, q, scale: float, out, stream=None) -> None:
+    check(lib().csa_attend_dense(C.c_void_p(h), layer, len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q),
+                                 float(scale), _ptr(out), _stream(stream)))
 
 
 def csa_read_errors(h: int, stream=None) -> int:

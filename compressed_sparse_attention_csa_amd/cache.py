@@ -66,14 +66,15 @@ class CsaCache:
         dev = self.device
         self.kbar = [torch.zeros((P, 64, D), dtype=kvt, device=dev) for _ in range(L)]
         self.vbar = [torch.zeros((P, 64, D), dtype=kvt, device=dev) for _ in range(L)]
-        self.kidx = torch.zeros((P, 64, DI), dtype=kvt, device=dev)
+        idx = spec.idx_heads > 0   # an HCA group (idx_heads = 0) has no indexer keys
+        self.kidx = torch.zeros((P, 64, DI), dtype=kvt, device=dev) if idx else None
         fp8 = spec.kv_dtype == "fp8"
         self.kbar_scale = [torch.ones(P, dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
         self.vbar_scale = [torch.ones(P, dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
-        self.kidx_scale = torch.ones(P, dtype=torch.float32, device=dev) if fp8 else None
+        self.kidx_scale = torch.ones(P, dtype=torch.float32, device=dev) if fp8 and idx else None
         self.kbar_stage = [torch.zeros((S, 64, D), dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
         self.vbar_stage = [torch.zeros((S, 64, D), dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
-        self.kidx_stage = torch.zeros((S, 64, DI), dtype=torch.float32, device=dev) if fp8 else None
+        self.kidx_stage = torch.zeros((S, 64, DI), dtype=torch.float32, device=dev) if fp8 and idx else None
         self.ring_k = [torch.zeros((S, R, D), dtype=actt, device=dev) for _ in range(L)]
         self.ring_v = [torch.zeros((S, R, D), dtype=actt, device=dev) for _ in range(L)]
         self.gate_stage = [torch.zeros((S, spec.ratio, D), dtype=actt, device=dev) for _ in range(L)]
@@ -100,10 +101,11 @@ class CsaCache:
                 b.vbar_scale[l] = self.vbar_scale[l].data_ptr()
                 b.kbar_stage[l] = self.kbar_stage[l].data_ptr()
                 b.vbar_stage[l] = self.vbar_stage[l].data_ptr()
-        b.kidx = self.kidx.data_ptr()
-        if fp8:
-            b.kidx_scale = self.kidx_scale.data_ptr()
-            b.kidx_stage = self.kidx_stage.data_ptr()
+        if idx:
+            b.kidx = self.kidx.data_ptr()
+            if fp8:
+                b.kidx_scale = self.kidx_scale.data_ptr()
+                b.kidx_stage = self.kidx_stage.data_ptr()
         b.block_table = self.block_table.data_ptr()
         b.workspace = self.workspace.data_ptr()
         b.workspace_bytes = ws
@@ -124,6 +126,12 @@ class CsaCache:
         if out is None:
             out = torch.empty_like(q)
         B.csa_attend(self.handle, layer, q_seq, q_pos, q, topk, k, scale, out, stream)
+        return out
+
+    def attend_dense(self, layer, q_seq, q_pos, q, scale, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        B.csa_attend_dense(self.handle, layer, q_seq, q_pos, q, scale, out, stream)
         return out
 
     def seq_len(self, layer, seq):

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   const int b_end = min(a.n_blocks, b_begin + a.blocks_per_split);
   const int n_keys = (b_end - b_begin) * kKeyBlock;
   const int32_t *bt = a.block_table + static_cast<int64_t>(seq) * a.bt_stride;
-  const int32_t *trow = a.topk + static_cast<int64_t>(qi) * a.k;
+  const int32_t *trow = a.dense ? nullptr : a.topk + static_cast<int64_t>(qi) * a.k;
   const int tid = threadIdx.x;
 
   // ---------------- 1. resolve every key of the split once: all Top-K reads
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       const int b = b_begin + i / kKeyBlock, kk = i % kKeyBlock;
       if (b < a.n_sparse_blocks) {
         const int slot = b * kKeyBlock + kk;
-        jv[u] = slot < a.k ? trow[slot] : -1;
+        jv[u] = a.dense ? (slot < n_vis ? slot : -1) : (slot < a.k ? trow[slot] : -1);
       }
     }
   }

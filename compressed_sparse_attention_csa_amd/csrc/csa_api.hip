@@ -52,13 +52,13 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 csa_status check_config(const csa_config *c) {
   if (!c) return fail(CSA_ERR_INVALID_ARG, "config is NULL");
-  if (c->ratio < 1 || c->ratio > 64) return fail(CSA_ERR_UNSUPPORTED, "ratio %d outside [1, 64]", c->ratio);
+  if (c->ratio < 1 || c->ratio > 256) return fail(CSA_ERR_UNSUPPORTED, "ratio %d outside [1, 256]", c->ratio);
   if (c->head_dim != CSA_HEAD_DIM) return fail(CSA_ERR_UNSUPPORTED, "head_dim %d != %d", c->head_dim, CSA_HEAD_DIM);
   if (c->idx_dim != CSA_IDX_DIM) return fail(CSA_ERR_UNSUPPORTED, "idx_dim %d != %d", c->idx_dim, CSA_IDX_DIM);
   if (!(c->q_heads == 16 || c->q_heads == 32 || c->q_heads == 64 || c->q_heads == 128))
     return fail(CSA_ERR_UNSUPPORTED, "q_heads %d not in {16, 32, 64, 128}", c->q_heads);
-  if (c->idx_heads < 1 || c->idx_heads > CSA_MAX_IDX_HEADS)
-    return fail(CSA_ERR_UNSUPPORTED, "idx_heads %d outside [1, %d]", c->idx_heads, CSA_MAX_IDX_HEADS);
+  if (c->idx_heads < 0 || c->idx_heads > CSA_MAX_IDX_HEADS)
+    return fail(CSA_ERR_UNSUPPORTED, "idx_heads %d outside [0, %d]", c->idx_heads, CSA_MAX_IDX_HEADS);
   if (c->window < 0) return fail(CSA_ERR_SHAPE, "window %d < 0", c->window);
   if (c->ring_rows < std::max(std::max(c->window, c->ratio), 1))
     return fail(CSA_ERR_SHAPE, "ring_rows %d < max(window, ratio, 1)", c->ring_rows);
@@ -199,10 +199,11 @@ csa_status csa_buffer_sizes_for(const csa_config *cfg, csa_buffer_sizes *out) {
   const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3;
   const int kb = dt_bytes(cfg->kv_dtype), ab = dt_bytes(cfg->act_dtype);
   out->kv_pool = P * kPage * kD * kb;
-  out->idx_pool = P * kPage * kDI * kb;
+  const bool idx = cfg->idx_heads > 0;
+  out->idx_pool = idx ? P * kPage * kDI * kb : 0;
   out->page_scale = fp8 ? P * 4 : 0;
   out->kv_stage = fp8 ? S * kPage * kD * 4 : 0;
-  out->idx_stage = fp8 ? S * kPage * kDI * 4 : 0;
+  out->idx_stage = fp8 && idx ? S * kPage * kDI * 4 : 0;
   out->ring = S * static_cast<size_t>(cfg->ring_rows) * kD * ab;
   out->gate_stage = S * static_cast<size_t>(cfg->ratio) * kD * ab;
   out->block_table = S * static_cast<size_t>(cfg->max_pages_per_seq) * 4;
@@ -233,9 +234,10 @@ csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_
     if (fp8 && (!bufs->kbar_scale[l] || !bufs->vbar_scale[l] || !bufs->kbar_stage[l] || !bufs->vbar_stage[l]))
       return fail(CSA_ERR_INVALID_ARG, "layer %d: fp8 caches need scale and staging buffers", l);
   }
-  if (!bufs->kidx || !bufs->block_table || !bufs->workspace)
-    return fail(CSA_ERR_INVALID_ARG, "kidx, block_table and workspace are required");
-  if (fp8 && (!bufs->kidx_scale || !bufs->kidx_stage))
+  if (!bufs->block_table || !bufs->workspace)
+    return fail(CSA_ERR_INVALID_ARG, "block_table and workspace are required");
+  if (cfg->idx_heads > 0 && !bufs->kidx) return fail(CSA_ERR_INVALID_ARG, "kidx is required when idx_heads > 0");
+  if (cfg->idx_heads > 0 && fp8 && (!bufs->kidx_scale || !bufs->kidx_stage))
     return fail(CSA_ERR_INVALID_ARG, "fp8 caches need kidx_scale and kidx_stage");
   if (reinterpret_cast<uintptr_t>(bufs->workspace) % 256 != 0) return fail(CSA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (bufs->workspace_bytes < kHead + 1024) return fail(CSA_ERR_CAPACITY, "workspace too small");
@@ -291,8 +293,8 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
   const csa_config &c = h->cfg;
   if (layer < 0 || layer >= c.n_layers) return fail(CSA_ERR_INVALID_ARG, "layer %d out of range", layer);
   if (n_seqs < 1 || !seq_ids || !n_new) return fail(CSA_ERR_INVALID_ARG, "n_seqs >= 1 with seq_ids and n_new required");
-  if ((layer == 0) != (proj_idx != nullptr))
-    return fail(CSA_ERR_INVALID_ARG, "layer 0 (and only layer 0) must pass proj_idx");
+  if ((layer == 0 && h->cfg.idx_heads > 0) != (proj_idx != nullptr))
+    return fail(CSA_ERR_INVALID_ARG, "layer 0 (and only layer 0) of a group with an indexer must pass proj_idx");
   int64_t total = 0;
   std::vector<char> seen(c.max_seqs, 0);
   for (int i = 0; i < n_seqs; ++i) {
@@ -399,6 +401,7 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
                           const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
   if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
   const csa_config &c = h->cfg;
+  if (c.idx_heads == 0) return fail(CSA_ERR_UNSUPPORTED, "this layer group has no indexer (idx_heads = 0)");
   if (n_q < 1 || !q_seq || !q_pos || !q_idx || !w_idx || !topk)
     return fail(CSA_ERR_INVALID_ARG, "n_q >= 1 and all pointers are required");
   if (k < 1 || k > CSA_MAX_TOPK) return fail(CSA_ERR_UNSUPPORTED, "k = %d outside [1, %d]", k, CSA_MAX_TOPK);
@@ -504,14 +507,21 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
   return CSA_OK;
 }
 
-csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q,
-                      const int32_t *topk, int32_t k, float scale, void *out, hipStream_t stream) {
+namespace {
+
+// Shared by csa_attend (keys = the Top-K rows) and csa_attend_dense (keys =
+// every visible entry: topk is NULL and k is replaced by the largest visible count).
+csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                       const void *q, const int32_t *topk, int32_t k, bool dense, float scale, void *out,
+                       hipStream_t stream) {
   if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
   const csa_config &c = h->cfg;
   if (layer < 0 || layer >= c.n_layers) return fail(CSA_ERR_INVALID_ARG, "layer %d out of range", layer);
   if (n_q < 1 || !q_seq || !q_pos || !q || !out) return fail(CSA_ERR_INVALID_ARG, "n_q >= 1 and q_seq, q_pos, q, out required");
-  if (k < 0 || k > CSA_MAX_TOPK) return fail(CSA_ERR_UNSUPPORTED, "k = %d outside [0, %d]", k, CSA_MAX_TOPK);
-  if (k > 0 && !topk) return fail(CSA_ERR_INVALID_ARG, "topk required when k > 0");
+  if (!dense) {
+    if (k < 0 || k > CSA_MAX_TOPK) return fail(CSA_ERR_UNSUPPORTED, "k = %d outside [0, %d]", k, CSA_MAX_TOPK);
+    if (k > 0 && !topk) return fail(CSA_ERR_INVALID_ARG, "topk required when k > 0");
+  }
   for (int i = 0; i < n_q; ++i) {
     if (q_seq[i] < 0 || q_seq[i] >= c.max_seqs) return fail(CSA_ERR_INVALID_ARG, "q_seq[%d] out of range", i);
     const int64_t L = h->len[static_cast<size_t>(layer) * c.max_seqs + q_seq[i]];
@@ -519,6 +529,13 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
       return fail(CSA_ERR_INVALID_ARG, "q_pos[%d] = %d not below the layer's sequence length %lld", i, q_pos[i], static_cast<long long>(L));
     if (c.window > 0 && (L - 1 - q_pos[i]) > c.ring_rows - c.window)
       return fail(CSA_ERR_CAPACITY, "query %d: window rows already left the %d-row ring", i, c.ring_rows);
+  }
+  if (dense) {
+    k = 0;
+    for (int i = 0; i < n_q; ++i) k = std::max(k, (q_pos[i] + 1) / c.ratio);
+    if (static_cast<int64_t>(n_blocks_for(k, c.window)) > static_cast<int64_t>(kMaxSplits) * (kAttMaxSplitKeys / kKeyBlock))
+      return fail(CSA_ERR_UNSUPPORTED, "dense attention over %d entries exceeds %d", k,
+                  kMaxSplits * kAttMaxSplitKeys - (c.window + kKeyBlock - 1) / kKeyBlock * kKeyBlock);
   }
   const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
@@ -529,15 +546,13 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
   a.ring_k = h->buf.ring_k[layer]; a.ring_v = h->buf.ring_v[layer];
   a.block_table = h->buf.block_table;
   a.err = h->err;
-  a.scale = scale; a.k = k; a.W = c.window; a.R = c.ring_rows; a.r = c.ratio;
+  a.scale = scale; a.k = k; a.W = c.window; a.R = c.ring_rows; a.r = c.ratio; a.dense = dense ? 1 : 0;
   a.bt_stride = c.max_pages_per_seq; a.pool_pages = c.pool_pages; a.H = c.q_heads;
   a.n_sparse_blocks = (k + kKeyBlock - 1) / kKeyBlock;
   a.n_blocks = n_blocks_for(k, c.window);
   const size_t qrow = static_cast<size_t>(c.q_heads) * kD * ab;
 
-  if (is_chunk(n_q, q_seq, q_pos)) {
-    if (a.n_blocks * kKeyBlock > kAttMaxSplitKeys)
-      return fail(CSA_ERR_UNSUPPORTED, "a prefill chunk supports at most %d keys per query", kAttMaxSplitKeys);
+  if (is_chunk(n_q, q_seq, q_pos) && a.n_blocks * kKeyBlock <= kAttMaxSplitKeys) {
     a.q = q; a.out = out; a.topk = topk;
     a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0];
     a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
@@ -549,7 +564,7 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
       AttendArgs b = a;
       b.q = reinterpret_cast<const char *>(q) + g0 * qrow;
       b.out = reinterpret_cast<char *>(out) + g0 * qrow;
-      b.topk = topk ? topk + static_cast<int64_t>(g0) * k : nullptr;
+      b.topk = topk && !dense ? topk + static_cast<int64_t>(g0) * k : nullptr;
       b.chunk = 0; b.n_q = nq;
       for (int i = 0; i < nq; ++i) { b.qd[i].seq = q_seq[g0 + i]; b.qd[i].pos = q_pos[g0 + i]; }
       const int nb = std::max(1, b.n_blocks);
@@ -567,6 +582,18 @@ csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *
   }
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_attend");
   return CSA_OK;
+}
+
+}  // namespace
+
+csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q,
+                      const int32_t *topk, int32_t k, float scale, void *out, hipStream_t stream) {
+  return attend_impl(h, layer, n_q, q_seq, q_pos, q, topk, k, false, scale, out, stream);
+}
+
+csa_status csa_attend_dense(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                            const void *q, float scale, void *out, hipStream_t stream) {
+  return attend_impl(h, layer, n_q, q_seq, q_pos, q, nullptr, 0, true, scale, out, stream);
 }
 
 csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags) {

@@ -152,6 +152,7 @@ struct AttendArgs {
   int32_t k, W, R, r, bt_stride, pool_pages, H;
   int32_t n_sparse_blocks, n_blocks, blocks_per_split, n_splits, n_q;
   int32_t chunk;            // 1: queries are a chunk (seq0, pos0 + i)
+  int32_t dense;            // 1: the sparse keys are every visible entry (topk unused)
   int32_t seq0, pos0;
   AttQuery qd[kAttMaxQ];
 };

@@ -67,10 +67,11 @@ typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
 /* Static shape of a layer group's cache.
  * Supported (kv_dtype, act_dtype): (F32, F32), (BF16, BF16), (FP8_E4M3, BF16). */
 typedef struct csa_config {
-  int32_t ratio;             /* r >= 1: raw rows per compressed entry (1 keeps main KV uncompressed) */
+  int32_t ratio;             /* r in [1, 256]: raw rows per compressed entry (1 keeps main KV uncompressed) */
   int32_t head_dim;          /* D, must be CSA_HEAD_DIM */
   int32_t q_heads;           /* H_q: query heads sharing the single KV head, multiple of 16, <= 128 */
-  int32_t idx_heads;         /* H_I: indexer query heads, 1..CSA_MAX_IDX_HEADS */
+  int32_t idx_heads;         /* H_I: indexer query heads, 0..CSA_MAX_IDX_HEADS. 0: no indexer - a
+                                heavily compressed (HCA) layer group, attended with csa_attend_dense */
   int32_t idx_dim;           /* D_I, must be CSA_IDX_DIM */
   int32_t window;            /* W >= 0: sliding-window length in raw rows (0 disables the branch) */
   int32_t ring_rows;         /* R: raw rows kept per sequence and layer; >= max(W, r, 1).
@@ -98,9 +99,9 @@ typedef struct csa_buffers {
   void *ring_k[CSA_MAX_LAYERS];      /* [max_seqs][R][D] act_dtype: last R raw keys (row i at slot i % R) */
   void *ring_v[CSA_MAX_LAYERS];      /* [max_seqs][R][D] act_dtype: last R raw values */
   void *gate_stage[CSA_MAX_LAYERS];  /* [max_seqs][r][D] act_dtype: gate logits of the open r-block */
-  void *kidx;                        /* [pool_pages][64][D_I] kv_dtype: indexer keys (layer 0) */
-  float *kidx_scale;                 /* [pool_pages] fp32 (fp8) */
-  float *kidx_stage;                 /* [max_seqs][64][D_I] fp32 (fp8) */
+  void *kidx;                        /* [pool_pages][64][D_I] kv_dtype: indexer keys (layer 0); NULL if idx_heads == 0 */
+  float *kidx_scale;                 /* [pool_pages] fp32 (fp8; NULL if idx_heads == 0) */
+  float *kidx_stage;                 /* [max_seqs][64][D_I] fp32 (fp8; NULL if idx_heads == 0) */
   const int32_t *block_table;        /* [max_seqs][max_pages_per_seq] physical page ids */
   void *workspace;                   /* scratch, >= csa_workspace_size() bytes, 256-byte aligned,
                                         zero-filled before csa_cache_create */
@@ -167,8 +168,9 @@ csa_status csa_seq_set_len(csa_cache_t h, int32_t layer, int32_t seq, int64_t le
  * re-quantised whole from fp32 staging, so incremental appends produce the
  * same bytes as one bulk call.
  *
- *   layer       0..n_layers-1. Layer 0 must pass proj_idx (it writes the
- *               indexer keys); other layers must pass NULL.
+ *   layer       0..n_layers-1. With an indexer (idx_heads > 0) layer 0 must
+ *               pass proj_idx (it writes the indexer keys); every other call
+ *               passes NULL.
  *   n_seqs      number of sequences appended to (>= 1); seq_ids (host) are distinct.
  *   n_new       (host) rows appended per sequence, >= 0.
  *   raw_k, raw_v, gate (dev) [sum(n_new)][D] act_dtype, sequences packed in
@@ -199,6 +201,7 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
  *               (a prefill chunk), the chunk kernels run.
  *   q_idx       (dev) [n_q][H_I][D_I] act_dtype.   w_idx (dev) [n_q][H_I] fp32, >= 0.
  *   k           1..CSA_MAX_TOPK.   topk (dev) [n_q][k] int32 output.
+ * Errors: CSA_ERR_UNSUPPORTED on a group without an indexer (idx_heads == 0).
  */
 csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
                           const void *q_idx, const float *w_idx, int32_t k, int32_t *topk,
@@ -227,6 +230,22 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
 csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
                       const int32_t *q_pos, const void *q, const int32_t *topk, int32_t k, float scale,
                       void *out, hipStream_t stream);
+
+/*
+ * csa_attend_dense - heavily compressed attention (HCA): one softmax over every
+ * compressed entry visible to the query ((j+1)*r <= t+1) plus the window rows,
+ * with no indexer selection. [Atlas] compressed-KV entry (HCA applies the same
+ * compression primitive far more aggressively and runs ordinary dense
+ * attention over the short compressed stream).
+ *
+ *   Arguments as for csa_attend, without topk and k.
+ *   out[t][h] = sum_key p * v over keys {Kbar[j] : j < (t+1)/r} u window rows.
+ * Errors: CSA_ERR_UNSUPPORTED when a query sees more than about 92,000
+ * entries (40 splits of 36 blocks of 64 keys).
+ */
+csa_status csa_attend_dense(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
+                            const int32_t *q_pos, const void *q, float scale, void *out,
+                            hipStream_t stream);
 
 /* Synchronises `stream`, returns the device error word in *flags (bit 0: a
  * page id outside the pool was met; bit 1: a Top-K index outside the visible

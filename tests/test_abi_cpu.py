@@ -76,7 +76,7 @@ def test_status_strings_and_sizes():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("head_dim", 64, 5), ("idx_dim", 32, 5), ("q_heads", 48, 5), ("idx_heads", 5, 5), ("ratio", 0, 5),
+    ("head_dim", 64, 5), ("idx_dim", 32, 5), ("q_heads", 48, 5), ("idx_heads", 5, 5), ("idx_heads", -1, 5), ("ratio", 0, 5), ("ratio", 257, 5),
     ("window", -1, 2), ("ring_rows", 64, 2), ("n_layers", 9, 2), ("pool_pages", 0, 2),
     ("kv_dtype", B.CSA_BF16, 3),                      # bf16 cache with... bf16 act is fine, so flip act below
 ])
@@ -200,5 +200,30 @@ def test_profile_masks_validated():
         assert L.csa_profile_end(C.c_void_p(h), 2, C.byref(ms), C.byref(n)) == 0
         assert n.value == 0 and ms.value == 0.0
         assert B.csa_profile_end(h, B.PROFILE_INDEX) == (0.0, 0)
+    finally:
+        B.csa_cache_destroy(h)
+
+
+def test_indexerless_group_accepted_and_sized():
+    """idx_heads = 0 (a heavily compressed group): no indexer buffers needed."""
+    cfg = _spec(idx_heads=0, ratio=128)
+    sz = B.csa_buffer_sizes_for(cfg)
+    assert sz.idx_pool == 0 and sz.idx_stage == 0 and sz.kv_pool > 0
+    b = B.Buffers()
+    fake = 0x10000
+    for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "gate_stage"):
+        for l in range(cfg.n_layers):
+            getattr(b, f)[l] = fake
+    b.block_table = fake
+    b.workspace = 0x20000
+    b.workspace_bytes = B.csa_workspace_size(cfg, 4, 1)
+    h = B.csa_cache_create(cfg, b)
+    try:
+        L = B.lib()
+        i32 = lambda xs: (C.c_int32 * len(xs))(*xs)
+        s = C.c_void_p(0)
+        f = C.c_void_p(fake)
+        assert L.csa_index_topk(C.c_void_p(h), 1, i32([0]), i32([0]), f, f, 16, f, s) == 5
+        assert L.csa_compress(C.c_void_p(h), 0, 1, i32([0]), i32([4]), f, f, f, f, s) == 1
     finally:
         B.csa_cache_destroy(h)

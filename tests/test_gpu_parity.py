@@ -615,3 +615,89 @@ def test_serving_steps_ragged_paged_fp8():
         got = cache.logical(cache.kidx, b, n).cpu().numpy()
         _, (codes, _) = O.store(ki[:n], "fp8")
         assert np.mean(got == codes) > 0.99
+
+
+# --------------------------------------------------------------------------- heavily compressed attention (no indexer)
+
+def _hca_case(kv, act, lens, r, W, H=64, seed=57, chunk=None):
+    """Compress with a large ratio and no indexer, then csa_attend_dense; the
+    oracle compresses the same raw rows and attends to every visible entry."""
+    max_pages = max(1, max(L // r for L in lens) // 64 + 2)
+    n_q = len(lens) if chunk is None else chunk[1]
+    R = max(W, r, 8) + (0 if chunk is None else chunk[1])
+    cache = make_cache(seed, ratio=r, q_heads=H, idx_heads=0, window=W, ring_rows=R, n_layers=1,
+                       max_seqs=len(lens), max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 3,
+                       kv_dtype=kv, act_dtype=act, max_queries=n_q, max_k=1)
+    assert cache.kidx is None
+    raws = []
+    for b, L in enumerate(lens):
+        rows = [raw_rows(seed, kind, 0, b, 0, L, act) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+        raws.append(tuple(to64(x) for x in rows))
+        cache.compress(0, [b], [L], *(x.cuda() for x in rows))
+    if chunk is None:
+        q_seq, q_pos = list(range(len(lens))), [L - 1 for L in lens]
+    else:
+        q_seq = [chunk[0]] * chunk[1]
+        q_pos = [lens[chunk[0]] - chunk[1] + i for i in range(chunk[1])]
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, n_q * H, 128, dtype=TORCH_ACT[act]).view(n_q, H, 128)
+    scale = 1.0 / math.sqrt(128)
+    got = to64(cache.attend_dense(0, q_seq, q_pos, q.cuda(), scale))
+    assert cache.read_errors() == 0
+    ents = {}
+    for i in range(n_q):
+        b = q_seq[i]
+        if b not in ents:
+            K, V, Z = raws[b]
+            kb, vb, _ = O.compress(K, V, Z, r)
+            ents[b] = (O.store(kb, kv)[0], O.store(vb, kv)[0])
+        K, V, _ = raws[b]
+        ref = O.hca_attend_step(to64(q[i]), q_pos[i], r, W, scale, ents[b][0], ents[b][1], K, V)
+        err = max_abs(got[i], ref)
+        assert err <= TOL[act], f"query {i} (seq {b}, t {q_pos[i]}): max-abs {err}"
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_hca_decode_matches_oracle(kv, act):
+    _hca_case(kv, act, lens=[128 * 300 + 77, 128 * 64, 200, 127], r=128, W=128)
+
+
+@pytest.mark.parametrize("r,W", [(16, 0), (16, 64), (64, 128), (4, 32)])
+def test_hca_ratios_and_windows(r, W):
+    _hca_case("fp8", "bf16", lens=[r * 1500 + 3, r * 70 + r - 1, 9], r=r, W=W)
+
+
+def test_hca_many_splits():
+    """4,096 entries (64 blocks) per query: the split-and-merge path."""
+    _hca_case("bf16", "bf16", lens=[16 * 4096, 16 * 4000 + 5], r=16, W=128, H=16)
+
+
+@pytest.mark.parametrize("kv,act", [("bf16", "bf16"), ("fp8", "bf16")])
+def test_hca_chunk_queries(kv, act):
+    _hca_case(kv, act, lens=[64 * 900 + 10, 300], r=64, W=128, chunk=(0, 96))
+
+
+def test_hca_ratio1_no_window_is_causal_attention():
+    """r = 1, W = 0: dense causal attention (torch SDPA)."""
+    L, H = 160, 16
+    cache = make_cache(43, ratio=1, q_heads=H, idx_heads=0, window=0, ring_rows=8, max_seqs=1, max_pages_per_seq=4,
+                       pool_pages=5, kv_dtype="f32", act_dtype="f32", max_queries=L, max_k=1)
+    K, V, Z = (raw_rows(43, kind, 0, 0, 0, L, "f32") for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+    cache.compress(0, [0], [L], K.cuda(), V.cuda(), Z.cuda())
+    q = Sy.normal_rows(43, Sy.stream_id(Sy.KIND_Q), 0, L * H, 128).view(L, H, 128)
+    out = cache.attend_dense(0, [0] * L, list(range(L)), q.cuda(), 1 / math.sqrt(128)).cpu()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.permute(1, 0, 2).double().unsqueeze(0), K.double()[None, None].expand(1, H, L, 128),
+        V.double()[None, None].expand(1, H, L, 128), is_causal=True, scale=1 / math.sqrt(128))[0].permute(1, 0, 2)
+    assert max_abs(out.double().numpy(), ref.numpy()) <= 2e-3
+
+
+def test_hca_group_rejects_indexer_calls():
+    cache = make_cache(3, ratio=32, q_heads=16, idx_heads=0, window=32, ring_rows=32, max_seqs=1,
+                       max_pages_per_seq=2, pool_pages=2, kv_dtype="bf16", act_dtype="bf16", max_queries=1, max_k=1)
+    K = raw_rows(3, Sy.KIND_K, 0, 0, 0, 64, "bf16").cuda()
+    with pytest.raises(RuntimeError):
+        cache.compress(0, [0], [64], K, K, K, Sy.proj_matrix(3, 128, 64).cuda())
+    cache.compress(0, [0], [64], K, K, K)
+    with pytest.raises(RuntimeError):
+        cache.index_topk([0], [63], torch.zeros((1, 1, 64), dtype=torch.bfloat16, device="cuda"),
+                         torch.ones((1, 1), device="cuda"), 1)
