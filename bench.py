@@ -50,6 +50,7 @@ def parse():
                     help="run one 512 MiB device copy after timing (reference kernel for HBM counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk MFMA-utilisation leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the prefill-chunk leg (development)")
+    ap.add_argument("--no-hca", action="store_true", help="skip the heavily-compressed-attention leg")
     return ap.parse_args()
 
 
@@ -137,6 +138,89 @@ def prefill_leg(seed, dev, steps=5):
            "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
     c.close()
     return res
+
+
+HCA_RATIO, HCA_REPLICAS = 128, 32
+
+
+def hca_leg(seed, dev, steps=50):
+    """Heavily compressed attention layer at the same 1M-token batch-4 decode:
+    r = 128 gives 8,192 fp8 entries per sequence, every one attended (no
+    indexer) together with the 128-token window, 64 heads. Timed over graph
+    replays rotating across 32 cache replicas (more than the last-level cache
+    holds); the attention kernel's own time from launch-stamped events."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+
+    entries = CONTEXT // HCA_RATIO
+    pages = entries // 64
+    spec = CacheSpec(ratio=HCA_RATIO, q_heads=HEADS, idx_heads=0, window=WINDOW, ring_rows=max(WINDOW, HCA_RATIO),
+                     n_layers=1, max_seqs=BATCH, max_pages_per_seq=pages, pool_pages=BATCH * pages,
+                     kv_dtype="fp8", act_dtype="bf16", max_queries=BATCH, max_k=1)
+    bt = torch.tensor(Sy.permutation(seed, BATCH * pages, salt=7), dtype=torch.int32).view(BATCH, pages).to(dev)
+    base = CsaCache(spec, dev, block_table=bt)
+    chunk = 1 << 18
+    for b in range(BATCH):
+        for r0 in range(0, CONTEXT, chunk):
+            rows = [Sy.normal_rows(seed, Sy.stream_id(kind, 7, b), r0, chunk, 128, dev, torch.bfloat16)
+                    for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+            base.compress(0, [b], [chunk], *rows)
+    caches = [base]
+    for _ in range(1, HCA_REPLICAS):
+        c = CsaCache(spec, dev, block_table=bt)
+        for src, dst in ((base.kbar, c.kbar), (base.vbar, c.vbar), (base.kbar_scale, c.kbar_scale),
+                         (base.vbar_scale, c.vbar_scale), (base.ring_k, c.ring_k), (base.ring_v, c.ring_v)):
+            for s_, d_ in zip(src, dst):
+                d_.copy_(s_)
+        for b in range(BATCH):
+            B.csa_seq_set_len(c.handle, 0, b, CONTEXT)
+        caches.append(c)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, 7), 0, BATCH * HEADS, 128, dev, torch.bfloat16).view(BATCH, HEADS, 128)
+    out = torch.empty_like(q)
+    q_seq, q_pos = list(range(BATCH)), [CONTEXT - 1] * BATCH
+    scale = 1.0 / math.sqrt(128)
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    for c in caches:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            B.csa_attend_dense(c.handle, 0, q_seq, q_pos, q, scale, out, torch.cuda.current_stream())
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (steps * len(graphs))
+    for c in caches:
+        B.csa_profile_begin(c.handle, B.PROFILE_ATTEND)
+    for i in range(len(caches)):
+        B.csa_attend_dense(caches[i].handle, 0, q_seq, q_pos, q, scale, out, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    k_ms, k_n = 0.0, 0
+    for c in caches:
+        ms, n = B.csa_profile_end(c.handle, B.PROFILE_ATTEND)
+        k_ms += ms
+        k_n += n
+    flags = max(c.read_errors() for c in caches)
+    if flags:
+        raise RuntimeError(f"HCA leg raised device error flags {flags}")
+    nbytes = BATCH * A.attend_bytes(entries, WINDOW, 128, HEADS, "fp8", "bf16")
+    kern_us = k_ms * 1e3 / max(k_n, 1)
+    for c in caches:
+        c.close()
+    return {"workload": "HCA decode layer: batch 4, 1,048,576 tokens, r=128 (8,192 fp8 entries, all attended), "
+                        "W=128, 64 heads", "us_per_call": round(us, 3), "tokens_per_s": round(BATCH / (us * 1e-6), 1),
+            "attend_kernel_us": round(kern_us, 3), "bytes": nbytes,
+            "hbm_gbps": round(nbytes / (kern_us * 1e-6) / 1e9, 1)}
 
 
 def build_cache(seed, replicas, dev):
@@ -371,10 +455,12 @@ def main():
                      "traffic_scope": traffic_scope,
                      "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
     }
+    del caches, graphs
+    torch.cuda.empty_cache()
     if not args.no_prefill:
-        del caches, graphs
-        torch.cuda.empty_cache()
         line["prefill"] = prefill_leg(args.seed, dev)
+    if not args.no_hca:
+        line["hca"] = hca_leg(args.seed, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)
