@@ -33,6 +33,8 @@ Parity status per function (what pins it in ``tests/test_oracle.py``):
                           banded SDPA; single key; equal logits -> mean
   hca_attend_step ....... r = 1, W = 0 -> torch SDPA causal; a pure-Python
                           loop softmax over the explicit key list
+  store_ring_rows ....... each row's amax element -> +-448 code; E4M3 relative
+                          error bound; exact round trip of on-grid rows
 None is "parity unpinned".
 """
 from __future__ import annotations
@@ -203,6 +205,29 @@ def store(x64: np.ndarray, dtype: str, page_entries: int = 64):
 # ---------------------------------------------------------------------------
 # a2 / a3: lightning-indexer scores and Top-K
 # ---------------------------------------------------------------------------
+
+def store_ring_rows(x64: np.ndarray, dtype: str):
+    """Raw window rows [n, D] as the ring holds them: unchanged for the
+    activation dtype, or E4M3 codes with one fp32 scale amax/448 per row.
+
+    The FP4 section keeps SWA KV in FP8 for its sensitivity to quantization;
+    the scale granularity is not given, so the reading is one scale per row
+    (rows enter the ring one token at a time) with the same codec as a page.
+    Returns (float64 values as stored, raw payload)."""
+    x64 = np.asarray(x64, dtype=np.float64)
+    if dtype != "fp8":
+        return x64.copy(), None
+    x32 = round_f32(x64)
+    codes = np.zeros(x64.shape, dtype=np.uint8)
+    scales = np.ones(x64.shape[0], dtype=np.float32)
+    vals = np.zeros(x64.shape, dtype=np.float64)
+    for i in range(x64.shape[0]):
+        c, sc = fp8_quantize_page(x32[i:i + 1])
+        codes[i] = c[0]
+        scales[i] = sc
+        vals[i] = e4m3_decode(c[0]) * np.float64(sc)
+    return vals, (codes, scales)
+
 
 def visible_entries(t: int, r: int) -> int:
     """Number of compressed entries a query at raw position t may see.

@@ -432,3 +432,30 @@ def test_hca_matches_loop_softmax_over_explicit_keys(r, W, t, s):
         tot = sum(e)
         want = [sum(e[i] * keys[i][1][d] for i in range(len(keys))) / tot for d in range(D)]
         np.testing.assert_allclose(got[h], want, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- fp8 window ring
+
+def test_fp8_ring_rows_codec():
+    """Per-row E4M3: the row's largest magnitude encodes to +-448 (the format's
+    maximum, quoted in the FP4 section as the FP8 range factor), every value is
+    within E4M3's half-step (2^-4 relative for normal codes) of the input, and
+    rows already on the scaled E4M3 grid come back exactly."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((40, 128)) * rng.uniform(0.01, 30, (40, 1))
+    x = O.decode_bf16(O.round_bf16(x))                       # raw rows are bf16
+    vals, (codes, scales) = O.store_ring_rows(x, "fp8")
+    for i in range(40):
+        j = int(np.argmax(np.abs(x[i])))
+        assert codes[i, j] & 0x7F == 0x7E
+        assert np.float32(scales[i]) == np.float32(np.float32(np.max(np.abs(x[i]))) / np.float32(448.0))
+        big = np.abs(x[i]) >= 2.0 ** -6 * scales[i]         # normal E4M3 range
+        assert np.all(np.abs(vals[i][big] - x[i][big]) <= 2.0 ** -4 * np.abs(x[i][big]) * (1 + 1e-6))
+    grid = O.e4m3_decode(np.arange(0, 126, dtype=np.uint8))   # finite non-negative codes up to 448
+    row = np.zeros((1, 128))
+    row[0, :126] = grid * 0.25
+    row[0, 126] = -448 * 0.25
+    got, _ = O.store_ring_rows(row, "fp8")
+    np.testing.assert_array_equal(got, row)
+    same, raw = O.store_ring_rows(x, "bf16")
+    assert raw is None and np.array_equal(same, x)
