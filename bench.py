@@ -256,7 +256,7 @@ def build_cache(seed, replicas, dev):
         for src, dst in ((base.kbar, c.kbar), (base.vbar, c.vbar), (base.kbar_scale, c.kbar_scale),
                          (base.vbar_scale, c.vbar_scale), (base.ring_k, c.ring_k), (base.ring_v, c.ring_v),
                          (base.kbar_stage, c.kbar_stage), (base.vbar_stage, c.vbar_stage),
-                         (base.gate_stage, c.gate_stage)):
+                         (base.block_stage, c.block_stage)):
             for s_, d_ in zip(src, dst):
                 d_.copy_(s_)
         c.kidx.copy_(base.kidx)

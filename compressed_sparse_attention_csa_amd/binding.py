@@ -39,7 +39,7 @@ class CsaError(RuntimeError):
 class Config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "ratio", "head_dim", "q_heads", "idx_heads", "idx_dim", "window", "ring_rows", "n_layers",
-        "max_seqs", "max_pages_per_seq", "pool_pages", "kv_dtype", "act_dtype")]
+        "max_seqs", "max_pages_per_seq", "pool_pages", "kv_dtype", "act_dtype", "swa_dtype")]
 
 
 class Buffers(C.Structure):
@@ -52,7 +52,9 @@ class Buffers(C.Structure):
         ("vbar_stage", C.c_void_p * CSA_MAX_LAYERS),
         ("ring_k", C.c_void_p * CSA_MAX_LAYERS),
         ("ring_v", C.c_void_p * CSA_MAX_LAYERS),
-        ("gate_stage", C.c_void_p * CSA_MAX_LAYERS),
+        ("ring_k_scale", C.c_void_p * CSA_MAX_LAYERS),
+        ("ring_v_scale", C.c_void_p * CSA_MAX_LAYERS),
+        ("block_stage", C.c_void_p * CSA_MAX_LAYERS),
         ("kidx", C.c_void_p),
         ("kidx_scale", C.c_void_p),
         ("kidx_stage", C.c_void_p),
@@ -64,7 +66,8 @@ class Buffers(C.Structure):
 
 class BufferSizes(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
-        "kv_pool", "idx_pool", "page_scale", "kv_stage", "idx_stage", "ring", "gate_stage", "block_table")]
+        "kv_pool", "idx_pool", "page_scale", "kv_stage", "idx_stage", "ring", "ring_scale", "block_stage",
+        "block_table")]
 
 
 EXPORTS = [
@@ -72,6 +75,7 @@ EXPORTS = [
     "csa_cache_create", "csa_cache_destroy", "csa_seq_reset", "csa_seq_len", "csa_seq_set_len",
     "csa_compress", "csa_index_topk", "csa_attend", "csa_read_errors",
     "csa_profile_begin", "csa_profile_end", "csa_debug_convert", "csa_attend_dense",
+    "csa_seq_set_swa_start", "csa_ring_write",
 ]
 
 _LIB = None
@@ -114,6 +118,10 @@ def lib() -> C.CDLL:
     L.csa_attend.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, i32, C.c_float, vp, vp]
     L.csa_attend_dense.restype = C.c_int
     L.csa_attend_dense.argtypes = [vp, i32, i32, pi32, pi32, vp, C.c_float, vp, vp]
+    L.csa_seq_set_swa_start.restype = C.c_int
+    L.csa_seq_set_swa_start.argtypes = [vp, i32, i32]
+    L.csa_ring_write.restype = C.c_int
+    L.csa_ring_write.argtypes = [vp, i32, i32, pi32, pi32, pi32, vp, vp, vp]
     L.csa_read_errors.restype = C.c_int
     L.csa_read_errors.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
     L.csa_profile_begin.restype = C.c_int
@@ -180,7 +188,16 @@ def csa_seq_set_len(h: int, layer: int, seq: int, length: int) -> None:
     check(lib().csa_seq_set_len(C.c_void_p(h), layer, seq, length))
 
 
+def csa_seq_set_swa_start(h: int, seq: int, start: int) -> None:
+    check(lib().csa_seq_set_swa_start(C.c_void_p(h), seq, start))
+
+
 # --------------------------------------------------------------------------- device calls
+
+def csa_ring_write(h: int, layer: int, seq_ids, pos0, n_rows, raw_k, raw_v, stream=None) -> None:
+    check(lib().csa_ring_write(C.c_void_p(h), layer, len(seq_ids), _i32(seq_ids), _i32(pos0), _i32(n_rows),
+                               _ptr(raw_k), _ptr(raw_v), _stream(stream)))
+
 
 def csa_compress(h: int, layer: int, seq_ids, n_new, raw_k, raw_v, gate, proj_idx=None, stream=None) -> None:
     check(lib().csa_compress(C.c_void_p(h), layer, len(seq_ids), _i32(seq_ids), _i32(n_new),

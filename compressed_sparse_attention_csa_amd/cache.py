@@ -30,6 +30,7 @@ class CacheSpec:
     pool_pages: int = 1
     kv_dtype: str = "bf16"
     act_dtype: str = "bf16"
+    swa_dtype: str = ""           # "": act_dtype; "fp8": E4M3 window ring with per-row scales
     max_queries: int = 1
     max_k: int = 512
 
@@ -48,6 +49,7 @@ class CacheSpec:
         c.pool_pages = self.pool_pages
         c.kv_dtype = B.DTYPE_CODES[self.kv_dtype]
         c.act_dtype = B.DTYPE_CODES[self.act_dtype]
+        c.swa_dtype = B.DTYPE_CODES[self.swa_dtype or self.act_dtype]
         return c
 
 
@@ -75,9 +77,14 @@ class CsaCache:
         self.kbar_stage = [torch.zeros((S, 64, D), dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
         self.vbar_stage = [torch.zeros((S, 64, D), dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
         self.kidx_stage = torch.zeros((S, 64, DI), dtype=torch.float32, device=dev) if fp8 and idx else None
-        self.ring_k = [torch.zeros((S, R, D), dtype=actt, device=dev) for _ in range(L)]
-        self.ring_v = [torch.zeros((S, R, D), dtype=actt, device=dev) for _ in range(L)]
-        self.gate_stage = [torch.zeros((S, spec.ratio, D), dtype=actt, device=dev) for _ in range(L)]
+        ring_fp8 = spec.swa_dtype == "fp8"
+        ringt = torch.uint8 if ring_fp8 else actt
+        self.ring_k = [torch.zeros((S, R, D), dtype=ringt, device=dev) for _ in range(L)]
+        self.ring_v = [torch.zeros((S, R, D), dtype=ringt, device=dev) for _ in range(L)]
+        self.ring_k_scale = [torch.ones((S, R), dtype=torch.float32, device=dev) for _ in range(L)] if ring_fp8 else []
+        self.ring_v_scale = [torch.ones((S, R), dtype=torch.float32, device=dev) for _ in range(L)] if ring_fp8 else []
+        # gate logits, raw keys and raw values of each sequence's open r-block
+        self.block_stage = [torch.zeros((S, 3, spec.ratio, D), dtype=actt, device=dev) for _ in range(L)]
         if block_table is None:
             block_table = torch.full((S, spec.max_pages_per_seq), -1, dtype=torch.int32, device=dev)
         assert block_table.shape == (S, spec.max_pages_per_seq) and block_table.dtype == torch.int32
@@ -88,6 +95,7 @@ class CsaCache:
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
         assert sz.kv_pool == self.kbar[0].numel() * self.kbar[0].element_size()
         assert sz.ring == self.ring_k[0].numel() * self.ring_k[0].element_size()
+        assert sz.block_stage == self.block_stage[0].numel() * self.block_stage[0].element_size()
 
         b = B.Buffers()
         for l in range(L):
@@ -95,7 +103,10 @@ class CsaCache:
             b.vbar[l] = self.vbar[l].data_ptr()
             b.ring_k[l] = self.ring_k[l].data_ptr()
             b.ring_v[l] = self.ring_v[l].data_ptr()
-            b.gate_stage[l] = self.gate_stage[l].data_ptr()
+            b.block_stage[l] = self.block_stage[l].data_ptr()
+            if ring_fp8:
+                b.ring_k_scale[l] = self.ring_k_scale[l].data_ptr()
+                b.ring_v_scale[l] = self.ring_v_scale[l].data_ptr()
             if fp8:
                 b.kbar_scale[l] = self.kbar_scale[l].data_ptr()
                 b.vbar_scale[l] = self.vbar_scale[l].data_ptr()
@@ -133,6 +144,12 @@ class CsaCache:
             out = torch.empty_like(q)
         B.csa_attend_dense(self.handle, layer, q_seq, q_pos, q, scale, out, stream)
         return out
+
+    def set_swa_start(self, seq, start):
+        B.csa_seq_set_swa_start(self.handle, seq, start)
+
+    def ring_write(self, layer, seq_ids, pos0, n_rows, raw_k, raw_v, stream=None):
+        B.csa_ring_write(self.handle, layer, seq_ids, pos0, n_rows, raw_k, raw_v, stream)
 
     def seq_len(self, layer, seq):
         return B.csa_seq_len(self.handle, layer, seq)

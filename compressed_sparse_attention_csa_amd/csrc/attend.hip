@@ -93,20 +93,21 @@ constexpr int32_t kMaskedRow = INT32_MIN;   // src_row of a key that takes no pa
 
 template <int SD> constexpr int elem_bytes_of() { return SD == DT_F32 ? 4 : (SD == DT_BF16 ? 2 : 1); }
 
+// RS: storage type of the window ring (ACT, or E4M3 with one scale per row);
 // HG: head groups (waves); NTW: 16-head tiles per wave.
-template <int ACT, int KV, int HG, int NTW>
+template <int ACT, int KV, int RS, int HG, int NTW>
 __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   using CT = typename ComputeT<KV>::type;
   constexpr int NT = HG * 64;
   constexpr int H = HG * NTW * 16;
-  constexpr int KE = elem_bytes_of<KV>(), AE = elem_bytes_of<ACT>();
+  constexpr int KE = elem_bytes_of<KV>(), AE = elem_bytes_of<ACT>(), RE = elem_bytes_of<RS>();
   constexpr int KS = kD + kpad<CT>();          // K row stride (elements)
   // bf16: V row-major like K, read as transposed MFMA fragments; fp32: V^T
   constexpr bool VROW = sizeof(CT) == 2;
   constexpr int VS = VROW ? KS : kKeyBlock + kpad<CT>();   // V (or V^T) row stride (elements)
   // a block's K and V rows move as 16-byte chunks, 16 consecutive lanes per
   // 256-byte row, so every wave load covers whole rows
-  constexpr int CPR_P = kD * KE / 16, CPR_R = kD * AE / 16;   // chunks per pool / ring row
+  constexpr int CPR_P = kD * KE / 16, CPR_R = kD * RE / 16;   // chunks per pool / ring row
   constexpr int CPR_MAX = CPR_P > CPR_R ? CPR_P : CPR_R;
   static_assert((CPR_P & (CPR_P - 1)) == 0 && (CPR_R & (CPR_R - 1)) == 0, "chunks per row are powers of two");
   constexpr int U = 2 * kKeyBlock * CPR_MAX / NT;              // chunk slots per thread per block
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   const int seq = a.chunk ? a.seq0 : a.qd[qi].seq;
   const int t = a.chunk ? a.pos0 + qi : a.qd[qi].pos;
   const int n_vis = (t + 1) / a.r;
-  const int swa_lo = max(0, t - a.W + 1);
+  const int swa_lo = max(a.chunk ? a.swa0 : a.qd[qi].swa, t - a.W + 1);   // replay start s bounds the window
   const int b_begin = split * a.blocks_per_split;
   const int b_end = min(a.n_blocks, b_begin + a.blocks_per_split);
   const int n_keys = (b_end - b_begin) * kKeyBlock;
@@ -206,13 +207,19 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   };
   auto load_scales = [&](int b) {
     ks_pref = vs_pref = 1.f;
-    if constexpr (KV == DT_FP8) {
-      if (tid < kKeyBlock && b < a.n_sparse_blocks) {
-        const int i = (b - b_begin) * kKeyBlock + tid;
-        const int32_t row = src_row[i];
-        if (row != kMaskedRow) {
+    if (tid < kKeyBlock) {
+      const int i = (b - b_begin) * kKeyBlock + tid;
+      const int32_t row = src_row[i];
+      if constexpr (KV == DT_FP8) {
+        if (b < a.n_sparse_blocks && row != kMaskedRow) {   // page scales
           ks_pref = a.kbar_scale[row >> 6];
           vs_pref = a.vbar_scale[row >> 6];
+        }
+      }
+      if constexpr (RS == DT_FP8) {
+        if (b >= a.n_sparse_blocks && row != kMaskedRow) {  // ring row scales
+          ks_pref = a.ring_k_scale[-row - 1];
+          vs_pref = a.ring_v_scale[-row - 1];
         }
       }
     }
@@ -244,11 +251,11 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     }
   };
   auto commit_slot = [&](int b, int s, const uint4 &u) {
-    if constexpr (KV == ACT) {
+    if constexpr (KV == RS) {
       commit_chunk(std::integral_constant<int, KV>{}, s, u);
     } else {
       if (b < a.n_sparse_blocks) commit_chunk(std::integral_constant<int, KV>{}, s, u);
-      else commit_chunk(std::integral_constant<int, ACT>{}, s, u);
+      else commit_chunk(std::integral_constant<int, RS>{}, s, u);
     }
   };
   auto load_round = [&](int r) {
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
         const int nslot = 2 * kKeyBlock * cpr;
         const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
         const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
-        const int64_t row_bytes = pool ? kD * KE : kD * AE;
+        const int64_t row_bytes = pool ? kD * KE : kD * RE;
         // every slot's row first (one LDS round trip), then every load
         int32_t rows[U];
 #pragma unroll
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       const int cpr = pool ? CPR_P : CPR_R;
       const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
       const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
-      const int64_t row_bytes = pool ? kD * KE : kD * AE;
+      const int64_t row_bytes = pool ? kD * KE : kD * RE;
       for (int u = 0; u < U; ++u) {
         const int s = tid + u * NT;
         if (s >= 2 * kKeyBlock * cpr) break;
@@ -513,24 +520,27 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   else reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16(out);
 }
 
-template <int ACT, int KV>
+template <int ACT, int KV, int RS>
 void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.H) {
-    case 16: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 1, 1>), dim3(n_wg), dim3(64), 0, s, e0, e1, 0, a); break;
-    case 32: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 2, 1>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
-    case 64: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 4, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
-    case 128: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, 4, 2>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 1, 1>), dim3(n_wg), dim3(64), 0, s, e0, e1, 0, a); break;
+    case 32: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 2, 1>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
+    case 64: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 4, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
+    case 128: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 4, 2>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
     default: break;
   }
 }
 
 }  // namespace
 
-void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, bool ring_fp8, hipStream_t s, hipEvent_t ev0,
+                   hipEvent_t ev1) {
   if (n_wg <= 0) return;
-  if (kv == DT_F32 && act == DT_F32) launch_attend_t<DT_F32, DT_F32>(a, n_wg, s, ev0, ev1);
-  else if (kv == DT_BF16 && act == DT_BF16) launch_attend_t<DT_BF16, DT_BF16>(a, n_wg, s, ev0, ev1);
-  else if (kv == DT_FP8 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP8>(a, n_wg, s, ev0, ev1);
+  if (kv == DT_F32 && act == DT_F32) launch_attend_t<DT_F32, DT_F32, DT_F32>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_BF16 && act == DT_BF16 && !ring_fp8) launch_attend_t<DT_BF16, DT_BF16, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_BF16 && act == DT_BF16) launch_attend_t<DT_BF16, DT_BF16, DT_FP8>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP8 && act == DT_BF16 && !ring_fp8) launch_attend_t<DT_BF16, DT_FP8, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP8 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP8, DT_FP8>(a, n_wg, s, ev0, ev1);
   if (a.n_splits > 1) {
     if (act == DT_F32) hipLaunchKernelGGL(attend_merge_kernel<DT_F32>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);
     else hipLaunchKernelGGL(attend_merge_kernel<DT_BF16>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
         const int row = e * r + u;
         float2 z = row >= it.old_len
                        ? load2<ACT>(a.gate, static_cast<int64_t>(it.row_off + row - it.old_len) * kD + d0)
-                       : load2<ACT>(a.gate_stage, (static_cast<int64_t>(seq) * r + row % r) * kD + d0);
+                       : load2<ACT>(a.block_stage, ((static_cast<int64_t>(seq) * 3 + 0) * r + row % r) * kD + d0);
         zm0 = fmaxf(zm0, z.x);
         zm1 = fmaxf(zm1, z.y);
       }
@@ -114,10 +114,11 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
           kx = load2<ACT>(a.raw_k, off);
           vx = load2<ACT>(a.raw_v, off);
         } else {
-          z = load2<ACT>(a.gate_stage, (static_cast<int64_t>(seq) * r + row % r) * kD + d0);
-          const int64_t ro = (static_cast<int64_t>(seq) * a.R + row % a.R) * kD + d0;
-          kx = load2<ACT>(a.ring_k, ro);
-          vx = load2<ACT>(a.ring_v, ro);
+          // a row of the block appended by an earlier call: from open-block staging
+          const int64_t so = (static_cast<int64_t>(seq) * 3 * r + row % r) * kD + d0;
+          z = load2<ACT>(a.block_stage, so);
+          kx = load2<ACT>(a.block_stage, so + static_cast<int64_t>(r) * kD);
+          vx = load2<ACT>(a.block_stage, so + 2 * static_cast<int64_t>(r) * kD);
         }
         const float w0 = expf(z.x - zm0), w1 = expf(z.y - zm1);
         ws0 += w0; ws1 += w1;
@@ -229,10 +230,11 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   }
 }
 
-// Copies the newest raw rows into the window ring and the open block's gate
-// logits into gate staging. Runs after the page kernel, which still reads the
-// previous ring/staging contents for a block straddling two calls.
-template <int ACT>
+// Copies the newest raw rows into the window ring (as E4M3 codes with one
+// fp32 scale amax/448 per row when RING8) and the open r-block's gate, key
+// and value rows into block staging. Runs after the page kernel, which still
+// reads the previous staging contents for a block straddling two calls.
+template <int ACT, bool RING8>
 __global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
   int wg = blockIdx.x, item = 0, acc = 0;
   for (; item < a.n_items - 1; ++item) {
@@ -243,23 +245,71 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
   const int chunk = wg - acc;
   const int new_len = it.old_len + it.n_new;
   const int lo = max(it.old_len, new_len - a.R);
-  const int glo = max(it.old_len, (new_len / a.r) * a.r);
+  const int glo = a.write_stage ? max(it.old_len, (new_len / a.r) * a.r) : new_len;
   constexpr int kEsz = ACT == DT_F32 ? 4 : 2;
   constexpr int kVec = kD * kEsz / 16;                 // 16-byte vectors per row
+  static_assert(64 % kVec == 0, "a row's vectors stay inside one wave");
   const int row_begin = min(lo, glo) + chunk * a.rows_per_wg;
   const int row_end = min(new_len, row_begin + a.rows_per_wg);
   const int n_vec = (row_end - row_begin) * kVec;
-  for (int v = threadIdx.x; v < n_vec; v += blockDim.x) {
+  for (int base = 0; base < n_vec; base += blockDim.x) {
+    const int v = base + threadIdx.x;
+    const bool live = v < n_vec;           // whole rows are live or not (n_vec is a multiple of kVec)
     const int row = row_begin + v / kVec, col = v % kVec;
     const int64_t src = static_cast<int64_t>(it.row_off + row - it.old_len) * kVec + col;
-    if (row >= lo) {
-      const int64_t dst = (static_cast<int64_t>(it.seq) * a.R + row % a.R) * kVec + col;
-      reinterpret_cast<uint4 *>(a.ring_k)[dst] = reinterpret_cast<const uint4 *>(a.raw_k)[src];
-      reinterpret_cast<uint4 *>(a.ring_v)[dst] = reinterpret_cast<const uint4 *>(a.raw_v)[src];
+    uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+    if (live) {
+      kx = reinterpret_cast<const uint4 *>(a.raw_k)[src];
+      vx = reinterpret_cast<const uint4 *>(a.raw_v)[src];
     }
-    if (row >= glo) {
-      const int64_t dst = (static_cast<int64_t>(it.seq) * a.r + row % a.r) * kVec + col;
-      reinterpret_cast<uint4 *>(a.gate_stage)[dst] = reinterpret_cast<const uint4 *>(a.gate)[src];
+    const int64_t slot = static_cast<int64_t>(it.seq) * a.R + row % a.R;
+    if constexpr (RING8) {
+      // row scale: amax over the row's kVec lanes (bf16 values are exact in fp32)
+      float fk[8], fv[8], mk = 0.f, mv = 0.f;
+      const uint32_t wk[4] = {kx.x, kx.y, kx.z, kx.w}, wv[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        fk[2 * q] = bf16_to_f32(static_cast<uint16_t>(wk[q] & 0xffffu));
+        fk[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(wk[q] >> 16));
+        fv[2 * q] = bf16_to_f32(static_cast<uint16_t>(wv[q] & 0xffffu));
+        fv[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(wv[q] >> 16));
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { mk = fmaxf(mk, fabsf(fk[q])); mv = fmaxf(mv, fabsf(fv[q])); }
+#pragma unroll
+      for (int o = 1; o < kVec; o <<= 1) {
+        mk = fmaxf(mk, __shfl_xor(mk, o, 64));
+        mv = fmaxf(mv, __shfl_xor(mv, o, 64));
+      }
+      const float sk = mk > 0.f ? mk / 448.0f : 1.0f;
+      const float sv = mv > 0.f ? mv / 448.0f : 1.0f;
+      if (live && row >= lo) {
+        uint32_t ck[2] = {0u, 0u}, cv[2] = {0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          ck[q >> 2] |= f32_to_e4m3(fk[q] / sk) << (8 * (q & 3));
+          cv[q >> 2] |= f32_to_e4m3(fv[q] / sv) << (8 * (q & 3));
+        }
+        reinterpret_cast<uint2 *>(a.ring_k)[slot * kVec + col] = make_uint2(ck[0], ck[1]);
+        reinterpret_cast<uint2 *>(a.ring_v)[slot * kVec + col] = make_uint2(cv[0], cv[1]);
+        if (col == 0) {
+          a.ring_k_scale[slot] = sk;
+          a.ring_v_scale[slot] = sv;
+        }
+      }
+    } else {
+      if (live && row >= lo) {
+        reinterpret_cast<uint4 *>(a.ring_k)[slot * kVec + col] = kx;
+        reinterpret_cast<uint4 *>(a.ring_v)[slot * kVec + col] = vx;
+      }
+    }
+    if (live && row >= glo) {
+      const int64_t dst = ((static_cast<int64_t>(it.seq) * 3) * a.r + row % a.r) * kVec + col;
+      const int64_t plane = static_cast<int64_t>(a.r) * kVec;
+      uint4 *st = reinterpret_cast<uint4 *>(a.block_stage);
+      st[dst] = reinterpret_cast<const uint4 *>(a.gate)[src];
+      st[dst + plane] = kx;
+      st[dst + 2 * plane] = vx;
     }
   }
 }
@@ -276,12 +326,14 @@ void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hip
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(kThreads), 0, s, a);
 }
 
-void launch_compress_ring(const RingArgs &a, int n_wg, int act, hipStream_t s) {
+void launch_compress_ring(const RingArgs &a, int n_wg, int act, bool ring_fp8, hipStream_t s) {
   if (n_wg <= 0) return;
   if (act == DT_F32)
-    hipLaunchKernelGGL((compress_ring_kernel<DT_F32>), dim3(n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((compress_ring_kernel<DT_F32, false>), dim3(n_wg), dim3(256), 0, s, a);
+  else if (ring_fp8)
+    hipLaunchKernelGGL((compress_ring_kernel<DT_BF16, true>), dim3(n_wg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((compress_ring_kernel<DT_BF16>), dim3(n_wg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((compress_ring_kernel<DT_BF16, false>), dim3(n_wg), dim3(256), 0, s, a);
 }
 
 }  // namespace csa

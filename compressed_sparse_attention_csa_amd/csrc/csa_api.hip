@@ -19,6 +19,7 @@ struct csa_cache {
   csa_config cfg;
   csa_buffers buf;
   std::vector<int64_t> len;  // [n_layers][max_seqs] raw rows appended
+  std::vector<int32_t> swa_start;  // [max_seqs] replay start s of the window branch
   uint32_t *err;             // device error word (workspace head)
   char *scratch;             // workspace after the head
   size_t scratch_bytes;
@@ -75,6 +76,8 @@ csa_status check_config(const csa_config *c) {
                   (c->kv_dtype == CSA_BF16 && c->act_dtype == CSA_BF16) ||
                   (c->kv_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16);
   if (!ok) return fail(CSA_ERR_DTYPE, "unsupported (kv_dtype, act_dtype) = (%d, %d)", c->kv_dtype, c->act_dtype);
+  if (c->swa_dtype != c->act_dtype && !(c->swa_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16))
+    return fail(CSA_ERR_DTYPE, "swa_dtype %d must be act_dtype, or FP8_E4M3 with BF16 activations", c->swa_dtype);
   return CSA_OK;
 }
 
@@ -204,8 +207,10 @@ csa_status csa_buffer_sizes_for(const csa_config *cfg, csa_buffer_sizes *out) {
   out->page_scale = fp8 ? P * 4 : 0;
   out->kv_stage = fp8 ? S * kPage * kD * 4 : 0;
   out->idx_stage = fp8 && idx ? S * kPage * kDI * 4 : 0;
-  out->ring = S * static_cast<size_t>(cfg->ring_rows) * kD * ab;
-  out->gate_stage = S * static_cast<size_t>(cfg->ratio) * kD * ab;
+  const bool ring8 = cfg->swa_dtype == CSA_FP8_E4M3;
+  out->ring = S * static_cast<size_t>(cfg->ring_rows) * kD * (ring8 ? 1 : ab);
+  out->ring_scale = ring8 ? S * static_cast<size_t>(cfg->ring_rows) * 4 : 0;
+  out->block_stage = S * 3 * static_cast<size_t>(cfg->ratio) * kD * ab;
   out->block_table = S * static_cast<size_t>(cfg->max_pages_per_seq) * 4;
   return CSA_OK;
 }
@@ -229,8 +234,10 @@ csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_
   if (!bufs || !out) return fail(CSA_ERR_INVALID_ARG, "buffers or out is NULL");
   const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3;
   for (int l = 0; l < cfg->n_layers; ++l) {
-    if (!bufs->kbar[l] || !bufs->vbar[l] || !bufs->ring_k[l] || !bufs->ring_v[l] || !bufs->gate_stage[l])
-      return fail(CSA_ERR_INVALID_ARG, "layer %d: kbar, vbar, ring_k, ring_v and gate_stage are required", l);
+    if (!bufs->kbar[l] || !bufs->vbar[l] || !bufs->ring_k[l] || !bufs->ring_v[l] || !bufs->block_stage[l])
+      return fail(CSA_ERR_INVALID_ARG, "layer %d: kbar, vbar, ring_k, ring_v and block_stage are required", l);
+    if (cfg->swa_dtype == CSA_FP8_E4M3 && (!bufs->ring_k_scale[l] || !bufs->ring_v_scale[l]))
+      return fail(CSA_ERR_INVALID_ARG, "layer %d: an fp8 window ring needs ring_k_scale and ring_v_scale", l);
     if (fp8 && (!bufs->kbar_scale[l] || !bufs->vbar_scale[l] || !bufs->kbar_stage[l] || !bufs->vbar_stage[l]))
       return fail(CSA_ERR_INVALID_ARG, "layer %d: fp8 caches need scale and staging buffers", l);
   }
@@ -247,6 +254,7 @@ csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_
   h->cfg = *cfg;
   h->buf = *bufs;
   h->len.assign(static_cast<size_t>(cfg->n_layers) * cfg->max_seqs, 0);
+  h->swa_start.assign(static_cast<size_t>(cfg->max_seqs), 0);
   h->err = reinterpret_cast<uint32_t *>(bufs->workspace);
   h->scratch = reinterpret_cast<char *>(bufs->workspace) + kHead;
   h->scratch_bytes = bufs->workspace_bytes - kHead;
@@ -268,6 +276,15 @@ csa_status csa_seq_reset(csa_cache_t h, int32_t seq) {
   if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
   if (seq < 0 || seq >= h->cfg.max_seqs) return fail(CSA_ERR_INVALID_ARG, "seq %d out of range", seq);
   for (int l = 0; l < h->cfg.n_layers; ++l) h->len[static_cast<size_t>(l) * h->cfg.max_seqs + seq] = 0;
+  h->swa_start[seq] = 0;
+  return CSA_OK;
+}
+
+csa_status csa_seq_set_swa_start(csa_cache_t h, int32_t seq, int32_t start) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  if (seq < 0 || seq >= h->cfg.max_seqs) return fail(CSA_ERR_INVALID_ARG, "seq %d out of range", seq);
+  if (start < 0) return fail(CSA_ERR_INVALID_ARG, "swa start %d < 0", start);
+  h->swa_start[seq] = start;
   return CSA_OK;
 }
 
@@ -317,7 +334,7 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   CompressArgs base{};
   base.raw_k = raw_k; base.raw_v = raw_v; base.gate = gate;
-  base.ring_k = h->buf.ring_k[layer]; base.ring_v = h->buf.ring_v[layer]; base.gate_stage = h->buf.gate_stage[layer];
+  base.block_stage = h->buf.block_stage[layer];
   base.proj = proj_idx;
   base.kbar = h->buf.kbar[layer]; base.vbar = h->buf.vbar[layer]; base.kidx = h->buf.kidx;
   base.kbar_scale = h->buf.kbar_scale[layer]; base.vbar_scale = h->buf.vbar_scale[layer]; base.kidx_scale = h->buf.kidx_scale;
@@ -342,8 +359,11 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
 
   RingArgs ring{};
   ring.raw_k = raw_k; ring.raw_v = raw_v; ring.gate = gate;
-  ring.ring_k = h->buf.ring_k[layer]; ring.ring_v = h->buf.ring_v[layer]; ring.gate_stage = h->buf.gate_stage[layer];
-  ring.r = c.ratio; ring.R = c.ring_rows; ring.rows_per_wg = 64;
+  ring.ring_k = h->buf.ring_k[layer]; ring.ring_v = h->buf.ring_v[layer];
+  ring.ring_k_scale = h->buf.ring_k_scale[layer]; ring.ring_v_scale = h->buf.ring_v_scale[layer];
+  ring.block_stage = h->buf.block_stage[layer];
+  ring.r = c.ratio; ring.R = c.ring_rows; ring.rows_per_wg = 64; ring.write_stage = 1;
+  const bool ring8 = c.swa_dtype == CSA_FP8_E4M3;
 
   for (size_t g0 = 0; g0 < items.size(); g0 += kCompressMaxItems) {
     const size_t g1 = std::min(items.size(), g0 + kCompressMaxItems);
@@ -390,10 +410,62 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
       wgR += R.chunks[R.n_items];
       R.n_items++;
     }
-    launch_compress_ring(R, wgR, act, stream);
+    launch_compress_ring(R, wgR, act, ring8, stream);
   }
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_compress");
   for (int i = 0; i < n_seqs; ++i) h->len[static_cast<size_t>(layer) * c.max_seqs + seq_ids[i]] += n_new[i];
+  return CSA_OK;
+}
+
+csa_status csa_ring_write(csa_cache_t h, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *pos0,
+                          const int32_t *n_rows, const void *raw_k, const void *raw_v, hipStream_t stream) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  const csa_config &c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(CSA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (n_seqs < 1 || !seq_ids || !pos0 || !n_rows) return fail(CSA_ERR_INVALID_ARG, "n_seqs >= 1 with seq_ids, pos0, n_rows");
+  int64_t total = 0;
+  std::vector<CompressItem> items;
+  std::vector<char> seen(c.max_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (s < 0 || s >= c.max_seqs) return fail(CSA_ERR_INVALID_ARG, "seq_ids[%d] out of range", i);
+    if (seen[s]) return fail(CSA_ERR_INVALID_ARG, "seq %d listed twice", s);
+    seen[s] = 1;
+    if (n_rows[i] < 0 || pos0[i] < 0) return fail(CSA_ERR_INVALID_ARG, "negative pos0 or n_rows at %d", i);
+    const int64_t L = h->len[static_cast<size_t>(layer) * c.max_seqs + s];
+    if (pos0[i] + static_cast<int64_t>(n_rows[i]) > L)
+      return fail(CSA_ERR_INVALID_ARG, "rows [%d, %lld) of seq %d are not appended yet", pos0[i],
+                  static_cast<long long>(pos0[i]) + n_rows[i], s);
+    if (pos0[i] < L - c.ring_rows)
+      return fail(CSA_ERR_CAPACITY, "row %d of seq %d already left the %d-row ring", pos0[i], s, c.ring_rows);
+    CompressItem it{};
+    it.seq = s; it.old_len = pos0[i]; it.n_new = n_rows[i]; it.row_off = static_cast<int32_t>(total);
+    total += n_rows[i];
+    if (it.n_new > 0) items.push_back(it);
+  }
+  if (total > 0 && (!raw_k || !raw_v)) return fail(CSA_ERR_INVALID_ARG, "raw_k and raw_v are required");
+  if (total == 0) return CSA_OK;
+  const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
+  RingArgs ring{};
+  ring.raw_k = raw_k; ring.raw_v = raw_v; ring.gate = nullptr;
+  ring.ring_k = h->buf.ring_k[layer]; ring.ring_v = h->buf.ring_v[layer];
+  ring.ring_k_scale = h->buf.ring_k_scale[layer]; ring.ring_v_scale = h->buf.ring_v_scale[layer];
+  ring.block_stage = h->buf.block_stage[layer];
+  ring.r = c.ratio; ring.R = c.ring_rows; ring.rows_per_wg = 64; ring.write_stage = 0;
+  for (size_t g0 = 0; g0 < items.size(); g0 += kCompressMaxItems) {
+    const size_t g1 = std::min(items.size(), g0 + kCompressMaxItems);
+    RingArgs R = ring;
+    R.n_items = 0;
+    int wg = 0;
+    for (size_t i = g0; i < g1; ++i) {
+      R.it[R.n_items] = items[i];
+      R.chunks[R.n_items] = (items[i].n_new + R.rows_per_wg - 1) / R.rows_per_wg;
+      wg += R.chunks[R.n_items];
+      R.n_items++;
+    }
+    launch_compress_ring(R, wg, act, c.swa_dtype == CSA_FP8_E4M3, stream);
+  }
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_ring_write");
   return CSA_OK;
 }
 
@@ -544,6 +616,8 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
   a.kbar = h->buf.kbar[layer]; a.vbar = h->buf.vbar[layer];
   a.kbar_scale = h->buf.kbar_scale[layer]; a.vbar_scale = h->buf.vbar_scale[layer];
   a.ring_k = h->buf.ring_k[layer]; a.ring_v = h->buf.ring_v[layer];
+  a.ring_k_scale = h->buf.ring_k_scale[layer]; a.ring_v_scale = h->buf.ring_v_scale[layer];
+  const bool ring8 = c.swa_dtype == CSA_FP8_E4M3;
   a.block_table = h->buf.block_table;
   a.err = h->err;
   a.scale = scale; a.k = k; a.W = c.window; a.R = c.ring_rows; a.r = c.ratio; a.dense = dense ? 1 : 0;
@@ -554,10 +628,10 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
 
   if (is_chunk(n_q, q_seq, q_pos) && a.n_blocks * kKeyBlock <= kAttMaxSplitKeys) {
     a.q = q; a.out = out; a.topk = topk;
-    a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0];
+    a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0]; a.swa0 = h->swa_start[q_seq[0]];
     a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
     const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
-    launch_attend(a, n_q, kv, act, stream, ev.start, ev.stop);
+    launch_attend(a, n_q, kv, act, ring8, stream, ev.start, ev.stop);
   } else {
     for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {
       const int nq = std::min(kAttMaxQ, n_q - g0);
@@ -566,7 +640,11 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       b.out = reinterpret_cast<char *>(out) + g0 * qrow;
       b.topk = topk && !dense ? topk + static_cast<int64_t>(g0) * k : nullptr;
       b.chunk = 0; b.n_q = nq;
-      for (int i = 0; i < nq; ++i) { b.qd[i].seq = q_seq[g0 + i]; b.qd[i].pos = q_pos[g0 + i]; }
+      for (int i = 0; i < nq; ++i) {
+        b.qd[i].seq = q_seq[g0 + i];
+        b.qd[i].pos = q_pos[g0 + i];
+        b.qd[i].swa = h->swa_start[q_seq[g0 + i]];
+      }
       const int nb = std::max(1, b.n_blocks);
       b.blocks_per_split = attend_blocks_per_split(nq, nb);
       b.n_splits = (nb + b.blocks_per_split - 1) / b.blocks_per_split;
@@ -577,7 +655,7 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
         b.part_ml = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(nq) * b.n_splits * c.q_heads * kD * 4, 256));
       }
       const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
-      launch_attend(b, nq * b.n_splits, kv, act, stream, ev.start, ev.stop);
+      launch_attend(b, nq * b.n_splits, kv, act, ring8, stream, ev.start, ev.stop);
     }
   }
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_attend");

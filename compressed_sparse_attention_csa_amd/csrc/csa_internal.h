@@ -21,7 +21,7 @@ struct CompressItem {
 
 struct CompressArgs {
   const void *raw_k, *raw_v, *gate;               // packed new rows [sum n_new][D]
-  const void *ring_k, *ring_v, *gate_stage;       // this layer's ring [max_seqs][R][D], gate stage [max_seqs][r][D]
+  const void *block_stage;                        // open-block gate/K/V rows [max_seqs][3][r][D]
   const float *proj;                              // [D][D_I] or null
   void *kbar, *vbar, *kidx;                       // pools
   float *kbar_scale, *vbar_scale, *kidx_scale;    // fp8 page scales
@@ -34,14 +34,17 @@ struct CompressArgs {
 
 struct RingArgs {
   const void *raw_k, *raw_v, *gate;
-  void *ring_k, *ring_v, *gate_stage;
+  void *ring_k, *ring_v;                          // [max_seqs][R][D] act dtype, or E4M3 codes
+  float *ring_k_scale, *ring_v_scale;             // [max_seqs][R] row scales (fp8 ring)
+  void *block_stage;                              // [max_seqs][3][r][D]
   int32_t r, R, n_items, rows_per_wg;
+  int32_t write_stage;                            // 0: window rows only (a replay)
   int32_t chunks[kCompressMaxItems];              // WGs per item
   CompressItem it[kCompressMaxItems];
 };
 
 void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s);
-void launch_compress_ring(const RingArgs &a, int n_wg, int act, hipStream_t s);
+void launch_compress_ring(const RingArgs &a, int n_wg, int act, bool ring_fp8, hipStream_t s);
 
 // ------------------------------------------------------------------ index (decode)
 
@@ -129,7 +132,7 @@ constexpr int kAttMaxQ = 128;
 constexpr int kKeyBlock = 64;        // keys per attention block
 
 struct AttQuery {
-  int32_t seq, pos;
+  int32_t seq, pos, swa;   // swa: replay start s of the window branch
 };
 
 constexpr int kAttMaxSplitKeys = 2304;   // keys one workgroup resolves up front (36 blocks)
@@ -144,6 +147,7 @@ struct AttendArgs {
   const void *kbar, *vbar;
   const float *kbar_scale, *vbar_scale;
   const void *ring_k, *ring_v;
+  const float *ring_k_scale, *ring_v_scale;   // per-row scales of an fp8 ring
   const int32_t *block_table;
   float *part_o;            // [n_q][n_splits][H][D] unnormalised partial outputs
   float *part_ml;           // [n_q][n_splits][2][H] running max and sum
@@ -153,13 +157,13 @@ struct AttendArgs {
   int32_t n_sparse_blocks, n_blocks, blocks_per_split, n_splits, n_q;
   int32_t chunk;            // 1: queries are a chunk (seq0, pos0 + i)
   int32_t dense;            // 1: the sparse keys are every visible entry (topk unused)
-  int32_t seq0, pos0;
+  int32_t seq0, pos0, swa0;
   AttQuery qd[kAttMaxQ];
 };
 
 // ev0/ev1 (may be null): events stamped with the start and end of the attention kernel launch.
-void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
-                   hipEvent_t ev1 = nullptr);
+void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, bool ring_fp8, hipStream_t s,
+                   hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 
 }  // namespace csa

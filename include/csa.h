@@ -82,13 +82,16 @@ typedef struct csa_config {
   int32_t pool_pages;        /* physical pages in every pool */
   int32_t kv_dtype;          /* csa_dtype of compressed entries and indexer keys */
   int32_t act_dtype;         /* csa_dtype of raw rows, queries and outputs (F32 or BF16) */
+  int32_t swa_dtype;         /* csa_dtype of the window ring: act_dtype, or CSA_FP8_E4M3 with
+                                BF16 activations (E4M3 codes, one fp32 scale amax/448 per row) */
 } csa_config;
 
 /* Device buffers of one handle (all caller-allocated, all "dev").
  * Pools are indexed by physical page: entry j of sequence b lives at slot
  * j % 64 of physical page block_table[b * max_pages_per_seq + j / 64].
  * Per-layer arrays use entries [0, n_layers); unused entries may be NULL.
- * Scale and staging arrays are used only when kv_dtype == CSA_FP8_E4M3 (else NULL). */
+ * Page scale and page staging arrays are used only when kv_dtype == CSA_FP8_E4M3,
+ * ring scales only when swa_dtype == CSA_FP8_E4M3 (else NULL). */
 typedef struct csa_buffers {
   void *kbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed keys */
   void *vbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed values */
@@ -96,9 +99,12 @@ typedef struct csa_buffers {
   float *vbar_scale[CSA_MAX_LAYERS];
   float *kbar_stage[CSA_MAX_LAYERS]; /* [max_seqs][64][D] fp32 values of each sequence's open page (fp8) */
   float *vbar_stage[CSA_MAX_LAYERS];
-  void *ring_k[CSA_MAX_LAYERS];      /* [max_seqs][R][D] act_dtype: last R raw keys (row i at slot i % R) */
-  void *ring_v[CSA_MAX_LAYERS];      /* [max_seqs][R][D] act_dtype: last R raw values */
-  void *gate_stage[CSA_MAX_LAYERS];  /* [max_seqs][r][D] act_dtype: gate logits of the open r-block */
+  void *ring_k[CSA_MAX_LAYERS];      /* [max_seqs][R][D] swa_dtype: last R raw keys (row i at slot i % R) */
+  void *ring_v[CSA_MAX_LAYERS];      /* [max_seqs][R][D] swa_dtype: last R raw values */
+  float *ring_k_scale[CSA_MAX_LAYERS]; /* [max_seqs][R] fp32 row scales (fp8 ring) */
+  float *ring_v_scale[CSA_MAX_LAYERS];
+  void *block_stage[CSA_MAX_LAYERS]; /* [max_seqs][3][r][D] act_dtype: gate logits, raw keys and raw
+                                        values of each sequence's open (incomplete) r-block */
   void *kidx;                        /* [pool_pages][64][D_I] kv_dtype: indexer keys (layer 0); NULL if idx_heads == 0 */
   float *kidx_scale;                 /* [pool_pages] fp32 (fp8; NULL if idx_heads == 0) */
   float *kidx_stage;                 /* [max_seqs][64][D_I] fp32 (fp8; NULL if idx_heads == 0) */
@@ -116,7 +122,8 @@ typedef struct csa_buffer_sizes {
   size_t kv_stage;     /* each kbar_stage[l] / vbar_stage[l] (0 unless fp8) */
   size_t idx_stage;    /* kidx_stage (0 unless fp8) */
   size_t ring;         /* each ring_k[l] / ring_v[l] */
-  size_t gate_stage;   /* each gate_stage[l] */
+  size_t ring_scale;   /* each ring_k_scale[l] / ring_v_scale[l] (0 unless the ring is fp8) */
+  size_t block_stage;  /* each block_stage[l] */
   size_t block_table;  /* block_table */
 } csa_buffer_sizes;
 
@@ -151,6 +158,13 @@ int64_t csa_seq_len(csa_cache_t h, int32_t layer, int32_t seq);
  * contents (checkpoint / resume). len must fit the sequence's block table. */
 csa_status csa_seq_set_len(csa_cache_t h, int32_t layer, int32_t seq, int64_t len);
 
+/* Sets the replay start s of sequence `seq` (every layer): its window branch
+ * then covers raw rows [max(s, t - W + 1), t] for a query at t.
+ * [Walkthrough] "SWA Bounded Replay" > "Replay only the window" (the window is
+ * truncated to the replay segment that starts at s). s = 0 (the default, and
+ * after csa_seq_reset) leaves the window untruncated. Host state only. */
+csa_status csa_seq_set_swa_start(csa_cache_t h, int32_t seq, int32_t start);
+
 /*
  * csa_compress - append raw rows to sequences of one layer and build the
  * compressed entries of every r-block they complete.
@@ -184,6 +198,22 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
                         const float *proj_idx, hipStream_t stream);
 
 /*
+ * csa_ring_write - rewrite window-ring rows of already appended positions
+ * without touching the compressed cache: the bounded replay regenerates only
+ * the local (SWA) keys and values and reuses the cached global KV
+ * ([Walkthrough] "SWA Bounded Replay" > "Encoder SWA Bounded Replay").
+ *
+ *   n_seqs, seq_ids (host): sequences; pos0, n_rows (host) [n_seqs]: rows
+ *   [pos0, pos0 + n_rows) are replaced; raw_k, raw_v (dev) [sum(n_rows)][D]
+ *   act_dtype, packed in seq_ids order. Rows are stored in the ring format
+ *   (fp8 rows take a fresh per-row scale).
+ * Errors: CSA_ERR_INVALID_ARG for rows not appended yet; CSA_ERR_CAPACITY for
+ * rows older than the ring holds (pos0 < len - R).
+ */
+csa_status csa_ring_write(csa_cache_t h, int32_t layer, int32_t n_seqs, const int32_t *seq_ids, const int32_t *pos0,
+                          const int32_t *n_rows, const void *raw_k, const void *raw_v, hipStream_t stream);
+
+/*
  * csa_index_topk - lightning-indexer scores and per-query Top-K over the
  * entries each query may see. [Walkthrough] CSA2 "The indexer selects, SWA
  * covers the rest" (indexer query against indexer key, top entries per
@@ -210,7 +240,7 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
 /*
  * csa_attend - one layer's attention for n_q queries: one softmax over the
  * gathered Top-K entries of that layer's compressed cache plus the raw rows
- * [max(0, t-W+1), t] of its window ring. [Walkthrough] CSA2 "The indexer
+ * [max(s, t-W+1), t] of its window ring (s: the sequence's replay start). [Walkthrough] CSA2 "The indexer
  * selects, SWA covers the rest"; "SWA Bounded Replay" > "Replay only the
  * window" (window rule); [Atlas] MQA/GQA entry (all query heads share the one
  * KV head). Reuse-mode layers call this with the Top-K rows produced for the

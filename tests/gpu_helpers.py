@@ -104,14 +104,31 @@ def fill_ring(cache: CsaCache, seed: int, layer: int, seq: int, length: int):
     Returns float64 (K, V) for rows [0, length) — rows older than the ring are
     returned too (the oracle may index them; the GPU must not need them)."""
     act = cache.spec.act_dtype
-    R = cache.cfg.ring_rows
     K = raw_rows(seed, Sy.KIND_K, layer, seq, 0, length, act)
     V = raw_rows(seed, Sy.KIND_V, layer, seq, 0, length, act)
-    lo = max(0, length - R)
-    rows = torch.arange(lo, length)
-    cache.ring_k[layer][seq, rows % R] = K[lo:].to(cache.device)
-    cache.ring_v[layer][seq, rows % R] = V[lo:].to(cache.device)
-    return to64(K), to64(V)
+    return write_ring_rows(cache, layer, seq, 0, K, V)
+
+
+def write_ring_rows(cache: CsaCache, layer: int, seq: int, row0: int, K: torch.Tensor, V: torch.Tensor):
+    """Raw rows [row0, row0 + n) into the ring slots of the newest R of them,
+    through the oracle's ring codec (per-row E4M3 for an fp8 ring). Returns
+    float64 (K, V) as the ring holds them (older rows: the raw values)."""
+    R = cache.cfg.ring_rows
+    n = K.shape[0]
+    lo = max(0, n - R)
+    rows = torch.arange(row0 + lo, row0 + n)
+    out = []
+    for x, ring, scales in ((K, cache.ring_k[layer], cache.ring_k_scale), (V, cache.ring_v[layer], cache.ring_v_scale)):
+        x64 = to64(x)
+        if cache.spec.swa_dtype == "fp8":
+            vals, (codes, sc) = O.store_ring_rows(x64[lo:], "fp8")
+            ring[seq, rows % R] = torch.from_numpy(codes).to(cache.device)
+            scales[layer][seq, rows % R] = torch.from_numpy(sc).to(cache.device)
+            x64[lo:] = vals
+        else:
+            ring[seq, rows % R] = x[lo:].to(cache.device)
+        out.append(x64)
+    return tuple(out)
 
 
 # --------------------------------------------------------------------------- comparisons

@@ -36,7 +36,7 @@ def _spec(**kw):
     c.ratio, c.head_dim, c.q_heads, c.idx_heads, c.idx_dim = 4, 128, 64, 4, 64
     c.window, c.ring_rows, c.n_layers = 128, 128, 2
     c.max_seqs, c.max_pages_per_seq, c.pool_pages = 4, 16, 64
-    c.kv_dtype, c.act_dtype = B.CSA_FP8_E4M3, B.CSA_BF16
+    c.kv_dtype, c.act_dtype, c.swa_dtype = B.CSA_FP8_E4M3, B.CSA_BF16, B.CSA_BF16
     for k, v in kw.items():
         setattr(c, k, v)
     return c
@@ -48,7 +48,8 @@ def _fake_handle(cfg, n_layers=None):
     n = n_layers or cfg.n_layers
     fake = 0x10000
     for l in range(n):
-        for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "gate_stage"):
+        for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "block_stage",
+                  "ring_k_scale", "ring_v_scale"):
             getattr(b, f)[l] = fake
     b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = fake
     b.workspace = 0x100000
@@ -67,7 +68,10 @@ def test_status_strings_and_sizes():
     assert sz.page_scale == 64 * 4
     assert sz.kv_stage == 4 * 64 * 128 * 4
     assert sz.ring == 4 * 128 * 128 * 2
-    assert sz.gate_stage == 4 * 4 * 128 * 2
+    assert sz.block_stage == 4 * 3 * 4 * 128 * 2
+    assert sz.ring_scale == 0
+    fp8_ring = B.csa_buffer_sizes_for(_spec(swa_dtype=B.CSA_FP8_E4M3))
+    assert fp8_ring.ring == 4 * 128 * 128 and fp8_ring.ring_scale == 4 * 128 * 4
     assert sz.block_table == 4 * 16 * 4
     assert B.csa_workspace_size(cfg, 8, 512) > 0
     # workspace grows with the number of queries and with k
@@ -104,7 +108,8 @@ def test_unaligned_workspace_rejected():
     cfg = _spec()
     b = B.Buffers()
     for l in range(cfg.n_layers):
-        for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "gate_stage"):
+        for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "block_stage",
+                  "ring_k_scale", "ring_v_scale"):
             getattr(b, f)[l] = 0x10000
     b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = 0x10000
     b.workspace = 0x100010
@@ -175,6 +180,36 @@ def test_device_calls_validate_before_launch():
         B.csa_cache_destroy(h)
 
 
+def test_window_replay_calls_validate():
+    """csa_seq_set_swa_start takes s >= 0 for a valid sequence; csa_ring_write
+    only rewrites rows that were appended and are still inside the ring."""
+    cfg = _spec()
+    h = _fake_handle(cfg)
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    s = C.c_void_p(0)
+    i32 = B._i32
+    try:
+        B.csa_seq_set_swa_start(h, 0, 100)
+        for seq, start in ((-1, 0), (cfg.max_seqs, 0), (0, -1)):
+            with pytest.raises(B.CsaError):
+                B.csa_seq_set_swa_start(h, seq, start)
+        B.csa_seq_set_len(h, 1, 0, 1000)
+        R = cfg.ring_rows
+        w = lambda seqs, p0, n, k=fake: L.csa_ring_write(C.c_void_p(h), 1, len(seqs), i32(seqs), i32(p0), i32(n), k, fake, s)
+        assert w([0], [990], [11]) == 1                  # row 1000 not appended yet
+        assert w([0], [1000 - R - 1], [2]) == 4          # row already left the ring
+        assert w([0, 0], [995, 996], [1, 1]) == 1        # a sequence listed twice
+        assert w([0], [-1], [1]) == 1
+        assert w([0], [995], [-1]) == 1
+        assert w([0], [995], [5], None) == 1             # rows need data
+        assert w([0], [995], [0], None) == 0             # nothing to write needs none
+        assert L.csa_ring_write(C.c_void_p(h), 7, 1, i32([0]), i32([995]), i32([1]), fake, fake, s) == 1
+        assert B.csa_seq_len(h, 1, 0) == 1000            # rewrites never change lengths
+    finally:
+        B.csa_cache_destroy(h)
+
+
 def test_destroyed_handle_rejected():
     cfg = _spec()
     h = _fake_handle(cfg)
@@ -211,7 +246,8 @@ def test_indexerless_group_accepted_and_sized():
     assert sz.idx_pool == 0 and sz.idx_stage == 0 and sz.kv_pool > 0
     b = B.Buffers()
     fake = 0x10000
-    for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "gate_stage"):
+    for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "block_stage",
+                  "ring_k_scale", "ring_v_scale"):
         for l in range(cfg.n_layers):
             getattr(b, f)[l] = fake
     b.block_table = fake

@@ -65,13 +65,13 @@ def test_device_codecs_match_oracle(golden_dir):
 
 # --------------------------------------------------------------------------- compress
 
-def _compress_case(kv, act, r, lens, seed=3, n_layers=1, chunks=None):
+def _compress_case(kv, act, r, lens, seed=3, n_layers=1, chunks=None, swa=""):
     """Compress seeded rows for each sequence of `lens` on the GPU (in one call,
     or in the given per-call chunk sizes) and return (cache, raw inputs)."""
     max_pages = max(1, max(L // r for L in lens) // 64 + 2)
     cache = make_cache(seed, ratio=r, q_heads=16, window=8, ring_rows=max(16, r), n_layers=n_layers,
                        max_seqs=len(lens), max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 3,
-                       kv_dtype=kv, act_dtype=act, max_queries=len(lens), max_k=64)
+                       kv_dtype=kv, act_dtype=act, max_queries=len(lens), max_k=64, swa_dtype=swa)
     P = Sy.proj_matrix(seed, 128, 64)
     raw = {}
     for layer in range(n_layers):
@@ -169,7 +169,7 @@ def test_compress_incremental_equals_bulk(kv, act):
                 assert torch.equal(bulk.logical_scales(sa, b, n).cpu(), inc.logical_scales(sb, b, n).cpu())
         R = bulk.cfg.ring_rows
         assert torch.equal(bulk.ring_k[0][b].cpu(), inc.ring_k[0][b].cpu())
-        assert torch.equal(bulk.gate_stage[0][b, : (L % 4)].cpu(), inc.gate_stage[0][b, : (L % 4)].cpu())
+        assert torch.equal(bulk.block_stage[0][b, :, : (L % 4)].cpu(), inc.block_stage[0][b, :, : (L % 4)].cpu())
 
 
 # --------------------------------------------------------------------------- index (isolated)
@@ -256,14 +256,18 @@ def test_index_chunk_short_context():
 
 # --------------------------------------------------------------------------- attend (isolated)
 
-def _attend_case(kv, act, lens, k, W, seed=21, n_layers=1, H=64, chunk=None, topk_mode="random", ones_col=False):
+def _attend_case(kv, act, lens, k, W, seed=21, n_layers=1, H=64, chunk=None, topk_mode="random", ones_col=False,
+                 swa="", swa_start=None):
     r = 4
     max_pages = max(L // r for L in lens) // 64 + 2
     n_q = len(lens) if chunk is None else chunk[1]
     R = max(W, r, 8) if chunk is None else max(W, r) + chunk[1]
     cache = make_cache(seed, ratio=r, q_heads=H, window=W, ring_rows=R, n_layers=n_layers, max_seqs=len(lens),
                        max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 2, kv_dtype=kv, act_dtype=act,
-                       max_queries=n_q, max_k=max(k, 1))
+                       max_queries=n_q, max_k=max(k, 1), swa_dtype=swa)
+    starts = swa_start or [0] * len(lens)
+    for b, s0 in enumerate(starts):
+        cache.set_swa_start(b, s0)
     kvs, rings = {}, {}
     for layer in range(n_layers):
         for b, L in enumerate(lens):
@@ -307,10 +311,10 @@ def _attend_case(kv, act, lens, k, W, seed=21, n_layers=1, H=64, chunk=None, top
         for i in range(n_q):
             kb, vb = kvs[layer, q_seq[i]]
             K, V = rings[layer, q_seq[i]]
-            ref = O.attend_step(q64[i], T[i, :k], q_pos[i], W, scale, kb, vb, K, V)
+            ref = O.attend_step(q64[i], T[i, :k], q_pos[i], W, scale, kb, vb, K, V, starts[q_seq[i]])
             err = max_abs(got[i], ref)
             assert err <= TOL[act], f"layer {layer} query {i}: max-abs {err}"
-            if ones_col and kv != "fp8":
+            if ones_col and kv != "fp8" and swa != "fp8":
                 assert np.max(np.abs(got[i][:, 5] - 1.0)) <= (1e-5 if act == "f32" else 2 ** -8)
     return cache
 
@@ -347,13 +351,13 @@ def test_attend_reuse_group_two_layers():
 
 # --------------------------------------------------------------------------- whole step
 
-def _chain(kv, act, lens, k, W, seed=31, n_layers=1, H=16, r=4, dense=False):
+def _chain(kv, act, lens, k, W, seed=31, n_layers=1, H=16, r=4, dense=False, swa=""):
     """Compress -> index -> attend on the GPU, and the same on the oracle, from the same raw rows."""
     max_pages = max(1, max(L // r for L in lens) // 64 + 2)
     R = max(W, r, 8)
     cache = make_cache(seed, ratio=r, q_heads=H, window=W, ring_rows=R, n_layers=n_layers, max_seqs=len(lens),
                        max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 5, kv_dtype=kv,
-                       act_dtype=act, max_queries=len(lens), max_k=k)
+                       act_dtype=act, max_queries=len(lens), max_k=k, swa_dtype=swa)
     P = Sy.proj_matrix(seed, 128, 64)
     raws = {}
     for layer in range(n_layers):
@@ -384,7 +388,8 @@ def _chain(kv, act, lens, k, W, seed=31, n_layers=1, H=16, r=4, dense=False):
         for layer in range(n_layers):
             K, V, Z = raws[layer, b]
             kb, vb, ki = O.compress(K, V, Z, r, P64 if layer == 0 else None)
-            comp[layer] = (O.store(kb, kv)[0], O.store(vb, kv)[0], K, V)
+            comp[layer] = (O.store(kb, kv)[0], O.store(vb, kv)[0], O.store_ring_rows(K, swa)[0],
+                           O.store_ring_rows(V, swa)[0])
             if layer == 0:
                 kis = O.store(ki, kv)[0]
         layers = [dict(q=to64(outs[l][0][b]), W=W, scale=scale, kbar=comp[l][0], vbar=comp[l][1], rawk=comp[l][2],
@@ -619,7 +624,7 @@ def test_serving_steps_ragged_paged_fp8():
 
 # --------------------------------------------------------------------------- heavily compressed attention (no indexer)
 
-def _hca_case(kv, act, lens, r, W, H=64, seed=57, chunk=None):
+def _hca_case(kv, act, lens, r, W, H=64, seed=57, chunk=None, swa=""):
     """Compress with a large ratio and no indexer, then csa_attend_dense; the
     oracle compresses the same raw rows and attends to every visible entry."""
     max_pages = max(1, max(L // r for L in lens) // 64 + 2)
@@ -627,7 +632,7 @@ def _hca_case(kv, act, lens, r, W, H=64, seed=57, chunk=None):
     R = max(W, r, 8) + (0 if chunk is None else chunk[1])
     cache = make_cache(seed, ratio=r, q_heads=H, idx_heads=0, window=W, ring_rows=R, n_layers=1,
                        max_seqs=len(lens), max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 3,
-                       kv_dtype=kv, act_dtype=act, max_queries=n_q, max_k=1)
+                       kv_dtype=kv, act_dtype=act, max_queries=n_q, max_k=1, swa_dtype=swa)
     assert cache.kidx is None
     raws = []
     for b, L in enumerate(lens):
@@ -650,7 +655,7 @@ def _hca_case(kv, act, lens, r, W, H=64, seed=57, chunk=None):
             K, V, Z = raws[b]
             kb, vb, _ = O.compress(K, V, Z, r)
             ents[b] = (O.store(kb, kv)[0], O.store(vb, kv)[0])
-        K, V, _ = raws[b]
+        K, V = (O.store_ring_rows(x, swa)[0] for x in raws[b][:2])
         ref = O.hca_attend_step(to64(q[i]), q_pos[i], r, W, scale, ents[b][0], ents[b][1], K, V)
         err = max_abs(got[i], ref)
         assert err <= TOL[act], f"query {i} (seq {b}, t {q_pos[i]}): max-abs {err}"
@@ -701,3 +706,156 @@ def test_hca_group_rejects_indexer_calls():
     with pytest.raises(RuntimeError):
         cache.index_topk([0], [63], torch.zeros((1, 1, 64), dtype=torch.bfloat16, device="cuda"),
                          torch.ones((1, 1), device="cuda"), 1)
+
+
+# --------------------------------------------------------------------------- window ring: fp8 rows, bounded replay
+
+def _ring_bytes(cache, layer, seq):
+    out = [cache.ring_k[layer][seq].cpu(), cache.ring_v[layer][seq].cpu()]
+    if cache.spec.swa_dtype == "fp8":
+        out += [cache.ring_k_scale[layer][seq].cpu(), cache.ring_v_scale[layer][seq].cpu()]
+    return out
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_fp8_ring_rows_match_oracle_codec(kv):
+    """Compress writes the newest R raw rows as E4M3 codes with one amax/448
+    scale per row: codes and scales equal the oracle's, byte for byte."""
+    lens = [4 * 200 + 3, 77, 5]
+    cache, raw, _ = _compress_case(kv, "bf16", 4, lens, swa="fp8")
+    R = cache.cfg.ring_rows
+    for b, L in enumerate(lens):
+        rows = np.arange(max(0, L - R), L)
+        for x, ring, sc in ((raw[0][b][0], cache.ring_k[0], cache.ring_k_scale[0]),
+                            (raw[0][b][1], cache.ring_v[0], cache.ring_v_scale[0])):
+            _, (codes, scales) = O.store_ring_rows(to64(x)[rows], "fp8")
+            assert np.array_equal(ring[b, rows % R].cpu().numpy(), codes)
+            assert np.array_equal(sc[b, rows % R].cpu().numpy(), scales)
+    assert cache.read_errors() == 0
+
+
+def test_fp8_ring_incremental_equals_bulk():
+    """Appending one row at a time or in uneven chunks leaves the same ring
+    codes, ring scales and open-block staging as one bulk append."""
+    lens = [4 * 70 + 3, 150]
+    bulk, _, _ = _compress_case("fp8", "bf16", 4, lens, seed=19, swa="fp8")
+    inc, _, _ = _compress_case("fp8", "bf16", 4, lens, seed=19, chunks=[1, 1, 5, 2, 30, 1, 64, 3], swa="fp8")
+    for b, L in enumerate(lens):
+        for x, y in zip(_ring_bytes(bulk, 0, b), _ring_bytes(inc, 0, b)):
+            assert torch.equal(x, y)
+        assert torch.equal(bulk.block_stage[0][b, :, : (L % 4)].cpu(), inc.block_stage[0][b, :, : (L % 4)].cpu())
+        n = L // 4
+        assert torch.equal(bulk.logical(bulk.kbar[0], b, n).cpu(), inc.logical(inc.kbar[0], b, n).cpu())
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attend_fp8_ring_decode_matches_oracle(kv):
+    _attend_case(kv, "bf16", lens=[4 * 700 + 2, 4 * 64, 37, 4], k=256, W=128, swa="fp8")
+
+
+def test_attend_fp8_ring_chunk_matches_oracle():
+    _attend_case("fp8", "bf16", lens=[4 * 600 + 1, 400], k=128, W=128, chunk=(0, 48), swa="fp8")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_step_decode_chain_fp8_ring(kv):
+    _chain(kv, "bf16", [4 * 2000 + 3, 999, 130], k=128, W=128, H=64, n_layers=2, swa="fp8")
+
+
+def test_hca_fp8_ring():
+    _hca_case("fp8", "bf16", lens=[64 * 500 + 7, 100], r=64, W=128, swa="fp8")
+
+
+@pytest.mark.parametrize("swa", ["", "fp8"])
+def test_window_bounded_by_replay_start(swa):
+    """With replay start s, the window of a query at t is [max(s, t - W + 1), t]:
+    s inside the window, at the query itself, before the window (no effect)."""
+    lens = [4 * 900 + 1, 4 * 300 + 2, 4 * 50, 4 * 64 + 3]
+    starts = [lens[0] - 40, lens[1] - 1, 10, lens[3] - 127]
+    _attend_case("bf16", "bf16", lens=lens, k=64, W=128, swa=swa, swa_start=starts)
+
+
+def test_window_replay_start_bounds_chunk_queries():
+    """A prefill chunk after a replay start: queries before s + W - 1 see a
+    truncated window, later ones the full W rows."""
+    L = 4 * 500
+    _attend_case("fp8", "bf16", lens=[L, 90], k=64, W=128, chunk=(0, 96), swa_start=[L - 96 - 20, 0])
+
+
+@pytest.mark.parametrize("swa", ["", "fp8"])
+def test_ring_replay_rewrites_window_only(swa):
+    """Bounded replay: rewrite the ring rows [s, L) of a sequence from a second
+    seeded stream. The compressed pages, indexer keys and open-block staging
+    stay byte-identical; attention with replay start s uses the new window
+    rows and the old compressed entries (the oracle gets exactly that)."""
+    r, W, H, k = 4, 128, 16, 64
+    lens = [4 * 400 + 2, 4 * 100]
+    cache, raw, P = _compress_case("fp8", "bf16", r, lens, seed=23, swa=swa)
+    # _compress_case sizes the ring at max(16, r) rows; rebuild with the window here
+    cache = make_cache(23, ratio=r, q_heads=H, window=W, ring_rows=W, max_seqs=2, max_pages_per_seq=cache.spec.max_pages_per_seq,
+                       pool_pages=cache.spec.pool_pages, kv_dtype="fp8", act_dtype="bf16", max_queries=2, max_k=k,
+                       swa_dtype=swa)
+    for b, L in enumerate(lens):
+        cache.compress(0, [b], [L], *(x.cuda() for x in raw[0][b]), P.cuda())
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (cache.kbar[0], cache.vbar[0], cache.kidx, cache.kbar_scale[0], cache.vbar_scale[0],
+                                  cache.kidx_scale, cache.block_stage[0])]
+    s0 = [lens[0] - 50, lens[1] - W]
+    newk = [raw_rows(99, Sy.KIND_K, 0, b, s0[b], L - s0[b], "bf16") for b, L in enumerate(lens)]
+    newv = [raw_rows(99, Sy.KIND_V, 0, b, s0[b], L - s0[b], "bf16") for b, L in enumerate(lens)]
+    cache.ring_write(0, [1, 0], [s0[1], s0[0]], [lens[1] - s0[1], lens[0] - s0[0]],
+                     torch.cat([newk[1], newk[0]]).cuda(), torch.cat([newv[1], newv[0]]).cuda())
+    for b in range(2):
+        cache.set_swa_start(b, s0[b])
+    torch.cuda.synchronize()
+    for x, y in zip(before, (cache.kbar[0], cache.vbar[0], cache.kidx, cache.kbar_scale[0], cache.vbar_scale[0],
+                              cache.kidx_scale, cache.block_stage[0])):
+        assert torch.equal(x, y)
+    assert [cache.seq_len(0, b) for b in range(2)] == lens
+    # ring contents: the oracle codec of the new rows
+    for b, L in enumerate(lens):
+        rows = np.arange(s0[b], L)
+        for x, ring in ((newk[b], cache.ring_k[0]), (newv[b], cache.ring_v[0])):
+            got = ring[b, rows % W].cpu()
+            if swa == "fp8":
+                assert np.array_equal(got.numpy(), O.store_ring_rows(to64(x), "fp8")[1][0])
+            else:
+                assert torch.equal(got, x)
+    # attention against the oracle: old entries, old window rows before s (masked by s), new rows from s
+    qi = Sy.normal_rows(23, Sy.stream_id(Sy.KIND_QI), 0, 2 * 4, 64, dtype=torch.bfloat16).view(2, 4, 64)
+    w = Sy.uniform_rows(23, Sy.stream_id(Sy.KIND_W), 0, 2, 4)
+    q_pos = [L - 1 for L in lens]
+    T = cache.index_topk([0, 1], q_pos, qi.cuda(), w.cuda(), k)
+    q = Sy.normal_rows(23, Sy.stream_id(Sy.KIND_Q), 0, 2 * H, 128, dtype=torch.bfloat16).view(2, H, 128)
+    scale = 1 / math.sqrt(128)
+    out = to64(cache.attend(0, [0, 1], q_pos, q.cuda(), T, k, scale))
+    assert cache.read_errors() == 0
+    Tg = T.cpu().numpy()
+    for b, L in enumerate(lens):
+        K, V, Z = (to64(x) for x in raw[0][b])
+        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        N = O.visible_entries(L - 1, r)
+        kis = O.store(ki, "fp8")[0]
+        To = O.topk(O.index_scores(to64(qi[b]), to64(w[b]), kis[:N]), k)
+        ok, msg = topk_matches(Tg[b], To, O.index_scores(to64(qi[b]), to64(w[b]), kis[:N]), rel=2e-2)
+        assert ok, msg
+        Kr, Vr = K.copy(), V.copy()
+        Kr[s0[b]:], Vr[s0[b]:] = to64(newk[b]), to64(newv[b])
+        Kr, Vr = O.store_ring_rows(Kr, swa)[0], O.store_ring_rows(Vr, swa)[0]
+        ref = O.attend_step(to64(q[b]), Tg[b][Tg[b] >= 0], L - 1, W, scale, O.store(kb, "fp8")[0],
+                            O.store(vb, "fp8")[0], Kr, Vr, s0[b])
+        assert max_abs(out[b], ref) <= TOL["bf16"]
+
+
+def test_ring_write_rejects_rows_outside_the_ring():
+    cache = make_cache(5, ratio=4, q_heads=16, window=32, ring_rows=32, max_seqs=1, max_pages_per_seq=2, pool_pages=2,
+                       kv_dtype="bf16", act_dtype="bf16", max_queries=1, max_k=1)
+    K = raw_rows(5, Sy.KIND_K, 0, 0, 0, 100, "bf16").cuda()
+    cache.compress(0, [0], [100], K, K, K, Sy.proj_matrix(5, 128, 64).cuda())
+    with pytest.raises(B.CsaError):
+        cache.ring_write(0, [0], [60], [8], K[:8], K[:8])       # row 60 left the 32-row ring
+    with pytest.raises(B.CsaError):
+        cache.ring_write(0, [0], [95], [8], K[:8], K[:8])       # rows 100.. not appended
+    cache.ring_write(0, [0], [68], [32], K[:32], K[:32])
+    torch.cuda.synchronize()
+    assert torch.equal(cache.ring_k[0][0, (np.arange(68, 100) % 32)].cpu(), K[:32].cpu())
