@@ -35,6 +35,12 @@ Parity status per function (what pins it in ``tests/test_oracle.py``):
                           loop softmax over the explicit key list
   store_ring_rows ....... each row's amax element -> +-448 code; E4M3 relative
                           error bound; exact round trip of on-grid rows
+  candidate_pool ........ pure-Python brute force with tie fixtures; block = 1
+                          -> the entry Top-K; all blocks kept when few are
+                          visible; the pages' 2,048 x 8 = 16,384 pool size
+  reindex_topk .......... pure-Python brute force; a pool covering every block
+                          -> the full Top-K; the Full layer's own query -> its
+                          own Top-K (k <= pool blocks, distinct scores)
 None is "parity unpinned".
 """
 from __future__ import annotations
@@ -351,6 +357,61 @@ def softmax_weights(q: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray
     m = logits.max(axis=1, keepdims=True)
     p = np.exp(logits - m)
     return p / p.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# hierarchical sparse indexer: the Full layer's candidate pool, Reindex mode
+# ---------------------------------------------------------------------------
+
+POOL_BLOCK = 8  # positions per pool block ("blocks of 8 positions")
+
+
+def candidate_pool(scores: np.ndarray, n_blocks: int, block: int = POOL_BLOCK) -> np.ndarray:
+    """The candidate pool a Full-mode layer builds for one query.
+
+    [Walkthrough] CSA2 "The Hierarchical Sparse Indexer": the Full layer's
+    scores over every visible position are grouped into blocks of `block`
+    positions, a block scores the maximum of its positions, and the best
+    `n_blocks` blocks are kept; every position of a kept block is a candidate.
+    Readings: positions are compressed entries (what the indexer scores);
+    blocks are aligned, [b*block, (b+1)*block), the last one cut at the
+    visible count; equal block scores go to the lower block; the block list
+    is ascending and padded with -1 when fewer blocks are visible (the same
+    rules as the entry Top-K, which this reuses on the block scores).
+
+    scores float32 [N] -> int32 [n_blocks] block ids.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    nb = (s.shape[0] + block - 1) // block
+    bs = np.array([s[b * block:(b + 1) * block].max() for b in range(nb)], dtype=np.float32)
+    return topk(bs, n_blocks)
+
+
+def pool_entries(pool: np.ndarray, n_vis: int, block: int = POOL_BLOCK) -> np.ndarray:
+    """Entries covered by a pool's blocks, ascending, visible ones only."""
+    b = np.asarray([int(x) for x in pool if x >= 0], dtype=np.int64)
+    e = (b[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return e[e < n_vis]
+
+
+def reindex_topk(q_idx: np.ndarray, w: np.ndarray, kidx: np.ndarray, pool: np.ndarray, k: int,
+                 n_vis: int, block: int = POOL_BLOCK) -> np.ndarray:
+    """Top-K of a Reindex-mode layer.
+
+    [Walkthrough] CSA2 "Full, Reindex, and Reuse" (a Reindex layer reuses the
+    shared indexer keys and rescores them with its own indexer query) and
+    "The Hierarchical Sparse Indexer" (deeper indexers score only inside the
+    candidate pool). Scores as index_scores over the pool's visible entries;
+    Top-K as topk (ties to the lower entry, ascending, -1 padding when the
+    pool holds fewer than k entries).
+    """
+    e = pool_entries(pool, n_vis, block)
+    s = index_scores(q_idx, w, np.asarray(kidx)[e])
+    sel = topk(s, k)                      # positions into e; e ascending keeps the rules
+    out = np.full(k, -1, dtype=np.int32)
+    m = sel >= 0
+    out[m] = e[sel[m]]
+    return out
 
 
 # ---------------------------------------------------------------------------

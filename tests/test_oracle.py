@@ -459,3 +459,100 @@ def test_fp8_ring_rows_codec():
     np.testing.assert_array_equal(got, row)
     same, raw = O.store_ring_rows(x, "bf16")
     assert raw is None and np.array_equal(same, x)
+
+
+# --------------------------------------------------------------------------- hierarchical indexer
+
+def _brute_pool(scores, n_blocks, block):
+    """Pure-Python loops: block maxima, sort by (score desc, block asc), keep, sort."""
+    n = len(scores)
+    blocks = []
+    b = 0
+    while b * block < n:
+        m = None
+        for i in range(b * block, min(n, (b + 1) * block)):
+            v = float(np.float32(scores[i]))
+            m = v if m is None or v > m else m
+        blocks.append((m, b))
+        b += 1
+    blocks.sort(key=lambda x: (-x[0], x[1]))
+    keep = sorted(b for _, b in blocks[:n_blocks])
+    return keep + [-1] * (n_blocks - len(keep))
+
+
+def test_candidate_pool_brute_force_and_ties():
+    rng = np.random.default_rng(31)
+    for n, nb, blk in [(1, 1, 8), (7, 1, 8), (8, 1, 8), (9, 2, 8), (100, 5, 8), (257, 32, 8), (300, 100, 8),
+                       (64, 3, 4), (50, 7, 1)]:
+        s = rng.random(n).astype(np.float32)
+        assert list(O.candidate_pool(s, nb, blk)) == _brute_pool(s, nb, blk), (n, nb, blk)
+    # ties: blocks 1 and 3 share the top maximum, blocks 0 and 2 the next one
+    s = np.array([0.5, 0.1, 0.9, 0.2, 0.5, 0.3, 0.9, 0.0], dtype=np.float32)
+    assert list(O.candidate_pool(s, 1, 2)) == [1]
+    assert list(O.candidate_pool(s, 3, 2)) == [0, 1, 3]
+    assert list(O.candidate_pool(np.zeros(40, np.float32), 2, 8)) == [0, 1]
+
+
+def test_candidate_pool_block1_is_entry_topk_and_small_contexts_keep_everything():
+    rng = np.random.default_rng(32)
+    s = rng.random(500).astype(np.float32)
+    assert np.array_equal(O.candidate_pool(s, 37, 1), O.topk(s, 37))
+    assert list(O.candidate_pool(s[:20], 8, 8)) == [0, 1, 2, -1, -1, -1, -1, -1]
+    assert list(O.pool_entries(np.array([2, -1]), 20)) == [16, 17, 18, 19]
+
+
+def test_candidate_pool_worked_size(golden_dir):
+    """The pages' pool: 2,048 blocks of 8 positions give 16,384 candidates."""
+    with open(os.path.join(golden_dir, "worked_sizes.json")) as f:
+        g = json.load(f)["candidate_pool"]
+    s = np.random.default_rng(33).random(262144).astype(np.float32)
+    pool = O.candidate_pool(s, g["blocks"], g["block_positions"])
+    assert O.pool_entries(pool, s.shape[0], g["block_positions"]).shape[0] == g["pool"]
+    assert g["blocks"] * g["block_positions"] == g["pool"]
+
+
+def _brute_reindex(q, w, kidx, pool, k, n_vis, block):
+    cand = []
+    for b in pool:
+        if b < 0:
+            continue
+        for e in range(b * block, b * block + block):
+            if e < n_vis:
+                s = 0.0
+                for h in range(q.shape[0]):
+                    dot = sum(float(q[h, d]) * float(kidx[e, d]) for d in range(q.shape[1]))
+                    s += float(w[h]) * max(0.0, dot)
+                cand.append((float(np.float32(s)), e))
+    cand.sort(key=lambda x: (-x[0], x[1]))
+    sel = sorted(e for _, e in cand[:k])
+    return sel + [-1] * (k - len(sel))
+
+
+def test_reindex_brute_force():
+    rng = np.random.default_rng(34)
+    for n_vis, nb, k in [(50, 3, 5), (50, 3, 30), (17, 4, 3), (200, 10, 12)]:
+        kidx = rng.standard_normal((n_vis + 5, 6))
+        q, w = rng.standard_normal((3, 6)), rng.random(3)
+        pool = np.array(sorted(rng.choice((n_vis + 7) // 8, size=min(nb, (n_vis + 7) // 8), replace=False)) + [-1])
+        got = O.reindex_topk(q, w, kidx, pool, k, n_vis)
+        assert list(got) == _brute_reindex(q, w, kidx, pool, k, n_vis, 8), (n_vis, nb, k)
+
+
+def test_reindex_full_pool_is_full_topk_and_own_query_recovers_full_selection():
+    rng = np.random.default_rng(35)
+    N, k, P = 3000, 64, 128
+    kidx = rng.standard_normal((N, 64))
+    q, w = rng.standard_normal((4, 64)), rng.random(4)
+    s = O.index_scores(q, w, kidx)
+    full = O.topk(s, k)
+    # a pool holding every block: Reindex is the plain Top-K, for any query
+    everything = np.arange((N + 7) // 8)
+    q2, w2 = rng.standard_normal((4, 64)), rng.random(4)
+    assert np.array_equal(O.reindex_topk(q2, w2, kidx, everything, k, N), O.topk(O.index_scores(q2, w2, kidx), k))
+    # the Full layer's pool contains its own Top-K (k <= P), so its own query finds it again
+    pool = O.candidate_pool(s, P)
+    assert set(full.tolist()) <= set(O.pool_entries(pool, N).tolist())
+    assert np.array_equal(O.reindex_topk(q, w, kidx, pool, k, N), full)
+    # a different query generally selects differently, but only from the pool
+    r2 = O.reindex_topk(q2, w2, kidx, pool, k, N)
+    assert set(r2.tolist()) <= set(O.pool_entries(pool, N).tolist())
