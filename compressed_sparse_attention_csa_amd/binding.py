@@ -20,6 +20,8 @@ CSA_PAGE_ENTRIES = 64
 CSA_HEAD_DIM = 128
 CSA_IDX_DIM = 64
 CSA_MAX_TOPK = 2048
+CSA_POOL_BLOCK = 8
+CSA_MAX_POOL_BLOCKS = 2048
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f32": CSA_F32, "bf16": CSA_BF16, "fp8": CSA_FP8_E4M3}
@@ -75,7 +77,7 @@ EXPORTS = [
     "csa_cache_create", "csa_cache_destroy", "csa_seq_reset", "csa_seq_len", "csa_seq_set_len",
     "csa_compress", "csa_index_topk", "csa_attend", "csa_read_errors",
     "csa_profile_begin", "csa_profile_end", "csa_debug_convert", "csa_attend_dense",
-    "csa_seq_set_swa_start", "csa_ring_write",
+    "csa_seq_set_swa_start", "csa_ring_write", "csa_index_topk_pool", "csa_index_reindex",
 ]
 
 _LIB = None
@@ -114,6 +116,10 @@ def lib() -> C.CDLL:
     L.csa_compress.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, vp, vp, vp]
     L.csa_index_topk.restype = C.c_int
     L.csa_index_topk.argtypes = [vp, i32, pi32, pi32, vp, vp, i32, vp, vp]
+    L.csa_index_topk_pool.restype = C.c_int
+    L.csa_index_topk_pool.argtypes = [vp, i32, pi32, pi32, vp, vp, i32, vp, i32, vp, vp]
+    L.csa_index_reindex.restype = C.c_int
+    L.csa_index_reindex.argtypes = [vp, i32, pi32, pi32, vp, vp, i32, vp, i32, vp, vp]
     L.csa_attend.restype = C.c_int
     L.csa_attend.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, i32, C.c_float, vp, vp]
     L.csa_attend_dense.restype = C.c_int
@@ -207,6 +213,18 @@ def csa_compress(h: int, layer: int, seq_ids, n_new, raw_k, raw_v, gate, proj_id
 def csa_index_topk(h: int, q_seq, q_pos, q_idx, w_idx, k: int, topk, stream=None) -> None:
     check(lib().csa_index_topk(C.c_void_p(h), len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q_idx), _ptr(w_idx),
                                k, _ptr(topk), _stream(stream)))
+
+
+def csa_index_topk_pool(h: int, q_seq, q_pos, q_idx, w_idx, k: int, topk, n_pool_blocks: int, pool,
+                        stream=None) -> None:
+    check(lib().csa_index_topk_pool(C.c_void_p(h), len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q_idx), _ptr(w_idx),
+                                    k, _ptr(topk), n_pool_blocks, _ptr(pool), _stream(stream)))
+
+
+def csa_index_reindex(h: int, q_seq, q_pos, q_idx, w_idx, n_pool_blocks: int, pool, k: int, topk,
+                      stream=None) -> None:
+    check(lib().csa_index_reindex(C.c_void_p(h), len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q_idx), _ptr(w_idx),
+                                  n_pool_blocks, _ptr(pool), k, _ptr(topk), _stream(stream)))
 
 
 def csa_attend(h: int, layer: int, q_seq, q_pos, q, topk, k: int, scale: float, out, stream=None) -> None:

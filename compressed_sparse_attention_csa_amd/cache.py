@@ -133,6 +133,20 @@ class CsaCache:
         B.csa_index_topk(self.handle, q_seq, q_pos, q_idx, w_idx, k, topk, stream)
         return topk
 
+    def index_topk_pool(self, q_seq, q_pos, q_idx, w_idx, k, n_pool_blocks, topk=None, pool=None, stream=None):
+        if topk is None:
+            topk = torch.empty((len(q_seq), k), dtype=torch.int32, device=self.device)
+        if pool is None:
+            pool = torch.empty((len(q_seq), n_pool_blocks), dtype=torch.int32, device=self.device)
+        B.csa_index_topk_pool(self.handle, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream)
+        return topk, pool
+
+    def index_reindex(self, q_seq, q_pos, q_idx, w_idx, pool, k, topk=None, stream=None):
+        if topk is None:
+            topk = torch.empty((len(q_seq), k), dtype=torch.int32, device=self.device)
+        B.csa_index_reindex(self.handle, q_seq, q_pos, q_idx, w_idx, pool.shape[1], pool, k, topk, stream)
+        return topk
+
     def attend(self, layer, q_seq, q_pos, q, topk, k, scale, out=None, stream=None):
         if out is None:
             out = torch.empty_like(q)

@@ -89,10 +89,12 @@ int64_t ecap(const csa_config &c) { return static_cast<int64_t>(c.max_pages_per_
 
 int64_t max_slices_for(int64_t s_stride) { return (s_stride + kFilterSlice - 1) / kFilterSlice; }
 
-// S, M, candidate scores, candidate indices (each [nq][s_stride]) and per-slice counts
+// S, M, candidate scores, candidate indices (each [nq][s_stride]), per-slice
+// counts and the 8-entry block maxima of the candidate pool
 size_t idx_decode_bytes(int nq, int64_t s_stride) {
   return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) * 4 +
-         align_up(static_cast<size_t>(nq) * max_slices_for(s_stride) * 4, 256);
+         align_up(static_cast<size_t>(nq) * max_slices_for(s_stride) * 4, 256) +
+         align_up(static_cast<size_t>(nq) * (s_stride / kPoolBlock) * 4, 256);
 }
 // sampled scores, tau, per-tile counts, per-tile candidate regions, fallback rows
 size_t idx_chunk_bytes(int nq, int64_t ss_stride, int64_t fb_stride) {
@@ -469,8 +471,11 @@ csa_status csa_ring_write(csa_cache_t h, int32_t layer, int32_t n_seqs, const in
   return CSA_OK;
 }
 
-csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
-                          const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
+namespace {
+
+// Argument checks shared by the index entry points.
+csa_status check_index_args(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
+                            const float *w_idx, int32_t k, const int32_t *topk) {
   if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
   const csa_config &c = h->cfg;
   if (c.idx_heads == 0) return fail(CSA_ERR_UNSUPPORTED, "this layer group has no indexer (idx_heads = 0)");
@@ -483,99 +488,235 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
     if (q_pos[i] < 0 || q_pos[i] >= L)
       return fail(CSA_ERR_INVALID_ARG, "q_pos[%d] = %d not below the sequence length %lld", i, q_pos[i], static_cast<long long>(L));
   }
+  return CSA_OK;
+}
+
+// Group size G = 2^glog2 of the threshold maxima for n scores and Top-k: at
+// least 4k groups where possible, at most kMaxGroups, G <= 2^gmax.
+int group_log2(int n, int k, int gmax) {
+  int glog2 = 0;
+  while (glog2 < gmax && (((n + (2 << glog2) - 1) >> (glog2 + 1)) >= 4 * k)) ++glog2;
+  while (glog2 < gmax && ((n + (1 << glog2) - 1) >> glog2) > kMaxGroups) ++glog2;
+  return glog2;
+}
+
+struct DecodeScratch {
+  float *S, *M, *cs, *B;
+  int32_t *cj, *cnt;
+  int32_t max_slices;
+};
+
+DecodeScratch carve_decode(csa_cache_t h, int nq, int64_t s_stride) {
+  DecodeScratch d{};
+  char *p = h->scratch;
+  const size_t row = align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
+  d.S = reinterpret_cast<float *>(p); p += row;
+  d.M = reinterpret_cast<float *>(p); p += row;
+  d.cs = reinterpret_cast<float *>(p); p += row;
+  d.cj = reinterpret_cast<int32_t *>(p); p += row;
+  d.cnt = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(nq) * max_slices_for(s_stride) * 4, 256);
+  d.B = reinterpret_cast<float *>(p);
+  d.max_slices = static_cast<int32_t>(max_slices_for(s_stride));
+  return d;
+}
+
+// Prefill chunk: queries of one sequence at consecutive positions.
+csa_status index_chunk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
+                       const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
+  const csa_config &c = h->cfg;
+  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
+  const int pos0 = q_pos[0];
+  const int n_max = (pos0 + n_q) / c.ratio;
+  const int64_t ss_stride = (static_cast<int64_t>(n_max) / kChunkSample + 255) / 256 * 256 + 256;
+  const int64_t fb_stride = (static_cast<int64_t>(n_max) + 63) / 64 * 64;
+  const size_t need = idx_chunk_bytes(n_q, ss_stride, fb_stride);
+  if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for a %d-token chunk (%zu > %zu bytes)", n_q, need, h->scratch_bytes);
+  char *p = h->scratch;
+  IdxChunkArgs s{};
+  s.ss = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * ss_stride * 4, 256);
+  const int64_t tiles = (fb_stride + 255) / 256;
+  s.tau = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * 4, 256);
+  s.cnt = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * 4, 256);
+  s.cand = reinterpret_cast<uint64_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 8, 256);
+  s.fb_rows = reinterpret_cast<float *>(p);
+  s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale;
+  s.bt_row = h->buf.block_table + static_cast<int64_t>(q_seq[0]) * c.max_pages_per_seq;
+  s.q_idx = q_idx; s.w_idx = w_idx; s.topk = topk; s.err = h->err;
+  s.pool_pages = c.pool_pages; s.h_i = c.idx_heads; s.ss_stride = static_cast<int32_t>(ss_stride);
+  s.fb_stride = static_cast<int32_t>(fb_stride); s.n_tok = n_q; s.pos0 = pos0; s.r = c.ratio; s.k = k;
+  s.m_s = std::max(1, (2 * k + kChunkSample - 1) / kChunkSample);
+  s.n_etiles = (n_max + 255) / 256;
+  s.n_stiles = (n_max / kChunkSample + 255) / 256;
+  s.kv_dtype = kv; s.act_dtype = act;
+  const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
+  launch_idx_chunk(s, kv, act, stream, ev.start, ev.stop);
+  launch_idx_chunk_select(s, stream);
+  return CSA_OK;
+}
+
+// Per-query path: scan -> filter -> final, plus the candidate pool when pool
+// is not null.
+csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
+                           const float *w_idx, int32_t k, int32_t *topk, int32_t n_pool, int32_t *pool,
+                           hipStream_t stream) {
+  const csa_config &c = h->cfg;
   const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   const int ab = dt_bytes(c.act_dtype);
+  for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
+    const int nq = std::min(kIdxMaxQ, n_q - g0);
+    int nmax = 0;
+    for (int i = 0; i < nq; ++i) nmax = std::max(nmax, (q_pos[g0 + i] + 1) / c.ratio);
+    const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(nmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
+    const size_t need = idx_decode_bytes(nq, s_stride);
+    if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small (%zu > %zu bytes)", need, h->scratch_bytes);
+    const DecodeScratch d = carve_decode(h, nq, s_stride);
 
-  if (is_chunk(n_q, q_seq, q_pos)) {
-    const int pos0 = q_pos[0];
-    const int n_max = (pos0 + n_q) / c.ratio;
-    const int64_t ss_stride = (static_cast<int64_t>(n_max) / kChunkSample + 255) / 256 * 256 + 256;
-    const int64_t fb_stride = (static_cast<int64_t>(n_max) + 63) / 64 * 64;
-    const size_t need = idx_chunk_bytes(n_q, ss_stride, fb_stride);
-    if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for a %d-token chunk (%zu > %zu bytes)", n_q, need, h->scratch_bytes);
-    char *p = h->scratch;
-    IdxChunkArgs s{};
-    s.ss = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * ss_stride * 4, 256);
-    const int64_t tiles = (fb_stride + 255) / 256;
-    s.tau = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(n_q) * 4, 256);
-    s.cnt = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * 4, 256);
-    s.cand = reinterpret_cast<uint64_t *>(p); p += align_up(static_cast<size_t>(n_q) * tiles * kChunkTileCand * 8, 256);
-    s.fb_rows = reinterpret_cast<float *>(p);
-    s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale;
-    s.bt_row = h->buf.block_table + static_cast<int64_t>(q_seq[0]) * c.max_pages_per_seq;
-    s.q_idx = q_idx; s.w_idx = w_idx; s.topk = topk; s.err = h->err;
-    s.pool_pages = c.pool_pages; s.h_i = c.idx_heads; s.ss_stride = static_cast<int32_t>(ss_stride);
-    s.fb_stride = static_cast<int32_t>(fb_stride); s.n_tok = n_q; s.pos0 = pos0; s.r = c.ratio; s.k = k;
-    s.m_s = std::max(1, (2 * k + kChunkSample - 1) / kChunkSample);
-    s.n_etiles = (n_max + 255) / 256;
-    s.n_stiles = (n_max / kChunkSample + 255) / 256;
-    s.kv_dtype = kv; s.act_dtype = act;
-    const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
-    launch_idx_chunk(s, kv, act, stream, ev.start, ev.stop);
-    launch_idx_chunk_select(s, stream);
-  } else {
-    for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
-      const int nq = std::min(kIdxMaxQ, n_q - g0);
-      int nmax = 0;
-      for (int i = 0; i < nq; ++i) nmax = std::max(nmax, (q_pos[g0 + i] + 1) / c.ratio);
-      const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(nmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
-      const size_t need = idx_decode_bytes(nq, s_stride);
-      if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small (%zu > %zu bytes)", need, h->scratch_bytes);
-      char *p = h->scratch;
-      float *S = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
-      float *M = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
-      float *cs = reinterpret_cast<float *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
-      int32_t *cj = reinterpret_cast<int32_t *>(p); p += align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
-      int32_t *cnt = reinterpret_cast<int32_t *>(p);
-      const int32_t max_slices = static_cast<int32_t>(max_slices_for(s_stride));
-
-      IdxScanArgs s{};
-      s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;
-      s.q_idx = reinterpret_cast<const char *>(q_idx) + static_cast<int64_t>(g0) * c.idx_heads * kDI * ab;
-      s.w_idx = w_idx + static_cast<int64_t>(g0) * c.idx_heads;
-      s.S = S; s.M = M; s.err = h->err;
-      s.bt_stride = c.max_pages_per_seq; s.pool_pages = c.pool_pages; s.h_i = c.idx_heads;
-      s.s_stride = static_cast<int32_t>(s_stride); s.n_q = nq;
-      IdxFilterArgs f{};
-      f.S = S; f.M = M; f.cand_s = cs; f.cand_j = cj; f.cnt = cnt; f.s_stride = s.s_stride; f.k = k; f.n_q = nq;
-      f.max_slices = max_slices;
-      IdxFinalArgs fin{};
-      fin.S = S; fin.cand_s = cs; fin.cand_j = cj; fin.cnt = cnt; fin.err = h->err;
-      fin.topk = topk + static_cast<int64_t>(g0) * k; fin.s_stride = s.s_stride; fin.k = k; fin.n_q = nq;
-      fin.max_slices = max_slices;
-      int wg = 0, slices = 0;
-      for (int i = 0; i < nq; ++i) {
-        const int N = (q_pos[g0 + i] + 1) / c.ratio;
-        // group size G = 2^glog2: at least 4k groups where possible, at most
-        // kMaxGroups, and G <= 256 entries and within one scan workgroup
-        constexpr int kGMax = kIdxChunk < 256 ? (kIdxChunk < 128 ? 6 : 7) : 8;
-        static_assert(kIdxChunk >= 64, "a scan workgroup covers whole pages");
-        int glog2 = 0;
-        while (glog2 < kGMax && (((N + (2 << glog2) - 1) >> (glog2 + 1)) >= 4 * k)) ++glog2;
-        while (glog2 < kGMax && ((N + (1 << glog2) - 1) >> glog2) > kMaxGroups) ++glog2;
-        if (((N + (1 << glog2) - 1) >> glog2) > kMaxGroups)
-          return fail(CSA_ERR_UNSUPPORTED, "query %d sees %d entries; at most %d are supported for k = %d", g0 + i, N, kMaxGroups << kGMax, k);
-        s.q[i].seq = q_seq[g0 + i];
-        s.q[i].n_vis = N;
-        s.q[i].chunk0 = wg;
-        s.q[i].glog2 = glog2;
-        wg += (N + kIdxChunk - 1) / kIdxChunk;
-        f.slice0[i] = slices;
-        f.n_vis[i] = N;
-        f.glog2[i] = glog2;
-        slices += N > k ? (N + kFilterSlice - 1) / kFilterSlice : 0;
-        fin.n_vis[i] = N;
-      }
-      f.slice0[nq] = slices;
-      s.total_wg = wg;
-      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
-      launch_idx_scan(s, kv, act, stream, ev.start, ev.stop);
-      launch_idx_filter(f, slices, stream);
-      launch_idx_final(fin, stream);
+    IdxScanArgs s{};
+    s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;
+    s.q_idx = reinterpret_cast<const char *>(q_idx) + static_cast<int64_t>(g0) * c.idx_heads * kDI * ab;
+    s.w_idx = w_idx + static_cast<int64_t>(g0) * c.idx_heads;
+    s.S = d.S; s.M = d.M; s.B = pool ? d.B : nullptr; s.err = h->err;
+    s.bt_stride = c.max_pages_per_seq; s.pool_pages = c.pool_pages; s.h_i = c.idx_heads;
+    s.s_stride = static_cast<int32_t>(s_stride); s.n_q = nq;
+    IdxFilterArgs f{};
+    f.S = d.S; f.M = d.M; f.cand_s = d.cs; f.cand_j = d.cj; f.cnt = d.cnt; f.s_stride = s.s_stride; f.k = k; f.n_q = nq;
+    f.max_slices = d.max_slices;
+    IdxFinalArgs fin{};
+    fin.S = d.S; fin.cand_s = d.cs; fin.cand_j = d.cj; fin.cnt = d.cnt; fin.err = h->err;
+    fin.topk = topk + static_cast<int64_t>(g0) * k; fin.s_stride = s.s_stride; fin.k = k; fin.n_q = nq;
+    fin.max_slices = d.max_slices;
+    IdxPoolArgs pa{};
+    pa.B = d.B; pa.pool = pool ? pool + static_cast<int64_t>(g0) * n_pool : nullptr; pa.err = h->err;
+    pa.b_stride = static_cast<int32_t>(s_stride / kPoolBlock); pa.n_out = n_pool; pa.n_q = nq;
+    int wg = 0, slices = 0;
+    for (int i = 0; i < nq; ++i) {
+      const int N = (q_pos[g0 + i] + 1) / c.ratio;
+      // groups of G <= 256 entries that stay within one scan workgroup
+      constexpr int kGMax = kIdxChunk < 256 ? (kIdxChunk < 128 ? 6 : 7) : 8;
+      static_assert(kIdxChunk >= 64, "a scan workgroup covers whole pages");
+      const int glog2 = group_log2(N, k, kGMax);
+      if (((N + (1 << glog2) - 1) >> glog2) > kMaxGroups)
+        return fail(CSA_ERR_UNSUPPORTED, "query %d sees %d entries; at most %d are supported for k = %d", g0 + i, N, kMaxGroups << kGMax, k);
+      s.q[i].seq = q_seq[g0 + i];
+      s.q[i].n_vis = N;
+      s.q[i].chunk0 = wg;
+      s.q[i].glog2 = glog2;
+      wg += (N + kIdxChunk - 1) / kIdxChunk;
+      f.slice0[i] = slices;
+      f.n_vis[i] = N;
+      f.glog2[i] = glog2;
+      slices += N > k ? (N + kFilterSlice - 1) / kFilterSlice : 0;
+      fin.n_vis[i] = N;
+      pa.n_vis[i] = N;
     }
+    f.slice0[nq] = slices;
+    s.total_wg = wg;
+    const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
+    launch_idx_scan(s, kv, act, stream, ev.start, ev.stop);
+    launch_idx_filter(f, slices, stream);
+    launch_idx_final(fin, stream);
+    if (pool) launch_idx_pool(pa, stream);
   }
+  return CSA_OK;
+}
+
+}  // namespace
+
+csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
+                          const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
+  csa_status st = check_index_args(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk);
+  if (st != CSA_OK) return st;
+  st = is_chunk(n_q, q_seq, q_pos) ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, stream)
+                                   : index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream);
+  if (st != CSA_OK) return st;
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_topk");
+  return CSA_OK;
+}
+
+csa_status csa_index_topk_pool(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                               const void *q_idx, const float *w_idx, int32_t k, int32_t *topk,
+                               int32_t n_pool_blocks, int32_t *pool, hipStream_t stream) {
+  csa_status st = check_index_args(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk);
+  if (st != CSA_OK) return st;
+  if (n_pool_blocks < 1 || n_pool_blocks > CSA_MAX_POOL_BLOCKS)
+    return fail(CSA_ERR_UNSUPPORTED, "n_pool_blocks = %d outside [1, %d]", n_pool_blocks, CSA_MAX_POOL_BLOCKS);
+  if (!pool) return fail(CSA_ERR_INVALID_ARG, "pool is required");
+  st = index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream);
+  if (st != CSA_OK) return st;
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_topk_pool");
+  return CSA_OK;
+}
+
+csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                             const void *q_idx, const float *w_idx, int32_t n_pool_blocks, const int32_t *pool,
+                             int32_t k, int32_t *topk, hipStream_t stream) {
+  csa_status st = check_index_args(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk);
+  if (st != CSA_OK) return st;
+  if (n_pool_blocks < 1 || n_pool_blocks > CSA_MAX_POOL_BLOCKS)
+    return fail(CSA_ERR_UNSUPPORTED, "n_pool_blocks = %d outside [1, %d]", n_pool_blocks, CSA_MAX_POOL_BLOCKS);
+  if (!pool) return fail(CSA_ERR_INVALID_ARG, "pool is required");
+  const csa_config &c = h->cfg;
+  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
+  const int ab = dt_bytes(c.act_dtype);
+  for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
+    const int nq = std::min(kIdxMaxQ, n_q - g0);
+    // positions of query i: min(pool blocks, visible blocks) * 8, cut at the visible entries
+    std::vector<int> npos(nq), nent(nq);
+    int vmax = 0;
+    for (int i = 0; i < nq; ++i) {
+      nent[i] = (q_pos[g0 + i] + 1) / c.ratio;
+      const int nb = std::min(n_pool_blocks, (nent[i] + kPoolBlock - 1) / kPoolBlock);
+      npos[i] = std::min(nb * kPoolBlock, nent[i]);
+      vmax = std::max(vmax, npos[i]);
+    }
+    const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(vmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
+    const size_t need = idx_decode_bytes(nq, s_stride);
+    if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small (%zu > %zu bytes)", need, h->scratch_bytes);
+    const DecodeScratch d = carve_decode(h, nq, s_stride);
+    IdxRescanArgs s{};
+    s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;
+    s.q_idx = reinterpret_cast<const char *>(q_idx) + static_cast<int64_t>(g0) * c.idx_heads * kDI * ab;
+    s.w_idx = w_idx + static_cast<int64_t>(g0) * c.idx_heads;
+    s.pool = pool + static_cast<int64_t>(g0) * n_pool_blocks; s.pool_stride = n_pool_blocks;
+    s.S = d.S; s.M = d.M; s.err = h->err;
+    s.bt_stride = c.max_pages_per_seq; s.pool_pages = c.pool_pages; s.h_i = c.idx_heads;
+    s.s_stride = static_cast<int32_t>(s_stride); s.n_q = nq;
+    IdxFilterArgs f{};
+    f.S = d.S; f.M = d.M; f.cand_s = d.cs; f.cand_j = d.cj; f.cnt = d.cnt; f.s_stride = s.s_stride; f.k = k; f.n_q = nq;
+    f.max_slices = d.max_slices;
+    IdxFinalArgs fin{};
+    fin.S = d.S; fin.cand_s = d.cs; fin.cand_j = d.cj; fin.cnt = d.cnt; fin.err = h->err;
+    fin.topk = topk + static_cast<int64_t>(g0) * k; fin.s_stride = s.s_stride; fin.k = k; fin.n_q = nq;
+    fin.max_slices = d.max_slices;
+    fin.pool = s.pool; fin.pool_stride = n_pool_blocks;
+    int wg = 0, slices = 0;
+    for (int i = 0; i < nq; ++i) {
+      const int V = npos[i];
+      const int glog2 = group_log2(V, k, 4);   // groups stay inside one 16-position MFMA tile
+      s.q[i].seq = q_seq[g0 + i];
+      s.q[i].n_vis = V;
+      s.q[i].chunk0 = wg;
+      s.q[i].glog2 = glog2;
+      s.n_ent[i] = nent[i];
+      wg += (V + kIdxChunk - 1) / kIdxChunk;
+      f.slice0[i] = slices;
+      f.n_vis[i] = V;
+      f.glog2[i] = glog2;
+      slices += V > k ? (V + kFilterSlice - 1) / kFilterSlice : 0;
+      fin.n_vis[i] = V;
+      fin.n_ent[i] = nent[i];
+    }
+    f.slice0[nq] = slices;
+    s.total_wg = wg;
+    const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
+    launch_idx_rescan(s, kv, act, stream, ev.start, ev.stop);
+    launch_idx_filter(f, slices, stream);
+    launch_idx_final(fin, stream);
+  }
+  if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_reindex");
   return CSA_OK;
 }
 

@@ -68,9 +68,36 @@ struct IdxScanArgs {
   const float *w_idx;  // [n_q][H_I]
   float *S;            // [n_q][s_stride]
   float *M;            // [n_q][s_stride]
+  float *B;            // [n_q][s_stride / kPoolBlock] maxima of 8-entry blocks, or null
   uint32_t *err;
   int32_t bt_stride, pool_pages, h_i, s_stride, n_q, total_wg;
   IdxQuery q[kIdxMaxQ];
+};
+
+// candidate pool of a Full-mode layer: the best n_out blocks by block maximum
+constexpr int kPoolBlock = 8;
+struct IdxPoolArgs {
+  const float *B;      // [n_q][b_stride]
+  int32_t *pool;       // [n_q][n_out] ascending block ids, -1 padding
+  uint32_t *err;
+  int32_t b_stride, n_out, n_q;
+  int32_t n_vis[kIdxMaxQ];   // visible entries per query
+};
+
+// Reindex scores: positions p of a query's pool row map to entries
+// pool[p / 8] * 8 + p % 8; q[i].n_vis counts positions, n_ent visible entries
+struct IdxRescanArgs {
+  const void *kidx;
+  const float *kidx_scale;
+  const int32_t *block_table;
+  const void *q_idx;
+  const float *w_idx;
+  const int32_t *pool;   // [n_q][pool_stride]
+  float *S, *M;          // [n_q][s_stride] position scores and group maxima
+  uint32_t *err;
+  int32_t bt_stride, pool_pages, h_i, s_stride, n_q, total_wg, pool_stride;
+  IdxQuery q[kIdxMaxQ];
+  int32_t n_ent[kIdxMaxQ];
 };
 
 struct IdxFilterArgs {
@@ -91,8 +118,10 @@ struct IdxFinalArgs {
   const int32_t *cnt;
   int32_t *topk;       // [n_q][k]
   uint32_t *err;
-  int32_t s_stride, k, n_q, max_slices;
+  const int32_t *pool; // null, or [n_q][pool_stride]: selected positions map through the pool row
+  int32_t s_stride, k, n_q, max_slices, pool_stride;
   int32_t n_vis[kIdxMaxQ];
+  int32_t n_ent[kIdxMaxQ];   // with a pool: visible entries (mapped entries past it become -1)
 };
 
 // chunk (prefill) index: all queries of one sequence at consecutive positions
@@ -125,6 +154,9 @@ void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
 void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
                       hipEvent_t ev1 = nullptr);
 void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s);
+void launch_idx_pool(const IdxPoolArgs &a, hipStream_t s);
+void launch_idx_rescan(const IdxRescanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 
 // ------------------------------------------------------------------ attend
 

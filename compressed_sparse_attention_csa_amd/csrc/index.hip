@@ -236,6 +236,21 @@ __device__ void bitonic_sort_u64(uint64_t *arr, int n) {
   }
 }
 
+// Output maps of the selects: the selected index itself, or (Reindex) the
+// entry that a pool position stands for.
+struct IdMap {
+  __device__ int32_t operator()(int i) const { return i; }
+};
+struct PoolMap {
+  const int32_t *row;   // the query's pool row (ascending block ids)
+  int n_ent;            // visible entries
+  __device__ int32_t operator()(int p) const {
+    const int b = row[p >> 3];
+    const int e = b * 8 + (p & 7);
+    return (b >= 0 && e < n_ent) ? e : -1;
+  }
+};
+
 // Exact Top-K from c candidate keys already in LDS (k <= c <= kSelCap): sort
 // the keys, keep the k largest (keys are unique: score bits, then ~index, so
 // ties go to the lower index), sort their indices ascending, write out[0..k).
@@ -256,8 +271,9 @@ __device__ void select_sorted_and_write(uint64_t *keys, int c, int k, int *sel, 
 // Exact Top-K of one query from `n` candidates given by a getter (any n >= k;
 // slow multi-pass radix path, used only when candidates overflow LDS),
 // written ascending into out[0..k). sel is LDS of >= next_pow2(k) ints.
-template <typename GetKey>
-__device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *hist, int *sh, int32_t *out) {
+template <typename GetKey, typename Map = IdMap>
+__device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *hist, int *sh, int32_t *out,
+                                 Map map = Map()) {
   const uint64_t kth = kth_largest_u64(key_of, n, k, hist, sh);
   if (threadIdx.x == 0) sh[2] = 0;
   __syncthreads();
@@ -274,7 +290,7 @@ __device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *his
   for (int i = k + threadIdx.x; i < np2; i += blockDim.x) sel[i] = 0x7fffffff;
   __syncthreads();
   bitonic_sort(sel, np2);
-  for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = sel[i];
+  for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = map(sel[i]);
 }
 
 
@@ -289,8 +305,9 @@ __device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *his
 constexpr int kRankCap = 1024;
 constexpr int kSelBins = 2048;
 
+template <typename Map = IdMap>
 __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist, float *red, int *sh,
-                               uint64_t *bin_keys, int32_t *out) {
+                               uint64_t *bin_keys, int32_t *out, Map map = Map()) {
   const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6, nw = bd >> 6;
   float lo = INFINITY, hi = -INFINITY;
   for (int i = t; i < c; i += bd) {
@@ -371,7 +388,7 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   for (int i = 0; i < w; ++i) inc2 += wsum2[i];
   int pos = inc2 - mine;
   for (int i = i0; i < i1; ++i)
-    if (cand_key[i] >= kth) out[pos++] = key_index(cand_key[i]);
+    if (cand_key[i] >= kth) out[pos++] = map(key_index(cand_key[i]));
   (void)nw;
   return true;
 }
@@ -514,6 +531,12 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
         for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
         s = okp[p] ? s * scs[p] : -1.f;   // a missing page scores -1 (and is flagged)
         if (g == 0 && e < N) Srow[e] = s;
+        if (a.B) {   // maxima of aligned 8-entry blocks (candidate pool)
+          float m8 = e < N ? s : -INFINITY;
+#pragma unroll
+          for (int o = 1; o < kPoolBlock; o <<= 1) m8 = fmaxf(m8, __shfl_xor(m8, o, 64));
+          if (g == 0 && (col & (kPoolBlock - 1)) == 0 && e < N) a.B[static_cast<int64_t>(qi) * (a.s_stride / kPoolBlock) + (e >> 3)] = m8;
+        }
         // group maxima: entries past N do not take part
         float m = e < N ? s : -INFINITY;
         if (G <= 16) {
@@ -630,20 +653,25 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
 
 // ------------------------------------------------------------------ decode final
 
-__global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
-  __shared__ uint64_t keys[kSelCap];
-  __shared__ uint64_t bin_keys[kRankCap];
-  __shared__ int sel[CSA_MAX_TOPK];
-  __shared__ int hist[kSelBins];
-  __shared__ int soff[kMaxSlices + 1];
-  __shared__ float red[32];
-  __shared__ int sh[4];
-  __shared__ int wsum_f[16];
-  const int qi = blockIdx.x, tid = threadIdx.x;
-  const int N = a.n_vis[qi], k = a.k;
-  int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
+struct FinalLds {
+  uint64_t keys[kSelCap];
+  uint64_t bin_keys[kRankCap];
+  int sel[CSA_MAX_TOPK];
+  int hist[kSelBins];
+  int soff[kMaxSlices + 1];
+  float red[32];
+  int sh[4];
+  int wsum_f[16];
+};
+
+template <typename Map>
+__device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, int k, int32_t *out, Map map) {
+  uint64_t *keys = L.keys, *bin_keys = L.bin_keys;
+  int *sel = L.sel, *hist = L.hist, *soff = L.soff, *sh = L.sh, *wsum_f = L.wsum_f;
+  float *red = L.red;
+  const int tid = threadIdx.x;
   if (N <= k) {
-    for (int i = tid; i < k; i += blockDim.x) out[i] = i < N ? i : -1;
+    for (int i = tid; i < k; i += blockDim.x) out[i] = i < N ? map(i) : -1;
     return;
   }
   // slice counts -> offsets (slices in index order, each region already ordered)
@@ -682,13 +710,199 @@ __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
       if (i < c) keys[i] = score_key(ts[u], tj[u]);
     }
     __syncthreads();
-    done = select_ordered(keys, c, k, hist, red, sh, bin_keys, out);
+    done = select_ordered(keys, c, k, hist, red, sh, bin_keys, out, map);
   }
   if (!done) {
     // heavy ties or too many candidates: exact select straight from the scores
     if (tid == 0) flag_error(a.err, ERR_FALLBACK);
     const float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
-    select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out);
+    select_and_write([&](int i) { return score_key(Srow[i], i); }, N, k, sel, hist, sh, out, map);
+  }
+}
+
+__global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
+  __shared__ FinalLds lds;
+  const int qi = blockIdx.x;
+  int32_t *out = a.topk + static_cast<int64_t>(qi) * a.k;
+  if (a.pool)
+    final_select(a, lds, qi, a.n_vis[qi], a.k, out, PoolMap{a.pool + static_cast<int64_t>(qi) * a.pool_stride, a.n_ent[qi]});
+  else
+    final_select(a, lds, qi, a.n_vis[qi], a.k, out, IdMap{});
+}
+
+// ------------------------------------------------------------------ candidate pool (Full layer)
+//
+// One workgroup per query over the block maxima B the scan wrote. A threshold
+// tau <= the n_out-th largest block maximum comes from the maxima of groups of
+// 2^gp blocks (distinct blocks, so at least n_out blocks are >= tau); blocks
+// >= tau are compacted in index order and the exact n_out best are kept.
+
+__global__ __launch_bounds__(1024) void idx_pool_kernel(const IdxPoolArgs a) {
+  __shared__ uint64_t keys[kSelCap];          // group maxima (as floats) first, then candidate keys
+  __shared__ uint64_t bin_keys[kRankCap];
+  __shared__ int sel[CSA_MAX_POOL_BLOCKS];
+  __shared__ int hist[kSelBins];
+  __shared__ float red[32];
+  __shared__ int sh[4];
+  __shared__ int wsum[16];
+  static_assert(kMaxGroups * sizeof(float) <= sizeof(keys), "group maxima fit the key buffer");
+  const int qi = blockIdx.x, t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
+  const int N = a.n_vis[qi], P = a.n_out;
+  const int nB = (N + kPoolBlock - 1) / kPoolBlock;
+  int32_t *out = a.pool + static_cast<int64_t>(qi) * P;
+  const float *Brow = a.B + static_cast<int64_t>(qi) * a.b_stride;
+  if (nB <= P) {
+    for (int i = t; i < P; i += bd) out[i] = i < nB ? i : -1;
+    return;
+  }
+  int gp = 0;
+  while (((nB + (1 << gp) - 1) >> gp) > kMaxGroups) ++gp;
+  const int nG = (nB + (1 << gp) - 1) >> gp;
+  float *vals = reinterpret_cast<float *>(keys);
+  for (int i = t; i < nG; i += bd) {
+    float m = -INFINITY;
+    for (int u = 0; u < (1 << gp); ++u) {
+      const int b = (i << gp) + u;
+      if (b < nB) m = fmaxf(m, Brow[b]);
+    }
+    vals[i] = m;
+  }
+  __syncthreads();
+  const float tau = nG > P ? tau_lower_bound([&](int i) { return vals[i]; }, nG, P, hist, red, sh) : -INFINITY;
+  __syncthreads();
+  // ordered compaction of the blocks >= tau over thread-contiguous ranges
+  const int span = (nB + bd - 1) / bd;
+  const int i0 = min(nB, t * span), i1 = min(nB, i0 + span);
+  int mine = 0;
+  for (int i = i0; i < i1; ++i) mine += Brow[i] >= tau;
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int c = 0;
+  for (int i = 0; i < (bd >> 6); ++i) c += wsum[i];
+  for (int i = 0; i < w; ++i) incl += wsum[i];
+  bool done = false;
+  if (c <= kSelCap) {
+    int pos = incl - mine;
+    for (int i = i0; i < i1; ++i) {
+      const float v = Brow[i];
+      if (v >= tau) keys[pos++] = score_key(v, i);
+    }
+    __syncthreads();
+    done = select_ordered(keys, c, P, hist, red, sh, bin_keys, out);
+  }
+  if (!done) {
+    if (t == 0) flag_error(a.err, ERR_FALLBACK);
+    select_and_write([&](int i) { return score_key(Brow[i], i); }, nB, P, sel, hist, sh, out);
+  }
+}
+
+// ------------------------------------------------------------------ Reindex scores
+//
+// The scan's MFMA scoring over pool positions instead of consecutive pages:
+// lane (g, col) of tile tl holds position p = wave_p0 + 16 tl + col, entry
+// pool[p / 8] * 8 + p % 8, so every lane resolves its own page. Positions whose
+// entry is not visible (the tail of the last block) score 0: equal scores go
+// to the lower position, so they are only picked when the pool holds fewer
+// than k entries, and then map to -1.
+
+template <int ACT, int KV>
+__global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRescanArgs a) {
+  using CT = typename ComputeT<KV>::type;
+  const int wg = blockIdx.x;
+  int qlo = 0, qhi = a.n_q;
+  while (qhi - qlo > 1) {
+    const int mid = (qlo + qhi) >> 1;
+    if (a.q[mid].chunk0 <= wg) qlo = mid; else qhi = mid;
+  }
+  const int qi = qlo;
+  const IdxQuery Q = a.q[qi];
+  const int V = Q.n_vis, n_ent = a.n_ent[qi];
+  const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_p0 = (wg - Q.chunk0) * kIdxChunk + w * 64;
+  if (wave_p0 >= V) return;   // no barriers below
+  constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
+  const int32_t *prow = a.pool + static_cast<int64_t>(qi) * a.pool_stride;
+  const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
+  float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
+  float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
+  const int glog2 = Q.glog2, G = 1 << glog2;
+
+  int ent[4], pg[4];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const int p = wave_p0 + tl * 16 + col;
+    const int b = p < V ? prow[p >> 3] : -1;
+    const int e = b * 8 + (p & 7);
+    if (p < V && (b < 0 || b * 8 >= n_ent) && g == 0 && (p & 7) == 0) flag_error(a.err, ERR_TOPK);
+    ent[tl] = (p < V && b >= 0 && e < n_ent) ? e : -1;
+  }
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) pg[tl] = ent[tl] >= 0 ? bt[ent[tl] >> 6] : -1;
+
+  Frag<CT> qa[2];
+  qa[0] = qa[1] = zero_frag<CT>();
+  if (col < a.h_i) {
+    const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + col) * kDI * AE;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qa[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+  }
+  float wv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
+
+  constexpr int RW = KE;
+  const char *kbase = reinterpret_cast<const char *>(a.kidx);
+  uint4 raw[4][RW];
+  bool ok[4];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    ok[tl] = ent[tl] >= 0 && pg[tl] >= 0 && pg[tl] < a.pool_pages;
+    if (ent[tl] >= 0 && !ok[tl] && g == 0) flag_error(a.err, ERR_PAGE);
+    if (ok[tl]) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          kbase + ((static_cast<int64_t>(pg[tl]) * kPage + (ent[tl] & 63)) * kDI + 16 * g) * KE);
+#pragma unroll
+      for (int u = 0; u < RW; ++u) raw[tl][u] = src[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < RW; ++u) raw[tl][u] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  float sc[4];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) sc[tl] = (KV == DT_FP8 && ok[tl]) ? a.kidx_scale[pg[tl]] : 1.f;
+
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const int p_tile = wave_p0 + tl * 16;
+    if (p_tile >= V) break;
+    Frag<CT> kb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const char *rp = reinterpret_cast<const char *>(&raw[tl][0]) + 8 * c * KE;
+      if constexpr (KV == DT_FP8) kb[c] = LoadFrag<DT_FP8, __bf16>::load(rp);
+      else if constexpr (KV == DT_BF16) kb[c] = LoadFrag<DT_BF16, __bf16>::load(rp);
+      else kb[c] = LoadFrag<DT_F32, float>::load(rp);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma(qa[0], kb[0], acc);
+    acc = mma(qa[1], kb[1], acc);
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
+    s = ok[tl] ? s * sc[tl] : 0.f;
+    const int p = p_tile + col;
+    if (g == 0 && p < V) Srow[p] = s;
+    float m = p < V ? s : -INFINITY;
+    for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (g == 0 && (col & (G - 1)) == 0 && p < V) Mrow[p >> glog2] = m;
   }
 }
 
@@ -1035,6 +1249,21 @@ void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s) {
 void launch_idx_final(const IdxFinalArgs &a, hipStream_t s) {
   if (a.n_q <= 0) return;
   hipLaunchKernelGGL(idx_final_kernel, dim3(a.n_q), dim3(512), 0, s, a);
+}
+
+void launch_idx_pool(const IdxPoolArgs &a, hipStream_t s) {
+  if (a.n_q <= 0) return;
+  hipLaunchKernelGGL(idx_pool_kernel, dim3(a.n_q), dim3(1024), 0, s, a);
+}
+
+void launch_idx_rescan(const IdxRescanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.total_wg <= 0) return;
+  if (kv == DT_F32 && act == DT_F32)
+    hipExtLaunchKernelGGL((idx_rescan_kernel<DT_F32, DT_F32>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
+  else if (kv == DT_BF16 && act == DT_BF16)
+    hipExtLaunchKernelGGL((idx_rescan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
+  else if (kv == DT_FP8 && act == DT_BF16)
+    hipExtLaunchKernelGGL((idx_rescan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
 }
 
 void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {

@@ -51,6 +51,8 @@ extern "C" {
 #define CSA_IDX_DIM 64        /* D_I: the one supported indexer key dimension */
 #define CSA_MAX_IDX_HEADS 4   /* H_I <= 4 */
 #define CSA_MAX_TOPK 2048     /* k <= 2048 */
+#define CSA_POOL_BLOCK 8          /* entries per candidate-pool block */
+#define CSA_MAX_POOL_BLOCKS 2048  /* blocks per candidate pool (16,384 entries) */
 
 typedef enum {
   CSA_OK = 0,
@@ -236,6 +238,50 @@ csa_status csa_ring_write(csa_cache_t h, int32_t layer, int32_t n_seqs, const in
 csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
                           const void *q_idx, const float *w_idx, int32_t k, int32_t *topk,
                           hipStream_t stream);
+
+/*
+ * csa_index_topk_pool - csa_index_topk for the group's Full-mode layer that
+ * also builds each query's candidate pool for deeper Reindex-mode layers.
+ * [Walkthrough] CSA2 "The Hierarchical Sparse Indexer" (the first Full layer
+ * scores every causally visible entry; blocks of 8 entries score the maximum
+ * of their entries; the best 2,048 blocks form a 16,384-entry pool).
+ *
+ *   Arguments as csa_index_topk, plus
+ *   n_pool_blocks  1..CSA_MAX_POOL_BLOCKS.
+ *   pool           (dev) [n_q][n_pool_blocks] int32 output: block ids b
+ *                  (entries [8b, 8b+8)) of the n_pool_blocks blocks with the
+ *                  largest block maximum max_{8b <= j < min(8b+8, N)} s[t][j]
+ *                  (ties -> lower b), ascending; -1 pads the row when fewer
+ *                  blocks are visible.
+ * Every query takes the per-query kernels (its scores over all visible
+ * entries are written to the workspace), also when the queries form a chunk.
+ * Errors: as csa_index_topk; CSA_ERR_UNSUPPORTED for n_pool_blocks out of range.
+ */
+csa_status csa_index_topk_pool(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                               const void *q_idx, const float *w_idx, int32_t k, int32_t *topk,
+                               int32_t n_pool_blocks, int32_t *pool, hipStream_t stream);
+
+/*
+ * csa_index_reindex - Top-K of a Reindex-mode layer: its own indexer query
+ * and weights score only the entries of each query's candidate pool (the
+ * shared indexer keys are reused). [Walkthrough] CSA2 "Full, Reindex, and
+ * Reuse" (Reindex rescores the reused keys with its own query) and "The
+ * Hierarchical Sparse Indexer" (deeper indexers search only the pool).
+ *
+ *   s[t][j] as csa_index_topk, for the visible entries j of the blocks in
+ *   pool[t]; topk[t] = the k of them with the largest s (ties -> lower j),
+ *   ascending; -1 pads the row when the pool holds fewer than k entries.
+ *
+ *   q_seq, q_pos, q_idx, w_idx, k, topk as csa_index_topk.
+ *   n_pool_blocks, pool (dev) [n_q][n_pool_blocks]: rows as
+ *   csa_index_topk_pool writes them (ascending block ids, -1 only as trailing
+ *   padding). A block past the visible entries is skipped and sets bit 1
+ *   (a Top-K index outside the visible range) of the csa_read_errors word.
+ * Errors: as csa_index_topk; CSA_ERR_UNSUPPORTED for n_pool_blocks out of range.
+ */
+csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                             const void *q_idx, const float *w_idx, int32_t n_pool_blocks, const int32_t *pool,
+                             int32_t k, int32_t *topk, hipStream_t stream);
 
 /*
  * csa_attend - one layer's attention for n_q queries: one softmax over the

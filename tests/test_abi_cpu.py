@@ -180,6 +180,38 @@ def test_device_calls_validate_before_launch():
         B.csa_cache_destroy(h)
 
 
+def test_pool_and_reindex_calls_validate():
+    """Pool sizes must lie in [1, CSA_MAX_POOL_BLOCKS] with a pool buffer; the
+    query checks are those of csa_index_topk; an indexer-less group refuses."""
+    cfg = _spec()
+    h = _fake_handle(cfg)
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    s = C.c_void_p(0)
+    i32 = B._i32
+    try:
+        B.csa_seq_set_len(h, 0, 0, 4096)
+        tp = lambda pos, k, nb, pool=fake: L.csa_index_topk_pool(C.c_void_p(h), 1, i32([0]), i32([pos]), fake, fake, k,
+                                                                 fake, nb, pool, s)
+        ri = lambda pos, k, nb, pool=fake: L.csa_index_reindex(C.c_void_p(h), 1, i32([0]), i32([pos]), fake, fake, nb,
+                                                               pool, k, fake, s)
+        for f in (tp, ri):
+            assert f(4095, 16, 0) == 5
+            assert f(4095, 16, B.CSA_MAX_POOL_BLOCKS + 1) == 5
+            assert f(4095, 16, 8, None) == 1
+            assert f(4096, 16, 8) == 1          # position past the sequence
+            assert f(4095, 0, 8) == 5
+    finally:
+        B.csa_cache_destroy(h)
+    h = _fake_handle(_spec(idx_heads=0))
+    try:
+        B.csa_seq_set_len(h, 0, 0, 4096)
+        assert L.csa_index_reindex(C.c_void_p(h), 1, i32([0]), i32([4095]), fake, fake, 8, fake, 16, fake, s) == 5
+        assert L.csa_index_topk_pool(C.c_void_p(h), 1, i32([0]), i32([4095]), fake, fake, 16, fake, 8, fake, s) == 5
+    finally:
+        B.csa_cache_destroy(h)
+
+
 def test_window_replay_calls_validate():
     """csa_seq_set_swa_start takes s >= 0 for a valid sequence; csa_ring_write
     only rewrites rows that were appended and are still inside the ring."""
