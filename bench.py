@@ -35,6 +35,7 @@ HBM_PEAK_GBPS = 8000.0
 
 # the workload
 BATCH, CONTEXT, RATIO, TOPK, WINDOW, HEADS, IDX_HEADS, LAYERS = 4, 1 << 20, 4, 1024, 128, 64, 4, 4
+POOL_BLOCKS = 2048   # candidate pool of the hierarchical indexer: 2,048 blocks of 8 entries
 
 
 def parse():
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk MFMA-utilisation leg")
     ap.add_argument("--prefill-only", action="store_true", help="only run the prefill-chunk leg (development)")
     ap.add_argument("--no-hca", action="store_true", help="skip the heavily-compressed-attention leg")
+    ap.add_argument("--no-hier", action="store_true", help="skip the hierarchical-indexer (pool / Reindex) leg")
+    ap.add_argument("--no-swa-fp8", action="store_true", help="skip the fp8 window-ring decode leg")
     return ap.parse_args()
 
 
@@ -223,7 +226,126 @@ def hca_leg(seed, dev, steps=50):
             "hbm_gbps": round(nbytes / (kern_us * 1e-6) / 1e9, 1)}
 
 
-def build_cache(seed, replicas, dev):
+def graph_us(calls, steps, warmup=3):
+    """Mean microseconds per replay of one HIP graph per callable, replays
+    rotating over the callables (each callable enqueues on the stream it gets)."""
+    import torch
+    graphs = []
+    cap = torch.cuda.Stream()
+    for fn in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn(torch.cuda.current_stream())
+        graphs.append(g)
+    for i in range(warmup * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = steps * len(graphs)
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / n
+
+
+def kernel_us(caches, kind, fn, reps):
+    """Mean duration of the score (kind 1) or attention (kind 2) kernel over
+    eager calls fn(i), from events the launches themselves stamp."""
+    import torch
+    from compressed_sparse_attention_csa_amd import binding as B
+    for c in caches:
+        B.csa_profile_begin(c.handle, kind)
+    for i in range(reps):
+        fn(i)
+    torch.cuda.synchronize()
+    ms, n = 0.0, 0
+    for c in caches:
+        m, k = B.csa_profile_end(c.handle, kind)
+        ms += m
+        n += k
+    return ms * 1e3 / max(n, 1)
+
+
+def hier_leg(caches, qi, w, steps, seed):
+    """Hierarchical sparse indexer on the headline caches: the Full layer's
+    Top-K with its 2,048-block candidate pool, and a Reindex layer's Top-K
+    inside that pool with its own indexer query (16,384 of 262,144 entries)."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    dev = qi.device
+    q_seq, q_pos = list(range(BATCH)), [CONTEXT - 1] * BATCH
+    nb = POOL_BLOCKS
+    topk = [torch.empty((BATCH, TOPK), dtype=torch.int32, device=dev) for _ in caches]
+    pools = [torch.empty((BATCH, nb), dtype=torch.int32, device=dev) for _ in caches]
+    t2 = [torch.empty((BATCH, TOPK), dtype=torch.int32, device=dev) for _ in caches]
+    qi2 = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI, 1), 0, BATCH * IDX_HEADS, 64, dev, torch.bfloat16).view(BATCH, IDX_HEADS, 64)
+    w2 = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W, 1), 0, BATCH, IDX_HEADS, dev)
+    full = [lambda s, c=c, r=r: B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, TOPK, topk[r], s)
+            for r, c in enumerate(caches)]
+    full_pool = [lambda s, c=c, r=r: B.csa_index_topk_pool(c.handle, q_seq, q_pos, qi, w, TOPK, topk[r], nb, pools[r], s)
+                 for r, c in enumerate(caches)]
+    reindex = [lambda s, c=c, r=r: B.csa_index_reindex(c.handle, q_seq, q_pos, qi2, w2, nb, pools[r], TOPK, t2[r], s)
+               for r, c in enumerate(caches)]
+    us_full = graph_us(full, steps)
+    us_pool = graph_us(full_pool, steps)      # also leaves every replica's pool in place
+    us_re = graph_us(reindex, steps)
+    stream = torch.cuda.current_stream()
+    rescan_us = kernel_us(caches, B.PROFILE_INDEX, lambda i: reindex[i % len(caches)](stream), steps)
+    flags = max(c.read_errors() for c in caches)
+    if flags & ~B.ERR_FALLBACK:
+        raise RuntimeError(f"hierarchical leg raised device error flags {flags}")
+    pool_entries = nb * 8
+    nbytes = BATCH * A.reindex_bytes(pool_entries, nb, 64, "fp8")
+    return {"workload": f"batch 4, 1,048,576 tokens (262,144 fp8 entries), Top-1024; pool of {nb} blocks x 8 entries "
+                        f"({pool_entries} candidates)",
+            "full_index_us": round(us_full, 3), "full_index_with_pool_us": round(us_pool, 3),
+            "reindex_us": round(us_re, 3), "reindex_score_kernel_us": round(rescan_us, 3),
+            "reindex_score_bytes": nbytes, "reindex_score_gbps": round(nbytes / (rescan_us * 1e-6) / 1e9, 1),
+            "fallback_flag": bool(flags & B.ERR_FALLBACK)}
+
+
+def swa_fp8_leg(seed, dev, replicas, qi, w, qs, steps):
+    """The headline decode step with the window ring stored as E4M3 (one
+    scale per row) instead of bf16: same caches otherwise, same graph timing."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+    caches = build_cache(seed, replicas, dev, swa="fp8")
+    q_seq, q_pos = list(range(BATCH)), [CONTEXT - 1] * BATCH
+    topk = [torch.empty((BATCH, TOPK), dtype=torch.int32, device=dev) for _ in caches]
+    outs = [torch.empty((BATCH, HEADS, 128), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
+    scale = 1.0 / math.sqrt(128)
+
+    def make(r):
+        c = caches[r]
+
+        def fn(s):
+            B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, TOPK, topk[r], s)
+            for l in range(LAYERS):
+                B.csa_attend(c.handle, l, q_seq, q_pos, qs[l], topk[r], TOPK, scale, outs[l], s)
+        return fn
+    us = graph_us([make(r) for r in range(len(caches))], steps)
+    stream = torch.cuda.current_stream()
+
+    def attend_only(i):
+        c = caches[i % len(caches)]
+        for l in range(LAYERS):
+            B.csa_attend(c.handle, l, q_seq, q_pos, qs[l], topk[i % len(caches)], TOPK, scale, outs[l], stream)
+    att_us = kernel_us(caches, B.PROFILE_ATTEND, attend_only, steps // 4 + 1)
+    flags = max(c.read_errors() for c in caches)
+    if flags:
+        raise RuntimeError(f"fp8-ring leg raised device error flags {flags}")
+    for c in caches:
+        c.close()
+    sb = A.decode_step_bytes(BATCH, CONTEXT // RATIO, 128, 64, HEADS, IDX_HEADS, TOPK, WINDOW, LAYERS, "fp8", "bf16", "fp8")
+    return {"workload": "the headline decode step with an fp8 (E4M3, scale per row) window ring",
+            "ms_per_step": round(us * 1e-3, 5), "tokens_per_s": round(BATCH / (us * 1e-6), 1),
+            "attend_kernel_us": round(att_us, 3), "step_bytes": sb}
+
+
+def build_cache(seed, replicas, dev, swa=""):
     import torch
     from compressed_sparse_attention_csa_amd import binding as B
     from compressed_sparse_attention_csa_amd import synth as Sy
@@ -233,7 +355,7 @@ def build_cache(seed, replicas, dev):
     pages = entries // 64
     spec = CacheSpec(ratio=RATIO, q_heads=HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW,
                      n_layers=LAYERS, max_seqs=BATCH, max_pages_per_seq=pages, pool_pages=BATCH * pages,
-                     kv_dtype="fp8", act_dtype="bf16", max_queries=BATCH, max_k=TOPK)
+                     kv_dtype="fp8", act_dtype="bf16", swa_dtype=swa, max_queries=BATCH, max_k=TOPK)
     perm = torch.tensor(Sy.permutation(seed, BATCH * pages, salt=3), dtype=torch.int32)
     bt = perm.view(BATCH, pages).to(dev)
     base = CsaCache(spec, dev, block_table=bt)
@@ -255,6 +377,7 @@ def build_cache(seed, replicas, dev):
         c = CsaCache(spec, dev, block_table=bt)
         for src, dst in ((base.kbar, c.kbar), (base.vbar, c.vbar), (base.kbar_scale, c.kbar_scale),
                          (base.vbar_scale, c.vbar_scale), (base.ring_k, c.ring_k), (base.ring_v, c.ring_v),
+                         (base.ring_k_scale, c.ring_k_scale), (base.ring_v_scale, c.ring_v_scale),
                          (base.kbar_stage, c.kbar_stage), (base.vbar_stage, c.vbar_stage),
                          (base.block_stage, c.block_stage)):
             for s_, d_ in zip(src, dst):
@@ -455,8 +578,13 @@ def main():
                      "traffic_scope": traffic_scope,
                      "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
     }
+    if not args.no_hier:
+        line["hierarchical"] = hier_leg(caches, qi, w, max(10, args.steps // 4), args.seed)
     del caches, graphs
     torch.cuda.empty_cache()
+    if not args.no_swa_fp8:
+        line["swa_fp8"] = swa_fp8_leg(args.seed, dev, args.replicas, qi, w, qs, args.steps)
+        torch.cuda.empty_cache()
     if not args.no_prefill:
         line["prefill"] = prefill_leg(args.seed, dev)
     if not args.no_hca:

@@ -25,26 +25,42 @@ def index_scan_bytes(n_entries: int, d_i: int, kv_dtype: str, page_entries: int 
     return b
 
 
-def attend_bytes(k_sel: int, window: int, d: int, h_q: int, kv_dtype: str, act_dtype: str) -> int:
+def attend_bytes(k_sel: int, window: int, d: int, h_q: int, kv_dtype: str, act_dtype: str,
+                 swa_dtype: str | None = None) -> int:
     """Bytes one query's attention reads and writes for one layer.
 
     Gathered compressed K and V rows (plus one K and one V page scale per
-    gathered entry for fp8), the window's raw K and V rows, the query, the
+    gathered entry for fp8), the window's K and V rows in the ring's format
+    (plus one K and one V row scale each for an fp8 ring), the query, the
     output, and the Top-K row it reads.
     """
     kvb = DTYPE_BYTES[kv_dtype]
     ab = DTYPE_BYTES[act_dtype]
+    sd = swa_dtype or act_dtype
     b = k_sel * 2 * d * kvb
     if kv_dtype == "fp8":
         b += k_sel * 2 * 4
-    b += window * 2 * d * ab
+    b += window * 2 * d * DTYPE_BYTES[sd]
+    if sd == "fp8":
+        b += window * 2 * 4
     b += 2 * h_q * d * ab
     b += k_sel * 4
     return b
 
 
+def reindex_bytes(pool_entries: int, n_blocks: int, d_i: int, kv_dtype: str) -> int:
+    """Bytes one query's Reindex scores read: the pool's indexer keys, its
+    block ids and (fp8) one page scale per block (an aligned 8-entry block
+    lies inside one 64-entry page)."""
+    b = pool_entries * d_i * DTYPE_BYTES[kv_dtype] + n_blocks * 4
+    if kv_dtype == "fp8":
+        b += n_blocks * 4
+    return b
+
+
 def decode_step_bytes(n_seq: int, entries: list[int] | int, d: int, d_i: int, h_q: int, h_i: int,
-                      k: int, window: int, group: int, kv_dtype: str, act_dtype: str) -> int:
+                      k: int, window: int, group: int, kv_dtype: str, act_dtype: str,
+                      swa_dtype: str | None = None) -> int:
     """Algorithmic HBM bytes of one decode step: one index pass + `group` attends.
 
     entries: visible compressed entries per sequence (one int for all, or a list).
@@ -57,7 +73,7 @@ def decode_step_bytes(n_seq: int, entries: list[int] | int, d: int, d_i: int, h_
         total += index_scan_bytes(n, d_i, kv_dtype)
         total += h_i * d_i * ab + h_i * 4 + k * 4          # q_idx, w, Top-K row written
         k_sel = min(k, n)
-        total += group * attend_bytes(k_sel, window, d, h_q, kv_dtype, act_dtype)
+        total += group * attend_bytes(k_sel, window, d, h_q, kv_dtype, act_dtype, swa_dtype)
     return total
 
 

@@ -94,7 +94,7 @@ int64_t max_slices_for(int64_t s_stride) { return (s_stride + kFilterSlice - 1) 
 size_t idx_decode_bytes(int nq, int64_t s_stride) {
   return align_up(static_cast<size_t>(nq) * s_stride * 4, 256) * 4 +
          align_up(static_cast<size_t>(nq) * max_slices_for(s_stride) * 4, 256) +
-         align_up(static_cast<size_t>(nq) * (s_stride / kPoolBlock) * 4, 256);
+         align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
 }
 // sampled scores, tau, per-tile counts, per-tile candidate regions, fallback rows
 size_t idx_chunk_bytes(int nq, int64_t ss_stride, int64_t fb_stride) {
@@ -587,10 +587,14 @@ csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, con
     fin.S = d.S; fin.cand_s = d.cs; fin.cand_j = d.cj; fin.cnt = d.cnt; fin.err = h->err;
     fin.topk = topk + static_cast<int64_t>(g0) * k; fin.s_stride = s.s_stride; fin.k = k; fin.n_q = nq;
     fin.max_slices = d.max_slices;
-    IdxPoolArgs pa{};
-    pa.B = d.B; pa.pool = pool ? pool + static_cast<int64_t>(g0) * n_pool : nullptr; pa.err = h->err;
-    pa.b_stride = static_cast<int32_t>(s_stride / kPoolBlock); pa.n_out = n_pool; pa.n_q = nq;
-    int wg = 0, slices = 0;
+    // the pool reuses filter and final on the block maxima B: a group of G >= 8
+    // entries is a group of G / 8 whole blocks, so the topk's group maxima M
+    // are maxima of distinct blocks and bound the n_pool-th block maximum
+    IdxFilterArgs pf = f;
+    pf.S = d.B; pf.k = n_pool;
+    IdxFinalArgs pfin = fin;
+    pfin.S = d.B; pfin.k = n_pool; pfin.topk = pool ? pool + static_cast<int64_t>(g0) * n_pool : nullptr;
+    int wg = 0, slices = 0, pslices = 0;
     for (int i = 0; i < nq; ++i) {
       const int N = (q_pos[g0 + i] + 1) / c.ratio;
       // groups of G <= 256 entries that stay within one scan workgroup
@@ -609,15 +613,25 @@ csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, con
       f.glog2[i] = glog2;
       slices += N > k ? (N + kFilterSlice - 1) / kFilterSlice : 0;
       fin.n_vis[i] = N;
-      pa.n_vis[i] = N;
+      const int nb = (N + kPoolBlock - 1) / kPoolBlock;
+      pf.slice0[i] = pslices;
+      pf.n_vis[i] = nb;
+      // groups smaller than a block give no bound: a huge group count of 1 turns the threshold off
+      pf.glog2[i] = glog2 >= 3 ? glog2 - 3 : 30;
+      pslices += nb > n_pool ? (nb + kFilterSlice - 1) / kFilterSlice : 0;
+      pfin.n_vis[i] = nb;
     }
     f.slice0[nq] = slices;
+    pf.slice0[nq] = pslices;
     s.total_wg = wg;
     const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
     launch_idx_scan(s, kv, act, stream, ev.start, ev.stop);
     launch_idx_filter(f, slices, stream);
     launch_idx_final(fin, stream);
-    if (pool) launch_idx_pool(pa, stream);
+    if (pool) {
+      launch_idx_filter(pf, pslices, stream);
+      launch_idx_final(pfin, stream);
+    }
   }
   return CSA_OK;
 }

@@ -68,21 +68,14 @@ struct IdxScanArgs {
   const float *w_idx;  // [n_q][H_I]
   float *S;            // [n_q][s_stride]
   float *M;            // [n_q][s_stride]
-  float *B;            // [n_q][s_stride / kPoolBlock] maxima of 8-entry blocks, or null
+  float *B;            // [n_q][s_stride] maxima of aligned 8-entry blocks (first N/8 used), or null
   uint32_t *err;
   int32_t bt_stride, pool_pages, h_i, s_stride, n_q, total_wg;
   IdxQuery q[kIdxMaxQ];
 };
 
-// candidate pool of a Full-mode layer: the best n_out blocks by block maximum
+// candidate pool of a Full-mode layer: blocks of 8 entries
 constexpr int kPoolBlock = 8;
-struct IdxPoolArgs {
-  const float *B;      // [n_q][b_stride]
-  int32_t *pool;       // [n_q][n_out] ascending block ids, -1 padding
-  uint32_t *err;
-  int32_t b_stride, n_out, n_q;
-  int32_t n_vis[kIdxMaxQ];   // visible entries per query
-};
 
 // Reindex scores: positions p of a query's pool row map to entries
 // pool[p / 8] * 8 + p % 8; q[i].n_vis counts positions, n_ent visible entries
@@ -154,7 +147,6 @@ void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
 void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
                       hipEvent_t ev1 = nullptr);
 void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s);
-void launch_idx_pool(const IdxPoolArgs &a, hipStream_t s);
 void launch_idx_rescan(const IdxRescanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
 

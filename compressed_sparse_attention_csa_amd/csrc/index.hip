@@ -535,7 +535,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
           float m8 = e < N ? s : -INFINITY;
 #pragma unroll
           for (int o = 1; o < kPoolBlock; o <<= 1) m8 = fmaxf(m8, __shfl_xor(m8, o, 64));
-          if (g == 0 && (col & (kPoolBlock - 1)) == 0 && e < N) a.B[static_cast<int64_t>(qi) * (a.s_stride / kPoolBlock) + (e >> 3)] = m8;
+          if (g == 0 && (col & (kPoolBlock - 1)) == 0 && e < N) a.B[static_cast<int64_t>(qi) * a.s_stride + (e >> 3)] = m8;
         }
         // group maxima: entries past N do not take part
         float m = e < N ? s : -INFINITY;
@@ -728,78 +728,6 @@ __global__ __launch_bounds__(512) void idx_final_kernel(const IdxFinalArgs a) {
     final_select(a, lds, qi, a.n_vis[qi], a.k, out, PoolMap{a.pool + static_cast<int64_t>(qi) * a.pool_stride, a.n_ent[qi]});
   else
     final_select(a, lds, qi, a.n_vis[qi], a.k, out, IdMap{});
-}
-
-// ------------------------------------------------------------------ candidate pool (Full layer)
-//
-// One workgroup per query over the block maxima B the scan wrote. A threshold
-// tau <= the n_out-th largest block maximum comes from the maxima of groups of
-// 2^gp blocks (distinct blocks, so at least n_out blocks are >= tau); blocks
-// >= tau are compacted in index order and the exact n_out best are kept.
-
-__global__ __launch_bounds__(1024) void idx_pool_kernel(const IdxPoolArgs a) {
-  __shared__ uint64_t keys[kSelCap];          // group maxima (as floats) first, then candidate keys
-  __shared__ uint64_t bin_keys[kRankCap];
-  __shared__ int sel[CSA_MAX_POOL_BLOCKS];
-  __shared__ int hist[kSelBins];
-  __shared__ float red[32];
-  __shared__ int sh[4];
-  __shared__ int wsum[16];
-  static_assert(kMaxGroups * sizeof(float) <= sizeof(keys), "group maxima fit the key buffer");
-  const int qi = blockIdx.x, t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
-  const int N = a.n_vis[qi], P = a.n_out;
-  const int nB = (N + kPoolBlock - 1) / kPoolBlock;
-  int32_t *out = a.pool + static_cast<int64_t>(qi) * P;
-  const float *Brow = a.B + static_cast<int64_t>(qi) * a.b_stride;
-  if (nB <= P) {
-    for (int i = t; i < P; i += bd) out[i] = i < nB ? i : -1;
-    return;
-  }
-  int gp = 0;
-  while (((nB + (1 << gp) - 1) >> gp) > kMaxGroups) ++gp;
-  const int nG = (nB + (1 << gp) - 1) >> gp;
-  float *vals = reinterpret_cast<float *>(keys);
-  for (int i = t; i < nG; i += bd) {
-    float m = -INFINITY;
-    for (int u = 0; u < (1 << gp); ++u) {
-      const int b = (i << gp) + u;
-      if (b < nB) m = fmaxf(m, Brow[b]);
-    }
-    vals[i] = m;
-  }
-  __syncthreads();
-  const float tau = nG > P ? tau_lower_bound([&](int i) { return vals[i]; }, nG, P, hist, red, sh) : -INFINITY;
-  __syncthreads();
-  // ordered compaction of the blocks >= tau over thread-contiguous ranges
-  const int span = (nB + bd - 1) / bd;
-  const int i0 = min(nB, t * span), i1 = min(nB, i0 + span);
-  int mine = 0;
-  for (int i = i0; i < i1; ++i) mine += Brow[i] >= tau;
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int c = 0;
-  for (int i = 0; i < (bd >> 6); ++i) c += wsum[i];
-  for (int i = 0; i < w; ++i) incl += wsum[i];
-  bool done = false;
-  if (c <= kSelCap) {
-    int pos = incl - mine;
-    for (int i = i0; i < i1; ++i) {
-      const float v = Brow[i];
-      if (v >= tau) keys[pos++] = score_key(v, i);
-    }
-    __syncthreads();
-    done = select_ordered(keys, c, P, hist, red, sh, bin_keys, out);
-  }
-  if (!done) {
-    if (t == 0) flag_error(a.err, ERR_FALLBACK);
-    select_and_write([&](int i) { return score_key(Brow[i], i); }, nB, P, sel, hist, sh, out);
-  }
 }
 
 // ------------------------------------------------------------------ Reindex scores
@@ -1249,11 +1177,6 @@ void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s) {
 void launch_idx_final(const IdxFinalArgs &a, hipStream_t s) {
   if (a.n_q <= 0) return;
   hipLaunchKernelGGL(idx_final_kernel, dim3(a.n_q), dim3(512), 0, s, a);
-}
-
-void launch_idx_pool(const IdxPoolArgs &a, hipStream_t s) {
-  if (a.n_q <= 0) return;
-  hipLaunchKernelGGL(idx_pool_kernel, dim3(a.n_q), dim3(1024), 0, s, a);
 }
 
 void launch_idx_rescan(const IdxRescanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
