@@ -33,6 +33,11 @@ Parity status per function (what pins it in ``tests/test_oracle.py``):
                           banded SDPA; single key; equal logits -> mean
   hca_attend_step ....... r = 1, W = 0 -> torch SDPA causal; a pure-Python
                           loop softmax over the explicit key list
+  e2m1_encode/decode .... the E2M1 value set from its bit layout; hand-worked
+                          ties; saturation at 6; the pages' 448 x 6 = 2688 range
+  fp4_quantize_rows ..... exact round trip of on-grid groups; amax -> +-6 when
+                          amax/6 is an E4M3 value; groups independent; the
+                          E2M1 half-step plus scale-rounding error bound
   store_ring_rows ....... each row's amax element -> +-448 code; E4M3 relative
                           error bound; exact round trip of on-grid rows
   candidate_pool ........ pure-Python brute force with tie fixtures; block = 1
@@ -175,14 +180,75 @@ def compress(K: np.ndarray, V: np.ndarray, Z: np.ndarray, r: int,
     return kbar, vbar, kidx
 
 
+# ---------------------------------------------------------------------------
+# FP4 main KV: E2M1 elements, one E4M3 scale per 16 channels
+# ---------------------------------------------------------------------------
+
+E2M1_MAX = 6.0      # the FP4 section's range 2688 = 448 (E4M3) x 6 (E2M1)
+FP4_GROUP = 16      # channels sharing one scale
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes -> float64: bit 3 sign, bits 2-1 exponent (bias 1),
+    bit 0 mantissa; exponent 0 is subnormal (0 or 0.5)."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(x32: np.ndarray) -> np.ndarray:
+    """float32 values -> E2M1 codes: nearest of the 8 magnitudes, a tie going
+    to the even code, saturating at 6; the sign bit is the input's IEEE sign."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    mags = e2m1_decode(np.arange(8))                       # 0, .5, 1, 1.5, 2, 3, 4, 6
+    d = np.abs(a[..., None] - mags)                         # [..., 8]
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))
+    code = np.where(a >= E2M1_MAX, 7, code)
+    return (code | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
+
+
+def fp4_quantize_rows(x32: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Entries [E, D] float32 -> (E2M1 codes [E, D], E4M3 scale codes [E, D/16]).
+
+    [Walkthrough] "FP4 main KV cache" (E2M1 elements, one E4M3 scale per 16
+    channels, no second-level scale). Reading (the scale rule is not given):
+    the scale is amax/6 of the 16 values (fp32 division) rounded to the
+    nearest E4M3 value; elements are E2M1(x / scale) with an IEEE fp32
+    division; a group whose scale rounds to 0 stores all-zero codes.
+    """
+    x32 = np.asarray(x32, dtype=np.float32)
+    E, D = x32.shape
+    g = x32.reshape(E, D // FP4_GROUP, FP4_GROUP)
+    amax = np.abs(g).max(axis=-1)
+    sc = e4m3_encode((amax / np.float32(E2M1_MAX)).astype(np.float32))
+    s = e4m3_decode(sc).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0))
+    q = (g / safe[..., None]).astype(np.float32)
+    codes = np.where(s[..., None] > 0, e2m1_encode(q), 0).astype(np.uint8)
+    return codes.reshape(E, D), sc
+
+
+def fp4_dequantize_rows(codes: np.ndarray, scale_codes: np.ndarray) -> np.ndarray:
+    E, D = codes.shape
+    s = e4m3_decode(scale_codes)
+    return (e2m1_decode(codes).reshape(E, D // FP4_GROUP, FP4_GROUP) * s[..., None]).reshape(E, D)
+
+
 def store(x64: np.ndarray, dtype: str, page_entries: int = 64):
     """Round compressed entries [E, width] to the cache format, page by page.
 
     Returns (values as float64 exactly as the cache holds them, raw payload):
     raw is float32 array ('f32'), uint16 bf16 bits ('bf16') or
-    (uint8 codes [E, width], float32 scales [n_pages]) ('fp8'). Page p holds
-    entries [64p, 64p+64) of the sequence; the last page may be partly filled
-    and its scale covers its filled entries only.
+    (uint8 codes [E, width], float32 scales [n_pages]) ('fp8'), or
+    (E2M1 codes [E, width], E4M3 scale codes [E, width/16]) ('fp4', every entry
+    on its own). Page p holds entries [64p, 64p+64) of the sequence; the last
+    page may be partly filled and its fp8 scale covers its filled entries only.
     """
     x64 = np.asarray(x64, dtype=np.float64)
     if dtype == "f32":
@@ -205,6 +271,9 @@ def store(x64: np.ndarray, dtype: str, page_entries: int = 64):
             scales[p] = s
             vals[sl] = e4m3_decode(c) * np.float64(s)
         return vals, (codes, scales)
+    if dtype == "fp4":
+        codes, sc = fp4_quantize_rows(round_f32(x64))
+        return fp4_dequantize_rows(codes, sc), (codes, sc)
     raise ValueError(dtype)
 
 

@@ -556,3 +556,74 @@ def test_reindex_full_pool_is_full_topk_and_own_query_recovers_full_selection():
     # a different query generally selects differently, but only from the pool
     r2 = O.reindex_topk(q2, w2, kidx, pool, k, N)
     assert set(r2.tolist()) <= set(O.pool_entries(pool, N).tolist())
+
+
+# --------------------------------------------------------------------------- FP4 main KV
+
+def test_e2m1_values_and_ties(golden_dir):
+    """E2M1 from its bit layout (1 sign, 2 exponent bits with bias 1, 1 mantissa
+    bit, exponent 0 subnormal): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6."""
+    expect = []
+    for c in range(16):
+        e, m = (c >> 1) & 3, c & 1
+        mag = (m * 0.5) if e == 0 else (1 + m / 2) * 2.0 ** (e - 1)
+        expect.append(-mag if c & 8 else mag)
+    assert O.e2m1_decode(np.arange(16)).tolist() == expect
+    with open(os.path.join(golden_dir, "worked_sizes.json")) as f:
+        g = json.load(f)["fp4_range"]
+    assert max(expect) == g["e2m1_max"] and g["e4m3_max"] * g["e2m1_max"] == g["range"]
+    assert float(O.e4m3_decode(np.array([0x7E]))[0]) * max(expect) == g["range"]
+    # round trip and hand-worked ties (ties go to the even code)
+    vals = np.array(expect, dtype=np.float32)
+    assert np.array_equal(O.e2m1_decode(O.e2m1_encode(vals)), vals.astype(np.float64))
+    x = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 1e9, 0.2, 0.3, 4.9, 5.1, -0.1, -2.6], dtype=np.float32)
+    assert O.e2m1_encode(x).tolist() == [0, 2, 2, 4, 4, 6, 6, 7, 7, 0, 1, 6, 7, 8, 13]
+
+
+def test_fp4_rows_quantization():
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal((50, 128)) * rng.uniform(0.01, 5, (50, 1))).astype(np.float32)
+    codes, sc = O.fp4_quantize_rows(x)
+    deq = O.fp4_dequantize_rows(codes, sc)
+    s = O.e4m3_decode(sc)                                     # [50, 8]
+    g = x.reshape(50, 8, 16).astype(np.float64)
+    q = np.abs(g) / s[..., None]
+    # E2M1 spacing at |x|/s: .5 below 2, 1 below 4, 2 up to 6; beyond 6 the value clips
+    half = np.where(q < 2, 0.25, np.where(q < 4, 0.5, 1.0))
+    err = np.abs(deq.reshape(50, 8, 16) - g) / s[..., None]
+    assert np.all(err <= np.maximum(half, q - 6.0) + 1e-12)
+    # the scale is amax/6 to E4M3's half-step (2^-4 relative for normal scales,
+    # 2^-10 absolute below 2^-6), so a normal-scale group clips at most to 6 / (1 - 2^-4)
+    t = np.abs(g).max(axis=-1) / 6.0
+    normal = t >= 2.0 ** -6
+    assert np.all(np.abs(s - t)[normal] <= 2.0 ** -4 * t[normal] * (1 + 1e-6))
+    assert np.all(np.abs(s - t)[~normal] <= 2.0 ** -10 * (1 + 1e-6))
+    assert np.all(q.max(axis=-1)[normal] <= 6.0 / (1 - 2.0 ** -4) + 1e-9)
+    # groups are independent: changing one group leaves every other code as it was
+    y = x.copy()
+    y[3, 16:32] *= 3.0
+    c2, s2 = O.fp4_quantize_rows(y)
+    mask = np.ones((50, 128), bool)
+    mask[3, 16:32] = False
+    assert np.array_equal(c2[mask], codes[mask])
+    assert np.array_equal(np.delete(s2.reshape(-1), 3 * 8 + 1), np.delete(sc.reshape(-1), 3 * 8 + 1))
+
+
+def test_fp4_on_grid_groups_round_trip():
+    """A group built as E2M1 values times an E4M3 scale s with amax = 6 s comes
+    back exactly, its amax element as code +-6; an all-zero group gives zeros."""
+    rng = np.random.default_rng(62)
+    mags = O.e2m1_decode(np.arange(16))
+    sgrid = O.e4m3_decode(np.arange(0x08, 0x7F, dtype=np.uint8))   # normal scales
+    rows = []
+    for i in range(40):
+        s = sgrid[rng.integers(len(sgrid))]
+        grp = mags[rng.integers(16, size=(8, 16))]
+        grp[:, 0] = 6.0 * np.where(rng.random(8) < .5, -1, 1)
+        rows.append((grp * s).reshape(-1))
+    x = np.array(rows, dtype=np.float32)
+    x[5, 32:48] = 0.0
+    vals, (codes, sc) = O.store(x.astype(np.float64), "fp4")
+    np.testing.assert_array_equal(vals, x.astype(np.float64))
+    assert np.all((codes.reshape(40, 8, 16)[..., 0] & 7)[np.arange(40) != 5] == 7)
+    assert np.all(codes[5, 32:48] == 0)
