@@ -23,8 +23,8 @@ CSA_MAX_TOPK = 2048
 CSA_POOL_BLOCK = 8
 CSA_MAX_POOL_BLOCKS = 2048
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
-DTYPE_CODES = {"f32": CSA_F32, "bf16": CSA_BF16, "fp8": CSA_FP8_E4M3}
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": CSA_F32, "bf16": CSA_BF16, "fp8": CSA_FP8_E4M3, "fp4": CSA_FP4_E2M1}
 
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_DTYPE",
           4: "CSA_ERR_CAPACITY", 5: "CSA_ERR_UNSUPPORTED", 6: "CSA_ERR_HIP"}
@@ -52,6 +52,8 @@ class Buffers(C.Structure):
         ("vbar_scale", C.c_void_p * CSA_MAX_LAYERS),
         ("kbar_stage", C.c_void_p * CSA_MAX_LAYERS),
         ("vbar_stage", C.c_void_p * CSA_MAX_LAYERS),
+        ("kbar_gscale", C.c_void_p * CSA_MAX_LAYERS),
+        ("vbar_gscale", C.c_void_p * CSA_MAX_LAYERS),
         ("ring_k", C.c_void_p * CSA_MAX_LAYERS),
         ("ring_v", C.c_void_p * CSA_MAX_LAYERS),
         ("ring_k_scale", C.c_void_p * CSA_MAX_LAYERS),
@@ -68,8 +70,8 @@ class Buffers(C.Structure):
 
 class BufferSizes(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
-        "kv_pool", "idx_pool", "page_scale", "kv_stage", "idx_stage", "ring", "ring_scale", "block_stage",
-        "block_table")]
+        "kv_pool", "idx_pool", "page_scale", "kv_stage", "idx_stage", "group_scale", "ring", "ring_scale",
+        "block_stage", "block_table")]
 
 
 EXPORTS = [

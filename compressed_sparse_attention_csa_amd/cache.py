@@ -14,7 +14,7 @@ import torch
 
 from . import binding as B
 
-_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "fp4": torch.uint8}
 
 
 @dataclass
@@ -66,17 +66,22 @@ class CsaCache:
         P, S, D, DI, L = spec.pool_pages, spec.max_seqs, B.CSA_HEAD_DIM, B.CSA_IDX_DIM, spec.n_layers
         R = self.cfg.ring_rows
         dev = self.device
-        self.kbar = [torch.zeros((P, 64, D), dtype=kvt, device=dev) for _ in range(L)]
-        self.vbar = [torch.zeros((P, 64, D), dtype=kvt, device=dev) for _ in range(L)]
+        fp8, fp4 = spec.kv_dtype == "fp8", spec.kv_dtype == "fp4"
+        row = D // 2 if fp4 else D           # fp4: two E2M1 codes per byte
+        self.kbar = [torch.zeros((P, 64, row), dtype=kvt, device=dev) for _ in range(L)]
+        self.vbar = [torch.zeros((P, 64, row), dtype=kvt, device=dev) for _ in range(L)]
+        # fp4: one E4M3 scale code per 16 channels of every entry
+        self.kbar_gscale = [torch.zeros((P, 64, D // 16), dtype=torch.uint8, device=dev) for _ in range(L)] if fp4 else []
+        self.vbar_gscale = [torch.zeros((P, 64, D // 16), dtype=torch.uint8, device=dev) for _ in range(L)] if fp4 else []
         idx = spec.idx_heads > 0   # an HCA group (idx_heads = 0) has no indexer keys
+        idx8 = fp8 or fp4          # fp4 main KV keeps fp8 indexer keys
         self.kidx = torch.zeros((P, 64, DI), dtype=kvt, device=dev) if idx else None
-        fp8 = spec.kv_dtype == "fp8"
         self.kbar_scale = [torch.ones(P, dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
         self.vbar_scale = [torch.ones(P, dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
-        self.kidx_scale = torch.ones(P, dtype=torch.float32, device=dev) if fp8 and idx else None
+        self.kidx_scale = torch.ones(P, dtype=torch.float32, device=dev) if idx8 and idx else None
         self.kbar_stage = [torch.zeros((S, 64, D), dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
         self.vbar_stage = [torch.zeros((S, 64, D), dtype=torch.float32, device=dev) for _ in range(L)] if fp8 else []
-        self.kidx_stage = torch.zeros((S, 64, DI), dtype=torch.float32, device=dev) if fp8 and idx else None
+        self.kidx_stage = torch.zeros((S, 64, DI), dtype=torch.float32, device=dev) if idx8 and idx else None
         ring_fp8 = spec.swa_dtype == "fp8"
         ringt = torch.uint8 if ring_fp8 else actt
         self.ring_k = [torch.zeros((S, R, D), dtype=ringt, device=dev) for _ in range(L)]
@@ -107,6 +112,9 @@ class CsaCache:
             if ring_fp8:
                 b.ring_k_scale[l] = self.ring_k_scale[l].data_ptr()
                 b.ring_v_scale[l] = self.ring_v_scale[l].data_ptr()
+            if fp4:
+                b.kbar_gscale[l] = self.kbar_gscale[l].data_ptr()
+                b.vbar_gscale[l] = self.vbar_gscale[l].data_ptr()
             if fp8:
                 b.kbar_scale[l] = self.kbar_scale[l].data_ptr()
                 b.vbar_scale[l] = self.vbar_scale[l].data_ptr()
@@ -114,7 +122,7 @@ class CsaCache:
                 b.vbar_stage[l] = self.vbar_stage[l].data_ptr()
         if idx:
             b.kidx = self.kidx.data_ptr()
-            if fp8:
+            if idx8:
                 b.kidx_scale = self.kidx_scale.data_ptr()
                 b.kidx_stage = self.kidx_stage.data_ptr()
         b.block_table = self.block_table.data_ptr()

@@ -66,11 +66,25 @@ __device__ __forceinline__ float f4_at(const float4 &f, int i) {
   return i == 0 ? f.x : (i == 1 ? f.y : (i == 2 ? f.z : f.w));
 }
 
-// 16 bytes of a row (E = 16 / element size elements) -> compute type.
+// 16 bytes of a row (E = 16 / element size elements) -> compute type. An fp4
+// chunk holds 32 elements, two 16-channel groups whose E4M3 scale codes are
+// bytes 0 and 1 of gsc; E2M1 x E4M3 products are exact in bf16.
 template <int SD, typename CT>
-__device__ __forceinline__ void chunk_values(const uint4 &u, CT *dst) {
+__device__ __forceinline__ void chunk_values(const uint4 &u, CT *dst, uint32_t gsc = 0) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-  if constexpr (SD == DT_F32) {
+  if constexpr (SD == DT_FP4) {
+    const float s0 = e4m3_to_f32(gsc & 0xffu), s1 = e4m3_to_f32((gsc >> 8) & 0xffu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sc = q < 2 ? s0 : s1;
+      const f32x2_t v0 = fp4x2_to_f32<0>(w[q]), v1 = fp4x2_to_f32<1>(w[q]);
+      const f32x2_t v2 = fp4x2_to_f32<2>(w[q]), v3 = fp4x2_to_f32<3>(w[q]);
+      dst[8 * q + 0] = to_ct<CT>(v0[0] * sc); dst[8 * q + 1] = to_ct<CT>(v0[1] * sc);
+      dst[8 * q + 2] = to_ct<CT>(v1[0] * sc); dst[8 * q + 3] = to_ct<CT>(v1[1] * sc);
+      dst[8 * q + 4] = to_ct<CT>(v2[0] * sc); dst[8 * q + 5] = to_ct<CT>(v2[1] * sc);
+      dst[8 * q + 6] = to_ct<CT>(v3[0] * sc); dst[8 * q + 7] = to_ct<CT>(v3[1] * sc);
+    }
+  } else if constexpr (SD == DT_F32) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) dst[q] = to_ct<CT>(__uint_as_float(w[q]));
   } else if constexpr (SD == DT_BF16) {
@@ -92,6 +106,7 @@ __device__ __forceinline__ void chunk_values(const uint4 &u, CT *dst) {
 constexpr int32_t kMaskedRow = INT32_MIN;   // src_row of a key that takes no part
 
 template <int SD> constexpr int elem_bytes_of() { return SD == DT_F32 ? 4 : (SD == DT_BF16 ? 2 : 1); }
+template <int SD> constexpr int row_bytes_of() { return SD == DT_FP4 ? kD / 2 : kD * elem_bytes_of<SD>(); }
 
 // RS: storage type of the window ring (ACT, or E4M3 with one scale per row);
 // HG: head groups (waves); NTW: 16-head tiles per wave.
@@ -100,14 +115,15 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   using CT = typename ComputeT<KV>::type;
   constexpr int NT = HG * 64;
   constexpr int H = HG * NTW * 16;
-  constexpr int KE = elem_bytes_of<KV>(), AE = elem_bytes_of<ACT>(), RE = elem_bytes_of<RS>();
+  constexpr int AE = elem_bytes_of<ACT>();
+  constexpr int64_t PRB = row_bytes_of<KV>(), RRB = row_bytes_of<RS>();   // pool / ring row bytes
   constexpr int KS = kD + kpad<CT>();          // K row stride (elements)
   // bf16: V row-major like K, read as transposed MFMA fragments; fp32: V^T
   constexpr bool VROW = sizeof(CT) == 2;
   constexpr int VS = VROW ? KS : kKeyBlock + kpad<CT>();   // V (or V^T) row stride (elements)
   // a block's K and V rows move as 16-byte chunks, 16 consecutive lanes per
   // 256-byte row, so every wave load covers whole rows
-  constexpr int CPR_P = kD * KE / 16, CPR_R = kD * RE / 16;   // chunks per pool / ring row
+  constexpr int CPR_P = row_bytes_of<KV>() / 16, CPR_R = row_bytes_of<RS>() / 16;   // chunks per pool / ring row
   constexpr int CPR_MAX = CPR_P > CPR_R ? CPR_P : CPR_R;
   static_assert((CPR_P & (CPR_P - 1)) == 0 && (CPR_R & (CPR_R - 1)) == 0, "chunks per row are powers of two");
   constexpr int U = 2 * kKeyBlock * CPR_MAX / NT;              // chunk slots per thread per block
@@ -194,6 +210,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   // A masked slot's register is never written (a zero written beside an
   // in-flight load would have to wait for it); vmask says which slots hold data.
   uint4 raw[PREFETCH ? U : 1];
+  uint32_t graw[KV == DT_FP4 && PREFETCH ? U : 1];   // fp4: the chunk's two group-scale codes
   uint32_t vmask = 0;
   float ks_pref = 1.f, vs_pref = 1.f;   // page scales of key tid (tid < 64)
   // slot s of a block with cpr (a power of two) chunks per row: (K or V, key, chunk)
@@ -204,6 +221,12 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     const int kv = s >= kKeyBlock * cpr;
     const int64_t r = row >= 0 ? row : -static_cast<int64_t>(row) - 1;
     return reinterpret_cast<const uint4 *>((kv ? vbase : kbase) + r * row_bytes) + (s & (cpr - 1));
+  };
+  // fp4 pool slot s of row `row`: its chunk's two group-scale codes (16-bit load)
+  auto slot_gscale = [&](int s, int32_t row) -> uint32_t {
+    const int kv = s >= kKeyBlock * CPR_P;
+    const uint8_t *g = (kv ? a.vbar_gs : a.kbar_gs) + static_cast<int64_t>(row) * (kD / kFp4Group);
+    return *reinterpret_cast<const uint16_t *>(g + 2 * (s & (CPR_P - 1)));
   };
   auto load_scales = [&](int b) {
     ks_pref = vs_pref = 1.f;
@@ -226,16 +249,16 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   };
   // chunk -> compute type -> K row-major or V^T in LDS; SD is the storage type
   // of the block's rows (pool or ring), so the element count is a constant
-  auto commit_chunk = [&](auto sd_tag, int s, const uint4 &u) {
+  auto commit_chunk = [&](auto sd_tag, int s, const uint4 &u, uint32_t gsc) {
     constexpr int SD = decltype(sd_tag)::value;
-    constexpr int E = 16 / elem_bytes_of<SD>();
+    constexpr int E = SD == DT_FP4 ? 32 : 16 / elem_bytes_of<SD>();
     constexpr int CPR = kD / E;
     if (s >= 2 * kKeyBlock * CPR) return;
     const int kv = s >= kKeyBlock * CPR;
     const int L = s - kv * kKeyBlock * CPR;
     const int key = L / CPR, d0 = (L % CPR) * E;
     CT vals[E];
-    chunk_values<SD, CT>(u, vals);
+    chunk_values<SD, CT>(u, vals, gsc);
     if (kv == 0) {
       CT *kd = Ks + key * KS + d0;
 #pragma unroll
@@ -250,12 +273,12 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       for (int q = 0; q < E; ++q) vd[q * VS] = vals[q];
     }
   };
-  auto commit_slot = [&](int b, int s, const uint4 &u) {
+  auto commit_slot = [&](int b, int s, const uint4 &u, uint32_t gsc) {
     if constexpr (KV == RS) {
-      commit_chunk(std::integral_constant<int, KV>{}, s, u);
+      commit_chunk(std::integral_constant<int, KV>{}, s, u, gsc);
     } else {
-      if (b < a.n_sparse_blocks) commit_chunk(std::integral_constant<int, KV>{}, s, u);
-      else commit_chunk(std::integral_constant<int, RS>{}, s, u);
+      if (b < a.n_sparse_blocks) commit_chunk(std::integral_constant<int, KV>{}, s, u, gsc);
+      else commit_chunk(std::integral_constant<int, RS>{}, s, u, gsc);
     }
   };
   auto load_round = [&](int r) {
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
         const int nslot = 2 * kKeyBlock * cpr;
         const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
         const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
-        const int64_t row_bytes = pool ? kD * KE : kD * RE;
+        const int64_t row_bytes = pool ? PRB : RRB;
         // every slot's row first (one LDS round trip), then every load
         int32_t rows[U];
 #pragma unroll
@@ -280,6 +303,9 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
         for (int u = 0; u < U; ++u) {
           if (rows[u] != kMaskedRow) {
             raw[u] = *slot_ptr(kbase, vbase, row_bytes, tid + u * NT, cpr, rows[u]);
+            if constexpr (KV == DT_FP4) {
+              if (pool) graw[u] = slot_gscale(tid + u * NT, rows[u]);
+            }
             vmask |= 1u << u;
           }
         }
@@ -291,18 +317,25 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     const int b = b_begin + r;
     if constexpr (PREFETCH) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) commit_slot(b, tid + u * NT, ((vmask >> u) & 1u) ? raw[u] : make_uint4(0, 0, 0, 0));
+      for (int u = 0; u < U; ++u) {
+        const bool on = (vmask >> u) & 1u;
+        uint32_t gsc = 0;
+        if constexpr (KV == DT_FP4) gsc = on ? graw[u] : 0u;
+        commit_slot(b, tid + u * NT, on ? raw[u] : make_uint4(0, 0, 0, 0), gsc);
+      }
     } else {
       const bool pool = b < a.n_sparse_blocks;
       const int cpr = pool ? CPR_P : CPR_R;
       const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
       const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
-      const int64_t row_bytes = pool ? kD * KE : kD * RE;
+      const int64_t row_bytes = pool ? PRB : RRB;
       for (int u = 0; u < U; ++u) {
         const int s = tid + u * NT;
         if (s >= 2 * kKeyBlock * cpr) break;
         const int32_t row = src_row[(b - b_begin) * kKeyBlock + slot_key(s, cpr)];
-        commit_slot(b, s, row != kMaskedRow ? *slot_ptr(kbase, vbase, row_bytes, s, cpr, row) : make_uint4(0, 0, 0, 0));
+        uint32_t gsc = 0;
+        if constexpr (KV == DT_FP4) gsc = (pool && row != kMaskedRow) ? slot_gscale(s, row) : 0u;
+        commit_slot(b, s, row != kMaskedRow ? *slot_ptr(kbase, vbase, row_bytes, s, cpr, row) : make_uint4(0, 0, 0, 0), gsc);
       }
     }
     if (tid < kKeyBlock) {
@@ -541,6 +574,8 @@ void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, bool ring_fp8
   else if (kv == DT_BF16 && act == DT_BF16) launch_attend_t<DT_BF16, DT_BF16, DT_FP8>(a, n_wg, s, ev0, ev1);
   else if (kv == DT_FP8 && act == DT_BF16 && !ring_fp8) launch_attend_t<DT_BF16, DT_FP8, DT_BF16>(a, n_wg, s, ev0, ev1);
   else if (kv == DT_FP8 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP8, DT_FP8>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP4 && act == DT_BF16 && !ring_fp8) launch_attend_t<DT_BF16, DT_FP4, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP4 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP4, DT_FP8>(a, n_wg, s, ev0, ev1);
   if (a.n_splits > 1) {
     if (act == DT_F32) hipLaunchKernelGGL(attend_merge_kernel<DT_F32>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);
     else hipLaunchKernelGGL(attend_merge_kernel<DT_BF16>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
 #pragma unroll
       for (int m = 0; m < kSlotsPerThread; ++m) ki[m] += kb_s[eb + 4 * m][d] * p;
     }
-    if constexpr (KV == DT_FP8) {
+    if constexpr (KV == DT_FP8 || KV == DT_FP4) {   // fp8 indexer keys
 #pragma unroll
       for (int m = 0; m < kSlotsPerThread; ++m) {
         const int slot = eb + 4 * m, e = pstart + slot;
@@ -165,7 +165,61 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   const int64_t kv_page = static_cast<int64_t>(pp) * kPage * kD;
   const int64_t ki_page = static_cast<int64_t>(pp) * kPage * kDI;
 
-  if constexpr (KV != DT_FP8) {
+  if constexpr (KV == DT_FP4) {
+    // ---- FP4 K/V: every entry on its own, one E4M3 scale amax/6 per 16
+    // channels (8 lanes of a wave); only the new entries are written
+    uint8_t *kp = reinterpret_cast<uint8_t *>(a.kbar) + static_cast<int64_t>(pp) * kPage * (kD / 2);
+    uint8_t *vp = reinterpret_cast<uint8_t *>(a.vbar) + static_cast<int64_t>(pp) * kPage * (kD / 2);
+    uint8_t *kg = a.kbar_gs + static_cast<int64_t>(pp) * kPage * (kD / kFp4Group);
+    uint8_t *vg = a.vbar_gs + static_cast<int64_t>(pp) * kPage * (kD / kFp4Group);
+#pragma unroll
+    for (int m = 0; m < kSlotsPerThread; ++m) {
+      const int slot = eb + 4 * m, e = pstart + slot;
+      float mk = fmaxf(fabsf(kk[m][0]), fabsf(kk[m][1]));
+      float mv = fmaxf(fabsf(vv[m][0]), fabsf(vv[m][1]));
+#pragma unroll
+      for (int o = 1; o < kFp4Group / 2; o <<= 1) {
+        mk = fmaxf(mk, __shfl_xor(mk, o, 64));
+        mv = fmaxf(mv, __shfl_xor(mv, o, 64));
+      }
+      const uint32_t gk = f32_to_e4m3(mk / 6.0f), gv = f32_to_e4m3(mv / 6.0f);
+      const float sk = e4m3_to_f32(gk), sv = e4m3_to_f32(gv);
+      const uint32_t ck = sk > 0.f ? f32_to_e2m1(kk[m][0] / sk) | (f32_to_e2m1(kk[m][1] / sk) << 4) : 0u;
+      const uint32_t cv = sv > 0.f ? f32_to_e2m1(vv[m][0] / sv) | (f32_to_e2m1(vv[m][1] / sv) << 4) : 0u;
+      if (page_ok && e >= e0 && e < e1) {
+        kp[slot * (kD / 2) + dp] = static_cast<uint8_t>(ck);
+        vp[slot * (kD / 2) + dp] = static_cast<uint8_t>(cv);
+        if ((dp & (kFp4Group / 2 - 1)) == 0) {
+          kg[slot * (kD / kFp4Group) + dp / (kFp4Group / 2)] = static_cast<uint8_t>(gk);
+          vg[slot * (kD / kFp4Group) + dp / (kFp4Group / 2)] = static_cast<uint8_t>(gv);
+        }
+      }
+    }
+    if (!a.write_idx) return;
+    // ---- FP8 indexer keys: one scale per page, amax over the filled slots
+    float ai = 0.f;
+#pragma unroll
+    for (int m = 0; m < kSlotsPerThread; ++m)
+      if (eb + 4 * m < filled) ai = fmaxf(ai, fabsf(ki[m]));
+    ai = block_max(ai, red + 8);
+    const float si = ai > 0.f ? ai / 448.0f : 1.0f;
+    if (page_ok) {
+      uint8_t *ip = reinterpret_cast<uint8_t *>(a.kidx) + ki_page;
+#pragma unroll
+      for (int m = 0; m < kSlotsPerThread; ++m) {
+        const int slot = eb + 4 * m;
+        if (slot < filled) ip[slot * kDI + c] = static_cast<uint8_t>(f32_to_e4m3(ki[m] / si));
+      }
+      if (threadIdx.x == 0) a.kidx_scale[pp] = si;
+    }
+    if (filled < kPage) {
+#pragma unroll
+      for (int m = 0; m < kSlotsPerThread; ++m) {
+        const int slot = eb + 4 * m, e = pstart + slot;
+        if (e >= e0 && e < e1) a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot) * kDI + c] = ki[m];
+      }
+    }
+  } else if constexpr (KV != DT_FP8) {
     if (!page_ok) return;
 #pragma unroll
     for (int m = 0; m < kSlotsPerThread; ++m) {
@@ -324,6 +378,8 @@ void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hip
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_BF16>), dim3(n_wg), dim3(kThreads), 0, s, a);
   else if (kv == DT_FP8 && act == DT_BF16)
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(kThreads), 0, s, a);
+  else if (kv == DT_FP4 && act == DT_BF16)
+    hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP4>), dim3(n_wg), dim3(kThreads), 0, s, a);
 }
 
 void launch_compress_ring(const RingArgs &a, int n_wg, int act, bool ring_fp8, hipStream_t s) {

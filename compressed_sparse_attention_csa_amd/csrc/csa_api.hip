@@ -49,6 +49,14 @@ bool handle_ok(csa_cache_t h) { return h != nullptr && h->magic == kMagic; }
 
 int dt_bytes(int dt) { return dt == CSA_F32 ? 4 : (dt == CSA_BF16 ? 2 : 1); }
 
+// Kernel dtypes of the compressed K/V and of the indexer keys (fp8 when K/V are fp4).
+int main_dt(const csa_config &c) {
+  return c.kv_dtype == CSA_F32 ? DT_F32 : c.kv_dtype == CSA_BF16 ? DT_BF16 : c.kv_dtype == CSA_FP8_E4M3 ? DT_FP8 : DT_FP4;
+}
+int idx_dt(const csa_config &c) {
+  return c.kv_dtype == CSA_F32 ? DT_F32 : c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8;
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 csa_status check_config(const csa_config *c) {
@@ -74,7 +82,8 @@ csa_status check_config(const csa_config *c) {
     return fail(CSA_ERR_UNSUPPORTED, "max_pages_per_seq * 64 * ratio exceeds 2^30 raw rows");
   const bool ok = (c->kv_dtype == CSA_F32 && c->act_dtype == CSA_F32) ||
                   (c->kv_dtype == CSA_BF16 && c->act_dtype == CSA_BF16) ||
-                  (c->kv_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16);
+                  (c->kv_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16) ||
+                  (c->kv_dtype == CSA_FP4_E2M1 && c->act_dtype == CSA_BF16);
   if (!ok) return fail(CSA_ERR_DTYPE, "unsupported (kv_dtype, act_dtype) = (%d, %d)", c->kv_dtype, c->act_dtype);
   if (c->swa_dtype != c->act_dtype && !(c->swa_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16))
     return fail(CSA_ERR_DTYPE, "swa_dtype %d must be act_dtype, or FP8_E4M3 with BF16 activations", c->swa_dtype);
@@ -172,8 +181,22 @@ __global__ void debug_convert_kernel(int kind, const void *in, void *out, int64_
     reinterpret_cast<uint16_t *>(out)[i] = __builtin_bit_cast(uint16_t, fp8x2_to_bf16<false>(c)[0]);
   } else if (kind == 2) {
     reinterpret_cast<uint8_t *>(out)[i] = static_cast<uint8_t>(f32_to_e4m3(reinterpret_cast<const float *>(in)[i]));
-  } else {
+  } else if (kind == 3) {
     reinterpret_cast<uint16_t *>(out)[i] = f32_to_bf16(reinterpret_cast<const float *>(in)[i]);
+  } else if (kind == 4) {
+    // byte i of the input sits at byte i % 4 of its 32-bit word, as in a packed row
+    const uint32_t w = reinterpret_cast<const uint32_t *>(in)[i >> 2];
+    f32x2_t v;
+    switch (i & 3) {
+      case 0: v = fp4x2_to_f32<0>(w); break;
+      case 1: v = fp4x2_to_f32<1>(w); break;
+      case 2: v = fp4x2_to_f32<2>(w); break;
+      default: v = fp4x2_to_f32<3>(w); break;
+    }
+    reinterpret_cast<float *>(out)[2 * i] = v[0];
+    reinterpret_cast<float *>(out)[2 * i + 1] = v[1];
+  } else {
+    reinterpret_cast<uint8_t *>(out)[i] = static_cast<uint8_t>(f32_to_e2m1(reinterpret_cast<const float *>(in)[i]));
   }
 }
 
@@ -201,14 +224,15 @@ csa_status csa_buffer_sizes_for(const csa_config *cfg, csa_buffer_sizes *out) {
   if (st != CSA_OK) return st;
   if (!out) return fail(CSA_ERR_INVALID_ARG, "out is NULL");
   const size_t P = cfg->pool_pages, S = cfg->max_seqs;
-  const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3;
+  const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3, fp4 = cfg->kv_dtype == CSA_FP4_E2M1;
   const int kb = dt_bytes(cfg->kv_dtype), ab = dt_bytes(cfg->act_dtype);
-  out->kv_pool = P * kPage * kD * kb;
+  out->kv_pool = fp4 ? P * kPage * kD / 2 : P * kPage * kD * kb;
   const bool idx = cfg->idx_heads > 0;
   out->idx_pool = idx ? P * kPage * kDI * kb : 0;
-  out->page_scale = fp8 ? P * 4 : 0;
+  out->page_scale = fp8 || fp4 ? P * 4 : 0;
   out->kv_stage = fp8 ? S * kPage * kD * 4 : 0;
-  out->idx_stage = fp8 && idx ? S * kPage * kDI * 4 : 0;
+  out->idx_stage = (fp8 || fp4) && idx ? S * kPage * kDI * 4 : 0;
+  out->group_scale = fp4 ? P * kPage * (kD / kFp4Group) : 0;
   const bool ring8 = cfg->swa_dtype == CSA_FP8_E4M3;
   out->ring = S * static_cast<size_t>(cfg->ring_rows) * kD * (ring8 ? 1 : ab);
   out->ring_scale = ring8 ? S * static_cast<size_t>(cfg->ring_rows) * 4 : 0;
@@ -234,7 +258,7 @@ csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_
   csa_status st = check_config(cfg);
   if (st != CSA_OK) return st;
   if (!bufs || !out) return fail(CSA_ERR_INVALID_ARG, "buffers or out is NULL");
-  const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3;
+  const bool fp8 = cfg->kv_dtype == CSA_FP8_E4M3, fp4 = cfg->kv_dtype == CSA_FP4_E2M1;
   for (int l = 0; l < cfg->n_layers; ++l) {
     if (!bufs->kbar[l] || !bufs->vbar[l] || !bufs->ring_k[l] || !bufs->ring_v[l] || !bufs->block_stage[l])
       return fail(CSA_ERR_INVALID_ARG, "layer %d: kbar, vbar, ring_k, ring_v and block_stage are required", l);
@@ -242,12 +266,14 @@ csa_status csa_cache_create(const csa_config *cfg, const csa_buffers *bufs, csa_
       return fail(CSA_ERR_INVALID_ARG, "layer %d: an fp8 window ring needs ring_k_scale and ring_v_scale", l);
     if (fp8 && (!bufs->kbar_scale[l] || !bufs->vbar_scale[l] || !bufs->kbar_stage[l] || !bufs->vbar_stage[l]))
       return fail(CSA_ERR_INVALID_ARG, "layer %d: fp8 caches need scale and staging buffers", l);
+    if (fp4 && (!bufs->kbar_gscale[l] || !bufs->vbar_gscale[l]))
+      return fail(CSA_ERR_INVALID_ARG, "layer %d: fp4 caches need kbar_gscale and vbar_gscale", l);
   }
   if (!bufs->block_table || !bufs->workspace)
     return fail(CSA_ERR_INVALID_ARG, "block_table and workspace are required");
   if (cfg->idx_heads > 0 && !bufs->kidx) return fail(CSA_ERR_INVALID_ARG, "kidx is required when idx_heads > 0");
-  if (cfg->idx_heads > 0 && fp8 && (!bufs->kidx_scale || !bufs->kidx_stage))
-    return fail(CSA_ERR_INVALID_ARG, "fp8 caches need kidx_scale and kidx_stage");
+  if (cfg->idx_heads > 0 && (fp8 || fp4) && (!bufs->kidx_scale || !bufs->kidx_stage))
+    return fail(CSA_ERR_INVALID_ARG, "fp8 and fp4 caches need kidx_scale and kidx_stage");
   if (reinterpret_cast<uintptr_t>(bufs->workspace) % 256 != 0) return fail(CSA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (bufs->workspace_bytes < kHead + 1024) return fail(CSA_ERR_CAPACITY, "workspace too small");
   csa_cache *h = new (std::nothrow) csa_cache();
@@ -331,14 +357,16 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
   if (total == 0) return CSA_OK;
   if (total > (1ll << 31) / kD) return fail(CSA_ERR_UNSUPPORTED, "too many rows in one call");
 
-  const bool fp8 = c.kv_dtype == CSA_FP8_E4M3;
-  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  // pages whose earlier entries are re-quantised from staging: fp8 K/V, or the fp8 indexer keys of fp4
+  const bool fp8 = c.kv_dtype == CSA_FP8_E4M3 || (c.kv_dtype == CSA_FP4_E2M1 && proj_idx != nullptr);
+  const int kv = main_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   CompressArgs base{};
   base.raw_k = raw_k; base.raw_v = raw_v; base.gate = gate;
   base.block_stage = h->buf.block_stage[layer];
   base.proj = proj_idx;
   base.kbar = h->buf.kbar[layer]; base.vbar = h->buf.vbar[layer]; base.kidx = h->buf.kidx;
+  base.kbar_gs = h->buf.kbar_gscale[layer]; base.vbar_gs = h->buf.vbar_gscale[layer];
   base.kbar_scale = h->buf.kbar_scale[layer]; base.vbar_scale = h->buf.vbar_scale[layer]; base.kidx_scale = h->buf.kidx_scale;
   base.kbar_stage = h->buf.kbar_stage[layer]; base.vbar_stage = h->buf.vbar_stage[layer]; base.kidx_stage = h->buf.kidx_stage;
   base.block_table = h->buf.block_table;
@@ -524,7 +552,7 @@ DecodeScratch carve_decode(csa_cache_t h, int nq, int64_t s_stride) {
 csa_status index_chunk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
                        const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
   const csa_config &c = h->cfg;
-  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int kv = idx_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   const int pos0 = q_pos[0];
   const int n_max = (pos0 + n_q) / c.ratio;
@@ -561,7 +589,7 @@ csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, con
                            const float *w_idx, int32_t k, int32_t *topk, int32_t n_pool, int32_t *pool,
                            hipStream_t stream) {
   const csa_config &c = h->cfg;
-  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int kv = idx_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   const int ab = dt_bytes(c.act_dtype);
   for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
@@ -672,7 +700,7 @@ csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, c
     return fail(CSA_ERR_UNSUPPORTED, "n_pool_blocks = %d outside [1, %d]", n_pool_blocks, CSA_MAX_POOL_BLOCKS);
   if (!pool) return fail(CSA_ERR_INVALID_ARG, "pool is required");
   const csa_config &c = h->cfg;
-  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int kv = idx_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   const int ab = dt_bytes(c.act_dtype);
   for (int g0 = 0; g0 < n_q; g0 += kIdxMaxQ) {
@@ -764,12 +792,13 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       return fail(CSA_ERR_UNSUPPORTED, "dense attention over %d entries exceeds %d", k,
                   kMaxSplits * kAttMaxSplitKeys - (c.window + kKeyBlock - 1) / kKeyBlock * kKeyBlock);
   }
-  const int kv = c.kv_dtype == CSA_F32 ? DT_F32 : (c.kv_dtype == CSA_BF16 ? DT_BF16 : DT_FP8);
+  const int kv = main_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   const int ab = dt_bytes(c.act_dtype);
   AttendArgs a{};
   a.kbar = h->buf.kbar[layer]; a.vbar = h->buf.vbar[layer];
   a.kbar_scale = h->buf.kbar_scale[layer]; a.vbar_scale = h->buf.vbar_scale[layer];
+  a.kbar_gs = h->buf.kbar_gscale[layer]; a.vbar_gs = h->buf.vbar_gscale[layer];
   a.ring_k = h->buf.ring_k[layer]; a.ring_v = h->buf.ring_v[layer];
   a.ring_k_scale = h->buf.ring_k_scale[layer]; a.ring_v_scale = h->buf.ring_v_scale[layer];
   const bool ring8 = c.swa_dtype == CSA_FP8_E4M3;
@@ -871,7 +900,8 @@ csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int3
 }
 
 csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream) {
-  if (kind < 0 || kind > 3 || !in || !out || n < 0) return fail(CSA_ERR_INVALID_ARG, "bad debug conversion arguments");
+  if (kind < 0 || kind > 5 || !in || !out || n < 0) return fail(CSA_ERR_INVALID_ARG, "bad debug conversion arguments");
+  if (kind == 4 && n % 4 != 0) return fail(CSA_ERR_INVALID_ARG, "kind 4 takes whole 32-bit words (n % 4 == 0)");
   if (n == 0) return CSA_OK;
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(debug_convert_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, kind, in, out, n);

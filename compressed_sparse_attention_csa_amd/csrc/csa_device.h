@@ -23,7 +23,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_FP4 = 3 };
+
+constexpr int kFp4Group = 16;   // channels sharing one E4M3 scale in an fp4 entry
 
 // error-word bits (see csa_read_errors)
 enum : uint32_t { ERR_PAGE = 1u, ERR_TOPK = 2u, ERR_FALLBACK = 4u };
@@ -79,6 +81,38 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   uint32_t mant = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));     // 8..16
   if (mant == 16u) { mant = 8u; ++e; }
   return sign | (static_cast<uint32_t>(e + 7) << 3) | (mant - 8u);
+}
+
+// One E4M3 code (low byte) -> fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  return fp8x2_to_f32<false>(code)[0];
+}
+
+// ------------------------------------------------------------------ fp4 e2m1
+
+// fp32 -> E2M1 code (bits 0-2 magnitude index of 0, .5, 1, 1.5, 2, 3, 4, 6;
+// bit 3 the input's sign): nearest magnitude, a tie going to the even code,
+// saturating at 6 (NaN saturates too).
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  const float a = fabsf(x);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return sign | c;
+}
+
+// Two E2M1 codes (byte `SEL` of w: low nibble first) -> two fp32 values, exact
+// (gfx950's fp4 conversion with a unit scale).
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(static_cast<int>(w), 1.0f, SEL);
 }
 
 // ------------------------------------------------------------------ fragments

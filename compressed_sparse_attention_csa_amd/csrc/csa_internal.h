@@ -24,6 +24,7 @@ struct CompressArgs {
   const void *block_stage;                        // open-block gate/K/V rows [max_seqs][3][r][D]
   const float *proj;                              // [D][D_I] or null
   void *kbar, *vbar, *kidx;                       // pools
+  uint8_t *kbar_gs, *vbar_gs;                     // fp4 group scales [pool_pages][64][D/16]
   float *kbar_scale, *vbar_scale, *kidx_scale;    // fp8 page scales
   float *kbar_stage, *vbar_stage, *kidx_stage;    // fp8 open-page staging
   const int32_t *block_table;
@@ -170,6 +171,7 @@ struct AttendArgs {
   const int32_t *topk;      // [n_q][k]
   const void *kbar, *vbar;
   const float *kbar_scale, *vbar_scale;
+  const uint8_t *kbar_gs, *vbar_gs;         // fp4 group scales [pool_pages][64][D/16]
   const void *ring_k, *ring_v;
   const float *ring_k_scale, *ring_v_scale;   // per-row scales of an fp8 ring
   const int32_t *block_table;

@@ -64,10 +64,16 @@ typedef enum {
   CSA_ERR_HIP = 6          /* a HIP runtime call failed */
 } csa_status;
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_FP4_E2M1 = 3 } csa_dtype;
 
 /* Static shape of a layer group's cache.
- * Supported (kv_dtype, act_dtype): (F32, F32), (BF16, BF16), (FP8_E4M3, BF16). */
+ * Supported (kv_dtype, act_dtype): (F32, F32), (BF16, BF16), (FP8_E4M3, BF16),
+ * (FP4_E2M1, BF16).
+ * FP4_E2M1 ([Walkthrough] "FP4 main KV cache": E2M1 elements, one E4M3 scale
+ * per 16 channels, no second-level scale) applies to the compressed K/V only:
+ * element pairs pack into bytes (channel 2i in the low nibble), each entry's 8
+ * group scales are E4M3 codes of amax/6 (round to nearest; a zero scale stores
+ * zero elements), and the indexer keys stay FP8_E4M3 with page scales. */
 typedef struct csa_config {
   int32_t ratio;             /* r in [1, 256]: raw rows per compressed entry (1 keeps main KV uncompressed) */
   int32_t head_dim;          /* D, must be CSA_HEAD_DIM */
@@ -82,7 +88,7 @@ typedef struct csa_config {
   int32_t max_seqs;          /* sequences addressable through the block table */
   int32_t max_pages_per_seq; /* block-table row length */
   int32_t pool_pages;        /* physical pages in every pool */
-  int32_t kv_dtype;          /* csa_dtype of compressed entries and indexer keys */
+  int32_t kv_dtype;          /* csa_dtype of compressed entries and indexer keys (FP4_E2M1: see above) */
   int32_t act_dtype;         /* csa_dtype of raw rows, queries and outputs (F32 or BF16) */
   int32_t swa_dtype;         /* csa_dtype of the window ring: act_dtype, or CSA_FP8_E4M3 with
                                 BF16 activations (E4M3 codes, one fp32 scale amax/448 per row) */
@@ -92,24 +98,29 @@ typedef struct csa_config {
  * Pools are indexed by physical page: entry j of sequence b lives at slot
  * j % 64 of physical page block_table[b * max_pages_per_seq + j / 64].
  * Per-layer arrays use entries [0, n_layers); unused entries may be NULL.
- * Page scale and page staging arrays are used only when kv_dtype == CSA_FP8_E4M3,
- * ring scales only when swa_dtype == CSA_FP8_E4M3 (else NULL). */
+ * Page scale and page staging arrays of K/V are used only when kv_dtype ==
+ * CSA_FP8_E4M3, those of the indexer keys with FP8_E4M3 or FP4_E2M1, group
+ * scales only with FP4_E2M1, ring scales only when swa_dtype == CSA_FP8_E4M3
+ * (else NULL). */
 typedef struct csa_buffers {
-  void *kbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed keys */
+  void *kbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed keys ([..][D/2] bytes for fp4) */
   void *vbar[CSA_MAX_LAYERS];        /* [pool_pages][64][D] kv_dtype: compressed values */
   float *kbar_scale[CSA_MAX_LAYERS]; /* [pool_pages] fp32 page scale (fp8) */
   float *vbar_scale[CSA_MAX_LAYERS];
   float *kbar_stage[CSA_MAX_LAYERS]; /* [max_seqs][64][D] fp32 values of each sequence's open page (fp8) */
   float *vbar_stage[CSA_MAX_LAYERS];
+  uint8_t *kbar_gscale[CSA_MAX_LAYERS]; /* [pool_pages][64][D/16] E4M3 group scales (fp4) */
+  uint8_t *vbar_gscale[CSA_MAX_LAYERS];
   void *ring_k[CSA_MAX_LAYERS];      /* [max_seqs][R][D] swa_dtype: last R raw keys (row i at slot i % R) */
   void *ring_v[CSA_MAX_LAYERS];      /* [max_seqs][R][D] swa_dtype: last R raw values */
   float *ring_k_scale[CSA_MAX_LAYERS]; /* [max_seqs][R] fp32 row scales (fp8 ring) */
   float *ring_v_scale[CSA_MAX_LAYERS];
   void *block_stage[CSA_MAX_LAYERS]; /* [max_seqs][3][r][D] act_dtype: gate logits, raw keys and raw
                                         values of each sequence's open (incomplete) r-block */
-  void *kidx;                        /* [pool_pages][64][D_I] kv_dtype: indexer keys (layer 0); NULL if idx_heads == 0 */
-  float *kidx_scale;                 /* [pool_pages] fp32 (fp8; NULL if idx_heads == 0) */
-  float *kidx_stage;                 /* [max_seqs][64][D_I] fp32 (fp8; NULL if idx_heads == 0) */
+  void *kidx;                        /* [pool_pages][64][D_I] indexer keys (layer 0), kv_dtype (fp8 when
+                                        kv_dtype is fp4); NULL if idx_heads == 0 */
+  float *kidx_scale;                 /* [pool_pages] fp32 (fp8/fp4; NULL if idx_heads == 0) */
+  float *kidx_stage;                 /* [max_seqs][64][D_I] fp32 (fp8/fp4; NULL if idx_heads == 0) */
   const int32_t *block_table;        /* [max_seqs][max_pages_per_seq] physical page ids */
   void *workspace;                   /* scratch, >= csa_workspace_size() bytes, 256-byte aligned,
                                         zero-filled before csa_cache_create */
@@ -120,9 +131,10 @@ typedef struct csa_buffers {
 typedef struct csa_buffer_sizes {
   size_t kv_pool;      /* each kbar[l] / vbar[l] */
   size_t idx_pool;     /* kidx */
-  size_t page_scale;   /* each *_scale (0 unless fp8) */
+  size_t page_scale;   /* each *_scale (0 unless fp8 or fp4) */
   size_t kv_stage;     /* each kbar_stage[l] / vbar_stage[l] (0 unless fp8) */
-  size_t idx_stage;    /* kidx_stage (0 unless fp8) */
+  size_t idx_stage;    /* kidx_stage (0 unless fp8 or fp4) */
+  size_t group_scale;  /* each kbar_gscale[l] / vbar_gscale[l] (0 unless fp4) */
   size_t ring;         /* each ring_k[l] / ring_v[l] */
   size_t ring_scale;   /* each ring_k_scale[l] / ring_v_scale[l] (0 unless the ring is fp8) */
   size_t block_stage;  /* each block_stage[l] */
@@ -347,7 +359,11 @@ csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int3
  * kind 0: fp8 e4m3 codes (uint8) -> fp32 as the attention/indexer kernels decode them;
  * kind 1: fp8 e4m3 codes (uint8) -> bf16 bits (uint16) as the MFMA operands are built;
  * kind 2: fp32 -> fp8 e4m3 codes (uint8) as the compressor encodes (RNE, saturating);
- * kind 3: fp32 -> bf16 bits (RNE). in/out are device pointers. */
+ * kind 3: fp32 -> bf16 bits (RNE);
+ * kind 4: fp4 byte pairs (uint8, n a multiple of 4) -> 2n fp32 (low nibble first) as the
+ *         attention kernel decodes packed E2M1 rows;
+ * kind 5: fp32 -> E2M1 codes (uint8, low 4 bits) as the compressor encodes.
+ * in/out are device pointers. */
 csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -44,8 +44,24 @@ def raw_rows(seed, kind, layer, seq, row0, n, act, device="cpu"):
 
 # --------------------------------------------------------------------------- writing oracle contents
 
+def pack_fp4(codes: np.ndarray) -> np.ndarray:
+    """E2M1 codes [E, D] -> bytes [E, D/2], channel 2i in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8) & 0xF
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
 def store_raw_to_torch(raw, dtype: str):
     """Oracle cache payload -> torch tensor of the pool's element type (CPU)."""
+    if dtype == "fp4":
+        return torch.from_numpy(np.ascontiguousarray(pack_fp4(raw[0])))
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(raw))
     if dtype == "bf16":
@@ -77,7 +93,7 @@ def write_scales(cache: CsaCache, scales_t: torch.Tensor, seq: int, scales: np.n
 def fill_index_keys(cache: CsaCache, seed: int, seq: int, n_entries: int):
     """Seeded indexer keys for `seq`, stored through the oracle's codec. Returns decoded float64 values."""
     x = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_KI, 0, seq), 0, n_entries, 64).double().numpy()
-    dt = cache.spec.kv_dtype
+    dt = "fp8" if cache.spec.kv_dtype == "fp4" else cache.spec.kv_dtype   # fp4 caches keep fp8 indexer keys
     vals, raw = O.store(x, dt)
     write_logical(cache, cache.kidx, seq, store_raw_to_torch(raw, dt))
     if dt == "fp8":
@@ -89,12 +105,15 @@ def fill_main_kv(cache: CsaCache, seed: int, layer: int, seq: int, n_entries: in
     """Seeded compressed K/V for (layer, seq) stored through the oracle's codec."""
     dt = cache.spec.kv_dtype
     out = []
-    for kind, pool, scales in ((Sy.KIND_KBAR, cache.kbar[layer], cache.kbar_scale), (Sy.KIND_VBAR, cache.vbar[layer], cache.vbar_scale)):
+    for kind, pool, scales, gsc in ((Sy.KIND_KBAR, cache.kbar[layer], cache.kbar_scale, cache.kbar_gscale),
+                                    (Sy.KIND_VBAR, cache.vbar[layer], cache.vbar_scale, cache.vbar_gscale)):
         x = Sy.normal_rows(seed, Sy.stream_id(kind, layer, seq), 0, n_entries, 128).double().numpy()
         vals, raw = O.store(x, dt)
         write_logical(cache, pool, seq, store_raw_to_torch(raw, dt))
         if dt == "fp8":
             write_scales(cache, scales[layer], seq, raw[1])
+        if dt == "fp4":
+            write_logical(cache, gsc[layer], seq, torch.from_numpy(np.ascontiguousarray(raw[1])))
         out.append(vals)
     return out
 

@@ -49,7 +49,7 @@ def _fake_handle(cfg, n_layers=None):
     fake = 0x10000
     for l in range(n):
         for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "block_stage",
-                  "ring_k_scale", "ring_v_scale"):
+                  "ring_k_scale", "ring_v_scale", "kbar_gscale", "vbar_gscale"):
             getattr(b, f)[l] = fake
     b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = fake
     b.workspace = 0x100000
@@ -109,7 +109,7 @@ def test_unaligned_workspace_rejected():
     b = B.Buffers()
     for l in range(cfg.n_layers):
         for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "block_stage",
-                  "ring_k_scale", "ring_v_scale"):
+                  "ring_k_scale", "ring_v_scale", "kbar_gscale", "vbar_gscale"):
             getattr(b, f)[l] = 0x10000
     b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = 0x10000
     b.workspace = 0x100010
@@ -279,7 +279,7 @@ def test_indexerless_group_accepted_and_sized():
     b = B.Buffers()
     fake = 0x10000
     for f in ("kbar", "vbar", "kbar_scale", "vbar_scale", "kbar_stage", "vbar_stage", "ring_k", "ring_v", "block_stage",
-                  "ring_k_scale", "ring_v_scale"):
+                  "ring_k_scale", "ring_v_scale", "kbar_gscale", "vbar_gscale"):
         for l in range(cfg.n_layers):
             getattr(b, f)[l] = fake
     b.block_table = fake
@@ -295,3 +295,31 @@ def test_indexerless_group_accepted_and_sized():
         assert L.csa_compress(C.c_void_p(h), 0, 1, i32([0]), i32([4]), f, f, f, f, s) == 1
     finally:
         B.csa_cache_destroy(h)
+
+
+def test_fp4_config_sizes_and_buffers():
+    """FP4 main KV: packed E2M1 rows (64 bytes), one E4M3 code per 16 channels of
+    an entry, fp8 indexer keys with page scales and staging, no K/V staging."""
+    cfg = _spec(kv_dtype=B.CSA_FP4_E2M1)
+    sz = B.csa_buffer_sizes_for(cfg)
+    P, S = cfg.pool_pages, cfg.max_seqs
+    assert sz.kv_pool == P * 64 * 64
+    assert sz.group_scale == P * 64 * 8
+    assert sz.idx_pool == P * 64 * 64
+    assert sz.page_scale == P * 4 and sz.idx_stage == S * 64 * 64 * 4 and sz.kv_stage == 0
+    assert B.csa_buffer_sizes_for(_spec()).group_scale == 0
+    with pytest.raises(B.CsaError) as e:
+        B.csa_buffer_sizes_for(_spec(kv_dtype=B.CSA_FP4_E2M1, act_dtype=B.CSA_F32, swa_dtype=B.CSA_F32))
+    assert e.value.status == 3
+    # group scales are required
+    b = B.Buffers()
+    for l in range(cfg.n_layers):
+        for f in ("kbar", "vbar", "ring_k", "ring_v", "block_stage"):
+            getattr(b, f)[l] = 0x10000
+    b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = 0x10000
+    b.workspace, b.workspace_bytes = 0x100000, B.csa_workspace_size(cfg, 8, 512)
+    with pytest.raises(B.CsaError):
+        B.csa_cache_create(cfg, b)
+    for l in range(cfg.n_layers):
+        b.kbar_gscale[l] = b.vbar_gscale[l] = 0x10000
+    B.csa_cache_destroy(B.csa_cache_create(cfg, b))

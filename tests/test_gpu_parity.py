@@ -18,7 +18,7 @@ from compressed_sparse_attention_csa_amd import synth as Sy
 from oracle import csa_oracle as O
 
 from gpu_helpers import (TOL, TORCH_ACT, bf16_ulp, e4m3_ulp, fill_index_keys, fill_main_kv, fill_ring, make_cache,
-                         max_abs, raw_rows, to64, topk_matches)
+                         max_abs, raw_rows, to64, topk_matches, unpack_fp4)
 
 pytestmark = pytest.mark.gpu
 
@@ -391,7 +391,7 @@ def _chain(kv, act, lens, k, W, seed=31, n_layers=1, H=16, r=4, dense=False, swa
             comp[layer] = (O.store(kb, kv)[0], O.store(vb, kv)[0], O.store_ring_rows(K, swa)[0],
                            O.store_ring_rows(V, swa)[0])
             if layer == 0:
-                kis = O.store(ki, kv)[0]
+                kis = O.store(ki, "fp8" if kv == "fp4" else kv)[0]   # fp4 caches keep fp8 indexer keys
         layers = [dict(q=to64(outs[l][0][b]), W=W, scale=scale, kbar=comp[l][0], vbar=comp[l][1], rawk=comp[l][2],
                        rawv=comp[l][3]) for l in range(n_layers)]
         To, oo = O.decode_step(to64(qi[b]), to64(w[b]), kis, r, k, L - 1, layers)
@@ -859,3 +859,97 @@ def test_ring_write_rejects_rows_outside_the_ring():
     cache.ring_write(0, [0], [68], [32], K[:32], K[:32])
     torch.cuda.synchronize()
     assert torch.equal(cache.ring_k[0][0, (np.arange(68, 100) % 32)].cpu(), K[:32].cpu())
+
+
+# --------------------------------------------------------------------------- FP4 main KV
+
+def test_device_fp4_codecs():
+    """E2M1 decode as the attention kernel unpacks a row (low nibble first) and
+    the compressor's encoder, against the oracle's format definition."""
+    b = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    out = torch.empty(512, dtype=torch.float32, device="cuda")
+    B.csa_debug_convert(4, b.cuda(), out)
+    got = out.cpu().numpy().astype(np.float64).reshape(256, 2)
+    bb = np.arange(256)
+    np.testing.assert_array_equal(got[:, 0], O.e2m1_decode(bb & 0xF))
+    np.testing.assert_array_equal(got[:, 1], O.e2m1_decode(bb >> 4))
+    rng = np.random.default_rng(71)
+    mags = O.e2m1_decode(np.arange(8))
+    mids = (mags[:-1] + mags[1:]) / 2
+    x = np.concatenate([rng.standard_normal(20000) * 3, rng.uniform(-8, 8, 5000), mids, -mids, mags, -mags,
+                        [0.0, -0.0, 6.0, 6.5, 100.0, -1e9, 1e-30]]).astype(np.float32)
+    codes = torch.empty(x.shape[0], dtype=torch.uint8, device="cuda")
+    B.csa_debug_convert(5, torch.from_numpy(x).cuda(), codes)
+    np.testing.assert_array_equal(codes.cpu().numpy(), O.e2m1_encode(x))
+
+
+def _check_fp4(cache, pool, gpool, seq, n, x64, what, exact):
+    """GPU fp4 entries of one stream vs the oracle's quantisation of x64: every
+    code and scale equal when the GPU's fp32 entries are the oracle's (exact),
+    else at least 99 % of them, and every GPU value a valid quantisation of x64."""
+    codes = unpack_fp4(cache.logical(pool, seq, n).cpu().numpy())
+    gsc = cache.logical(gpool, seq, n).cpu().numpy()
+    _, (oc, osc) = O.store(x64, "fp4")
+    if exact:
+        assert np.array_equal(codes, oc) and np.array_equal(gsc, osc), what
+        return
+    assert np.mean(codes == oc) > 0.99 and np.mean(gsc == osc) > 0.99, (what, np.mean(codes == oc), np.mean(gsc == osc))
+    deq = O.fp4_dequantize_rows(codes, gsc)
+    s = O.e4m3_decode(gsc)
+    g = np.abs(x64).reshape(n, 8, 16) / np.where(s > 0, s, 1)[..., None]
+    half = np.where(g < 2, 0.25, np.where(g < 4, 0.5, 1.0)) * s[..., None]
+    clip = np.maximum(0, g - 6.0) * s[..., None]
+    err = np.abs(deq - x64).reshape(n, 8, 16)
+    assert np.all(err <= half + clip + 1e-6 * np.abs(x64).reshape(n, 8, 16).max() + 1e-12), what
+
+
+@pytest.mark.parametrize("r", [1, 4])
+def test_compress_fp4_matches_oracle(r):
+    """r = 1: entries are the raw bf16 rows, so the fp4 bytes equal the oracle's
+    exactly; r = 4: pooled fp32 entries may differ from the oracle's by an ulp."""
+    lens = [64 * 4 * 3 + 21, 517, 5] if r == 4 else [300, 129, 64]
+    cache, raw, P = _compress_case("fp4", "bf16", r, lens)
+    for b, L in enumerate(lens):
+        K, V, Z = (to64(t) for t in raw[0][b])
+        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        n = L // r
+        if n == 0:
+            continue
+        _check_fp4(cache, cache.kbar[0], cache.kbar_gscale[0], b, n, kb, f"kbar seq {b}", exact=r == 1)
+        _check_fp4(cache, cache.vbar[0], cache.vbar_gscale[0], b, n, vb, f"vbar seq {b}", exact=r == 1)
+        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, "fp8", f"kidx seq {b}")
+    assert cache.read_errors() == 0
+
+
+def test_compress_fp4_incremental_equals_bulk():
+    lens = [64 * 4 * 2 + 13, 301]
+    bulk, _, _ = _compress_case("fp4", "bf16", 4, lens, seed=9)
+    inc, _, _ = _compress_case("fp4", "bf16", 4, lens, seed=9, chunks=[1, 3, 2, 1, 7, 64, 1, 1, 200, 5])
+    for b, L in enumerate(lens):
+        n = L // 4
+        for pa, pb in ((bulk.kbar[0], inc.kbar[0]), (bulk.vbar[0], inc.vbar[0]), (bulk.kbar_gscale[0], inc.kbar_gscale[0]),
+                       (bulk.vbar_gscale[0], inc.vbar_gscale[0]), (bulk.kidx, inc.kidx)):
+            assert torch.equal(bulk.logical(pa, b, n).cpu(), inc.logical(pb, b, n).cpu())
+        assert torch.equal(bulk.logical_scales(bulk.kidx_scale, b, n).cpu(), inc.logical_scales(inc.kidx_scale, b, n).cpu())
+
+
+@pytest.mark.parametrize("swa", ["", "fp8"])
+def test_attend_fp4_decode_matches_oracle(swa):
+    _attend_case("fp4", "bf16", lens=[4 * 700 + 2, 4 * 64, 37, 4], k=256, W=128, swa=swa)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_attend_fp4_head_counts(H):
+    _attend_case("fp4", "bf16", lens=[4 * 500 + 3, 4 * 90], k=200, W=64, H=H)
+
+
+def test_attend_fp4_chunk_matches_oracle():
+    _attend_case("fp4", "bf16", lens=[4 * 600 + 1, 400], k=128, W=128, chunk=(0, 48))
+
+
+def test_step_decode_chain_fp4():
+    _chain("fp4", "bf16", [4 * 3000 + 2, 4100, 777], k=256, W=128, H=64, n_layers=2)
+
+
+def test_hca_fp4():
+    _hca_case("fp4", "bf16", lens=[64 * 500 + 7, 100], r=64, W=128)
