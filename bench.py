@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-hca", action="store_true", help="skip the heavily-compressed-attention leg")
     ap.add_argument("--no-hier", action="store_true", help="skip the hierarchical-indexer (pool / Reindex) leg")
     ap.add_argument("--no-swa-fp8", action="store_true", help="skip the fp8 window-ring decode leg")
+    ap.add_argument("--no-fp4", action="store_true", help="skip the fp4 main-KV decode leg")
     return ap.parse_args()
 
 
@@ -306,13 +307,14 @@ def hier_leg(caches, qi, w, steps, seed):
             "fallback_flag": bool(flags & B.ERR_FALLBACK)}
 
 
-def swa_fp8_leg(seed, dev, replicas, qi, w, qs, steps):
-    """The headline decode step with the window ring stored as E4M3 (one
-    scale per row) instead of bf16: same caches otherwise, same graph timing."""
+def variant_leg(seed, dev, replicas, qi, w, qs, steps, kv="fp8", swa=""):
+    """The headline decode step on caches of another storage format (the
+    window ring as E4M3 with one scale per row, or FP4 main K/V): same
+    workload, same graph timing."""
     import torch
     from compressed_sparse_attention_csa_amd import accounting as A
     from compressed_sparse_attention_csa_amd import binding as B
-    caches = build_cache(seed, replicas, dev, swa="fp8")
+    caches = build_cache(seed, replicas, dev, swa=swa, kv=kv)
     q_seq, q_pos = list(range(BATCH)), [CONTEXT - 1] * BATCH
     topk = [torch.empty((BATCH, TOPK), dtype=torch.int32, device=dev) for _ in caches]
     outs = [torch.empty((BATCH, HEADS, 128), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
@@ -336,16 +338,18 @@ def swa_fp8_leg(seed, dev, replicas, qi, w, qs, steps):
     att_us = kernel_us(caches, B.PROFILE_ATTEND, attend_only, steps // 4 + 1)
     flags = max(c.read_errors() for c in caches)
     if flags:
-        raise RuntimeError(f"fp8-ring leg raised device error flags {flags}")
+        raise RuntimeError(f"{kv}/{swa or 'bf16'} leg raised device error flags {flags}")
     for c in caches:
         c.close()
-    sb = A.decode_step_bytes(BATCH, CONTEXT // RATIO, 128, 64, HEADS, IDX_HEADS, TOPK, WINDOW, LAYERS, "fp8", "bf16", "fp8")
-    return {"workload": "the headline decode step with an fp8 (E4M3, scale per row) window ring",
+    sb = A.decode_step_bytes(BATCH, CONTEXT // RATIO, 128, 64, HEADS, IDX_HEADS, TOPK, WINDOW, LAYERS, kv, "bf16",
+                             swa or "bf16")
+    what = {"fp8": "fp8 pages (fp32 scale per page)", "fp4": "fp4 entries (E2M1, E4M3 scale per 16 channels)"}[kv]
+    return {"workload": f"the headline decode step, main K/V as {what}, window ring {swa or 'bf16'}",
             "ms_per_step": round(us * 1e-3, 5), "tokens_per_s": round(BATCH / (us * 1e-6), 1),
             "attend_kernel_us": round(att_us, 3), "step_bytes": sb}
 
 
-def build_cache(seed, replicas, dev, swa=""):
+def build_cache(seed, replicas, dev, swa="", kv="fp8"):
     import torch
     from compressed_sparse_attention_csa_amd import binding as B
     from compressed_sparse_attention_csa_amd import synth as Sy
@@ -355,7 +359,7 @@ def build_cache(seed, replicas, dev, swa=""):
     pages = entries // 64
     spec = CacheSpec(ratio=RATIO, q_heads=HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW,
                      n_layers=LAYERS, max_seqs=BATCH, max_pages_per_seq=pages, pool_pages=BATCH * pages,
-                     kv_dtype="fp8", act_dtype="bf16", swa_dtype=swa, max_queries=BATCH, max_k=TOPK)
+                     kv_dtype=kv, act_dtype="bf16", swa_dtype=swa, max_queries=BATCH, max_k=TOPK)
     perm = torch.tensor(Sy.permutation(seed, BATCH * pages, salt=3), dtype=torch.int32)
     bt = perm.view(BATCH, pages).to(dev)
     base = CsaCache(spec, dev, block_table=bt)
@@ -379,6 +383,7 @@ def build_cache(seed, replicas, dev, swa=""):
                          (base.vbar_scale, c.vbar_scale), (base.ring_k, c.ring_k), (base.ring_v, c.ring_v),
                          (base.ring_k_scale, c.ring_k_scale), (base.ring_v_scale, c.ring_v_scale),
                          (base.kbar_stage, c.kbar_stage), (base.vbar_stage, c.vbar_stage),
+                         (base.kbar_gscale, c.kbar_gscale), (base.vbar_gscale, c.vbar_gscale),
                          (base.block_stage, c.block_stage)):
             for s_, d_ in zip(src, dst):
                 d_.copy_(s_)
@@ -583,7 +588,10 @@ def main():
     del caches, graphs
     torch.cuda.empty_cache()
     if not args.no_swa_fp8:
-        line["swa_fp8"] = swa_fp8_leg(args.seed, dev, args.replicas, qi, w, qs, args.steps)
+        line["swa_fp8"] = variant_leg(args.seed, dev, args.replicas, qi, w, qs, args.steps, kv="fp8", swa="fp8")
+        torch.cuda.empty_cache()
+    if not args.no_fp4:
+        line["fp4_kv"] = variant_leg(args.seed, dev, args.replicas, qi, w, qs, args.steps, kv="fp4")
         torch.cuda.empty_cache()
     if not args.no_prefill:
         line["prefill"] = prefill_leg(args.seed, dev)

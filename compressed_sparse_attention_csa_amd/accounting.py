@@ -18,7 +18,9 @@ def kv_cache_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, elem_b
 
 
 def index_scan_bytes(n_entries: int, d_i: int, kv_dtype: str, page_entries: int = 64) -> int:
-    """Bytes one query's indexer scan reads: its visible indexer keys (+ page scales)."""
+    """Bytes one query's indexer scan reads: its visible indexer keys (+ page
+    scales). Caches with fp4 K/V keep fp8 indexer keys."""
+    kv_dtype = "fp8" if kv_dtype == "fp4" else kv_dtype
     b = n_entries * d_i * DTYPE_BYTES[kv_dtype]
     if kv_dtype == "fp8":
         b += -(-n_entries // page_entries) * 4
@@ -34,10 +36,12 @@ def attend_bytes(k_sel: int, window: int, d: int, h_q: int, kv_dtype: str, act_d
     (plus one K and one V row scale each for an fp8 ring), the query, the
     output, and the Top-K row it reads.
     """
-    kvb = DTYPE_BYTES[kv_dtype]
     ab = DTYPE_BYTES[act_dtype]
     sd = swa_dtype or act_dtype
-    b = k_sel * 2 * d * kvb
+    if kv_dtype == "fp4":                 # d/2 code bytes + d/16 E4M3 group-scale bytes per row
+        b = k_sel * 2 * (d // 2 + d // 16)
+    else:
+        b = k_sel * 2 * d * DTYPE_BYTES[kv_dtype]
     if kv_dtype == "fp8":
         b += k_sel * 2 * 4
     b += window * 2 * d * DTYPE_BYTES[sd]

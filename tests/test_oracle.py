@@ -627,3 +627,14 @@ def test_fp4_on_grid_groups_round_trip():
     np.testing.assert_array_equal(vals, x.astype(np.float64))
     assert np.all((codes.reshape(40, 8, 16)[..., 0] & 7)[np.arange(40) != 5] == 7)
     assert np.all(codes[5, 32:48] == 0)
+
+
+def test_fp4_and_ring_byte_accounting():
+    """Per gathered fp4 row: 64 code bytes + 8 scale bytes, for K and V; an fp8
+    window row: 128 bytes + one fp32 scale; fp4 caches scan fp8 indexer keys."""
+    from compressed_sparse_attention_csa_amd import accounting as A
+    base = A.attend_bytes(0, 0, 128, 64, "fp4", "bf16")
+    assert A.attend_bytes(1024, 0, 128, 64, "fp4", "bf16") - base == 1024 * 2 * (64 + 8) + 1024 * 4 - 0
+    assert A.attend_bytes(0, 128, 128, 64, "fp8", "bf16", "fp8") - A.attend_bytes(0, 0, 128, 64, "fp8", "bf16") == 128 * 2 * (128 + 4)
+    assert A.index_scan_bytes(262144, 64, "fp4") == A.index_scan_bytes(262144, 64, "fp8") == 262144 * 64 + 4096 * 4
+    assert A.reindex_bytes(16384, 2048, 64, "fp8") == 16384 * 64 + 2048 * 8
