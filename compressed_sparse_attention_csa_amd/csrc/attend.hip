@@ -104,6 +104,12 @@ __device__ __forceinline__ void chunk_values(const uint4 &u, CT *dst, uint32_t g
 }
 
 constexpr int32_t kMaskedRow = INT32_MIN;   // src_row of a key that takes no part
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.f;             // log2 headroom of the lazily rescaled softmax
+
+// 2^x with the hardware instruction alone (results below 2^-126 flush to 0,
+// which a softmax weight can lose).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int SD> constexpr int elem_bytes_of() { return SD == DT_F32 ? 4 : (SD == DT_BF16 ? 2 : 1); }
 template <int SD> constexpr int row_bytes_of() { return SD == DT_FP4 ? kD / 2 : kD * elem_bytes_of<SD>(); }
@@ -116,6 +122,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   constexpr int NT = HG * 64;
   constexpr int H = HG * NTW * 16;
   constexpr int AE = elem_bytes_of<ACT>();
+  constexpr bool VSCALE = KV == DT_FP8 || RS == DT_FP8;   // value rows carry a page or row scale
   constexpr int64_t PRB = row_bytes_of<KV>(), RRB = row_bytes_of<RS>();   // pool / ring row bytes
   constexpr int KS = kD + kpad<CT>();          // K row stride (elements)
   // bf16: V row-major like K, read as transposed MFMA fragments; fp32: V^T
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     }
     if (tid < kKeyBlock) {
       const bool valid = kvalid[(b - b_begin) * kKeyBlock + tid] != 0;
-      kmul[tid] = valid ? a.scale * ks_pref : 0.f;
+      kmul[tid] = valid ? a.scale * kLog2e * ks_pref : 0.f;   // logits in log2 units
       kbias[tid] = valid ? 0.f : -INFINITY;
       vsc[tid] = vs_pref;
     }
@@ -413,25 +420,32 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
         }
       bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
       bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      const float m_new = fmaxf(m_run[j], bm);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run[j] - m_new);
+      // Lazy rescaling: O and l stay relative to the reference max m_run, which
+      // moves only when a head's block max exceeds it by more than kRescale
+      // (probabilities stay <= 2^kRescale); the wave rescales all its heads then.
+      if (__builtin_amdgcn_ballot_w64(bm > m_run[j] + kRescale) != 0) {
+        const float m_new = fmaxf(m_run[j], bm);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
+        l_run[j] *= alpha;
+        m_run[j] = m_new;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float av = __shfl(alpha, 4 * g + v, 64);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) O[j][n][v] *= av;
+        }
+      }
+      const float m_ref = m_run[j] == -INFINITY ? 0.f : m_run[j];   // masked keys: exp2(-inf) = 0
       float psum = 0.f;
       float p[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          p[kt][v] = (x[kt][v] == -INFINITY) ? 0.f : __expf(x[kt][v] - m_new);
+          p[kt][v] = fast_exp2(x[kt][v] - m_ref);
           psum += p[kt][v];
         }
-      l_run[j] = l_run[j] * alpha + psum;
-      m_run[j] = m_new;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float av = __shfl(alpha, 4 * g + v, 64);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) O[j][n][v] *= av;
-      }
+      l_run[j] += psum;
       // O += P . V over the two 32-key halves; V^T fragments read one step ahead
       auto load_vf = [&](int kc, int n) {
         Frag<CT> vf;
@@ -452,7 +466,8 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       };
       float4 vs4[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) vs4[kt] = *reinterpret_cast<const float4 *>(&vsc[16 * kt + 4 * g]);
+      for (int kt = 0; kt < 4; ++kt)
+        vs4[kt] = VSCALE ? *reinterpret_cast<const float4 *>(&vsc[16 * kt + 4 * g]) : make_float4(1.f, 1.f, 1.f, 1.f);
       Frag<CT> vfb[2];
       vfb[0] = load_vf(0, 0);
 #pragma unroll
@@ -543,7 +558,7 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   float L = 0.f, acc = 0.f;
 #pragma unroll
   for (int s = 0; s < kAttMaxSplits; ++s) {
-    const float e = (m[s] == -INFINITY) ? 0.f : __expf(m[s] - mx);
+    const float e = (m[s] == -INFINITY) ? 0.f : fast_exp2(m[s] - mx);   // running maxima are in log2 units
     L += e * l[s];
     acc += e * o[s];
   }
