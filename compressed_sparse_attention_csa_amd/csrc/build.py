@@ -24,6 +24,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # packed fp32 instructions stay off: the compiler must not emit v_pk_*_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary vector registers: score and softmax epilogues read
+    # them directly instead of copying out of accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
 ]
 
