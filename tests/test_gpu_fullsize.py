@@ -211,3 +211,90 @@ def test_serving_64_requests_4k_to_256k_sampled():
     for b in (int(np.argmax(lens)), int(np.argmin(lens))):
         _check_query(seed, dev, b, pos[b], qi[b], w[b], q[b], Tg[b], out[b], k, W, "fp8", 2e-2, final[b])
     c.close()
+
+
+def _seq0_entries(bm, seed, dev, layer, kv):
+    """Oracle compressed entries of sequence 0 of `layer` at the benchmark's
+    1M-token size, stored in `kv` (indexer keys fp8 for fp8 and fp4 caches)."""
+    E = bm.CONTEXT // bm.RATIO
+    P = to64(Sy.proj_matrix(seed, 128, 64)) if layer == 0 else None
+    kb, vb = np.empty((E, 128)), np.empty((E, 128))
+    ki = np.empty((E, 64)) if layer == 0 else None
+    step = 1 << 18
+    for r0 in range(0, bm.CONTEXT, step):
+        K, V, Z = (to64(_rows(seed, kind, layer, 0, r0, step, dev)) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+        a, b_, c_ = O.compress(K, V, Z, bm.RATIO, P)
+        sl = slice(r0 // bm.RATIO, (r0 + step) // bm.RATIO)
+        kb[sl], vb[sl] = a, b_
+        if layer == 0:
+            ki[sl] = c_
+    return O.store(kb, kv)[0], O.store(vb, kv)[0], (O.store(ki, "fp8")[0] if layer == 0 else None)
+
+
+def _block_scores(s):
+    nb = (s.shape[0] + 7) // 8
+    return np.maximum.reduceat(s.astype(np.float32), np.arange(0, s.shape[0], 8))[:nb]
+
+
+def test_hierarchical_indexer_1m_sampled(bench_mod):
+    """The benchmark's 1M-token batch-4 cache: the Full layer's Top-1024 with a
+    2,048-block pool, then a Reindex layer's Top-1024 inside the pool; sequence
+    0 against the oracle's pool and Reindex selection (2e-2 tie band: the fp8
+    indexer keys are compressed on each side), every row checked for validity."""
+    bm = bench_mod
+    seed, dev, nb = 0, torch.device("cuda:0"), 2048
+    c = bm.build_cache(seed, 1, dev)[0]
+    q_seq, q_pos = list(range(bm.BATCH)), [bm.CONTEXT - 1] * bm.BATCH
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, bm.BATCH * 4, 64, dev, torch.bfloat16).view(bm.BATCH, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, bm.BATCH, 4, dev)
+    qi2 = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI, 1), 0, bm.BATCH * 4, 64, dev, torch.bfloat16).view(bm.BATCH, 4, 64)
+    w2 = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W, 1), 0, bm.BATCH, 4, dev)
+    T, P = c.index_topk_pool(q_seq, q_pos, qi, w, bm.TOPK, nb)
+    T2 = c.index_reindex(q_seq, q_pos, qi2, w2, P, bm.TOPK)
+    assert c.read_errors() & ~B.ERR_FALLBACK == 0
+    Tg, Pg, T2g = T.cpu().numpy(), P.cpu().numpy(), T2.cpu().numpy()
+    E = bm.CONTEXT // bm.RATIO
+    for b in range(bm.BATCH):
+        assert np.all(np.diff(Pg[b]) > 0) and Pg[b][0] >= 0 and Pg[b][-1] < E // 8
+        ents = set(O.pool_entries(Pg[b], E).tolist())
+        assert set(T2g[b].tolist()) <= ents and np.all(np.diff(T2g[b]) > 0)
+        assert set(Tg[b].tolist()) <= ents            # the Full Top-K lies in its own pool
+    _, _, kis = _seq0_entries(bm, seed, dev, 0, "fp8")
+    s = O.index_scores(to64(qi[0]), to64(w[0]), kis)
+    Po = O.candidate_pool(s, nb)
+    ok, msg = topk_matches(Pg[0], Po, _block_scores(s), rel=2e-2)
+    assert ok, "pool: " + msg
+    s2 = O.index_scores(to64(qi2[0]), to64(w2[0]), kis)
+    ok, msg = topk_matches(T2g[0], O.reindex_topk(to64(qi2[0]), to64(w2[0]), kis, Po, bm.TOPK, E), s2, rel=2e-2)
+    assert ok, "reindex: " + msg
+    c.close()
+
+
+def test_decode_1m_fp4_sampled(bench_mod):
+    """The benchmark's decode step on fp4 K/V (E2M1, E4M3 scale per 16 channels,
+    fp8 indexer keys): sequence 0's Top-K and layer-0 attention against the
+    oracle's fp4 entries."""
+    bm = bench_mod
+    seed, dev = 0, torch.device("cuda:0")
+    c = bm.build_cache(seed, 1, dev, kv="fp4")[0]
+    q_seq, q_pos = list(range(bm.BATCH)), [bm.CONTEXT - 1] * bm.BATCH
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, bm.BATCH * 4, 64, dev, torch.bfloat16).view(bm.BATCH, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, bm.BATCH, 4, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, 0), 0, bm.BATCH * bm.HEADS, 128, dev, torch.bfloat16).view(bm.BATCH, bm.HEADS, 128)
+    T = c.index_topk(q_seq, q_pos, qi, w, bm.TOPK)
+    scale = 1.0 / math.sqrt(128)
+    out = to64(c.attend(0, q_seq, q_pos, q, T, bm.TOPK, scale))
+    assert c.read_errors() == 0
+    kb, vb, kis = _seq0_entries(bm, seed, dev, 0, "fp4")
+    s = O.index_scores(to64(qi[0]), to64(w[0]), kis)
+    To = O.topk(s, bm.TOPK)
+    ok, msg = topk_matches(T.cpu().numpy()[0], To, s, rel=2e-2)
+    assert ok, msg
+    t = bm.CONTEXT - 1
+    lo = t - bm.WINDOW + 1
+    Kw, Vw = np.zeros((bm.CONTEXT, 128)), np.zeros((bm.CONTEXT, 128))
+    Kw[lo:] = to64(_rows(seed, Sy.KIND_K, 0, 0, lo, bm.WINDOW, dev))
+    Vw[lo:] = to64(_rows(seed, Sy.KIND_V, 0, 0, lo, bm.WINDOW, dev))
+    ref = O.attend_step(to64(q[0]), To, t, bm.WINDOW, scale, kb, vb, Kw, Vw)
+    assert max_abs(out[0], ref) <= 2e-2
+    c.close()
