@@ -522,6 +522,54 @@ def test_graph_replay_matches_eager():
     assert cache.read_errors() == 0
 
 
+@pytest.mark.parametrize("kv,swa", [("fp8", "fp8"), ("fp4", "")])
+def test_graph_replay_hierarchical_step_matches_eager(kv, swa):
+    """Full layer with a candidate pool, a Reindex layer, attention of both
+    (fp4 K/V, or fp8 pages with an fp8 ring) and a window-ring rewrite, captured
+    in one HIP graph: every replay reproduces the eager outputs bit for bit."""
+    cache = make_cache(73, ratio=4, q_heads=64, window=128, ring_rows=128, n_layers=2, max_seqs=3,
+                       max_pages_per_seq=40, pool_pages=121, kv_dtype=kv, act_dtype="bf16", max_queries=3, max_k=512,
+                       swa_dtype=swa)
+    lens = [4 * 2500, 4 * 1000 + 3, 4 * 300]
+    for b, L in enumerate(lens):
+        for layer in range(2):
+            fill_main_kv(cache, 73, layer, b, L // 4)
+            fill_ring(cache, 73, layer, b, L)
+            B.csa_seq_set_len(cache.handle, layer, b, L)
+        fill_index_keys(cache, 73, b, L // 4)
+    q_seq, q_pos = [0, 1, 2], [L - 1 for L in lens]
+    qi = [Sy.normal_rows(73, Sy.stream_id(Sy.KIND_QI, l), 0, 12, 64, dtype=torch.bfloat16).view(3, 4, 64).cuda() for l in range(2)]
+    w = [Sy.uniform_rows(73, Sy.stream_id(Sy.KIND_W, l), 0, 3, 4).cuda() for l in range(2)]
+    q = [Sy.normal_rows(73, Sy.stream_id(Sy.KIND_Q, l), 0, 192, 128, dtype=torch.bfloat16).view(3, 64, 128).cuda() for l in range(2)]
+    newk = raw_rows(74, Sy.KIND_K, 0, 0, 0, 8, "bf16").cuda()
+    T = [torch.empty((3, 512), dtype=torch.int32, device="cuda") for _ in range(2)]
+    P = torch.empty((3, 64), dtype=torch.int32, device="cuda")
+    out = [torch.empty((3, 64, 128), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+    def step(st):
+        B.csa_ring_write(cache.handle, 1, [0], [lens[0] - 8], [8], newk, newk, st)
+        B.csa_index_topk_pool(cache.handle, q_seq, q_pos, qi[0], w[0], 512, T[0], 64, P, st)
+        B.csa_index_reindex(cache.handle, q_seq, q_pos, qi[1], w[1], 64, P, 512, T[1], st)
+        for l in range(2):
+            B.csa_attend(cache.handle, l, q_seq, q_pos, q[l], T[l], 512, 0.088, out[l], st)
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    refs = [x.clone() for x in (T[0], T[1], P, out[0], out[1])]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(4):
+        for x in (T[0], T[1], P, out[0], out[1]):
+            x.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()       # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for x, r in zip((T[0], T[1], P, out[0], out[1]), refs):
+            assert torch.equal(x, r), f"replay {rep} differs"
+        del junk
+    assert cache.read_errors() & ~B.ERR_FALLBACK == 0
+
+
 @pytest.mark.parametrize("kv,act", DT_CASES)
 def test_index_chunk_threshold_fallback_is_exact(kv, act):
     """Adversarial prefill chunk: only the entries the threshold pass samples
