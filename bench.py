@@ -125,8 +125,14 @@ def prefill_leg(seed, dev, steps=5):
     torch.cuda.synchronize()
     scan_ms, n = B.csa_profile_end(c.handle, B.PROFILE_INDEX)
     att_kernel_ms, n_att = B.csa_profile_end(c.handle, B.PROFILE_ATTEND)
+    # the chunk's Full-layer index with and without its per-query candidate pool
+    # (2,048 blocks of 8 entries), the cache holding the chunk
+    pool = torch.empty((PF_CHUNK, POOL_BLOCKS), dtype=torch.int32, device=dev)
+    idx_us = graph_us([lambda st: B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, PF_K, T, st)], steps)
+    pool_us = graph_us([lambda st: B.csa_index_topk_pool(c.handle, q_seq, q_pos, qi, w, PF_K, T, POOL_BLOCKS, pool, st)],
+                       steps)
     flags = c.read_errors()
-    if flags:
+    if flags & ~B.ERR_FALLBACK:
         raise RuntimeError(f"prefill leg raised device error flags {flags}")
     idx_flops = A.index_flops(A.prefill_visible_scores(PF_PRIOR, PF_CHUNK, RATIO), IDX_HEADS, 64)
     att_flops = A.attend_flops(PF_CHUNK, HEADS, PF_K + WINDOW, 128)
@@ -139,6 +145,7 @@ def prefill_leg(seed, dev, steps=5):
            "attend": {"tflops": round(att_flops / (att_ms * 1e-3) / 1e12, 1),
                       "util": round(att_flops / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                       "us": round(att_ms * 1e3, 2), "gflop": round(att_flops / 1e9, 2)},
+           "index_us": round(idx_us, 2), "index_with_pool_us": round(pool_us, 2),
            "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
     c.close()
     return res

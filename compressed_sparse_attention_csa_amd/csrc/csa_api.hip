@@ -550,7 +550,7 @@ DecodeScratch carve_decode(csa_cache_t h, int nq, int64_t s_stride) {
 
 // Prefill chunk: queries of one sequence at consecutive positions.
 csa_status index_chunk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q_idx,
-                       const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
+                       const float *w_idx, int32_t k, int32_t *topk, int32_t n_pool, int32_t *pool, hipStream_t stream) {
   const csa_config &c = h->cfg;
   const int kv = idx_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
@@ -577,8 +577,12 @@ csa_status index_chunk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const i
   s.n_etiles = (n_max + 255) / 256;
   s.n_stiles = (n_max / kChunkSample + 255) / 256;
   s.kv_dtype = kv; s.act_dtype = act;
+  // pool: block maxima in the fallback rows, selected before the Top-K select can reuse them
+  s.pool = pool; s.n_pool = n_pool;
+  s.bmax = pool ? s.fb_rows : nullptr; s.bm_stride = s.fb_stride;
   const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
   launch_idx_chunk(s, kv, act, stream, ev.start, ev.stop);
+  launch_idx_chunk_pool(s, stream);
   launch_idx_chunk_select(s, stream);
   return CSA_OK;
 }
@@ -670,7 +674,7 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
                           const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
   csa_status st = check_index_args(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk);
   if (st != CSA_OK) return st;
-  st = is_chunk(n_q, q_seq, q_pos) ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, stream)
+  st = is_chunk(n_q, q_seq, q_pos) ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream)
                                    : index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream);
   if (st != CSA_OK) return st;
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_topk");
@@ -685,7 +689,9 @@ csa_status csa_index_topk_pool(csa_cache_t h, int32_t n_q, const int32_t *q_seq,
   if (n_pool_blocks < 1 || n_pool_blocks > CSA_MAX_POOL_BLOCKS)
     return fail(CSA_ERR_UNSUPPORTED, "n_pool_blocks = %d outside [1, %d]", n_pool_blocks, CSA_MAX_POOL_BLOCKS);
   if (!pool) return fail(CSA_ERR_INVALID_ARG, "pool is required");
-  st = index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream);
+  st = is_chunk(n_q, q_seq, q_pos)
+           ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream)
+           : index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream);
   if (st != CSA_OK) return st;
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_topk_pool");
   return CSA_OK;

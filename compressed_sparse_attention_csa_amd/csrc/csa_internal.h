@@ -136,7 +136,12 @@ struct IdxChunkArgs {
   float *fb_rows;          // [n_tok][fb_stride] full rows for the exact fallback
   int32_t *topk;           // [n_tok][k]
   uint32_t *err;
+  // candidate pool (null when not built): 8-entry block maxima [n_tok][bm_stride],
+  // stored in fb_rows (the pool select runs before the Top-K select may need them)
+  float *bmax;
+  int32_t *pool;           // [n_tok][n_pool] ascending block ids, -1 padding
   int32_t pool_pages, h_i, ss_stride, fb_stride, n_tok, pos0, r, k, m_s, n_etiles, n_stiles, kv_dtype, act_dtype;
+  int32_t bm_stride, n_pool;
 };
 
 // ev0/ev1 (may be null): events stamped with the start and end of the launch
@@ -148,6 +153,7 @@ void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
 void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
                       hipEvent_t ev1 = nullptr);
 void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s);
+void launch_idx_chunk_pool(const IdxChunkArgs &a, hipStream_t s);
 void launch_idx_rescan(const IdxRescanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
 

@@ -861,6 +861,7 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
   using CT = typename ComputeT<KV>::type;
   constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
   constexpr bool SAMPLE = MODE == 0;
+  constexpr bool POOL = MODE == 2;   // the full pass also writes 8-entry block maxima
   constexpr int kChunkElems = 16 / KE;                 // elements per 16-byte load
   constexpr int kChunksPerRow = kDI / kChunkElems;
   constexpr int kLoads = kCE * kChunksPerRow / 256;    // 16-byte loads per thread per tile
@@ -1017,6 +1018,14 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
           for (int v = 0; v < 4; ++v) s += wq[mt][v] * relu_bits(acc[mt][nt][v]);
           if constexpr (KV == DT_FP8) s *= psc[nt];
           const bool vis = full || (qok[mt] && e < nvis[mt]);
+          if constexpr (POOL) {
+            // the 8 lanes of an aligned block hold consecutive entries of one query
+            float m8 = vis ? s : -INFINITY;
+#pragma unroll
+            for (int o = 1; o < kPoolBlock; o <<= 1) m8 = fmaxf(m8, __shfl_xor(m8, o, 64));
+            if ((col & (kPoolBlock - 1)) == 0 && qok[mt] && e < nvis[mt])
+              a.bmax[static_cast<int64_t>(qo) * a.bm_stride + (e >> 3)] = m8;
+          }
           if constexpr (SAMPLE) {
             if (vis) a.ss[static_cast<int64_t>(qo) * a.ss_stride + m0 + le] = s;
           } else {
@@ -1157,7 +1166,39 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
   }
 }
 
+// Candidate pool of each chunk query: the n_pool best 8-entry blocks by the
+// block maxima the full pass wrote (ties -> lower block), ascending.
+__global__ __launch_bounds__(512) void idx_chunk_pool_kernel(const IdxChunkArgs a) {
+  __shared__ uint64_t keys[kSelCap];
+  __shared__ uint64_t bin_keys[kRankCap];
+  __shared__ int sel[CSA_MAX_POOL_BLOCKS];
+  __shared__ int hist[kSelBins];
+  __shared__ float red[32];
+  __shared__ int sh[4];
+  const int qi = blockIdx.x, tid = threadIdx.x, bd = blockDim.x;
+  const int N = (a.pos0 + qi + 1) / a.r, P = a.n_pool;
+  const int nB = (N + kPoolBlock - 1) / kPoolBlock;
+  int32_t *out = a.pool + static_cast<int64_t>(qi) * P;
+  const float *row = a.bmax + static_cast<int64_t>(qi) * a.bm_stride;
+  if (nB <= P) {
+    for (int i = tid; i < P; i += bd) out[i] = i < nB ? i : -1;
+    return;
+  }
+  bool done = false;
+  if (nB <= kSelCap) {
+    for (int i = tid; i < nB; i += bd) keys[i] = score_key(row[i], i);
+    __syncthreads();
+    done = select_ordered(keys, nB, P, hist, red, sh, bin_keys, out);
+  }
+  if (!done) select_and_write([&](int i) { return score_key(row[i], i); }, nB, P, sel, hist, sh, out);
+}
+
 }  // namespace
+
+void launch_idx_chunk_pool(const IdxChunkArgs &a, hipStream_t s) {
+  if (a.n_tok <= 0 || !a.pool) return;
+  hipLaunchKernelGGL(idx_chunk_pool_kernel, dim3(a.n_tok), dim3(512), 0, s, a);
+}
 
 void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.total_wg <= 0) return;
@@ -1204,7 +1245,8 @@ void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hip
   };
   gemm(std::integral_constant<int, 0>{}, a.n_stiles, nullptr, nullptr);
   hipLaunchKernelGGL(idx_chunk_tau_kernel, dim3(a.n_tok), dim3(256), 0, s, a);
-  gemm(std::integral_constant<int, 1>{}, a.n_etiles, ev0, ev1);
+  if (a.pool) gemm(std::integral_constant<int, 2>{}, a.n_etiles, ev0, ev1);
+  else gemm(std::integral_constant<int, 1>{}, a.n_etiles, ev0, ev1);
 }
 
 void launch_idx_chunk_select(const IdxChunkArgs &a, hipStream_t s) {

@@ -265,8 +265,8 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
  *                  largest block maximum max_{8b <= j < min(8b+8, N)} s[t][j]
  *                  (ties -> lower b), ascending; -1 pads the row when fewer
  *                  blocks are visible.
- * Every query takes the per-query kernels (its scores over all visible
- * entries are written to the workspace), also when the queries form a chunk.
+ * Chunk queries take the chunk kernels (the score GEMM also writes the block
+ * maxima); other queries the per-query kernels.
  * Errors: as csa_index_topk; CSA_ERR_UNSUPPORTED for n_pool_blocks out of range.
  */
 csa_status csa_index_topk_pool(csa_cache_t h, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,

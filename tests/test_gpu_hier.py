@@ -116,6 +116,22 @@ def test_pool_for_chunk_queries():
     _pool_case("bf16", "bf16", lens=[4 * 12000, 40], k=256, n_blocks=512, chunk=(0, 150))
 
 
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_pool_chunk_kernels_match_oracle(kv, act):
+    """Chunk queries take the score GEMM, which also writes the block maxima:
+    a 600-token chunk whose early queries see fewer blocks than the pool."""
+    _pool_case(kv, act, lens=[4 * 20000 + 3, 50], k=512, n_blocks=2048, chunk=(0, 600))
+
+
+def test_pool_chunk_long_context():
+    """More visible blocks than the pool select holds in LDS (7,500 > 6,144)."""
+    _pool_case("fp8", "bf16", lens=[4 * 60000 + 1], k=1024, n_blocks=2048, chunk=(0, 64))
+
+
+def test_pool_chunk_exact_ties():
+    _pool_case("bf16", "bf16", lens=[4 * 3000], k=64, n_blocks=50, dup_keys=True, exact=True, chunk=(0, 200))
+
+
 def _random_pool(rng, n_ent, n_blocks, force_last=False):
     nb = (n_ent + 7) // 8
     if nb <= n_blocks:
