@@ -979,7 +979,10 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
     // scores the same query, so the group's ballot orders its slots by entry
     int run[4] = {0, 0, 0, 0};
     // every (query, entry) pair of the wave visible in this tile: skip the per-score test
-    const bool full = qw + 15 < a.n_tok && entry_of(m0 + kCE - 1) < nvis_lo;
+    // (the tile's code comes in two copies: without any visibility test for
+    // the common fully visible tile, and with it)
+    auto tile_body = [&](auto full_tag) {
+    constexpr bool full = decltype(full_tag)::value;
 #pragma unroll 1
     for (int pg = 0; pg < kCE / 64; ++pg) {
       float psc[4];
@@ -1041,6 +1044,9 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
         }
       }
     }
+    };
+    if (qw + 15 < a.n_tok && entry_of(m0 + kCE - 1) < nvis_lo) tile_body(std::true_type{});
+    else tile_body(std::false_type{});
     if constexpr (!SAMPLE) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
