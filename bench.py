@@ -11,8 +11,9 @@ queries plus 4 csa_attend calls (one per layer). Inputs are seeded synthetic
 data resident in HBM before timing; steps rotate over 8 identical cache
 replicas so the 256 MB last-level cache cannot hold a step's working set.
 
-The timed steps are replays of one HIP graph per replica (the step's kernels
-captured once). Prints one JSON line: decode tokens/s, the indexer scan
+The timed steps are HIP graph replays (a graph holds one step on every
+replica, as a model's decode iteration holds several layer groups). Prints
+one JSON line: decode tokens/s, the indexer scan
 kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events around
 every scan launch of an eager pass over the same steps), and the CPU
 oracle's throughput on a bounded sample of the same step.
@@ -194,23 +195,7 @@ def hca_leg(seed, dev, steps=50):
     q_seq, q_pos = list(range(BATCH)), [CONTEXT - 1] * BATCH
     scale = 1.0 / math.sqrt(128)
     torch.cuda.synchronize()
-    graphs = []
-    cap = torch.cuda.Stream()
-    for c in caches:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            B.csa_attend_dense(c.handle, 0, q_seq, q_pos, q, scale, out, torch.cuda.current_stream())
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps * len(graphs)):
-        graphs[i % len(graphs)].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (steps * len(graphs))
+    us = graph_us([lambda s, c=c: B.csa_attend_dense(c.handle, 0, q_seq, q_pos, q, scale, out, s) for c in caches], steps)
     for c in caches:
         B.csa_profile_begin(c.handle, B.PROFILE_ATTEND)
     for i in range(len(caches)):
@@ -235,25 +220,22 @@ def hca_leg(seed, dev, steps=50):
 
 
 def graph_us(calls, steps, warmup=3):
-    """Mean microseconds per replay of one HIP graph per callable, replays
-    rotating over the callables (each callable enqueues on the stream it gets)."""
+    """Mean microseconds per call when one HIP graph holding every callable
+    once, in order, is replayed `steps` times (each callable enqueues on the
+    stream it gets; the callables are the replicas of one step)."""
     import torch
-    graphs = []
-    cap = torch.cuda.Stream()
-    for fn in calls:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for fn in calls:
             fn(torch.cuda.current_stream())
-        graphs.append(g)
-    for i in range(warmup * len(graphs)):
-        graphs[i % len(graphs)].replay()
+    for _ in range(warmup):
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    n = steps * len(graphs)
-    for i in range(n):
-        graphs[i % len(graphs)].replay()
+    for _ in range(steps):
+        g.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e6 / n
+    return (time.perf_counter() - t0) * 1e6 / (steps * len(calls))
 
 
 def kernel_us(caches, kind, fn, reps):
@@ -515,25 +497,36 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # one HIP graph per replica: the step's kernels are launched by replay, so
-    # host-side launch cost does not enter the timed region
-    graphs = []
+    # The step's kernels are launched by HIP graph replay, so host-side launch
+    # cost does not enter the timed region. One graph holds a step on every
+    # replica, in the way a model's decode iteration captures several layer
+    # groups in one graph; single-step graphs per replica cover a remainder.
+    def enqueue(r, s_):
+        c = caches[r]
+        B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, TOPK, topk[r], s_)
+        for l in range(LAYERS):
+            B.csa_attend(c.handle, l, q_seq, q_pos, qs[l], topk[r], TOPK, scale, outs[l], s_)
     cap = torch.cuda.Stream()
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all, stream=cap):
+        for r in range(len(caches)):
+            enqueue(r, torch.cuda.current_stream())
+    graphs = []
     for r in range(len(caches)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            c = caches[r]
-            s_ = torch.cuda.current_stream()
-            B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, TOPK, topk[r], s_)
-            for l in range(LAYERS):
-                B.csa_attend(c.handle, l, q_seq, q_pos, qs[l], topk[r], TOPK, scale, outs[l], s_)
+            enqueue(r, torch.cuda.current_stream())
         graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
+
+    def run_steps(n):
+        for _ in range(n // len(caches)):
+            g_all.replay()
+        for i in range(n % len(caches)):
+            graphs[i].replay()
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -592,7 +585,7 @@ def main():
     }
     if not args.no_hier:
         line["hierarchical"] = hier_leg(caches, qi, w, max(10, args.steps // 4), args.seed)
-    del caches, graphs
+    del caches, graphs, g_all
     torch.cuda.empty_cache()
     if not args.no_swa_fp8:
         line["swa_fp8"] = variant_leg(args.seed, dev, args.replicas, qi, w, qs, args.steps, kv="fp8", swa="fp8")
