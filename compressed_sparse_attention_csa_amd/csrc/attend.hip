@@ -12,10 +12,12 @@
 // being a run of blocks, and has HG waves (head groups). Each round it gathers
 // one block into LDS, K row-major and V transposed in the MFMA compute type
 // (fp8 codes convert exactly to bf16; page scales are applied to the logits
-// and probabilities): a block's rows move as 16-byte chunks, 16 consecutive
-// lanes per 256-byte row, and the next block is already in flight in
-// registers during this block's math. Each wave then runs, for its 16-head
-// tiles:
+// and probabilities): a block's rows move as 16-byte chunks, CPR consecutive
+// lanes per row, as raw buffer loads whose 32-bit offsets come from a per-key
+// table built once per split (a key that takes no part points past the end
+// of the buffer and reads zeros, so no lane branches), and the next block is
+// already in flight in registers during this block's math. Each wave then
+// runs, for its 16-head tiles:
 //   S^T[key][head] = K . Q^T  (keys as MFMA rows, heads as columns), so a lane
 //   holds one head and 4 keys per 16-key tile; after the online-softmax update
 //   those probabilities are already the A operand of O = P . V (heads as rows,
@@ -103,7 +105,20 @@ __device__ __forceinline__ void chunk_values(const uint4 &u, CT *dst, uint32_t g
   }
 }
 
-constexpr int32_t kMaskedRow = INT32_MIN;   // src_row of a key that takes no part
+// Gathers are buffer loads: a row's address is a 32-bit byte offset into its
+// pool (or ring) buffer, and a key that takes no part gets an offset past the
+// buffer's end, where the load returns zeros without touching memory. Buffers
+// hold at most kOobOffset bytes, so no in-row chunk offset wraps back in range.
+constexpr uint32_t kOobOffset = kAttMaxBufferBytes;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void *p, uint32_t bytes) {
+  // stride 0 (raw buffer: range check on the byte offset), 32-bit dword format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.f;             // log2 headroom of the lazily rescaled softmax
 
@@ -138,7 +153,9 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   constexpr int KV_LDS = (kKeyBlock * KS + (VROW ? kKeyBlock : kD) * VS) * static_cast<int>(sizeof(CT));
 
   __shared__ __align__(16) char kv_lds[KV_LDS];
-  __shared__ int32_t src_row[kAttMaxSplitKeys];   // >= 0 pool row; < 0: -(ring row) - 1; kMaskedRow
+  // byte offset of each key's row in the pool (Top-K blocks) or ring (window
+  // blocks) buffer; kOobOffset for a key that takes no part
+  __shared__ uint32_t src_off[kAttMaxSplitKeys];
   __shared__ uint8_t kvalid[kAttMaxSplitKeys];
   // per key of the block: logit = S * kmul + kbias (kmul = scale x page scale,
   // kbias = -inf for a masked key), probability weight vsc = value page scale
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     if (i >= n_keys) continue;
     const int b = b_begin + i / kKeyBlock, kk = i % kKeyBlock;
     int valid = 0;
-    int32_t row = 0;
+    uint32_t off = kOobOffset;
     if (b < a.n_sparse_blocks) {
       const int j = jv[u], pp = pv[u];
       if (j >= 0) {
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
           flag_error(a.err, ERR_TOPK);
         } else if (pp >= 0 && pp < a.pool_pages) {
           valid = 1;
-          row = pp * kPage + (j & 63);
+          off = static_cast<uint32_t>(pp * kPage + (j & 63)) * static_cast<uint32_t>(PRB);
         } else {
           flag_error(a.err, ERR_PAGE);
         }
@@ -205,145 +222,127 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       const int r = swa_lo + (b - a.n_sparse_blocks) * kKeyBlock + kk;
       if (r <= t) {
         valid = 1;
-        row = -(seq * a.R + r % a.R) - 1;
+        off = static_cast<uint32_t>(seq * a.R + r % a.R) * static_cast<uint32_t>(RRB);
       }
     }
-    src_row[i] = valid ? row : kMaskedRow;
+    src_off[i] = off;
     kvalid[i] = valid;
   }
   __syncthreads();
 
-  // ---------------- gather: slot s of block b = (K or V, key, 16-byte chunk)
-  // A masked slot's register is never written (a zero written beside an
-  // in-flight load would have to wait for it); vmask says which slots hold data.
-  uint4 raw[PREFETCH ? U : 1];
-  uint32_t graw[KV == DT_FP4 && PREFETCH ? U : 1];   // fp4: the chunk's two group-scale codes
-  uint32_t vmask = 0;
-  float ks_pref = 1.f, vs_pref = 1.f;   // page scales of key tid (tid < 64)
-  // slot s of a block with cpr (a power of two) chunks per row: (K or V, key, chunk)
-  auto slot_key = [](int s, int cpr) { return (s & (kKeyBlock * cpr - 1)) >> (31 - __builtin_clz(cpr)); };
-  // 16-byte chunk of slot s, for a block whose rows live at kbase / vbase with
-  // row_bytes per row (ring rows are stored as -(row) - 1)
-  auto slot_ptr = [](const char *kbase, const char *vbase, int64_t row_bytes, int s, int cpr, int32_t row) {
-    const int kv = s >= kKeyBlock * cpr;
-    const int64_t r = row >= 0 ? row : -static_cast<int64_t>(row) - 1;
-    return reinterpret_cast<const uint4 *>((kv ? vbase : kbase) + r * row_bytes) + (s & (cpr - 1));
-  };
-  // fp4 pool slot s of row `row`: its chunk's two group-scale codes (16-bit load)
-  auto slot_gscale = [&](int s, int32_t row) -> uint32_t {
-    const int kv = s >= kKeyBlock * CPR_P;
-    const uint8_t *g = (kv ? a.vbar_gs : a.kbar_gs) + static_cast<int64_t>(row) * (kD / kFp4Group);
-    return *reinterpret_cast<const uint16_t *>(g + 2 * (s & (CPR_P - 1)));
+  // ---------------- gather: slot u of a thread in a block whose rows have CPR
+  // 16-byte chunks is chunk (tid mod CPR) of key ((u NT + tid) mod 64 CPR) / CPR,
+  // of K for the first 64 CPR slots of the block and of V for the next; slots
+  // past 2 x 64 CPR are unused. Which slots are K, V or unused is known at
+  // compile time per u, and a K slot and its V slot share one row offset.
+  const __amdgpu_buffer_rsrc_t pool_k = buffer_of(a.kbar, a.pool_bytes), pool_v = buffer_of(a.vbar, a.pool_bytes);
+  const __amdgpu_buffer_rsrc_t ring_k = buffer_of(a.ring_k, a.ring_bytes), ring_v = buffer_of(a.ring_v, a.ring_bytes);
+  constexpr int UW = U < 8 ? U : 8;      // slots in registers at once
+  uint4 raw[UW];
+  uint32_t graw[KV == DT_FP4 ? UW : 1];  // fp4: the chunk's two group-scale codes
+  float ks_pref = 1.f, vs_pref = 1.f;   // page (or ring row) scales of key tid (tid < 64)
+  // the loads of slots [u0, u0 + UW) of block b (rows stored as SD) into v[], gs[]
+  auto gather = [&](auto sd_tag, int b, int u0, uint4 *v, uint32_t *gs) {
+    constexpr int SD = decltype(sd_tag)::value;
+    constexpr int CPR = row_bytes_of<SD>() / 16;
+    constexpr bool POOL_SD = SD == KV;
+    const bool pool = b < a.n_sparse_blocks;
+    const __amdgpu_buffer_rsrc_t rk = pool ? pool_k : ring_k, rv = pool ? pool_v : ring_v;
+    const uint32_t *offs = src_off + (b - b_begin) * kKeyBlock;
+    const uint32_t chunk_off = static_cast<uint32_t>(tid & (CPR - 1)) * 16u;
+#pragma unroll
+    for (int w = 0; w < UW; ++w) {
+      const int u = u0 + w;
+      if (u * NT >= 2 * kKeyBlock * CPR) break;
+      const bool is_v = u * NT >= kKeyBlock * CPR;
+      const int key = ((u * NT) % (kKeyBlock * CPR) + tid) / CPR;
+      const uint32_t row_off = offs[key];
+      v[w] = buffer_load16(is_v ? rv : rk, row_off + chunk_off);
+      if constexpr (KV == DT_FP4 && POOL_SD) {
+        // 8 scale bytes per fp4 row (64 B): two per 16-byte chunk
+        const uint8_t *gbase = is_v ? a.vbar_gs : a.kbar_gs;
+        const uint32_t goff = row_off >= kOobOffset ? kOobOffset : (row_off >> 3) + chunk_off / 8u;
+        gs[w] = __builtin_amdgcn_raw_buffer_load_b16(buffer_of(gbase, a.gs_bytes), goff, 0, 0);
+      }
+    }
   };
   auto load_scales = [&](int b) {
     ks_pref = vs_pref = 1.f;
     if (tid < kKeyBlock) {
-      const int i = (b - b_begin) * kKeyBlock + tid;
-      const int32_t row = src_row[i];
+      const uint32_t off = src_off[(b - b_begin) * kKeyBlock + tid];
       if constexpr (KV == DT_FP8) {
-        if (b < a.n_sparse_blocks && row != kMaskedRow) {   // page scales
-          ks_pref = a.kbar_scale[row >> 6];
-          vs_pref = a.vbar_scale[row >> 6];
+        if (b < a.n_sparse_blocks && off != kOobOffset) {   // page scales
+          const uint32_t page = off / static_cast<uint32_t>(PRB * kPage);
+          ks_pref = a.kbar_scale[page];
+          vs_pref = a.vbar_scale[page];
         }
       }
       if constexpr (RS == DT_FP8) {
-        if (b >= a.n_sparse_blocks && row != kMaskedRow) {  // ring row scales
-          ks_pref = a.ring_k_scale[-row - 1];
-          vs_pref = a.ring_v_scale[-row - 1];
+        if (b >= a.n_sparse_blocks && off != kOobOffset) {  // ring row scales
+          const uint32_t row = off / static_cast<uint32_t>(RRB);
+          ks_pref = a.ring_k_scale[row];
+          vs_pref = a.ring_v_scale[row];
         }
       }
     }
   };
-  // chunk -> compute type -> K row-major or V^T in LDS; SD is the storage type
-  // of the block's rows (pool or ring), so the element count is a constant
-  auto commit_chunk = [&](auto sd_tag, int s, const uint4 &u, uint32_t gsc) {
+  // slots [u0, u0 + UW) of a block (rows stored as SD) -> compute type -> K
+  // row-major and V row-major (bf16) or V^T (fp32) in LDS
+  auto commit = [&](auto sd_tag, int u0, const uint4 *v, const uint32_t *gs) {
     constexpr int SD = decltype(sd_tag)::value;
     constexpr int E = SD == DT_FP4 ? 32 : 16 / elem_bytes_of<SD>();
     constexpr int CPR = kD / E;
-    if (s >= 2 * kKeyBlock * CPR) return;
-    const int kv = s >= kKeyBlock * CPR;
-    const int L = s - kv * kKeyBlock * CPR;
-    const int key = L / CPR, d0 = (L % CPR) * E;
-    CT vals[E];
-    chunk_values<SD, CT>(u, vals, gsc);
-    if (kv == 0) {
-      CT *kd = Ks + key * KS + d0;
 #pragma unroll
-      for (int q = 0; q < E; ++q) kd[q] = vals[q];
-    } else if constexpr (VROW) {
-      CT *vd = Vt + key * VS + d0;
+    for (int w = 0; w < UW; ++w) {
+      const int u = u0 + w;
+      if (u * NT >= 2 * kKeyBlock * CPR) break;
+      const bool is_v = u * NT >= kKeyBlock * CPR;
+      const int key = ((u * NT) % (kKeyBlock * CPR) + tid) / CPR, d0 = (tid & (CPR - 1)) * E;
+      CT vals[E];
+      uint32_t gsc = 0;
+      if constexpr (SD == DT_FP4) gsc = gs[w];
+      chunk_values<SD, CT>(v[w], vals, gsc);
+      if (!is_v) {
+        CT *kd = Ks + key * KS + d0;
 #pragma unroll
-      for (int q = 0; q < E; ++q) vd[q] = vals[q];
-    } else {
-      CT *vd = Vt + d0 * VS + key;
+        for (int q = 0; q < E; ++q) kd[q] = vals[q];
+      } else if constexpr (VROW) {
+        CT *vd = Vt + key * VS + d0;
 #pragma unroll
-      for (int q = 0; q < E; ++q) vd[q * VS] = vals[q];
-    }
-  };
-  auto commit_slot = [&](int b, int s, const uint4 &u, uint32_t gsc) {
-    if constexpr (KV == RS) {
-      commit_chunk(std::integral_constant<int, KV>{}, s, u, gsc);
-    } else {
-      if (b < a.n_sparse_blocks) commit_chunk(std::integral_constant<int, KV>{}, s, u, gsc);
-      else commit_chunk(std::integral_constant<int, RS>{}, s, u, gsc);
+        for (int q = 0; q < E; ++q) vd[q] = vals[q];
+      } else {
+        CT *vd = Vt + d0 * VS + key;
+#pragma unroll
+        for (int q = 0; q < E; ++q) vd[q * VS] = vals[q];
+      }
     }
   };
   auto load_round = [&](int r) {
     const int b = b_begin + r;
+    if (b >= b_end) return;
     if constexpr (PREFETCH) {
-      vmask = 0;
-      if (b < b_end) {
-        const bool pool = b < a.n_sparse_blocks;
-        const int cpr = pool ? CPR_P : CPR_R;
-        const int nslot = 2 * kKeyBlock * cpr;
-        const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
-        const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
-        const int64_t row_bytes = pool ? PRB : RRB;
-        // every slot's row first (one LDS round trip), then every load
-        int32_t rows[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int s = tid + u * NT;
-          rows[u] = s < nslot ? src_row[(b - b_begin) * kKeyBlock + slot_key(s, cpr)] : kMaskedRow;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (rows[u] != kMaskedRow) {
-            raw[u] = *slot_ptr(kbase, vbase, row_bytes, tid + u * NT, cpr, rows[u]);
-            if constexpr (KV == DT_FP4) {
-              if (pool) graw[u] = slot_gscale(tid + u * NT, rows[u]);
-            }
-            vmask |= 1u << u;
-          }
-        }
-      }
+      if (b < a.n_sparse_blocks) gather(std::integral_constant<int, KV>{}, b, 0, raw, graw);
+      else gather(std::integral_constant<int, RS>{}, b, 0, raw, graw);
     }
-    if (b < b_end) load_scales(b);
+    load_scales(b);
   };
   auto commit_round = [&](int r) {
     const int b = b_begin + r;
     if constexpr (PREFETCH) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool on = (vmask >> u) & 1u;
-        uint32_t gsc = 0;
-        if constexpr (KV == DT_FP4) gsc = on ? graw[u] : 0u;
-        commit_slot(b, tid + u * NT, on ? raw[u] : make_uint4(0, 0, 0, 0), gsc);
-      }
+      if (b < a.n_sparse_blocks) commit(std::integral_constant<int, KV>{}, 0, raw, graw);
+      else commit(std::integral_constant<int, RS>{}, 0, raw, graw);
     } else {
-      const bool pool = b < a.n_sparse_blocks;
-      const int cpr = pool ? CPR_P : CPR_R;
-      const char *kbase = reinterpret_cast<const char *>(pool ? a.kbar : a.ring_k);
-      const char *vbase = reinterpret_cast<const char *>(pool ? a.vbar : a.ring_v);
-      const int64_t row_bytes = pool ? PRB : RRB;
-      for (int u = 0; u < U; ++u) {
-        const int s = tid + u * NT;
-        if (s >= 2 * kKeyBlock * cpr) break;
-        const int32_t row = src_row[(b - b_begin) * kKeyBlock + slot_key(s, cpr)];
-        uint32_t gsc = 0;
-        if constexpr (KV == DT_FP4) gsc = (pool && row != kMaskedRow) ? slot_gscale(s, row) : 0u;
-        commit_slot(b, s, row != kMaskedRow ? *slot_ptr(kbase, vbase, row_bytes, s, cpr, row) : make_uint4(0, 0, 0, 0), gsc);
-      }
+      // rows too wide to hold a block in registers (fp32): gather and commit
+      // UW slots at a time
+      auto slices = [&](auto sd_tag) {
+#pragma unroll
+        for (int u0 = 0; u0 < U; u0 += UW) {
+          gather(sd_tag, b, u0, raw, graw);
+          commit(sd_tag, u0, raw, graw);
+        }
+      };
+      if (b < a.n_sparse_blocks) slices(std::integral_constant<int, KV>{});
+      else slices(std::integral_constant<int, RS>{});
     }
     if (tid < kKeyBlock) {
       const bool valid = kvalid[(b - b_begin) * kKeyBlock + tid] != 0;

@@ -59,6 +59,19 @@ int idx_dt(const csa_config &c) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// bytes of one compressed K (or V) row, one window-ring row, and each layer's
+// K (or V) pool and ring
+uint64_t pool_row_bytes(const csa_config &c) {
+  return c.kv_dtype == CSA_FP4_E2M1 ? kD / 2 : static_cast<uint64_t>(kD) * dt_bytes(c.kv_dtype);
+}
+uint64_t ring_row_bytes(const csa_config &c) {
+  return c.swa_dtype == CSA_FP8_E4M3 ? kD : static_cast<uint64_t>(kD) * dt_bytes(c.act_dtype);
+}
+uint64_t pool_bytes_of(const csa_config &c) { return static_cast<uint64_t>(c.pool_pages) * kPage * pool_row_bytes(c); }
+uint64_t ring_bytes_of(const csa_config &c) {
+  return static_cast<uint64_t>(c.max_seqs) * static_cast<uint64_t>(c.ring_rows) * ring_row_bytes(c);
+}
+
 csa_status check_config(const csa_config *c) {
   if (!c) return fail(CSA_ERR_INVALID_ARG, "config is NULL");
   if (c->ratio < 1 || c->ratio > 256) return fail(CSA_ERR_UNSUPPORTED, "ratio %d outside [1, 256]", c->ratio);
@@ -87,6 +100,11 @@ csa_status check_config(const csa_config *c) {
   if (!ok) return fail(CSA_ERR_DTYPE, "unsupported (kv_dtype, act_dtype) = (%d, %d)", c->kv_dtype, c->act_dtype);
   if (c->swa_dtype != c->act_dtype && !(c->swa_dtype == CSA_FP8_E4M3 && c->act_dtype == CSA_BF16))
     return fail(CSA_ERR_DTYPE, "swa_dtype %d must be act_dtype, or FP8_E4M3 with BF16 activations", c->swa_dtype);
+  // attention gathers address each K/V pool and ring with 32-bit byte offsets
+  if (pool_bytes_of(*c) > kAttMaxBufferBytes || ring_bytes_of(*c) > kAttMaxBufferBytes)
+    return fail(CSA_ERR_UNSUPPORTED, "each K/V pool and ring must hold at most %u bytes (pool %llu, ring %llu)",
+                kAttMaxBufferBytes, static_cast<unsigned long long>(pool_bytes_of(*c)),
+                static_cast<unsigned long long>(ring_bytes_of(*c)));
   return CSA_OK;
 }
 
@@ -807,6 +825,9 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
   a.kbar_gs = h->buf.kbar_gscale[layer]; a.vbar_gs = h->buf.vbar_gscale[layer];
   a.ring_k = h->buf.ring_k[layer]; a.ring_v = h->buf.ring_v[layer];
   a.ring_k_scale = h->buf.ring_k_scale[layer]; a.ring_v_scale = h->buf.ring_v_scale[layer];
+  a.pool_bytes = static_cast<uint32_t>(pool_bytes_of(c));   // check_config bounds both by kAttMaxBufferBytes
+  a.ring_bytes = static_cast<uint32_t>(ring_bytes_of(c));
+  a.gs_bytes = kv == DT_FP4 ? static_cast<uint32_t>(static_cast<uint64_t>(c.pool_pages) * kPage * (kD / kFp4Group)) : 0u;
   const bool ring8 = c.swa_dtype == CSA_FP8_E4M3;
   a.block_table = h->buf.block_table;
   a.err = h->err;

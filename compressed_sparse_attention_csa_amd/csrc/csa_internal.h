@@ -166,6 +166,7 @@ struct AttQuery {
   int32_t seq, pos, swa;   // swa: replay start s of the window branch
 };
 
+constexpr uint32_t kAttMaxBufferBytes = 0xfffff000u;   // largest K/V pool or ring an attention gather addresses
 constexpr int kAttMaxSplitKeys = 2304;   // keys one workgroup resolves up front (36 blocks)
 constexpr int kAttKeyStreams = 1;        // 64-key blocks a decode workgroup processes per round
 constexpr int kAttChunkKeyStreams = 1;   // the same for a prefill chunk (one workgroup per query)
@@ -180,6 +181,7 @@ struct AttendArgs {
   const uint8_t *kbar_gs, *vbar_gs;         // fp4 group scales [pool_pages][64][D/16]
   const void *ring_k, *ring_v;
   const float *ring_k_scale, *ring_v_scale;   // per-row scales of an fp8 ring
+  uint32_t pool_bytes, ring_bytes, gs_bytes;  // bytes of each K (= V) pool, ring and fp4 group-scale pool
   const int32_t *block_table;
   float *part_o;            // [n_q][n_splits][H][D] unnormalised partial outputs
   float *part_ml;           // [n_q][n_splits][2][H] running max and sum

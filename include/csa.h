@@ -87,7 +87,10 @@ typedef struct csa_config {
   int32_t n_layers;          /* 1..CSA_MAX_LAYERS; layer 0 is the indexing (Full) layer */
   int32_t max_seqs;          /* sequences addressable through the block table */
   int32_t max_pages_per_seq; /* block-table row length */
-  int32_t pool_pages;        /* physical pages in every pool */
+  int32_t pool_pages;        /* physical pages in every pool. Each layer's K (or V) pool,
+                                pool_pages * 64 rows, and its window ring, max_seqs * R rows,
+                                must each fit in 0xfffff000 bytes (attention addresses
+                                them with 32-bit offsets): CSA_ERR_UNSUPPORTED otherwise */
   int32_t kv_dtype;          /* csa_dtype of compressed entries and indexer keys (FP4_E2M1: see above) */
   int32_t act_dtype;         /* csa_dtype of raw rows, queries and outputs (F32 or BF16) */
   int32_t swa_dtype;         /* csa_dtype of the window ring: act_dtype, or CSA_FP8_E4M3 with

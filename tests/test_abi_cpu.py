@@ -94,6 +94,22 @@ def test_bad_configs_rejected(field, value, status):
     assert B.csa_workspace_size(cfg, 8, 512) == 0
 
 
+def test_pool_and_ring_byte_limits():
+    """Attention addresses each K/V pool and window ring with 32-bit byte
+    offsets: configs whose pool or ring passes 0xfffff000 bytes are refused."""
+    lim = 0xFFFFF000
+    fits = _spec(pool_pages=lim // (64 * 128))           # fp8 rows of 128 B: just inside
+    assert B.csa_buffer_sizes_for(fits).kv_pool <= lim
+    for cfg in (_spec(pool_pages=lim // (64 * 128) + 1),  # one page more
+                _spec(kv_dtype=B.CSA_BF16, pool_pages=lim // (64 * 256) + 1),
+                _spec(max_seqs=lim // (128 * 2 * 128) + 1, max_pages_per_seq=1, pool_pages=64)):
+        with pytest.raises(B.CsaError) as e:
+            B.csa_buffer_sizes_for(cfg)
+        assert e.value.status == 5   # CSA_ERR_UNSUPPORTED
+    # an fp4 pool of the same page count is half the bytes of an fp8 one
+    assert B.csa_buffer_sizes_for(_spec(kv_dtype=B.CSA_FP4_E2M1, pool_pages=lim // (64 * 128) + 1)).kv_pool <= lim
+
+
 def test_create_requires_buffers():
     cfg = _spec()
     b = B.Buffers()
