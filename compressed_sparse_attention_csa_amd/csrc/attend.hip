@@ -140,9 +140,11 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   constexpr bool VSCALE = KV == DT_FP8 || RS == DT_FP8;   // value rows carry a page or row scale
   constexpr int64_t PRB = row_bytes_of<KV>(), RRB = row_bytes_of<RS>();   // pool / ring row bytes
   constexpr int KS = kD + kpad<CT>();          // K row stride (elements)
-  // bf16: V row-major like K, read as transposed MFMA fragments; fp32: V^T
+  // bf16: V row-major like K, read as transposed MFMA fragments; fp32: V^T.
+  // A transposed read covers 4 rows x 32 bytes per 16 lanes, so bf16 V rows are
+  // padded by 32 bytes (8 banks) to keep those rows on disjoint banks.
   constexpr bool VROW = sizeof(CT) == 2;
-  constexpr int VS = VROW ? KS : kKeyBlock + kpad<CT>();   // V (or V^T) row stride (elements)
+  constexpr int VS = VROW ? kD + 16 : kKeyBlock + kpad<CT>();   // V (or V^T) row stride (elements)
   // a block's K and V rows move as 16-byte chunks, 16 consecutive lanes per
   // 256-byte row, so every wave load covers whole rows
   constexpr int CPR_P = row_bytes_of<KV>() / 16, CPR_R = row_bytes_of<RS>() / 16;   // chunks per pool / ring row
@@ -158,10 +160,13 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   __shared__ uint32_t src_off[kAttMaxSplitKeys];
   __shared__ uint8_t kvalid[kAttMaxSplitKeys];
   // per key of the block: logit = S * kmul + kbias (kmul = scale x page scale,
-  // kbias = -inf for a masked key), probability weight vsc = value page scale
-  __shared__ __align__(16) float kmul[kKeyBlock];
-  __shared__ __align__(16) float kbias[kKeyBlock];
-  __shared__ __align__(16) float vsc[kKeyBlock];
+  // kbias = -inf for a masked key), probability weight vsc = value page scale.
+  // Without page or row scales kmul is one constant and the block's masked
+  // keys are the zero bits of kmask.
+  __shared__ __align__(16) float kmul[VSCALE ? kKeyBlock : 1];
+  __shared__ __align__(16) float kbias[VSCALE ? kKeyBlock : 1];
+  __shared__ __align__(16) float vsc[VSCALE ? kKeyBlock : 1];
+  __shared__ uint64_t kmask;
   CT *Ks = reinterpret_cast<CT *>(kv_lds);                       // [64][KS]
   CT *Vt = Ks + kKeyBlock * KS;                                  // [64][VS] (bf16) or [D][VS]
 
@@ -344,11 +349,16 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       if (b < a.n_sparse_blocks) slices(std::integral_constant<int, KV>{});
       else slices(std::integral_constant<int, RS>{});
     }
-    if (tid < kKeyBlock) {
+    if (tid < kKeyBlock) {   // wave 0
       const bool valid = kvalid[(b - b_begin) * kKeyBlock + tid] != 0;
-      kmul[tid] = valid ? a.scale * kLog2e * ks_pref : 0.f;   // logits in log2 units
-      kbias[tid] = valid ? 0.f : -INFINITY;
-      vsc[tid] = vs_pref;
+      if constexpr (VSCALE) {
+        kmul[tid] = valid ? a.scale * kLog2e * ks_pref : 0.f;   // logits in log2 units
+        kbias[tid] = valid ? 0.f : -INFINITY;
+        vsc[tid] = vs_pref;
+      } else {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+        if (tid == 0) kmask = m;
+      }
     }
   };
 
@@ -402,10 +412,28 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       }
       // per-key factors of the lane's keys 16*kt + 4*g + v, four at a time
       float4 km[4], kbi[4];
+      if constexpr (VSCALE) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        km[kt] = *reinterpret_cast<const float4 *>(&kmul[16 * kt + 4 * g]);
-        kbi[kt] = *reinterpret_cast<const float4 *>(&kbias[16 * kt + 4 * g]);
+        for (int kt = 0; kt < 4; ++kt) {
+          km[kt] = *reinterpret_cast<const float4 *>(&kmul[16 * kt + 4 * g]);
+          kbi[kt] = *reinterpret_cast<const float4 *>(&kbias[16 * kt + 4 * g]);
+        }
+      } else {
+        const float c = a.scale * kLog2e;   // logits in log2 units
+        const uint64_t mk = kmask;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          km[kt] = make_float4(c, c, c, c);
+          kbi[kt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (mk != ~0ull) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const uint32_t nib = static_cast<uint32_t>(mk >> (16 * kt + 4 * g)) & 0xfu;
+            kbi[kt] = make_float4((nib & 1u) ? 0.f : -INFINITY, (nib & 2u) ? 0.f : -INFINITY,
+                                  (nib & 4u) ? 0.f : -INFINITY, (nib & 8u) ? 0.f : -INFINITY);
+          }
+        }
       }
       // logits and online softmax (lane's head = col; keys 16*kt + 4*g + v)
       float x[4][4];
@@ -466,7 +494,8 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       float4 vs4[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        vs4[kt] = VSCALE ? *reinterpret_cast<const float4 *>(&vsc[16 * kt + 4 * g]) : make_float4(1.f, 1.f, 1.f, 1.f);
+        if constexpr (VSCALE) vs4[kt] = *reinterpret_cast<const float4 *>(&vsc[16 * kt + 4 * g]);
+        else vs4[kt] = make_float4(1.f, 1.f, 1.f, 1.f);
       Frag<CT> vfb[2];
       vfb[0] = load_vf(0, 0);
 #pragma unroll
