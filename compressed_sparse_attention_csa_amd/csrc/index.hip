@@ -21,7 +21,7 @@
 //            (score bits, ~index), so ties go to the lower index; bitonic sort
 //            of the chosen indices; -1 padding.
 // Prefill chunk (queries of one sequence at consecutive positions):
-//   chunk scan   - MFMA GEMM tile of 64 queries x 256 entries, with (query,
+//   chunk scan   - MFMA GEMM tile of 32 queries x 256 entries, with (query,
 //                  head) pairs as the 16 rows of each tile, so every lane's 4
 //                  accumulators are the 4 heads of one (query, entry) score.
 //   chunk select - per query: tau from its group maxima, filter, exact select.
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
 // ------------------------------------------------------------------ chunk (prefill) index
 //
 // Queries of one sequence at consecutive positions share the indexer keys, so
-// scores are an MFMA GEMM: tiles of 64 queries x 256 entries, the 16 rows of
+// scores are an MFMA GEMM: tiles of 32 queries x 256 entries, the 16 rows of
 // each MFMA tile being 4 queries x 4 indexer heads, so each lane's 4
 // accumulators are the 4 heads of one (query, entry) pair.
 // The full score matrix is never written. A sample GEMM over every 16th entry
@@ -847,7 +847,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
 // the row and selects exactly), finds the exact k-th key by binning plus an
 // exact rank inside one bin, and orders the output with an LDS bitmap.
 
-constexpr int kCQ = 64;     // queries per tile
+// 4 queries per MFMA row tile, kMT row tiles per wave, 4 waves: 32 queries per
+// workgroup keeps the wave at 3 per SIMD (64 would need 2 more row tiles of
+// accumulators and query fragments, leaving room for 2)
+constexpr int kMT = 2;
+constexpr int kCQ = 16 * kMT;   // queries per tile
 constexpr int kCE = 256;    // entries per tile
 constexpr int kLdsRow = kDI + 8;
 constexpr int kWgCand = kChunkTileCand;
@@ -884,7 +888,7 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
   if (et_end <= et_begin) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, col = lane & 15;
-  const int qw = q0 + 16 * w;   // the wave's first query
+  const int qw = q0 + 4 * kMT * w;   // the wave's first query
   const char *kbase = reinterpret_cast<const char *>(a.kidx);
 
   // physical page of every page the walked tiles touch (pages are contiguous
@@ -896,10 +900,10 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
   }
 
   // A operands: (query, head) pairs as rows: row = 4*q + h
-  Frag<CT> qa[4][2];
-  float wq[4][4], tq[4];
+  Frag<CT> qa[kMT][2];
+  float wq[kMT][4], tq[kMT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < kMT; ++mt) {
     const int qq = qw + 4 * mt + (col >> 2), hh = col & 3;
     qa[mt][0] = qa[mt][1] = zero_frag<CT>();
     if (qq < a.n_tok && hh < a.h_i) {
@@ -914,10 +918,10 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
     if constexpr (!SAMPLE) tq[mt] = qo < a.n_tok ? a.tau[qo] : INFINITY;
   }
   // visibility of each of the lane's queries, and of the wave's first (smallest) one
-  int nvis[4];
-  bool qok[4];
+  int nvis[kMT];
+  bool qok[kMT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < kMT; ++mt) {
     const int qo = qw + 4 * mt + g;
     qok[mt] = qo < a.n_tok;
     nvis[mt] = (a.pos0 + qo + 1) / a.r;
@@ -977,7 +981,7 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
 
     // candidates of (query, this tile) so far; every lane of a 16-lane group
     // scores the same query, so the group's ballot orders its slots by entry
-    int run[4] = {0, 0, 0, 0};
+    int run[kMT] = {};
     // every (query, entry) pair of the wave visible in this tile: skip the per-score test
     // (the tile's code comes in two copies: without any visibility test for
     // the common fully visible tile, and with it)
@@ -988,9 +992,9 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
       float psc[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) psc[nt] = KV == DT_FP8 ? rsc[pg * 64 + nt * 16 + col] : 1.f;
-      f32x4_t acc[4][4];
+      f32x4_t acc[kMT][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1004,13 +1008,13 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
           else kb[c] = LoadFrag<DT_BF16, __bf16>::load(src);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < kMT; ++mt) {
           acc[mt][nt] = mma(qa[mt][0], kb[0], acc[mt][nt]);
           acc[mt][nt] = mma(qa[mt][1], kb[1], acc[mt][nt]);
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < kMT; ++mt) {
         const int qo = qw + 4 * mt + g;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -1045,11 +1049,11 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
       }
     }
     };
-    if (qw + 15 < a.n_tok && entry_of(m0 + kCE - 1) < nvis_lo) tile_body(std::true_type{});
+    if (qw + 4 * kMT - 1 < a.n_tok && entry_of(m0 + kCE - 1) < nvis_lo) tile_body(std::true_type{});
     else tile_body(std::false_type{});
     if constexpr (!SAMPLE) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < kMT; ++mt) {
         const int qo = qw + 4 * mt + g;
         if (col == 0 && qo < a.n_tok) a.cnt[static_cast<int64_t>(qo) * a.n_etiles + et] = run[mt];
       }
