@@ -201,6 +201,27 @@ template <> struct Elem<DT_BF16> {
 
 // ------------------------------------------------------------------ reductions
 
+// Lane exchange inside each row of 16 lanes by DPP: a register-to-register
+// move, where __shfl_xor would go through the LDS crossbar (ds_bpermute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppSwap1 = 0xb1;        // quad_perm [1,0,3,2]: lane i <- i ^ 1
+constexpr int kDppSwap2 = 0x4e;        // quad_perm [2,3,0,1]: lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i of each 8 <- 7 - i (the other quad)
+constexpr int kDppRowMirror = 0x140;   // lane i of each 16 <- 15 - i (the other 8)
+
+// Max over the aligned group of n lanes holding this lane, n in {1, 2, 4, 8,
+// 16}; n is the same on every lane, and every lane of the wave is active.
+__device__ __forceinline__ float group_max(float v, int n) {
+  if (n > 1) v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  if (n > 2) v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  if (n > 4) v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  if (n > 8) v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -533,18 +533,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
         if (g == 0 && e < N) Srow[e] = s;
         if (a.B) {   // maxima of aligned 8-entry blocks (candidate pool)
           float m8 = e < N ? s : -INFINITY;
-#pragma unroll
-          for (int o = 1; o < kPoolBlock; o <<= 1) m8 = fmaxf(m8, __shfl_xor(m8, o, 64));
+          m8 = group_max(m8, kPoolBlock);
           if (g == 0 && (col & (kPoolBlock - 1)) == 0 && e < N) a.B[static_cast<int64_t>(qi) * a.s_stride + (e >> 3)] = m8;
         }
         // group maxima: entries past N do not take part
         float m = e < N ? s : -INFINITY;
         if (G <= 16) {
-          for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          m = group_max(m, G);
           if (g == 0 && (col & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
         } else {
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          m = group_max(m, 16);
           run = fmaxf(run, m);
           if (!cross && ((((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N))) {
             if (lane == 0) Mrow[e_tile >> glog2] = run;
@@ -829,7 +827,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
     const int p = p_tile + col;
     if (g == 0 && p < V) Srow[p] = s;
     float m = p < V ? s : -INFINITY;
-    for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = group_max(m, G);
     if (g == 0 && (col & (G - 1)) == 0 && p < V) Mrow[p >> glog2] = m;
   }
 }
@@ -1028,8 +1026,7 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
           if constexpr (POOL) {
             // the 8 lanes of an aligned block hold consecutive entries of one query
             float m8 = vis ? s : -INFINITY;
-#pragma unroll
-            for (int o = 1; o < kPoolBlock; o <<= 1) m8 = fmaxf(m8, __shfl_xor(m8, o, 64));
+            m8 = group_max(m8, kPoolBlock);
             if ((col & (kPoolBlock - 1)) == 0 && qok[mt] && e < nvis[mt])
               a.bmax[static_cast<int64_t>(qo) * a.bm_stride + (e >> 3)] = m8;
           }
