@@ -212,6 +212,20 @@ constexpr int kDppSwap2 = 0x4e;        // quad_perm [2,3,0,1]: lane i <- i ^ 2
 constexpr int kDppHalfMirror = 0x141;  // lane i of each 8 <- 7 - i (the other quad)
 constexpr int kDppRowMirror = 0x140;   // lane i of each 16 <- 15 - i (the other 8)
 
+// Inclusive prefix sum over the 64 lanes in lane order (every lane active):
+// shifts by 1, 2, 4 and 8 inside each row of 16 (a lane past its row's start
+// adds 0), then row 0's total into row 1 and row 2's into row 3, then rows 0-1's
+// total into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // Max over the aligned group of n lanes holding this lane, n in {1, 2, 4, 8,
 // 16}; n is the same on every lane, and every lane of the wave is active.
 __device__ __forceinline__ float group_max(float v, int n) {
@@ -222,10 +236,23 @@ __device__ __forceinline__ float group_max(float v, int n) {
   return v;
 }
 
+// Max (min) over the 64 lanes, on every lane (every lane active): each row
+// of 16 by DPP, then the four row results read as scalars.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = group_max(v, 16);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = -group_max(-v, 16);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fminf(fminf(r0, r1), fminf(r2, r3));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

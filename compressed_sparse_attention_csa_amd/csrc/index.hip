@@ -65,11 +65,7 @@ __device__ uint64_t kth_largest_u64(Get get, int n, int k, int *hist, int *sh) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; s += c[j]; }
       int incl = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
+      incl = wave_incl_sum(incl);
       const int excl = incl - s;
       if (excl < rem && rem <= incl) {
         int cum = excl;
@@ -128,8 +124,7 @@ __device__ __forceinline__ float block_reduce_max(float v, float *red) {
   return r;
 }
 __device__ __forceinline__ float block_reduce_min(float v, float *red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  v = wave_min(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -140,11 +135,8 @@ __device__ __forceinline__ float block_reduce_min(float v, float *red) {
 
 // Block-wide min and max in one exchange (red holds >= 2 x waves floats).
 __device__ __forceinline__ void block_reduce_minmax(float &lo, float &hi, float *red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lo = fminf(lo, __shfl_xor(lo, o, 64));
-    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
-  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
   const int nw = blockDim.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = lo; red[nw + (threadIdx.x >> 6)] = hi; }
@@ -190,11 +182,7 @@ __device__ float tau_lower_bound(Get get, int n, int k, int *hist, float *red, i
   // block-wide inclusive scan of tot in thread order
   int incl = owner ? tot : 0;
   const int lane = t & 63, w = t >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  incl = wave_incl_sum(incl);
   __shared__ int wsum[16];
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
@@ -334,11 +322,7 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
     tot += cnt[j];
   }
   int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  incl = wave_incl_sum(incl);
   __shared__ int wsum2[16];
   if (lane == 63) wsum2[w] = incl;
   __syncthreads();
@@ -377,11 +361,7 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   int mine = 0;
   for (int i = i0; i < i1; ++i) mine += cand_key[i] >= kth;
   int inc2 = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc2, o, 64);
-    if (lane >= o) inc2 += y;
-  }
+  inc2 = wave_incl_sum(inc2);
   __syncthreads();
   if (lane == 63) wsum2[w] = inc2;
   __syncthreads();
@@ -403,11 +383,7 @@ __device__ void block_prefix_sum(int *arr, int n, int *wsum) {
   int mine = 0;
   for (int i = i0; i < i1; ++i) mine += arr[i];
   int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  incl = wave_incl_sum(incl);
   __syncthreads();
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
@@ -628,11 +604,7 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
 #pragma unroll
   for (int u = 0; u < kPer; ++u) mine += (t0 + u < e_end && sv[u] >= tau) ? 1 : 0;
   int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  incl = wave_incl_sum(incl);
   if (lane == 63) wcnt[w] = incl;
   __syncthreads();
   int pos = incl - mine;
