@@ -445,8 +445,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
           x[kt][v] = fmaf(S[kt][v], f4_at(km[kt], v), f4_at(kbi[kt], v));
           bm = fmaxf(bm, x[kt][v]);
         }
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = max_xor32(max_xor16(bm));
       // Lazy rescaling: O and l stay relative to the reference max m_run, which
       // moves only when a head's block max exceeds it by more than kRescale
       // (probabilities stay <= 2^kRescale); the wave rescales all its heads then.
@@ -521,8 +520,7 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   float Lh[NTW][4], Mh[NTW][4];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    float l_tot = l_run[j] + __shfl_xor(l_run[j], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = sum_xor32(sum_xor16(l_run[j]));
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       Mh[j][v] = __shfl(m_run[j], 4 * g + v, 64);

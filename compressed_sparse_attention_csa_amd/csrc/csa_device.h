@@ -236,6 +236,26 @@ __device__ __forceinline__ float group_max(float v, int n) {
   return v;
 }
 
+// Lane i combined with lane i ^ 16 (i ^ 32), on every lane: the permlane swaps
+// exchange rows 0 <-> 1 and 2 <-> 3 (halves 0 <-> 1) between two copies of v,
+// and the combine is symmetric, so either copy may come first.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Max (min) over the 64 lanes, on every lane (every lane active): each row
 // of 16 by DPP, then the four row results read as scalars.
 __device__ __forceinline__ float wave_max(float v) {
