@@ -8,8 +8,8 @@
 // indexer K projected from the main-KV entry) and "Causal Encoder-Decoder" >
 // "One hidden state feeds the decoder" (entries C and compression weights Z).
 //
-// One workgroup owns one (sequence, page): it computes the page's new entries
-// in fp32, then writes them. For FP8 pages it also re-quantises the page's
+// One workgroup owns one (sequence, page) - for fp32 and bf16 pages, one of
+// its 8-slot parts: it computes the new entries in fp32, then writes them. For FP8 pages it also re-quantises the page's
 // earlier entries (kept in fp32 staging) under the page's new amax, so the
 // bytes of a page never depend on how its entries were appended.
 #include "csa_device.h"
@@ -49,16 +49,21 @@ __device__ __forceinline__ void store1(void *base, int64_t elem, float a) {
 }
 
 constexpr int kThreads = 256;
-constexpr int kSlotsPerThread = kPage / (kThreads / 64);   // 16
+constexpr int kPageParts = 8;   // workgroups per fp32 / bf16 page
 
 template <int ACT, int KV>
 __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const CompressArgs a) {
-  __shared__ float kb_s[kPage][kD];
+  // fp32 / bf16 pages: each page is split over kPageParts workgroups of SPW
+  // slots; fp8 and fp4 pages need a page-wide amax and stay whole
+  constexpr int PARTS = (KV == DT_F32 || KV == DT_BF16) ? kPageParts : 1;
+  constexpr int SPW = kPage / PARTS, SPT = SPW / (kThreads / 64);   // slots per workgroup / thread
+  __shared__ float kb_s[SPW][kD];
   __shared__ float p_s[kD][kDI];   // indexer projection, staged once
   __shared__ float red[16];
 
   // ---- which (sequence, page) this workgroup owns
-  int wg = blockIdx.x, item = 0, acc = 0;
+  int wg = blockIdx.x / PARTS, item = 0, acc = 0;
+  const int slot0 = (blockIdx.x % PARTS) * SPW;   // this workgroup's first slot of the page
   for (; item < a.n_items - 1; ++item) {
     if (wg < acc + a.it[item].n_pages) break;
     acc += a.it[item].n_pages;
@@ -88,10 +93,10 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     for (int u = 0; u < kD * kDI / 4 / kThreads; ++u) reinterpret_cast<float4 *>(&p_s[0][0])[u * kThreads + t] = tmp[u];
   }
 
-  float kk[kSlotsPerThread][2], vv[kSlotsPerThread][2];
+  float kk[SPT][2], vv[SPT][2];
 #pragma unroll
-  for (int m = 0; m < kSlotsPerThread; ++m) {
-    const int slot = eb + 4 * m, e = pstart + slot;
+  for (int m = 0; m < SPT; ++m) {
+    const int slot = slot0 + eb + 4 * m, e = pstart + slot;
     float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
     if (e >= e0 && e < e1) {
       // gated pooling over rows [e*r, e*r + r): softmax of the gate per channel
@@ -136,27 +141,27 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     kk[m][0] = k0; kk[m][1] = k1;
     vv[m][0] = v0; vv[m][1] = v1;
     if (a.write_idx) {
-      kb_s[slot][d0] = k0;
-      kb_s[slot][d0 + 1] = k1;
+      kb_s[slot - slot0][d0] = k0;
+      kb_s[slot - slot0][d0 + 1] = k1;
     }
   }
 
   // ---- indexer key: KI = Kbar @ P (fp32, before any rounding); thread owns column c
   const int c = dp;
-  float ki[kSlotsPerThread];
+  float ki[SPT];
 #pragma unroll
-  for (int m = 0; m < kSlotsPerThread; ++m) ki[m] = 0.f;
+  for (int m = 0; m < SPT; ++m) ki[m] = 0.f;
   if (a.write_idx) {
     __syncthreads();
     for (int d = 0; d < kD; ++d) {
       const float p = p_s[d][c];
 #pragma unroll
-      for (int m = 0; m < kSlotsPerThread; ++m) ki[m] += kb_s[eb + 4 * m][d] * p;
+      for (int m = 0; m < SPT; ++m) ki[m] += kb_s[eb + 4 * m][d] * p;
     }
     if constexpr (KV == DT_FP8 || KV == DT_FP4) {   // fp8 indexer keys
 #pragma unroll
-      for (int m = 0; m < kSlotsPerThread; ++m) {
-        const int slot = eb + 4 * m, e = pstart + slot;
+      for (int m = 0; m < SPT; ++m) {
+        const int slot = slot0 + eb + 4 * m, e = pstart + slot;
         if (slot < filled && e < e0) ki[m] = a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot) * kDI + c];
       }
     }
@@ -173,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     uint8_t *kg = a.kbar_gs + static_cast<int64_t>(pp) * kPage * (kD / kFp4Group);
     uint8_t *vg = a.vbar_gs + static_cast<int64_t>(pp) * kPage * (kD / kFp4Group);
 #pragma unroll
-    for (int m = 0; m < kSlotsPerThread; ++m) {
-      const int slot = eb + 4 * m, e = pstart + slot;
+    for (int m = 0; m < SPT; ++m) {
+      const int slot = slot0 + eb + 4 * m, e = pstart + slot;
       float mk = fmaxf(fabsf(kk[m][0]), fabsf(kk[m][1]));
       float mv = fmaxf(fabsf(vv[m][0]), fabsf(vv[m][1]));
 #pragma unroll
@@ -199,31 +204,31 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     // ---- FP8 indexer keys: one scale per page, amax over the filled slots
     float ai = 0.f;
 #pragma unroll
-    for (int m = 0; m < kSlotsPerThread; ++m)
-      if (eb + 4 * m < filled) ai = fmaxf(ai, fabsf(ki[m]));
+    for (int m = 0; m < SPT; ++m)
+      if (slot0 + eb + 4 * m < filled) ai = fmaxf(ai, fabsf(ki[m]));
     ai = block_max(ai, red + 8);
     const float si = ai > 0.f ? ai / 448.0f : 1.0f;
     if (page_ok) {
       uint8_t *ip = reinterpret_cast<uint8_t *>(a.kidx) + ki_page;
 #pragma unroll
-      for (int m = 0; m < kSlotsPerThread; ++m) {
-        const int slot = eb + 4 * m;
+      for (int m = 0; m < SPT; ++m) {
+        const int slot = slot0 + eb + 4 * m;
         if (slot < filled) ip[slot * kDI + c] = static_cast<uint8_t>(f32_to_e4m3(ki[m] / si));
       }
       if (threadIdx.x == 0) a.kidx_scale[pp] = si;
     }
     if (filled < kPage) {
 #pragma unroll
-      for (int m = 0; m < kSlotsPerThread; ++m) {
-        const int slot = eb + 4 * m, e = pstart + slot;
+      for (int m = 0; m < SPT; ++m) {
+        const int slot = slot0 + eb + 4 * m, e = pstart + slot;
         if (e >= e0 && e < e1) a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot) * kDI + c] = ki[m];
       }
     }
   } else if constexpr (KV != DT_FP8) {
     if (!page_ok) return;
 #pragma unroll
-    for (int m = 0; m < kSlotsPerThread; ++m) {
-      const int slot = eb + 4 * m, e = pstart + slot;
+    for (int m = 0; m < SPT; ++m) {
+      const int slot = slot0 + eb + 4 * m, e = pstart + slot;
       if (e >= e0 && e < e1) {
         store2<KV>(a.kbar, kv_page + slot * kD + d0, kk[m][0], kk[m][1]);
         store2<KV>(a.vbar, kv_page + slot * kD + d0, vv[m][0], vv[m][1]);
@@ -234,8 +239,8 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     // ---- FP8: one scale per page and stream, amax over the filled slots
     float ak = 0.f, av = 0.f, ai = 0.f;
 #pragma unroll
-    for (int m = 0; m < kSlotsPerThread; ++m) {
-      if (eb + 4 * m < filled) {
+    for (int m = 0; m < SPT; ++m) {
+      if (slot0 + eb + 4 * m < filled) {
         ak = fmaxf(ak, fmaxf(fabsf(kk[m][0]), fabsf(kk[m][1])));
         av = fmaxf(av, fmaxf(fabsf(vv[m][0]), fabsf(vv[m][1])));
         ai = fmaxf(ai, fabsf(ki[m]));
@@ -253,8 +258,8 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
       uint8_t *vp = reinterpret_cast<uint8_t *>(a.vbar) + kv_page;
       uint8_t *ip = reinterpret_cast<uint8_t *>(a.kidx) + ki_page;
 #pragma unroll
-      for (int m = 0; m < kSlotsPerThread; ++m) {
-        const int slot = eb + 4 * m;
+      for (int m = 0; m < SPT; ++m) {
+        const int slot = slot0 + eb + 4 * m;
         if (slot < filled) {
           const uint32_t ck = f32_to_e4m3(kk[m][0] / sk) | (f32_to_e4m3(kk[m][1] / sk) << 8);
           const uint32_t cv = f32_to_e4m3(vv[m][0] / sv) | (f32_to_e4m3(vv[m][1] / sv) << 8);
@@ -271,8 +276,8 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     }
     if (open_after) {
 #pragma unroll
-      for (int m = 0; m < kSlotsPerThread; ++m) {
-        const int slot = eb + 4 * m, e = pstart + slot;
+      for (int m = 0; m < SPT; ++m) {
+        const int slot = slot0 + eb + 4 * m, e = pstart + slot;
         if (e >= e0 && e < e1) {
           const int64_t so = (static_cast<int64_t>(seq) * kPage + slot) * kD + d0;
           *reinterpret_cast<float2 *>(a.kbar_stage + so) = make_float2(kk[m][0], kk[m][1]);
@@ -373,9 +378,9 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
 void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s) {
   if (n_wg <= 0) return;
   if (kv == DT_F32 && act == DT_F32)
-    hipLaunchKernelGGL((compress_pages_kernel<DT_F32, DT_F32>), dim3(n_wg), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((compress_pages_kernel<DT_F32, DT_F32>), dim3(n_wg * kPageParts), dim3(kThreads), 0, s, a);
   else if (kv == DT_BF16 && act == DT_BF16)
-    hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_BF16>), dim3(n_wg), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_BF16>), dim3(n_wg * kPageParts), dim3(kThreads), 0, s, a);
   else if (kv == DT_FP8 && act == DT_BF16)
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(kThreads), 0, s, a);
   else if (kv == DT_FP4 && act == DT_BF16)
