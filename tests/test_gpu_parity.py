@@ -724,6 +724,13 @@ def test_hca_many_splits():
     _hca_case("bf16", "bf16", lens=[16 * 4096, 16 * 4000 + 5], r=16, W=128, H=16)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_hca_more_blocks_than_splits(kv):
+    """12,000 entries (188 blocks) for one query: more blocks than a query may
+    be split into, so every workgroup walks several blocks in sequence."""
+    _hca_case(kv, "bf16", lens=[4 * 12000 + 1, 4 * 2500], r=4, W=128, H=16)
+
+
 @pytest.mark.parametrize("kv,act", [("bf16", "bf16"), ("fp8", "bf16")])
 def test_hca_chunk_queries(kv, act):
     _hca_case(kv, act, lens=[64 * 900 + 10, 300], r=64, W=128, chunk=(0, 96))
