@@ -15,6 +15,7 @@ import torch
 
 from compressed_sparse_attention_csa_amd import binding as B
 from compressed_sparse_attention_csa_amd import synth as Sy
+from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
 from oracle import csa_oracle as O
 
 from gpu_helpers import (TOL, TORCH_ACT, bf16_ulp, e4m3_ulp, fill_index_keys, fill_main_kv, fill_ring, make_cache,
@@ -455,6 +456,40 @@ def test_page_placement_does_not_change_results():
         T = cache.index_topk([0, 1], [9999, 3999], qi, w, 512)
         o = cache.attend(0, [0, 1], [9999, 3999], q, T, 512, 0.088)
         outs.append((T.cpu(), o.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_pool_at_the_32bit_offset_limit():
+    """Attention gathers address a pool with 32-bit byte offsets. A pool just
+    under the 0xfffff000-byte limit, holding the sequences' pages at its top
+    end (row offsets above 2^31 and up to the limit), gives the same Top-K and
+    bit-identical outputs as the same contents at the start of a small pool."""
+    big = 0xFFFFF000 // (64 * 128)        # fp8 rows of 128 B
+    lens = [4 * 2500, 4 * 1000]
+    outs = []
+    for pool_pages, top in ((90, False), (big, True)):
+        spec = CacheSpec(ratio=4, q_heads=64, window=128, ring_rows=128, max_seqs=2, max_pages_per_seq=40,
+                         pool_pages=pool_pages, kv_dtype="fp8", act_dtype="bf16", max_queries=2, max_k=512)
+        first = pool_pages - 80 if top else 0
+        bt = torch.arange(first, first + 80, dtype=torch.int32).flip(0).view(2, 40).cuda()
+        cache = CsaCache(spec, "cuda", block_table=bt)
+        assert B.csa_buffer_sizes_for(spec.config()).kv_pool <= 0xFFFFF000
+        for b, L in enumerate(lens):
+            fill_main_kv(cache, 7, 0, b, L // 4)
+            fill_index_keys(cache, 7, b, L // 4)
+            fill_ring(cache, 7, 0, b, L)
+            B.csa_seq_set_len(cache.handle, 0, b, L)
+        qi = Sy.normal_rows(7, Sy.stream_id(Sy.KIND_QI), 0, 8, 64, dtype=torch.bfloat16).view(2, 4, 64).cuda()
+        w = Sy.uniform_rows(7, Sy.stream_id(Sy.KIND_W), 0, 2, 4).cuda()
+        q = Sy.normal_rows(7, Sy.stream_id(Sy.KIND_Q), 0, 128, 128, dtype=torch.bfloat16).view(2, 64, 128).cuda()
+        T = cache.index_topk([0, 1], [lens[0] - 1, lens[1] - 1], qi, w, 512)
+        o = cache.attend(0, [0, 1], [lens[0] - 1, lens[1] - 1], q, T, 512, 0.088)
+        assert cache.read_errors() == 0
+        outs.append((T.cpu(), o.cpu()))
+        cache.close()
+        del cache
+        torch.cuda.empty_cache()
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1])
 
