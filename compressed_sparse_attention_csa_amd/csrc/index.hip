@@ -1094,6 +1094,13 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
   bool done = false;
   if (sh[3] == 0 && c >= k && c <= kChunkCandCap && n_tiles <= kMaxChunkTiles) {
     const uint64_t *cq = a.cand + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
+    // the tile of every candidate position, written tile by tile (bin_keys is
+    // free until the select; c <= kChunkCandCap 16-bit entries fit it)
+    static_assert(kChunkCandCap * 2 <= kRankCap * 8 && kMaxChunkTiles <= 65536, "tile map fits bin_keys");
+    uint16_t *tile_of = reinterpret_cast<uint16_t *>(bin_keys);
+    for (int t = tid; t < n_tiles; t += bd)
+      for (int i = toff[t]; i < toff[t + 1]; ++i) tile_of[i] = static_cast<uint16_t>(t);
+    __syncthreads();
     constexpr int kPer = kChunkCandCap / 512;
     uint64_t tk[kPer];
 #pragma unroll
@@ -1101,11 +1108,7 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
       const int i = u * 512 + tid;
       tk[u] = 0;
       if (i < c) {
-        int lo = 0, hi = n_tiles;       // tile with toff[lo] <= i < toff[lo + 1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (toff[mid] <= i) lo = mid; else hi = mid;
-        }
+        const int lo = tile_of[i];
         tk[u] = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];
       }
     }
