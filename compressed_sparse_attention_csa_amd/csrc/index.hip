@@ -655,6 +655,17 @@ __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, 
   bool done = false;
   if (c >= k && c <= kSelCap) {
     const int64_t qbase = static_cast<int64_t>(qi) * a.s_stride;
+    // the slice of every candidate position, written slice by slice into
+    // bin_keys (free until the select) when the candidates fit it
+    constexpr int kMapCap = kRankCap * 4;   // 16-bit entries in bin_keys
+    static_assert(kMaxSlices <= 65536, "slice ids fit 16 bits");
+    uint16_t *slice_of = reinterpret_cast<uint16_t *>(bin_keys);
+    const bool mapped = c <= kMapCap;
+    if (mapped) {
+      for (int t = tid; t < ns; t += blockDim.x)
+        for (int i = soff[t]; i < soff[t + 1]; ++i) slice_of[i] = static_cast<uint16_t>(t);
+      __syncthreads();
+    }
     constexpr int kPer = (kSelCap + 511) / 512;
     float ts[kPer];
     int tj[kPer];
@@ -664,10 +675,15 @@ __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, 
       ts[u] = 0.f;
       tj[u] = 0;
       if (i < c) {
-        int lo = 0, hi = ns;            // slice s with soff[s] <= i < soff[s+1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (soff[mid] <= i) lo = mid; else hi = mid;
+        int lo = 0;                     // slice s with soff[s] <= i < soff[s+1]
+        if (mapped) {
+          lo = slice_of[i];
+        } else {
+          int hi = ns;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (soff[mid] <= i) lo = mid; else hi = mid;
+          }
         }
         const int64_t o = qbase + static_cast<int64_t>(lo) * kFilterSlice + (i - soff[lo]);
         ts[u] = a.cand_s[o];
