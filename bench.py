@@ -458,7 +458,7 @@ def cpu_baseline(seed, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -60,7 +60,7 @@ typedef enum {
   CSA_ERR_SHAPE = 2,       /* sizes inconsistent with the config */
   CSA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
   CSA_ERR_CAPACITY = 4,    /* sequence, page, ring or workspace capacity exceeded */
-  CSA_ERR_UNSUPPORTED = 5, /* valid request outside this build's limits */
+  CSA_ERR_UNSUPPORTED = 5, /* valid request outside the library's limits */
   CSA_ERR_HIP = 6          /* a HIP runtime call failed */
 } csa_status;
 

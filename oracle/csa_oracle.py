@@ -321,7 +321,7 @@ def index_scores(q_idx: np.ndarray, w: np.ndarray, kidx: np.ndarray) -> np.ndarr
     [Walkthrough] CSA2 "The indexer selects, SWA covers the rest" (indexer
     query against indexer key); [Atlas] trained-sparse-attention entries (a
     lightning indexer, run as MQA: several indexer query heads over one shared
-    key). The ReLU-weighted head sum is this build's stated form of the
+    key). The ReLU-weighted head sum is the reading taken here of the
     lightning-indexer score; no extra scale is applied (with ReLU and w >= 0 a
     positive scale would not change the ranking).
 
