@@ -13,10 +13,11 @@ replicas so the 256 MB last-level cache cannot hold a step's working set.
 
 The timed steps are HIP graph replays (a graph holds one step on every
 replica, as a model's decode iteration holds several layer groups). Prints
-one JSON line: decode tokens/s, the indexer scan
-kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events around
-every scan launch of an eager pass over the same steps), and the CPU
-oracle's throughput on a bounded sample of the same step.
+one JSON line: decode tokens/s, the indexer scan kernel's achieved HBM
+bandwidth against the 8 TB/s peak (HIP events around every scan launch of an
+eager pass over the same steps) and against a plain streaming read of the same
+size on the same GPU, and the CPU oracle's throughput on a bounded sample of
+the same step.
 """
 from __future__ import annotations
 
@@ -557,6 +558,13 @@ def main():
     sb = scan_bytes_per_launch()
     achieved = sb / (scan_avg_ms * 1e-3) / 1e9
     traffic, traffic_scope = traffic_from_profiles()
+    # the same number of bytes read by a plain 16-byte non-temporal streaming
+    # kernel over 8 rotating buffers: what one launch of this size gets here
+    ref_bufs = [torch.empty(sb, dtype=torch.uint8, device=dev) for _ in range(8)]
+    B.csa_debug_stream_read(ref_bufs, sb, 8)
+    ref_us = B.csa_debug_stream_read(ref_bufs, sb, 80)
+    del ref_bufs
+    ref_gbps = sb / (ref_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -582,6 +590,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "traffic_scope": traffic_scope,
                      "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
+        "read_ceiling": {"kernel": "streaming read, 16-byte non-temporal loads, 8 rotating buffers",
+                         "bytes": sb, "avg_launch_us": round(ref_us, 3), "achieved": round(ref_gbps, 1),
+                         "unit": "GB/s", "scan_frac": round(achieved / ref_gbps, 4)},
     }
     if not args.no_hier:
         line["hierarchical"] = hier_leg(caches, qi, w, max(10, args.steps // 4), args.seed)

@@ -80,6 +80,7 @@ EXPORTS = [
     "csa_compress", "csa_index_topk", "csa_attend", "csa_read_errors",
     "csa_profile_begin", "csa_profile_end", "csa_debug_convert", "csa_attend_dense",
     "csa_seq_set_swa_start", "csa_ring_write", "csa_index_topk_pool", "csa_index_reindex",
+    "csa_debug_stream_read",
 ]
 
 _LIB = None
@@ -138,6 +139,8 @@ def lib() -> C.CDLL:
     L.csa_profile_end.argtypes = [vp, C.c_int32, C.POINTER(C.c_double), pi32]
     L.csa_debug_convert.restype = C.c_int
     L.csa_debug_convert.argtypes = [i32, vp, vp, i64, vp]
+    L.csa_debug_stream_read.restype = C.c_int
+    L.csa_debug_stream_read.argtypes = [C.POINTER(C.c_void_p), i32, i64, i32, vp, C.POINTER(C.c_float)]
     _LIB = L
     return L
 
@@ -262,3 +265,12 @@ def csa_profile_end(h: int, kernel: int = PROFILE_INDEX) -> tuple[float, int]:
 
 def csa_debug_convert(kind: int, inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     check(lib().csa_debug_convert(kind, _ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
+
+
+def csa_debug_stream_read(bufs, nbytes: int, reps: int, stream=None) -> float:
+    """Mean launch duration (us) of a 16-byte non-temporal streaming read of
+    nbytes, rotating over the device buffers (tensors or raw addresses)."""
+    ptrs = (C.c_void_p * len(bufs))(*[b.data_ptr() if isinstance(b, torch.Tensor) else int(b) for b in bufs])
+    us = C.c_float(0.0)
+    check(lib().csa_debug_stream_read(ptrs, len(bufs), int(nbytes), int(reps), _stream(stream), C.byref(us)))
+    return float(us.value)

@@ -9,6 +9,8 @@
 #include <string>
 #include <vector>
 
+#include <hip/hip_ext.h>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -216,6 +218,22 @@ __global__ void debug_convert_kernel(int kind, const void *in, void *out, int64_
   } else {
     reinterpret_cast<uint8_t *>(out)[i] = static_cast<uint8_t>(f32_to_e2m1(reinterpret_cast<const float *>(in)[i]));
   }
+}
+
+// Streaming read of n16 16-byte words with non-temporal loads. The xor of the
+// words feeds an empty volatile asm statement, so the loads stay and nothing
+// is written.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *p, int64_t n16) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i0 + u * 256;
+    if (i < n16) acc ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i);
+  }
+  const unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  asm volatile("" : : "v"(x));
 }
 
 }  // namespace
@@ -924,6 +942,39 @@ csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int3
   h->profiling &= ~kernel;
   if (h->profiling == 0) h->events_used = 0;
   return CSA_OK;
+}
+
+csa_status csa_debug_stream_read(const void *const *bufs, int32_t n_bufs, int64_t bytes, int32_t reps,
+                                 hipStream_t stream, float *avg_us) {
+  if (!bufs || n_bufs < 1 || !avg_us || reps < 1 || bytes <= 0 || bytes % 16 != 0)
+    return fail(CSA_ERR_INVALID_ARG, "bad stream-read arguments");
+  for (int i = 0; i < n_bufs; ++i)
+    if (!bufs[i] || reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0)
+      return fail(CSA_ERR_INVALID_ARG, "buffer %d is null or not 16-byte aligned", i);
+  const int64_t n16 = bytes / 16, blocks = (n16 + 1023) / 1024;
+  std::vector<hipEvent_t> ev(2 * static_cast<size_t>(reps), nullptr);
+  csa_status st = CSA_OK;
+  for (auto &e : ev)
+    if (hipEventCreate(&e) != hipSuccess) { st = fail(CSA_ERR_HIP, "event creation failed"); break; }
+  if (st == CSA_OK) {
+    for (int r = 0; r < reps; ++r)
+      hipExtLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, ev[2 * r],
+                            ev[2 * r + 1], 0, reinterpret_cast<const uint4 *>(bufs[r % n_bufs]), n16);
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) {
+      st = fail(CSA_ERR_HIP, "stream-read launch failed");
+    } else {
+      double tot = 0.0;
+      for (int r = 0; r < reps; ++r) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]) != hipSuccess) { st = fail(CSA_ERR_HIP, "event timing failed"); break; }
+        tot += ms;
+      }
+      if (st == CSA_OK) *avg_us = static_cast<float>(tot * 1e3 / reps);
+    }
+  }
+  for (auto &e : ev)
+    if (e) (void)hipEventDestroy(e);
+  return st;
 }
 
 csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream) {

@@ -369,6 +369,18 @@ csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int3
  * in/out are device pointers. */
 csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream);
 
+/* Streaming-read reference for the indexer scan's bandwidth (a measurement aid,
+ * not part of the method): reads `bytes` of device memory per launch with
+ * 16-byte non-temporal loads (the scan's load form), `reps` launches rotating
+ * over the n_bufs device buffers bufs[i] (each >= bytes, 16-byte aligned; use
+ * enough of them to exceed the last-level cache), each launch timed by events
+ * it stamps itself. Writes nothing to device memory. Synchronises `stream`;
+ * *avg_us receives the mean launch duration in microseconds. Errors:
+ * CSA_ERR_INVALID_ARG for null or misaligned buffers, bytes not a positive
+ * multiple of 16, reps < 1; CSA_ERR_HIP on a launch or event failure. */
+csa_status csa_debug_stream_read(const void *const *bufs, int32_t n_bufs, int64_t bytes, int32_t reps,
+                                 hipStream_t stream, float *avg_us);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,6 +110,18 @@ def test_pool_and_ring_byte_limits():
     assert B.csa_buffer_sizes_for(_spec(kv_dtype=B.CSA_FP4_E2M1, pool_pages=lim // (64 * 128) + 1)).kv_pool <= lim
 
 
+def test_stream_read_validates_before_launch():
+    """The streaming-read reference rejects bad arguments on the host (status 1,
+    CSA_ERR_INVALID_ARG): no buffers, a null or misaligned buffer, a size that
+    is not a positive multiple of 16, no launches."""
+    L = B.lib()
+    us = C.c_float(0.0)
+    for bufs, nbytes, reps in (([], 1 << 20, 4), ([0], 1 << 20, 4), ([0x10008], 1 << 20, 4), ([0x10000], 100, 4),
+                               ([0x10000], 1 << 20, 0), ([0x10000], 0, 4)):
+        ptrs = (C.c_void_p * max(1, len(bufs)))(*bufs)
+        assert L.csa_debug_stream_read(ptrs, len(bufs), nbytes, reps, C.c_void_p(0), C.byref(us)) == 1
+
+
 def test_create_requires_buffers():
     cfg = _spec()
     b = B.Buffers()
