@@ -566,24 +566,46 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
 // Combines the split partials of (query, head): one softmax over the union of
 // every split's keys. Thread d owns output dimension d; all of its loads are
 // independent, so the merge costs about one memory round trip.
-template <int ACT>
+template <int ACT, int MS>
 __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   const int qi = blockIdx.x / a.H, h = blockIdx.x % a.H, d = threadIdx.x;
   const int64_t q0 = static_cast<int64_t>(qi) * a.n_splits;
-  float m[kAttMaxSplits], l[kAttMaxSplits], o[kAttMaxSplits];
+  // (m, l) are the same for every thread: with many splits they are staged
+  // through LDS by one thread per split instead of filling scalar registers
+  constexpr bool STAGE = MS > 40;
+  static_assert(MS <= kD, "one thread per split stages (m, l)");
+  __shared__ float ms_st[STAGE ? MS : 1], ls_st[STAGE ? MS : 1];
+  float m[MS], l[MS], o[MS];
+  if constexpr (STAGE) {
+    if (d < MS) {
+      const bool ok = d < a.n_splits;
+      ms_st[d] = ok ? a.part_ml[((q0 + d) * 2 + 0) * a.H + h] : -INFINITY;
+      ls_st[d] = ok ? a.part_ml[((q0 + d) * 2 + 1) * a.H + h] : 0.f;
+    }
+  }
 #pragma unroll
-  for (int s = 0; s < kAttMaxSplits; ++s) {
+  for (int s = 0; s < MS; ++s) {
     const bool ok = s < a.n_splits;
-    m[s] = ok ? a.part_ml[((q0 + s) * 2 + 0) * a.H + h] : -INFINITY;
-    l[s] = ok ? a.part_ml[((q0 + s) * 2 + 1) * a.H + h] : 0.f;
+    if constexpr (!STAGE) {
+      m[s] = ok ? a.part_ml[((q0 + s) * 2 + 0) * a.H + h] : -INFINITY;
+      l[s] = ok ? a.part_ml[((q0 + s) * 2 + 1) * a.H + h] : 0.f;
+    }
     o[s] = ok ? a.part_o[((q0 + s) * a.H + h) * kD + d] : 0.f;
+  }
+  if constexpr (STAGE) {
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      m[s] = ms_st[s];
+      l[s] = ls_st[s];
+    }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kAttMaxSplits; ++s) mx = fmaxf(mx, m[s]);
+  for (int s = 0; s < MS; ++s) mx = fmaxf(mx, m[s]);
   float L = 0.f, acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < kAttMaxSplits; ++s) {
+  for (int s = 0; s < MS; ++s) {
     const float e = (m[s] == -INFINITY) ? 0.f : fast_exp2(m[s] - mx);   // running maxima are in log2 units
     L += e * l[s];
     acc += e * o[s];
@@ -617,9 +639,13 @@ void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, bool ring_fp8
   else if (kv == DT_FP8 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP8, DT_FP8>(a, n_wg, s, ev0, ev1);
   else if (kv == DT_FP4 && act == DT_BF16 && !ring_fp8) launch_attend_t<DT_BF16, DT_FP4, DT_BF16>(a, n_wg, s, ev0, ev1);
   else if (kv == DT_FP4 && act == DT_BF16) launch_attend_t<DT_BF16, DT_FP4, DT_FP8>(a, n_wg, s, ev0, ev1);
-  if (a.n_splits > 1) {
-    if (act == DT_F32) hipLaunchKernelGGL(attend_merge_kernel<DT_F32>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);
-    else hipLaunchKernelGGL(attend_merge_kernel<DT_BF16>, dim3(a.n_q * a.H), dim3(kD), 0, s, a);
+  // the merge's per-thread arrays hold MS splits: 40 covers decode batches
+  if (a.n_splits > 40) {
+    if (act == DT_F32) hipLaunchKernelGGL((attend_merge_kernel<DT_F32, kAttMaxSplits>), dim3(a.n_q * a.H), dim3(kD), 0, s, a);
+    else hipLaunchKernelGGL((attend_merge_kernel<DT_BF16, kAttMaxSplits>), dim3(a.n_q * a.H), dim3(kD), 0, s, a);
+  } else if (a.n_splits > 1) {
+    if (act == DT_F32) hipLaunchKernelGGL((attend_merge_kernel<DT_F32, 40>), dim3(a.n_q * a.H), dim3(kD), 0, s, a);
+    else hipLaunchKernelGGL((attend_merge_kernel<DT_BF16, 40>), dim3(a.n_q * a.H), dim3(kD), 0, s, a);
   }
 }
 

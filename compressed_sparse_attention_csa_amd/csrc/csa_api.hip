@@ -140,7 +140,6 @@ size_t attend_bytes(int nq, int n_splits, int H) {
 
 int n_blocks_for(int k, int W) { return (k + kKeyBlock - 1) / kKeyBlock + (W > 0 ? (W + kKeyBlock - 1) / kKeyBlock : 0); }
 
-constexpr int kMaxSplits = kAttMaxSplits;
 
 // Blocks of 64 keys per attention workgroup for a decode batch of nq queries
 // with nb blocks each: enough workgroups to spread the gathers over the chip,
@@ -154,7 +153,8 @@ int attend_blocks_per_split(int nq, int nb) {
   int bps = kAttKeyStreams;
   (void)nq;
 #endif
-  bps = std::max(bps, (nb + kMaxSplits - 1) / kMaxSplits);
+  const int ms = att_max_splits(nq);
+  bps = std::max(bps, (nb + ms - 1) / ms);
   bps = std::min(bps, kAttMaxSplitKeys / kKeyBlock);
   return std::max(1, bps);
 }
@@ -286,7 +286,10 @@ size_t csa_workspace_size(const csa_config *cfg, int32_t max_queries, int32_t ma
   const int64_t s_chunk = (E + 63) / 64 * 64;
   const int64_t ss_chunk = (E / kChunkSample + 255) / 256 * 256 + 256;
   const size_t b = max_queries > 1 ? idx_chunk_bytes(max_queries, ss_chunk, s_chunk) : 0;
-  const size_t c = attend_bytes(std::min<int>(max_queries, kAttMaxQ), kMaxSplits, cfg->q_heads);
+  // attention partials: a launch of nq <= nq_att queries uses nq x att_max_splits(nq)
+  // query-splits, at most min(nq_att x kAttMaxSplits, kAttSplitBudget)
+  const int nq_att = std::min<int>(max_queries, kAttMaxQ);
+  const size_t c = attend_bytes(1, std::min(nq_att * kAttMaxSplits, kAttSplitBudget), cfg->q_heads);
   return kHead + std::max(a, std::max(b, c)) + 1024;
 }
 
@@ -830,9 +833,10 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
   if (dense) {
     k = 0;
     for (int i = 0; i < n_q; ++i) k = std::max(k, (q_pos[i] + 1) / c.ratio);
-    if (static_cast<int64_t>(n_blocks_for(k, c.window)) > static_cast<int64_t>(kMaxSplits) * (kAttMaxSplitKeys / kKeyBlock))
+    const int ms = att_max_splits(std::min(n_q, kAttMaxQ));
+    if (static_cast<int64_t>(n_blocks_for(k, c.window)) > static_cast<int64_t>(ms) * (kAttMaxSplitKeys / kKeyBlock))
       return fail(CSA_ERR_UNSUPPORTED, "dense attention over %d entries exceeds %d", k,
-                  kMaxSplits * kAttMaxSplitKeys - (c.window + kKeyBlock - 1) / kKeyBlock * kKeyBlock);
+                  ms * kAttMaxSplitKeys - (c.window + kKeyBlock - 1) / kKeyBlock * kKeyBlock);
   }
   const int kv = main_dt(c);
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;

@@ -170,7 +170,14 @@ constexpr uint32_t kAttMaxBufferBytes = 0xfffff000u;   // largest K/V pool or ri
 constexpr int kAttMaxSplitKeys = 2304;   // keys one workgroup resolves up front (36 blocks)
 constexpr int kAttKeyStreams = 1;        // 64-key blocks a decode workgroup processes per round
 constexpr int kAttChunkKeyStreams = 1;   // the same for a prefill chunk (one workgroup per query)
-constexpr int kAttMaxSplits = 40;        // splits per query combined by the merge kernel
+constexpr int kAttMaxSplits = 80;        // splits per query combined by the merge kernel
+constexpr int kAttSplitBudget = kAttMaxQ * 40;   // queries x splits of one launch (partials workspace)
+
+// Most splits a launch of nq queries may use: the partials of nq x splits fit the budget.
+inline int att_max_splits(int nq) {
+  const int b = kAttSplitBudget / (nq > 0 ? nq : 1);
+  return b < 1 ? 1 : (b < kAttMaxSplits ? b : kAttMaxSplits);
+}
 
 struct AttendArgs {
   const void *q;            // [n_q][H][D]
