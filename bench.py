@@ -64,16 +64,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PF_PRIOR, PF_CHUNK, PF_K = 131072, 2048, 1024
 
 
-def prefill_leg(seed, dev, steps=5):
-    """Prefill chunk: 2,048 new tokens appended to a 131,072-token context (bf16,
-    r = 4, Top-1024 per query token, W = 128, 64 heads). One step = compress the
-    chunk, index (MFMA score GEMM + exact select) and attend all 2,048 tokens.
-    Reports MFMA utilisation of the index score GEMM (the pass that scores every
-    visible entry) and of the attention kernel, each timed by HIP events that
-    its launch stamps (the last of the steps)."""
+def build_prefill(seed, dev):
+    """The prefill-chunk workload on `dev`: a bf16 cache holding the
+    131,072-token context (pages in a seeded permuted order), the chunk's raw
+    rows, queries and outputs, and chunk_step(stream), which compresses the
+    chunk, indexes and attends all of its 2,048 tokens."""
     import torch
-    from compressed_sparse_attention_csa_amd import accounting as A
-    from compressed_sparse_attention_csa_amd import binding as B
     from compressed_sparse_attention_csa_amd import synth as Sy
     from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
 
@@ -99,6 +95,22 @@ def prefill_leg(seed, dev, steps=5):
         c.compress(0, [0], [PF_CHUNK], ck, cv, cz, P, stream=stream)
         c.index_topk(q_seq, q_pos, qi, w, PF_K, T, stream=stream)
         c.attend(0, q_seq, q_pos, q, T, PF_K, scale, out, stream=stream)
+    return dict(cache=c, qi=qi, w=w, q=q, T=T, out=out, q_seq=q_seq, q_pos=q_pos, scale=scale, chunk_step=chunk_step)
+
+
+def prefill_leg(seed, dev, steps=5):
+    """Prefill chunk: 2,048 new tokens appended to a 131,072-token context (bf16,
+    r = 4, Top-1024 per query token, W = 128, 64 heads). One step = compress the
+    chunk, index (MFMA score GEMM + exact select) and attend all 2,048 tokens.
+    Reports MFMA utilisation of the index score GEMM (the pass that scores every
+    visible entry) and of the attention kernel, each timed by HIP events that
+    its launch stamps (the last of the steps)."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+
+    W_ = build_prefill(seed, dev)
+    c, qi, w, T, q_seq, q_pos, chunk_step = (W_[k] for k in ("cache", "qi", "w", "T", "q_seq", "q_pos", "chunk_step"))
 
     # warm-up, then the step captured once and replayed: host-side argument
     # marshalling stays out of the timed region

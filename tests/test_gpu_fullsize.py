@@ -4,7 +4,8 @@ The 1,048,576-token batch-4 decode (fp8 cache, 4 layers sharing one Top-1024,
 W = 128, 64 heads) is built on the GPU exactly as bench.py builds it; one step
 runs through the C ABI. The oracle recomputes, for sequence 0, the indexer
 keys of all 262,144 entries from the same seeded raw rows, its Top-K, and the
-attention of layers 0 and 3.
+attention of layers 0 and 3. The prefill chunk (2,048 tokens on a
+131,072-token context) is checked the same way on sampled query tokens.
 """
 import math
 import os
@@ -297,4 +298,39 @@ def test_decode_1m_fp4_sampled(bench_mod):
     Vw[lo:] = to64(_rows(seed, Sy.KIND_V, 0, 0, lo, bm.WINDOW, dev))
     ref = O.attend_step(to64(q[0]), To, t, bm.WINDOW, scale, kb, vb, Kw, Vw)
     assert max_abs(out[0], ref) <= 2e-2
+    c.close()
+
+
+def test_prefill_chunk_2048_on_131k_sampled(bench_mod):
+    """The benchmark's prefill chunk (2,048 bf16 tokens after a 131,072-token
+    context, pages in permuted order, Top-1024, W = 128, 64 heads), one step
+    through the C ABI: its first, a middle and its last query against the
+    oracle, whose entries come from the same seeded raw rows (the chunk's own
+    entries are visible to its later queries)."""
+    bm = bench_mod
+    seed, dev = 0, torch.device("cuda:0")
+    W_ = bm.build_prefill(seed, dev)
+    c = W_["cache"]
+    B.csa_seq_set_len(c.handle, 0, 0, bm.PF_PRIOR)
+    W_["chunk_step"](torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert c.read_errors() & ~B.ERR_FALLBACK == 0
+    T, out = W_["T"].cpu().numpy(), W_["out"]
+    n_rows = bm.PF_PRIOR + bm.PF_CHUNK
+    kbs, vbs, kis = _oracle_entries(seed, 0, 0, n_rows, dev, True, "bf16")
+    for i in (0, 777, bm.PF_CHUNK - 1):
+        t = bm.PF_PRIOR + i
+        N = O.visible_entries(t, bm.RATIO)
+        s = O.index_scores(to64(W_["qi"][i]), to64(W_["w"][i]), kis[:N])
+        To = O.topk(s, bm.PF_K)
+        ok, msg = topk_matches(T[i], To, s)
+        assert ok, f"chunk query {i}: {msg}"
+        lo = t - bm.WINDOW + 1
+        Kw = np.zeros((t + 1, 128))
+        Vw = np.zeros((t + 1, 128))
+        Kw[lo:] = to64(_rows(seed, Sy.KIND_K, 0, 0, lo, bm.WINDOW, dev))
+        Vw[lo:] = to64(_rows(seed, Sy.KIND_V, 0, 0, lo, bm.WINDOW, dev))
+        ref = O.attend_step(to64(W_["q"][i]), To, t, bm.WINDOW, W_["scale"], kbs, vbs, Kw, Vw)
+        err = max_abs(to64(out[i]), ref)
+        assert err <= 2e-2, f"chunk query {i}: max-abs {err}"
     c.close()

@@ -326,7 +326,7 @@ def test_attend_decode_matches_oracle(kv, act):
 
 
 @pytest.mark.parametrize("kv,act", DT_CASES)
-@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("H", [16, 32, 128])
 def test_attend_head_counts(kv, act, H):
     _attend_case(kv, act, lens=[4 * 700, 999], k=70, W=100, H=H)
 
@@ -843,8 +843,16 @@ def test_attend_fp8_ring_decode_matches_oracle(kv):
     _attend_case(kv, "bf16", lens=[4 * 700 + 2, 4 * 64, 37, 4], k=256, W=128, swa="fp8")
 
 
-def test_attend_fp8_ring_chunk_matches_oracle():
-    _attend_case("fp8", "bf16", lens=[4 * 600 + 1, 400], k=128, W=128, chunk=(0, 48), swa="fp8")
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
+def test_attend_fp8_ring_chunk_matches_oracle(kv):
+    _attend_case(kv, "bf16", lens=[4 * 600 + 1, 400], k=128, W=128, chunk=(0, 48), swa="fp8")
+
+
+@pytest.mark.parametrize("kv,act", DT_CASES)
+def test_attend_chunk_head_counts(kv, act):
+    # 32 and 128 heads in a prefill chunk, with a ragged last Top-K block
+    for H in (32, 128):
+        _attend_case(kv, act, lens=[4 * 900 + 2, 64], k=150, W=64, H=H, chunk=(0, 40))
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
