@@ -168,20 +168,15 @@ def prefill_leg(seed, dev, steps=5):
 HCA_RATIO, HCA_REPLICAS = 128, 32
 
 
-def hca_leg(seed, dev, steps=50):
-    """Heavily compressed attention layer at the same 1M-token batch-4 decode:
-    r = 128 gives 8,192 fp8 entries per sequence, every one attended (no
-    indexer) together with the 128-token window, 64 heads. Timed over graph
-    replays rotating across 32 cache replicas (more than the last-level cache
-    holds); the attention kernel's own time from launch-stamped events."""
+def build_hca(seed, dev):
+    """The HCA workload's cache on `dev`: batch 4, each sequence's 1,048,576
+    raw rows (layer stream 7) compressed at r = 128 into fp8 pages in a seeded
+    permuted order, no indexer. Returns (cache, spec, block table)."""
     import torch
-    from compressed_sparse_attention_csa_amd import accounting as A
-    from compressed_sparse_attention_csa_amd import binding as B
     from compressed_sparse_attention_csa_amd import synth as Sy
     from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
 
-    entries = CONTEXT // HCA_RATIO
-    pages = entries // 64
+    pages = CONTEXT // HCA_RATIO // 64
     spec = CacheSpec(ratio=HCA_RATIO, q_heads=HEADS, idx_heads=0, window=WINDOW, ring_rows=max(WINDOW, HCA_RATIO),
                      n_layers=1, max_seqs=BATCH, max_pages_per_seq=pages, pool_pages=BATCH * pages,
                      kv_dtype="fp8", act_dtype="bf16", max_queries=BATCH, max_k=1)
@@ -193,6 +188,29 @@ def hca_leg(seed, dev, steps=50):
             rows = [Sy.normal_rows(seed, Sy.stream_id(kind, 7, b), r0, chunk, 128, dev, torch.bfloat16)
                     for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
             base.compress(0, [b], [chunk], *rows)
+    return base, spec, bt
+
+
+def hca_q(seed, dev):
+    """The HCA leg's batch of queries (64 heads, bf16)."""
+    import torch
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    return Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, 7), 0, BATCH * HEADS, 128, dev, torch.bfloat16).view(BATCH, HEADS, 128)
+
+
+def hca_leg(seed, dev, steps=50):
+    """Heavily compressed attention layer at the same 1M-token batch-4 decode:
+    r = 128 gives 8,192 fp8 entries per sequence, every one attended (no
+    indexer) together with the 128-token window, 64 heads. Timed over graph
+    replays rotating across 32 cache replicas (more than the last-level cache
+    holds); the attention kernel's own time from launch-stamped events."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd.cache import CsaCache
+
+    entries = CONTEXT // HCA_RATIO
+    base, spec, bt = build_hca(seed, dev)
     caches = [base]
     for _ in range(1, HCA_REPLICAS):
         c = CsaCache(spec, dev, block_table=bt)
@@ -203,7 +221,7 @@ def hca_leg(seed, dev, steps=50):
         for b in range(BATCH):
             B.csa_seq_set_len(c.handle, 0, b, CONTEXT)
         caches.append(c)
-    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, 7), 0, BATCH * HEADS, 128, dev, torch.bfloat16).view(BATCH, HEADS, 128)
+    q = hca_q(seed, dev)
     out = torch.empty_like(q)
     q_seq, q_pos = list(range(BATCH)), [CONTEXT - 1] * BATCH
     scale = 1.0 / math.sqrt(128)

@@ -4,8 +4,10 @@ The 1,048,576-token batch-4 decode (fp8 cache, 4 layers sharing one Top-1024,
 W = 128, 64 heads) is built on the GPU exactly as bench.py builds it; one step
 runs through the C ABI. The oracle recomputes, for sequence 0, the indexer
 keys of all 262,144 entries from the same seeded raw rows, its Top-K, and the
-attention of layers 0 and 3. The prefill chunk (2,048 tokens on a
-131,072-token context) is checked the same way on sampled query tokens.
+attention of layers 0 and 3. The fp4 and fp8-ring decode variants, the HCA
+layer (r = 128, every entry attended) and the prefill chunk (2,048 tokens on a
+131,072-token context) are checked the same way on sampled sequences or
+query tokens.
 """
 import math
 import os
@@ -271,13 +273,15 @@ def test_hierarchical_indexer_1m_sampled(bench_mod):
     c.close()
 
 
-def test_decode_1m_fp4_sampled(bench_mod):
-    """The benchmark's decode step on fp4 K/V (E2M1, E4M3 scale per 16 channels,
-    fp8 indexer keys): sequence 0's Top-K and layer-0 attention against the
-    oracle's fp4 entries."""
+@pytest.mark.parametrize("kv,swa", [("fp4", ""), ("fp8", "fp8")])
+def test_decode_1m_variant_sampled(bench_mod, kv, swa):
+    """The benchmark's decode-step variants: fp4 K/V (E2M1, E4M3 scale per 16
+    channels) with a bf16 window ring, and fp8 K/V pages with an fp8 window ring
+    (one scale per row); fp8 indexer keys in both. Sequence 0's Top-K and
+    layer-0 attention against the oracle's entries and ring rows."""
     bm = bench_mod
     seed, dev = 0, torch.device("cuda:0")
-    c = bm.build_cache(seed, 1, dev, kv="fp4")[0]
+    c = bm.build_cache(seed, 1, dev, swa=swa, kv=kv)[0]
     q_seq, q_pos = list(range(bm.BATCH)), [bm.CONTEXT - 1] * bm.BATCH
     qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, bm.BATCH * 4, 64, dev, torch.bfloat16).view(bm.BATCH, 4, 64)
     w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, bm.BATCH, 4, dev)
@@ -286,7 +290,7 @@ def test_decode_1m_fp4_sampled(bench_mod):
     scale = 1.0 / math.sqrt(128)
     out = to64(c.attend(0, q_seq, q_pos, q, T, bm.TOPK, scale))
     assert c.read_errors() == 0
-    kb, vb, kis = _seq0_entries(bm, seed, dev, 0, "fp4")
+    kb, vb, kis = _seq0_entries(bm, seed, dev, 0, kv)
     s = O.index_scores(to64(qi[0]), to64(w[0]), kis)
     To = O.topk(s, bm.TOPK)
     ok, msg = topk_matches(T.cpu().numpy()[0], To, s, rel=2e-2)
@@ -294,8 +298,8 @@ def test_decode_1m_fp4_sampled(bench_mod):
     t = bm.CONTEXT - 1
     lo = t - bm.WINDOW + 1
     Kw, Vw = np.zeros((bm.CONTEXT, 128)), np.zeros((bm.CONTEXT, 128))
-    Kw[lo:] = to64(_rows(seed, Sy.KIND_K, 0, 0, lo, bm.WINDOW, dev))
-    Vw[lo:] = to64(_rows(seed, Sy.KIND_V, 0, 0, lo, bm.WINDOW, dev))
+    Kw[lo:] = O.store_ring_rows(to64(_rows(seed, Sy.KIND_K, 0, 0, lo, bm.WINDOW, dev)), swa)[0]
+    Vw[lo:] = O.store_ring_rows(to64(_rows(seed, Sy.KIND_V, 0, 0, lo, bm.WINDOW, dev)), swa)[0]
     ref = O.attend_step(to64(q[0]), To, t, bm.WINDOW, scale, kb, vb, Kw, Vw)
     assert max_abs(out[0], ref) <= 2e-2
     c.close()
@@ -333,4 +337,36 @@ def test_prefill_chunk_2048_on_131k_sampled(bench_mod):
         ref = O.attend_step(to64(W_["q"][i]), To, t, bm.WINDOW, W_["scale"], kbs, vbs, Kw, Vw)
         err = max_abs(to64(out[i]), ref)
         assert err <= 2e-2, f"chunk query {i}: max-abs {err}"
+    c.close()
+
+
+def test_hca_1m_dense_sampled(bench_mod):
+    """The benchmark's HCA layer (batch 4, 1,048,576 tokens at r = 128: 8,192
+    fp8 entries per sequence, all attended, with the 128-token window, 64
+    heads), one call through the C ABI; sequences 0 and 3 against the oracle
+    from the same seeded raw rows."""
+    bm = bench_mod
+    seed, dev = 0, torch.device("cuda:0")
+    c, _, _ = bm.build_hca(seed, dev)
+    q = bm.hca_q(seed, dev)
+    t = bm.CONTEXT - 1
+    out = to64(c.attend_dense(0, list(range(bm.BATCH)), [t] * bm.BATCH, q, 1.0 / math.sqrt(128)))
+    assert c.read_errors() == 0
+    step = 1 << 18
+    lo = t - bm.WINDOW + 1
+    for b in (0, 3):
+        E = bm.CONTEXT // bm.HCA_RATIO
+        kb, vb = np.empty((E, 128)), np.empty((E, 128))
+        for r0 in range(0, bm.CONTEXT, step):
+            K, V, Z = (to64(_rows(seed, kind, 7, b, r0, step, dev)) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+            a, v_, _ = O.compress(K, V, Z, bm.HCA_RATIO)
+            kb[r0 // bm.HCA_RATIO:(r0 + step) // bm.HCA_RATIO], vb[r0 // bm.HCA_RATIO:(r0 + step) // bm.HCA_RATIO] = a, v_
+        Kw = np.zeros((bm.CONTEXT, 128))
+        Vw = np.zeros((bm.CONTEXT, 128))
+        Kw[lo:] = to64(_rows(seed, Sy.KIND_K, 7, b, lo, bm.WINDOW, dev))
+        Vw[lo:] = to64(_rows(seed, Sy.KIND_V, 7, b, lo, bm.WINDOW, dev))
+        ref = O.hca_attend_step(to64(q[b]), t, bm.HCA_RATIO, bm.WINDOW, 1.0 / math.sqrt(128),
+                                O.store(kb, "fp8")[0], O.store(vb, "fp8")[0], Kw, Vw)
+        err = max_abs(out[b], ref)
+        assert err <= 2e-2, f"sequence {b}: max-abs {err}"
     c.close()
