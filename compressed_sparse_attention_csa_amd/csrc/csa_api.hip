@@ -145,14 +145,9 @@ int n_blocks_for(int k, int W) { return (k + kKeyBlock - 1) / kKeyBlock + (W > 0
 // with nb blocks each: enough workgroups to spread the gathers over the chip,
 // few enough splits that the fused merge stays cheap.
 int attend_blocks_per_split(int nq, int nb) {
-#ifdef CSA_ATTEND_BPS
-  int bps = CSA_ATTEND_BPS;
-#else
   // Latency-bound: a workgroup that walks several blocks in sequence waits a
   // memory round trip per block, so decode batches take one round per split.
   int bps = kAttKeyStreams;
-  (void)nq;
-#endif
   const int ms = att_max_splits(nq);
   bps = std::max(bps, (nb + ms - 1) / ms);
   bps = std::min(bps, kAttMaxSplitKeys / kKeyBlock);
@@ -833,12 +828,18 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
   if (dense) {
     k = 0;
     for (int i = 0; i < n_q; ++i) k = std::max(k, (q_pos[i] + 1) / c.ratio);
-    const int ms = att_max_splits(std::min(n_q, kAttMaxQ));
-    if (static_cast<int64_t>(n_blocks_for(k, c.window)) > static_cast<int64_t>(ms) * (kAttMaxSplitKeys / kKeyBlock))
-      return fail(CSA_ERR_UNSUPPORTED, "dense attention over %d entries exceeds %d", k,
-                  ms * kAttMaxSplitKeys - (c.window + kKeyBlock - 1) / kKeyBlock * kKeyBlock);
   }
   const int kv = main_dt(c);
+  // the splits of one query (the keys a workgroup resolves up front times the
+  // splits the merge combines) bound the keys a decode query can attend to
+  {
+    const int ms = att_max_splits(std::min(n_q, kAttMaxQ));
+    const int per_split = kv == DT_F32 ? kAttMaxSplitKeys : kAttSplitMaxKeys;
+    const int64_t nb = n_blocks_for(k, c.window);
+    if (!is_chunk(n_q, q_seq, q_pos) && nb > static_cast<int64_t>(ms) * (per_split / kKeyBlock))
+      return fail(CSA_ERR_UNSUPPORTED, "a query attends to %lld keys (%d entries + window %d); at most %d are supported",
+                  static_cast<long long>(nb * kKeyBlock), k, c.window, ms * per_split);
+  }
   const int act = c.act_dtype == CSA_F32 ? DT_F32 : DT_BF16;
   const int ab = dt_bytes(c.act_dtype);
   AttendArgs a{};
@@ -855,6 +856,7 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
   a.err = h->err;
   a.scale = scale; a.k = k; a.W = c.window; a.R = c.ring_rows; a.r = c.ratio; a.dense = dense ? 1 : 0;
   a.bt_stride = c.max_pages_per_seq; a.pool_pages = c.pool_pages; a.H = c.q_heads;
+  a.act_f32 = act == DT_F32 ? 1 : 0;
   a.n_sparse_blocks = (k + kKeyBlock - 1) / kKeyBlock;
   a.n_blocks = n_blocks_for(k, c.window);
   const size_t qrow = static_cast<size_t>(c.q_heads) * kD * ab;
@@ -865,6 +867,43 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
     a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
     const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
     launch_attend(a, n_q, kv, act, ring8, stream, ev.start, ev.stop);
+  } else if (kv != DT_F32) {
+    // decode and dense queries: one 64-key block per workgroup for a decode
+    // query (its blocks' gathers run side by side on as many CUs); four blocks
+    // side by side and several rounds per workgroup for a dense query, whose
+    // many blocks would otherwise leave the merge with too many partials
+    for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {
+      const int nq = std::min(kAttMaxQ, n_q - g0);
+      AttendArgs b = a;
+      b.q = reinterpret_cast<const char *>(q) + g0 * qrow;
+      b.out = reinterpret_cast<char *>(out) + g0 * qrow;
+      b.topk = topk && !dense ? topk + static_cast<int64_t>(g0) * k : nullptr;
+      b.chunk = 0; b.n_q = nq;
+      for (int i = 0; i < nq; ++i) {
+        b.qd[i].seq = q_seq[g0 + i];
+        b.qd[i].pos = q_pos[g0 + i];
+        b.qd[i].swa = h->swa_start[q_seq[g0 + i]];
+      }
+      const int nb = std::max(1, b.n_blocks);
+      const int ms = att_max_splits(nq);
+      const int ks = dense && c.q_heads <= 64 ? 4 : 1;
+      const int streams = (nb + ks - 1) / ks;
+      int rounds = dense ? (streams + kAttDenseSplits - 1) / kAttDenseSplits : 1;
+      rounds = std::max(rounds, (streams + ms - 1) / ms);
+      rounds = std::min(rounds, kAttSplitMaxKeys / (kKeyBlock * ks));
+      const int splits = (streams + rounds - 1) / rounds;
+      if (splits > ms) return fail(CSA_ERR_UNSUPPORTED, "too many attention splits per query");
+      b.blocks_per_split = ks * rounds;
+      b.n_splits = splits;
+      if (splits > 1) {
+        const size_t need = attend_bytes(nq, splits, c.q_heads);
+        if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for attention partials");
+        b.part_o = reinterpret_cast<float *>(h->scratch);
+        b.part_ml = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(nq) * splits * c.q_heads * kD * 4, 256));
+      }
+      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
+      launch_attend_decode(b, nq * splits, kv, ring8, ks, stream, ev.start, ev.stop);
+    }
   } else {
     for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {
       const int nq = std::min(kAttMaxQ, n_q - g0);
@@ -881,6 +920,7 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       const int nb = std::max(1, b.n_blocks);
       b.blocks_per_split = attend_blocks_per_split(nq, nb);
       b.n_splits = (nb + b.blocks_per_split - 1) / b.blocks_per_split;
+      if (b.n_splits > kAttMaxSplits) return fail(CSA_ERR_UNSUPPORTED, "too many attention splits per query");
       if (b.n_splits > 1) {
         const size_t need = attend_bytes(nq, b.n_splits, c.q_heads);
         if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for attention partials");

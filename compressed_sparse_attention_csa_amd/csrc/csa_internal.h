@@ -196,11 +196,22 @@ struct AttendArgs {
   float scale;
   int32_t k, W, R, r, bt_stride, pool_pages, H;
   int32_t n_sparse_blocks, n_blocks, blocks_per_split, n_splits, n_q;
+  int32_t act_f32;          // outputs are fp32 (else bf16)
   int32_t chunk;            // 1: queries are a chunk (seq0, pos0 + i)
   int32_t dense;            // 1: the sparse keys are every visible entry (topk unused)
   int32_t seq0, pos0, swa0;
   AttQuery qd[kAttMaxQ];
 };
+
+constexpr int kAttSplitMaxKeys = 2048;   // keys one decode-kernel workgroup resolves up front (32 blocks)
+constexpr int kAttDenseSplits = 40;      // splits per dense query the merge kernel takes in registers
+
+// Decode and dense attention with bf16 compute (kv: bf16, fp8 or fp4): one
+// workgroup per (query, split), key_streams (1 or 4) 64-key blocks side by
+// side per round, a.blocks_per_split blocks per split; with several splits the
+// merge kernel follows. n_wg = n_q x n_splits.
+void launch_attend_decode(const AttendArgs &a, int n_wg, int kv, bool ring_fp8, int key_streams, hipStream_t s,
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // ev0/ev1 (may be null): events stamped with the start and end of the attention kernel launch.
 void launch_attend(const AttendArgs &a, int n_wg, int kv, int act, bool ring_fp8, hipStream_t s,

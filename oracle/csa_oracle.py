@@ -30,7 +30,10 @@ Parity status per function (what pins it in ``tests/test_oracle.py``):
   index_scores .......... pure-Python brute force; H_I = 1, w = 1 -> ReLU(q.k)
   topk .................. brute-force full sort with hand-made tie fixtures
   attend / attend_step .. r = 1, k = all, W = 0 -> torch SDPA causal; k = 0 ->
-                          banded SDPA; single key; equal logits -> mean
+                          banded SDPA; single key; equal logits -> mean; with
+                          V = identity the output rows are the softmax weights,
+                          equal to torch.softmax of the same logits and summing
+                          to one
   hca_attend_step ....... r = 1, W = 0 -> torch SDPA causal; a pure-Python
                           loop softmax over the explicit key list
   e2m1_encode/decode .... the E2M1 value set from its bit layout; hand-worked
@@ -418,14 +421,6 @@ def hca_attend_step(q: np.ndarray, t: int, r: int, W: int, scale: float,
     """
     T = np.arange(visible_entries(t, r), dtype=np.int64)
     return attend_step(q, T, t, W, scale, kbar, vbar, rawk, rawv, swa_start)
-
-
-def softmax_weights(q: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
-    """The attention weights attend() uses (for the sums-to-one check)."""
-    logits = scale * (np.asarray(q, np.float64) @ np.asarray(keys, np.float64).T)
-    m = logits.max(axis=1, keepdims=True)
-    p = np.exp(logits - m)
-    return p / p.sum(axis=1, keepdims=True)
 
 
 # ---------------------------------------------------------------------------

@@ -16,6 +16,8 @@ from compressed_sparse_attention_csa_amd import synth as Sy
 from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
 from oracle import csa_oracle as O
 
+import parity_bounds as PB
+
 TORCH_ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
 TOL = {"f32": 2e-3, "bf16": 2e-2}
 
@@ -176,11 +178,31 @@ def max_abs(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
 
 
-def bf16_ulp(x: np.ndarray) -> np.ndarray:
-    _, e = np.frexp(np.abs(x))
-    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+# --------------------------------------------------------------------------- oracle entries with error bands
+
+def oracle_entries(K64, V64, Z64, r, P64=None):
+    """The oracle's compressed entries (float64, before rounding) and, for each
+    value, the band within which a correct fp32 implementation may differ
+    (parity_bounds.value_band of its absolute terms). Returns
+    (kbar, vbar, kidx, band_kbar, band_vbar, band_kidx); kidx and its band are
+    None without a projection."""
+    kb, vb, ki = O.compress(K64, V64, Z64, r, P64)
+    TK, TV, TI = PB.pooled_terms(K64, V64, Z64, r, P64)
+    bi = None if TI is None else PB.value_band(TI, 128 + r + 8)
+    return kb, vb, ki, PB.value_band(TK, r), PB.value_band(TV, r), bi
 
 
-def e4m3_ulp(x: np.ndarray) -> np.ndarray:
-    _, e = np.frexp(np.abs(x))
-    return np.ldexp(1.0, np.maximum(e, -5) - 4)
+def check_topk_chain(gpu_row, qi64, w64, ki64, band_ki, kdtype, n_vis, k, what=""):
+    """A Top-K row the GPU computed from keys it compressed itself, against the
+    oracle's keys (ki64, all stored entries of the sequence): exact within the
+    1e-6 relative band, except that keys whose stored codes may legitimately
+    differ (parity_bounds.key_score_slack) carry their score slack."""
+    dt = "fp8" if kdtype == "fp4" else kdtype
+    kis = O.store(ki64, dt)[0]
+    s = O.index_scores(qi64, w64, kis[:n_vis])
+    slack = PB.key_score_slack(qi64, w64, ki64, band_ki, dt)[:n_vis]
+    ok, msg = PB.topk_valid(gpu_row, s, k, slack)
+    assert ok, f"{what}: {msg}"
+    if msg:
+        print(f"[topk] {what}: {msg}; keys with slack > 0: {int(np.sum(slack > 0))} of {n_vis}")
+    return s

@@ -5,7 +5,11 @@ write oracle-made cache contents into the device pools, so index and attend
 are compared on identical inputs; chain tests run the whole step on each side
 from the same raw rows. Bars: Top-K sets exact except near-ties within 1e-6
 relative of the k-th oracle score; outputs max-abs 2e-3 (fp32) / 2e-2
-(bf16, fp8).
+(bf16, fp8). Where both sides compress the same raw rows, stored codes must
+equal the oracle's rounding except at rounding boundaries within the fp32
+error band (tests/parity_bounds.py), and a chained Top-K row must be a valid
+Top-K of the oracle's scores within 1e-6 relative plus the score slack of
+exactly those keys.
 """
 import math
 
@@ -18,8 +22,9 @@ from compressed_sparse_attention_csa_amd import synth as Sy
 from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
 from oracle import csa_oracle as O
 
-from gpu_helpers import (TOL, TORCH_ACT, bf16_ulp, e4m3_ulp, fill_index_keys, fill_main_kv, fill_ring, make_cache,
-                         max_abs, raw_rows, to64, topk_matches, unpack_fp4)
+import parity_bounds as PB
+from gpu_helpers import (TOL, TORCH_ACT, check_topk_chain, fill_index_keys, fill_main_kv, fill_ring, make_cache,
+                         max_abs, oracle_entries, raw_rows, to64, topk_matches, unpack_fp4)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,27 +115,29 @@ def _compress_case(kv, act, r, lens, seed=3, n_layers=1, chunks=None, swa=""):
     return cache, raw, P
 
 
-def _check_stored(cache, pool, scales, seq, n, x64, kv, what):
-    """GPU pool contents of one stream vs the oracle's rounding of x64."""
+def _check_stored(cache, pool, scales, seq, n, x64, band, kv, what):
+    """GPU pool contents of one stream vs the oracle's rounding of x64: fp32
+    values within the fp32 error band of the exact values; bf16 and E4M3
+    codes equal, except where a value lies within its error band of a rounding
+    boundary (then the other rounding is allowed, and counted); E4M3 page
+    scales within the uncertainty of their page's amax."""
     got_raw = cache.logical(pool, seq, n).cpu()
+    x64, band = x64[:n], band[:n]
     if kv == "f32":
-        got = got_raw.double().numpy()
-        err = np.abs(got - x64)
-        assert np.all(err <= 1e-5 * np.maximum(1.0, np.abs(x64))), (what, err.max())
-    elif kv == "bf16":
-        got = got_raw.double().numpy()
-        assert np.all(np.abs(got - x64) <= bf16_ulp(x64)), (what, np.max(np.abs(got - x64) / bf16_ulp(x64)))
+        err = np.abs(got_raw.double().numpy() - x64)
+        assert np.all(err <= band), (what, float(np.max(err / band)))
+        return
+    if kv == "bf16":
+        allowed, bad = PB.check_stored(got_raw.view(torch.int16).numpy().view(np.uint16), x64, band, "bf16")
     else:
-        _, (ocodes, oscales) = O.store(x64, "fp8")
+        codes, oscales, _, _, rel_s = PB.fp8_pages(x64, band)
         gs = cache.logical_scales(scales, seq, n).cpu().double().numpy()
-        np.testing.assert_allclose(gs, oscales, rtol=2e-6, err_msg=what)
-        pages = np.arange(n) // 64
-        got = O.e4m3_decode(got_raw.numpy()) * gs[pages][:, None]
-        ref = O.e4m3_decode(ocodes) * oscales[pages][:, None].astype(np.float64)
-        tol = e4m3_ulp(ref / oscales[pages][:, None]) * oscales[pages][:, None]
-        assert np.all(np.abs(got - ref) <= tol * 1.0001), (what, np.max(np.abs(got - ref) / tol))
-        same = np.mean(got_raw.numpy() == ocodes)
-        assert same > 0.99, (what, same)
+        os64 = oscales.astype(np.float64)
+        assert np.all(np.abs(gs - os64) <= os64 * (rel_s + 2 * PB.U32)), (what, "page scales")
+        allowed, bad = PB.check_stored(got_raw.numpy(), x64, band, "fp8")
+    assert bad == 0, f"{what}: {bad} codes differ from the oracle's rounding outside every error band"
+    if allowed:
+        print(f"[codes] {what}: {allowed} of {x64.size} codes at a rounding boundary take the other neighbour")
 
 
 @pytest.mark.parametrize("kv,act", DT_CASES)
@@ -140,13 +147,14 @@ def test_compress_matches_oracle(kv, act, r):
     cache, raw, P = _compress_case(kv, act, r, lens)
     for b, L in enumerate(lens):
         K, V, Z = (to64(t) for t in raw[0][b])
-        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        kb, vb, ki, bk, bv, bi = oracle_entries(K, V, Z, r, to64(P))
         n = L // r
         if n == 0:
             continue
-        _check_stored(cache, cache.kbar[0], cache.kbar_scale[0] if kv == "fp8" else None, b, n, kb, kv, f"kbar seq {b}")
-        _check_stored(cache, cache.vbar[0], cache.vbar_scale[0] if kv == "fp8" else None, b, n, vb, kv, f"vbar seq {b}")
-        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, kv, f"kidx seq {b}")
+        sc = kv == "fp8"
+        _check_stored(cache, cache.kbar[0], cache.kbar_scale[0] if sc else None, b, n, kb, bk, kv, f"kbar seq {b}")
+        _check_stored(cache, cache.vbar[0], cache.vbar_scale[0] if sc else None, b, n, vb, bv, kv, f"vbar seq {b}")
+        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, bi, kv, f"kidx seq {b}")
         # ring holds the last R raw rows, bit for bit
         R = cache.cfg.ring_rows
         rows = np.arange(max(0, L - R), L)
@@ -388,18 +396,17 @@ def _chain(kv, act, lens, k, W, seed=31, n_layers=1, H=16, r=4, dense=False, swa
         comp = {}
         for layer in range(n_layers):
             K, V, Z = raws[layer, b]
-            kb, vb, ki = O.compress(K, V, Z, r, P64 if layer == 0 else None)
+            kb, vb, ki, _, _, bi = oracle_entries(K, V, Z, r, P64 if layer == 0 else None)
             comp[layer] = (O.store(kb, kv)[0], O.store(vb, kv)[0], O.store_ring_rows(K, swa)[0],
                            O.store_ring_rows(V, swa)[0])
             if layer == 0:
                 kis = O.store(ki, "fp8" if kv == "fp4" else kv)[0]   # fp4 caches keep fp8 indexer keys
+                ki0, bi0 = ki, bi
         layers = [dict(q=to64(outs[l][0][b]), W=W, scale=scale, kbar=comp[l][0], vbar=comp[l][1], rawk=comp[l][2],
                        rawv=comp[l][3]) for l in range(n_layers)]
         To, oo = O.decode_step(to64(qi[b]), to64(w[b]), kis, r, k, L - 1, layers)
         N = O.visible_entries(L - 1, r)
-        s = O.index_scores(to64(qi[b]), to64(w[b]), kis[:N])
-        ok, msg = topk_matches(Tg[b], To, s, rel=1e-6 if kv == "f32" else 2e-2)
-        assert ok, f"seq {b}: {msg}"
+        check_topk_chain(Tg[b], to64(qi[b]), to64(w[b]), ki0, bi0, kv, N, k, f"seq {b}")
         for l in range(n_layers):
             err = max_abs(outs[l][1][b], oo[l])
             assert err <= TOL[act], f"seq {b} layer {l}: max-abs {err}"
@@ -688,21 +695,19 @@ def test_serving_steps_ragged_paged_fp8():
     Tg = T.cpu().numpy()
     for b in ids:
         K, V, Z = (to64(t) for t in raw[b])
-        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        kb, vb, ki, bk, bv, bi = oracle_entries(K, V, Z, r, to64(P))
         kis, kbs, vbs = O.store(ki, "fp8")[0], O.store(kb, "fp8")[0], O.store(vb, "fp8")[0]
         t = final[b] - 1
         N = O.visible_entries(t, r)
-        s = O.index_scores(to64(qi[b]), to64(w[b]), kis[:N])
+        s = check_topk_chain(Tg[b], to64(qi[b]), to64(w[b]), ki, bi, "fp8", N, k, f"request {b}")
         To = O.topk(s, k)
-        ok, msg = topk_matches(Tg[b], To, s, rel=2e-2)
-        assert ok, f"request {b}: {msg}"
         ref = O.attend_step(to64(q[b]), To, t, W, scale, kbs, vbs, K, V)
         assert max_abs(out[b], ref) <= 2e-2, f"request {b}: max-abs {max_abs(out[b], ref)}"
-        # the device pages equal a one-shot quantisation of the same entries
+        # the device pages after one-token appends equal a one-shot quantisation of the same entries
         n = final[b] // r
-        got = cache.logical(cache.kidx, b, n).cpu().numpy()
-        _, (codes, _) = O.store(ki[:n], "fp8")
-        assert np.mean(got == codes) > 0.99
+        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, bi, "fp8", f"request {b} kidx")
+        _check_stored(cache, cache.kbar[0], cache.kbar_scale[0], b, n, kb, bk, "fp8", f"request {b} kbar")
+        _check_stored(cache, cache.vbar[0], cache.vbar_scale[0], b, n, vb, bv, "fp8", f"request {b} vbar")
 
 
 # --------------------------------------------------------------------------- heavily compressed attention (no indexer)
@@ -931,16 +936,13 @@ def test_ring_replay_rewrites_window_only(swa):
     Tg = T.cpu().numpy()
     for b, L in enumerate(lens):
         K, V, Z = (to64(x) for x in raw[0][b])
-        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        kb, vb, ki, _, _, bi = oracle_entries(K, V, Z, r, to64(P))
         N = O.visible_entries(L - 1, r)
-        kis = O.store(ki, "fp8")[0]
-        To = O.topk(O.index_scores(to64(qi[b]), to64(w[b]), kis[:N]), k)
-        ok, msg = topk_matches(Tg[b], To, O.index_scores(to64(qi[b]), to64(w[b]), kis[:N]), rel=2e-2)
-        assert ok, msg
+        To = O.topk(check_topk_chain(Tg[b], to64(qi[b]), to64(w[b]), ki, bi, "fp8", N, k, f"seq {b}"), k)
         Kr, Vr = K.copy(), V.copy()
         Kr[s0[b]:], Vr[s0[b]:] = to64(newk[b]), to64(newv[b])
         Kr, Vr = O.store_ring_rows(Kr, swa)[0], O.store_ring_rows(Vr, swa)[0]
-        ref = O.attend_step(to64(q[b]), Tg[b][Tg[b] >= 0], L - 1, W, scale, O.store(kb, "fp8")[0],
+        ref = O.attend_step(to64(q[b]), To, L - 1, W, scale, O.store(kb, "fp8")[0],
                             O.store(vb, "fp8")[0], Kr, Vr, s0[b])
         assert max_abs(out[b], ref) <= TOL["bf16"]
 
@@ -981,24 +983,21 @@ def test_device_fp4_codecs():
     np.testing.assert_array_equal(codes.cpu().numpy(), O.e2m1_encode(x))
 
 
-def _check_fp4(cache, pool, gpool, seq, n, x64, what, exact):
+def _check_fp4(cache, pool, gpool, seq, n, x64, band, what, exact):
     """GPU fp4 entries of one stream vs the oracle's quantisation of x64: every
-    code and scale equal when the GPU's fp32 entries are the oracle's (exact),
-    else at least 99 % of them, and every GPU value a valid quantisation of x64."""
+    code and group scale equal when the GPU's fp32 entries are the oracle's
+    (exact); otherwise equal except where a group amax / 6 or an element's
+    quotient lies within its error band of a rounding boundary (counted)."""
     codes = unpack_fp4(cache.logical(pool, seq, n).cpu().numpy())
     gsc = cache.logical(gpool, seq, n).cpu().numpy()
-    _, (oc, osc) = O.store(x64, "fp4")
+    _, (oc, osc) = O.store(x64[:n], "fp4")
     if exact:
         assert np.array_equal(codes, oc) and np.array_equal(gsc, osc), what
         return
-    assert np.mean(codes == oc) > 0.99 and np.mean(gsc == osc) > 0.99, (what, np.mean(codes == oc), np.mean(gsc == osc))
-    deq = O.fp4_dequantize_rows(codes, gsc)
-    s = O.e4m3_decode(gsc)
-    g = np.abs(x64).reshape(n, 8, 16) / np.where(s > 0, s, 1)[..., None]
-    half = np.where(g < 2, 0.25, np.where(g < 4, 0.5, 1.0)) * s[..., None]
-    clip = np.maximum(0, g - 6.0) * s[..., None]
-    err = np.abs(deq - x64).reshape(n, 8, 16)
-    assert np.all(err <= half + clip + 1e-6 * np.abs(x64).reshape(n, 8, 16).max() + 1e-12), what
+    allowed, bad = PB.check_fp4(codes, gsc, x64[:n], band[:n])
+    assert bad == 0, f"{what}: {bad} fp4 codes differ from the oracle's quantisation outside every error band"
+    if allowed:
+        print(f"[codes] {what}: {allowed} fp4 codes at a rounding boundary take the other neighbour")
 
 
 @pytest.mark.parametrize("r", [1, 4])
@@ -1009,13 +1008,13 @@ def test_compress_fp4_matches_oracle(r):
     cache, raw, P = _compress_case("fp4", "bf16", r, lens)
     for b, L in enumerate(lens):
         K, V, Z = (to64(t) for t in raw[0][b])
-        kb, vb, ki = O.compress(K, V, Z, r, to64(P))
+        kb, vb, ki, bk, bv, bi = oracle_entries(K, V, Z, r, to64(P))
         n = L // r
         if n == 0:
             continue
-        _check_fp4(cache, cache.kbar[0], cache.kbar_gscale[0], b, n, kb, f"kbar seq {b}", exact=r == 1)
-        _check_fp4(cache, cache.vbar[0], cache.vbar_gscale[0], b, n, vb, f"vbar seq {b}", exact=r == 1)
-        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, "fp8", f"kidx seq {b}")
+        _check_fp4(cache, cache.kbar[0], cache.kbar_gscale[0], b, n, kb, bk, f"kbar seq {b}", exact=r == 1)
+        _check_fp4(cache, cache.vbar[0], cache.vbar_gscale[0], b, n, vb, bv, f"vbar seq {b}", exact=r == 1)
+        _check_stored(cache, cache.kidx, cache.kidx_scale, b, n, ki, bi, "fp8", f"kidx seq {b}")
     assert cache.read_errors() == 0
 
 

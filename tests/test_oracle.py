@@ -322,8 +322,13 @@ def test_attend_degenerate_cases():
     vals1 = vals.copy()
     vals1[:, 3] = 1.0
     np.testing.assert_allclose(O.attend(q, keys, vals1, 0.3)[:, 3], 1.0, atol=1e-14)
-    p = O.softmax_weights(q, keys, 0.3)
+    # V = identity: each output row is that head's weight vector over the keys,
+    # which must be torch's softmax of the same scaled logits and sum to one
+    p = O.attend(q, keys, np.eye(keys.shape[0]), 0.3)
+    ref = torch.softmax(torch.from_numpy(0.3 * (q @ keys.T)), dim=1).numpy()
+    np.testing.assert_allclose(p, ref, rtol=0, atol=1e-15)
     np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(p > 0)
     assert O.attend(q, np.zeros((0, D)), np.zeros((0, D)), 1.0).shape == (H, D)
 
 
