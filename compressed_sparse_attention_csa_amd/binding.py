@@ -80,7 +80,7 @@ EXPORTS = [
     "csa_compress", "csa_index_topk", "csa_attend", "csa_read_errors",
     "csa_profile_begin", "csa_profile_end", "csa_debug_convert", "csa_attend_dense",
     "csa_seq_set_swa_start", "csa_ring_write", "csa_index_topk_pool", "csa_index_reindex",
-    "csa_debug_stream_read",
+    "csa_debug_stream_read", "csa_attend_noalloc",
 ]
 
 _LIB = None
@@ -125,6 +125,8 @@ def lib() -> C.CDLL:
     L.csa_index_reindex.argtypes = [vp, i32, pi32, pi32, vp, vp, i32, vp, i32, vp, vp]
     L.csa_attend.restype = C.c_int
     L.csa_attend.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, i32, C.c_float, vp, vp]
+    L.csa_attend_noalloc.restype = C.c_int
+    L.csa_attend_noalloc.argtypes = [vp, i32, i32, pi32, pi32, vp, vp, i32, C.c_float, vp, vp]
     L.csa_attend_dense.restype = C.c_int
     L.csa_attend_dense.argtypes = [vp, i32, i32, pi32, pi32, vp, C.c_float, vp, vp]
     L.csa_seq_set_swa_start.restype = C.c_int
@@ -235,6 +237,11 @@ def csa_index_reindex(h: int, q_seq, q_pos, q_idx, w_idx, n_pool_blocks: int, po
 def csa_attend(h: int, layer: int, q_seq, q_pos, q, topk, k: int, scale: float, out, stream=None) -> None:
     check(lib().csa_attend(C.c_void_p(h), layer, len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q), _ptr(topk),
                            k, float(scale), _ptr(out), _stream(stream)))
+
+
+def csa_attend_noalloc(h: int, layer: int, q_seq, q_pos, q, topk, k: int, scale: float, out, stream=None) -> None:
+    check(lib().csa_attend_noalloc(C.c_void_p(h), layer, len(q_seq), _i32(q_seq), _i32(q_pos), _ptr(q), _ptr(topk),
+                                   k, float(scale), _ptr(out), _stream(stream)))
 
 
 def csa_attend_dense(h: int, layer: int, q_seq, q_pos, q, scale: float, out, stream=None) -> None:

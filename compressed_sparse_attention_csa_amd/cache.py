@@ -161,6 +161,12 @@ class CsaCache:
         B.csa_attend(self.handle, layer, q_seq, q_pos, q, topk, k, scale, out, stream)
         return out
 
+    def attend_noalloc(self, layer, q_seq, q_pos, q, topk, k, scale, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        B.csa_attend_noalloc(self.handle, layer, q_seq, q_pos, q, topk, k, scale, out, stream)
+        return out
+
     def attend_dense(self, layer, q_seq, q_pos, q, scale, out=None, stream=None):
         if out is None:
             out = torch.empty_like(q)

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -15,6 +16,13 @@
 #include "csa_internal.h"
 
 using namespace csa;
+
+// Scratch of csa_attend_noalloc: a device array of this library, one copy per
+// GPU the library runs on, held until the process ends. Host code never uses
+// the array's name as an address: each device's copy is looked up once, with
+// that device current, and kept per device (static_scratch below).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 struct csa_cache {
   uint64_t magic;
@@ -48,6 +56,29 @@ csa_status fail(csa_status s, const char *fmt, ...) {
 }
 
 bool handle_ok(csa_cache_t h) { return h != nullptr && h->magic == kMagic; }
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (nullptr on failure, with the message set).
+char *static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(CSA_ERR_HIP, "no current device for the static scratch");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      fail(CSA_ERR_HIP, "hipGetSymbolAddress of the static scratch failed on device %d", dev);
+      return nullptr;
+    }
+    scratch_ptr[dev] = p;
+  }
+  return static_cast<char *>(scratch_ptr[dev]);
+}
 
 int dt_bytes(int dt) { return dt == CSA_F32 ? 4 : (dt == CSA_BF16 ? 2 : 1); }
 
@@ -806,9 +837,11 @@ namespace {
 
 // Shared by csa_attend (keys = the Top-K rows) and csa_attend_dense (keys =
 // every visible entry: topk is NULL and k is replaced by the largest visible count).
+// scratch: where the split partials go (the handle's workspace, or the static
+// scratch of csa_attend_noalloc, which also records no profiling events)
 csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
                        const void *q, const int32_t *topk, int32_t k, bool dense, float scale, void *out,
-                       hipStream_t stream) {
+                       hipStream_t stream, char *scratch_base, size_t scratch_bytes, bool profile) {
   if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
   const csa_config &c = h->cfg;
   if (layer < 0 || layer >= c.n_layers) return fail(CSA_ERR_INVALID_ARG, "layer %d out of range", layer);
@@ -865,7 +898,7 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
     a.q = q; a.out = out; a.topk = topk;
     a.chunk = 1; a.seq0 = q_seq[0]; a.pos0 = q_pos[0]; a.swa0 = h->swa_start[q_seq[0]];
     a.blocks_per_split = std::max(1, a.n_blocks); a.n_splits = 1; a.n_q = n_q;
-    const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
+    const ProfPair ev = profile ? prof_events(h, stream, CSA_PROFILE_ATTEND) : ProfPair{};
     launch_attend(a, n_q, kv, act, ring8, stream, ev.start, ev.stop);
   } else if (kv != DT_F32) {
     // decode and dense queries: one 64-key block per workgroup for a decode
@@ -897,11 +930,12 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       b.n_splits = splits;
       if (splits > 1) {
         const size_t need = attend_bytes(nq, splits, c.q_heads);
-        if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for attention partials");
-        b.part_o = reinterpret_cast<float *>(h->scratch);
-        b.part_ml = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(nq) * splits * c.q_heads * kD * 4, 256));
+        if (need > scratch_bytes)
+          return fail(CSA_ERR_CAPACITY, "attention partials need %zu bytes of scratch, %zu available", need, scratch_bytes);
+        b.part_o = reinterpret_cast<float *>(scratch_base);
+        b.part_ml = reinterpret_cast<float *>(scratch_base + align_up(static_cast<size_t>(nq) * splits * c.q_heads * kD * 4, 256));
       }
-      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
+      const ProfPair ev = profile ? prof_events(h, stream, CSA_PROFILE_ATTEND) : ProfPair{};
       launch_attend_decode(b, nq * splits, kv, ring8, ks, stream, ev.start, ev.stop);
     }
   } else {
@@ -923,11 +957,12 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       if (b.n_splits > kAttMaxSplits) return fail(CSA_ERR_UNSUPPORTED, "too many attention splits per query");
       if (b.n_splits > 1) {
         const size_t need = attend_bytes(nq, b.n_splits, c.q_heads);
-        if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small for attention partials");
-        b.part_o = reinterpret_cast<float *>(h->scratch);
-        b.part_ml = reinterpret_cast<float *>(h->scratch + align_up(static_cast<size_t>(nq) * b.n_splits * c.q_heads * kD * 4, 256));
+        if (need > scratch_bytes)
+          return fail(CSA_ERR_CAPACITY, "attention partials need %zu bytes of scratch, %zu available", need, scratch_bytes);
+        b.part_o = reinterpret_cast<float *>(scratch_base);
+        b.part_ml = reinterpret_cast<float *>(scratch_base + align_up(static_cast<size_t>(nq) * b.n_splits * c.q_heads * kD * 4, 256));
       }
-      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_ATTEND);
+      const ProfPair ev = profile ? prof_events(h, stream, CSA_PROFILE_ATTEND) : ProfPair{};
       launch_attend(b, nq * b.n_splits, kv, act, ring8, stream, ev.start, ev.stop);
     }
   }
@@ -939,12 +974,26 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
 
 csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos, const void *q,
                       const int32_t *topk, int32_t k, float scale, void *out, hipStream_t stream) {
-  return attend_impl(h, layer, n_q, q_seq, q_pos, q, topk, k, false, scale, out, stream);
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  return attend_impl(h, layer, n_q, q_seq, q_pos, q, topk, k, false, scale, out, stream, h->scratch, h->scratch_bytes,
+                     true);
+}
+
+csa_status csa_attend_noalloc(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
+                              const void *q, const int32_t *topk, int32_t k, float scale, void *out,
+                              hipStream_t stream) {
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  char *p = static_scratch();
+  if (!p) return CSA_ERR_HIP;
+  return attend_impl(h, layer, n_q, q_seq, q_pos, q, topk, k, false, scale, out, stream, p, kStaticScratchBytes,
+                     false);
 }
 
 csa_status csa_attend_dense(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq, const int32_t *q_pos,
                             const void *q, float scale, void *out, hipStream_t stream) {
-  return attend_impl(h, layer, n_q, q_seq, q_pos, q, nullptr, 0, true, scale, out, stream);
+  if (!handle_ok(h)) return fail(CSA_ERR_INVALID_ARG, "invalid handle");
+  return attend_impl(h, layer, n_q, q_seq, q_pos, q, nullptr, 0, true, scale, out, stream, h->scratch,
+                     h->scratch_bytes, true);
 }
 
 csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags) {

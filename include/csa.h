@@ -22,7 +22,8 @@
  * - Every pointer named "dev" is device memory; every other pointer is host
  *   memory. The library never allocates device memory: the caller allocates
  *   every buffer (e.g. torch tensors) and keeps it alive while the handle
- *   lives. Nothing here synchronises a stream except csa_read_errors().
+ *   lives. (The one exception is csa_attend_noalloc's fixed device array,
+ *   part of the library's code object.) Nothing here synchronises a stream except csa_read_errors().
  * - All work is enqueued on the caller's stream, in call order. A handle is
  *   not thread-safe and must be used from one stream at a time.
  * - Every entry point validates its arguments on the host before enqueuing
@@ -321,6 +322,26 @@ csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, c
 csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
                       const int32_t *q_pos, const void *q, const int32_t *topk, int32_t k, float scale,
                       void *out, hipStream_t stream);
+
+/*
+ * csa_attend_noalloc - csa_attend for callers that cannot allocate or pass
+ * scratch memory per call (code under HIP graph capture that must not touch
+ * the handle's workspace, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, results and errors as csa_attend; the split
+ * partials go to a fixed 16 MiB device array of the library (one per GPU,
+ * held until the process ends; its address is looked up on the first call on
+ * each device) instead of the handle's workspace. Nothing is allocated and
+ * nothing needs clearing: every partial is written before it is read.
+ * A call needs n_q x splits x (H x D + 2 H) x 4 bytes of it (at most 80
+ * splits per query; a decode query has one split per 64 keys of Top-K and
+ * window): CSA_ERR_CAPACITY when that exceeds 16 MiB, before any launch.
+ * All calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads, other handles) race and must be serialised by the
+ * caller. Records no profiling events.
+ */
+csa_status csa_attend_noalloc(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
+                              const int32_t *q_pos, const void *q, const int32_t *topk, int32_t k, float scale,
+                              void *out, hipStream_t stream);
 
 /*
  * csa_attend_dense - heavily compressed attention (HCA): one softmax over every
