@@ -192,6 +192,13 @@ bool is_chunk(int n, const int32_t *seq, const int32_t *pos) {
   return true;
 }
 
+// A chunk is indexed as one (shared score GEMM, per-query candidate select)
+// while its last query sees at most kChunkMaxEntries entries; past that, query
+// by query (the decode path scans up to 2M entries per query).
+bool index_as_chunk(const csa_config &c, int n, const int32_t *seq, const int32_t *pos) {
+  return is_chunk(n, seq, pos) && (static_cast<int64_t>(pos[n - 1]) + 1) / c.ratio <= kChunkMaxEntries;
+}
+
 // Event pair for the next profiled launch, or {nullptr, nullptr} when profiling
 // is off or the stream is being captured. The launcher hands the pair to
 // hipExtLaunchKernelGGL, which stamps them with the kernel's own start and end.
@@ -667,7 +674,9 @@ csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, con
     for (int i = 0; i < nq; ++i) nmax = std::max(nmax, (q_pos[g0 + i] + 1) / c.ratio);
     const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(nmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
     const size_t need = idx_decode_bytes(nq, s_stride);
-    if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small (%zu > %zu bytes)", need, h->scratch_bytes);
+    if (need > h->scratch_bytes)
+      return fail(CSA_ERR_CAPACITY, "workspace too small for %d queries indexed one by one (%zu > %zu bytes)", nq, need,
+                  h->scratch_bytes);
     const DecodeScratch d = carve_decode(h, nq, s_stride);
 
     IdxScanArgs s{};
@@ -739,8 +748,9 @@ csa_status csa_index_topk(csa_cache_t h, int32_t n_q, const int32_t *q_seq, cons
                           const float *w_idx, int32_t k, int32_t *topk, hipStream_t stream) {
   csa_status st = check_index_args(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk);
   if (st != CSA_OK) return st;
-  st = is_chunk(n_q, q_seq, q_pos) ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream)
-                                   : index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream);
+  st = index_as_chunk(h->cfg, n_q, q_seq, q_pos)
+           ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream)
+           : index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, 0, nullptr, stream);
   if (st != CSA_OK) return st;
   if (hipGetLastError() != hipSuccess) return fail(CSA_ERR_HIP, "kernel launch failed in csa_index_topk");
   return CSA_OK;
@@ -754,7 +764,7 @@ csa_status csa_index_topk_pool(csa_cache_t h, int32_t n_q, const int32_t *q_seq,
   if (n_pool_blocks < 1 || n_pool_blocks > CSA_MAX_POOL_BLOCKS)
     return fail(CSA_ERR_UNSUPPORTED, "n_pool_blocks = %d outside [1, %d]", n_pool_blocks, CSA_MAX_POOL_BLOCKS);
   if (!pool) return fail(CSA_ERR_INVALID_ARG, "pool is required");
-  st = is_chunk(n_q, q_seq, q_pos)
+  st = index_as_chunk(h->cfg, n_q, q_seq, q_pos)
            ? index_chunk(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream)
            : index_per_query(h, n_q, q_seq, q_pos, q_idx, w_idx, k, topk, n_pool_blocks, pool, stream);
   if (st != CSA_OK) return st;
@@ -787,7 +797,9 @@ csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, c
     }
     const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(vmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
     const size_t need = idx_decode_bytes(nq, s_stride);
-    if (need > h->scratch_bytes) return fail(CSA_ERR_CAPACITY, "workspace too small (%zu > %zu bytes)", need, h->scratch_bytes);
+    if (need > h->scratch_bytes)
+      return fail(CSA_ERR_CAPACITY, "workspace too small for %d queries indexed one by one (%zu > %zu bytes)", nq, need,
+                  h->scratch_bytes);
     const DecodeScratch d = carve_decode(h, nq, s_stride);
     IdxRescanArgs s{};
     s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;

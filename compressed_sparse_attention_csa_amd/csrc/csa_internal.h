@@ -122,6 +122,8 @@ struct IdxFinalArgs {
 constexpr int kChunkSample = 16;     // the sample GEMM scores entries 16m + 15
 constexpr int kChunkCandCap = 4096;  // candidates one select keeps in LDS
 constexpr int kChunkTileCand = 64;   // candidate slots per (query, 256-entry tile)
+constexpr int kChunkMaxTiles = 1024; // 256-entry tiles per query the chunk select takes
+constexpr int kChunkMaxEntries = kChunkMaxTiles * 256;   // larger chunks are indexed query by query
 
 struct IdxChunkArgs {
   const void *kidx;

@@ -88,8 +88,19 @@ __device__ uint64_t kth_largest_u64(Get get, int n, int k, int *hist, int *sh) {
 // included, are negative integers); no NaN quieting step.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Sort keys: a score's 32 bits in an order-preserving form (non-negative
+// scores get the sign bit set, negative ones - a missing page's -1 - have
+// every bit flipped, so they sort below every real score; -0 counts as +0),
+// then ~index so that equal scores go to the lower index.
+__device__ __forceinline__ uint32_t score_bits(float s) {
+  const uint32_t u = s == 0.f ? 0u : __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float bits_score(uint32_t b) {
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
 __device__ __forceinline__ uint64_t score_key(float s, int j) {
-  return (static_cast<uint64_t>(__float_as_uint(s)) << 32) | static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(j));
+  return (static_cast<uint64_t>(score_bits(s)) << 32) | static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(j));
 }
 __device__ __forceinline__ int key_index(uint64_t key) {
   return static_cast<int>(0xffffffffu - static_cast<uint32_t>(key & 0xffffffffull));
@@ -283,7 +294,7 @@ __device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *his
 
 
 // Exact Top-K of c candidates held in LDS in ascending index order (keys
-// cand_key[i] = score bits << 32 | ~index, scores >= 0), written ascending
+// cand_key[i] = score_key(score, index)), written ascending
 // into out[0..k), c >= k. The k-th largest key is found without sorting:
 // a linear histogram of the scores locates the bin b* holding it; every
 // candidate in a higher bin is selected; inside b* the (k - above) largest
@@ -299,14 +310,14 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6, nw = bd >> 6;
   float lo = INFINITY, hi = -INFINITY;
   for (int i = t; i < c; i += bd) {
-    const float v = __uint_as_float(static_cast<uint32_t>(cand_key[i] >> 32));
+    const float v = bits_score(static_cast<uint32_t>(cand_key[i] >> 32));
     lo = fminf(lo, v);
     hi = fmaxf(hi, v);
   }
   block_reduce_minmax(lo, hi, red);
   const float sc = hi > lo ? static_cast<float>(kSelBins - 1) / (hi - lo) : 0.f;
   auto bin_of = [&](uint64_t key) {
-    return min(kSelBins - 1, static_cast<int>((__uint_as_float(static_cast<uint32_t>(key >> 32)) - lo) * sc));
+    return min(kSelBins - 1, static_cast<int>((bits_score(static_cast<uint32_t>(key >> 32)) - lo) * sc));
   };
   for (int i = t; i < kSelBins; i += bd) hist[i] = 0;
   __syncthreads();
@@ -844,7 +855,8 @@ constexpr int kWgCand = kChunkTileCand;
 constexpr int kChunkTilesPerWg = 4;   // entry tiles a full-score workgroup walks (next tile prefetched)
 // the sample pass touches 64 pages per tile and has few tiles: one tile per workgroup
 template <int MODE> constexpr int chunk_tiles_per_wg() { return MODE == 0 ? 1 : kChunkTilesPerWg; }
-constexpr int kMaxChunkTiles = 1024;  // entry tiles per query the select accepts (262,144 entries)
+constexpr int kMaxChunkTiles = kChunkMaxTiles;  // entry tiles per query the select accepts (262,144 entries)
+static_assert(kMaxChunkTiles * kCE == kChunkMaxEntries, "host routing and the select agree on the limit");
 
 template <int ACT, int KV, int MODE>
 __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs a) {
@@ -1095,20 +1107,25 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
     return;
   }
   // per-tile candidate counts of this query -> offsets (tiles past its visible range hold none)
+  // (the host sends longer rows query by query; a longer one here goes to the fallback)
   const int n_tiles = (N + kCE - 1) / kCE;
+  const bool fits = n_tiles <= kMaxChunkTiles;
   const int32_t *tc = a.cnt + static_cast<int64_t>(qi) * a.n_etiles;
-  if (tid == 0) { toff[0] = 0; sh[3] = 0; }
+  if (tid == 0) { toff[0] = 0; sh[3] = fits ? 0 : 1; }
   __syncthreads();
-  for (int i = tid; i < n_tiles; i += bd) {
-    const int v = tc[i];
-    if (v > kWgCand) sh[3] = 1;          // a tile overflowed its slots
-    toff[i + 1] = min(v, kWgCand);
+  int c = 0;
+  if (fits) {
+    for (int i = tid; i < n_tiles; i += bd) {
+      const int v = tc[i];
+      if (v > kWgCand) sh[3] = 1;          // a tile overflowed its slots
+      toff[i + 1] = min(v, kWgCand);
+    }
+    __syncthreads();
+    block_prefix_sum(toff, n_tiles, wsum);
+    c = toff[n_tiles];
   }
-  __syncthreads();
-  block_prefix_sum(toff, n_tiles, wsum);
-  const int c = toff[n_tiles];
   bool done = false;
-  if (sh[3] == 0 && c >= k && c <= kChunkCandCap && n_tiles <= kMaxChunkTiles) {
+  if (sh[3] == 0 && c >= k && c <= kChunkCandCap) {
     const uint64_t *cq = a.cand + static_cast<int64_t>(qi) * a.n_etiles * kWgCand;
     // the tile of every candidate position, written tile by tile (bin_keys is
     // free until the select; c <= kChunkCandCap 16-bit entries fit it)

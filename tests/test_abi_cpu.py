@@ -42,7 +42,7 @@ def _spec(**kw):
     return c
 
 
-def _fake_handle(cfg, n_layers=None):
+def _fake_handle(cfg, n_layers=None, workspace_bytes=None):
     """A handle over placeholder (never dereferenced) addresses."""
     b = B.Buffers()
     n = n_layers or cfg.n_layers
@@ -53,7 +53,7 @@ def _fake_handle(cfg, n_layers=None):
             getattr(b, f)[l] = fake
     b.kidx = b.kidx_scale = b.kidx_stage = b.block_table = fake
     b.workspace = 0x100000
-    b.workspace_bytes = B.csa_workspace_size(cfg, 8, 512)
+    b.workspace_bytes = workspace_bytes or B.csa_workspace_size(cfg, 8, 512)
     return B.csa_cache_create(cfg, b)
 
 
@@ -351,3 +351,29 @@ def test_fp4_config_sizes_and_buffers():
     for l in range(cfg.n_layers):
         b.kbar_gscale[l] = b.vbar_gscale[l] = 0x10000
     B.csa_cache_destroy(B.csa_cache_create(cfg, b))
+
+
+def test_long_chunks_are_indexed_query_by_query():
+    """A chunk whose last query sees more entries than the chunk select takes
+    (262,144) is planned by the per-query index path, which scans up to 2M
+    entries a query; a shorter chunk by the chunk path. A 1 MiB workspace fits
+    neither plan, so each shows itself through its own capacity error, raised
+    on the host before anything is enqueued."""
+    cfg = _spec(n_layers=1, max_seqs=1, max_pages_per_seq=4300, pool_pages=4300)
+    h = _fake_handle(cfg, workspace_bytes=1 << 20)
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    s = C.c_void_p(0)
+    i32 = B._i32
+    try:
+        for n_vis, plan in ((4200 * 64, b"one by one"), (262144, b"-token chunk"), (200000, b"-token chunk")):
+            length = 4 * n_vis + 3
+            B.csa_seq_set_len(h, 0, 0, length)
+            pos = list(range(length - 8, length))
+            assert L.csa_index_topk(C.c_void_p(h), 8, i32([0] * 8), i32(pos), fake, fake, 16, fake, s) == 4
+            assert plan in L.csa_last_error(), (n_vis, L.csa_last_error())
+            assert L.csa_index_topk_pool(C.c_void_p(h), 8, i32([0] * 8), i32(pos), fake, fake, 16, fake, 64,
+                                         fake, s) == 4
+            assert plan in L.csa_last_error(), (n_vis, L.csa_last_error())
+    finally:
+        B.csa_cache_destroy(h)

@@ -525,6 +525,31 @@ def test_bad_page_ids_are_flagged_not_faulting():
     assert cache.read_errors() & B.ERR_TOPK
 
 
+@pytest.mark.parametrize("n_tok", [1, 8])
+def test_bad_pages_lose_the_exact_fallback(n_tok):
+    """All-zero indexer queries tie every real entry at score 0, which sends the
+    decode select (n_tok = 1) and the chunk select (n_tok = 8) to the exact
+    full-row fallback. There the entries of pages whose ids lie outside the pool
+    score below every real entry, so the Top-K is the lowest-index real entries
+    and skips those pages."""
+    r, n, k = 4, 16000, 64
+    L = r * n
+    cache = make_cache(62, ratio=r, q_heads=16, window=16, ring_rows=32, max_seqs=1, max_pages_per_seq=n // 64 + 2,
+                       pool_pages=n // 64 + 4, kv_dtype="bf16", act_dtype="bf16", max_queries=n_tok, max_k=k)
+    fill_index_keys(cache, 62, 0, n)
+    B.csa_seq_set_len(cache.handle, 0, 0, L)
+    cache.block_table[0, 0] = 1000      # outside the pool
+    cache.block_table[0, 2] = -7
+    qi = torch.zeros((n_tok, 4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((n_tok, 4), device="cuda")
+    T = cache.index_topk([0] * n_tok, list(range(L - n_tok, L)), qi, w, k).cpu().numpy()
+    flags = cache.read_errors()
+    assert flags & B.ERR_PAGE and flags & B.ERR_FALLBACK, flags
+    want = np.arange(64, 64 + k, dtype=np.int32)     # page 1, the first page with a valid id
+    for i in range(n_tok):
+        assert np.array_equal(T[i], want), f"query {i}: {T[i][:8]}..."
+
+
 def test_graph_replay_matches_eager():
     """The decode step captured in a HIP graph: every replay, with eager work in
     between, reproduces the eager outputs bit for bit."""
