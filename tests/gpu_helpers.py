@@ -197,12 +197,57 @@ def check_topk_chain(gpu_row, qi64, w64, ki64, band_ki, kdtype, n_vis, k, what="
     oracle's keys (ki64, all stored entries of the sequence): exact within the
     1e-6 relative band, except that keys whose stored codes may legitimately
     differ (parity_bounds.key_score_slack) carry their score slack."""
-    dt = "fp8" if kdtype == "fp4" else kdtype
-    kis = O.store(ki64, dt)[0]
-    s = O.index_scores(qi64, w64, kis[:n_vis])
-    slack = PB.key_score_slack(qi64, w64, ki64, band_ki, dt)[:n_vis]
-    ok, msg = PB.topk_valid(gpu_row, s, k, slack)
-    assert ok, f"{what}: {msg}"
-    if msg:
-        print(f"[topk] {what}: {msg}; keys with slack > 0: {int(np.sum(slack > 0))} of {n_vis}")
-    return s
+    return TopkRows(ki64, band_ki, kdtype).check(gpu_row, qi64, w64, n_vis, k, what)
+
+
+def check_stored_pool(cache, pool, scales, seq, n, x64, band, kv, what):
+    """GPU pool contents of one stream vs the oracle's rounding of x64: fp32
+    values within the fp32 error band of the exact values; bf16 and E4M3
+    codes equal, except where a value lies within its error band of a rounding
+    boundary (then the other rounding is allowed, and counted); E4M3 page
+    scales within the uncertainty of their page's amax."""
+    got_raw = cache.logical(pool, seq, n).cpu()
+    x64, band = x64[:n], band[:n]
+    if kv == "f32":
+        err = np.abs(got_raw.double().numpy() - x64)
+        assert np.all(err <= band), (what, float(np.max(err / band)))
+        return
+    if kv == "bf16":
+        allowed, bad = PB.check_stored(got_raw.view(torch.int16).numpy().view(np.uint16), x64, band, "bf16")
+    else:
+        codes, oscales, _, _, rel_s = PB.fp8_pages(x64, band)
+        gs = cache.logical_scales(scales, seq, n).cpu().double().numpy()
+        os64 = oscales.astype(np.float64)
+        assert np.all(np.abs(gs - os64) <= os64 * (rel_s + 2 * PB.U32)), (what, "page scales")
+        allowed, bad = PB.check_stored(got_raw.numpy(), x64, band, "fp8")
+    assert bad == 0, f"{what}: {bad} codes differ from the oracle's rounding outside every error band"
+    if allowed:
+        print(f"[codes] {what}: {allowed} of {x64.size} codes at a rounding boundary take the other neighbour")
+
+
+class TopkRows:
+    """The oracle's indexer keys of one sequence (float64 before rounding, with
+    their fp32 error bands), stored as the cache stores them, against which
+    many Top-K rows are checked: scores of the stored keys, and per key the
+    slack that legitimate code flips allow (parity_bounds.key_slack_parts)."""
+
+    def __init__(self, ki64, band_ki, kdtype):
+        self.dt = "fp8" if kdtype == "fp4" else kdtype   # fp4 caches keep fp8 indexer keys
+        self.kis = O.store(ki64, self.dt)[0]
+        self.M, self.rel = PB.key_slack_parts(ki64, band_ki, self.dt)
+
+    def scores(self, qi64, w64, n_vis):
+        return O.index_scores(qi64, w64, self.kis[:n_vis])
+
+    def slack(self, qi64, w64, s, n_vis):
+        coef = (np.asarray(w64, np.float64)[:, None] * np.abs(np.asarray(qi64, np.float64))).sum(axis=0)
+        return self.M[:n_vis] @ coef + self.rel[:n_vis] * np.abs(np.asarray(s, np.float64))
+
+    def check(self, gpu_row, qi64, w64, n_vis, k, what=""):
+        """Assert the GPU row is a valid Top-k; returns the oracle's scores."""
+        s = self.scores(qi64, w64, n_vis)
+        ok, msg = PB.topk_valid(gpu_row, s, k, self.slack(qi64, w64, s, n_vis))
+        assert ok, f"{what}: {msg}"
+        if msg:
+            print(f"[topk] {what}: {msg}")
+        return s

@@ -203,6 +203,30 @@ def check_fp4(got_codes, got_gsc, x64, band_x):
 
 # --------------------------------------------------------------------------- indexer scores
 
+def key_slack_parts(x64: np.ndarray, band_x: np.ndarray, dtype: str, page: int = 64):
+    """The query-independent parts of key_score_slack: per key j and dimension
+    d, how far the stored key's dequantised value may move (M[j, d]: one grid
+    step plus the band where the code may flip, else 0), and the relative
+    uncertainty of its page scale (rel[j], fp8 only). The slack of a query
+    (q_idx, w) is then M @ sum_h w_h |q_h| + rel * |score|."""
+    E = x64.shape[0]
+    if dtype == "f32":
+        return np.zeros((E, x64.shape[1])), np.zeros(E)
+    if dtype == "bf16":
+        x32 = O.round_f32(x64).astype(np.float64)
+        b = band_x + U32 * np.abs(x64)
+        near = near_midpoint(x32, b, "bf16")
+        step, _ = _grid(np.abs(x32) + b, "bf16")
+        return near * (step + b), np.zeros(E)
+    if dtype == "fp8":
+        codes, scales, q, band_q, rel_s = fp8_pages(x64, band_x, page)
+        near = near_midpoint(q, band_q, "e4m3")
+        step, _ = _grid(np.abs(q) + band_q, "e4m3")
+        pidx = np.arange(E) // page
+        return near * (step + band_q) * scales.astype(np.float64)[pidx][:, None], rel_s[pidx]
+    raise ValueError(dtype)
+
+
 def key_score_slack(qi: np.ndarray, w: np.ndarray, x64: np.ndarray, band_x: np.ndarray, dtype: str,
                     page: int = 64) -> np.ndarray:
     """Per key j: the most its indexer score can move between the oracle's
@@ -214,24 +238,12 @@ def key_score_slack(qi: np.ndarray, w: np.ndarray, x64: np.ndarray, band_x: np.n
     qi = np.asarray(qi, np.float64)
     w = np.asarray(w, np.float64)
     coef = (w[:, None] * np.abs(qi)).sum(axis=0)          # [D_I]
-    if dtype == "f32":
-        return np.zeros(x64.shape[0])
-    if dtype == "bf16":
-        x32 = O.round_f32(x64).astype(np.float64)
-        b = band_x + U32 * np.abs(x64)
-        near = near_midpoint(x32, b, "bf16")
-        step, _ = _grid(np.abs(x32) + b, "bf16")
-        return (near * (step + b)) @ coef
-    if dtype == "fp8":
-        codes, scales, q, band_q, rel_s = fp8_pages(x64, band_x, page)
-        near = near_midpoint(q, band_q, "e4m3")
-        step, _ = _grid(np.abs(q) + band_q, "e4m3")
-        step = step + band_q
-        pidx = np.arange(x64.shape[0]) // page
-        vals = O.e4m3_decode(codes) * scales.astype(np.float64)[pidx][:, None]
-        score = np.maximum(vals @ qi.T, 0.0) @ w
-        return (near * step * scales.astype(np.float64)[pidx][:, None]) @ coef + rel_s[pidx] * np.abs(score)
-    raise ValueError(dtype)
+    M, rel = key_slack_parts(x64, band_x, dtype, page)
+    if not np.any(rel):
+        return M @ coef
+    stored = O.store(x64, dtype)[0]
+    score = np.maximum(stored @ qi.T, 0.0) @ w
+    return M @ coef + rel * np.abs(score)
 
 
 def topk_valid(gpu_row: np.ndarray, s: np.ndarray, k: int, slack: np.ndarray | None = None, eps: float = 1e-6):

@@ -24,7 +24,8 @@ from oracle import csa_oracle as O
 
 import parity_bounds as PB
 from gpu_helpers import (TOL, TORCH_ACT, check_topk_chain, fill_index_keys, fill_main_kv, fill_ring, make_cache,
-                         max_abs, oracle_entries, raw_rows, to64, topk_matches, unpack_fp4)
+                         max_abs, oracle_entries, raw_rows, to64, topk_matches, unpack_fp4,
+                         check_stored_pool)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,29 +116,7 @@ def _compress_case(kv, act, r, lens, seed=3, n_layers=1, chunks=None, swa=""):
     return cache, raw, P
 
 
-def _check_stored(cache, pool, scales, seq, n, x64, band, kv, what):
-    """GPU pool contents of one stream vs the oracle's rounding of x64: fp32
-    values within the fp32 error band of the exact values; bf16 and E4M3
-    codes equal, except where a value lies within its error band of a rounding
-    boundary (then the other rounding is allowed, and counted); E4M3 page
-    scales within the uncertainty of their page's amax."""
-    got_raw = cache.logical(pool, seq, n).cpu()
-    x64, band = x64[:n], band[:n]
-    if kv == "f32":
-        err = np.abs(got_raw.double().numpy() - x64)
-        assert np.all(err <= band), (what, float(np.max(err / band)))
-        return
-    if kv == "bf16":
-        allowed, bad = PB.check_stored(got_raw.view(torch.int16).numpy().view(np.uint16), x64, band, "bf16")
-    else:
-        codes, oscales, _, _, rel_s = PB.fp8_pages(x64, band)
-        gs = cache.logical_scales(scales, seq, n).cpu().double().numpy()
-        os64 = oscales.astype(np.float64)
-        assert np.all(np.abs(gs - os64) <= os64 * (rel_s + 2 * PB.U32)), (what, "page scales")
-        allowed, bad = PB.check_stored(got_raw.numpy(), x64, band, "fp8")
-    assert bad == 0, f"{what}: {bad} codes differ from the oracle's rounding outside every error band"
-    if allowed:
-        print(f"[codes] {what}: {allowed} of {x64.size} codes at a rounding boundary take the other neighbour")
+_check_stored = check_stored_pool
 
 
 @pytest.mark.parametrize("kv,act", DT_CASES)
