@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-hier", action="store_true", help="skip the hierarchical-indexer (pool / Reindex) leg")
     ap.add_argument("--no-swa-fp8", action="store_true", help="skip the fp8 window-ring decode leg")
     ap.add_argument("--no-fp4", action="store_true", help="skip the fp4 main-KV decode leg")
+    ap.add_argument("--no-c1", action="store_true", help="skip the batch-1 4,096-token fp32 decode leg")
+    ap.add_argument("--no-c2", action="store_true", help="skip the batch-32 65,536-token bf16 decode leg")
+    ap.add_argument("--no-c5", action="store_true", help="skip the 64-request ragged serving leg")
     return ap.parse_args()
 
 
@@ -369,6 +372,182 @@ def variant_leg(seed, dev, replicas, qi, w, qs, steps, kv="fp8", swa=""):
             "attend_kernel_us": round(att_us, 3), "step_bytes": sb}
 
 
+C1_CONTEXT, C1_HEADS, C1_K = 4096, 16, 64
+C2_BATCH, C2_CONTEXT, C2_K = 32, 1 << 16, 512
+C5_REQUESTS, C5_MIN, C5_MAX, C5_K = 64, 4096, 262144, 512
+
+
+def timed_decode(caches, q_seq, q_pos, qi, w, qs, k, steps, compress=None):
+    """A decode step - optionally compress(cache, stream) first, then one
+    csa_index_topk and one csa_attend per query tensor in qs (the layers that
+    share the Top-K) - timed as graph replays over the replicas (one graph
+    holds a step on each). Returns (us per step, score-kernel us, attention-kernel
+    us), the kernel times from launch-stamped events over eager steps without
+    the compress."""
+    import torch
+    from compressed_sparse_attention_csa_amd import binding as B
+    dev = qi.device
+    topk = [torch.empty((len(q_seq), k), dtype=torch.int32, device=dev) for _ in caches]
+    outs = [torch.empty_like(q) for q in qs]
+    scale = 1.0 / math.sqrt(128)
+
+    def index_attend(r, s_):
+        c = caches[r]
+        B.csa_index_topk(c.handle, q_seq, q_pos, qi, w, k, topk[r], s_)
+        for l, q in enumerate(qs):
+            B.csa_attend(c.handle, l, q_seq, q_pos, q, topk[r], k, scale, outs[l], s_)
+
+    def make(r):
+        def fn(s_):
+            if compress is not None:
+                compress(caches[r], s_)
+            index_attend(r, s_)
+        return fn
+    us = graph_us([make(r) for r in range(len(caches))], steps)
+    stream = torch.cuda.current_stream()
+    for c in caches:
+        B.csa_profile_begin(c.handle, B.PROFILE_INDEX | B.PROFILE_ATTEND)
+    for i in range(max(len(caches), steps // 4)):
+        index_attend(i % len(caches), stream)
+    torch.cuda.synchronize()
+    sms, sn, ams, an = 0.0, 0, 0.0, 0
+    for c in caches:
+        m, n = B.csa_profile_end(c.handle, B.PROFILE_INDEX)
+        sms, sn = sms + m, sn + n
+        m, n = B.csa_profile_end(c.handle, B.PROFILE_ATTEND)
+        ams, an = ams + m, an + n
+    flags = max(c.read_errors() for c in caches)
+    if flags:
+        raise RuntimeError(f"device error flags {flags}")
+    return us, sms * 1e3 / max(sn, 1), ams * 1e3 / max(an, 1)
+
+
+def decode_record(workload, us, scan_us, att_us, nbytes, n_tokens, extra=None):
+    rec = {"workload": workload, "us_per_step": round(us, 3), "tokens_per_s": round(n_tokens / (us * 1e-6), 1),
+           "step_bytes": nbytes, "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "score_kernel_us": round(scan_us, 3), "attend_kernel_us": round(att_us, 3)}
+    rec.update(extra or {})
+    return rec
+
+
+def c1_leg(seed, dev, replicas, steps):
+    """Single decode step, batch 1, 4,096-token fp32 context: r = 4 (1,024
+    entries), 16 query heads, 4 indexer heads, Top-64, W = 128. Launch-latency
+    bound: reports microseconds per step."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+    pages = C1_CONTEXT // RATIO // 64
+    spec = CacheSpec(ratio=RATIO, q_heads=C1_HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW, n_layers=1,
+                     max_seqs=1, max_pages_per_seq=pages, pool_pages=pages, kv_dtype="f32", act_dtype="f32",
+                     max_queries=1, max_k=C1_K)
+    bt = torch.tensor(Sy.permutation(seed, pages, salt=1), dtype=torch.int32).view(1, pages).to(dev)
+    base = CsaCache(spec, dev, block_table=bt)
+    rows = [Sy.normal_rows(seed, Sy.stream_id(kind, 0, 0), 0, C1_CONTEXT, 128, dev, torch.float32)
+            for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+    base.compress(0, [0], [C1_CONTEXT], *rows, Sy.proj_matrix(seed, 128, 64, device=dev))
+    caches = [base] + [base.clone() for _ in range(replicas - 1)]
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, IDX_HEADS, 64, dev, torch.float32).view(1, IDX_HEADS, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, 1, IDX_HEADS, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, C1_HEADS, 128, dev, torch.float32).view(1, C1_HEADS, 128)
+    us, sus, aus = timed_decode(caches, [0], [C1_CONTEXT - 1], qi, w, [q], C1_K, steps)
+    nbytes = A.decode_step_bytes(1, C1_CONTEXT // RATIO, 128, 64, C1_HEADS, IDX_HEADS, C1_K, WINDOW, 1, "f32", "f32")
+    for c in caches:
+        c.close()
+    return decode_record("decode, batch 1, 4,096-token fp32 context, r=4, Top-64, W=128, 16 heads", us, sus, aus,
+                         nbytes, 1, {"bound": "launch latency", "replicas": replicas})
+
+
+def c2_leg(seed, dev, replicas, steps):
+    """Batched decode: 32 sequences of 65,536 bf16 tokens (16,384 entries
+    each), 64 query heads, Top-512, W = 128, one layer. HBM bound: 70 % of the
+    8 TB/s peak is the target."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+    pages = C2_CONTEXT // RATIO // 64
+    spec = CacheSpec(ratio=RATIO, q_heads=HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW, n_layers=1,
+                     max_seqs=C2_BATCH, max_pages_per_seq=pages, pool_pages=C2_BATCH * pages, kv_dtype="bf16",
+                     act_dtype="bf16", max_queries=C2_BATCH, max_k=C2_K)
+    bt = torch.tensor(Sy.permutation(seed, C2_BATCH * pages, salt=9), dtype=torch.int32).view(C2_BATCH, pages).to(dev)
+    base = CsaCache(spec, dev, block_table=bt)
+    P = Sy.proj_matrix(seed, 128, 64, device=dev)
+    for b in range(C2_BATCH):
+        rows = [Sy.normal_rows(seed, Sy.stream_id(kind, 0, b), 0, C2_CONTEXT, 128, dev, torch.bfloat16)
+                for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+        base.compress(0, [b], [C2_CONTEXT], *rows, P)
+    caches = [base] + [base.clone() for _ in range(replicas - 1)]
+    B_ = C2_BATCH
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, B_ * IDX_HEADS, 64, dev, torch.bfloat16).view(B_, IDX_HEADS, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, B_, IDX_HEADS, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, B_ * HEADS, 128, dev, torch.bfloat16).view(B_, HEADS, 128)
+    us, sus, aus = timed_decode(caches, list(range(B_)), [C2_CONTEXT - 1] * B_, qi, w, [q], C2_K, steps)
+    nbytes = A.decode_step_bytes(B_, C2_CONTEXT // RATIO, 128, 64, HEADS, IDX_HEADS, C2_K, WINDOW, 1, "bf16", "bf16")
+    for c in caches:
+        c.close()
+    return decode_record("decode, batch 32, 65,536-token bf16 contexts, r=4, Top-512, W=128, 64 heads", us, sus, aus,
+                         nbytes, B_, {"target_us": round(nbytes / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e6, 2),
+                                      "replicas": replicas})
+
+
+def c5_leg(seed, dev, replicas, steps):
+    """Mixed serving step: 64 requests with contexts drawn log-uniform from 4K
+    to 256K tokens in one paged fp8 pool (64-entry pages in a shuffled order).
+    A step appends one token to every request (csa_compress: closes a block for
+    about a quarter of them, fp8 page re-encode), then indexes (Top-512) and
+    attends (W = 128, 64 heads). Bytes are exact for the drawn lengths."""
+    import torch
+    from compressed_sparse_attention_csa_amd import accounting as A
+    from compressed_sparse_attention_csa_amd import binding as B
+    from compressed_sparse_attention_csa_amd import synth as Sy
+    from compressed_sparse_attention_csa_amd.cache import CacheSpec, CsaCache
+    n = C5_REQUESTS
+    lens = Sy.log_uniform_lengths(seed, n, C5_MIN, C5_MAX)
+    pages = [((L + 1) // RATIO + 63) // 64 for L in lens]
+    pool = sum(pages)
+    perm = Sy.permutation(seed, pool, salt=13)
+    bt = torch.full((n, max(pages)), -1, dtype=torch.int32)
+    off = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = torch.tensor(perm[off:off + p], dtype=torch.int32)
+        off += p
+    spec = CacheSpec(ratio=RATIO, q_heads=HEADS, idx_heads=IDX_HEADS, window=WINDOW, ring_rows=WINDOW, n_layers=1,
+                     max_seqs=n, max_pages_per_seq=max(pages), pool_pages=pool, kv_dtype="fp8", act_dtype="bf16",
+                     max_queries=n, max_k=C5_K)
+    base = CsaCache(spec, dev, block_table=bt.to(dev))
+    P = Sy.proj_matrix(seed, 128, 64, device=dev)
+    for b, L in enumerate(lens):
+        rows = [Sy.normal_rows(seed, Sy.stream_id(kind, 0, b), 0, L, 128, dev, torch.bfloat16)
+                for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+        base.compress(0, [b], [L], *rows, P)
+    caches = [base] + [base.clone() for _ in range(replicas - 1)]
+    ids = list(range(n))
+    new = [torch.cat([Sy.normal_rows(seed, Sy.stream_id(kind, 0, b), lens[b], 1, 128, dev, torch.bfloat16)
+                      for b in ids]) for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z)]
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, n * IDX_HEADS, 64, dev, torch.bfloat16).view(n, IDX_HEADS, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, n, IDX_HEADS, dev)
+    q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q), 0, n * HEADS, 128, dev, torch.bfloat16).view(n, HEADS, 128)
+
+    # the graph replays the same append (token L of every request): writes the
+    # same bytes each time, so every replay is a full serving step
+    def compress(c, s_):
+        B.csa_compress(c.handle, 0, ids, [1] * n, new[0], new[1], new[2], P, s_)
+    us, sus, aus = timed_decode(caches, ids, lens, qi, w, [q], C5_K, steps, compress=compress)
+    ents = [(L + 1) // RATIO for L in lens]
+    cb = sum(A.compress_bytes(L, 1, RATIO, 128, 64, "fp8", "bf16", WINDOW) for L in lens)
+    nbytes = cb + A.decode_step_bytes(n, ents, 128, 64, HEADS, IDX_HEADS, C5_K, WINDOW, 1, "fp8", "bf16")
+    for c in caches:
+        c.close()
+    return decode_record("serving step: 64 requests, contexts log-uniform 4K-256K tokens (one paged fp8 pool), "
+                         "append 1 token each (compress) + index Top-512 + attend W=128, 64 heads", us, sus, aus,
+                         nbytes, n, {"compress_bytes": cb, "context_tokens": int(sum(lens)),
+                                     "closing_blocks": int(sum((L + 1) % RATIO == 0 for L in lens)),
+                                     "replicas": replicas})
+
+
 def build_cache(seed, replicas, dev, swa="", kv="fp8"):
     import torch
     from compressed_sparse_attention_csa_amd import binding as B
@@ -424,16 +603,21 @@ def scan_bytes_per_launch():
     return BATCH * per_q
 
 
+def attend_bytes_per_launch():
+    from compressed_sparse_attention_csa_amd import accounting as A
+    return BATCH * A.attend_bytes(TOPK, WINDOW, 128, HEADS, "fp8", "bf16")
+
+
 def step_bytes():
     from compressed_sparse_attention_csa_amd import accounting as A
     return A.decode_step_bytes(BATCH, CONTEXT // RATIO, 128, 64, HEADS, IDX_HEADS, TOPK, WINDOW, LAYERS, "fp8", "bf16")
 
 
-def traffic_from_profiles():
-    """(HBM bytes per scan launch, scope) from the committed counter record, if
-    it was taken on the current scan kernel source; else (None, None)."""
-    path = os.path.join(ROOT, "profiles", "index_scan_1m_decode_traffic.json")
-    src = os.path.join(ROOT, "compressed_sparse_attention_csa_amd", "csrc", "index.hip")
+def traffic_from_profiles(record="index_scan_1m_decode_traffic.json", source="index.hip"):
+    """(HBM bytes per launch, scope) from a committed counter record, if it was
+    taken on the current source of its kernel; else (None, None)."""
+    path = os.path.join(ROOT, "profiles", record)
+    src = os.path.join(ROOT, "compressed_sparse_attention_csa_amd", "csrc", source)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -446,44 +630,85 @@ def traffic_from_profiles():
         return None, None
 
 
-def cpu_baseline(seed, budget_s):
-    """The oracle, as it stands, on one query of the step at a time: indexer
-    scores over 262,144 fp8-decoded indexer keys, Top-1024, and 4 layer attends
-    (64 heads over 1,024 gathered entries + 128 window rows)."""
+def cpu_baseline(seed, budget_s, dev):
+    """The oracle, as it stands, on the headline step's own seeded inputs:
+    sequence 0's indexer keys and layer K/V come from the same seeded raw rows
+    the GPU cache is built from (generated on the device by the same
+    counter-based generator, then compressed and stored by the oracle in
+    float64), and its query inputs are the step's. One oracle decode_step
+    (indexer scores over 262,144 fp8 keys, Top-1024, 4 layer attends of 64
+    heads over 1,024 gathered entries + 128 window rows) is repeated for
+    `budget_s` seconds. Preparing the oracle's cache is not timed. Layers 1-3
+    hold only the entries the step selects (the only ones it reads)."""
     import numpy as np
     import threadpoolctl
+    import torch
+    from compressed_sparse_attention_csa_amd import synth as Sy
     from oracle import csa_oracle as O
 
-    rng = np.random.default_rng(seed)
-    E = CONTEXT // RATIO
-    kidx, _ = O.store(rng.standard_normal((E, 64)) * 0.5, "fp8")
+    def rows(kind, layer, r0, n):
+        x = Sy.normal_rows(seed, Sy.stream_id(kind, layer, 0), r0, n, 128, dev, torch.bfloat16)
+        return x.float().cpu().double().numpy()
+
+    E, t = CONTEXT // RATIO, CONTEXT - 1
+    P = Sy.proj_matrix(seed, 128, 64).double().numpy()
+    kb = np.empty((E, 128))
+    vb = np.empty((E, 128))
+    ki = np.empty((E, 64))
+    step = 1 << 18
+    t_prep = time.perf_counter()
+    for r0 in range(0, CONTEXT, step):
+        a, b, c = O.compress(rows(Sy.KIND_K, 0, r0, step), rows(Sy.KIND_V, 0, r0, step),
+                             rows(Sy.KIND_Z, 0, r0, step), RATIO, P)
+        kb[r0 // RATIO:(r0 + step) // RATIO], vb[r0 // RATIO:(r0 + step) // RATIO] = a, b
+        ki[r0 // RATIO:(r0 + step) // RATIO] = c
+    kis = O.store(ki, "fp8")[0]
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, BATCH * IDX_HEADS, 64, dev,
+                        torch.bfloat16).float().cpu().double().numpy()[:IDX_HEADS]
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, BATCH, IDX_HEADS, dev).cpu().double().numpy()[0]
+    T = O.topk(O.index_scores(qi, w, kis), TOPK)
     layers = []
-    for _ in range(LAYERS):
-        # compressed K/V rows: only gathered rows are touched, a 65,536-entry pool indexed modulo stands in
-        pool_k, _ = O.store(rng.standard_normal((65536, 128)) * 0.5, "fp8")
-        pool_v, _ = O.store(rng.standard_normal((65536, 128)) * 0.5, "fp8")
-        layers.append((pool_k, pool_v, rng.standard_normal((WINDOW, 128)), rng.standard_normal((WINDOW, 128))))
-    scale = 1 / math.sqrt(128)
+    for layer in range(LAYERS):
+        q = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_Q, layer), 0, BATCH * HEADS, 128, dev,
+                           torch.bfloat16).float().cpu().double().numpy()[:HEADS]
+        if layer == 0:
+            kbl, vbl = O.store(kb, "fp8")[0], O.store(vb, "fp8")[0]
+        else:
+            # only the pages holding selected entries (a page's scale is its
+            # amax, so each is compressed and stored whole)
+            kbl, vbl = np.zeros((E, 128)), np.zeros((E, 128))
+            sel = np.unique(T // 64)
+            for r0 in range(0, CONTEXT, step):
+                ps = sel[(sel >= r0 // (64 * RATIO)) & (sel < (r0 + step) // (64 * RATIO))]
+                if not len(ps):
+                    continue
+                idx = torch.from_numpy((ps[:, None] * 64 * RATIO - r0 + np.arange(64 * RATIO)).reshape(-1)).to(dev)
+                K, V, Z = (Sy.normal_rows(seed, Sy.stream_id(kind, layer, 0), r0, step, 128, dev, torch.bfloat16)
+                           .index_select(0, idx).float().cpu().double().numpy()
+                           for kind in (Sy.KIND_K, Sy.KIND_V, Sy.KIND_Z))
+                a, b, _ = O.compress(K, V, Z, RATIO)
+                ents = (ps[:, None] * 64 + np.arange(64)).reshape(-1)
+                kbl[ents], vbl[ents] = O.store(a, "fp8")[0], O.store(b, "fp8")[0]
+        rawk, rawv = np.zeros((CONTEXT, 128)), np.zeros((CONTEXT, 128))
+        rawk[t - WINDOW + 1:] = rows(Sy.KIND_K, layer, t - WINDOW + 1, WINDOW)
+        rawv[t - WINDOW + 1:] = rows(Sy.KIND_V, layer, t - WINDOW + 1, WINDOW)
+        layers.append(dict(q=q, W=WINDOW, scale=1 / math.sqrt(128), kbar=kbl, vbar=vbl, rawk=rawk, rawv=rawv))
+    prep_s = time.perf_counter() - t_prep
     n, t0 = 0, time.perf_counter()
     while True:
-        qi = rng.standard_normal((IDX_HEADS, 64))
-        w = rng.uniform(0, 1, IDX_HEADS)
-        s = O.index_scores(qi, w, kidx)
-        T = O.topk(s, TOPK)
-        for pk, pv, rk, rv in layers:
-            q = rng.standard_normal((HEADS, 128))
-            ent = T[T >= 0] % pk.shape[0]
-            keys = np.concatenate([pk[ent], rk], axis=0)
-            vals = np.concatenate([pv[ent], rv], axis=0)
-            O.attend(q, keys, vals, scale)
+        To, _ = O.decode_step(qi, w, kis, RATIO, TOPK, t, layers)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s and n >= 3:
             break
+    assert np.array_equal(To, T)
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
-    return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} single-query steps of the workload (index over {E:,} fp8 indexer keys, Top-{TOPK}, "
-                      f"{LAYERS} attends of {HEADS} heads over {TOPK}+{WINDOW} keys) in {el:.1f} s, float64 NumPy"}
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{n} repetitions of sequence 0's decode step on the workload's own seeded inputs "
+                      f"(oracle decode_step: scores over {E:,} fp8 indexer keys, Top-{TOPK}, {LAYERS} attends of "
+                      f"{HEADS} heads over {TOPK}+{WINDOW} keys) in {el:.1f} s, float64 NumPy; cores = BLAS "
+                      f"threads; preparing the oracle's cache took {prep_s:.1f} s (not timed)"}
 
 
 def main():
@@ -561,17 +786,21 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # kernel timing: eager steps with a HIP event pair around every scan launch
+    # kernel timing: eager steps, a HIP event pair stamped by every scan and
+    # every attention launch
     for c in caches:
-        B.csa_profile_begin(c.handle)
+        B.csa_profile_begin(c.handle, B.PROFILE_INDEX | B.PROFILE_ATTEND)
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    scan_ms, launches = 0.0, 0
+    scan_ms, launches, att_ms, att_launches = 0.0, 0, 0.0, 0
     for c in caches:
-        ms, n = B.csa_profile_end(c.handle)
+        ms, n = B.csa_profile_end(c.handle, B.PROFILE_INDEX)
         scan_ms += ms
         launches += n
+        ms, n = B.csa_profile_end(c.handle, B.PROFILE_ATTEND)
+        att_ms += ms
+        att_launches += n
     flags = max(c.read_errors() for c in caches)
     if flags:
         raise RuntimeError(f"device error flags {flags}")
@@ -588,6 +817,10 @@ def main():
     sb = scan_bytes_per_launch()
     achieved = sb / (scan_avg_ms * 1e-3) / 1e9
     traffic, traffic_scope = traffic_from_profiles()
+    att_avg_ms = att_ms / max(1, att_launches)
+    ab = attend_bytes_per_launch()
+    att_achieved = ab / (att_avg_ms * 1e-3) / 1e9
+    att_traffic, att_scope = traffic_from_profiles("attend_decode_1m_traffic.json", "attend.hip")
     # the same number of bytes read by a plain 16-byte non-temporal streaming
     # kernel over 8 rotating buffers: what one launch of this size gets here
     ref_bufs = [torch.empty(sb, dtype=torch.uint8, device=dev) for _ in range(8)]
@@ -595,6 +828,20 @@ def main():
     ref_us = B.csa_debug_stream_read(ref_bufs, sb, 80)
     del ref_bufs
     ref_gbps = sb / (ref_us * 1e-6) / 1e9
+    scan_rec = {"bound": "hbm", "kernel": "idx_scan (indexer scores over the fp8 indexer-key pages)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_scope": traffic_scope,
+                "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches,
+                "launches_per_step": 1}
+    att_rec = {"bound": "hbm", "kernel": "attend_decode (gathered Top-K + window attention, one layer, 4 queries)",
+               "achieved": round(att_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+               "frac": round(att_achieved / HBM_PEAK_GBPS, 4), "traffic": att_traffic, "traffic_scope": att_scope,
+               "bytes_per_launch": ab, "avg_launch_us": round(att_avg_ms * 1e3, 3), "launches": att_launches,
+               "launches_per_step": LAYERS}
+    # the roofline line is the kernel that takes most of a step's time
+    scan_step_us, att_step_us = scan_avg_ms * 1e3, att_avg_ms * 1e3 * LAYERS
+    dominant, other = (att_rec, scan_rec) if att_step_us >= scan_step_us else (scan_rec, att_rec)
+    step_gbps = step_bytes() / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -613,13 +860,11 @@ def main():
                    "batch": BATCH, "context": CONTEXT, "ratio": RATIO, "k": TOPK, "window": WINDOW,
                    "q_heads": HEADS, "idx_heads": IDX_HEADS, "group_layers": LAYERS, "kv_dtype": "fp8_e4m3",
                    "replicas": len(caches), "parallelism": "none (1 GPU)"},
-        "step_hbm_gbps": round(step_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
-        "step_bytes": step_bytes(),
-        "roofline": {"bound": "hbm", "kernel": "idx_scan (indexer scores over the fp8 indexer-key pages)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "traffic_scope": traffic_scope,
-                     "bytes_per_launch": sb, "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches": launches},
+        "roofline": dominant,
+        "step_roofline": {"bound": "hbm", "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(step_gbps / HBM_PEAK_GBPS, 4), "bytes_per_step": step_bytes(),
+                          "scope": "algorithmic bytes of the whole step over its graph-replay time"},
+        "scan_roofline" if other is scan_rec else "attend_roofline": other,
         "read_ceiling": {"kernel": "streaming read, 16-byte non-temporal loads, 8 rotating buffers",
                          "bytes": sb, "avg_launch_us": round(ref_us, 3), "achieved": round(ref_gbps, 1),
                          "unit": "GB/s", "scan_frac": round(achieved / ref_gbps, 4)},
@@ -634,12 +879,20 @@ def main():
     if not args.no_fp4:
         line["fp4_kv"] = variant_leg(args.seed, dev, args.replicas, qi, w, qs, args.steps, kv="fp4")
         torch.cuda.empty_cache()
+    if not args.no_c2:
+        line["c2_batch32_64k"] = c2_leg(args.seed, dev, args.replicas, args.steps)
+        torch.cuda.empty_cache()
+    if not args.no_c5:
+        line["c5_serving_64"] = c5_leg(args.seed, dev, args.replicas, args.steps)
+        torch.cuda.empty_cache()
+    if not args.no_c1:
+        line["c1_batch1_4k_fp32"] = c1_leg(args.seed, dev, args.replicas, args.steps)
     if not args.no_prefill:
         line["prefill"] = prefill_leg(args.seed, dev)
     if not args.no_hca:
         line["hca"] = hca_leg(args.seed, dev)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds, dev)
     print(json.dumps(line), flush=True)
 
 

@@ -52,6 +52,59 @@ def attend_bytes(k_sel: int, window: int, d: int, h_q: int, kv_dtype: str, act_d
     return b
 
 
+def compress_bytes(old_len: int, n_new: int, r: int, d: int, d_i: int, kv_dtype: str, act_dtype: str,
+                   ring_rows: int, swa_dtype: str | None = None, with_index: bool = True, page: int = 64) -> int:
+    """Bytes one sequence's append of n_new raw rows after old_len moves in one
+    layer (csa_compress).
+
+    Read: the new rows' gate logits, keys and values; the open block's earlier
+    rows from block staging when that block closes now; for fp8 pages, the
+    fp32 staging of each touched page's earlier entries (a page's scale is its
+    amax, so its earlier entries are re-encoded) and, with the indexer, the
+    projection matrix once. Written: the newest min(n_new, R) keys and values
+    into the window ring (plus one scale per row for an fp8 ring); the rows
+    of the block still open afterwards into block staging; the new entries'
+    K, V (and indexer key) codes - for fp8 pages every filled slot of each
+    touched page, its scales, and the fp32 staging of the new entries while
+    the page stays open; for fp4 K/V, the new entries' codes and group scales
+    with fp8 indexer keys handled as an fp8 page.
+    """
+    ab = DTYPE_BYTES[act_dtype]
+    sd = swa_dtype or act_dtype
+    di = d_i if with_index else 0
+    new_len = old_len + n_new
+    nb_old, nb_new = old_len // r, new_len // r
+    b = n_new * 3 * d * ab
+    if nb_new > nb_old:
+        b += (old_len - nb_old * r) * 3 * d * ab
+    b += (new_len - max(old_len, nb_new * r)) * 3 * d * ab
+    ring = min(n_new, ring_rows)
+    b += ring * 2 * d * (1 if sd == "fp8" else DTYPE_BYTES[sd]) + (ring * 2 * 4 if sd == "fp8" else 0)
+    if nb_new == nb_old:
+        return b
+    if di:
+        b += d * di * 4
+    for p in range(nb_old // page, (nb_new - 1) // page + 1):
+        p0 = p * page
+        e0, e1 = max(p0, nb_old), min(p0 + page, nb_new)
+        filled, new = e1 - p0, e1 - e0
+        still_open = filled < page
+        if kv_dtype == "fp8":
+            b += (e0 - p0) * (2 * d + di) * 4
+            b += filled * (2 * d + di) + (3 if di else 2) * 4
+            if still_open:
+                b += new * (2 * d + di) * 4
+        elif kv_dtype == "fp4":
+            b += new * 2 * (d // 2 + d // 16)
+            if di:
+                b += (e0 - p0) * di * 4 + filled * di + 4
+                if still_open:
+                    b += new * di * 4
+        else:
+            b += new * (2 * d + di) * DTYPE_BYTES[kv_dtype]
+    return b
+
+
 def reindex_bytes(pool_entries: int, n_blocks: int, d_i: int, kv_dtype: str) -> int:
     """Bytes one query's Reindex scores read: the pool's indexer keys, its
     block ids and (fp8) one page scale per block (an aligned 8-entry block

@@ -129,7 +129,29 @@ class CsaCache:
         b.workspace = self.workspace.data_ptr()
         b.workspace_bytes = ws
         self._bufs = b
+        self._swa = {}
         self.handle = B.csa_cache_create(self.cfg, b)
+
+    def clone(self) -> "CsaCache":
+        """Another cache with this one's contents: every device buffer copied,
+        the same block table, sequence lengths and replay starts (replicas of
+        one workload)."""
+        c = CsaCache(self.spec, self.device, block_table=self.block_table)
+        for name in ("kbar", "vbar", "kbar_gscale", "vbar_gscale", "kbar_scale", "vbar_scale", "kbar_stage",
+                     "vbar_stage", "ring_k", "ring_v", "ring_k_scale", "ring_v_scale", "block_stage"):
+            for src, dst in zip(getattr(self, name), getattr(c, name)):
+                dst.copy_(src)
+        for name in ("kidx", "kidx_scale", "kidx_stage"):
+            if getattr(self, name) is not None:
+                getattr(c, name).copy_(getattr(self, name))
+        for layer in range(self.cfg.n_layers):
+            for seq in range(self.cfg.max_seqs):
+                n = B.csa_seq_len(self.handle, layer, seq)
+                if n:
+                    B.csa_seq_set_len(c.handle, layer, seq, n)
+        for seq, start in self._swa.items():
+            c.set_swa_start(seq, start)
+        return c
 
     # ----------------------------------------------------------------- calls
     def compress(self, layer, seq_ids, n_new, raw_k, raw_v, gate, proj_idx=None, stream=None):
@@ -175,6 +197,7 @@ class CsaCache:
 
     def set_swa_start(self, seq, start):
         B.csa_seq_set_swa_start(self.handle, seq, start)
+        self._swa[seq] = start
 
     def ring_write(self, layer, seq_ids, pos0, n_rows, raw_k, raw_v, stream=None):
         B.csa_ring_write(self.handle, layer, seq_ids, pos0, n_rows, raw_k, raw_v, stream)

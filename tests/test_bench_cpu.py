@@ -57,3 +57,27 @@ def test_traffic_record_gated_by_kernel_source(tmp_path, monkeypatch):
     assert bench.traffic_from_profiles() == (None, None)
     path.unlink()                              # no record
     assert bench.traffic_from_profiles() == (None, None)
+
+
+def test_compress_bytes_of_one_token_appends():
+    # fp8 pages, bf16 rows and window ring (R = 128), r = 4, with the indexer.
+    # Token 11 closes block 2 (entry 2, slot 2 of page 0): the new row's gate/K/V,
+    # rows 8-10 back from block staging, the row into the ring, the projection
+    # (128 x 64 fp32), page 0's two earlier entries from fp32 staging, all three
+    # entries' K/V/indexer codes and the three page scales, the new entry's staging.
+    row = 3 * 128 * 2
+    closing = row + 3 * row + 2 * 128 * 2 + 128 * 64 * 4 + 2 * 320 * 4 + 3 * 320 + 3 * 4 + 320 * 4
+    assert A.compress_bytes(11, 1, 4, 128, 64, "fp8", "bf16", 128) == closing == 41164
+    # token 12 opens block 3: the row in, into block staging and into the ring
+    assert A.compress_bytes(12, 1, 4, 128, 64, "fp8", "bf16", 128) == row + row + 2 * 128 * 2
+    # the entry that fills page 0 (slot 63) leaves no staging behind
+    full = row + 3 * row + 512 + 128 * 64 * 4 + 63 * 320 * 4 + 64 * 320 + 3 * 4
+    assert A.compress_bytes(255, 1, 4, 128, 64, "fp8", "bf16", 128) == full
+    # bf16 pages write only the new entry
+    assert A.compress_bytes(11, 1, 4, 128, 64, "bf16", "bf16", 128) == row + 3 * row + 512 + 128 * 64 * 4 + 320 * 2
+
+
+def test_attend_bytes_per_launch():
+    # 4 queries, one layer: gathered fp8 K/V rows with page scales, bf16 window rows, q, out, Top-K row
+    assert bench.attend_bytes_per_launch() == 4 * (1024 * 2 * (128 + 4) + 128 * 2 * 128 * 2 + 2 * 64 * 128 * 2
+                                                   + 1024 * 4) == 1490944
