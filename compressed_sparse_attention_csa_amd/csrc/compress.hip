@@ -48,6 +48,17 @@ __device__ __forceinline__ void store1(void *base, int64_t elem, float a) {
   }
 }
 
+// The item a workgroup belongs to: the last one whose first workgroup is <= wg
+// (a binary search over the launcher's prefix, log2(items) dependent loads).
+__device__ __forceinline__ int item_of(const int32_t *wg0, int n_items, int wg) {
+  int lo = 0, hi = n_items;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (wg0[mid] <= wg) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 constexpr int kThreads = 256;
 constexpr int kPageParts = 8;   // workgroups per fp32 / bf16 page
 
@@ -62,14 +73,11 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   __shared__ float red[16];
 
   // ---- which (sequence, page) this workgroup owns
-  int wg = blockIdx.x / PARTS, item = 0, acc = 0;
+  const int wg = blockIdx.x / PARTS;
   const int slot0 = (blockIdx.x % PARTS) * SPW;   // this workgroup's first slot of the page
-  for (; item < a.n_items - 1; ++item) {
-    if (wg < acc + a.it[item].n_pages) break;
-    acc += a.it[item].n_pages;
-  }
+  const int item = item_of(a.wg0, a.n_items, wg);
   const CompressItem it = a.it[item];
-  const int page = it.page0 + (wg - acc);
+  const int page = it.page0 + (wg - a.wg0[item]);
   const int seq = it.seq;
   const int r = a.r;
   const int new_len = it.old_len + it.n_new;
@@ -93,38 +101,48 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
     for (int u = 0; u < kD * kDI / 4 / kThreads; ++u) reinterpret_cast<float4 *>(&p_s[0][0])[u * kThreads + t] = tmp[u];
   }
 
+  // fp8 pages: the fp32 values of the page's earlier entries, from staging.
+  // Every slot of a sequence's staging page is valid memory, so the loads are
+  // issued for every slot up front (all in flight together) and selected below.
+  float2 stk[SPT], stv[SPT];
+  if constexpr (KV == DT_FP8) {
+#pragma unroll
+    for (int m = 0; m < SPT; ++m) {
+      const int64_t so = (static_cast<int64_t>(seq) * kPage + slot0 + eb + 4 * m) * kD + d0;
+      stk[m] = *reinterpret_cast<const float2 *>(a.kbar_stage + so);
+      stv[m] = *reinterpret_cast<const float2 *>(a.vbar_stage + so);
+    }
+  }
+
+  // A row of entry e's block: from the packed input when this call appends it,
+  // else from open-block staging (appended by an earlier call).
+  auto row_src = [&](int row, int plane, const void *fresh) -> float2 {
+    const bool is_new = row >= it.old_len;
+    const void *base = is_new ? fresh : a.block_stage;
+    const int64_t off = is_new ? static_cast<int64_t>(it.row_off + row - it.old_len) * kD + d0
+                               : ((static_cast<int64_t>(seq) * 3 + plane) * r + row % r) * kD + d0;
+    return load2<ACT>(base, off);
+  };
+
   float kk[SPT][2], vv[SPT][2];
 #pragma unroll
   for (int m = 0; m < SPT; ++m) {
-    const int slot = slot0 + eb + 4 * m, e = pstart + slot;
+    const int slot = slot0 + eb + 4 * m, e = pstart + slot;   // the same for every lane of a wave
     float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
     if (e >= e0 && e < e1) {
       // gated pooling over rows [e*r, e*r + r): softmax of the gate per channel
       float zm0 = -INFINITY, zm1 = -INFINITY;
+#pragma unroll 4
       for (int u = 0; u < r; ++u) {
-        const int row = e * r + u;
-        float2 z = row >= it.old_len
-                       ? load2<ACT>(a.gate, static_cast<int64_t>(it.row_off + row - it.old_len) * kD + d0)
-                       : load2<ACT>(a.block_stage, ((static_cast<int64_t>(seq) * 3 + 0) * r + row % r) * kD + d0);
+        const float2 z = row_src(e * r + u, 0, a.gate);
         zm0 = fmaxf(zm0, z.x);
         zm1 = fmaxf(zm1, z.y);
       }
       float ws0 = 0.f, ws1 = 0.f;
+#pragma unroll 4
       for (int u = 0; u < r; ++u) {
         const int row = e * r + u;
-        float2 z, kx, vx;
-        if (row >= it.old_len) {
-          const int64_t off = static_cast<int64_t>(it.row_off + row - it.old_len) * kD + d0;
-          z = load2<ACT>(a.gate, off);
-          kx = load2<ACT>(a.raw_k, off);
-          vx = load2<ACT>(a.raw_v, off);
-        } else {
-          // a row of the block appended by an earlier call: from open-block staging
-          const int64_t so = (static_cast<int64_t>(seq) * 3 * r + row % r) * kD + d0;
-          z = load2<ACT>(a.block_stage, so);
-          kx = load2<ACT>(a.block_stage, so + static_cast<int64_t>(r) * kD);
-          vx = load2<ACT>(a.block_stage, so + 2 * static_cast<int64_t>(r) * kD);
-        }
+        const float2 z = row_src(row, 0, a.gate), kx = row_src(row, 1, a.raw_k), vx = row_src(row, 2, a.raw_v);
         const float w0 = expf(z.x - zm0), w1 = expf(z.y - zm1);
         ws0 += w0; ws1 += w1;
         k0 += w0 * kx.x; k1 += w1 * kx.y;
@@ -132,11 +150,8 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
       }
       k0 /= ws0; k1 /= ws1; v0 /= ws0; v1 /= ws1;
     } else if (KV == DT_FP8 && slot < filled && e < e0) {
-      // an entry appended by an earlier call: its fp32 value from staging
-      const int64_t so = (static_cast<int64_t>(seq) * kPage + slot) * kD + d0;
-      const float2 kx = *reinterpret_cast<const float2 *>(a.kbar_stage + so);
-      const float2 vx = *reinterpret_cast<const float2 *>(a.vbar_stage + so);
-      k0 = kx.x; k1 = kx.y; v0 = vx.x; v1 = vx.y;
+      // an entry appended by an earlier call
+      k0 = stk[m].x; k1 = stk[m].y; v0 = stv[m].x; v1 = stv[m].y;
     }
     kk[m][0] = k0; kk[m][1] = k1;
     vv[m][0] = v0; vv[m][1] = v1;
@@ -151,18 +166,40 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   float ki[SPT];
 #pragma unroll
   for (int m = 0; m < SPT; ++m) ki[m] = 0.f;
+  // fp8 indexer keys of earlier entries from staging, issued before the projection
+  float sti[SPT];
+  if constexpr (KV == DT_FP8 || KV == DT_FP4) {
+    if (a.write_idx) {
+#pragma unroll
+      for (int m = 0; m < SPT; ++m)
+        sti[m] = a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot0 + eb + 4 * m) * kDI + c];
+    }
+  }
   if (a.write_idx) {
     __syncthreads();
-    for (int d = 0; d < kD; ++d) {
-      const float p = p_s[d][c];
+    // new entries only (a slot is new for every lane of its wave or for none):
+    // an earlier entry's key comes from staging (fp8 keys) or is not rewritten
 #pragma unroll
-      for (int m = 0; m < SPT; ++m) ki[m] += kb_s[eb + 4 * m][d] * p;
+    for (int m = 0; m < SPT; ++m) {
+      const int e = pstart + slot0 + eb + 4 * m;
+      if (e >= e0 && e < e1) {
+        const float *kr = &kb_s[eb + 4 * m][0];
+        float acc = 0.f;
+        for (int d = 0; d < kD; d += 4) {
+          const float4 k4 = *reinterpret_cast<const float4 *>(kr + d);
+          acc += k4.x * p_s[d][c];
+          acc += k4.y * p_s[d + 1][c];
+          acc += k4.z * p_s[d + 2][c];
+          acc += k4.w * p_s[d + 3][c];
+        }
+        ki[m] = acc;
+      }
     }
     if constexpr (KV == DT_FP8 || KV == DT_FP4) {   // fp8 indexer keys
 #pragma unroll
       for (int m = 0; m < SPT; ++m) {
         const int slot = slot0 + eb + 4 * m, e = pstart + slot;
-        if (slot < filled && e < e0) ki[m] = a.kidx_stage[(static_cast<int64_t>(seq) * kPage + slot) * kDI + c];
+        if (slot < filled && e < e0) ki[m] = sti[m];
       }
     }
   }
@@ -261,8 +298,8 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
       for (int m = 0; m < SPT; ++m) {
         const int slot = slot0 + eb + 4 * m;
         if (slot < filled) {
-          const uint32_t ck = f32_to_e4m3(kk[m][0] / sk) | (f32_to_e4m3(kk[m][1] / sk) << 8);
-          const uint32_t cv = f32_to_e4m3(vv[m][0] / sv) | (f32_to_e4m3(vv[m][1] / sv) << 8);
+          const uint32_t ck = f32x2_to_e4m3x2(kk[m][0] / sk, kk[m][1] / sk);
+          const uint32_t cv = f32x2_to_e4m3x2(vv[m][0] / sv, vv[m][1] / sv);
           *reinterpret_cast<uint16_t *>(kp + slot * kD + d0) = static_cast<uint16_t>(ck);
           *reinterpret_cast<uint16_t *>(vp + slot * kD + d0) = static_cast<uint16_t>(cv);
           if (a.write_idx) ip[slot * kDI + c] = static_cast<uint8_t>(f32_to_e4m3(ki[m] / si));
@@ -295,13 +332,10 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
 // reads the previous staging contents for a block straddling two calls.
 template <int ACT, bool RING8>
 __global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
-  int wg = blockIdx.x, item = 0, acc = 0;
-  for (; item < a.n_items - 1; ++item) {
-    if (wg < acc + a.chunks[item]) break;
-    acc += a.chunks[item];
-  }
+  const int wg = blockIdx.x;
+  const int item = item_of(a.wg0, a.n_items, wg);
   const CompressItem it = a.it[item];
-  const int chunk = wg - acc;
+  const int chunk = wg - a.wg0[item];
   const int new_len = it.old_len + it.n_new;
   const int lo = max(it.old_len, new_len - a.R);
   const int glo = a.write_stage ? max(it.old_len, (new_len / a.r) * a.r) : new_len;
@@ -375,8 +409,11 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
 
 }  // namespace
 
-void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s) {
+void launch_compress_pages(const CompressArgs &args, int n_wg, int kv, int act, hipStream_t s) {
   if (n_wg <= 0) return;
+  CompressArgs a = args;
+  a.wg0[0] = 0;
+  for (int i = 0; i < a.n_items; ++i) a.wg0[i + 1] = a.wg0[i] + a.it[i].n_pages;
   if (kv == DT_F32 && act == DT_F32)
     hipLaunchKernelGGL((compress_pages_kernel<DT_F32, DT_F32>), dim3(n_wg * kPageParts), dim3(kThreads), 0, s, a);
   else if (kv == DT_BF16 && act == DT_BF16)
@@ -387,8 +424,11 @@ void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hip
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP4>), dim3(n_wg), dim3(kThreads), 0, s, a);
 }
 
-void launch_compress_ring(const RingArgs &a, int n_wg, int act, bool ring_fp8, hipStream_t s) {
+void launch_compress_ring(const RingArgs &args, int n_wg, int act, bool ring_fp8, hipStream_t s) {
   if (n_wg <= 0) return;
+  RingArgs a = args;
+  a.wg0[0] = 0;
+  for (int i = 0; i < a.n_items; ++i) a.wg0[i + 1] = a.wg0[i] + a.chunks[i];
   if (act == DT_F32)
     hipLaunchKernelGGL((compress_ring_kernel<DT_F32, false>), dim3(n_wg), dim3(256), 0, s, a);
   else if (ring_fp8)

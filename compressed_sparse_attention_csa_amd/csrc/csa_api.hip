@@ -933,7 +933,9 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       const int ms = att_max_splits(nq);
       const int ks = dense && c.q_heads <= 64 ? 4 : 1;
       const int streams = (nb + ks - 1) / ks;
-      int rounds = dense ? (streams + kAttDenseSplits - 1) / kAttDenseSplits : 1;
+      // a large decode batch already fills the chip: two blocks per workgroup
+      // halve the partials the merge reads
+      int rounds = dense ? (streams + kAttDenseSplits - 1) / kAttDenseSplits : (nq * nb > kAttWideBatch ? 2 : 1);
       rounds = std::max(rounds, (streams + ms - 1) / ms);
       rounds = std::min(rounds, kAttSplitMaxKeys / (kKeyBlock * ks));
       const int splits = (streams + rounds - 1) / rounds;

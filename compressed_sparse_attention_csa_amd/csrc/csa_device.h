@@ -67,20 +67,16 @@ __device__ __forceinline__ bf16x2_t fp8x2_to_bf16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, HI);
 }
 
-// fp32 -> E4M3 code, round-to-nearest-even, saturating to +-448. The sign bit
-// is the sign of the input (a negative value that rounds to zero gives 0x80).
+// fp32 -> E4M3 codes, round-to-nearest-even, saturating to +-448 (NaN
+// saturates too): the input is clamped, then gfx950's v_cvt_pk_fp8_f32
+// rounds it. The sign bit is the sign of the input (a negative value that
+// rounds to zero gives 0x80). Two at once: lo in bits 0-7, hi in bits 8-15.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float lo, float hi) {
+  const float a = fminf(fmaxf(lo, -448.0f), 448.0f), b = fminf(fmaxf(hi, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (!(a < 448.0f)) return sign | 0x7eu;            // also catches NaN / inf
-  if (a < 0.015625f) {                                 // below 2^-6: spacing 2^-9
-    const uint32_t m = static_cast<uint32_t>(rintf(a * 512.0f));  // 0..8 (8 == 2^-6 == code 0x08)
-    return sign | m;
-  }
-  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;   // -6..8
-  uint32_t mant = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));     // 8..16
-  if (mant == 16u) { mant = 8u; ++e; }
-  return sign | (static_cast<uint32_t>(e + 7) << 3) | (mant - 8u);
+  return f32x2_to_e4m3x2(x, x) & 0xffu;
 }
 
 // One E4M3 code (low byte) -> fp32.

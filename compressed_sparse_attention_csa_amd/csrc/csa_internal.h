@@ -31,6 +31,7 @@ struct CompressArgs {
   uint32_t *err;
   int32_t r, R, bt_stride, pool_pages, write_idx, n_items;
   CompressItem it[kCompressMaxItems];
+  int32_t wg0[kCompressMaxItems + 1];             // first page workgroup of each item (set by the launcher)
 };
 
 struct RingArgs {
@@ -42,6 +43,7 @@ struct RingArgs {
   int32_t write_stage;                            // 0: window rows only (a replay)
   int32_t chunks[kCompressMaxItems];              // WGs per item
   CompressItem it[kCompressMaxItems];
+  int32_t wg0[kCompressMaxItems + 1];             // first workgroup of each item (set by the launcher)
 };
 
 void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s);
@@ -207,6 +209,7 @@ struct AttendArgs {
 
 constexpr int kAttSplitMaxKeys = 2048;   // keys one decode-kernel workgroup resolves up front (32 blocks)
 constexpr int kAttDenseSplits = 40;      // splits per dense query the merge kernel takes in registers
+constexpr int kAttWideBatch = 512;       // decode (query, block) pairs above which a workgroup takes two blocks
 
 // Decode and dense attention with bf16 compute (kv: bf16, fp8 or fp4): one
 // workgroup per (query, split), key_streams (1 or 4) 64-key blocks side by
