@@ -130,11 +130,18 @@ template <int SD> constexpr int elem_bytes_of() { return SD == DT_F32 ? 4 : (SD 
 template <int SD> constexpr int row_bytes_of() { return SD == DT_FP4 ? kD / 2 : kD * elem_bytes_of<SD>(); }
 
 // RS: storage type of the window ring (ACT, or E4M3 with one scale per row);
-// HG: head groups (waves); NTW: 16-head tiles per wave.
-template <int ACT, int KV, int RS, int HG, int NTW>
-__global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
+// HG: head groups; NTW: 16-head tiles per wave; KH: key halves. The HG x KH
+// waves split each staged 64-key block: wave (hg, kh) takes head tiles
+// hg + HG j and, with KH = 2, only the block's keys [32 kh, 32 kh + 32), so a
+// key's K and V are read from LDS by HG waves instead of all of them. With
+// KH = 2 the two halves keep their own softmax states (m, l, O) and combine
+// them through LDS at the end.
+template <int ACT, int KV, int RS, int HG, int NTW, int KH>
+__global__ __launch_bounds__(HG * KH * 64) void attend_kernel(const AttendArgs a) {
   using CT = typename ComputeT<KV>::type;
-  constexpr int NT = HG * 64;
+  static_assert(KH == 1 || KH == 2, "one or two key halves");
+  constexpr int NT = HG * KH * 64;
+  constexpr int NKT = 4 / KH;                  // 16-key tiles of a block per wave
   constexpr int H = HG * NTW * 16;
   constexpr int AE = elem_bytes_of<ACT>();
   constexpr bool VSCALE = KV == DT_FP8 || RS == DT_FP8;   // value rows carry a page or row scale
@@ -152,7 +159,11 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
   static_assert((CPR_P & (CPR_P - 1)) == 0 && (CPR_R & (CPR_R - 1)) == 0, "chunks per row are powers of two");
   constexpr int U = 2 * kKeyBlock * CPR_MAX / NT;              // chunk slots per thread per block
   constexpr bool PREFETCH = U <= 8;                            // whole block held in registers
-  constexpr int KV_LDS = (kKeyBlock * KS + (VROW ? kKeyBlock : kD) * VS) * static_cast<int>(sizeof(CT));
+  constexpr int KV_STAGE = (kKeyBlock * KS + (VROW ? kKeyBlock : kD) * VS) * static_cast<int>(sizeof(CT));
+  // the second key half's (m, l, O) per head group, after the last block
+  constexpr int OSTR = kD + 4;
+  constexpr int HALF_LDS = KH == 2 ? HG * NTW * 16 * (OSTR + 2) * 4 : 0;
+  constexpr int KV_LDS = KV_STAGE > HALF_LDS ? KV_STAGE : HALF_LDS;
 
   __shared__ __align__(16) char kv_lds[KV_LDS];
   // byte offset of each key's row in the pool (Top-K blocks) or ring (window
@@ -362,7 +373,8 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     }
   };
 
-  const int lane = tid & 63, hg = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hg = wave % HG, kh = wave / HG, g = lane >> 4, col = lane & 15;
 
   // Q fragments (B operand of S^T) for this wave's head tiles
   Frag<CT> qf[NTW][4];
@@ -389,10 +401,12 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
     if (r + 1 < n_rounds) load_round(r + 1);   // in flight during this round's math
     const CT *Kb = Ks;
     const CT *Vb = Vt;
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      // S^T tiles; the next tile's K fragments are read while this one multiplies
-      f32x4_t S[4];
+    // S^T tiles of this wave's keys (tile i is block key tile kt0 + i) for all
+    // of its head tiles: each K fragment is read from LDS once, and the next
+    // tile's are read while this one multiplies
+    const int kt0 = kh * NKT;
+    f32x4_t S[NTW][NKT];
+    {
       Frag<CT> kf[2][4];
       auto load_kf = [&](Frag<CT> (&dst)[4], int kt) {
 #pragma unroll
@@ -402,48 +416,61 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
           else dst[c] = LoadFrag<DT_BF16, __bf16>::load(src);
         }
       };
-      load_kf(kf[0], 0);
+      load_kf(kf[0], kt0);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        if (kt + 1 < 4) load_kf(kf[(kt + 1) & 1], kt + 1);
-        S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NKT; ++i) {
+        if (i + 1 < NKT) load_kf(kf[(i + 1) & 1], kt0 + i + 1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) S[kt] = mma(kf[kt & 1][c], qf[j][c], S[kt]);
-      }
-      // per-key factors of the lane's keys 16*kt + 4*g + v, four at a time
-      float4 km[4], kbi[4];
-      if constexpr (VSCALE) {
+        for (int j = 0; j < NTW; ++j) {
+          S[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          km[kt] = *reinterpret_cast<const float4 *>(&kmul[16 * kt + 4 * g]);
-          kbi[kt] = *reinterpret_cast<const float4 *>(&kbias[16 * kt + 4 * g]);
-        }
-      } else {
-        const float c = a.scale * kLog2e;   // logits in log2 units
-        const uint64_t mk = kmask;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          km[kt] = make_float4(c, c, c, c);
-          kbi[kt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (mk != ~0ull) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            const uint32_t nib = static_cast<uint32_t>(mk >> (16 * kt + 4 * g)) & 0xfu;
-            kbi[kt] = make_float4((nib & 1u) ? 0.f : -INFINITY, (nib & 2u) ? 0.f : -INFINITY,
-                                  (nib & 4u) ? 0.f : -INFINITY, (nib & 8u) ? 0.f : -INFINITY);
-          }
+          for (int c = 0; c < 4; ++c) S[j][i] = mma(kf[i & 1][c], qf[j][c], S[j][i]);
         }
       }
-      // logits and online softmax (lane's head = col; keys 16*kt + 4*g + v)
-      float x[4][4];
+    }
+    // per-key factors of the lane's keys 16*(kt0 + i) + 4*g + v, four at a time
+    float4 km[NKT], kbi[NKT];
+    if constexpr (VSCALE) {
+#pragma unroll
+      for (int i = 0; i < NKT; ++i) {
+        km[i] = *reinterpret_cast<const float4 *>(&kmul[16 * (kt0 + i) + 4 * g]);
+        kbi[i] = *reinterpret_cast<const float4 *>(&kbias[16 * (kt0 + i) + 4 * g]);
+      }
+    } else {
+      const float c = a.scale * kLog2e;   // logits in log2 units
+      const uint64_t mk = kmask;
+#pragma unroll
+      for (int i = 0; i < NKT; ++i) {
+        km[i] = make_float4(c, c, c, c);
+        kbi[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (mk != ~0ull) {
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+          const uint32_t nib = static_cast<uint32_t>(mk >> (16 * (kt0 + i) + 4 * g)) & 0xfu;
+          kbi[i] = make_float4((nib & 1u) ? 0.f : -INFINITY, (nib & 2u) ? 0.f : -INFINITY,
+                               (nib & 4u) ? 0.f : -INFINITY, (nib & 8u) ? 0.f : -INFINITY);
+        }
+      }
+    }
+    float4 vs4[NKT];
+#pragma unroll
+    for (int i = 0; i < NKT; ++i)
+      if constexpr (VSCALE) vs4[i] = *reinterpret_cast<const float4 *>(&vsc[16 * (kt0 + i) + 4 * g]);
+      else vs4[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+    // logits and online softmax per head tile (lane's head = col)
+    constexpr int NKC = NKT / 2;   // 32-key halves of this wave
+    Frag<CT> pf[NTW][NKC];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      float x[NKT][4];
       float bm = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int i = 0; i < NKT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          x[kt][v] = fmaf(S[kt][v], f4_at(km[kt], v), f4_at(kbi[kt], v));
-          bm = fmaxf(bm, x[kt][v]);
+          x[i][v] = fmaf(S[j][i][v], f4_at(km[i], v), f4_at(kbi[i], v));
+          bm = fmaxf(bm, x[i][v]);
         }
       bm = max_xor32(max_xor16(bm));
       // Lazy rescaling: O and l stay relative to the reference max m_run, which
@@ -463,57 +490,57 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       }
       const float m_ref = m_run[j] == -INFINITY ? 0.f : m_run[j];   // masked keys: exp2(-inf) = 0
       float psum = 0.f;
-      float p[4][4];
+      float p[NKT][4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int i = 0; i < NKT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          p[kt][v] = fast_exp2(x[kt][v] - m_ref);
-          psum += p[kt][v];
+          p[i][v] = fast_exp2(x[i][v] - m_ref);
+          psum += p[i][v];
         }
       l_run[j] += psum;
-      // O += P . V over the two 32-key halves; V^T fragments read one step ahead
-      auto load_vf = [&](int kc, int n) {
-        Frag<CT> vf;
-        if constexpr (VROW) {
-          // keys 32kc + 4g + (0..3) and + 16 for dim 16n + col: in each 16-lane
-          // group lane i reads 4 dims of key 4g + i/4, and the transposing read
-          // hands lane col those 4 keys at its dim
-          const CT *vr = Vb + (32 * kc + 4 * g + (col >> 2)) * VS + 16 * n + 4 * (col & 3);
-          const uint2 lo = lds_read_tr16(vr);
-          const uint2 hi = lds_read_tr16(vr + 16 * VS);
-          vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        } else {
-          const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) { vf.v[u] = vr[u]; vf.v[4 + u] = vr[16 + u]; }
-        }
-        return vf;
-      };
-      float4 vs4[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        if constexpr (VSCALE) vs4[kt] = *reinterpret_cast<const float4 *>(&vsc[16 * kt + 4 * g]);
-        else vs4[kt] = make_float4(1.f, 1.f, 1.f, 1.f);
-      Frag<CT> vfb[2];
-      vfb[0] = load_vf(0, 0);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
+      for (int c2 = 0; c2 < NKC; ++c2) {
         float pv[8];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          pv[v] = p[2 * kc][v] * f4_at(vs4[2 * kc], v);
-          pv[4 + v] = p[2 * kc + 1][v] * f4_at(vs4[2 * kc + 1], v);
+          pv[v] = p[2 * c2][v] * f4_at(vs4[2 * c2], v);
+          pv[4 + v] = p[2 * c2 + 1][v] * f4_at(vs4[2 * c2 + 1], v);
         }
-        const Frag<CT> pf = frag_from_f32(pv, static_cast<Frag<CT> *>(nullptr));
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int step = kc * 8 + n;
-          if (step + 1 < 16) vfb[(step + 1) & 1] = load_vf((step + 1) >> 3, (step + 1) & 7);
-          O[j][n] = mma(pf, vfb[step & 1], O[j][n]);
-        }
+        pf[j][c2] = frag_from_f32(pv, static_cast<Frag<CT> *>(nullptr));
       }
     }
+    // O += P . V over this wave's 32-key halves: each V^T fragment is read
+    // once (one step ahead) and serves every head tile
+    auto load_vf = [&](int kc, int n) {
+      Frag<CT> vf;
+      if constexpr (VROW) {
+        // keys 32kc + 4g + (0..3) and + 16 for dim 16n + col: in each 16-lane
+        // group lane i reads 4 dims of key 4g + i/4, and the transposing read
+        // hands lane col those 4 keys at its dim
+        const CT *vr = Vb + (32 * kc + 4 * g + (col >> 2)) * VS + 16 * n + 4 * (col & 3);
+        const uint2 lo = lds_read_tr16(vr);
+        const uint2 hi = lds_read_tr16(vr + 16 * VS);
+        vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      } else {
+        const CT *vr = Vb + (16 * n + col) * VS + 32 * kc + 4 * g;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { vf.v[u] = vr[u]; vf.v[4 + u] = vr[16 + u]; }
+      }
+      return vf;
+    };
+    const int kc0 = kh * NKC;
+    Frag<CT> vfb[2];
+    vfb[0] = load_vf(kc0, 0);
+#pragma unroll
+    for (int c2 = 0; c2 < NKC; ++c2)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int step = c2 * 8 + n;
+        if (step + 1 < NKC * 8) vfb[(step + 1) & 1] = load_vf(kc0 + ((step + 1) >> 3), (step + 1) & 7);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) O[j][n] = mma(pf[j][c2], vfb[step & 1], O[j][n]);
+      }
   }
 
   // ---------------- 2. per O row (head 16*tile + 4g + v): its running max and sum
@@ -526,6 +553,40 @@ __global__ __launch_bounds__(HG * 64) void attend_kernel(const AttendArgs a) {
       Mh[j][v] = __shfl(m_run[j], 4 * g + v, 64);
       Lh[j][v] = __shfl(l_tot, 4 * g + v, 64);
     }
+  }
+
+  if constexpr (KH == 2) {
+    // the second key half hands its (m, l, O) to the first through LDS; the
+    // first rescales both to their common maximum and carries on alone
+    float *ho = reinterpret_cast<float *>(kv_lds) + hg * NTW * 16 * (OSTR + 2);   // [NTW*16][OSTR] O, then m, l
+    float *hm = ho + NTW * 16 * OSTR;
+    __syncthreads();                   // every wave is done with the last block's K and V
+    if (kh == 1) {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int hr = 16 * j + 4 * g + v;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) ho[hr * OSTR + 16 * n + col] = O[j][n][v];
+          if (col == 0) { hm[2 * hr] = Mh[j][v]; hm[2 * hr + 1] = Lh[j][v]; }
+        }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int hr = 16 * j + 4 * g + v;
+        const float m1 = hm[2 * hr], l1 = hm[2 * hr + 1], m0 = Mh[j][v];
+        const float mx = fmaxf(m0, m1);
+        const float s0 = mx == -INFINITY ? 0.f : fast_exp2(m0 - mx), s1 = mx == -INFINITY ? 0.f : fast_exp2(m1 - mx);
+        Mh[j][v] = mx;
+        Lh[j][v] = Lh[j][v] * s0 + l1 * s1;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) O[j][n][v] = O[j][n][v] * s0 + ho[hr * OSTR + 16 * n + col] * s1;
+      }
   }
 
   if (a.n_splits == 1) {
@@ -1081,10 +1142,12 @@ __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
 template <int ACT, int KV, int RS>
 void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.H) {
-    case 16: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 1, 1>), dim3(n_wg), dim3(64), 0, s, e0, e1, 0, a); break;
-    case 32: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 2, 1>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
-    case 64: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 4, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
-    case 128: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 4, 2>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
+    // 16 heads: two waves, each on half of every block's keys; more heads:
+    // one wave per 16-head tile (two tiles for 128), every wave on all keys
+    case 16: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 1, 1, 2>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
+    case 32: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 2, 1, 1>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
+    case 64: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 4, 1, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
+    case 128: hipExtLaunchKernelGGL((attend_kernel<ACT, KV, RS, 4, 2, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
     default: break;
   }
 }
