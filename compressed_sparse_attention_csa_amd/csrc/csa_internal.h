@@ -136,7 +136,7 @@ struct IdxChunkArgs {
   float *ss;               // [n_tok][ss_stride] sampled scores
   float *tau;              // [n_tok] thresholds
   int32_t *cnt;            // [n_tok][n_etiles] candidates per (query, entry tile)
-  uint64_t *cand;          // [n_tok][n_etiles][kChunkTileCand] keys (score bits << 32 | ~entry), entry order
+  uint64_t *cand;          // [n_tok][n_etiles][kChunkTileCand] candidates (entry << 32 | score bits), entry order
   float *fb_rows;          // [n_tok][fb_stride] full rows for the exact fallback
   int32_t *topk;           // [n_tok][k]
   uint32_t *err;

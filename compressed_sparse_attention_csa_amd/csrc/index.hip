@@ -1038,7 +1038,8 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
             if (take) {
               const int slot = run[mt] + __popc(seg & ((1u << col) - 1u));
               if (slot < kWgCand)
-                a.cand[(static_cast<int64_t>(qo) * a.n_etiles + et) * kWgCand + slot] = score_key(s, e);
+                a.cand[(static_cast<int64_t>(qo) * a.n_etiles + et) * kWgCand + slot] =
+                    (static_cast<uint64_t>(static_cast<uint32_t>(e)) << 32) | __float_as_uint(s);
             }
             run[mt] += __popc(seg);
           }
@@ -1142,7 +1143,8 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
       tk[u] = 0;
       if (i < c) {
         const int lo = tile_of[i];
-        tk[u] = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];
+        const uint64_t se = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];   // entry << 32 | score bits
+        tk[u] = score_key(__uint_as_float(static_cast<uint32_t>(se)), static_cast<int>(se >> 32));
       }
     }
 #pragma unroll
