@@ -162,26 +162,15 @@ __device__ __forceinline__ void block_reduce_minmax(float &lo, float &hi, float 
 // bins holding at least k values are kept, and tau is the smallest value in
 // them (an actual element, so at least k elements are >= tau). Any tau below
 // the k-th largest keeps the filter exact; binning only decides how tight it is.
-template <typename Get>
-__device__ float tau_lower_bound(Get get, int n, int k, int *hist, float *red, int *sh) {
-  const int t = threadIdx.x, bd = blockDim.x;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int i = t; i < n; i += bd) {
-    const float v = get(i);
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-  }
-  block_reduce_minmax(lo, hi, red);
-  if (!(hi > lo)) return lo;
-  const float sc = static_cast<float>(kTauBins - 1) / (hi - lo);
-  for (int i = t; i < kTauBins; i += bd) hist[i] = 0;
-  __syncthreads();
-  for (int i = t; i < n; i += bd) {
-    const int b = min(kTauBins - 1, static_cast<int>((get(i) - lo) * sc));
-    atomicAdd(&hist[b], 1);
-  }
-  __syncthreads();
-  // suffix counts from the top bin down: thread t owns bins [kTauBins-1-4t-3, kTauBins-1-4t]
+__device__ __forceinline__ float f4_elem(const float4 &f, int i) {
+  return i == 0 ? f.x : (i == 1 ? f.y : (i == 2 ? f.z : f.w));
+}
+
+// The bin holding the k-th largest of the values counted in hist (bins in
+// ascending value order): suffix counts from the top bin down, thread t owning
+// bins [kTauBins-1-4t-3, kTauBins-1-4t].
+__device__ int kth_bin_from_top(const int *hist, int k, int *sh) {
+  const int t = threadIdx.x;
   if (t == 0) sh[0] = 0;
   __syncthreads();
   int c4[4], tot = 0;
@@ -210,12 +199,76 @@ __device__ float tau_lower_bound(Get get, int n, int k, int *hist, float *red, i
     }
   }
   __syncthreads();
-  const int bstar = sh[0];
+  return sh[0];
+}
+
+// A threshold tau <= the k-th largest of n (> k) non-negative values given by
+// get(i): values are binned linearly between their min and max, the highest
+// bins holding at least k values are kept, and tau is the smallest value in
+// them (an actual element, so at least k elements are >= tau). Any tau below
+// the k-th largest keeps the filter exact; binning only decides how tight it is.
+template <typename Get>
+__device__ float tau_lower_bound(Get get, int n, int k, int *hist, float *red, int *sh) {
+  const int t = threadIdx.x, bd = blockDim.x;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = t; i < n; i += bd) {
+    const float v = get(i);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  block_reduce_minmax(lo, hi, red);
+  if (!(hi > lo)) return lo;
+  const float sc = static_cast<float>(kTauBins - 1) / (hi - lo);
+  for (int i = t; i < kTauBins; i += bd) hist[i] = 0;
+  __syncthreads();
+  for (int i = t; i < n; i += bd) {
+    const int b = min(kTauBins - 1, static_cast<int>((get(i) - lo) * sc));
+    atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  const int bstar = kth_bin_from_top(hist, k, sh);
   float m = INFINITY;
   for (int i = t; i < n; i += bd) {
     const float v = get(i);
     if (min(kTauBins - 1, static_cast<int>((v - lo) * sc)) >= bstar) m = fminf(m, v);
   }
+  return block_reduce_min(m, red);
+}
+
+// The same threshold over values held in registers by a 256-thread block:
+// thread t holds values 4 (256 u + t) + q (q < 4) in v[u], those below n valid.
+template <int U>
+__device__ float tau_lower_bound_regs(const float4 (&v)[U], int n, int k, int *hist, float *red, int *sh) {
+  const int t = threadIdx.x;
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (4 * (256 * u + t) + q < n) {
+        lo = fminf(lo, f4_elem(v[u], q));
+        hi = fmaxf(hi, f4_elem(v[u], q));
+      }
+  block_reduce_minmax(lo, hi, red);
+  if (!(hi > lo)) return lo;
+  const float sc = static_cast<float>(kTauBins - 1) / (hi - lo);
+  for (int i = t; i < kTauBins; i += 256) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (4 * (256 * u + t) + q < n) atomicAdd(&hist[min(kTauBins - 1, static_cast<int>((f4_elem(v[u], q) - lo) * sc))], 1);
+  __syncthreads();
+  const int bstar = kth_bin_from_top(hist, k, sh);
+  float m = INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x = f4_elem(v[u], q);
+      if (4 * (256 * u + t) + q < n && min(kTauBins - 1, static_cast<int>((x - lo) * sc)) >= bstar) m = fminf(m, x);
+    }
   return block_reduce_min(m, red);
 }
 
@@ -560,7 +613,6 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
 // ------------------------------------------------------------------ decode filter
 
 __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) {
-  __shared__ float vals[kMaxGroups];
   __shared__ int hist[kTauBins];
   __shared__ float red[32];
   __shared__ int sh[4];
@@ -592,23 +644,17 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
       for (int q = 0; q < 4; ++q) sv[u + q] = t0 + u + q < e_end ? Srow[t0 + u + q] : -1.f;
     }
   }
-  // group maxima -> LDS (8 independent loads per round)
-  for (int base = 0; base < nG; base += 256 * 8) {
-    float tmp[8];
+  // the query's group maxima in registers, 16-byte loads issued with the
+  // score loads (one round trip); M rows are padded to 256 floats
+  constexpr int kGU = kMaxGroups / 1024;
+  float4 mv[kGU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * 256 + tid;
-      tmp[u] = i < nG ? Mrow[i] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * 256 + tid;
-      if (i < nG) vals[i] = tmp[u];
-    }
+  for (int u = 0; u < kGU; ++u) {
+    const int i4 = 256 * u + tid;
+    mv[u] = 4 * i4 < nG ? *reinterpret_cast<const float4 *>(Mrow + 4 * i4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  __syncthreads();
   float tau = 0.f;
-  if (nG > a.k) tau = tau_lower_bound([&](int i) { return vals[i]; }, nG, a.k, hist, red, sh);
+  if (nG > a.k) tau = tau_lower_bound_regs(mv, nG, a.k, hist, red, sh);
 
   // ordered compaction into this slice's own region
   int mine = 0;
