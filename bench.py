@@ -52,7 +52,9 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device copy after timing (reference kernel for HBM counters)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk MFMA-utilisation leg")
-    ap.add_argument("--prefill-only", action="store_true", help="only run the prefill-chunk leg (development)")
+    ap.add_argument("--prefill-only", action="store_true", help="only run the prefill-chunk leg (same as --only prefill)")
+    ap.add_argument("--only", choices=["c1", "c2", "c5", "prefill", "hca"],
+                    help="run only this leg and print its record (profiling one workload at a time)")
     ap.add_argument("--no-hca", action="store_true", help="skip the heavily-compressed-attention leg")
     ap.add_argument("--no-hier", action="store_true", help="skip the hierarchical-indexer (pool / Reindex) leg")
     ap.add_argument("--no-swa-fp8", action="store_true", help="skip the fp8 window-ring decode leg")
@@ -724,8 +726,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.lib()
-    if args.prefill_only:
-        print(json.dumps(prefill_leg(args.seed, dev)), flush=True)
+    only = "prefill" if args.prefill_only else args.only
+    if only:
+        legs = {"c1": lambda: c1_leg(args.seed, dev, args.replicas, args.steps),
+                "c2": lambda: c2_leg(args.seed, dev, args.replicas, args.steps),
+                "c5": lambda: c5_leg(args.seed, dev, args.replicas, args.steps),
+                "prefill": lambda: prefill_leg(args.seed, dev),
+                "hca": lambda: hca_leg(args.seed, dev)}
+        print(json.dumps(legs[only]()), flush=True)
         return
     t_build = time.time()
     caches = build_cache(args.seed, args.replicas, dev)
