@@ -318,6 +318,13 @@ csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, c
  *   q           (dev) [n_q][H_q][D] act_dtype.   topk (dev) [n_q][k] int32, k >= 0.
  *   scale       logit scale (1/sqrt(D) in the method).
  *   out         (dev) [n_q][H_q][D] act_dtype.
+ * Errors: CSA_ERR_INVALID_ARG for a bad layer, pointer or position;
+ * CSA_ERR_CAPACITY when a query's window rows already left the ring or the
+ * workspace cannot hold the split partials; CSA_ERR_UNSUPPORTED for k outside
+ * [0, CSA_MAX_TOPK] or when a decode query's keys (k + W) need more splits
+ * than the merge takes: min(80, 5120 / min(n_q, 128)) splits of 2,048 keys
+ * (2,304 for fp32 caches), i.e. 163,840 keys for batches of up to 64.
+ * Prefill chunks (consecutive positions of one sequence) have no such bound.
  */
 csa_status csa_attend(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
                       const int32_t *q_pos, const void *q, const int32_t *topk, int32_t k, float scale,
@@ -352,8 +359,8 @@ csa_status csa_attend_noalloc(csa_cache_t h, int32_t layer, int32_t n_q, const i
  *
  *   Arguments as for csa_attend, without topk and k.
  *   out[t][h] = sum_key p * v over keys {Kbar[j] : j < (t+1)/r} u window rows.
- * Errors: CSA_ERR_UNSUPPORTED when a query sees more than about 92,000
- * entries (40 splits of 36 blocks of 64 keys).
+ * Errors: as csa_attend, with k replaced by the visible entries: a decode
+ * query may see up to 163,840 keys (entries + W) in batches of up to 64.
  */
 csa_status csa_attend_dense(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t *q_seq,
                             const int32_t *q_pos, const void *q, float scale, void *out,
@@ -379,7 +386,10 @@ csa_status csa_read_errors(csa_cache_t h, hipStream_t stream, uint32_t *flags);
 csa_status csa_profile_begin(csa_cache_t h, int32_t kernels);
 csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int32_t *launches);
 
-/* Runs the device number-format routines on n values (tests of the codecs):
+/* ---- Test and measurement hooks (not part of the method) ---------------- */
+
+/* Test hook: runs the device number-format routines on n values (the codec
+ * tests compare them with the oracle's encoders bit for bit):
  * kind 0: fp8 e4m3 codes (uint8) -> fp32 as the attention/indexer kernels decode them;
  * kind 1: fp8 e4m3 codes (uint8) -> bf16 bits (uint16) as the MFMA operands are built;
  * kind 2: fp32 -> fp8 e4m3 codes (uint8) as the compressor encodes (RNE, saturating);
@@ -390,8 +400,9 @@ csa_status csa_profile_end(csa_cache_t h, int32_t kernel, double *total_ms, int3
  * in/out are device pointers. */
 csa_status csa_debug_convert(int32_t kind, const void *in, void *out, int64_t n, hipStream_t stream);
 
-/* Streaming-read reference for the indexer scan's bandwidth (a measurement aid,
- * not part of the method): reads `bytes` of device memory per launch with
+/* Measurement hook: a streaming-read reference for the indexer scan's
+ * bandwidth, reported by the benchmark beside the scan. Reads `bytes` of
+ * device memory per launch with
  * 16-byte non-temporal loads (the scan's load form), `reps` launches rotating
  * over the n_bufs device buffers bufs[i] (each >= bytes, 16-byte aligned; use
  * enough of them to exceed the last-level cache), each launch timed by events
