@@ -503,18 +503,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
 #pragma unroll
     for (int p = 0; p < PPW; ++p) pps[p] = wave_e0 + p * kPage < N ? bt[(wave_e0 >> 6) + p] : -1;
 
-    // A operand: indexer query heads as rows (rows >= H_I are zero)
-    Frag<CT> qa[2];
-    qa[0] = qa[1] = zero_frag<CT>();
-    if (col < a.h_i) {
-      const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + col) * kDI * AE;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) qa[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
-    }
-    float wv[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
-
+    // A operands, one per 16-entry tile of a page: the indexer heads in rows
+    // [4 tl, 4 tl + 4), zero elsewhere. The page's four tiles accumulate into
+    // one MFMA result whose lane (g, col) holds the heads' dot products for
+    // entry 16 g + col of the page, so the epilogue runs once per page with
+    // every lane scoring one entry (rows >= H_I of a tile are zero).
     // every key load of the wave in flight together: lane (g, col) reads dims
     // [16g, 16g + 16) of entry col of each 16-entry tile; the key stream is
     // read once, so the loads are non-temporal
@@ -547,13 +540,32 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
       if (!okp[p] && lane == 0 && wave_e0 + p * kPage < N) flag_error(a.err, ERR_PAGE);
       scs[p] = (KV == DT_FP8 && okp[p]) ? a.kidx_scale[pps[p]] : 1.f;
     }
+    // (issued after the key loads, which are the long pole) this lane's head
+    // row, placed in the tile (col / 4) whose rows it supplies
+    Frag<CT> qv[2];
+    qv[0] = qv[1] = zero_frag<CT>();
+    if ((col & 3) < a.h_i) {
+      const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + (col & 3)) * kDI * AE;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qv[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+    }
+    Frag<CT> qa[4][2];
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qa[tl][c] = (col >> 2) == tl ? qv[c] : zero_frag<CT>();
+    float wv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
 
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
+      const int e_page = wave_e0 + p * kPage;
+      if (e_page >= N) break;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl) {
-        const int e_tile = wave_e0 + p * kPage + tl * 16;
-        if (e_tile >= N) break;
+        if (e_page + tl * 16 >= N) break;
         Frag<CT> kb[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -562,33 +574,30 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
           else if constexpr (KV == DT_BF16) kb[c] = LoadFrag<DT_BF16, __bf16>::load(rp);
           else kb[c] = LoadFrag<DT_F32, float>::load(rp);
         }
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(qa[0], kb[0], acc);
-        acc = mma(qa[1], kb[1], acc);
-        const int e = e_tile + col;
-        float s = 0.f;
+        acc = mma(qa[tl][0], kb[0], acc);
+        acc = mma(qa[tl][1], kb[1], acc);
+      }
+      const int e = e_page + lane;   // lane = 16 g + col
+      float s = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
-        s = okp[p] ? s * scs[p] : -1.f;   // a missing page scores -1 (and is flagged)
-        if (g == 0 && e < N) Srow[e] = s;
-        if (a.B) {   // maxima of aligned 8-entry blocks (candidate pool)
-          float m8 = e < N ? s : -INFINITY;
-          m8 = group_max(m8, kPoolBlock);
-          if (g == 0 && (col & (kPoolBlock - 1)) == 0 && e < N) a.B[static_cast<int64_t>(qi) * a.s_stride + (e >> 3)] = m8;
-        }
-        // group maxima: entries past N do not take part
-        float m = e < N ? s : -INFINITY;
-        if (G <= 16) {
-          m = group_max(m, G);
-          if (g == 0 && (col & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
-        } else {
-          m = group_max(m, 16);
-          run = fmaxf(run, m);
-          if (!cross && ((((e_tile + 16) & (G - 1)) == 0) || (e_tile + 16 >= N))) {
-            if (lane == 0) Mrow[e_tile >> glog2] = run;
-            run = -INFINITY;
-          }
-        }
+      for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
+      s = okp[p] ? s * scs[p] : -1.f;   // a missing page scores -1 (and is flagged)
+      if (e < N) Srow[e] = s;
+      if (a.B) {   // maxima of aligned 8-entry blocks (candidate pool)
+        float m8 = e < N ? s : -INFINITY;
+        m8 = group_max(m8, kPoolBlock);
+        if ((col & (kPoolBlock - 1)) == 0 && e < N) a.B[static_cast<int64_t>(qi) * a.s_stride + (e >> 3)] = m8;
+      }
+      // group maxima: entries past N do not take part; a group of G <= 64
+      // entries is G consecutive lanes
+      float m = e < N ? s : -INFINITY;
+      m = group_max(m, G < 16 ? G : 16);
+      if (G >= 32) m = max_xor16(m);
+      if (G >= 64) m = max_xor32(m);
+      if (!cross) {
+        if ((lane & (G - 1)) == 0 && e < N) Mrow[e >> glog2] = m;
+      } else {
+        run = fmaxf(run, m);
       }
     }
   }
@@ -817,17 +826,6 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) pg[tl] = ent[tl] >= 0 ? bt[ent[tl] >> 6] : -1;
 
-  Frag<CT> qa[2];
-  qa[0] = qa[1] = zero_frag<CT>();
-  if (col < a.h_i) {
-    const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + col) * kDI * AE;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) qa[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
-  }
-  float wv[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
-
   constexpr int RW = KE;
   const char *kbase = reinterpret_cast<const char *>(a.kidx);
   uint4 raw[4][RW];
@@ -849,11 +847,24 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
   float sc[4];
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) sc[tl] = (KV == DT_FP8 && ok[tl]) ? a.kidx_scale[pg[tl]] : 1.f;
+  // (after the key loads) this lane's head row, in the tile (col / 4) whose
+  // rows it supplies: the four tiles accumulate into one MFMA result whose
+  // lane (g, col) holds the heads of position 16 g + col, as in the scan
+  Frag<CT> qv[2];
+  qv[0] = qv[1] = zero_frag<CT>();
+  if ((col & 3) < a.h_i) {
+    const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + (col & 3)) * kDI * AE;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qv[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+  }
+  float wv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
 
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
-    const int p_tile = wave_p0 + tl * 16;
-    if (p_tile >= V) break;
+    if (wave_p0 + tl * 16 >= V) break;
     Frag<CT> kb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -862,19 +873,22 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
       else if constexpr (KV == DT_BF16) kb[c] = LoadFrag<DT_BF16, __bf16>::load(rp);
       else kb[c] = LoadFrag<DT_F32, float>::load(rp);
     }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mma(qa[0], kb[0], acc);
-    acc = mma(qa[1], kb[1], acc);
-    float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
-    s = ok[tl] ? s * sc[tl] : 0.f;
-    const int p = p_tile + col;
-    if (g == 0 && p < V) Srow[p] = s;
-    float m = p < V ? s : -INFINITY;
-    m = group_max(m, G);
-    if (g == 0 && (col & (G - 1)) == 0 && p < V) Mrow[p >> glog2] = m;
+    const Frag<CT> q0 = (col >> 2) == tl ? qv[0] : zero_frag<CT>(), q1 = (col >> 2) == tl ? qv[1] : zero_frag<CT>();
+    acc = mma(q0, kb[0], acc);
+    acc = mma(q1, kb[1], acc);
   }
+  // lane (g, col): position 16 g + col of the wave, its tile g's scale and validity
+  const float scl = g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
+  const bool okl = g == 0 ? ok[0] : (g == 1 ? ok[1] : (g == 2 ? ok[2] : ok[3]));
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
+  s = okl ? s * scl : 0.f;
+  const int p = wave_p0 + lane;
+  if (p < V) Srow[p] = s;
+  float m = p < V ? s : -INFINITY;
+  m = group_max(m, G);
+  if ((col & (G - 1)) == 0 && p < V) Mrow[p >> glog2] = m;
 }
 
 // ------------------------------------------------------------------ chunk (prefill) index
