@@ -672,6 +672,23 @@ csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, con
     const int nq = std::min(kIdxMaxQ, n_q - g0);
     int nmax = 0;
     for (int i = 0; i < nq; ++i) nmax = std::max(nmax, (q_pos[g0 + i] + 1) / c.ratio);
+    // short rows (no pool): one workgroup per query scores and selects
+    const int key_bytes = kv == DT_F32 ? 4 : (kv == DT_BF16 ? 2 : 1);
+    if (!pool && nmax <= kSmallEntries && static_cast<int64_t>(nmax) * kDI * key_bytes <= kSmallBytes) {
+      IdxScanArgs s{};
+      s.kidx = h->buf.kidx; s.kidx_scale = h->buf.kidx_scale; s.block_table = h->buf.block_table;
+      s.q_idx = reinterpret_cast<const char *>(q_idx) + static_cast<int64_t>(g0) * c.idx_heads * kDI * ab;
+      s.w_idx = w_idx + static_cast<int64_t>(g0) * c.idx_heads;
+      s.err = h->err;
+      s.bt_stride = c.max_pages_per_seq; s.pool_pages = c.pool_pages; s.h_i = c.idx_heads; s.n_q = nq;
+      for (int i = 0; i < nq; ++i) {
+        s.q[i].seq = q_seq[g0 + i];
+        s.q[i].n_vis = (q_pos[g0 + i] + 1) / c.ratio;
+      }
+      const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
+      launch_idx_small(s, kv, act, topk + static_cast<int64_t>(g0) * k, k, stream, ev.start, ev.stop);
+      continue;
+    }
     const int64_t s_stride = std::max<int64_t>(kIdxChunk, (static_cast<int64_t>(nmax) + kIdxChunk - 1) / kIdxChunk * kIdxChunk);
     const size_t need = idx_decode_bytes(nq, s_stride);
     if (need > h->scratch_bytes)

@@ -152,6 +152,13 @@ struct IdxChunkArgs {
 // that does the score work (the scan; in chunk mode the full-score GEMM pass).
 void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,
                      hipEvent_t ev1 = nullptr);
+// Short rows: a query with at most kSmallEntries visible entries and at most
+// kSmallBytes of indexer keys is scored and selected by one workgroup (one
+// launch for the group; topk rows as for the final kernel).
+constexpr int kSmallEntries = 4096;
+constexpr int kSmallBytes = 256 << 10;
+void launch_idx_small(const IdxScanArgs &a, int kv, int act, int32_t *topk, int k, hipStream_t s,
+                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s);
 void launch_idx_final(const IdxFinalArgs &a, hipStream_t s);
 void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hipEvent_t ev0 = nullptr,

@@ -619,6 +619,120 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
   }
 }
 
+// ------------------------------------------------------------------ short rows
+//
+// A query whose visible indexer keys are few (at most kSmallEntries, and at
+// most kSmallBytes of keys) is scored and selected by one workgroup: its 16
+// waves score pages w, w + 16, ... with the scan's MFMA tile (small_batch
+// pages' loads in flight at once), the keys go to LDS, and the same exact
+// select as the final kernel writes the ascending row. One launch instead of
+// scan, filter and final.
+constexpr int kSmallWaves = 16;
+template <int KV> constexpr int small_batch() { return 4 / elem_bytes<KV>(); }
+
+template <int ACT, int KV>
+__global__ __launch_bounds__(kSmallWaves * 64) void idx_small_kernel(const IdxScanArgs a, int32_t *topk, int k) {
+  using CT = typename ComputeT<KV>::type;
+  constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
+  constexpr int RW = KE;                 // uint4 per lane per 16-entry tile
+  constexpr int PB = small_batch<KV>();  // pages per wave in flight
+  __shared__ uint64_t keys[kSmallEntries];
+  __shared__ uint64_t bin_keys[kRankCap];
+  __shared__ int hist[kSelBins];
+  __shared__ float red[32];
+  __shared__ int sh[4];
+  const int qi = blockIdx.x, tid = threadIdx.x;
+  const IdxQuery Q = a.q[qi];
+  const int N = Q.n_vis;
+  int32_t *out = topk + static_cast<int64_t>(qi) * k;
+  if (N <= k) {
+    for (int i = tid; i < k; i += kSmallWaves * 64) out[i] = i < N ? i : -1;
+    return;
+  }
+  const int lane = tid & 63, g = lane >> 4, col = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_pages = (N + kPage - 1) / kPage;   // <= 64: 4 per wave
+  const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
+  // lane j holds the physical id of this wave's j-th page (page w + 16 j)
+  const int my_pp = (lane < 4 && w + kSmallWaves * lane < n_pages) ? bt[w + kSmallWaves * lane] : -1;
+  Frag<CT> qv[2];
+  qv[0] = qv[1] = zero_frag<CT>();
+  if ((col & 3) < a.h_i) {
+    const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + (col & 3)) * kDI * AE;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qv[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+  }
+  float wv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
+  const char *kbase = reinterpret_cast<const char *>(a.kidx);
+
+  for (int j0 = 0; w + kSmallWaves * j0 < n_pages; j0 += PB) {
+    uint4 raw[PB][4][RW];
+    bool okp[PB];
+    int pps[PB];
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      const int page = w + kSmallWaves * (j0 + jj);
+      pps[jj] = __builtin_amdgcn_readlane(my_pp, (j0 + jj) & 63);
+      okp[jj] = page < n_pages && pps[jj] >= 0 && pps[jj] < a.pool_pages;
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) {
+        const int e = page * kPage + tl * 16 + col;
+        if (okp[jj] && e < N) {
+          const uint4 *src = reinterpret_cast<const uint4 *>(kbase + ((static_cast<int64_t>(pps[jj]) * kPage + (e & 63)) * kDI + 16 * g) * KE);
+#pragma unroll
+          for (int u = 0; u < RW; ++u) raw[jj][tl][u] = src[u];
+        } else {
+#pragma unroll
+          for (int u = 0; u < RW; ++u) raw[jj][tl][u] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    float scs[PB];
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      const int page = w + kSmallWaves * (j0 + jj);
+      if (page < n_pages && !okp[jj] && lane == 0) flag_error(a.err, ERR_PAGE);
+      scs[jj] = (KV == DT_FP8 && okp[jj]) ? a.kidx_scale[pps[jj]] : 1.f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < PB; ++jj) {
+      const int page = w + kSmallWaves * (j0 + jj);
+      if (page >= n_pages) break;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) {
+        Frag<CT> kb[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const char *rp = reinterpret_cast<const char *>(&raw[jj][tl][0]) + 8 * c * KE;
+          if constexpr (KV == DT_FP8) kb[c] = LoadFrag<DT_FP8, __bf16>::load(rp);
+          else if constexpr (KV == DT_BF16) kb[c] = LoadFrag<DT_BF16, __bf16>::load(rp);
+          else kb[c] = LoadFrag<DT_F32, float>::load(rp);
+        }
+        // this lane's head row only in the tile whose rows it supplies
+        const bool mine = (col >> 2) == tl;
+        acc = mma(mine ? qv[0] : zero_frag<CT>(), kb[0], acc);
+        acc = mma(mine ? qv[1] : zero_frag<CT>(), kb[1], acc);
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s += wv[v] * fmaxf(acc[v], 0.f);
+      s = okp[jj] ? s * scs[jj] : -1.f;   // a missing page scores -1 (and is flagged)
+      const int e = page * kPage + lane;
+      if (e < N) keys[e] = score_key(s, e);
+    }
+  }
+  __syncthreads();
+  if (!select_ordered(keys, N, k, hist, red, sh, bin_keys, out)) {
+    // heavy ties: the exact radix select over the same keys
+    if (tid == 0) flag_error(a.err, ERR_FALLBACK);
+    __syncthreads();
+    select_and_write([&](int i) { return keys[i]; }, N, k, reinterpret_cast<int *>(bin_keys), hist, sh, out);
+  }
+}
+
 // ------------------------------------------------------------------ decode filter
 
 __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) {
@@ -1285,6 +1399,17 @@ void launch_idx_scan(const IdxScanArgs &a, int kv, int act, hipStream_t s, hipEv
     hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_BF16>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
   else if (kv == DT_FP8 && act == DT_BF16)
     hipExtLaunchKernelGGL((idx_scan_kernel<DT_BF16, DT_FP8>), dim3(a.total_wg), dim3(kScanWaves * 64), 0, s, ev0, ev1, 0, a);
+}
+
+void launch_idx_small(const IdxScanArgs &a, int kv, int act, int32_t *topk, int k, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1) {
+  if (a.n_q <= 0) return;
+  if (kv == DT_F32 && act == DT_F32)
+    hipExtLaunchKernelGGL((idx_small_kernel<DT_F32, DT_F32>), dim3(a.n_q), dim3(kSmallWaves * 64), 0, s, ev0, ev1, 0, a, topk, k);
+  else if (kv == DT_BF16 && act == DT_BF16)
+    hipExtLaunchKernelGGL((idx_small_kernel<DT_BF16, DT_BF16>), dim3(a.n_q), dim3(kSmallWaves * 64), 0, s, ev0, ev1, 0, a, topk, k);
+  else if (kv == DT_FP8 && act == DT_BF16)
+    hipExtLaunchKernelGGL((idx_small_kernel<DT_BF16, DT_FP8>), dim3(a.n_q), dim3(kSmallWaves * 64), 0, s, ev0, ev1, 0, a, topk, k);
 }
 
 void launch_idx_filter(const IdxFilterArgs &a, int n_wg, hipStream_t s) {

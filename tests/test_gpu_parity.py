@@ -228,6 +228,8 @@ def test_index_fewer_heads(h_i):
 @pytest.mark.parametrize("kv,act", DT_CASES)
 def test_index_exact_ties_go_to_lower_index(kv, act):
     _index_case(kv, act, lens=[4 * 3000, 4 * 200], k=96, dup_keys=True, exact=True)
+    # rows past the one-workgroup limit go through scan, filter and final
+    _index_case(kv, act, lens=[4 * 9000, 4 * 5000], k=96, dup_keys=True, exact=True)
 
 
 @pytest.mark.parametrize("kv,act", DT_CASES)
@@ -504,14 +506,14 @@ def test_bad_page_ids_are_flagged_not_faulting():
     assert cache.read_errors() & B.ERR_TOPK
 
 
-@pytest.mark.parametrize("n_tok", [1, 8])
-def test_bad_pages_lose_the_exact_fallback(n_tok):
+@pytest.mark.parametrize("n_tok,n", [(1, 16000), (8, 16000), (1, 2000)])
+def test_bad_pages_lose_the_exact_fallback(n_tok, n):
     """All-zero indexer queries tie every real entry at score 0, which sends the
-    decode select (n_tok = 1) and the chunk select (n_tok = 8) to the exact
-    full-row fallback. There the entries of pages whose ids lie outside the pool
-    score below every real entry, so the Top-K is the lowest-index real entries
-    and skips those pages."""
-    r, n, k = 4, 16000, 64
+    decode select (n_tok = 1; a short row, n = 2,000, in the one-workgroup
+    kernel) and the chunk select (n_tok = 8) to the exact fallback. There the
+    entries of pages whose ids lie outside the pool score below every real
+    entry, so the Top-K is the lowest-index real entries and skips those pages."""
+    r, k = 4, 64
     L = r * n
     cache = make_cache(62, ratio=r, q_heads=16, window=16, ring_rows=32, max_seqs=1, max_pages_per_seq=n // 64 + 2,
                        pool_pages=n // 64 + 4, kv_dtype="bf16", act_dtype="bf16", max_queries=n_tok, max_k=k)
