@@ -357,6 +357,38 @@ __device__ void select_and_write(GetKey key_of, int n, int k, int *sel, int *his
 constexpr int kRankCap = 1024;
 constexpr int kSelBins = 2048;
 
+// The bin b* of hist (kSelBins counts, bins ascending in value) that holds the
+// k-th largest counted value, and how many values lie in higher bins:
+// sh[0] = b*, sh[1] = that count. Suffix counts, kSelBins / blockDim bins per
+// thread from the top; ends with a barrier.
+__device__ void boundary_bin(const int *hist, int k, int *sh) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
+  constexpr int kMaxPer = kSelBins / 256;
+  const int per = kSelBins / bd;
+  int cnt[kMaxPer], tot = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    cnt[j] = j < per ? hist[kSelBins - 1 - per * t - j] : 0;
+    tot += cnt[j];
+  }
+  int incl = tot;
+  incl = wave_incl_sum(incl);
+  __shared__ int wsum_b[16];
+  if (lane == 63) wsum_b[w] = incl;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum_b[i];
+  const int excl = incl - tot;
+  if (excl < k && incl >= k) {
+    int cum = excl;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      if (j < per && cum + cnt[j] >= k) { sh[0] = kSelBins - 1 - per * t - j; sh[1] = cum; break; }
+      cum += cnt[j];
+    }
+  }
+  __syncthreads();
+}
+
 template <typename Map = IdMap>
 __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist, float *red, int *sh,
                                uint64_t *bin_keys, int32_t *out, Map map = Map()) {
@@ -376,31 +408,7 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   __syncthreads();
   for (int i = t; i < c; i += bd) atomicAdd(&hist[bin_of(cand_key[i])], 1);
   __syncthreads();
-  // bin b* holding the k-th largest: suffix counts, kSelBins / bd bins per thread (descending)
-  constexpr int kMaxPer = kSelBins / 256;
-  const int per = kSelBins / bd;
-  int cnt[kMaxPer], tot = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    cnt[j] = j < per ? hist[kSelBins - 1 - per * t - j] : 0;
-    tot += cnt[j];
-  }
-  int incl = tot;
-  incl = wave_incl_sum(incl);
-  __shared__ int wsum2[16];
-  if (lane == 63) wsum2[w] = incl;
-  __syncthreads();
-  for (int i = 0; i < w; ++i) incl += wsum2[i];
-  const int excl = incl - tot;
-  if (excl < k && incl >= k) {
-    int cum = excl;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      if (j < per && cum + cnt[j] >= k) { sh[0] = kSelBins - 1 - per * t - j; sh[1] = cum; break; }
-      cum += cnt[j];
-    }
-  }
-  __syncthreads();
+  boundary_bin(hist, k, sh);
   const int bstar = sh[0], above = sh[1];
   const int need = k - above;            // keys to take from bin b*
   const int m = hist[bstar];
@@ -426,7 +434,7 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   for (int i = i0; i < i1; ++i) mine += cand_key[i] >= kth;
   int inc2 = mine;
   inc2 = wave_incl_sum(inc2);
-  __syncthreads();
+  __shared__ int wsum2[16];
   if (lane == 63) wsum2[w] = inc2;
   __syncthreads();
   for (int i = 0; i < w; ++i) inc2 += wsum2[i];
@@ -434,6 +442,75 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
   for (int i = i0; i < i1; ++i)
     if (cand_key[i] >= kth) out[pos++] = map(key_index(cand_key[i]));
   (void)nw;
+  return true;
+}
+
+// The same selection over candidates held in registers by the block: thread t
+// holds candidates [t s, t s + s) (s = ceil(c / blockDim) <= P) in kr[0..s),
+// so every thread's candidates are consecutive and the compaction keeps their
+// order. No pass re-reads the candidates from LDS; each key's bin is computed
+// once.
+template <int P, typename Map = IdMap>
+__device__ bool select_ordered_regs(const uint64_t (&kr)[P], int c, int k, int *hist, float *red, int *sh,
+                                    uint64_t *bin_keys, int32_t *out, Map map = Map()) {
+  const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
+  const int span = (c + bd - 1) / bd, i0 = t * span;
+  bool ok[P];
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    ok[u] = u < span && i0 + u < c;
+    if (ok[u]) {
+      const float v = bits_score(static_cast<uint32_t>(kr[u] >> 32));
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+  }
+  for (int i = t; i < kSelBins; i += bd) hist[i] = 0;
+  block_reduce_minmax(lo, hi, red);   // its barriers also order the clear before the counts
+  const float sc = hi > lo ? static_cast<float>(kSelBins - 1) / (hi - lo) : 0.f;
+  int bn[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    bn[u] = -1;
+    if (ok[u]) {
+      bn[u] = min(kSelBins - 1, static_cast<int>((bits_score(static_cast<uint32_t>(kr[u] >> 32)) - lo) * sc));
+      atomicAdd(&hist[bn[u]], 1);
+    }
+  }
+  __syncthreads();
+  boundary_bin(hist, k, sh);
+  const int bstar = sh[0], above = sh[1];
+  const int need = k - above;            // keys to take from bin b*
+  const int m = hist[bstar];
+  if (m > kRankCap) return false;
+  if (t == 0) sh[2] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < P; ++u)
+    if (bn[u] == bstar) bin_keys[atomicAdd(&sh[2], 1)] = kr[u];
+  __syncthreads();
+  // threshold key: the need-th largest key of the bin, by exact rank
+  for (int i = t; i < m; i += bd) {
+    const uint64_t x = bin_keys[i];
+    int r = 0;
+    for (int j = 0; j < m; ++j) r += bin_keys[j] > x;
+    if (r == need - 1) sh[3] = static_cast<int>(i);
+  }
+  __syncthreads();
+  const uint64_t kth = bin_keys[sh[3]];
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < P; ++u) mine += (ok[u] && kr[u] >= kth) ? 1 : 0;
+  int inc = wave_incl_sum(mine);
+  __shared__ int wsum_r[16];
+  if (lane == 63) wsum_r[w] = inc;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) inc += wsum_r[i];
+  int pos = inc - mine;
+#pragma unroll
+  for (int u = 0; u < P; ++u)
+    if (ok[u] && kr[u] >= kth) out[pos++] = map(key_index(kr[u]));
   return true;
 }
 
@@ -804,7 +881,6 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
 // ------------------------------------------------------------------ decode final
 
 struct FinalLds {
-  uint64_t keys[kSelCap];
   uint64_t bin_keys[kRankCap];
   int sel[CSA_MAX_TOPK];
   int hist[kSelBins];
@@ -816,7 +892,7 @@ struct FinalLds {
 
 template <typename Map>
 __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, int k, int32_t *out, Map map) {
-  uint64_t *keys = L.keys, *bin_keys = L.bin_keys;
+  uint64_t *bin_keys = L.bin_keys;
   int *sel = L.sel, *hist = L.hist, *soff = L.soff, *sh = L.sh, *wsum_f = L.wsum_f;
   float *red = L.red;
   const int tid = threadIdx.x;
@@ -846,15 +922,17 @@ __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, 
         for (int i = soff[t]; i < soff[t + 1]; ++i) slice_of[i] = static_cast<uint16_t>(t);
       __syncthreads();
     }
+    // thread tid holds candidates [tid s, tid s + s), s = ceil(c / 512), in registers
     constexpr int kPer = (kSelCap + 511) / 512;
+    const int span = (c + 511) / 512, i0 = tid * span;
     float ts[kPer];
     int tj[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * 512 + tid;
+    for (int u = 0; u < kPer; ++u) {   // every load first, then the keys
+      const int i = i0 + u;
       ts[u] = 0.f;
       tj[u] = 0;
-      if (i < c) {
+      if (u < span && i < c) {
         int lo = 0;                     // slice s with soff[s] <= i < soff[s+1]
         if (mapped) {
           lo = slice_of[i];
@@ -870,13 +948,11 @@ __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, 
         tj[u] = a.cand_j[o];
       }
     }
+    uint64_t tk[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * 512 + tid;
-      if (i < c) keys[i] = score_key(ts[u], tj[u]);
-    }
-    __syncthreads();
-    done = select_ordered(keys, c, k, hist, red, sh, bin_keys, out, map);
+    for (int u = 0; u < kPer; ++u) tk[u] = score_key(ts[u], tj[u]);
+    // (the select's first barrier comes after every read of slice_of, which it then reuses)
+    done = select_ordered_regs(tk, c, k, hist, red, sh, bin_keys, out, map);
   }
   if (!done) {
     // heavy ties or too many candidates: exact select straight from the scores
@@ -1265,15 +1341,13 @@ __device__ __forceinline__ float chunk_k(const IdxChunkArgs &a, int pp, int slot
 // Per query: its candidates (per-tile slot runs, already in entry order) are
 // gathered into LDS and the exact Top-K is selected and written ascending.
 __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArgs a) {
-  __shared__ uint64_t keys[kChunkCandCap];   // the fallback reuses it as its index list
   __shared__ uint64_t bin_keys[kRankCap];
   __shared__ int hist[kSelBins];
   __shared__ float red[32];
   __shared__ int sh[4];
   __shared__ int wsum[16];
   __shared__ int toff[kMaxChunkTiles + 1];
-  int *sel = reinterpret_cast<int *>(keys);
-  static_assert(kChunkCandCap * 2 >= CSA_MAX_TOPK, "fallback index list fits the key buffer");
+  __shared__ int sel[CSA_MAX_TOPK];           // the fallback's index list
   const int qi = blockIdx.x, tid = threadIdx.x, bd = blockDim.x;
   const int N = (a.pos0 + qi + 1) / a.r, k = a.k;
   int32_t *out = a.topk + static_cast<int64_t>(qi) * k;
@@ -1309,25 +1383,24 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
     for (int t = tid; t < n_tiles; t += bd)
       for (int i = toff[t]; i < toff[t + 1]; ++i) tile_of[i] = static_cast<uint16_t>(t);
     __syncthreads();
+    // thread tid holds candidates [tid s, tid s + s), s = ceil(c / 512), in registers
     constexpr int kPer = kChunkCandCap / 512;
+    const int span = (c + 511) / 512, i0 = tid * span;
     uint64_t tk[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * 512 + tid;
+    for (int u = 0; u < kPer; ++u) {   // every load first, then the keys
+      const int i = i0 + u;
       tk[u] = 0;
-      if (i < c) {
+      if (u < span && i < c) {
         const int lo = tile_of[i];
-        const uint64_t se = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];   // entry << 32 | score bits
-        tk[u] = score_key(__uint_as_float(static_cast<uint32_t>(se)), static_cast<int>(se >> 32));
+        tk[u] = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];   // entry << 32 | score bits
       }
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = u * 512 + tid;
-      if (i < c) keys[i] = tk[u];
-    }
-    __syncthreads();
-    done = select_ordered(keys, c, k, hist, red, sh, bin_keys, out);
+    for (int u = 0; u < kPer; ++u)
+      tk[u] = score_key(__uint_as_float(static_cast<uint32_t>(tk[u])), static_cast<int>(tk[u] >> 32));
+    // (the select's first barrier comes after every read of tile_of, which it then reuses)
+    done = select_ordered_regs(tk, c, k, hist, red, sh, bin_keys, out);
     __syncthreads();
   }
   if (!done) {
