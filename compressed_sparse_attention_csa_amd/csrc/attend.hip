@@ -626,20 +626,16 @@ __global__ __launch_bounds__(HG * KH * 64) void attend_kernel(const AttendArgs a
 
 // ------------------------------------------------------------------ decode and dense queries
 //
-// One workgroup per (query, split); a split is a run of KS x rounds 64-key
-// blocks. The workgroup's KS key streams each take one block per round
-// (stream s of round r: block first + r KS + s) and stage it in their own LDS
-// region; the HG waves of a stream are its head groups, as in the chunk kernel
-// above, so one gathered block serves all 16 HG NTW heads. Decode queries use
-// one stream and one round (one 64-key block per workgroup: the gathers of a
-// query's blocks run side by side on as many CUs, which is what bounds this
-// latency-bound step); dense queries with many blocks use four streams.
-// After the last round the streams' softmax states (m, l, O) are combined
-// through LDS, where O is also transposed so that every lane owns 8
-// contiguous dims of one head: the output (one split) or the split's partial
-// state goes out as 16-byte stores (a one-stream workgroup stores straight
-// from its accumulators), and attend_merge_kernel combines the partials of a
-// query's splits.
+// One workgroup per (query, split); a split is a run of 64-key blocks taken
+// one per round, the next block's gather in flight in registers during this
+// block's math. The HG waves are head groups, as in the chunk kernel above, so
+// one gathered block serves all 16 HG NTW heads. A decode query's workgroups
+// take one block each (the gathers of a query's blocks run side by side on as
+// many CUs, which is what bounds this latency-bound step; a wide batch takes
+// two); a dense query's take a few rounds each, so that the merge combines at
+// most kAttDenseSplits partials. The split's softmax state (m, l, O) goes out
+// straight from the MFMA accumulators: the output when the query has one
+// split, else the partial state that attend_merge_kernel combines.
 
 template <int SD> __device__ __forceinline__ constexpr int cpr_of() { return row_bytes_of<SD>() / 16; }
 
@@ -683,40 +679,35 @@ __device__ __forceinline__ void pack_bf16(const uint4 &u, uint32_t gsc, uint4 *d
 
 // LDS holds at most two one-stream workgroups per CU (two waves per SIMD), so
 // the compiler may give each wave up to 256 registers instead of spilling.
-template <int KV, int RS, int HG, int NTW, int KS>
-__global__ __launch_bounds__(HG * KS * 64) __attribute__((amdgpu_waves_per_eu(1, KS == 1 ? 2 : 4)))
+template <int KV, int RS, int HG, int NTW>
+__global__ __launch_bounds__(HG * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void attend_decode_kernel(const AttendArgs a) {
   using CT = __bf16;
   static_assert(KV != DT_F32, "bf16 compute path");
-  constexpr int NTS = HG * 64;                 // threads of one key stream
-  constexpr int NT = NTS * KS;
+  constexpr int NT = HG * 64;
   constexpr int H = HG * NTW * 16;
   constexpr bool VSCALE = KV == DT_FP8 || RS == DT_FP8;
   constexpr int64_t PRB = row_bytes_of<KV>(), RRB = row_bytes_of<RS>();
   constexpr int KSTR = kD + 8;                 // K row stride (bf16 elements)
   constexpr int VSTR = kD + 16;                // V row stride: conflict-free transposed reads
-  constexpr int STREAM_LDS = kKeyBlock * (KSTR + VSTR) * 2;
-  constexpr int MSTR = kD + 4;                 // rows of the combined state (floats)
-  constexpr int MERGE_LDS = KS * H * MSTR * 4;
-  constexpr int KV_LDS = KS * STREAM_LDS > MERGE_LDS ? KS * STREAM_LDS : MERGE_LDS;
+  constexpr int KV_LDS = kKeyBlock * (KSTR + VSTR) * 2;
   // 16-byte slots per thread per block of pool (P) and ring (R) rows; a block
   // is held in registers between rounds (prefetched) when its slots fit UW
-  constexpr int U_P = 2 * kKeyBlock * cpr_of<KV>() / NTS, U_R = 2 * kKeyBlock * cpr_of<RS>() / NTS;
-  constexpr int UCAP = NT >= 1024 ? 4 : 8;
+  constexpr int U_P = 2 * kKeyBlock * cpr_of<KV>() / NT, U_R = 2 * kKeyBlock * cpr_of<RS>() / NT;
+  constexpr int UCAP = 8;
   constexpr int UW = (U_P > U_R ? U_P : U_R) < UCAP ? (U_P > U_R ? U_P : U_R) : UCAP;
   constexpr bool PRE_P = U_P <= UW, PRE_R = U_R <= UW;
 
   __shared__ __align__(16) char kv_lds[KV_LDS];
   __shared__ __align__(16) uint32_t off_t[kAttSplitMaxKeys];   // byte offset of every key (kOobOffset: none)
-  __shared__ __align__(16) float kmul[KS][VSCALE ? kKeyBlock : 1];
-  __shared__ __align__(16) float kbias[KS][VSCALE ? kKeyBlock : 1];
-  __shared__ __align__(16) float vscl[KS][VSCALE ? kKeyBlock : 1];
-  __shared__ uint64_t kmask[KS];
-  __shared__ float ml[KS][2][H];
+  __shared__ __align__(16) float kmul[VSCALE ? kKeyBlock : 1];
+  __shared__ __align__(16) float kbias[VSCALE ? kKeyBlock : 1];
+  __shared__ __align__(16) float vscl[VSCALE ? kKeyBlock : 1];
+  __shared__ uint64_t kmask;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ks = wave / HG, hg = wave % HG, ts = tid % NTS;   // stream, head group (wave-uniform), thread in stream
+  const int hg = wave;                         // head group (wave-uniform)
   const int g = lane >> 4, col = lane & 15;
   const int qi = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
   const int seq = a.qd[qi].seq, t = a.qd[qi].pos;
@@ -763,7 +754,7 @@ void attend_decode_kernel(const AttendArgs a) {
 
   const __amdgpu_buffer_rsrc_t pool_k = buffer_of(a.kbar, a.pool_bytes), pool_v = buffer_of(a.vbar, a.pool_bytes);
   const __amdgpu_buffer_rsrc_t ring_k = buffer_of(a.ring_k, a.ring_bytes), ring_v = buffer_of(a.ring_v, a.ring_bytes);
-  CT *Ks = reinterpret_cast<CT *>(kv_lds + ks * STREAM_LDS);
+  CT *Ks = reinterpret_cast<CT *>(kv_lds);
   CT *Vs = Ks + kKeyBlock * KSTR;
 
   // a block's 16-byte slots in registers, one array per row kind (pool rows
@@ -774,7 +765,7 @@ void attend_decode_kernel(const AttendArgs a) {
   uint32_t graw[KV == DT_FP4 ? WP : 1];
   float ks_pref = 1.f, vs_pref = 1.f;
   // slots [u0, u0 + W) of this stream's block b (pool rows when POOL): slot u of
-  // thread ts is chunk ts % CPR of key ((u NTS + ts) mod 64 CPR) / CPR, of K for
+  // thread tid is chunk tid % CPR of key ((u NT + tid) mod 64 CPR) / CPR, of K for
   // the first 64 CPR slots and of V for the next
   auto gather = [&](auto pool_tag, int b, int u0) {
     constexpr bool POOL = decltype(pool_tag)::value;
@@ -784,13 +775,13 @@ void attend_decode_kernel(const AttendArgs a) {
     uint4 *raw = POOL ? rawp : rawr;
     const __amdgpu_buffer_rsrc_t rk = POOL ? pool_k : ring_k, rv = POOL ? pool_v : ring_v;
     const uint32_t *offs = off_t + (b - b_begin) * kKeyBlock;
-    const uint32_t chunk_off = static_cast<uint32_t>(ts & (CPR - 1)) * 16u;
+    const uint32_t chunk_off = static_cast<uint32_t>(tid & (CPR - 1)) * 16u;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const int u = u0 + w;
-      if (u * NTS >= 2 * kKeyBlock * CPR) break;
-      const bool is_v = u * NTS >= kKeyBlock * CPR;
-      const uint32_t row_off = offs[((u * NTS) % (kKeyBlock * CPR) + ts) / CPR];
+      if (u * NT >= 2 * kKeyBlock * CPR) break;
+      const bool is_v = u * NT >= kKeyBlock * CPR;
+      const uint32_t row_off = offs[((u * NT) % (kKeyBlock * CPR) + tid) / CPR];
       raw[w] = buffer_load16(is_v ? rv : rk, row_off + chunk_off);
       if constexpr (KV == DT_FP4 && POOL) {
         const uint8_t *gbase = is_v ? a.vbar_gs : a.kbar_gs;
@@ -801,8 +792,8 @@ void attend_decode_kernel(const AttendArgs a) {
   };
   auto load_scales = [&](int b) {
     ks_pref = vs_pref = 1.f;
-    if (ts < kKeyBlock) {
-      const uint32_t off = off_t[(b - b_begin) * kKeyBlock + ts];
+    if (tid < kKeyBlock) {
+      const uint32_t off = off_t[(b - b_begin) * kKeyBlock + tid];
       if constexpr (KV == DT_FP8) {
         if (b < a.n_sparse_blocks && off != kOobOffset) {
           const uint32_t page = off / static_cast<uint32_t>(PRB * kPage);
@@ -829,9 +820,9 @@ void attend_decode_kernel(const AttendArgs a) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const int u = u0 + w;
-      if (u * NTS >= 2 * kKeyBlock * CPR) break;
-      const bool is_v = u * NTS >= kKeyBlock * CPR;
-      const int key = ((u * NTS) % (kKeyBlock * CPR) + ts) / CPR, d0 = (ts & (CPR - 1)) * E;
+      if (u * NT >= 2 * kKeyBlock * CPR) break;
+      const bool is_v = u * NT >= kKeyBlock * CPR;
+      const int key = ((u * NT) % (kKeyBlock * CPR) + tid) / CPR, d0 = (tid & (CPR - 1)) * E;
       uint4 packed[E / 8];
       pack_bf16<SD>(raw[w], KV == DT_FP4 && POOL ? graw[KV == DT_FP4 ? w : 0] : 0u, packed);
       uint4 *dst = reinterpret_cast<uint4 *>(is_v ? Vs + key * VSTR + d0 : Ks + key * KSTR + d0);
@@ -842,7 +833,7 @@ void attend_decode_kernel(const AttendArgs a) {
   using PoolTag = std::integral_constant<bool, true>;
   using RingTag = std::integral_constant<bool, false>;
   auto load_round = [&](int r) {
-    const int b = b_begin + r * KS + ks;
+    const int b = b_begin + r;
     if (b >= b_end) return;
     if (b < a.n_sparse_blocks) {
       if constexpr (PRE_P) gather(PoolTag{}, b, 0);
@@ -863,7 +854,7 @@ void attend_decode_kernel(const AttendArgs a) {
     }
   };
   auto commit_round = [&](int r) {
-    const int b = b_begin + r * KS + ks;
+    const int b = b_begin + r;
     if (b >= b_end) return;
     if (b < a.n_sparse_blocks) {
       if constexpr (PRE_P) commit(PoolTag{}, 0);
@@ -872,15 +863,15 @@ void attend_decode_kernel(const AttendArgs a) {
       if constexpr (PRE_R) commit(RingTag{}, 0);
       else slices(RingTag{}, b);
     }
-    if (ts < kKeyBlock) {   // the stream's first wave
-      const bool valid = off_t[(b - b_begin) * kKeyBlock + ts] != kOobOffset;
+    if (tid < kKeyBlock) {   // the first wave
+      const bool valid = off_t[(b - b_begin) * kKeyBlock + tid] != kOobOffset;
       if constexpr (VSCALE) {
-        kmul[ks][ts] = valid ? a.scale * kLog2e * ks_pref : 0.f;
-        kbias[ks][ts] = valid ? 0.f : -INFINITY;
-        vscl[ks][ts] = vs_pref;
+        kmul[tid] = valid ? a.scale * kLog2e * ks_pref : 0.f;
+        kbias[tid] = valid ? 0.f : -INFINITY;
+        vscl[tid] = vs_pref;
       } else {
         const uint64_t m = __builtin_amdgcn_ballot_w64(valid);
-        if (ts == 0) kmask[ks] = m;
+        if (tid == 0) kmask = m;
       }
     }
   };
@@ -895,14 +886,13 @@ void attend_decode_kernel(const AttendArgs a) {
     l_run[j] = 0.f;
   }
 
-  const int n_rounds = (b_end - b_begin + KS - 1) / KS;
+  const int n_rounds = b_end - b_begin;
   load_round(0);
   for (int r = 0; r < n_rounds; ++r) {
     if (r > 0) __syncthreads();          // previous round's LDS reads are done
     commit_round(r);
     __syncthreads();
     if (r + 1 < n_rounds) load_round(r + 1);
-    if (b_begin + r * KS + ks >= b_end) continue;   // this stream has no block this round
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       // S^T tiles: keys as MFMA rows, the wave's 16 heads as columns
@@ -921,13 +911,13 @@ void attend_decode_kernel(const AttendArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         if constexpr (VSCALE) {
-          const float4 km = *reinterpret_cast<const float4 *>(&kmul[ks][16 * kt + 4 * g]);
-          const float4 kb = *reinterpret_cast<const float4 *>(&kbias[ks][16 * kt + 4 * g]);
+          const float4 km = *reinterpret_cast<const float4 *>(&kmul[16 * kt + 4 * g]);
+          const float4 kb = *reinterpret_cast<const float4 *>(&kbias[16 * kt + 4 * g]);
           S[kt][0] = fmaf(S[kt][0], km.x, kb.x); S[kt][1] = fmaf(S[kt][1], km.y, kb.y);
           S[kt][2] = fmaf(S[kt][2], km.z, kb.z); S[kt][3] = fmaf(S[kt][3], km.w, kb.w);
         } else {
           const float c = a.scale * kLog2e;
-          const uint32_t nib = static_cast<uint32_t>(kmask[ks] >> (16 * kt + 4 * g)) & 0xfu;
+          const uint32_t nib = static_cast<uint32_t>(kmask >> (16 * kt + 4 * g)) & 0xfu;
 #pragma unroll
           for (int v = 0; v < 4; ++v) S[kt][v] = (nib >> v) & 1u ? S[kt][v] * c : -INFINITY;
         }
@@ -969,8 +959,8 @@ void attend_decode_kernel(const AttendArgs a) {
           pv[4 + v] = S[2 * kc + 1][v];
         }
         if constexpr (VSCALE) {
-          const float4 s0 = *reinterpret_cast<const float4 *>(&vscl[ks][32 * kc + 4 * g]);
-          const float4 s1 = *reinterpret_cast<const float4 *>(&vscl[ks][32 * kc + 16 + 4 * g]);
+          const float4 s0 = *reinterpret_cast<const float4 *>(&vscl[32 * kc + 4 * g]);
+          const float4 s1 = *reinterpret_cast<const float4 *>(&vscl[32 * kc + 16 + 4 * g]);
           pv[0] *= s0.x; pv[1] *= s0.y; pv[2] *= s0.z; pv[3] *= s0.w;
           pv[4] *= s1.x; pv[5] *= s1.y; pv[6] *= s1.z; pv[7] *= s1.w;
         }
@@ -988,100 +978,31 @@ void attend_decode_kernel(const AttendArgs a) {
     }
   }
 
-  if constexpr (KS == 1) {
-    // one stream: its state goes out straight from the MFMA accumulators
-    // (lane (g, col) holds dims 16 n + col of heads 4 g + v)
-    const int64_t pb = static_cast<int64_t>(qi) * a.n_splits + split;
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const float l_tot = sum_xor32(sum_xor16(l_run[j]));
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int h = 16 * (hg + HG * j) + 4 * g + v;
-        if (a.n_splits == 1) {
-          const float lv = __shfl(l_tot, 4 * g + v, 64);
-          const float inv = lv > 0.f ? 1.f / lv : 0.f;
-          uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + (static_cast<int64_t>(qi) * H + h) * kD;
-#pragma unroll
-          for (int n = 0; n < 8; ++n) dst[16 * n + col] = f32_to_bf16(O[j][n][v] * inv);
-        } else {
-          float *dst = a.part_o + (pb * H + h) * kD;
-#pragma unroll
-          for (int n = 0; n < 8; ++n) dst[16 * n + col] = O[j][n][v];
-        }
-      }
-      if (a.n_splits > 1 && g == 0) {
-        const int h = 16 * (hg + HG * j) + col;
-        a.part_ml[(pb * 2 + 0) * H + h] = m_run[j];
-        a.part_ml[(pb * 2 + 1) * H + h] = l_tot;
-      }
-    }
-    return;
-  }
-
-  // ---------------- combine the streams' (m, l, O) through LDS; lane (head
-  // lane / 4, dims DS ks + DPL (lane % 4) ...) of wave (ks, hg) then owns DPL
-  // contiguous dims of one head (DS = 128 / KS dims per stream)
-  constexpr int DS = kD / KS;
-  constexpr int DPL = DS / 4;
-  __syncthreads();                       // every stream's math is done: reuse kv_lds
-  float *Ost = reinterpret_cast<float *>(kv_lds);    // [KS][H][MSTR]
+  // the state goes out straight from the MFMA accumulators
+  // (lane (g, col) holds dims 16 n + col of heads 4 g + v)
+  const int64_t pb = static_cast<int64_t>(qi) * a.n_splits + split;
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    const int h0 = 16 * (hg + HG * j);
     const float l_tot = sum_xor32(sum_xor16(l_run[j]));
-    if (g == 0) {
-      ml[ks][0][h0 + col] = m_run[j];
-      ml[ks][1][h0 + col] = l_tot;
-    }
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * (hg + HG * j) + 4 * g + v;
+      if (a.n_splits == 1) {
+        const float lv = __shfl(l_tot, 4 * g + v, 64);
+        const float inv = lv > 0.f ? 1.f / lv : 0.f;
+        uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + (static_cast<int64_t>(qi) * H + h) * kD;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) Ost[(ks * H + h0 + 4 * g + v) * MSTR + 16 * n + col] = O[j][n][v];
-  }
-  __syncthreads();
-  const int64_t pbase = static_cast<int64_t>(qi) * a.n_splits + split;
+        for (int n = 0; n < 8; ++n) dst[16 * n + col] = f32_to_bf16(O[j][n][v] * inv);
+      } else {
+        float *dst = a.part_o + (pb * H + h) * kD;
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int h = 16 * (hg + HG * j) + (lane >> 2);
-    const int d0 = DS * ks + DPL * (lane & 3);
-    float ms[KS], M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) { ms[s] = ml[s][0][h]; M = fmaxf(M, ms[s]); }
-    float L = 0.f, acc[DPL];
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[d] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const float e = KS == 1 ? 1.f : (ms[s] == -INFINITY ? 0.f : fast_exp2(ms[s] - M));
-      L += e * ml[s][1][h];
-      const float *src = Ost + (s * H + h) * MSTR + d0;
-#pragma unroll
-      for (int d = 0; d < DPL; d += 4) {
-        const float4 o = *reinterpret_cast<const float4 *>(src + d);
-        acc[d] += e * o.x; acc[d + 1] += e * o.y; acc[d + 2] += e * o.z; acc[d + 3] += e * o.w;
+        for (int n = 0; n < 8; ++n) dst[16 * n + col] = O[j][n][v];
       }
     }
-    if (a.n_splits == 1) {
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + (static_cast<int64_t>(qi) * H + h) * kD + d0;
-#pragma unroll
-      for (int d = 0; d < DPL; d += 8) {
-        uint4 w;
-        w.x = f32x2_to_bf16x2(acc[d] * inv, acc[d + 1] * inv);
-        w.y = f32x2_to_bf16x2(acc[d + 2] * inv, acc[d + 3] * inv);
-        w.z = f32x2_to_bf16x2(acc[d + 4] * inv, acc[d + 5] * inv);
-        w.w = f32x2_to_bf16x2(acc[d + 6] * inv, acc[d + 7] * inv);
-        *reinterpret_cast<uint4 *>(dst + d) = w;
-      }
-    } else {
-      float *dst = a.part_o + (pbase * H + h) * kD + d0;
-#pragma unroll
-      for (int d = 0; d < DPL; d += 4) *reinterpret_cast<float4 *>(dst + d) = make_float4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
-      if (ks == 0 && (lane & 3) == 0) {
-        a.part_ml[(pbase * 2 + 0) * H + h] = M;
-        a.part_ml[(pbase * 2 + 1) * H + h] = L;
-      }
+    if (a.n_splits > 1 && g == 0) {
+      const int h = 16 * (hg + HG * j) + col;
+      a.part_ml[(pb * 2 + 0) * H + h] = m_run[j];
+      a.part_ml[(pb * 2 + 1) * H + h] = l_tot;
     }
   }
 }
@@ -1152,23 +1073,15 @@ void launch_attend_t(const AttendArgs &a, int n_wg, hipStream_t s, hipEvent_t e0
   }
 }
 
-template <int KV, int RS, int KS>
+template <int KV, int RS>
 void launch_attend_decode_t(const AttendArgs &a, int n_wg, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (a.H) {
-    case 16: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 1, 1, KS>), dim3(n_wg), dim3(64 * KS), 0, s, e0, e1, 0, a); break;
-    case 32: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 2, 1, KS>), dim3(n_wg), dim3(128 * KS), 0, s, e0, e1, 0, a); break;
-    case 64: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 4, 1, KS>), dim3(n_wg), dim3(256 * KS), 0, s, e0, e1, 0, a); break;
-    case 128:
-      if constexpr (KS == 1) hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 4, 2, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a);
-      break;
+    case 16: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 1, 1>), dim3(n_wg), dim3(64), 0, s, e0, e1, 0, a); break;
+    case 32: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 2, 1>), dim3(n_wg), dim3(128), 0, s, e0, e1, 0, a); break;
+    case 64: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 4, 1>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
+    case 128: hipExtLaunchKernelGGL((attend_decode_kernel<KV, RS, 4, 2>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a); break;
     default: break;
   }
-}
-
-template <int KV, int RS>
-void launch_attend_decode_ks(const AttendArgs &a, int n_wg, int ks, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (ks == 4) launch_attend_decode_t<KV, RS, 4>(a, n_wg, s, e0, e1);
-  else launch_attend_decode_t<KV, RS, 1>(a, n_wg, s, e0, e1);
 }
 
 // the merge's per-thread arrays hold MS splits: 40 covers decode batches
@@ -1186,15 +1099,15 @@ void launch_merge(const AttendArgs &a, hipStream_t s) {
 
 }  // namespace
 
-void launch_attend_decode(const AttendArgs &a, int n_wg, int kv, bool ring_fp8, int key_streams, hipStream_t s,
-                          hipEvent_t ev0, hipEvent_t ev1) {
+void launch_attend_decode(const AttendArgs &a, int n_wg, int kv, bool ring_fp8, hipStream_t s, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   if (n_wg <= 0) return;
-  if (kv == DT_BF16 && !ring_fp8) launch_attend_decode_ks<DT_BF16, DT_BF16>(a, n_wg, key_streams, s, ev0, ev1);
-  else if (kv == DT_BF16) launch_attend_decode_ks<DT_BF16, DT_FP8>(a, n_wg, key_streams, s, ev0, ev1);
-  else if (kv == DT_FP8 && !ring_fp8) launch_attend_decode_ks<DT_FP8, DT_BF16>(a, n_wg, key_streams, s, ev0, ev1);
-  else if (kv == DT_FP8) launch_attend_decode_ks<DT_FP8, DT_FP8>(a, n_wg, key_streams, s, ev0, ev1);
-  else if (kv == DT_FP4 && !ring_fp8) launch_attend_decode_ks<DT_FP4, DT_BF16>(a, n_wg, key_streams, s, ev0, ev1);
-  else if (kv == DT_FP4) launch_attend_decode_ks<DT_FP4, DT_FP8>(a, n_wg, key_streams, s, ev0, ev1);
+  if (kv == DT_BF16 && !ring_fp8) launch_attend_decode_t<DT_BF16, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_BF16) launch_attend_decode_t<DT_BF16, DT_FP8>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP8 && !ring_fp8) launch_attend_decode_t<DT_FP8, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP8) launch_attend_decode_t<DT_FP8, DT_FP8>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP4 && !ring_fp8) launch_attend_decode_t<DT_FP4, DT_BF16>(a, n_wg, s, ev0, ev1);
+  else if (kv == DT_FP4) launch_attend_decode_t<DT_FP4, DT_FP8>(a, n_wg, s, ev0, ev1);
   launch_merge(a, s);
 }
 

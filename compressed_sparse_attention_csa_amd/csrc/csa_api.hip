@@ -931,9 +931,9 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
     launch_attend(a, n_q, kv, act, ring8, stream, ev.start, ev.stop);
   } else if (kv != DT_F32) {
     // decode and dense queries: one 64-key block per workgroup for a decode
-    // query (its blocks' gathers run side by side on as many CUs); four blocks
-    // side by side and several rounds per workgroup for a dense query, whose
-    // many blocks would otherwise leave the merge with too many partials
+    // query (its blocks' gathers run side by side on as many CUs); several
+    // rounds of one block per workgroup for a dense query, whose many blocks
+    // would otherwise leave the merge with too many partials
     for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {
       const int nq = std::min(kAttMaxQ, n_q - g0);
       AttendArgs b = a;
@@ -948,16 +948,14 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
       }
       const int nb = std::max(1, b.n_blocks);
       const int ms = att_max_splits(nq);
-      const int ks = dense && c.q_heads <= 64 ? 4 : 1;
-      const int streams = (nb + ks - 1) / ks;
       // a large decode batch already fills the chip: two blocks per workgroup
       // halve the partials the merge reads
-      int rounds = dense ? (streams + kAttDenseSplits - 1) / kAttDenseSplits : (nq * nb > kAttWideBatch ? 2 : 1);
-      rounds = std::max(rounds, (streams + ms - 1) / ms);
-      rounds = std::min(rounds, kAttSplitMaxKeys / (kKeyBlock * ks));
-      const int splits = (streams + rounds - 1) / rounds;
+      int rounds = dense ? (nb + kAttDenseSplits - 1) / kAttDenseSplits : (nq * nb > kAttWideBatch ? 2 : 1);
+      rounds = std::max(rounds, (nb + ms - 1) / ms);
+      rounds = std::min(rounds, kAttSplitMaxKeys / kKeyBlock);
+      const int splits = (nb + rounds - 1) / rounds;
       if (splits > ms) return fail(CSA_ERR_UNSUPPORTED, "too many attention splits per query");
-      b.blocks_per_split = ks * rounds;
+      b.blocks_per_split = rounds;
       b.n_splits = splits;
       if (splits > 1) {
         const size_t need = attend_bytes(nq, splits, c.q_heads);
@@ -967,7 +965,7 @@ csa_status attend_impl(csa_cache_t h, int32_t layer, int32_t n_q, const int32_t 
         b.part_ml = reinterpret_cast<float *>(scratch_base + align_up(static_cast<size_t>(nq) * splits * c.q_heads * kD * 4, 256));
       }
       const ProfPair ev = profile ? prof_events(h, stream, CSA_PROFILE_ATTEND) : ProfPair{};
-      launch_attend_decode(b, nq * splits, kv, ring8, ks, stream, ev.start, ev.stop);
+      launch_attend_decode(b, nq * splits, kv, ring8, stream, ev.start, ev.stop);
     }
   } else {
     for (int g0 = 0; g0 < n_q; g0 += kAttMaxQ) {

@@ -27,16 +27,6 @@ enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_FP4 = 3 };
 
 constexpr int kFp4Group = 16;   // channels sharing one E4M3 scale in an fp4 entry
 
-// Workgroups of a launch are dealt to the 8 XCDs round-robin (workgroup b
-// runs on XCD b mod 8), and each XCD has its own L2. This maps workgroup b of
-// n to a logical index such that every XCD holds one contiguous run of logical
-// indices, so neighbouring tiles that read the same rows share an L2.
-__device__ __forceinline__ int xcd_contiguous(int b, int n) {
-  constexpr int kXcds = 8;
-  const int x = b % kXcds, i = b / kXcds, q = n / kXcds, r = n % kXcds;
-  return x * q + (x < r ? x : r) + i;
-}
-
 // error-word bits (see csa_read_errors)
 enum : uint32_t { ERR_PAGE = 1u, ERR_TOPK = 2u, ERR_FALLBACK = 4u };
 

@@ -215,14 +215,14 @@ struct AttendArgs {
 };
 
 constexpr int kAttSplitMaxKeys = 2048;   // keys one decode-kernel workgroup resolves up front (32 blocks)
-constexpr int kAttDenseSplits = 40;      // splits per dense query the merge kernel takes in registers
+constexpr int kAttDenseSplits = 64;      // splits per dense query at most: a workgroup takes ceil(blocks / 64) rounds
 constexpr int kAttWideBatch = 512;       // decode (query, block) pairs above which a workgroup takes two blocks
 
 // Decode and dense attention with bf16 compute (kv: bf16, fp8 or fp4): one
-// workgroup per (query, split), key_streams (1 or 4) 64-key blocks side by
-// side per round, a.blocks_per_split blocks per split; with several splits the
-// merge kernel follows. n_wg = n_q x n_splits.
-void launch_attend_decode(const AttendArgs &a, int n_wg, int kv, bool ring_fp8, int key_streams, hipStream_t s,
+// workgroup per (query, split), one 64-key block per round, a.blocks_per_split
+// blocks per split; with several splits the merge kernel follows.
+// n_wg = n_q x n_splits.
+void launch_attend_decode(const AttendArgs &a, int n_wg, int kv, bool ring_fp8, hipStream_t s,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // ev0/ev1 (may be null): events stamped with the start and end of the attention kernel launch.
