@@ -1084,11 +1084,67 @@ void launch_attend_decode_t(const AttendArgs &a, int n_wg, hipStream_t s, hipEve
   }
 }
 
-// the merge's per-thread arrays hold MS splits: 40 covers decode batches
+// The same combination for queries with at most MS splits, 8 (query, head)
+// pairs per workgroup: 32 threads per pair, each owning 4 contiguous output
+// dims (16-byte partial loads, all issued before the first use). Eight times
+// fewer workgroups than one per pair: at these sizes the launch of the many
+// small workgroups, not the loads, set the merge's time.
+template <int ACT, int MS>
+__global__ __launch_bounds__(256) void attend_merge_wide_kernel(const AttendArgs a) {
+  const int tid = threadIdx.x;
+  const int pair = blockIdx.x * 8 + (tid >> 5);
+  if (pair >= a.n_q * a.H) return;   // no barriers below
+  const int qi = pair / a.H, h = pair - qi * a.H, d0 = 4 * (tid & 31);
+  const int n = a.n_splits;
+  const int64_t q0 = static_cast<int64_t>(qi) * n;
+  float m[MS], l[MS];
+  float4 o[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const bool ok = s < n;
+    m[s] = ok ? a.part_ml[((q0 + s) * 2 + 0) * a.H + h] : -INFINITY;
+    l[s] = ok ? a.part_ml[((q0 + s) * 2 + 1) * a.H + h] : 0.f;
+    o[s] = ok ? *reinterpret_cast<const float4 *>(a.part_o + ((q0 + s) * a.H + h) * kD + d0)
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < MS; ++s) mx = fmaxf(mx, m[s]);
+  float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const float e = (m[s] == -INFINITY) ? 0.f : fast_exp2(m[s] - mx);   // running maxima are in log2 units
+    L += e * l[s];
+    acc[0] += e * o[s].x; acc[1] += e * o[s].y; acc[2] += e * o[s].z; acc[3] += e * o[s].w;
+  }
+  float r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = L > 0.f ? acc[i] / L : 0.f;
+  const int64_t oi = (static_cast<int64_t>(qi) * a.H + h) * kD + d0;
+  if constexpr (ACT == DT_F32)
+    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + oi) = make_float4(r[0], r[1], r[2], r[3]);
+  else
+    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + oi) =
+        make_uint2(f32x2_to_bf16x2(r[0], r[1]), f32x2_to_bf16x2(r[2], r[3]));
+}
+
+
+// Merge kernels: with at least 1,024 (query, head) pairs and up to 24 splits,
+// 8 pairs per workgroup; otherwise one workgroup per pair (measured faster
+// when the pairs are few: 256 pairs of 18 splits), with (m, l) in registers
+// up to 40 splits and staged through LDS up to kAttMaxSplits.
 void launch_merge(const AttendArgs &a, hipStream_t s) {
   if (a.n_splits <= 1) return;
   const dim3 grid(a.n_q * a.H), block(kD);
-  if (a.n_splits > 40) {
+  const dim3 grid_w((a.n_q * a.H + 7) / 8), block_w(256);
+  const bool wide = a.n_q * a.H >= 1024;
+  if (wide && a.n_splits <= 8) {
+    if (a.act_f32) hipLaunchKernelGGL((attend_merge_wide_kernel<DT_F32, 8>), grid_w, block_w, 0, s, a);
+    else hipLaunchKernelGGL((attend_merge_wide_kernel<DT_BF16, 8>), grid_w, block_w, 0, s, a);
+  } else if (wide && a.n_splits <= 24) {
+    if (a.act_f32) hipLaunchKernelGGL((attend_merge_wide_kernel<DT_F32, 24>), grid_w, block_w, 0, s, a);
+    else hipLaunchKernelGGL((attend_merge_wide_kernel<DT_BF16, 24>), grid_w, block_w, 0, s, a);
+  } else if (a.n_splits > 40) {
     if (a.act_f32) hipLaunchKernelGGL((attend_merge_kernel<DT_F32, kAttMaxSplits>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((attend_merge_kernel<DT_BF16, kAttMaxSplits>), grid, block, 0, s, a);
   } else {

@@ -320,6 +320,13 @@ def test_attend_head_counts(kv, act, H):
     _attend_case(kv, act, lens=[4 * 700, 999], k=70, W=100, H=H)
 
 
+@pytest.mark.parametrize("kv,act,k", [("bf16", "bf16", 256), ("fp8", "bf16", 1024), ("f32", "f32", 256)])
+def test_attend_many_pairs_merge(kv, act, k):
+    """16 queries x 64 heads = 1,024 (query, head) pairs with 6 or 18 splits
+    each: the merge kernel that takes 8 pairs per workgroup."""
+    _attend_case(kv, act, lens=[4 * (1100 + 37 * i) + i % 4 for i in range(16)], k=k, W=128)
+
+
 @pytest.mark.parametrize("k,W", [(0, 128), (64, 0), (1, 1), (1024, 128), (33, 200)])
 def test_attend_branch_edges(k, W):
     _attend_case("bf16", "bf16", lens=[4 * 5000, 4 * 20 + 3, 17], k=k, W=W)
