@@ -70,12 +70,13 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   constexpr int SPW = kPage / PARTS, SPT = SPW / (kThreads / 64);   // slots per workgroup / thread
   __shared__ float kb_s[SPW][kD];
   __shared__ float p_s[kD][kDI];   // indexer projection, staged once
-  __shared__ float red[16];
+  __shared__ float red[48];
 
-  // ---- which (sequence, page) this workgroup owns
+  // ---- which (sequence, page) this workgroup owns: with as many page
+  // workgroups as items every item has one page, and the item is the workgroup
   const int wg = blockIdx.x / PARTS;
   const int slot0 = (blockIdx.x % PARTS) * SPW;   // this workgroup's first slot of the page
-  const int item = item_of(a.wg0, a.n_items, wg);
+  const int item = static_cast<int>(gridDim.x) / PARTS == a.n_items ? wg : item_of(a.wg0, a.n_items, wg);
   const CompressItem it = a.it[item];
   const int page = it.page0 + (wg - a.wg0[item]);
   const int seq = it.seq;
@@ -184,15 +185,17 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
       const int e = pstart + slot0 + eb + 4 * m;
       if (e >= e0 && e < e1) {
         const float *kr = &kb_s[eb + 4 * m][0];
-        float acc = 0.f;
+        // four partial sums (d mod 4) shorten the dependent chain
+        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+#pragma unroll 8
         for (int d = 0; d < kD; d += 4) {
           const float4 k4 = *reinterpret_cast<const float4 *>(kr + d);
-          acc += k4.x * p_s[d][c];
-          acc += k4.y * p_s[d + 1][c];
-          acc += k4.z * p_s[d + 2][c];
-          acc += k4.w * p_s[d + 3][c];
+          acc0 += k4.x * p_s[d][c];
+          acc1 += k4.y * p_s[d + 1][c];
+          acc2 += k4.z * p_s[d + 2][c];
+          acc3 += k4.w * p_s[d + 3][c];
         }
-        ki[m] = acc;
+        ki[m] = (acc0 + acc1) + (acc2 + acc3);
       }
     }
     if constexpr (KV == DT_FP8 || KV == DT_FP4) {   // fp8 indexer keys
@@ -283,9 +286,7 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
         ai = fmaxf(ai, fabsf(ki[m]));
       }
     }
-    ak = block_max(ak, red);
-    av = block_max(av, red + 4);
-    ai = block_max(ai, red + 8);
+    block_max3(ak, av, ai, red);
     const float sk = ak > 0.f ? ak / 448.0f : 1.0f;
     const float sv = av > 0.f ? av / 448.0f : 1.0f;
     const float si = ai > 0.f ? ai / 448.0f : 1.0f;

@@ -293,4 +293,23 @@ __device__ __forceinline__ float block_max(float v, float *scratch /* >= 16 floa
   return r;
 }
 
+// Block-wide maxima of three values at once (two barriers instead of six).
+__device__ __forceinline__ void block_max3(float &a, float &b, float &c, float *scratch /* >= 48 floats of LDS */) {
+  a = wave_max(a);
+  b = wave_max(b);
+  c = wave_max(c);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { scratch[w] = a; scratch[16 + w] = b; scratch[32 + w] = c; }
+  __syncthreads();
+  a = scratch[0];
+  b = scratch[16];
+  c = scratch[32];
+  for (int i = 1; i < nw; ++i) {
+    a = fmaxf(a, scratch[i]);
+    b = fmaxf(b, scratch[16 + i]);
+    c = fmaxf(c, scratch[32 + i]);
+  }
+}
+
 }  // namespace csa
