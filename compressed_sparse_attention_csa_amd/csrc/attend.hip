@@ -1132,25 +1132,36 @@ __global__ __launch_bounds__(256) void attend_merge_wide_kernel(const AttendArgs
 // Merge kernels: with at least 1,024 (query, head) pairs and up to 24 splits,
 // 8 pairs per workgroup; otherwise one workgroup per pair (measured faster
 // when the pairs are few: 256 pairs of 18 splits), with (m, l) in registers
-// up to 40 splits and staged through LDS up to kAttMaxSplits.
-void launch_merge(const AttendArgs &a, hipStream_t s) {
-  if (a.n_splits <= 1) return;
+// up to 40 splits and staged through LDS beyond. Each kernel is unrolled for
+// the smallest split count MS >= the query's: the guarded loads of unused
+// splits still cost issue slots (44 splits: 5.1 us at MS = 80, 4.3 at 48).
+template <int ACT>
+void launch_merge_t(const AttendArgs &a, hipStream_t s) {
+  const int n = a.n_splits;
   const dim3 grid(a.n_q * a.H), block(kD);
   const dim3 grid_w((a.n_q * a.H + 7) / 8), block_w(256);
-  const bool wide = a.n_q * a.H >= 1024;
-  if (wide && a.n_splits <= 8) {
-    if (a.act_f32) hipLaunchKernelGGL((attend_merge_wide_kernel<DT_F32, 8>), grid_w, block_w, 0, s, a);
-    else hipLaunchKernelGGL((attend_merge_wide_kernel<DT_BF16, 8>), grid_w, block_w, 0, s, a);
-  } else if (wide && a.n_splits <= 24) {
-    if (a.act_f32) hipLaunchKernelGGL((attend_merge_wide_kernel<DT_F32, 24>), grid_w, block_w, 0, s, a);
-    else hipLaunchKernelGGL((attend_merge_wide_kernel<DT_BF16, 24>), grid_w, block_w, 0, s, a);
-  } else if (a.n_splits > 40) {
-    if (a.act_f32) hipLaunchKernelGGL((attend_merge_kernel<DT_F32, kAttMaxSplits>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attend_merge_kernel<DT_BF16, kAttMaxSplits>), grid, block, 0, s, a);
+  if (a.n_q * a.H >= 1024 && n <= 24) {
+    if (n <= 8) hipLaunchKernelGGL((attend_merge_wide_kernel<ACT, 8>), grid_w, block_w, 0, s, a);
+    else hipLaunchKernelGGL((attend_merge_wide_kernel<ACT, 24>), grid_w, block_w, 0, s, a);
+  } else if (n <= 8) {
+    hipLaunchKernelGGL((attend_merge_kernel<ACT, 8>), grid, block, 0, s, a);
+  } else if (n <= 24) {
+    hipLaunchKernelGGL((attend_merge_kernel<ACT, 24>), grid, block, 0, s, a);
+  } else if (n <= 40) {
+    hipLaunchKernelGGL((attend_merge_kernel<ACT, 40>), grid, block, 0, s, a);
+  } else if (n <= 48) {
+    hipLaunchKernelGGL((attend_merge_kernel<ACT, 48>), grid, block, 0, s, a);
+  } else if (n <= 64) {
+    hipLaunchKernelGGL((attend_merge_kernel<ACT, 64>), grid, block, 0, s, a);
   } else {
-    if (a.act_f32) hipLaunchKernelGGL((attend_merge_kernel<DT_F32, 40>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attend_merge_kernel<DT_BF16, 40>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attend_merge_kernel<ACT, kAttMaxSplits>), grid, block, 0, s, a);
   }
+}
+
+void launch_merge(const AttendArgs &a, hipStream_t s) {
+  if (a.n_splits <= 1) return;
+  if (a.act_f32) launch_merge_t<DT_F32>(a, s);
+  else launch_merge_t<DT_BF16>(a, s);
 }
 
 }  // namespace
