@@ -157,6 +157,18 @@ size_t idx_decode_bytes(int nq, int64_t s_stride) {
          align_up(static_cast<size_t>(nq) * s_stride * 4, 256);
 }
 // sampled scores, tau, per-tile counts, per-tile candidate regions, fallback rows
+// Workgroups per query when every one of the nq queries has the same
+// non-zero count (first_of(i): query i's first workgroup, total: all of
+// them), else 0: the filter kernel then finds a workgroup's query by division.
+template <typename First>
+int uniform_count(First first_of, int nq, int total) {
+  if (nq <= 0 || total <= 0 || total % nq != 0) return 0;
+  const int per = total / nq;
+  for (int i = 0; i < nq; ++i)
+    if (first_of(i) != i * per) return 0;
+  return per;
+}
+
 size_t idx_chunk_bytes(int nq, int64_t ss_stride, int64_t fb_stride) {
   const int64_t tiles = (fb_stride + 255) / 256;
   return align_up(static_cast<size_t>(nq) * ss_stride * 4, 256) + align_up(static_cast<size_t>(nq) * 4, 256) +
@@ -747,6 +759,8 @@ csa_status index_per_query(csa_cache_t h, int32_t n_q, const int32_t *q_seq, con
     f.slice0[nq] = slices;
     pf.slice0[nq] = pslices;
     s.total_wg = wg;
+    f.uniform = uniform_count([&](int i) { return f.slice0[i]; }, nq, slices);
+    pf.uniform = uniform_count([&](int i) { return pf.slice0[i]; }, nq, pslices);
     const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
     launch_idx_scan(s, kv, act, stream, ev.start, ev.stop);
     launch_idx_filter(f, slices, stream);
@@ -853,6 +867,7 @@ csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, c
     }
     f.slice0[nq] = slices;
     s.total_wg = wg;
+    f.uniform = uniform_count([&](int i) { return f.slice0[i]; }, nq, slices);
     const ProfPair ev = prof_events(h, stream, CSA_PROFILE_INDEX);
     launch_idx_rescan(s, kv, act, stream, ev.start, ev.stop);
     launch_idx_filter(f, slices, stream);

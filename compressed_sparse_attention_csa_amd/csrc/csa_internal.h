@@ -105,6 +105,7 @@ struct IdxFilterArgs {
   int32_t slice0[kIdxMaxQ + 1];   // prefix of filter WGs
   int32_t n_vis[kIdxMaxQ];
   int32_t glog2[kIdxMaxQ];
+  int32_t uniform;                // filter WGs per query when every query has as many, else 0
 };
 
 struct IdxFinalArgs {

@@ -818,9 +818,16 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
   __shared__ int sh[4];
   __shared__ int wcnt[4];
   const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int qi = 0;
-  for (; qi < a.n_q - 1; ++qi)
-    if (wg < a.slice0[qi + 1]) break;
+  int qi = 0;   // owning query: the last one whose first workgroup is <= wg
+  if (a.uniform > 0) {
+    qi = __builtin_amdgcn_readfirstlane(wg / a.uniform);
+  } else {
+    int hi = a.n_q;
+    while (hi - qi > 1) {
+      const int mid = (qi + hi) >> 1;
+      if (a.slice0[mid] <= wg) qi = mid; else hi = mid;
+    }
+  }
   const int slice = wg - a.slice0[qi];
   const int N = a.n_vis[qi];
   const int glog2 = a.glog2[qi];
