@@ -929,37 +929,44 @@ __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, 
         for (int i = soff[t]; i < soff[t + 1]; ++i) slice_of[i] = static_cast<uint16_t>(t);
       __syncthreads();
     }
-    // thread tid holds candidates [tid s, tid s + s), s = ceil(c / 512), in registers
-    constexpr int kPer = (kSelCap + 511) / 512;
+    // thread tid holds candidates [tid s, tid s + s), s = ceil(c / 512), in
+    // registers; the code is unrolled for the smallest P >= s of 4, 8, 12
+    static_assert((kSelCap + 511) / 512 <= 12, "at most 12 candidates per thread");
     const int span = (c + 511) / 512, i0 = tid * span;
-    float ts[kPer];
-    int tj[kPer];
+    auto gather_select = [&](auto per_tag) {
+      constexpr int P = decltype(per_tag)::value;
+      float ts[P];
+      int tj[P];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {   // every load first, then the keys
-      const int i = i0 + u;
-      ts[u] = 0.f;
-      tj[u] = 0;
-      if (u < span && i < c) {
-        int lo = 0;                     // slice s with soff[s] <= i < soff[s+1]
-        if (mapped) {
-          lo = slice_of[i];
-        } else {
-          int hi = ns;
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (soff[mid] <= i) lo = mid; else hi = mid;
+      for (int u = 0; u < P; ++u) {   // every load first, then the keys
+        const int i = i0 + u;
+        ts[u] = 0.f;
+        tj[u] = 0;
+        if (u < span && i < c) {
+          int lo = 0;                     // slice s with soff[s] <= i < soff[s+1]
+          if (mapped) {
+            lo = slice_of[i];
+          } else {
+            int hi = ns;
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (soff[mid] <= i) lo = mid; else hi = mid;
+            }
           }
+          const int64_t o = qbase + static_cast<int64_t>(lo) * kFilterSlice + (i - soff[lo]);
+          ts[u] = a.cand_s[o];
+          tj[u] = a.cand_j[o];
         }
-        const int64_t o = qbase + static_cast<int64_t>(lo) * kFilterSlice + (i - soff[lo]);
-        ts[u] = a.cand_s[o];
-        tj[u] = a.cand_j[o];
       }
-    }
-    uint64_t tk[kPer];
+      uint64_t tk[P];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) tk[u] = score_key(ts[u], tj[u]);
-    // (the select's first barrier comes after every read of slice_of, which it then reuses)
-    done = select_ordered_regs(tk, c, k, hist, red, sh, bin_keys, out, map);
+      for (int u = 0; u < P; ++u) tk[u] = score_key(ts[u], tj[u]);
+      // (the select's first barrier comes after every read of slice_of, which it then reuses)
+      return select_ordered_regs(tk, c, k, hist, red, sh, bin_keys, out, map);
+    };
+    if (span <= 4) done = gather_select(std::integral_constant<int, 4>{});
+    else if (span <= 8) done = gather_select(std::integral_constant<int, 8>{});
+    else done = gather_select(std::integral_constant<int, 12>{});
   }
   if (!done) {
     // heavy ties or too many candidates: exact select straight from the scores
@@ -1390,24 +1397,29 @@ __global__ __launch_bounds__(512) void idx_chunk_select_kernel(const IdxChunkArg
     for (int t = tid; t < n_tiles; t += bd)
       for (int i = toff[t]; i < toff[t + 1]; ++i) tile_of[i] = static_cast<uint16_t>(t);
     __syncthreads();
-    // thread tid holds candidates [tid s, tid s + s), s = ceil(c / 512), in registers
-    constexpr int kPer = kChunkCandCap / 512;
+    // thread tid holds candidates [tid s, tid s + s), s = ceil(c / 512), in
+    // registers; the code is unrolled for the smallest P >= s of 4 and 8
+    static_assert(kChunkCandCap / 512 == 8, "at most 8 candidates per thread");
     const int span = (c + 511) / 512, i0 = tid * span;
-    uint64_t tk[kPer];
+    auto gather_select = [&](auto per_tag) {
+      constexpr int P = decltype(per_tag)::value;
+      uint64_t tk[P];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {   // every load first, then the keys
-      const int i = i0 + u;
-      tk[u] = 0;
-      if (u < span && i < c) {
-        const int lo = tile_of[i];
-        tk[u] = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];   // entry << 32 | score bits
+      for (int u = 0; u < P; ++u) {   // every load first, then the keys
+        const int i = i0 + u;
+        tk[u] = 0;
+        if (u < span && i < c) {
+          const int lo = tile_of[i];
+          tk[u] = cq[static_cast<int64_t>(lo) * kWgCand + (i - toff[lo])];   // entry << 32 | score bits
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      tk[u] = score_key(__uint_as_float(static_cast<uint32_t>(tk[u])), static_cast<int>(tk[u] >> 32));
-    // (the select's first barrier comes after every read of tile_of, which it then reuses)
-    done = select_ordered_regs(tk, c, k, hist, red, sh, bin_keys, out);
+      for (int u = 0; u < P; ++u)
+        tk[u] = score_key(__uint_as_float(static_cast<uint32_t>(tk[u])), static_cast<int>(tk[u] >> 32));
+      // (the select's first barrier comes after every read of tile_of, which it then reuses)
+      return select_ordered_regs(tk, c, k, hist, red, sh, bin_keys, out);
+    };
+    done = span <= 4 ? gather_select(std::integral_constant<int, 4>{}) : gather_select(std::integral_constant<int, 8>{});
     __syncthreads();
   }
   if (!done) {
