@@ -852,16 +852,22 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
     }
   }
   // the query's group maxima in registers, 16-byte loads issued with the
-  // score loads (one round trip); M rows are padded to 256 floats
-  constexpr int kGU = kMaxGroups / 1024;
-  float4 mv[kGU];
+  // score loads (one round trip; M rows are padded to 256 floats), U float4
+  // per thread: the smallest of 2, 4, 8 that holds the query's nG maxima
+  static_assert(kMaxGroups == 8 * 1024, "at most 8 float4 of group maxima per thread");
+  auto threshold = [&](auto u_tag) {
+    constexpr int U = decltype(u_tag)::value;
+    float4 mv[U];
 #pragma unroll
-  for (int u = 0; u < kGU; ++u) {
-    const int i4 = 256 * u + tid;
-    mv[u] = 4 * i4 < nG ? *reinterpret_cast<const float4 *>(Mrow + 4 * i4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float tau = 0.f;
-  if (nG > a.k) tau = tau_lower_bound_regs(mv, nG, a.k, hist, red, sh);
+    for (int u = 0; u < U; ++u) {
+      const int i4 = 256 * u + tid;
+      mv[u] = 4 * i4 < nG ? *reinterpret_cast<const float4 *>(Mrow + 4 * i4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return nG > a.k ? tau_lower_bound_regs(mv, nG, a.k, hist, red, sh) : 0.f;
+  };
+  const float tau = nG <= 2048 ? threshold(std::integral_constant<int, 2>{})
+                  : nG <= 4096 ? threshold(std::integral_constant<int, 4>{})
+                               : threshold(std::integral_constant<int, 8>{});
 
   // ordered compaction into this slice's own region
   int mine = 0;
