@@ -677,8 +677,8 @@ __device__ __forceinline__ void pack_bf16(const uint4 &u, uint32_t gsc, uint4 *d
   }
 }
 
-// LDS holds at most two one-stream workgroups per CU (two waves per SIMD), so
-// the compiler may give each wave up to 256 registers instead of spilling.
+// Two waves per SIMD at most (amdgpu_waves_per_eu), so the compiler may give
+// each wave up to 256 registers instead of spilling.
 template <int KV, int RS, int HG, int NTW>
 __global__ __launch_bounds__(HG * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void attend_decode_kernel(const AttendArgs a) {
@@ -764,7 +764,7 @@ void attend_decode_kernel(const AttendArgs a) {
   uint4 rawp[WP], rawr[WR];
   uint32_t graw[KV == DT_FP4 ? WP : 1];
   float ks_pref = 1.f, vs_pref = 1.f;
-  // slots [u0, u0 + W) of this stream's block b (pool rows when POOL): slot u of
+  // slots [u0, u0 + W) of block b (pool rows when POOL): slot u of
   // thread tid is chunk tid % CPR of key ((u NT + tid) mod 64 CPR) / CPR, of K for
   // the first 64 CPR slots and of V for the next
   auto gather = [&](auto pool_tag, int b, int u0) {
