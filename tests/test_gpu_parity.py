@@ -327,6 +327,12 @@ def test_attend_many_pairs_merge(kv, act, k):
     _attend_case(kv, act, lens=[4 * (1100 + 37 * i) + i % 4 for i in range(16)], k=k, W=128)
 
 
+def test_attend_merge_many_splits():
+    """A decode query with a 4,096-row window: 80 splits of 64 keys, the merge
+    that stages each split's (m, l) through LDS."""
+    _attend_case("bf16", "bf16", lens=[4 * 5000 + 1], k=1024, W=4096, H=16)
+
+
 @pytest.mark.parametrize("k,W", [(0, 128), (64, 0), (1, 1), (1024, 128), (33, 200)])
 def test_attend_branch_edges(k, W):
     _attend_case("bf16", "bf16", lens=[4 * 5000, 4 * 20 + 3, 17], k=k, W=W)
@@ -775,6 +781,12 @@ def test_hca_ratios_and_windows(r, W):
 def test_hca_many_splits():
     """4,096 entries (64 blocks) per query: the split-and-merge path."""
     _hca_case("bf16", "bf16", lens=[16 * 4096, 16 * 4000 + 5], r=16, W=128, H=16)
+
+
+def test_hca_three_rounds():
+    """8,192 entries (130 blocks with the window): 44 splits of three 64-key
+    rounds each, merged by the 48-split merge."""
+    _hca_case("fp8", "bf16", lens=[4 * 8192 + 3, 4 * 300], r=4, W=128, H=16)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
