@@ -62,23 +62,20 @@ __device__ __forceinline__ int item_of(const int32_t *wg0, int n_items, int wg) 
 constexpr int kThreads = 256;
 constexpr int kPageParts = 8;   // workgroups per fp32 / bf16 page
 
+// fp32 / bf16 pages: each page is split over kPageParts workgroups of SPW
+// slots; fp8 and fp4 pages need a page-wide amax and stay whole
+template <int KV> constexpr int page_parts() { return (KV == DT_F32 || KV == DT_BF16) ? kPageParts : 1; }
+
+// The workgroup's share of one (sequence, page): slots [slot0, slot0 + SPW) of
+// page `page` of item `it`.
 template <int ACT, int KV>
-__global__ __launch_bounds__(kThreads) void compress_pages_kernel(const CompressArgs a) {
-  // fp32 / bf16 pages: each page is split over kPageParts workgroups of SPW
-  // slots; fp8 and fp4 pages need a page-wide amax and stay whole
-  constexpr int PARTS = (KV == DT_F32 || KV == DT_BF16) ? kPageParts : 1;
+__device__ void compress_page(const CompressArgs &a, const CompressItem &it, int page, int slot0) {
+  constexpr int PARTS = page_parts<KV>();
   constexpr int SPW = kPage / PARTS, SPT = SPW / (kThreads / 64);   // slots per workgroup / thread
   __shared__ float kb_s[SPW][kD];
   __shared__ float p_s[kD][kDI];   // indexer projection, staged once
   __shared__ float red[48];
 
-  // ---- which (sequence, page) this workgroup owns: with as many page
-  // workgroups as items every item has one page, and the item is the workgroup
-  const int wg = blockIdx.x / PARTS;
-  const int slot0 = (blockIdx.x % PARTS) * SPW;   // this workgroup's first slot of the page
-  const int item = static_cast<int>(gridDim.x) / PARTS == a.n_items ? wg : item_of(a.wg0, a.n_items, wg);
-  const CompressItem it = a.it[item];
-  const int page = it.page0 + (wg - a.wg0[item]);
   const int seq = it.seq;
   const int r = a.r;
   const int new_len = it.old_len + it.n_new;
@@ -327,16 +324,25 @@ __global__ __launch_bounds__(kThreads) void compress_pages_kernel(const Compress
   }
 }
 
+template <int ACT, int KV>
+__global__ __launch_bounds__(kThreads) void compress_pages_kernel(const CompressArgs a) {
+  // which (sequence, page) this workgroup owns: with as many page workgroups
+  // as items every item has one page, and the item is the workgroup
+  constexpr int PARTS = page_parts<KV>();
+  const int wg = blockIdx.x / PARTS;
+  const int item = static_cast<int>(gridDim.x) / PARTS == a.n_items ? wg : item_of(a.wg0, a.n_items, wg);
+  const CompressItem it = a.it[item];
+  compress_page<ACT, KV>(a, it, it.page0 + (wg - a.wg0[item]), (blockIdx.x % PARTS) * (kPage / PARTS));
+}
+
 // Copies the newest raw rows into the window ring (as E4M3 codes with one
 // fp32 scale amax/448 per row when RING8) and the open r-block's gate, key
 // and value rows into block staging. Runs after the page kernel, which still
 // reads the previous staging contents for a block straddling two calls.
-template <int ACT, bool RING8>
-__global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
-  const int wg = blockIdx.x;
-  const int item = item_of(a.wg0, a.n_items, wg);
-  const CompressItem it = a.it[item];
-  const int chunk = wg - a.wg0[item];
+// Ring and block-staging rows of one item, chunk `chunk` of rows_per_wg rows
+// (RA: RingArgs or RingPtrs).
+template <int ACT, bool RING8, typename RA>
+__device__ void compress_ring_rows(const RA &a, const CompressItem &it, int chunk) {
   const int new_len = it.old_len + it.n_new;
   const int lo = max(it.old_len, new_len - a.R);
   const int glo = a.write_stage ? max(it.old_len, (new_len / a.r) * a.r) : new_len;
@@ -408,6 +414,28 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
   }
 }
 
+// One workgroup per item, each writing at most one page and one chunk of ring
+// rows (a single-token decode append): the page first, then the ring and
+// block-staging rows. The page reads the open block's staged rows before the
+// ring part overwrites block staging (the barrier between them), and the
+// items are distinct sequences, so workgroups touch disjoint staging. One
+// launch instead of the page and ring kernels.
+template <int ACT, int KV, bool RING8>
+__global__ __launch_bounds__(kThreads) void compress_step_kernel(const CompressArgs a, const RingPtrs rp) {
+  static_assert(page_parts<KV>() == 1, "whole pages only");
+  const CompressItem it = a.it[blockIdx.x];
+  if (it.n_pages > 0) compress_page<ACT, KV>(a, it, it.page0, 0);
+  __syncthreads();
+  compress_ring_rows<ACT, RING8>(rp, it, 0);
+}
+
+template <int ACT, bool RING8>
+__global__ __launch_bounds__(256) void compress_ring_kernel(const RingArgs a) {
+  const int wg = blockIdx.x;
+  const int item = item_of(a.wg0, a.n_items, wg);
+  compress_ring_rows<ACT, RING8>(a, a.it[item], wg - a.wg0[item]);
+}
+
 }  // namespace
 
 void launch_compress_pages(const CompressArgs &args, int n_wg, int kv, int act, hipStream_t s) {
@@ -423,6 +451,15 @@ void launch_compress_pages(const CompressArgs &args, int n_wg, int kv, int act, 
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP8>), dim3(n_wg), dim3(kThreads), 0, s, a);
   else if (kv == DT_FP4 && act == DT_BF16)
     hipLaunchKernelGGL((compress_pages_kernel<DT_BF16, DT_FP4>), dim3(n_wg), dim3(kThreads), 0, s, a);
+}
+
+void launch_compress_step(const CompressArgs &a, const RingPtrs &rp, int kv, int act, bool ring_fp8, hipStream_t s) {
+  if (a.n_items <= 0 || act != DT_BF16) return;
+  const dim3 grid(a.n_items), block(kThreads);
+  if (kv == DT_FP8 && ring_fp8) hipLaunchKernelGGL((compress_step_kernel<DT_BF16, DT_FP8, true>), grid, block, 0, s, a, rp);
+  else if (kv == DT_FP8) hipLaunchKernelGGL((compress_step_kernel<DT_BF16, DT_FP8, false>), grid, block, 0, s, a, rp);
+  else if (kv == DT_FP4 && ring_fp8) hipLaunchKernelGGL((compress_step_kernel<DT_BF16, DT_FP4, true>), grid, block, 0, s, a, rp);
+  else if (kv == DT_FP4) hipLaunchKernelGGL((compress_step_kernel<DT_BF16, DT_FP4, false>), grid, block, 0, s, a, rp);
 }
 
 void launch_compress_ring(const RingArgs &args, int n_wg, int act, bool ring_fp8, hipStream_t s) {

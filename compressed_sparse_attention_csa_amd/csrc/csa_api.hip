@@ -479,8 +479,34 @@ csa_status csa_compress(csa_cache_t h, int32_t layer, int32_t n_seqs, const int3
   ring.r = c.ratio; ring.R = c.ring_rows; ring.rows_per_wg = 64; ring.write_stage = 1;
   const bool ring8 = c.swa_dtype == CSA_FP8_E4M3;
 
+  const RingPtrs rp{raw_k, raw_v, gate, ring.ring_k, ring.ring_v, ring.ring_k_scale, ring.ring_v_scale,
+                    ring.block_stage, ring.r, ring.R, ring.rows_per_wg, ring.write_stage};
   for (size_t g0 = 0; g0 < items.size(); g0 += kCompressMaxItems) {
     const size_t g1 = std::min(items.size(), g0 + kCompressMaxItems);
+    // fp8 / fp4 pages, every item writing at most one page and one chunk of
+    // ring rows (a single-token append): one workgroup per item does both
+    bool one_step = (fp8 || kv == DT_FP4) && act == DT_BF16;
+    for (size_t i = g0; i < g1 && one_step; ++i) {
+      const CompressItem &it = items[i];
+      const int nb_old = it.old_len / c.ratio, nb_new = (it.old_len + it.n_new) / c.ratio;
+      if (nb_new > nb_old && nb_old / kPage != (nb_new - 1) / kPage) one_step = false;
+      const int new_len = it.old_len + it.n_new;
+      const int first = std::min(std::max(it.old_len, new_len - c.ring_rows), std::max(it.old_len, (new_len / c.ratio) * c.ratio));
+      if (new_len - first > ring.rows_per_wg) one_step = false;
+    }
+    if (one_step) {
+      CompressArgs F = base;
+      F.n_items = 0;
+      for (size_t i = g0; i < g1; ++i) {
+        CompressItem it = items[i];
+        const int nb_old = it.old_len / c.ratio, nb_new = (it.old_len + it.n_new) / c.ratio;
+        it.page0 = nb_old / kPage;
+        it.n_pages = nb_new > nb_old ? 1 : 0;
+        F.it[F.n_items++] = it;
+      }
+      launch_compress_step(F, rp, kv, act, ring8, stream);
+      continue;
+    }
     // page launches: A = first pages holding earlier entries (fp8 only), B = the rest
     CompressArgs A = base, B = base;
     A.n_items = B.n_items = 0;

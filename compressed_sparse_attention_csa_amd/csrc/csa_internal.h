@@ -46,8 +46,22 @@ struct RingArgs {
   int32_t wg0[kCompressMaxItems + 1];             // first workgroup of each item (set by the launcher)
 };
 
+// The fields of RingArgs that one item's ring rows need.
+struct RingPtrs {
+  const void *raw_k, *raw_v, *gate;
+  void *ring_k, *ring_v;
+  float *ring_k_scale, *ring_v_scale;
+  void *block_stage;
+  int32_t r, R, rows_per_wg, write_stage;
+};
+
 void launch_compress_pages(const CompressArgs &a, int n_wg, int kv, int act, hipStream_t s);
 void launch_compress_ring(const RingArgs &a, int n_wg, int act, bool ring_fp8, hipStream_t s);
+// One workgroup per item (a.n_items of them, fp8 or fp4 pages), for calls in
+// which every item writes at most one page and at most rp.rows_per_wg ring
+// rows: the item's page (it.n_pages = 0 or 1, at it.page0), then its ring and
+// block-staging rows, in one launch.
+void launch_compress_step(const CompressArgs &a, const RingPtrs &rp, int kv, int act, bool ring_fp8, hipStream_t s);
 
 // ------------------------------------------------------------------ index (decode)
 
