@@ -99,19 +99,6 @@ __device__ void compress_page(const CompressArgs &a, const CompressItem &it, int
     for (int u = 0; u < kD * kDI / 4 / kThreads; ++u) reinterpret_cast<float4 *>(&p_s[0][0])[u * kThreads + t] = tmp[u];
   }
 
-  // fp8 pages: the fp32 values of the page's earlier entries, from staging.
-  // Every slot of a sequence's staging page is valid memory, so the loads are
-  // issued for every slot up front (all in flight together) and selected below.
-  float2 stk[SPT], stv[SPT];
-  if constexpr (KV == DT_FP8) {
-#pragma unroll
-    for (int m = 0; m < SPT; ++m) {
-      const int64_t so = (static_cast<int64_t>(seq) * kPage + slot0 + eb + 4 * m) * kD + d0;
-      stk[m] = *reinterpret_cast<const float2 *>(a.kbar_stage + so);
-      stv[m] = *reinterpret_cast<const float2 *>(a.vbar_stage + so);
-    }
-  }
-
   // A row of entry e's block: from the packed input when this call appends it,
   // else from open-block staging (appended by an earlier call).
   auto row_src = [&](int row, int plane, const void *fresh) -> float2 {
@@ -147,15 +134,34 @@ __device__ void compress_page(const CompressArgs &a, const CompressItem &it, int
         v0 += w0 * vx.x; v1 += w1 * vx.y;
       }
       k0 /= ws0; k1 /= ws1; v0 /= ws0; v1 /= ws1;
-    } else if (KV == DT_FP8 && slot < filled && e < e0) {
-      // an entry appended by an earlier call
-      k0 = stk[m].x; k1 = stk[m].y; v0 = stv[m].x; v1 = stv[m].y;
     }
     kk[m][0] = k0; kk[m][1] = k1;
     vv[m][0] = v0; vv[m][1] = v1;
     if (a.write_idx) {
       kb_s[slot - slot0][d0] = k0;
       kb_s[slot - slot0][d0 + 1] = k1;
+    }
+  }
+
+  // fp8 pages: the fp32 values of the page's earlier entries, from staging,
+  // loaded after the new entries' rows (which the pooling above waited for).
+  // Every slot of a sequence's staging page is valid memory, so the loads are
+  // issued for every slot (all in flight together) and selected afterwards.
+  if constexpr (KV == DT_FP8) {
+    float2 stk[SPT], stv[SPT];
+#pragma unroll
+    for (int m = 0; m < SPT; ++m) {
+      const int64_t so = (static_cast<int64_t>(seq) * kPage + slot0 + eb + 4 * m) * kD + d0;
+      stk[m] = *reinterpret_cast<const float2 *>(a.kbar_stage + so);
+      stv[m] = *reinterpret_cast<const float2 *>(a.vbar_stage + so);
+    }
+#pragma unroll
+    for (int m = 0; m < SPT; ++m) {
+      const int slot = slot0 + eb + 4 * m, e = pstart + slot;
+      if (slot < filled && e < e0) {   // an entry appended by an earlier call
+        kk[m][0] = stk[m].x; kk[m][1] = stk[m].y;
+        vv[m][0] = stv[m].x; vv[m][1] = stv[m].y;
+      }
     }
   }
 
