@@ -883,7 +883,7 @@ csa_status csa_index_reindex(csa_cache_t h, int32_t n_q, const int32_t *q_seq, c
       s.q[i].chunk0 = wg;
       s.q[i].glog2 = glog2;
       s.n_ent[i] = nent[i];
-      wg += (V + kIdxChunk - 1) / kIdxChunk;
+      wg += (V + kRescanChunk - 1) / kRescanChunk;
       f.slice0[i] = slices;
       f.n_vis[i] = V;
       f.glog2[i] = glog2;

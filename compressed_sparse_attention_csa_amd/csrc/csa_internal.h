@@ -66,9 +66,10 @@ void launch_compress_step(const CompressArgs &a, const RingPtrs &rp, int kv, int
 // ------------------------------------------------------------------ index (decode)
 
 constexpr int kIdxMaxQ = 128;        // queries per decode launch group
-constexpr int kScanPagesPerWave = 1;                     // indexer-key pages per scan wave
+constexpr int kScanPagesPerWave = 2;                     // indexer-key pages per scan wave
 constexpr int kScanWaves = 4;                            // waves per scan workgroup
 constexpr int kIdxChunk = kScanWaves * kScanPagesPerWave * 64;   // entries per scan workgroup
+constexpr int kRescanChunk = kScanWaves * 64;                   // pool positions per Reindex scoring workgroup
 constexpr int kFilterSlice = 4096;   // scores per filter workgroup
 constexpr int kMaxGroups = 8192;     // group maxima per query (threshold select in LDS)
 constexpr int kMaxSlices = 512;      // filter slices per query (<= 2M visible entries)

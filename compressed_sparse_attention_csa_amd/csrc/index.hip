@@ -567,7 +567,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
   constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
 
   const int glog2 = Q.glog2, G = 1 << glog2;
-  const bool cross = G > PPW * kPage;   // a group spans several waves of the workgroup
+  // a group of more than one page: its maximum is gathered across the wave's
+  // pages (run) and, when it spans several waves, through LDS
+  static_assert(kScanPagesPerWave <= 2, "a group of G > 64 entries is whole waves");
+  const bool cross = G > kPage;
   float *Srow = a.S + static_cast<int64_t>(qi) * a.s_stride;
   float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
   const int wave_e0 = chunk * kIdxChunk + w * (PPW * kPage);
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
     }
   }
   if (cross) {
-    // groups of G entries = G / (PPW * 64) consecutive waves, all inside this workgroup
+    // groups of G entries = G / (PPW * 64) consecutive waves (at least one), all inside this workgroup
     __shared__ float wmax[kScanWaves];
     if (lane == 0) wmax[w] = run;
     __syncthreads();
@@ -1015,7 +1018,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
   const int V = Q.n_vis, n_ent = a.n_ent[qi];
   const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave_p0 = (wg - Q.chunk0) * kIdxChunk + w * 64;
+  const int wave_p0 = (wg - Q.chunk0) * kRescanChunk + w * 64;
   if (wave_p0 >= V) return;   // no barriers below
   constexpr int AE = elem_bytes<ACT>(), KE = elem_bytes<KV>();
   const int32_t *prow = a.pool + static_cast<int64_t>(qi) * a.pool_stride;

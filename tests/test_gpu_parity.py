@@ -220,6 +220,14 @@ def test_index_decode_large_k(kv, act, k):
     _index_case(kv, act, lens=[4 * 65536, 4 * 9000 + 2, 4 * 3 * k], k=k)
 
 
+@pytest.mark.parametrize("kv,act", [("bf16", "bf16"), ("fp8", "bf16")])
+@pytest.mark.parametrize("n,k", [(300000, 16), (50000, 64)])
+def test_index_decode_wide_groups(kv, act, n, k):
+    """Many entries and a small k: threshold groups of 256 entries (two scan
+    waves, combined through LDS) and of 128 entries (both pages of a wave)."""
+    _index_case(kv, act, lens=[4 * n + 3, 4 * (n // 4)], k=k)
+
+
 @pytest.mark.parametrize("h_i", [1, 2, 3])
 def test_index_fewer_heads(h_i):
     _index_case("bf16", "bf16", lens=[4 * 5000, 4 * 777], k=100, h_i=h_i)
