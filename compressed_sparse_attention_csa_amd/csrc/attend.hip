@@ -1008,41 +1008,35 @@ void attend_decode_kernel(const AttendArgs a) {
 }
 
 // Combines the split partials of (query, head): one softmax over the union of
-// every split's keys. Thread d owns output dimension d; all of its loads are
-// independent, so the merge costs about one memory round trip.
+// every split's keys. Thread d owns output dimension d. Threads s < MS load
+// split s's (m, l) with one vector load each and stage them through LDS; the
+// partial loads take a clamped split index instead of a guard, so every load
+// is issued unconditionally and the merge costs about one memory round trip
+// (a split past the query's count repeats the last one with weight 0).
 template <int ACT, int MS>
 __global__ __launch_bounds__(kD) void attend_merge_kernel(const AttendArgs a) {
   const int qi = blockIdx.x / a.H, h = blockIdx.x % a.H, d = threadIdx.x;
-  const int64_t q0 = static_cast<int64_t>(qi) * a.n_splits;
-  // (m, l) are the same for every thread: with many splits they are staged
-  // through LDS by one thread per split instead of filling scalar registers
-  constexpr bool STAGE = MS > 40;
+  const int n = a.n_splits;
+  const int64_t q0 = static_cast<int64_t>(qi) * n;
   static_assert(MS <= kD, "one thread per split stages (m, l)");
-  __shared__ float ms_st[STAGE ? MS : 1], ls_st[STAGE ? MS : 1];
-  float m[MS], l[MS], o[MS];
-  if constexpr (STAGE) {
-    if (d < MS) {
-      const bool ok = d < a.n_splits;
-      ms_st[d] = ok ? a.part_ml[((q0 + d) * 2 + 0) * a.H + h] : -INFINITY;
-      ls_st[d] = ok ? a.part_ml[((q0 + d) * 2 + 1) * a.H + h] : 0.f;
-    }
+  __shared__ float ms_st[MS], ls_st[MS];
+  const float *ml = a.part_ml + q0 * 2 * a.H + h;               // split s: m at [2 s H], l at [(2 s + 1) H]
+  const float *po = a.part_o + (q0 * a.H + h) * kD + d;         // split s at [s H kD]
+  const int sd = min(d, n - 1), HD = a.H * kD;
+  const float mv = ml[2 * sd * a.H], lv = ml[(2 * sd + 1) * a.H];
+  float o[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) o[s] = po[min(s, n - 1) * HD];
+  if (d < MS) {
+    ms_st[d] = d < n ? mv : -INFINITY;
+    ls_st[d] = d < n ? lv : 0.f;
   }
+  __syncthreads();
+  float m[MS], l[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
-    const bool ok = s < a.n_splits;
-    if constexpr (!STAGE) {
-      m[s] = ok ? a.part_ml[((q0 + s) * 2 + 0) * a.H + h] : -INFINITY;
-      l[s] = ok ? a.part_ml[((q0 + s) * 2 + 1) * a.H + h] : 0.f;
-    }
-    o[s] = ok ? a.part_o[((q0 + s) * a.H + h) * kD + d] : 0.f;
-  }
-  if constexpr (STAGE) {
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < MS; ++s) {
-      m[s] = ms_st[s];
-      l[s] = ls_st[s];
-    }
+    m[s] = ms_st[s];
+    l[s] = ls_st[s];
   }
   float mx = -INFINITY;
 #pragma unroll

@@ -450,16 +450,15 @@ __device__ bool select_ordered(const uint64_t *cand_key, int c, int k, int *hist
 // so every thread's candidates are consecutive and the compaction keeps their
 // order. No pass re-reads the candidates from LDS; each key's bin is computed
 // once.
+// ok[u] marks the slots that hold a candidate: the candidates of all threads,
+// taken in thread order and then slot order, are in ascending index order.
 template <int P, typename Map = IdMap>
-__device__ bool select_ordered_regs(const uint64_t (&kr)[P], int c, int k, int *hist, float *red, int *sh,
-                                    uint64_t *bin_keys, int32_t *out, Map map = Map()) {
+__device__ __forceinline__ bool select_ordered_regs_ok(const uint64_t (&kr)[P], const bool (&ok)[P], int k, int *hist, float *red,
+                                       int *sh, uint64_t *bin_keys, int32_t *out, Map map = Map()) {
   const int t = threadIdx.x, bd = blockDim.x, lane = t & 63, w = t >> 6;
-  const int span = (c + bd - 1) / bd, i0 = t * span;
-  bool ok[P];
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int u = 0; u < P; ++u) {
-    ok[u] = u < span && i0 + u < c;
     if (ok[u]) {
       const float v = bits_score(static_cast<uint32_t>(kr[u] >> 32));
       lo = fminf(lo, v);
@@ -512,6 +511,17 @@ __device__ bool select_ordered_regs(const uint64_t (&kr)[P], int c, int k, int *
   for (int u = 0; u < P; ++u)
     if (ok[u] && kr[u] >= kth) out[pos++] = map(key_index(kr[u]));
   return true;
+}
+
+// Thread t holds candidates [t s, t s + s) of c (s = ceil(c / blockDim) <= P).
+template <int P, typename Map = IdMap>
+__device__ __forceinline__ bool select_ordered_regs(const uint64_t (&kr)[P], int c, int k, int *hist, float *red, int *sh,
+                                    uint64_t *bin_keys, int32_t *out, Map map = Map()) {
+  const int span = (c + blockDim.x - 1) / blockDim.x, i0 = threadIdx.x * span;
+  bool ok[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) ok[u] = u < span && i0 + u < c;
+  return select_ordered_regs_ok(kr, ok, k, hist, red, sh, bin_keys, out, map);
 }
 
 
@@ -840,37 +850,33 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
   const int e_begin = slice * kFilterSlice, e_end = min(N, e_begin + kFilterSlice);
 
   // this slice's scores, 16 consecutive per thread (so a thread-order prefix
-  // keeps ascending index order); every load issued before any is used
+  // keeps ascending index order), and the query's group maxima in registers:
+  // U float4 per thread, the smallest of 2, 4, 8 that holds its nG maxima (M
+  // rows are padded to 256 floats). Both sets of loads sit in one branch-free
+  // stretch per U, maxima first, so they share one round trip.
   constexpr int kPer = kFilterSlice / 256;
   const int t0 = e_begin + tid * kPer;
   float sv[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; u += 4) {
-    if (t0 + u + 3 < e_end) {
-      const float4 v = *reinterpret_cast<const float4 *>(Srow + t0 + u);
-      sv[u] = v.x; sv[u + 1] = v.y; sv[u + 2] = v.z; sv[u + 3] = v.w;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sv[u + q] = t0 + u + q < e_end ? Srow[t0 + u + q] : -1.f;
-    }
-  }
-  // the query's group maxima in registers, 16-byte loads issued with the
-  // score loads (one round trip; M rows are padded to 256 floats), U float4
-  // per thread: the smallest of 2, 4, 8 that holds the query's nG maxima
   static_assert(kMaxGroups == 8 * 1024, "at most 8 float4 of group maxima per thread");
-  auto threshold = [&](auto u_tag) {
+  auto load_threshold = [&](auto u_tag) {
     constexpr int U = decltype(u_tag)::value;
+    // addresses are clamped into the row instead of guarded, so no load waits
+    // on a branch; values past nG (maxima) or e_end (scores) are never used
     float4 mv[U];
+    const int last4 = max(0, (nG - 1) >> 2);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i4 = 256 * u + tid;
-      mv[u] = 4 * i4 < nG ? *reinterpret_cast<const float4 *>(Mrow + 4 * i4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < U; ++u) mv[u] = *reinterpret_cast<const float4 *>(Mrow + 4 * min(256 * u + tid, last4));
+    const int smax = a.s_stride - 4;
+#pragma unroll
+    for (int u = 0; u < kPer; u += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(Srow + min(t0 + u, smax));
+      sv[u] = v.x; sv[u + 1] = v.y; sv[u + 2] = v.z; sv[u + 3] = v.w;
     }
     return nG > a.k ? tau_lower_bound_regs(mv, nG, a.k, hist, red, sh) : 0.f;
   };
-  const float tau = nG <= 2048 ? threshold(std::integral_constant<int, 2>{})
-                  : nG <= 4096 ? threshold(std::integral_constant<int, 4>{})
-                               : threshold(std::integral_constant<int, 8>{});
+  const float tau = nG <= 2048 ? load_threshold(std::integral_constant<int, 2>{})
+                  : nG <= 4096 ? load_threshold(std::integral_constant<int, 4>{})
+                               : load_threshold(std::integral_constant<int, 8>{});
 
   // ordered compaction into this slice's own region
   int mine = 0;
@@ -896,6 +902,12 @@ __global__ __launch_bounds__(256) void idx_filter_kernel(const IdxFilterArgs a) 
 
 // ------------------------------------------------------------------ decode final
 
+// Speculative candidate load of the final select: queries with at most
+// kFinalSpecSlices filter slices read every slice's first 512 / ns2 * 8 slots
+// together with the counts (8 per thread of 512).
+constexpr int kFinalSpecSlices = 64;
+constexpr int kFinalSpecPer = 8;
+
 struct FinalLds {
   uint64_t bin_keys[kRankCap];
   int sel[CSA_MAX_TOPK];
@@ -907,7 +919,7 @@ struct FinalLds {
 };
 
 template <typename Map>
-__device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, int k, int32_t *out, Map map) {
+__device__ __forceinline__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, int k, int32_t *out, Map map) {
   uint64_t *bin_keys = L.bin_keys;
   int *sel = L.sel, *hist = L.hist, *soff = L.soff, *sh = L.sh, *wsum_f = L.wsum_f;
   float *red = L.red;
@@ -916,9 +928,56 @@ __device__ void final_select(const IdxFinalArgs &a, FinalLds &L, int qi, int N, 
     for (int i = tid; i < k; i += blockDim.x) out[i] = i < N ? map(i) : -1;
     return;
   }
-  // slice counts -> offsets (slices in index order, each region already ordered)
   const int ns = (N + kFilterSlice - 1) / kFilterSlice;
   const int32_t *cnts = a.cnt + static_cast<int64_t>(qi) * a.max_slices;
+  if (ns <= kFinalSpecSlices) {
+    // the slice counts and the first slots of every slice in one round trip:
+    // 512 / ns2 threads per slice (ns2 = ns rounded up to a power of two),
+    // 8 consecutive slots each, so thread order then slot order is index order
+    int ns2 = 1;
+    while (ns2 < ns) ns2 <<= 1;
+    const int tps = 512 / ns2, sl = tid / tps, j0 = (tid % tps) * kFinalSpecPer;
+    const int e0 = sl * kFilterSlice;
+    const int n_sl = sl < ns ? min(kFilterSlice, N - e0) : 0;   // entries (and slots) of the slice
+    const int64_t o0 = static_cast<int64_t>(qi) * a.s_stride + e0 + j0;
+    const int cs = sl < ns ? cnts[sl] : 0;
+    float ts[kFinalSpecPer];
+    int tj[kFinalSpecPer];
+    if (j0 + kFinalSpecPer <= n_sl) {
+#pragma unroll
+      for (int u = 0; u < kFinalSpecPer; u += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.cand_s + o0 + u);
+        const int4 j = *reinterpret_cast<const int4 *>(a.cand_j + o0 + u);
+        ts[u] = v.x; ts[u + 1] = v.y; ts[u + 2] = v.z; ts[u + 3] = v.w;
+        tj[u] = j.x; tj[u + 1] = j.y; tj[u + 2] = j.z; tj[u + 3] = j.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kFinalSpecPer; ++u) {
+        ts[u] = j0 + u < n_sl ? a.cand_s[o0 + u] : 0.f;
+        tj[u] = j0 + u < n_sl ? a.cand_j[o0 + u] : 0;
+      }
+    }
+    bool ok[kFinalSpecPer];
+    uint64_t tk[kFinalSpecPer];
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kFinalSpecPer; ++u) {
+      ok[u] = j0 + u < cs;
+      tk[u] = score_key(ts[u], tj[u]);
+      mine += ok[u] ? 1 : 0;
+    }
+    // every slice's candidates inside its slots, and at least k of them
+    const bool over = (tid % tps) == tps - 1 && cs > j0 + kFinalSpecPer;
+    int incl = wave_incl_sum(mine);
+    if ((tid & 63) == 63) wsum_f[tid >> 6] = incl;
+    const bool any_over = __syncthreads_or(over);
+    int c = 0;
+    for (int i = 0; i < 8; ++i) c += wsum_f[i];
+    if (!any_over && c >= k && select_ordered_regs_ok(tk, ok, k, hist, red, sh, bin_keys, out, map)) return;
+    __syncthreads();   // the general path below reuses the same LDS
+  }
+  // slice counts -> offsets (slices in index order, each region already ordered)
   for (int i = tid; i < ns; i += blockDim.x) soff[i + 1] = cnts[i];
   if (tid == 0) soff[0] = 0;
   __syncthreads();
