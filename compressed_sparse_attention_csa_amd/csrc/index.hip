@@ -551,6 +551,14 @@ __device__ void block_prefix_sum(int *arr, int n, int *wsum) {
 
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 
+// A wave-uniform load of data no kernel of this launch writes, through the
+// scalar cache into a scalar register (no vector register, and its wait is
+// separate from the vector loads' counter).
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)(p);
+}
+
 // One workgroup = kScanWaves waves, each owning kScanPagesPerWave consecutive pages of
 // one query's visible entries. A wave reads its page ids, issues every key
 // load of its pages at once, and scores 16 entries per MFMA (indexer heads as
@@ -587,6 +595,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
   float run = -INFINITY;
 
   if (wave_e0 < N) {
+    // this lane's head row (placed in the tile col / 4 whose rows it
+    // supplies), issued first: in flight during the block-table round trip
+    // instead of behind the key stream
+    Frag<CT> qv[2];
+    qv[0] = qv[1] = zero_frag<CT>();
+    if ((col & 3) < a.h_i) {
+      const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + (col & 3)) * kDI * AE;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qv[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
+    }
     const int32_t *bt = a.block_table + static_cast<int64_t>(Q.seq) * a.bt_stride;
     const char *kbase = reinterpret_cast<const char *>(a.kidx);
     int pps[PPW];
@@ -628,34 +646,25 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
       if (!okp[p] && lane == 0 && wave_e0 + p * kPage < N) flag_error(a.err, ERR_PAGE);
-      scs[p] = (KV == DT_FP8 && okp[p]) ? a.kidx_scale[pps[p]] : 1.f;
+      scs[p] = (KV == DT_FP8 && okp[p]) ? scalar_load(a.kidx_scale + pps[p]) : 1.f;
     }
-    // (issued after the key loads, which are the long pole) this lane's head
-    // row, placed in the tile (col / 4) whose rows it supplies
-    Frag<CT> qv[2];
-    qv[0] = qv[1] = zero_frag<CT>();
-    if ((col & 3) < a.h_i) {
-      const char *qrow = reinterpret_cast<const char *>(a.q_idx) + (static_cast<int64_t>(qi) * a.h_i + (col & 3)) * kDI * AE;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) qv[c] = LoadFrag<ACT, CT>::load(qrow + (16 * g + 8 * c) * AE);
-    }
-    Frag<CT> qa[4][2];
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) qa[tl][c] = (col >> 2) == tl ? qv[c] : zero_frag<CT>();
+    // head weights and page scales are scalar loads issued after the keys:
+    // scalar loads complete out of order, so any earlier one would hold the
+    // block-table wait
     float wv[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? a.w_idx[qi * a.h_i + v] : 0.f;
-
+    for (int v = 0; v < 4; ++v) wv[v] = v < a.h_i ? scalar_load(a.w_idx + qi * a.h_i + v) : 0.f;
+    // tiles outer, pages inner: only one tile's A operands are live at a time
+    f32x4_t accp[PPW];
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-      const int e_page = wave_e0 + p * kPage;
-      if (e_page >= N) break;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < PPW; ++p) accp[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int tl = 0; tl < 4; ++tl) {
-        if (e_page + tl * 16 >= N) break;
+    for (int tl = 0; tl < 4; ++tl) {
+      const Frag<CT> qa0 = (col >> 2) == tl ? qv[0] : zero_frag<CT>();
+      const Frag<CT> qa1 = (col >> 2) == tl ? qv[1] : zero_frag<CT>();
+#pragma unroll
+      for (int p = 0; p < PPW; ++p) {
+        if (wave_e0 + p * kPage + tl * 16 >= N) continue;
         Frag<CT> kb[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -664,9 +673,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_scan_kernel(const IdxScan
           else if constexpr (KV == DT_BF16) kb[c] = LoadFrag<DT_BF16, __bf16>::load(rp);
           else kb[c] = LoadFrag<DT_F32, float>::load(rp);
         }
-        acc = mma(qa[tl][0], kb[0], acc);
-        acc = mma(qa[tl][1], kb[1], acc);
+        accp[p] = mma(qa0, kb[0], accp[p]);
+        accp[p] = mma(qa1, kb[1], accp[p]);
       }
+    }
+
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+      const int e_page = wave_e0 + p * kPage;
+      if (e_page >= N) break;
+      const f32x4_t acc = accp[p];
       const int e = e_page + lane;   // lane = 16 g + col
       float s = 0.f;
 #pragma unroll
