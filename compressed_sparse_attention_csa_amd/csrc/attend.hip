@@ -193,6 +193,26 @@ __global__ __launch_bounds__(HG * KH * 64) void attend_kernel(const AttendArgs a
   const int32_t *trow = a.dense ? nullptr : a.topk + static_cast<int64_t>(qi) * a.k;
   const int tid = threadIdx.x;
 
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hg = wave % HG, kh = wave / HG, g = lane >> 4, col = lane & 15;
+
+  // Q fragments (B operand of S^T) for this wave's head tiles, loaded first:
+  // in flight during the key resolution
+  Frag<CT> qf[NTW][4];
+  f32x4_t O[NTW][8];
+  float m_run[NTW], l_run[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int head = 16 * (hg + HG * j) + col;
+    const char *qrow = reinterpret_cast<const char *>(a.q) + (static_cast<int64_t>(qi) * H + head) * kD * AE;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[j][c] = LoadFrag<ACT, CT>::load(qrow + (32 * g + 8 * c) * AE);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) O[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
+
   // ---------------- 1. resolve every key of the split once: all Top-K reads
   // of a thread first, then all of its block-table reads (two round trips)
   constexpr int kMaxPer = (kAttMaxSplitKeys + NT - 1) / NT;
@@ -373,24 +393,6 @@ __global__ __launch_bounds__(HG * KH * 64) void attend_kernel(const AttendArgs a
     }
   };
 
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, hg = wave % HG, kh = wave / HG, g = lane >> 4, col = lane & 15;
-
-  // Q fragments (B operand of S^T) for this wave's head tiles
-  Frag<CT> qf[NTW][4];
-  f32x4_t O[NTW][8];
-  float m_run[NTW], l_run[NTW];
-#pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int head = 16 * (hg + HG * j) + col;
-    const char *qrow = reinterpret_cast<const char *>(a.q) + (static_cast<int64_t>(qi) * H + head) * kD * AE;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qf[j][c] = LoadFrag<ACT, CT>::load(qrow + (32 * g + 8 * c) * AE);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) O[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
-  }
 
   const int n_rounds = b_end - b_begin;
   if (n_rounds > 0) load_round(0);

@@ -1102,17 +1102,28 @@ __global__ __launch_bounds__(kScanWaves * 64) void idx_rescan_kernel(const IdxRe
   float *Mrow = a.M + static_cast<int64_t>(qi) * a.s_stride;
   const int glog2 = Q.glog2, G = 1 << glog2;
 
-  int ent[4], pg[4];
+  // the four block ids, then the four pages, each set in one round trip:
+  // addresses are clamped into the rows instead of guarded, so no load waits
+  // behind the error checks (V >= 1 here; the block-table row has >= 1 entry)
+  int bid[4], ent[4], pg[4];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) bid[tl] = prow[min(wave_p0 + tl * 16 + col, V - 1) >> 3];
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
     const int p = wave_p0 + tl * 16 + col;
-    const int b = p < V ? prow[p >> 3] : -1;
+    const int b = p < V ? bid[tl] : -1;
     const int e = b * 8 + (p & 7);
-    if (p < V && (b < 0 || b * 8 >= n_ent) && g == 0 && (p & 7) == 0) flag_error(a.err, ERR_TOPK);
     ent[tl] = (p < V && b >= 0 && e < n_ent) ? e : -1;
   }
 #pragma unroll
-  for (int tl = 0; tl < 4; ++tl) pg[tl] = ent[tl] >= 0 ? bt[ent[tl] >> 6] : -1;
+  for (int tl = 0; tl < 4; ++tl) pg[tl] = bt[max(ent[tl], 0) >> 6];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const int p = wave_p0 + tl * 16 + col;
+    const int b = p < V ? bid[tl] : -1;
+    if (p < V && (b < 0 || b * 8 >= n_ent) && g == 0 && (p & 7) == 0) flag_error(a.err, ERR_TOPK);
+    if (ent[tl] < 0) pg[tl] = -1;
+  }
 
   constexpr int RW = KE;
   const char *kbase = reinterpret_cast<const char *>(a.kidx);
@@ -1408,6 +1419,12 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
 }
 
 // Per query: tau from its sampled scores.
+// U float4 per thread hold a query's samples when ns <= 1024 U (the host picks
+// the smallest U of 1, 2, 4, 8, 16 that covers the chunk's last query; each U is
+// its own kernel so the common small case keeps few registers and many
+// workgroups per CU). The loads take one round trip (rows are padded to 256
+// floats; addresses past the last sample are clamped and those values ignored).
+template <int U>
 __global__ __launch_bounds__(256) void idx_chunk_tau_kernel(const IdxChunkArgs a) {
   __shared__ int hist[kTauBins];
   __shared__ float red[32];
@@ -1418,7 +1435,11 @@ __global__ __launch_bounds__(256) void idx_chunk_tau_kernel(const IdxChunkArgs a
   float tau = 0.f;
   if (ns > a.m_s) {
     const float *row = a.ss + static_cast<int64_t>(qi) * a.ss_stride;
-    tau = tau_lower_bound([&](int i) { return row[i]; }, ns, a.m_s, hist, red, sh);
+    float4 v[U];
+    const int last4 = (ns - 1) >> 2;
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const float4 *>(row + 4 * min(256 * u + static_cast<int>(threadIdx.x), last4));
+    tau = tau_lower_bound_regs(v, ns, a.m_s, hist, red, sh);
   }
   if (threadIdx.x == 0) a.tau[qi] = tau;
 }
@@ -1553,7 +1574,14 @@ __global__ __launch_bounds__(512) void idx_chunk_pool_kernel(const IdxChunkArgs 
   }
   bool done = false;
   if (nB <= kSelCap) {
-    for (int i = tid; i < nB; i += bd) keys[i] = score_key(row[i], i);
+    // every load issued before the first use (clamped addresses, one round trip)
+    constexpr int kPer = (kSelCap + 511) / 512;
+    float v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) v[u] = row[min(tid + u * bd, nB - 1)];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (tid + u * bd < nB) keys[tid + u * bd] = score_key(v[u], tid + u * bd);
     __syncthreads();
     done = select_ordered(keys, nB, P, hist, red, sh, bin_keys, out);
   }
@@ -1622,7 +1650,14 @@ void launch_idx_chunk(const IdxChunkArgs &a, int kv, int act, hipStream_t s, hip
       hipExtLaunchKernelGGL((idx_chunk_gemm_kernel<DT_BF16, DT_FP8, M>), dim3(n_wg), dim3(256), 0, s, e0, e1, 0, a);
   };
   gemm(std::integral_constant<int, 0>{}, a.n_stiles, nullptr, nullptr);
-  hipLaunchKernelGGL(idx_chunk_tau_kernel, dim3(a.n_tok), dim3(256), 0, s, a);
+  static_assert(kChunkMaxEntries / kChunkSample <= 16 * 1024, "at most 16 float4 of samples per thread");
+  const int ns_max = (a.pos0 + a.n_tok) / a.r / kChunkSample;   // the last query sees the most
+  const dim3 tg(a.n_tok), tb(256);
+  if (ns_max <= 1024) hipLaunchKernelGGL(idx_chunk_tau_kernel<1>, tg, tb, 0, s, a);
+  else if (ns_max <= 2048) hipLaunchKernelGGL(idx_chunk_tau_kernel<2>, tg, tb, 0, s, a);
+  else if (ns_max <= 4096) hipLaunchKernelGGL(idx_chunk_tau_kernel<4>, tg, tb, 0, s, a);
+  else if (ns_max <= 8192) hipLaunchKernelGGL(idx_chunk_tau_kernel<8>, tg, tb, 0, s, a);
+  else hipLaunchKernelGGL(idx_chunk_tau_kernel<16>, tg, tb, 0, s, a);
   if (a.pool) gemm(std::integral_constant<int, 2>{}, a.n_etiles, ev0, ev1);
   else gemm(std::integral_constant<int, 1>{}, a.n_etiles, ev0, ev1);
 }
