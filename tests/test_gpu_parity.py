@@ -673,6 +673,48 @@ def test_index_chunk_threshold_fallback_is_exact(kv, act):
         assert ok, f"token {i}: {msg}"
 
 
+@pytest.mark.parametrize("kv,act", [("fp8", "bf16"), ("f32", "f32")])
+def test_index_decode_candidates_crowd_one_slice(kv, act):
+    """The decode final select reads every filter slice's first slots together
+    with the slice counts; a slice with more candidates than those slots sends
+    the query down the two-step path (counts, then candidates). Keys of one
+    4,096-entry slice are scaled up so that nearly all of the Top-512 (and so
+    hundreds of candidates) sit in it; the result must still be the oracle's
+    Top-K, without the exact full-row fallback."""
+    from gpu_helpers import store_raw_to_torch, write_logical, write_scales
+    r, k, seed = 4, 512, 19
+    lens = [4 * 65536, 4 * 40000 + 1]
+    max_pages = max(L // r for L in lens) // 64 + 2
+    cache = make_cache(seed, ratio=r, q_heads=16, idx_heads=4, window=0, ring_rows=8, max_seqs=len(lens),
+                       max_pages_per_seq=max_pages, pool_pages=len(lens) * max_pages + 1, kv_dtype=kv,
+                       act_dtype=act, max_queries=len(lens), max_k=k)
+    keys = []
+    for b, L in enumerate(lens):
+        n = L // r
+        x = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_KI, 0, b), 0, n, 64).double().numpy()
+        x[3 * 4096: 4 * 4096] *= 3.0           # slice 3 holds nearly every large score
+        vals, rawv = O.store(x, kv)
+        write_logical(cache, cache.kidx, b, store_raw_to_torch(rawv, kv))
+        if kv == "fp8":
+            write_scales(cache, cache.kidx_scale, b, rawv[1])
+        keys.append(vals)
+        B.csa_seq_set_len(cache.handle, 0, b, L)
+    q_seq, q_pos = [0, 1], [L - 1 for L in lens]
+    qi = Sy.normal_rows(seed, Sy.stream_id(Sy.KIND_QI), 0, 2 * 4, 64, dtype=TORCH_ACT[act]).view(2, 4, 64)
+    w = Sy.uniform_rows(seed, Sy.stream_id(Sy.KIND_W), 0, 2, 4)
+    T = cache.index_topk(q_seq, q_pos, qi.cuda(), w.cuda(), k).cpu().numpy()
+    assert cache.read_errors() == 0, "no fallback and no error expected"
+    q64, w64 = to64(qi), to64(w)
+    for i in range(2):
+        N = O.visible_entries(q_pos[i], r)
+        s = O.index_scores(q64[i], w64[i], keys[i][:N])
+        To = O.topk(s, k)
+        in_slice = int(np.sum((To >= 3 * 4096) & (To < 4 * 4096)))
+        assert in_slice > 64, f"query {i}: only {in_slice} of the Top-{k} in the crowded slice"
+        ok, msg = topk_matches(T[i], To, s)
+        assert ok, f"query {i}: {msg}"
+
+
 def test_index_chunk_exact_ties():
     _index_case("bf16", "bf16", lens=[4 * 3000], k=96, dup_keys=True, exact=True, chunk=(0, 130))
 
