@@ -1339,6 +1339,10 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
     // candidates of (query, this tile) so far; every lane of a 16-lane group
     // scores the same query, so the group's ballot orders its slots by entry
     int run[kMT] = {};
+    uint64_t *cand_t[kMT];   // this tile's candidate slots of each of the lane's queries
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+      cand_t[mt] = a.cand + (static_cast<int64_t>(min(qw + 4 * mt + g, a.n_tok - 1)) * a.n_etiles + et) * kWgCand;
     // every (query, entry) pair of the wave visible in this tile: skip the per-score test
     // (the tile's code comes in two copies: without any visibility test for
     // the common fully visible tile, and with it)
@@ -1395,10 +1399,12 @@ __global__ __launch_bounds__(256) void idx_chunk_gemm_kernel(const IdxChunkArgs 
             const bool take = vis && s >= tq[mt];
             const uint32_t seg = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(take) >> (16 * g)) & 0xffffu;
             if (take) {
-              const int slot = run[mt] + __popc(seg & ((1u << col) - 1u));
-              if (slot < kWgCand)
-                a.cand[(static_cast<int64_t>(qo) * a.n_etiles + et) * kWgCand + slot] =
-                    (static_cast<uint64_t>(static_cast<uint32_t>(e)) << 32) | __float_as_uint(s);
+              // a tile with more than kWgCand candidates sends its query to the
+              // select's exact fallback, which ignores the slots: the index is
+              // clamped instead of tested
+              const uint32_t slot = min(static_cast<uint32_t>(run[mt]) + __popc(seg & ((1u << col) - 1u)),
+                                        static_cast<uint32_t>(kWgCand - 1));
+              cand_t[mt][slot] = (static_cast<uint64_t>(static_cast<uint32_t>(e)) << 32) | __float_as_uint(s);
             }
             run[mt] += __popc(seg);
           }
